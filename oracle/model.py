@@ -1,0 +1,276 @@
+"""fp64 numpy reference of the nanochat GPT forward: batched prefill and KV-cache decode.
+
+TEST INFRASTRUCTURE ONLY (tests, the graft smoke check and the benchmark's CPU-baseline
+leg may use it; the product path must not).  It imports nothing from the product.
+
+What is computed, and where the pages say so:
+  * dense decoder-only Transformer, Llama-like but simplified
+    [yelogs.com launch write-up, section "technical details and official Q&A",
+    answer on the model architecture; szyisi.cn launch article, introduction];
+  * rotary position embedding, no absolute position embedding [same answer; apidog.com/th
+    "How to train your own ChatGPT for $50", section "How nanochat works" part 1 (GPT model),
+    architecture features; geoz.com.cn summary, section on development tricks: a concise
+    self-written RoPE with precomputed rotary tables];
+  * QK-norm on queries and keys [yelogs.com architecture answer; apidog.com part 1];
+  * RMSNorm without learnable parameters, after the token embedding and before the MLP
+    [yelogs.com architecture answer; szyisi.cn, pretraining section: besides the matrices
+    and embeddings the model has no other trainable parameters];
+  * untied token embedding and LM head [yelogs.com architecture answer; apidog.com part 1];
+  * squared-ReLU MLP activation [yelogs.com architecture answer (formula lost in the
+    extracted text); geoz.com.cn development tricks; apidog.com part 1];
+  * no bias in any linear layer [yelogs.com architecture answer];
+  * multi-query attention, one K/V head shared by every query head [yelogs.com answer];
+  * a softcap on the logits [yelogs.com architecture answer];
+  * inference with a KV cache: prefill of the prompt, then one token per decode step
+    [szyisi.cn, section on the base model and the Engine class; apidog.com part 6,
+    inference engine].
+
+Readings where the pages are silent (each is listed with its reason in the design notes):
+  * norm placement: pre-norm before attention and before the MLP, one norm right after the
+    embedding, and a final norm before the LM head;
+  * RMSNorm: x / sqrt(mean(x^2) + eps), eps a config value (1e-6), also used for QK-norm;
+  * RoPE: rotation of the pair (i, i + hd/2) by angle p * base^(-2i/hd), positions from 0,
+    applied before QK-norm (the two commute, since the rotation keeps mean(x^2));
+  * attention: scale 1/sqrt(hd), causal including the diagonal, full max-subtracted softmax;
+  * MLP: d -> d_ff -> d, activation relu(x)^2, no gate;
+  * residual: plain x <- x + f(norm(x));
+  * softcap: cap * tanh(z / cap).
+
+Everything is evaluated in float64 with plain numpy operations: no tiling, no online
+softmax, no fusion.  Weights may arrive in any float dtype; they are widened to float64
+exactly once, when the model object is built.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def rms_norm(x, eps):
+    """Parameter-free RMSNorm over the last axis: x / sqrt(mean(x^2) + eps)."""
+    x = np.asarray(x, dtype=F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps)
+
+
+def rope_tables(n_pos, head_dim, base):
+    """cos/sin of the rotation angles, shape [n_pos, head_dim/2].
+
+    Angle for position p and pair i is p * base^(-2i/head_dim), computed in float64
+    (the precomputed rotary table of the geoz.com.cn development-tricks section)."""
+    half = head_dim // 2
+    i = np.arange(half, dtype=F64)
+    inv_freq = np.power(F64(base), -2.0 * i / head_dim)
+    ang = np.arange(n_pos, dtype=F64)[:, None] * inv_freq[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def rope(x, pos, cos, sin):
+    """Rotate the last axis of x by the angles of integer positions `pos`.
+
+    x has shape [..., hd]; pos is an integer array broadcastable against x.shape[:-1].
+    The first half of the vector is paired with the second half: (x1, x2) ->
+    (x1 cos - x2 sin, x1 sin + x2 cos)."""
+    x = np.asarray(x, dtype=F64)
+    half = x.shape[-1] // 2
+    c = cos[pos]
+    s = sin[pos]
+    x1 = x[..., :half]
+    x2 = x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def relu2(z):
+    """Squared ReLU: max(z, 0)^2."""
+    r = np.maximum(np.asarray(z, dtype=F64), 0.0)
+    return r * r
+
+
+def softcap(z, cap):
+    """Logit softcap cap * tanh(z / cap)."""
+    return cap * np.tanh(np.asarray(z, dtype=F64) / cap)
+
+
+def linear(x, w):
+    """Bias-free linear layer with a weight stored [out, in]: y = x W^T."""
+    return np.asarray(x, dtype=F64) @ np.asarray(w, dtype=F64).T
+
+
+def causal_attention(q, k, v, q_pos):
+    """Causal softmax attention with shared K/V heads.
+
+    q: [Tq, H, hd]; k, v: [Tk, n_kv, hd] holding key positions 0..Tk-1;
+    q_pos: [Tq] absolute position of each query.  Query t sees keys j <= q_pos[t].
+    Query head h reads K/V head h // (H / n_kv); with n_kv = 1 every query head shares
+    the single K/V head (multi-query attention)."""
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    tq, n_head, hd = q.shape
+    tk, n_kv, _ = k.shape
+    group = n_head // n_kv
+    hidden = np.arange(tk)[None, :] > np.asarray(q_pos)[:, None]
+    y = np.empty((tq, n_head, hd), dtype=F64)
+    for h in range(n_head):
+        g = h // group
+        s = (q[:, h, :] @ k[:, g, :].T) / np.sqrt(F64(hd))
+        s = np.where(hidden, -np.inf, s)
+        s = s - np.max(s, axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / np.sum(p, axis=1, keepdims=True)
+        y[:, h, :] = p @ v[:, g, :]
+    return y
+
+
+def param_count(n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, vocab):
+    """Number of weights: untied embedding and head, four attention matrices and two MLP
+    matrices per layer, no biases and no norm parameters."""
+    per_layer = (d_model * n_head * head_dim          # Wq
+                 + 2 * d_model * n_kv_head * head_dim  # Wk, Wv
+                 + n_head * head_dim * d_model         # Wo
+                 + 2 * d_model * d_ff)                 # Wfc, Wproj
+    return 2 * vocab * d_model + n_layer * per_layer
+
+
+_CFG_FIELDS = ("n_layer", "d_model", "n_head", "n_kv_head", "head_dim", "d_ff", "vocab",
+               "rope_base", "softcap", "norm_eps")
+_LAYER_KEYS = ("wq", "wk", "wv", "wo", "wfc", "wproj")
+
+
+class OracleModel:
+    """The forward pass of one model, holding float64 copies of its weights.
+
+    cfg: any object with the attributes n_layer, d_model, n_head, n_kv_head, head_dim, d_ff,
+    vocab, rope_base, softcap, norm_eps.
+    weights: {"wte": [V, d], "layers": [{"wq": [H*hd, d], "wk": [n_kv*hd, d],
+    "wv": [n_kv*hd, d], "wo": [d, H*hd], "wfc": [d_ff, d], "wproj": [d, d_ff]}, ...],
+    "lm_head": [V, d]}.
+    """
+
+    def __init__(self, cfg, weights):
+        for f in _CFG_FIELDS:
+            setattr(self, f, getattr(cfg, f))
+        assert self.n_head % self.n_kv_head == 0
+        self.wte = np.asarray(weights["wte"], dtype=F64)
+        self.lm_head = np.asarray(weights["lm_head"], dtype=F64)
+        self.layers = [{k: np.asarray(lw[k], dtype=F64) for k in _LAYER_KEYS}
+                       for lw in weights["layers"]]
+        assert len(self.layers) == self.n_layer
+        self._cos = np.zeros((0, self.head_dim // 2))
+        self._sin = self._cos
+
+    # -- helpers ---------------------------------------------------------------------
+    def _tables(self, n_pos):
+        if self._cos.shape[0] < n_pos:
+            self._cos, self._sin = rope_tables(max(n_pos, 2 * self._cos.shape[0]),
+                                               self.head_dim, self.rope_base)
+        return self._cos, self._sin
+
+    def _qkv(self, lw, x, pos):
+        """Pre-attention norm, projections, RoPE and QK-norm for rows x at positions pos."""
+        t = x.shape[0]
+        h = rms_norm(x, self.norm_eps)
+        q = linear(h, lw["wq"]).reshape(t, self.n_head, self.head_dim)
+        k = linear(h, lw["wk"]).reshape(t, self.n_kv_head, self.head_dim)
+        v = linear(h, lw["wv"]).reshape(t, self.n_kv_head, self.head_dim)
+        cos, sin = self._tables(int(np.max(pos)) + 1)
+        q = rms_norm(rope(q, pos[:, None], cos, sin), self.norm_eps)
+        k = rms_norm(rope(k, pos[:, None], cos, sin), self.norm_eps)
+        return q, k, v
+
+    def _mlp(self, lw, x):
+        return linear(relu2(linear(rms_norm(x, self.norm_eps), lw["wfc"])), lw["wproj"])
+
+    def _head(self, x):
+        return softcap(linear(rms_norm(x, self.norm_eps), self.lm_head), self.softcap)
+
+    # -- cache -----------------------------------------------------------------------
+    def new_cache(self, batch, max_seq):
+        shape = (self.n_layer, batch, max_seq, self.n_kv_head, self.head_dim)
+        return {"k": np.zeros(shape, dtype=F64), "v": np.zeros(shape, dtype=F64),
+                "lens": np.zeros(batch, dtype=np.int64), "max_seq": max_seq}
+
+    # -- prefill ---------------------------------------------------------------------
+    def prefill(self, tokens, max_seq=None, logits_at=None, cache=None):
+        """Full-sequence forward of tokens [B, T] at positions 0..T-1.
+
+        Returns (logits, cache).  logits is [B, T, V], or [B, len(logits_at), V] when
+        logits_at lists the positions whose logits are wanted (the others are simply not
+        evaluated).  The cache holds the post-RoPE, post-norm keys and the values of every
+        layer, and lens = T."""
+        tokens = np.asarray(tokens)
+        b_sz, t_len = tokens.shape
+        max_seq = t_len if max_seq is None else max_seq
+        if cache is None:
+            cache = self.new_cache(b_sz, max_seq)
+        assert np.all(cache["lens"] == 0)
+        at = np.arange(t_len) if logits_at is None else np.asarray(logits_at)
+        logits = np.empty((b_sz, at.shape[0], self.vocab), dtype=F64)
+        pos = np.arange(t_len)
+        for b in range(b_sz):
+            x = rms_norm(self.wte[tokens[b]], self.norm_eps)
+            for li, lw in enumerate(self.layers):
+                q, k, v = self._qkv(lw, x, pos)
+                cache["k"][li, b, :t_len] = k
+                cache["v"][li, b, :t_len] = v
+                y = causal_attention(q, k, v, pos)
+                x = x + linear(y.reshape(t_len, -1), lw["wo"])
+                x = x + self._mlp(lw, x)
+            logits[b] = self._head(x[at])
+        cache["lens"][:] = t_len
+        return logits, cache
+
+    # -- decode ----------------------------------------------------------------------
+    def decode_step(self, cache, tokens):
+        """One new token per row: row b sits at position lens[b] and attends to cache
+        positions 0..lens[b] (its own key included).  Returns logits [B, V]; lens += 1."""
+        tokens = np.asarray(tokens).reshape(-1)
+        b_sz = tokens.shape[0]
+        assert b_sz == cache["lens"].shape[0]
+        assert np.all(cache["lens"] < cache["max_seq"])
+        logits = np.empty((b_sz, self.vocab), dtype=F64)
+        for b in range(b_sz):
+            p = int(cache["lens"][b])
+            pos = np.array([p])
+            x = rms_norm(self.wte[tokens[b:b + 1]], self.norm_eps)
+            for li, lw in enumerate(self.layers):
+                q, k, v = self._qkv(lw, x, pos)
+                cache["k"][li, b, p] = k[0]
+                cache["v"][li, b, p] = v[0]
+                y = causal_attention(q, cache["k"][li, b, :p + 1], cache["v"][li, b, :p + 1],
+                                     pos)
+                x = x + linear(y.reshape(1, -1), lw["wo"])
+                x = x + self._mlp(lw, x)
+            logits[b] = self._head(x)[0]
+        cache["lens"] += 1
+        return logits
+
+    def truncate(self, cache, lens):
+        """Shrink the cached length of each row (keys beyond the new length are dropped)."""
+        lens = np.asarray(lens, dtype=np.int64)
+        assert np.all(lens <= cache["lens"])
+        for b, n in enumerate(lens):
+            cache["k"][:, b, n:] = 0.0
+            cache["v"][:, b, n:] = 0.0
+        cache["lens"][:] = lens
+
+    def greedy(self, prompt, steps, max_seq=None):
+        """Greedy continuation of prompt [B, T] for `steps` tokens (ties: lowest index).
+
+        Returns (tokens [B, steps], logits [B, steps, V]) where logits[:, s] are the
+        logits that produced tokens[:, s + 1] (so tokens[:, 0] is the argmax of the
+        prompt's last position and step s feeds tokens[:, s])."""
+        prompt = np.asarray(prompt)
+        b_sz, t_len = prompt.shape
+        max_seq = t_len + steps if max_seq is None else max_seq
+        logits0, cache = self.prefill(prompt, max_seq=max_seq, logits_at=[t_len - 1])
+        tok = np.argmax(logits0[:, 0], axis=-1)
+        toks = np.empty((b_sz, steps), dtype=np.int64)
+        step_logits = np.empty((b_sz, steps, self.vocab), dtype=F64)
+        for s in range(steps):
+            toks[:, s] = tok
+            step_logits[:, s] = self.decode_step(cache, tok)
+            tok = np.argmax(step_logits[:, s], axis=-1)
+        return toks, step_logits

@@ -1,0 +1,272 @@
+"""Pins of the oracle's whole forward pass (prefill, decode, greedy) at micro sizes.
+
+The pages print no model outputs, so the end-to-end values are pinned by (1) a scalar
+pure-Python implementation written from the layer definitions, (2) structural invariants
+that any correct forward must satisfy, (3) closed forms of special cases, and (4) the
+pages' parameter-count and training-budget figures for the count helper."""
+
+import json
+import math
+import os
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from dense_decoder_only_bf16_amd.inputs import (TINY, Shape, make_tokens, make_weights,
+                                                from_depth)
+from oracle import OracleModel, param_count
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+MICRO = Shape("micro", n_layer=2, d_model=8, n_head=2, head_dim=4, d_ff=32, vocab=11,
+              dtype="f32", max_seq=16)
+
+
+def micro_weights(shape=MICRO, seed=0, std=0.3):
+    return make_weights(shape, seed=seed, std=std)
+
+
+# ------------------------------------------------------- scalar reference ------------
+def _norm(vec, eps):
+    ms = sum(a * a for a in vec) / len(vec)
+    return [a / math.sqrt(ms + eps) for a in vec]
+
+
+def _matvec(w, vec):
+    # nn.Linear convention: weight [out][in], y_o = sum_i W[o][i] x_i
+    return [sum(w[o][i] * vec[i] for i in range(len(vec))) for o in range(len(w))]
+
+
+def _rot(vec, p, base):
+    hd = len(vec)
+    half = hd // 2
+    out = [0.0] * hd
+    for i in range(half):
+        ang = p * base ** (-2.0 * i / hd)
+        a, b = vec[i], vec[i + half]
+        out[i] = a * math.cos(ang) - b * math.sin(ang)
+        out[i + half] = a * math.sin(ang) + b * math.cos(ang)
+    return out
+
+
+def scalar_forward(shape, w, tokens):
+    """Logits [T][V] of one row, written with Python scalars and loops."""
+    eps, hd, nh, nkv = shape.norm_eps, shape.head_dim, shape.n_head, shape.n_kv_head
+    wl = lambda a: a.astype(float).tolist()  # noqa: E731
+    xs = [_norm(wl(w["wte"][t]), eps) for t in tokens]
+    for lw in w["layers"]:
+        wq, wk, wv, wo = wl(lw["wq"]), wl(lw["wk"]), wl(lw["wv"]), wl(lw["wo"])
+        wfc, wproj = wl(lw["wfc"]), wl(lw["wproj"])
+        qs, ks, vs = [], [], []
+        for p, x in enumerate(xs):
+            h = _norm(x, eps)
+            q, k, v = _matvec(wq, h), _matvec(wk, h), _matvec(wv, h)
+            qs.append([_norm(_rot(q[i * hd:(i + 1) * hd], p, shape.rope_base), eps)
+                       for i in range(nh)])
+            ks.append([_norm(_rot(k[i * hd:(i + 1) * hd], p, shape.rope_base), eps)
+                       for i in range(nkv)])
+            vs.append([v[i * hd:(i + 1) * hd] for i in range(nkv)])
+        new = []
+        for p, x in enumerate(xs):
+            y = []
+            for hh in range(nh):
+                g = hh * nkv // nh
+                sc = [sum(qs[p][hh][c] * ks[j][g][c] for c in range(hd)) / math.sqrt(hd)
+                      for j in range(p + 1)]
+                m = max(sc)
+                e = [math.exp(s - m) for s in sc]
+                z = sum(e)
+                y += [sum(e[j] * vs[j][g][c] for j in range(p + 1)) / z for c in range(hd)]
+            x = [a + b for a, b in zip(x, _matvec(wo, y))]
+            u = [max(a, 0.0) ** 2 for a in _matvec(wfc, _norm(x, eps))]
+            x = [a + b for a, b in zip(x, _matvec(wproj, u))]
+            new.append(x)
+        xs = new
+    lm = wl(w["lm_head"])
+    return [[shape.softcap * math.tanh(z / shape.softcap)
+             for z in _matvec(lm, _norm(x, eps))] for x in xs]
+
+
+@pytest.mark.parametrize("n_kv", [1, 2])
+def test_prefill_matches_scalar_loops(n_kv):
+    shape = replace(MICRO, n_kv_head=n_kv)
+    w = micro_weights(shape, seed=3)
+    toks = make_tokens(shape.vocab, 2, 6, seed=4)
+    m = OracleModel(shape, w)
+    logits, _ = m.prefill(toks)
+    for b in range(2):
+        ref = np.array(scalar_forward(shape, w, toks[b].tolist()))
+        assert np.allclose(logits[b], ref, rtol=0, atol=1e-12)
+
+
+def test_zero_blocks_closed_form():
+    # With Wo = Wproj = 0 the blocks add nothing; the logits are then
+    # cap * tanh(norm(norm(e)) . lm_head / cap).  e = [3, 4] has mean square 12.5.
+    shape = Shape("z", 1, 2, 1, 2, 4, 3, "f32", 4, norm_eps=0.0)
+    w = micro_weights(shape, seed=1)
+    w["wte"] = np.array([[3.0, 4.0], [1.0, 0.0], [0.0, 2.0]], dtype=np.float32)
+    w["lm_head"] = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]], dtype=np.float32)
+    for k in ("wo", "wproj"):
+        w["layers"][0][k][:] = 0.0
+    logits, _ = OracleModel(shape, w).prefill(np.array([[0, 2]]))
+    s = math.sqrt(12.5)
+    want0 = [15 * math.tanh(v / 15) for v in (3 / s, 4 / s, 7 / s)]
+    want1 = [15 * math.tanh(v / 15) for v in (0.0, math.sqrt(2), math.sqrt(2))]
+    assert np.allclose(logits[0, 0], want0, atol=1e-14)
+    assert np.allclose(logits[0, 1], want1, atol=1e-14)
+
+
+# ------------------------------------------------------- cache / causality ----------
+def test_prefill_equals_token_by_token_decode():
+    w = micro_weights(seed=5)
+    m = OracleModel(MICRO, w)
+    toks = make_tokens(MICRO.vocab, 3, 9, seed=6)
+    full, _ = m.prefill(toks)
+    cache = m.new_cache(3, 16)
+    for t in range(9):
+        step = m.decode_step(cache, toks[:, t])
+        assert np.allclose(step, full[:, t], rtol=0, atol=1e-12)
+    assert np.all(cache["lens"] == 9)
+
+
+def test_tiny_prefill_equals_decode_and_cache_contents():
+    w = make_weights(TINY, seed=0)
+    m = OracleModel(TINY, w)
+    toks = make_tokens(TINY.vocab, 1, 12, seed=1)
+    full, c_pre = m.prefill(toks, max_seq=16)
+    c_dec = m.new_cache(1, 16)
+    for t in range(12):
+        assert np.allclose(m.decode_step(c_dec, toks[:, t]), full[:, t], rtol=0, atol=1e-10)
+    assert np.allclose(c_pre["k"], c_dec["k"], atol=1e-12)
+    assert np.allclose(c_pre["v"], c_dec["v"], atol=1e-12)
+    # cached keys are QK-normalised: norm sqrt(hd) * (ms / (ms + eps))^(1/2), where the
+    # raw keys' mean square ms is about 0.05 here, so the eps shortfall is about 1e-5.
+    kk = c_pre["k"][:, 0, :12, 0]
+    nrm = np.linalg.norm(kk, axis=-1) / math.sqrt(TINY.head_dim)
+    assert np.all(nrm < 1.0) and np.all(nrm > 1.0 - 1e-4)
+
+
+def test_prefix_logits_unchanged_when_appending():
+    w = micro_weights(seed=7)
+    m = OracleModel(MICRO, w)
+    toks = make_tokens(MICRO.vocab, 2, 10, seed=8)
+    short, _ = m.prefill(toks[:, :6])
+    long, _ = m.prefill(toks)
+    assert np.allclose(long[:, :6], short, rtol=0, atol=1e-13)
+
+
+def test_truncation_equals_shorter_prefill():
+    w = micro_weights(seed=9)
+    m = OracleModel(MICRO, w)
+    toks = make_tokens(MICRO.vocab, 2, 10, seed=10)
+    _, cache = m.prefill(toks, max_seq=16)
+    m.truncate(cache, [4, 7])
+    nxt = make_tokens(MICRO.vocab, 2, 1, seed=11)[:, 0]
+    got = m.decode_step(cache, nxt)
+    for b, n in enumerate([4, 7]):
+        seq = np.concatenate([toks[b, :n], nxt[b:b + 1]])[None]
+        ref, _ = m.prefill(seq)
+        assert np.allclose(got[b], ref[0, -1], rtol=0, atol=1e-12)
+
+
+def test_rows_independent_and_permutation():
+    w = micro_weights(seed=12)
+    m = OracleModel(MICRO, w)
+    toks = make_tokens(MICRO.vocab, 4, 7, seed=13)
+    full, _ = m.prefill(toks)
+    for b in range(4):
+        one, _ = m.prefill(toks[b:b + 1])
+        assert np.array_equal(one[0], full[b])
+    perm = [2, 0, 3, 1]
+    pf, _ = m.prefill(toks[perm])
+    assert np.array_equal(pf, full[perm])
+
+
+def test_logits_at_selects_positions():
+    w = micro_weights(seed=14)
+    m = OracleModel(MICRO, w)
+    toks = make_tokens(MICRO.vocab, 2, 8, seed=15)
+    full, _ = m.prefill(toks)
+    part, _ = m.prefill(toks, logits_at=[0, 5, 7])
+    assert np.array_equal(part, full[:, [0, 5, 7]])
+
+
+# ------------------------------------------------------- MQA, scale invariances -----
+def test_mqa_equals_mha_with_replicated_kv():
+    w = micro_weights(seed=16)
+    toks = make_tokens(MICRO.vocab, 2, 7, seed=17)
+    mqa, _ = OracleModel(MICRO, w).prefill(toks)
+    mha_shape = replace(MICRO, n_kv_head=MICRO.n_head)
+    w2 = {"wte": w["wte"], "lm_head": w["lm_head"], "layers": []}
+    for lw in w["layers"]:
+        d = dict(lw)
+        d["wk"] = np.tile(lw["wk"], (MICRO.n_head, 1))
+        d["wv"] = np.tile(lw["wv"], (MICRO.n_head, 1))
+        w2["layers"].append(d)
+    mha, _ = OracleModel(mha_shape, w2).prefill(toks)
+    assert np.allclose(mqa, mha, rtol=0, atol=1e-12)
+
+
+def test_embedding_and_qk_scale_invariance_at_eps0():
+    shape = replace(MICRO, norm_eps=0.0)
+    w = micro_weights(shape, seed=18)
+    toks = make_tokens(shape.vocab, 2, 6, seed=19)
+    base, _ = OracleModel(shape, w).prefill(toks)
+    w_s = dict(w)
+    w_s["wte"] = w["wte"].astype(np.float64) * 7.5
+    scaled, _ = OracleModel(shape, w_s).prefill(toks)
+    assert np.allclose(scaled, base, rtol=0, atol=1e-12)
+    w_q = {"wte": w["wte"], "lm_head": w["lm_head"],
+           "layers": [dict(lw, wq=lw["wq"].astype(np.float64) * 3.0, wk=lw["wk"] * 0.25) for lw in w["layers"]]}
+    qk, _ = OracleModel(shape, w_q).prefill(toks)
+    assert np.allclose(qk, base, rtol=0, atol=1e-12)
+
+
+def test_softcap_binds_under_stress():
+    w = micro_weights(seed=20)
+    w["lm_head"] = w["lm_head"] * 100.0
+    toks = make_tokens(MICRO.vocab, 2, 6, seed=21)
+    logits, _ = OracleModel(MICRO, w).prefill(toks)
+    assert np.all(np.abs(logits) <= MICRO.softcap)
+    assert np.max(np.abs(logits)) > 0.99 * MICRO.softcap
+
+
+# ------------------------------------------------------- greedy ----------------------
+def test_greedy_consistent_with_prefill():
+    w = micro_weights(seed=22)
+    m = OracleModel(MICRO, w)
+    prompt = make_tokens(MICRO.vocab, 2, 4, seed=23)
+    toks, logits = m.greedy(prompt, 5)
+    seq = np.concatenate([prompt, toks], axis=1)
+    full, _ = m.prefill(seq)
+    assert np.array_equal(toks[:, 0], np.argmax(full[:, 3], -1))
+    for s in range(5):
+        assert np.allclose(logits[:, s], full[:, 4 + s], atol=1e-12)
+        if s + 1 < 5:
+            assert np.array_equal(toks[:, s + 1], np.argmax(logits[:, s], -1))
+
+
+# ------------------------------------------------------- sizes from the pages -------
+def test_param_count_matches_pages():
+    g = json.load(open(os.path.join(GOLDEN, "pages_numbers.json")))
+    s = g["d20_shape"]
+    d = s["d_model"]
+    # The pages' d20 count (about 560M) is the multi-head configuration.
+    n = param_count(s["n_layer"], d, s["n_head"], s["n_head"], s["head_dim"], 4 * d,
+                    g["vocab"]["value"])
+    assert n == 560_988_160
+    assert abs(n - s["approx_params"]) / s["approx_params"] < 0.01
+    tokens = n * g["chinchilla_tokens"]["tokens_per_param"]
+    assert abs(tokens - g["chinchilla_tokens"]["approx_tokens"]) / 11.2e9 < 0.01
+    t = g["tokens_per_step"]
+    assert t["rows"] * t["seq_len"] * t["gpus"] == t["value"]
+    assert abs(tokens / t["value"] - g["iterations"]["approx"]) / 21400 < 0.01
+    assert abs(6 * n * tokens - g["total_flops"]["approx"]) / 4e19 < 0.1
+    # the depth knob reproduces the d20 shape
+    sh = from_depth(20)
+    assert (sh.d_model, sh.n_head, sh.head_dim) == (d, s["n_head"], s["head_dim"])
+    # and the model-weight list has exactly param_count entries for MQA too
+    from dense_decoder_only_bf16_amd.inputs import weight_shapes
+    tot = sum(a * b for _, (a, b) in weight_shapes(sh))
+    assert tot == param_count(20, d, 10, 1, 128, 4 * d, 65536) == 502_005_760
