@@ -1,0 +1,92 @@
+// Shared device-side definitions for the gfx950 kernels: vector types, MFMA wrappers,
+// wave reductions, conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// A "chunk" is 8 consecutive elements along the contraction axis held by one lane as an
+// MFMA operand: 16 bytes for bf16, 32 bytes for fp32.
+template <typename T> struct Chunk;
+template <> struct Chunk<bf16> { typedef bf16x8 type; typedef bf16x4 half; };
+template <> struct Chunk<float> { typedef f32x8 type; typedef f32x4 half; };
+
+// 32x32 output tile, 16-deep contraction.  Operand layout (both element types): lane l
+// holds row/column (l % 32) and contraction indices 8*(l/32) .. 8*(l/32)+7.
+// Output layout: lane l, register j holds row 8*(j/4) + 4*(l/32) + (j%4), column l % 32.
+// For fp32 the 16-deep step is eight 2-deep MFMAs; MFMA i contracts element i of every
+// lane, so both element types sum over the same 16 indices.
+__device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma32(f32x8 a, f32x8 b, f32x16 c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], c, 0, 0, 0);
+    return c;
+}
+
+// 16x16 output tile, 32-deep contraction.  Operand layout: lane l holds row/column (l % 16)
+// and contraction indices 8*(l/16) .. 8*(l/16)+7.  Output: lane l, register j holds row
+// 4*(l/16) + j, column l % 16.
+__device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f32x8 a, f32x8 b, f32x4 c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+    return c;
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename V> __device__ __forceinline__ V zero_vec() {
+    V v;
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(V) / sizeof(v[0])); ++i) v[i] = 0;
+    return v;
+}
+
+// Butterfly sum / max over the 64 lanes of a wave (every lane gets the result).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// 2^x on the hardware exponential unit.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// tanh from the identity tanh(y) = sign(y) (1 - e^(-2|y|)) / (1 + e^(-2|y|)), with the
+// exponential taken as 2^(-2|y| log2 e).  Relative error a few ulp away from 0; for
+// |y| < 2^-4 the odd Taylor series y - y^3/3 + 2y^5/15 is used instead, which avoids the
+// cancellation in 1 - e^(-2|y|).
+__device__ __forceinline__ float tanh_f32(float y) {
+    float a = fabsf(y);
+    float r;
+    if (a < 0.0625f) {
+        float y2 = y * y;
+        r = y * (1.0f + y2 * (-1.0f / 3.0f + y2 * (2.0f / 15.0f)));
+    } else {
+        float e = fast_exp2(-2.8853900817779268f * a);  // e^(-2a)
+        r = copysignf((1.0f - e) / (1.0f + e), y);
+    }
+    return r;
+}

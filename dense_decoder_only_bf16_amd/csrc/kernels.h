@@ -1,0 +1,88 @@
+// Host-side launchers of the gfx950 kernels (one definition per .hip file).  Every
+// launcher enqueues on `st` and returns hipGetLastError() of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nc {
+
+enum DType { F32 = 0, BF16 = 1 };
+
+// Epilogues of the matrix product C = A[M,K] B[N,K]^T (fp32 accumulation):
+//   STORE   out_f32[z][m][n] = C            (raw product; z = K-split index)
+//   RELU2   out_t[m][n] = relu(r_m C)^2     (r_m = 1/sqrt(sum_p ss_in[p][m]/K + eps))
+//   RESID   x[m][n] += C; out_t[m][n] = x; ss_out[tile_n][m] = sum over the tile of x^2
+//   SOFTCAP out_f32[m][n] = cap tanh(r_m C / cap)
+enum Epi { EPI_STORE = 0, EPI_RELU2 = 1, EPI_RESID = 2, EPI_SOFTCAP = 3 };
+
+struct GemmArgs {
+    const void* A;  // [M][lda] dtype, K contiguous
+    const void* B;  // [N][ldb] dtype, K contiguous (torch.nn.Linear weight layout)
+    int M, N, K, lda, ldb;
+    int k_split;        // grid z; K / k_split must be a multiple of the K tile
+    float* out_f32;     // STORE / SOFTCAP output, RESID residual x (fp32)
+    void* out_t;        // RELU2 output, RESID dtype copy of x
+    int ldo;            // row stride of the outputs (elements)
+    long long z_stride; // STORE: elements between K-split slices
+    const float* ss_in; // RELU2 / SOFTCAP row statistics: ss_in[p * M_stride + m]
+    int ss_in_parts, ss_stride;
+    float* ss_out;      // RESID: ss_out[tile_n * ss_stride + m]
+    float eps, cap;
+};
+
+// Tile shapes: GEMM_BIG is for M in the thousands (prefill), GEMM_SKINNY for M <= 64.
+enum GemmTile { GEMM_BIG = 0, GEMM_SKINNY = 1 };
+int gemm_tile_n(GemmTile t);   // N extent of one tile (ss_out parts = ceil(N / tile_n))
+int gemm_tile_k(DType dt);     // K granularity
+hipError_t launch_gemm(DType dt, GemmTile tile, Epi epi, const GemmArgs& a, hipStream_t st);
+
+// Row-wise finish of a K-split product: sums `splits` fp32 slices part[z][m][n] (slice
+// stride z_stride) and applies the RELU2 / RESID / SOFTCAP epilogue of one full row per
+// block.  RESID writes ss_out[m] (one part).
+hipError_t launch_finish(DType dt, Epi epi, const float* part, int splits, long long z_stride,
+                         int M, int N, float* out_f32, void* out_t, int ldo,
+                         const float* ss_in, int ss_in_parts, int ss_stride, int norm_dim,
+                         float* ss_out, float eps, float cap, hipStream_t st);
+
+// x[m] = norm(wte[tok[m]]) (fp32), act[m] = dtype copy, ss[m] = sum(x^2).
+hipError_t launch_embed(DType dt, const int32_t* tok, int M, const void* wte, int vocab, int d,
+                        float eps, float* x, void* act, float* ss, hipStream_t st);
+
+// Pre-attention finish of the raw QKV product part[z][m][(H+2)*hd]:
+// scale row m by r_m, rotate q heads and the k head at position pos(m), QK-normalise,
+// write q [m][H][hd] and k, v into the cache of layer `layer`.
+// Position of row m: prefill (lens == nullptr) pos = m % T, row b = m / T;
+// decode (lens != nullptr) b = m, pos = lens[b].
+struct QkvPostArgs {
+    const float* part; int splits; long long z_stride;
+    int M, T, H, hd;
+    const float* ss_in; int ss_in_parts, ss_stride, norm_dim;
+    const int32_t* lens;
+    const float* rope_cos; const float* rope_sin; // [max_seq][hd/2]
+    void* q;          // [M][H][hd]
+    void* kc;         // K cache of this layer: [B][S][hd]
+    void* vtc;        // V cache of this layer, transposed: [B][hd][S]
+    int S;            // cache capacity (positions)
+    float eps;
+};
+hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st);
+
+// Causal multi-query attention over a full prefill: q [B*T][H][hd], K/V of this layer in
+// the cache (positions 0..T-1), y [B*T][H*hd].
+hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, const void* vtc,
+                               void* y, int B, int T, int H, int S, hipStream_t st);
+
+// Decode attention, one query per row at position lens[b] (keys 0..lens[b]):
+// split phase writes per-chunk partial (max, sum, o) and the combine phase merges them.
+int attn_decode_chunk();
+hipError_t launch_attn_decode(DType dt, int hd, const void* q, const void* kc, const void* vtc,
+                              const int32_t* lens, void* y, float* part, int B, int H, int S,
+                              int max_chunks, hipStream_t st);
+
+hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st);
+hipError_t launch_lens_add(int32_t* lens, int B, int32_t delta, int32_t set_value, hipStream_t st);
+hipError_t launch_kv_export(DType dt, int hd, const void* kc, const void* vtc, void* k_out,
+                            void* v_out, int B, int S, int S_out, hipStream_t st);
+
+}  // namespace nc

@@ -1,0 +1,279 @@
+// Row-wise kernels: embedding + norm, the QKV finish (RoPE, QK-norm, KV-cache write),
+// the K-split finish of decode projections, greedy argmax and small cache utilities.
+//
+// RMSNorm has no learnable parameters and sits after the token embedding (yelogs.com
+// launch write-up, architecture answer); RoPE with precomputed tables (geoz.com.cn
+// development-tricks section) and QK-norm (yelogs.com architecture answer; apidog.com/th
+// part 1) finish the query and key projections.  Each of these is one wave per row (or
+// per row and head) with wavefront reductions for the sums of squares.
+#include "common.h"
+#include "kernels.h"
+
+namespace nc {
+
+// ------------------------------------------------------------------ embedding -------
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok, int M,
+                                                    const T* __restrict__ wte, int vocab, int d,
+                                                    float eps, float* __restrict__ x,
+                                                    T* __restrict__ act, float* __restrict__ ss) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    int t = tok[row];
+    t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
+    const T* e = wte + (long long)t * d;
+    float s = 0.f;
+    for (int i = lane; i < d; i += 64) {
+        float v = to_f32(e[i]);
+        s += v * v;
+    }
+    s = wave_sum(s);
+    const float r = 1.0f / sqrtf(s / (float)d + eps);
+    float s2 = 0.f;
+    for (int i = lane; i < d; i += 64) {
+        float v = to_f32(e[i]) * r;
+        x[(long long)row * d + i] = v;
+        act[(long long)row * d + i] = from_f32<T>(v);
+        s2 += v * v;
+    }
+    s2 = wave_sum(s2);
+    if (lane == 0) ss[row] = s2;
+}
+
+hipError_t launch_embed(DType dt, const int32_t* tok, int M, const void* wte, int vocab, int d,
+                        float eps, float* x, void* act, float* ss, hipStream_t st) {
+    dim3 grid((M + 3) / 4);
+    if (dt == BF16)
+        hipLaunchKernelGGL(embed_kernel<bf16>, grid, dim3(256), 0, st, tok, M, (const bf16*)wte,
+                           vocab, d, eps, x, (bf16*)act, ss);
+    else
+        hipLaunchKernelGGL(embed_kernel<float>, grid, dim3(256), 0, st, tok, M, (const float*)wte,
+                           vocab, d, eps, x, (float*)act, ss);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ QKV finish ------
+// One wave per (row, head slot); slots 0..H-1 are query heads, H the key head, H+1 the
+// value head.  Lane i < hd/2 holds the RoPE pair (i, i + hd/2).
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
+    const int lane = threadIdx.x & 63;
+    const long long gw = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int slots = a.H + 2;
+    if (gw >= (long long)a.M * slots) return;
+    const int m = (int)(gw / slots), j = (int)(gw % slots);
+    const int half = a.hd / 2;
+    int b, pos;
+    if (a.lens) {
+        b = m;
+        pos = a.lens[b];
+    } else {
+        b = m / a.T;
+        pos = m % a.T;
+    }
+    if (pos < 0 || pos >= a.S) return;  // capacity is checked by the host; stay in bounds
+    float s = 0.f;
+    for (int q = 0; q < a.ss_in_parts; ++q) s += a.ss_in[(long long)q * a.ss_stride + m];
+    const float r = 1.0f / sqrtf(s / (float)a.norm_dim + a.eps);
+    const int N = slots * a.hd;
+    const bool act = lane < half;
+    float v1 = 0.f, v2 = 0.f;
+    if (act) {
+        const float* src = a.part + (long long)m * N + j * a.hd;
+        for (int z = 0; z < a.splits; ++z) {
+            v1 += src[(long long)z * a.z_stride + lane];
+            v2 += src[(long long)z * a.z_stride + lane + half];
+        }
+        v1 *= r;
+        v2 *= r;
+    }
+    if (j <= a.H) {
+        float c = 0.f, sn = 0.f;
+        if (act) {
+            c = a.rope_cos[(long long)pos * half + lane];
+            sn = a.rope_sin[(long long)pos * half + lane];
+        }
+        float o1 = v1 * c - v2 * sn;
+        float o2 = v1 * sn + v2 * c;
+        float ms = wave_sum(o1 * o1 + o2 * o2) / (float)a.hd;
+        float rr = 1.0f / sqrtf(ms + a.eps);
+        o1 *= rr;
+        o2 *= rr;
+        if (act) {
+            T* dst;
+            if (j < a.H)
+                dst = (T*)a.q + ((long long)m * a.H + j) * a.hd;
+            else
+                dst = (T*)a.kc + ((long long)b * a.S + pos) * a.hd;
+            dst[lane] = from_f32<T>(o1);
+            dst[lane + half] = from_f32<T>(o2);
+        }
+    } else if (act) {
+        T* vt = (T*)a.vtc + (long long)b * a.hd * a.S;
+        vt[(long long)lane * a.S + pos] = from_f32<T>(v1);
+        vt[(long long)(lane + half) * a.S + pos] = from_f32<T>(v2);
+    }
+}
+
+hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st) {
+    long long waves = (long long)a.M * (a.H + 2);
+    dim3 grid((unsigned)((waves + 3) / 4));
+    if (dt == BF16)
+        hipLaunchKernelGGL(qkv_post_kernel<bf16>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(qkv_post_kernel<float>, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ K-split finish --
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void finish_kernel(const float* __restrict__ part, int splits,
+                                                     long long zs, int M, int N,
+                                                     float* __restrict__ out_f32, T* __restrict__ out_t,
+                                                     int ldo, const float* __restrict__ ss_in,
+                                                     int ss_parts, int ss_stride, int norm_dim,
+                                                     float* __restrict__ ss_out, float eps, float cap) {
+    __shared__ float red[4];
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    float r = 1.f;
+    if (EPI != EPI_RESID) {
+        float s = 0.f;
+        for (int q = 0; q < ss_parts; ++q) s += ss_in[(long long)q * ss_stride + m];
+        r = 1.0f / sqrtf(s / (float)norm_dim + eps);
+    }
+    float sq = 0.f;
+    for (int n = tid; n < N; n += 256) {
+        float v = 0.f;
+        for (int z = 0; z < splits; ++z) v += part[(long long)z * zs + (long long)m * N + n];
+        long long o = (long long)m * ldo + n;
+        if (EPI == EPI_RELU2) {
+            float t = fmaxf(v * r, 0.f);
+            out_t[o] = from_f32<T>(t * t);
+        } else if (EPI == EPI_SOFTCAP) {
+            out_f32[o] = cap * tanh_f32(v * r / cap);
+        } else {
+            float xn = out_f32[o] + v;
+            out_f32[o] = xn;
+            out_t[o] = from_f32<T>(xn);
+            sq += xn * xn;
+        }
+    }
+    if (EPI == EPI_RESID) {
+        sq = wave_sum(sq);
+        if ((tid & 63) == 0) red[tid >> 6] = sq;
+        __syncthreads();
+        if (tid == 0) ss_out[m] = red[0] + red[1] + red[2] + red[3];
+    }
+}
+
+template <typename T>
+static hipError_t finish_t(Epi epi, const float* part, int splits, long long zs, int M, int N,
+                           float* out_f32, void* out_t, int ldo, const float* ss_in, int ss_parts,
+                           int ss_stride, int norm_dim, float* ss_out, float eps, float cap,
+                           hipStream_t st) {
+    dim3 grid(M);
+#define NC_FIN(E)                                                                             \
+    hipLaunchKernelGGL((finish_kernel<T, E>), grid, dim3(256), 0, st, part, splits, zs, M, N, \
+                       out_f32, (T*)out_t, ldo, ss_in, ss_parts, ss_stride, norm_dim, ss_out,  \
+                       eps, cap)
+    if (epi == EPI_RELU2) NC_FIN(EPI_RELU2);
+    else if (epi == EPI_SOFTCAP) NC_FIN(EPI_SOFTCAP);
+    else if (epi == EPI_RESID) NC_FIN(EPI_RESID);
+    else return hipErrorInvalidValue;
+#undef NC_FIN
+    return hipGetLastError();
+}
+
+hipError_t launch_finish(DType dt, Epi epi, const float* part, int splits, long long z_stride,
+                         int M, int N, float* out_f32, void* out_t, int ldo, const float* ss_in,
+                         int ss_in_parts, int ss_stride, int norm_dim, float* ss_out, float eps,
+                         float cap, hipStream_t st) {
+    if (dt == BF16)
+        return finish_t<bf16>(epi, part, splits, z_stride, M, N, out_f32, out_t, ldo, ss_in,
+                              ss_in_parts, ss_stride, norm_dim, ss_out, eps, cap, st);
+    return finish_t<float>(epi, part, splits, z_stride, M, N, out_f32, out_t, ldo, ss_in,
+                           ss_in_parts, ss_stride, norm_dim, ss_out, eps, cap, st);
+}
+
+// ------------------------------------------------------------------ argmax ----------
+// Lowest index wins ties; NaN never wins against a number.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+    if (v != v) return false;
+    if (bv != bv) return true;
+    return v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ logits, int V,
+                                                     int32_t* __restrict__ out) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const float* row = logits + (long long)b * V;
+    float bv = __builtin_nanf("");
+    int bi = 0x7fffffff;
+    for (int i = tid; i < V; i += 256) {
+        float v = row[i];
+        if (better(v, i, bv, bi)) { bv = v; bi = i; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float ov = __shfl_xor(bv, o, 64);
+        int oi = __shfl_xor(bi, o, 64);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if ((tid & 63) == 0) { sv[tid >> 6] = bv; si[tid >> 6] = bi; }
+    __syncthreads();
+    if (tid == 0) {
+        for (int w = 1; w < 4; ++w)
+            if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
+        out[b] = (bi == 0x7fffffff) ? 0 : bi;
+    }
+}
+
+hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st) {
+    hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(256), 0, st, logits, V, out);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ cache utilities -
+__global__ void lens_kernel(int32_t* lens, int B, int32_t delta, int32_t set_value) {
+    int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) lens[b] = set_value >= 0 ? set_value : lens[b] + delta;
+}
+
+hipError_t launch_lens_add(int32_t* lens, int B, int32_t delta, int32_t set_value, hipStream_t st) {
+    hipLaunchKernelGGL(lens_kernel, dim3((B + 255) / 256), dim3(256), 0, st, lens, B, delta, set_value);
+    return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void kv_export_kernel(const T* __restrict__ kc, const T* __restrict__ vtc,
+                                                        T* __restrict__ ko, T* __restrict__ vo, int B,
+                                                        int S, int S_out, int hd) {
+    long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    long long total = (long long)B * S_out * hd;
+    if (i >= total) return;
+    int d = (int)(i % hd);
+    long long bs = i / hd;
+    int s = (int)(bs % S_out);
+    int b = (int)(bs / S_out);
+    ko[i] = kc[((long long)b * S + s) * hd + d];
+    vo[i] = vtc[((long long)b * hd + d) * S + s];
+}
+
+hipError_t launch_kv_export(DType dt, int hd, const void* kc, const void* vtc, void* k_out,
+                            void* v_out, int B, int S, int S_out, hipStream_t st) {
+    long long total = (long long)B * S_out * hd;
+    dim3 grid((unsigned)((total + 255) / 256));
+    if (dt == BF16)
+        hipLaunchKernelGGL(kv_export_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)kc,
+                           (const bf16*)vtc, (bf16*)k_out, (bf16*)v_out, B, S, S_out, hd);
+    else
+        hipLaunchKernelGGL(kv_export_kernel<float>, grid, dim3(256), 0, st, (const float*)kc,
+                           (const float*)vtc, (float*)k_out, (float*)v_out, B, S, S_out, hd);
+    return hipGetLastError();
+}
+
+}  // namespace nc

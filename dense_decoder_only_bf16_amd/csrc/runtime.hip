@@ -1,0 +1,531 @@
+// Host runtime behind the C ABI in include/nc.h: model and KV-cache objects, argument
+// checks, workspace management and the per-layer launch schedule of prefill and decode.
+//
+// Schedule of one layer (the block structure of the yelogs.com launch write-up's
+// architecture answer; plain pre-norm residual reading):
+//   QKV product (raw, fp32)  -> qkv_post: row norm scale, RoPE, QK-norm, KV-cache write
+//   attention (prefill: flash kernel; decode: split-context + combine)
+//   O product  + residual epilogue (x += ., dtype copy of x, per-row sum of squares)
+//   FC product + norm scale + ReLU^2 epilogue
+//   PROJ product + residual epilogue
+// then the LM head with norm scale and softcap.  Prefill uses the large MFMA tile with the
+// epilogues fused; decode (M = batch rows) uses the skinny tile with K split across
+// workgroups and a row-wise finish kernel that applies the same epilogues.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/nc.h"
+#include "kernels.h"
+
+using namespace nc;
+
+namespace {
+
+thread_local std::string g_err;
+
+nc_status fail(nc_status code, const std::string& msg) {
+    g_err = msg;
+    return code;
+}
+
+#define HIP_TRY(expr)                                                                        \
+    do {                                                                                     \
+        hipError_t e_ = (expr);                                                              \
+        if (e_ != hipSuccess)                                                                \
+            return fail(e_ == hipErrorOutOfMemory ? NC_ERR_OOM : NC_ERR_DEVICE,              \
+                        std::string(#expr) + ": " + hipGetErrorString(e_));                  \
+    } while (0)
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+struct nc_model {
+    nc_config cfg;
+    DType dt;
+    size_t esz;
+    int device;
+    void* arena = nullptr;
+    const void* wte = nullptr;
+    const void* lm = nullptr;
+    struct Layer {
+        const void *wqkv, *wo, *wfc, *wproj;
+    };
+    std::vector<Layer> layers;
+    float* rope_cos = nullptr;
+    float* rope_sin = nullptr;
+    int live_kv = 0;
+};
+
+struct nc_kv {
+    nc_model* m;
+    int B, max_seq, S;  // S: allocated positions per row (stride), multiple of 64
+    void* kcache = nullptr;  // [L][B][S][hd]
+    void* vcache = nullptr;  // [L][B][hd][S]
+    int32_t* lens_dev = nullptr;
+    std::vector<int32_t> lens_host;
+    // workspace, sized for `cap_m` token rows
+    long long cap_m = 0;
+    int ss_parts_max = 0;
+    float* x = nullptr;       // [M][d] fp32 residual
+    void* act = nullptr;      // [M][d] dtype copy of x
+    float* ss_a = nullptr;    // [parts][M] sums of squares feeding the QKV / LM-head norm
+    float* ss_b = nullptr;    // [parts][M] sums of squares feeding the MLP norm
+    float* qkv = nullptr;     // [splits][M][(H+2) hd] raw products
+    void* q = nullptr;        // [M][H][hd]
+    void* y = nullptr;        // [M][H hd] attention output
+    void* u = nullptr;        // [M][d_ff] MLP hidden
+    float* gpart = nullptr;   // [splits][M][N] K-split partial products (decode)
+    long long gpart_elems = 0;
+    float* apart = nullptr;   // decode attention partials
+    long long apart_elems = 0;
+};
+
+namespace {
+
+void ws_free(nc_kv* kv) {
+    void* ptrs[] = {kv->x, kv->act, kv->ss_a, kv->ss_b, kv->qkv, kv->q, kv->y, kv->u, kv->gpart, kv->apart};
+    for (void* p : ptrs)
+        if (p) (void)hipFree(p);
+    kv->x = nullptr; kv->act = nullptr; kv->ss_a = nullptr; kv->ss_b = nullptr; kv->qkv = nullptr;
+    kv->q = nullptr; kv->y = nullptr; kv->u = nullptr; kv->gpart = nullptr; kv->apart = nullptr;
+    kv->cap_m = 0;
+    kv->gpart_elems = 0;
+    kv->apart_elems = 0;
+}
+
+constexpr int kMaxSplit = 16;
+
+// Grow the workspace to hold M token rows (and decode partials when `decode`).
+nc_status ws_ensure(nc_kv* kv, long long M) {
+    if (M <= kv->cap_m) return NC_OK;
+    const nc_config& c = kv->m->cfg;
+    const size_t es = kv->m->esz;
+    HIP_TRY(hipDeviceSynchronize());
+    ws_free(kv);
+    const long long d = c.d_model, hq = (long long)c.n_head * c.head_dim;
+    const long long nqkv = (long long)(c.n_head + 2) * c.head_dim;
+    const long long split_rows = std::min<long long>(M, 128);  // K-split only for small M
+    kv->ss_parts_max = (c.d_model + 127) / 128;
+    const long long qkv_elems = std::max(M * nqkv, kMaxSplit * split_rows * nqkv);
+#define WS_ALLOC(ptr, bytes) HIP_TRY(hipMalloc((void**)&(ptr), (size_t)(bytes)))
+    WS_ALLOC(kv->x, M * d * 4);
+    WS_ALLOC(kv->act, M * d * es);
+    WS_ALLOC(kv->ss_a, (long long)kv->ss_parts_max * M * 4);
+    WS_ALLOC(kv->ss_b, (long long)kv->ss_parts_max * M * 4);
+    WS_ALLOC(kv->qkv, qkv_elems * 4);
+    WS_ALLOC(kv->q, M * hq * es);
+    WS_ALLOC(kv->y, M * hq * es);
+    WS_ALLOC(kv->u, M * c.d_ff * es);
+    kv->gpart_elems = kMaxSplit * split_rows * std::max<long long>(d, c.d_ff);
+    WS_ALLOC(kv->gpart, kv->gpart_elems * 4);
+    const int max_chunks = (kv->S + attn_decode_chunk() - 1) / attn_decode_chunk();
+    kv->apart_elems = (long long)kv->B * max_chunks * 16 * (c.head_dim + 2);
+    WS_ALLOC(kv->apart, kv->apart_elems * 4);
+#undef WS_ALLOC
+    kv->cap_m = M;
+    return NC_OK;
+}
+
+nc_status check_cfg(const nc_config* c) {
+    if (!c) return fail(NC_ERR_INVALID_ARG, "cfg is NULL");
+    if (c->n_layer < 1 || c->d_model < 1 || c->n_head < 1 || c->head_dim < 1 || c->d_ff < 1 ||
+        c->vocab < 1 || c->max_seq < 1)
+        return fail(NC_ERR_INVALID_ARG, "all sizes must be positive");
+    if (c->dtype != NC_F32 && c->dtype != NC_BF16) return fail(NC_ERR_INVALID_ARG, "dtype must be NC_F32 or NC_BF16");
+    if (c->n_kv_head != 1) return fail(NC_ERR_UNSUPPORTED, "only n_kv_head == 1 (multi-query attention) is supported");
+    if (c->head_dim != 64 && c->head_dim != 128) return fail(NC_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if ((long long)c->n_head * c->head_dim != c->d_model) return fail(NC_ERR_INVALID_ARG, "d_model must equal n_head * head_dim");
+    if (c->n_head > 16) return fail(NC_ERR_UNSUPPORTED, "n_head > 16 is not supported by the decode attention kernel");
+    if (c->d_model % 64 || c->d_ff % 64) return fail(NC_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
+    if (!(c->softcap > 0.f) || !(c->norm_eps >= 0.f) || !(c->rope_base > 0.f))
+        return fail(NC_ERR_INVALID_ARG, "softcap and rope_base must be > 0, norm_eps >= 0");
+    if (c->max_seq > (1 << 24)) return fail(NC_ERR_INVALID_ARG, "max_seq too large");
+    return NC_OK;
+}
+
+nc_status check_device(int* dev_out) {
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n < 1) return fail(NC_ERR_DEVICE, "no HIP device available");
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, dev));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(NC_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", gfx950 required");
+    *dev_out = dev;
+    return NC_OK;
+}
+
+nc_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(NC_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+    return NC_OK;
+}
+#define LAUNCH(expr)                                \
+    do {                                            \
+        nc_status s_ = launched((expr), #expr);     \
+        if (s_ != NC_OK) return s_;                 \
+    } while (0)
+
+// Largest K split <= want that divides K into multiples of the K tile.
+int pick_split(int K, int kt, int want) {
+    int tiles = K / kt;
+    int s = std::max(1, std::min(want, tiles));
+    while (s > 1 && tiles % s) --s;
+    return s;
+}
+
+// One decode projection: skinny tile, K split sized to fill the GPU, then the epilogue.
+nc_status decode_gemm(nc_kv* kv, Epi epi, const void* A, int lda, const void* W, int N, int K,
+                      float* out_f32, void* out_t, int ldo, const float* ss_in, int ss_parts,
+                      float* ss_out, hipStream_t st, float* qkv_out = nullptr, int* split_out = nullptr) {
+    nc_model* m = kv->m;
+    const int M = kv->B;
+    const int tn = gemm_tile_n(GEMM_SKINNY);
+    const int base = ((N + tn - 1) / tn) * ((M + 31) / 32);
+    const int want = std::max(1, std::min(kMaxSplit, 512 / std::max(1, base)));
+    const int split = pick_split(K, gemm_tile_k(m->dt), want);
+    GemmArgs a{};
+    a.A = A; a.B = W; a.M = M; a.N = N; a.K = K; a.lda = lda; a.ldb = K;
+    a.k_split = split; a.ldo = N; a.eps = m->cfg.norm_eps; a.cap = m->cfg.softcap;
+    if (epi == EPI_STORE) {  // QKV: raw partials consumed by qkv_post
+        a.out_f32 = qkv_out;
+        a.z_stride = (long long)M * N;
+        LAUNCH(launch_gemm(m->dt, GEMM_SKINNY, EPI_STORE, a, st));
+        *split_out = split;
+        return NC_OK;
+    }
+    if (split == 1 && epi == EPI_SOFTCAP) {
+        a.out_f32 = out_f32; a.ldo = ldo; a.ss_in = ss_in; a.ss_in_parts = ss_parts; a.ss_stride = (int)kv->cap_m;
+        LAUNCH(launch_gemm(m->dt, GEMM_SKINNY, EPI_SOFTCAP, a, st));
+        return NC_OK;
+    }
+    a.out_f32 = kv->gpart;
+    a.z_stride = (long long)M * N;
+    if ((long long)split * M * N > kv->gpart_elems) return fail(NC_ERR_STATE, "decode partial buffer too small");
+    LAUNCH(launch_gemm(m->dt, GEMM_SKINNY, EPI_STORE, a, st));
+    LAUNCH(launch_finish(m->dt, epi, kv->gpart, split, (long long)M * N, M, N, out_f32, out_t, ldo,
+                         ss_in, ss_parts, (int)kv->cap_m, K, ss_out, m->cfg.norm_eps, m->cfg.softcap, st));
+    return NC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nc_abi_version(void) { return NC_ABI_VERSION; }
+
+const char* nc_last_error(void) { return g_err.c_str(); }
+
+nc_status nc_model_create(const nc_config* cfg, const void* const* weights, nc_model** out) {
+    try {
+        if (!out) return fail(NC_ERR_INVALID_ARG, "out is NULL");
+        *out = nullptr;
+        nc_status s = check_cfg(cfg);
+        if (s != NC_OK) return s;
+        if (!weights) return fail(NC_ERR_INVALID_ARG, "weights is NULL");
+        const int nw = 6 * cfg->n_layer + 2;
+        for (int i = 0; i < nw; ++i)
+            if (!weights[i]) return fail(NC_ERR_INVALID_ARG, "weight pointer " + std::to_string(i) + " is NULL");
+        int dev = 0;
+        s = check_device(&dev);
+        if (s != NC_OK) return s;
+
+        nc_model* m = new nc_model();
+        m->cfg = *cfg;
+        m->dt = cfg->dtype == NC_BF16 ? BF16 : F32;
+        m->esz = cfg->dtype == NC_BF16 ? 2 : 4;
+        m->device = dev;
+        const size_t d = cfg->d_model, hd = cfg->head_dim, H = cfg->n_head, V = cfg->vocab, F = cfg->d_ff;
+        const size_t es = m->esz;
+        const size_t sz_emb = align_up(V * d * es, 256);
+        const size_t sz_qkv = align_up((H + 2) * hd * d * es, 256);
+        const size_t sz_o = align_up(d * H * hd * es, 256);
+        const size_t sz_fc = align_up(F * d * es, 256);
+        const size_t total = 2 * sz_emb + cfg->n_layer * (sz_qkv + sz_o + 2 * sz_fc);
+        hipError_t e = hipMalloc(&m->arena, total);
+        if (e != hipSuccess) {
+            delete m;
+            return fail(NC_ERR_OOM, std::string("weight arena: ") + hipGetErrorString(e));
+        }
+        char* p = (char*)m->arena;
+        auto cp = [&](void* dst, const void* src, size_t bytes) {
+            return hipMemcpy(dst, src, bytes, hipMemcpyDefault);
+        };
+        hipError_t ce = cp(p, weights[0], V * d * es);
+        m->wte = p;
+        p += sz_emb;
+        m->layers.resize(cfg->n_layer);
+        for (int l = 0; l < cfg->n_layer && ce == hipSuccess; ++l) {
+            const void* const* w = weights + 1 + 6 * l;
+            nc_model::Layer& L = m->layers[l];
+            L.wqkv = p;
+            ce = cp(p, w[0], H * hd * d * es);
+            if (ce == hipSuccess) ce = cp(p + H * hd * d * es, w[1], hd * d * es);
+            if (ce == hipSuccess) ce = cp(p + (H + 1) * hd * d * es, w[2], hd * d * es);
+            p += sz_qkv;
+            L.wo = p;
+            if (ce == hipSuccess) ce = cp(p, w[3], d * H * hd * es);
+            p += sz_o;
+            L.wfc = p;
+            if (ce == hipSuccess) ce = cp(p, w[4], F * d * es);
+            p += sz_fc;
+            L.wproj = p;
+            if (ce == hipSuccess) ce = cp(p, w[5], d * F * es);
+            p += sz_fc;
+        }
+        if (ce == hipSuccess) ce = cp(p, weights[nw - 1], V * d * es);
+        m->lm = p;
+        // RoPE tables: angle p * base^(-2i/hd), evaluated in double, stored fp32.
+        const size_t half = hd / 2, S = cfg->max_seq;
+        std::vector<float> hc(S * half), hs(S * half);
+        for (size_t i = 0; i < half; ++i) {
+            const double inv = std::pow((double)cfg->rope_base, -2.0 * (double)i / (double)hd);
+            for (size_t t = 0; t < S; ++t) {
+                const double a = (double)t * inv;
+                hc[t * half + i] = (float)std::cos(a);
+                hs[t * half + i] = (float)std::sin(a);
+            }
+        }
+        if (ce == hipSuccess) ce = hipMalloc((void**)&m->rope_cos, S * half * 4);
+        if (ce == hipSuccess) ce = hipMalloc((void**)&m->rope_sin, S * half * 4);
+        if (ce == hipSuccess) ce = hipMemcpy(m->rope_cos, hc.data(), S * half * 4, hipMemcpyHostToDevice);
+        if (ce == hipSuccess) ce = hipMemcpy(m->rope_sin, hs.data(), S * half * 4, hipMemcpyHostToDevice);
+        if (ce != hipSuccess) {
+            nc_model_free(m);
+            return fail(ce == hipErrorOutOfMemory ? NC_ERR_OOM : NC_ERR_DEVICE,
+                        std::string("model upload: ") + hipGetErrorString(ce));
+        }
+        *out = m;
+        return NC_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(NC_ERR_OOM, "host allocation failed");
+    } catch (...) {
+        return fail(NC_ERR_DEVICE, "unexpected exception");
+    }
+}
+
+void nc_model_free(nc_model* m) {
+    if (!m) return;
+    (void)hipDeviceSynchronize();
+    if (m->arena) (void)hipFree(m->arena);
+    if (m->rope_cos) (void)hipFree(m->rope_cos);
+    if (m->rope_sin) (void)hipFree(m->rope_sin);
+    delete m;
+}
+
+nc_status nc_kv_create(nc_model* m, int32_t batch, int32_t max_seq, nc_kv** out) {
+    try {
+        if (!out) return fail(NC_ERR_INVALID_ARG, "out is NULL");
+        *out = nullptr;
+        if (!m) return fail(NC_ERR_INVALID_ARG, "model is NULL");
+        if (batch < 1 || max_seq < 1) return fail(NC_ERR_INVALID_ARG, "batch and max_seq must be >= 1");
+        if (max_seq > m->cfg.max_seq) return fail(NC_ERR_INVALID_ARG, "max_seq exceeds the model's max_seq");
+        nc_kv* kv = new nc_kv();
+        kv->m = m;
+        kv->B = batch;
+        kv->max_seq = max_seq;
+        kv->S = (int)align_up(max_seq, 64);
+        kv->lens_host.assign(batch, 0);
+        const nc_config& c = m->cfg;
+        const size_t bytes = (size_t)c.n_layer * batch * kv->S * c.head_dim * m->esz;
+        hipError_t e = hipMalloc(&kv->kcache, bytes);
+        if (e == hipSuccess) e = hipMalloc(&kv->vcache, bytes);
+        if (e == hipSuccess) e = hipMalloc((void**)&kv->lens_dev, batch * sizeof(int32_t));
+        if (e == hipSuccess) e = hipMemset(kv->kcache, 0, bytes);
+        if (e == hipSuccess) e = hipMemset(kv->vcache, 0, bytes);
+        if (e == hipSuccess) e = hipMemset(kv->lens_dev, 0, batch * sizeof(int32_t));
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) {
+            if (kv->kcache) (void)hipFree(kv->kcache);
+            if (kv->vcache) (void)hipFree(kv->vcache);
+            if (kv->lens_dev) (void)hipFree(kv->lens_dev);
+            delete kv;
+            return fail(e == hipErrorOutOfMemory ? NC_ERR_OOM : NC_ERR_DEVICE,
+                        std::string("kv allocation: ") + hipGetErrorString(e));
+        }
+        m->live_kv++;
+        *out = kv;
+        return NC_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(NC_ERR_OOM, "host allocation failed");
+    } catch (...) {
+        return fail(NC_ERR_DEVICE, "unexpected exception");
+    }
+}
+
+void nc_kv_free(nc_kv* kv) {
+    if (!kv) return;
+    (void)hipDeviceSynchronize();
+    ws_free(kv);
+    if (kv->kcache) (void)hipFree(kv->kcache);
+    if (kv->vcache) (void)hipFree(kv->vcache);
+    if (kv->lens_dev) (void)hipFree(kv->lens_dev);
+    kv->m->live_kv--;
+    delete kv;
+}
+
+nc_status nc_kv_set_lens(nc_kv* kv, const int32_t* lens) {
+    if (!kv || !lens) return fail(NC_ERR_INVALID_ARG, "NULL argument");
+    for (int b = 0; b < kv->B; ++b)
+        if (lens[b] < 0 || lens[b] > kv->lens_host[b])
+            return fail(NC_ERR_INVALID_ARG, "lens may only shrink (0 <= new <= current)");
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipMemcpy(kv->lens_dev, lens, kv->B * sizeof(int32_t), hipMemcpyHostToDevice));
+    std::copy(lens, lens + kv->B, kv->lens_host.begin());
+    return NC_OK;
+}
+
+nc_status nc_kv_get_lens(const nc_kv* kv, int32_t* lens) {
+    if (!kv || !lens) return fail(NC_ERR_INVALID_ARG, "NULL argument");
+    std::copy(kv->lens_host.begin(), kv->lens_host.end(), lens);
+    return NC_OK;
+}
+
+nc_status nc_kv_export(nc_kv* kv, int32_t layer, void* k_out, void* v_out, void* stream) {
+    if (!kv || !k_out || !v_out) return fail(NC_ERR_INVALID_ARG, "NULL argument");
+    const nc_config& c = kv->m->cfg;
+    if (layer < 0 || layer >= c.n_layer) return fail(NC_ERR_INVALID_ARG, "layer out of range");
+    const size_t per_layer = (size_t)kv->B * kv->S * c.head_dim * kv->m->esz;
+    const char* kc = (const char*)kv->kcache + layer * per_layer;
+    const char* vc = (const char*)kv->vcache + layer * per_layer;
+    LAUNCH(launch_kv_export(kv->m->dt, c.head_dim, kc, vc, k_out, v_out, kv->B, kv->S, kv->max_seq,
+                            (hipStream_t)stream));
+    return NC_OK;
+}
+
+nc_status nc_argmax(const float* logits, int32_t B, int32_t V, int32_t* out, void* stream) {
+    if (!logits || !out) return fail(NC_ERR_INVALID_ARG, "NULL argument");
+    if (B < 1 || V < 1) return fail(NC_ERR_INVALID_ARG, "B and V must be >= 1");
+    LAUNCH(launch_argmax(logits, B, V, out, (hipStream_t)stream));
+    return NC_OK;
+}
+
+nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, nc_kv* kv,
+                     float* logits, void* stream) {
+    try {
+        if (!m || !tokens || !kv) return fail(NC_ERR_INVALID_ARG, "NULL argument");
+        if (kv->m != m) return fail(NC_ERR_INVALID_ARG, "kv belongs to another model");
+        if (B != kv->B) return fail(NC_ERR_INVALID_ARG, "B differs from the cache's batch");
+        if (T < 1 || T > kv->max_seq) return fail(NC_ERR_CAPACITY, "T must be in [1, kv max_seq]");
+        for (int b = 0; b < B; ++b)
+            if (kv->lens_host[b] != 0) return fail(NC_ERR_STATE, "prefill needs an empty cache (all lengths 0)");
+        const long long M = (long long)B * T;
+        nc_status s = ws_ensure(kv, M);
+        if (s != NC_OK) return s;
+        hipStream_t st = (hipStream_t)stream;
+        const nc_config& c = m->cfg;
+        const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab;
+        const int nqkv = (H + 2) * hd;
+        const int tn = gemm_tile_n(GEMM_BIG);
+        const int parts_d = (d + tn - 1) / tn;
+        const size_t per_layer = (size_t)B * kv->S * hd * m->esz;
+        const int Mi = (int)M;
+
+        LAUNCH(launch_embed(m->dt, tokens, Mi, m->wte, V, d, c.norm_eps, kv->x, kv->act, kv->ss_a, st));
+        int ss_a_parts = 1;
+        for (int l = 0; l < c.n_layer; ++l) {
+            const nc_model::Layer& L = m->layers[l];
+            GemmArgs g{};
+            g.M = Mi; g.lda = d; g.k_split = 1; g.eps = c.norm_eps; g.cap = c.softcap;
+            // QKV raw product
+            g.A = kv->act; g.B = L.wqkv; g.N = nqkv; g.K = d; g.ldb = d;
+            g.out_f32 = kv->qkv; g.ldo = nqkv; g.z_stride = 0;
+            LAUNCH(launch_gemm(m->dt, GEMM_BIG, EPI_STORE, g, st));
+            QkvPostArgs qa{};
+            qa.part = kv->qkv; qa.splits = 1; qa.z_stride = 0; qa.M = Mi; qa.T = T; qa.H = H; qa.hd = hd;
+            qa.ss_in = kv->ss_a; qa.ss_in_parts = ss_a_parts; qa.ss_stride = (int)kv->cap_m; qa.norm_dim = d;
+            qa.lens = nullptr; qa.rope_cos = m->rope_cos; qa.rope_sin = m->rope_sin;
+            qa.q = kv->q; qa.kc = (char*)kv->kcache + l * per_layer; qa.vtc = (char*)kv->vcache + l * per_layer;
+            qa.S = kv->S; qa.eps = c.norm_eps;
+            LAUNCH(launch_qkv_post(m->dt, qa, st));
+            LAUNCH(launch_attn_prefill(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->y, B, T, H, kv->S, st));
+            // O product + residual
+            g.A = kv->y; g.lda = H * hd; g.B = L.wo; g.N = d; g.K = H * hd; g.ldb = H * hd;
+            g.out_f32 = kv->x; g.out_t = kv->act; g.ldo = d; g.ss_out = kv->ss_b; g.ss_stride = (int)kv->cap_m;
+            LAUNCH(launch_gemm(m->dt, GEMM_BIG, EPI_RESID, g, st));
+            // FC + norm + relu^2
+            g.A = kv->act; g.lda = d; g.B = L.wfc; g.N = F; g.K = d; g.ldb = d;
+            g.out_t = kv->u; g.ldo = F; g.ss_in = kv->ss_b; g.ss_in_parts = parts_d; g.ss_stride = (int)kv->cap_m;
+            LAUNCH(launch_gemm(m->dt, GEMM_BIG, EPI_RELU2, g, st));
+            // PROJ + residual
+            g.A = kv->u; g.lda = F; g.B = L.wproj; g.N = d; g.K = F; g.ldb = F;
+            g.out_f32 = kv->x; g.out_t = kv->act; g.ldo = d; g.ss_out = kv->ss_a; g.ss_stride = (int)kv->cap_m;
+            LAUNCH(launch_gemm(m->dt, GEMM_BIG, EPI_RESID, g, st));
+            ss_a_parts = parts_d;
+        }
+        if (logits) {
+            GemmArgs g{};
+            g.A = kv->act; g.lda = d; g.B = m->lm; g.M = Mi; g.N = V; g.K = d; g.ldb = d; g.k_split = 1;
+            g.out_f32 = logits; g.ldo = V; g.ss_in = kv->ss_a; g.ss_in_parts = ss_a_parts;
+            g.ss_stride = (int)kv->cap_m; g.eps = c.norm_eps; g.cap = c.softcap;
+            LAUNCH(launch_gemm(m->dt, GEMM_BIG, EPI_SOFTCAP, g, st));
+        }
+        LAUNCH(launch_lens_add(kv->lens_dev, B, 0, T, st));
+        std::fill(kv->lens_host.begin(), kv->lens_host.end(), T);
+        return NC_OK;
+    } catch (...) {
+        return fail(NC_ERR_DEVICE, "unexpected exception");
+    }
+}
+
+nc_status nc_decode_step(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* kv, float* logits,
+                         void* stream) {
+    try {
+        if (!m || !tokens || !kv || !logits) return fail(NC_ERR_INVALID_ARG, "NULL argument");
+        if (kv->m != m) return fail(NC_ERR_INVALID_ARG, "kv belongs to another model");
+        if (B != kv->B) return fail(NC_ERR_INVALID_ARG, "B differs from the cache's batch");
+        for (int b = 0; b < B; ++b)
+            if (kv->lens_host[b] + 1 > kv->max_seq) return fail(NC_ERR_CAPACITY, "a row is full (lens + 1 > max_seq)");
+        nc_status s = ws_ensure(kv, B);
+        if (s != NC_OK) return s;
+        hipStream_t st = (hipStream_t)stream;
+        const nc_config& c = m->cfg;
+        const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab;
+        const int nqkv = (H + 2) * hd;
+        const size_t per_layer = (size_t)B * kv->S * hd * m->esz;
+        const int max_chunks = (kv->S + attn_decode_chunk() - 1) / attn_decode_chunk();
+
+        LAUNCH(launch_embed(m->dt, tokens, B, m->wte, V, d, c.norm_eps, kv->x, kv->act, kv->ss_a, st));
+        for (int l = 0; l < c.n_layer; ++l) {
+            const nc_model::Layer& L = m->layers[l];
+            int split = 1;
+            s = decode_gemm(kv, EPI_STORE, kv->act, d, L.wqkv, nqkv, d, nullptr, nullptr, 0, nullptr, 0,
+                            nullptr, st, kv->qkv, &split);
+            if (s != NC_OK) return s;
+            QkvPostArgs qa{};
+            qa.part = kv->qkv; qa.splits = split; qa.z_stride = (long long)B * nqkv; qa.M = B; qa.T = 1;
+            qa.H = H; qa.hd = hd; qa.ss_in = kv->ss_a; qa.ss_in_parts = 1; qa.ss_stride = (int)kv->cap_m;
+            qa.norm_dim = d; qa.lens = kv->lens_dev; qa.rope_cos = m->rope_cos; qa.rope_sin = m->rope_sin;
+            qa.q = kv->q; qa.kc = (char*)kv->kcache + l * per_layer; qa.vtc = (char*)kv->vcache + l * per_layer;
+            qa.S = kv->S; qa.eps = c.norm_eps;
+            LAUNCH(launch_qkv_post(m->dt, qa, st));
+            LAUNCH(launch_attn_decode(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->lens_dev, kv->y, kv->apart, B, H,
+                                      kv->S, max_chunks, st));
+            s = decode_gemm(kv, EPI_RESID, kv->y, H * hd, L.wo, d, H * hd, kv->x, kv->act, d, nullptr, 0,
+                            kv->ss_b, st);
+            if (s != NC_OK) return s;
+            s = decode_gemm(kv, EPI_RELU2, kv->act, d, L.wfc, F, d, nullptr, kv->u, F, kv->ss_b, 1, nullptr, st);
+            if (s != NC_OK) return s;
+            s = decode_gemm(kv, EPI_RESID, kv->u, F, L.wproj, d, F, kv->x, kv->act, d, nullptr, 0, kv->ss_a, st);
+            if (s != NC_OK) return s;
+        }
+        s = decode_gemm(kv, EPI_SOFTCAP, kv->act, d, m->lm, V, d, logits, nullptr, V, kv->ss_a, 1, nullptr, st);
+        if (s != NC_OK) return s;
+        LAUNCH(launch_lens_add(kv->lens_dev, B, 1, -1, st));
+        for (int b = 0; b < B; ++b) kv->lens_host[b] += 1;
+        return NC_OK;
+    } catch (...) {
+        return fail(NC_ERR_DEVICE, "unexpected exception");
+    }
+}
+
+}  // extern "C"

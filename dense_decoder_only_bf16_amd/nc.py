@@ -1,0 +1,228 @@
+"""ctypes binding of libnc.so: the same entry points as include/nc.h, marshalling only.
+
+Every step of the forward pass runs in the library's HIP kernels; this module converts
+Python arguments (torch device tensors, ints, shapes) to the C types and raises NcError on a
+non-zero status.  There is no fallback: if libnc.so is missing or fails to load, every
+call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnc.so")
+
+NC_OK = 0
+NC_ERR_INVALID_ARG = -1
+NC_ERR_UNSUPPORTED = -2
+NC_ERR_OOM = -3
+NC_ERR_CAPACITY = -4
+NC_ERR_STATE = -5
+NC_ERR_DEVICE = -6
+NC_F32 = 0
+NC_BF16 = 1
+
+_CODE_NAMES = {NC_ERR_INVALID_ARG: "NC_ERR_INVALID_ARG", NC_ERR_UNSUPPORTED: "NC_ERR_UNSUPPORTED",
+               NC_ERR_OOM: "NC_ERR_OOM", NC_ERR_CAPACITY: "NC_ERR_CAPACITY",
+               NC_ERR_STATE: "NC_ERR_STATE", NC_ERR_DEVICE: "NC_ERR_DEVICE"}
+
+EXPORTED = ("nc_model_create", "nc_model_free", "nc_kv_create", "nc_kv_free", "nc_kv_set_lens",
+            "nc_kv_get_lens", "nc_kv_export", "nc_prefill", "nc_decode_step", "nc_argmax",
+            "nc_last_error", "nc_abi_version")
+
+
+class NcError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{_CODE_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class nc_config(ctypes.Structure):
+    _fields_ = [("n_layer", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_head", ctypes.c_int32), ("n_kv_head", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("softcap", ctypes.c_float),
+                ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run "
+                              "`python -m dense_decoder_only_bf16_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32
+        L.nc_model_create.argtypes = [ctypes.POINTER(nc_config), ctypes.POINTER(vp), ctypes.POINTER(vp)]
+        L.nc_model_free.argtypes = [vp]
+        L.nc_model_free.restype = None
+        L.nc_kv_create.argtypes = [vp, i32, i32, ctypes.POINTER(vp)]
+        L.nc_kv_free.argtypes = [vp]
+        L.nc_kv_free.restype = None
+        L.nc_kv_set_lens.argtypes = [vp, ctypes.POINTER(i32)]
+        L.nc_kv_get_lens.argtypes = [vp, ctypes.POINTER(i32)]
+        L.nc_kv_export.argtypes = [vp, i32, vp, vp, vp]
+        L.nc_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+        L.nc_decode_step.argtypes = [vp, vp, i32, vp, vp, vp]
+        L.nc_argmax.argtypes = [vp, i32, i32, vp, vp]
+        L.nc_last_error.argtypes = []
+        L.nc_last_error.restype = ctypes.c_char_p
+        L.nc_abi_version.argtypes = []
+        L.nc_abi_version.restype = i32
+        for name in ("nc_model_create", "nc_kv_create", "nc_kv_set_lens", "nc_kv_get_lens",
+                     "nc_kv_export", "nc_prefill", "nc_decode_step", "nc_argmax"):
+            getattr(L, name).restype = st
+        _lib = L
+    return _lib
+
+
+def _check(code):
+    if code != NC_OK:
+        raise NcError(code, lib().nc_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    """Device address of a torch tensor (or None / int passthrough)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_config(shape, max_seq=None):
+    """nc_config from an object with the model-shape attributes (see inputs.Shape)."""
+    return nc_config(shape.n_layer, shape.d_model, shape.n_head, shape.n_kv_head, shape.head_dim,
+                     shape.d_ff, shape.vocab, max_seq or shape.max_seq, shape.rope_base,
+                     shape.softcap, shape.norm_eps,
+                     NC_BF16 if shape.dtype == "bf16" else NC_F32)
+
+
+# ------------------------------------------------------------------ entry points ------
+def nc_abi_version():
+    return lib().nc_abi_version()
+
+
+def nc_last_error():
+    return lib().nc_last_error().decode(errors="replace")
+
+
+def nc_model_create(cfg, weights):
+    """cfg: nc_config; weights: 6L+2 device tensors (or raw addresses) in canonical order."""
+    arr = (ctypes.c_void_p * len(weights))(*[_ptr(w) for w in weights])
+    out = ctypes.c_void_p()
+    _check(lib().nc_model_create(ctypes.byref(cfg), arr, ctypes.byref(out)))
+    return out
+
+
+def nc_model_free(m):
+    lib().nc_model_free(m)
+
+
+def nc_kv_create(m, batch, max_seq):
+    out = ctypes.c_void_p()
+    _check(lib().nc_kv_create(m, batch, max_seq, ctypes.byref(out)))
+    return out
+
+
+def nc_kv_free(kv):
+    lib().nc_kv_free(kv)
+
+
+def nc_kv_set_lens(kv, lens):
+    a = np.ascontiguousarray(lens, dtype=np.int32)
+    _check(lib().nc_kv_set_lens(kv, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+
+
+def nc_kv_get_lens(kv, batch):
+    a = np.zeros(batch, dtype=np.int32)
+    _check(lib().nc_kv_get_lens(kv, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+    return a
+
+
+def nc_kv_export(kv, layer, k_out, v_out, stream=None):
+    _check(lib().nc_kv_export(kv, layer, _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+def nc_prefill(m, tokens, B, T, kv, logits, stream=None):
+    _check(lib().nc_prefill(m, _ptr(tokens), B, T, kv, _ptr(logits), _stream(stream)))
+
+
+def nc_decode_step(m, tokens, B, kv, logits, stream=None):
+    _check(lib().nc_decode_step(m, _ptr(tokens), B, kv, _ptr(logits), _stream(stream)))
+
+
+def nc_argmax(logits, B, V, out, stream=None):
+    _check(lib().nc_argmax(_ptr(logits), B, V, _ptr(out), _stream(stream)))
+
+
+# ------------------------------------------------------------------ convenience -------
+def upload_weights(weights_list, dtype, device="cuda"):
+    """float32 numpy arrays (exact values of the storage dtype) -> device tensors."""
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return [torch.from_numpy(np.ascontiguousarray(w)).to(device=device).to(tdt) for w in weights_list]
+
+
+class Model:
+    """Owning wrapper: model handle + its KV caches."""
+
+    def __init__(self, shape, weights_list, max_seq=None, device="cuda"):
+        self.shape = shape
+        self.cfg = make_config(shape, max_seq)
+        dev = upload_weights(weights_list, shape.dtype, device)
+        self.handle = nc_model_create(self.cfg, dev)
+        del dev
+
+    def new_kv(self, batch, max_seq):
+        return KV(self, batch, max_seq)
+
+    def close(self):
+        if self.handle is not None:
+            nc_model_free(self.handle)
+            self.handle = None
+
+
+class KV:
+    def __init__(self, model, batch, max_seq):
+        self.model, self.batch, self.max_seq = model, batch, max_seq
+        self.handle = nc_kv_create(model.handle, batch, max_seq)
+
+    def prefill(self, tokens, logits, stream=None):
+        B, T = tokens.shape
+        nc_prefill(self.model.handle, tokens, B, T, self.handle, logits, stream)
+
+    def decode(self, tokens, logits, stream=None):
+        nc_decode_step(self.model.handle, tokens, self.batch, self.handle, logits, stream)
+
+    def set_lens(self, lens):
+        nc_kv_set_lens(self.handle, lens)
+
+    def lens(self):
+        return nc_kv_get_lens(self.handle, self.batch)
+
+    def export(self, layer, k_out, v_out, stream=None):
+        nc_kv_export(self.handle, layer, k_out, v_out, stream)
+
+    def close(self):
+        if self.handle is not None:
+            nc_kv_free(self.handle)
+            self.handle = None

@@ -1,0 +1,137 @@
+/*
+ * nc.h -- C ABI of the gfx950 (MI355X) forward pass of nanochat's GPT:
+ * batched prefill and KV-cache incremental decode.
+ *
+ * The model computed (sources: yelogs.com nanochat launch write-up, section on technical
+ * details and the author's Q&A, architecture answer; apidog.com/th "How to train your own
+ * ChatGPT for $50", section "How nanochat works", parts 1 (GPT model), 3 (precision) and
+ * 6 (inference engine); geoz.com.cn summary, development-tricks section):
+ *
+ *   x      = norm(wte[token])                                  (fp32 residual stream)
+ *   per layer l:
+ *     h    = norm(x)
+ *     q    = norm(rope(h Wq^T, pos)) per head,  k = norm(rope(h Wk^T, pos)),  v = h Wv^T
+ *     y_h  = softmax(q_h k^T / sqrt(hd) + causal mask) v   (one K/V head shared by all
+ *            query heads: multi-query attention)
+ *     x   += concat_h(y_h) Wo^T
+ *     x   += relu(norm(x) Wfc^T)^2 Wproj^T
+ *   logits = cap * tanh(norm(x) Wlm^T / cap)                   (fp32)
+ *
+ * norm(z) = z / sqrt(mean(z^2) + eps) has no parameters.  RoPE rotates the pair
+ * (i, i + hd/2) by pos * base^(-2i/hd).  Linear layers have no bias; weights are stored
+ * [out, in] as in torch.nn.Linear.  Matrix products take dtype operands (bf16 or fp32)
+ * with fp32 accumulation; the residual stream, norms, softmax and logits are fp32.
+ *
+ * Conventions for every call:
+ *  - Every pointer named *_dev is device memory on the current HIP device; pointers named
+ *    *_host are host memory.  Device buffers must be 16-byte aligned.
+ *  - Calls that take a `stream` (a hipStream_t passed as void*, NULL = default stream) only
+ *    enqueue work and return; the caller keeps inputs alive and reads outputs after the
+ *    stream reaches that point.  One nc_kv must not be used on two streams at once.
+ *  - Every call returns NC_OK (0) or a negative nc_status.  On error nothing is enqueued
+ *    and no state changes; nc_last_error() returns a message for the calling thread.
+ *    Faults of already-enqueued kernels surface as NC_ERR_DEVICE from a later call.
+ *  - No C++ exception and no abort crosses this boundary.
+ */
+#ifndef NC_H
+#define NC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t nc_status;
+
+#define NC_OK 0
+#define NC_ERR_INVALID_ARG (-1) /* null pointer, bad size or shape, mismatched batch     */
+#define NC_ERR_UNSUPPORTED (-2) /* valid but not supported (head_dim, n_kv_head, device) */
+#define NC_ERR_OOM (-3)         /* device allocation failed                               */
+#define NC_ERR_CAPACITY (-4)    /* a row would exceed the cache's max_seq                 */
+#define NC_ERR_STATE (-5)       /* call not allowed in the object's state                 */
+#define NC_ERR_DEVICE (-6)      /* no usable GPU, or a HIP runtime error                  */
+
+#define NC_F32 0
+#define NC_BF16 1
+
+#define NC_ABI_VERSION 1
+
+/* Model shape.  Requirements: d_model == n_head * head_dim; n_kv_head == 1 (multi-query
+ * attention); head_dim in {64, 128}; d_model, d_ff multiples of 64; vocab >= 1;
+ * max_seq >= 1 (longest position the RoPE table covers); softcap > 0; norm_eps >= 0. */
+typedef struct nc_config {
+    int32_t n_layer;
+    int32_t d_model;
+    int32_t n_head;
+    int32_t n_kv_head;
+    int32_t head_dim;
+    int32_t d_ff;
+    int32_t vocab;
+    int32_t max_seq;
+    float rope_base;
+    float softcap;
+    float norm_eps;
+    int32_t dtype; /* NC_F32 or NC_BF16: storage type of weights, matmul operands, KV cache */
+} nc_config;
+
+typedef struct nc_model nc_model; /* weights + RoPE table, owned by the library          */
+typedef struct nc_kv nc_kv;       /* KV cache + per-row lengths + workspace, library-owned */
+
+/* Build a model from 6*n_layer + 2 device tensors of cfg->dtype elements, row-major
+ * [out, in], in canonical order:
+ *   wte [vocab, d_model],
+ *   per layer: Wq [n_head*hd, d], Wk [hd, d], Wv [hd, d], Wo [d, n_head*hd],
+ *              Wfc [d_ff, d], Wproj [d, d_ff],
+ *   lm_head [vocab, d_model].
+ * The library copies (and repacks) them into memory it owns, synchronously; the caller may
+ * free its tensors when this returns.  Fails with NC_ERR_DEVICE if no gfx950 GPU is
+ * current, NC_ERR_UNSUPPORTED / NC_ERR_INVALID_ARG for a bad cfg. */
+nc_status nc_model_create(const nc_config* cfg, const void* const* weights_dev,
+                          nc_model** out);
+void nc_model_free(nc_model* m); /* NULL is a no-op; all kv objects must be freed first */
+
+/* KV cache for `batch` rows of up to `max_seq` positions (max_seq <= cfg.max_seq).
+ * Layout (library-private): K [L][batch][max_seq][hd], V transposed [L][batch][hd][max_seq],
+ * both cfg.dtype; keys are stored after RoPE and QK-norm.  All lengths start at 0. */
+nc_status nc_kv_create(nc_model* m, int32_t batch, int32_t max_seq, nc_kv** out);
+void nc_kv_free(nc_kv* kv); /* NULL is a no-op; synchronises the device first */
+
+/* Shrink row lengths (lens_host[b] <= current length; 0 empties a row).  Keys past the new
+ * length are ignored from then on: truncation equals a shorter prefill (causality).
+ * Synchronous with respect to the device. */
+nc_status nc_kv_set_lens(nc_kv* kv, const int32_t* lens_host);
+/* Current row lengths as the host sees them once enqueued work completes. */
+nc_status nc_kv_get_lens(const nc_kv* kv, int32_t* lens_host);
+
+/* Copy layer `layer` of the cache out in plain layout: k_dev and v_dev are
+ * [batch][max_seq][hd] of cfg.dtype (rows past each length hold stale values). */
+nc_status nc_kv_export(nc_kv* kv, int32_t layer, void* k_dev, void* v_dev, void* stream);
+
+/* Prefill: tokens_dev int32 [B, T] at positions 0..T-1 of every row.  Requires every
+ * length 0, B == batch of kv, 1 <= T <= kv max_seq.  logits_dev: fp32 [B, T, vocab] for
+ * every position, or NULL to fill the cache only.  On success lengths become T.
+ * Token ids outside [0, vocab) are clamped (memory-safe; their outputs are meaningless). */
+nc_status nc_prefill(nc_model* m, const int32_t* tokens_dev, int32_t B, int32_t T,
+                     nc_kv* kv, float* logits_dev, void* stream);
+
+/* One decode step: row b takes token tokens_dev[b] at position lens[b] and attends to
+ * cache positions 0..lens[b].  Requires B == batch of kv and lens[b] + 1 <= max_seq for
+ * every row (NC_ERR_CAPACITY otherwise).  logits_dev: fp32 [B, vocab] (not NULL).
+ * On success every length grows by one. */
+nc_status nc_decode_step(nc_model* m, const int32_t* tokens_dev, int32_t B, nc_kv* kv,
+                         float* logits_dev, void* stream);
+
+/* Greedy pick: out_dev[b] = argmax_v logits_dev[b, v] over fp32 [B, V]; ties go to the
+ * lowest index; NaN compares below every number. */
+nc_status nc_argmax(const float* logits_dev, int32_t B, int32_t V, int32_t* out_dev,
+                    void* stream);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* nc_last_error(void);
+int32_t nc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NC_H */

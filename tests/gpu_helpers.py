@@ -1,0 +1,48 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C-ABI binding and
+compare with the oracle."""
+
+import numpy as np
+
+from dense_decoder_only_bf16_amd import nc
+from dense_decoder_only_bf16_amd.inputs import canonical_list
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def gpu_model(shape, weights, max_seq=None):
+    return nc.Model(shape, canonical_list(weights), max_seq=max_seq)
+
+
+def prefill(model, tokens, max_seq, logits=True):
+    torch = torch_mod()
+    B, T = tokens.shape
+    kv = model.new_kv(B, max_seq)
+    tok = torch.from_numpy(np.ascontiguousarray(tokens, dtype=np.int32)).cuda()
+    out = torch.empty((B, T, model.shape.vocab), device="cuda", dtype=torch.float32) if logits else None
+    kv.prefill(tok, out)
+    torch.cuda.synchronize()
+    return kv, (out.cpu().numpy() if logits else None)
+
+
+def decode(model, kv, tokens):
+    torch = torch_mod()
+    tok = torch.from_numpy(np.ascontiguousarray(tokens, dtype=np.int32)).cuda()
+    out = torch.empty((kv.batch, model.shape.vocab), device="cuda", dtype=torch.float32)
+    kv.decode(tok, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def agreement(a, b):
+    """Fraction of rows whose argmax (last axis) matches."""
+    return float(np.mean(np.argmax(a, -1) == np.argmax(b, -1)))
+
+
+def report(tag, got, want):
+    err = float(np.max(np.abs(got - want)))
+    agr = agreement(got, want)
+    print(f"[{tag}] max_abs={err:.3e} argmax_agree={agr:.4f} n={got.shape[:-1]}", flush=True)
+    return err, agr

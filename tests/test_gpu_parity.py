@@ -1,0 +1,190 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Bars: fp32 model max |logit error| <= 1e-4; bf16 models max |logit error| <= 3e-2 and
+greedy-argmax agreement >= 99% over the checked positions.  Decode is teacher-forced:
+the GPU is fed the oracle's greedy tokens (tiny) or seeded tokens (bf16), so logits are
+comparable at every step."""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from dense_decoder_only_bf16_amd import nc
+from dense_decoder_only_bf16_amd.inputs import (TINY, Shape, make_tokens, make_weights,
+                                                make_lens)
+from oracle import OracleModel
+
+from gpu_helpers import agreement, decode, gpu_model, prefill, report, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+BF16_TOL = 3e-2
+AGREE = 0.99
+
+# bf16 model small enough for the oracle to check every output, with ragged sizes:
+# T not a multiple of any tile, vocab not a multiple of 128.
+SMALL_BF16 = Shape("small-bf16", n_layer=2, d_model=256, n_head=2, head_dim=128, d_ff=1024,
+                   vocab=1000, dtype="bf16", max_seq=320)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = make_weights(TINY, seed=0)
+    return w, OracleModel(TINY, w), gpu_model(TINY, w)
+
+
+def test_tiny_prefill_and_greedy_decode(tiny):
+    w, orc, gm = tiny
+    prompt = make_tokens(TINY.vocab, 1, 64, seed=1)
+    want_pre, _ = orc.prefill(prompt)
+    toks, want_steps = orc.greedy(prompt, 16, max_seq=80)
+    kv, got_pre = prefill(gm, prompt, 80)
+    err, _ = report("tiny prefill", got_pre, want_pre)
+    assert err <= F32_TOL
+    # greedy continuation on the GPU reproduces the oracle's tokens
+    assert np.array_equal(np.argmax(got_pre[:, -1], -1), toks[:, 0])
+    for s in range(16):
+        got = decode(gm, kv, toks[:, s])
+        err, _ = report(f"tiny decode {s}", got, want_steps[:, s])
+        assert err <= F32_TOL
+        if s + 1 < 16:
+            assert np.array_equal(np.argmax(got, -1), toks[:, s + 1])
+    assert np.array_equal(kv.lens(), [80])
+    kv.close()
+
+
+def test_tiny_cache_contents(tiny):
+    torch = torch_mod()
+    w, orc, gm = tiny
+    prompt = make_tokens(TINY.vocab, 1, 64, seed=1)
+    _, cache = orc.prefill(prompt, max_seq=80)
+    kv, _ = prefill(gm, prompt, 80, logits=False)
+    for layer in range(TINY.n_layer):
+        k = torch.empty((1, 80, 64), device="cuda", dtype=torch.float32)
+        v = torch.empty_like(k)
+        kv.export(layer, k, v)
+        torch.cuda.synchronize()
+        k, v = k.cpu().numpy(), v.cpu().numpy()
+        assert np.max(np.abs(k[0, :64] - cache["k"][layer, 0, :64, 0])) < 1e-5
+        assert np.max(np.abs(v[0, :64] - cache["v"][layer, 0, :64, 0])) < 1e-5
+    kv.close()
+
+
+@pytest.fixture(scope="module")
+def small():
+    w = make_weights(SMALL_BF16, seed=3)
+    return w, OracleModel(SMALL_BF16, w), gpu_model(SMALL_BF16, w)
+
+
+def test_bf16_small_prefill_ragged(small):
+    w, orc, gm = small
+    toks = make_tokens(SMALL_BF16.vocab, 3, 200, seed=4)
+    want, _ = orc.prefill(toks)
+    kv, got = prefill(gm, toks, 320)
+    err, agr = report("small bf16 prefill", got, want)
+    assert err <= BF16_TOL and agr >= AGREE
+    kv.close()
+
+
+def test_bf16_small_decode_teacher_forced(small):
+    w, orc, gm = small
+    toks = make_tokens(SMALL_BF16.vocab, 3, 216, seed=5)
+    want, _ = orc.prefill(toks)
+    kv, _ = prefill(gm, toks[:, :200], 320, logits=False)
+    got = np.stack([decode(gm, kv, toks[:, 200 + s]) for s in range(16)], axis=1)
+    err, agr = report("small bf16 decode", got, want[:, 200:216])
+    assert err <= BF16_TOL and agr >= AGREE
+    kv.close()
+
+
+def test_bf16_small_truncated_rows(small):
+    # prefill, shrink rows to different lengths, decode: equals shorter prefills
+    w, orc, gm = small
+    toks = make_tokens(SMALL_BF16.vocab, 3, 300, seed=6)
+    lens = np.array([1, 77, 300], dtype=np.int32)
+    kv, _ = prefill(gm, toks, 320, logits=False)
+    kv.set_lens(lens)
+    nxt = make_tokens(SMALL_BF16.vocab, 1, 3, seed=7)[0]
+    got = decode(gm, kv, nxt)
+    for b in range(3):
+        seq = np.concatenate([toks[b, :lens[b]], nxt[b:b + 1]])[None]
+        ref, _ = orc.prefill(seq, logits_at=[lens[b]])
+        err = np.max(np.abs(got[b] - ref[0, 0]))
+        assert err <= BF16_TOL, (b, err)
+        assert np.argmax(got[b]) == np.argmax(ref[0, 0])
+    assert np.array_equal(kv.lens(), lens + 1)
+    kv.close()
+
+
+def test_prefill_single_token_and_batch_independence(small):
+    w, orc, gm = small
+    toks = make_tokens(SMALL_BF16.vocab, 4, 1, seed=8)
+    want, _ = orc.prefill(toks)
+    kv, got = prefill(gm, toks, 8)
+    err, agr = report("small bf16 T=1", got, want)
+    assert err <= BF16_TOL
+    kv.close()
+    # row b of a batched prefill equals a batch-1 prefill of row b, bitwise
+    toks = make_tokens(SMALL_BF16.vocab, 3, 70, seed=9)
+    kv, full = prefill(gm, toks, 80)
+    kv.close()
+    for b in range(3):
+        kv1, one = prefill(gm, toks[b:b + 1], 80)
+        kv1.close()
+        assert np.array_equal(one[0], full[b])
+
+
+def test_determinism(small):
+    w, orc, gm = small
+    toks = make_tokens(SMALL_BF16.vocab, 2, 150, seed=10)
+    kv1, a = prefill(gm, toks, 160)
+    kv2, b = prefill(gm, toks, 160)
+    assert np.array_equal(a, b)
+    nxt = make_tokens(SMALL_BF16.vocab, 1, 2, seed=11)[0]
+    assert np.array_equal(decode(gm, kv1, nxt), decode(gm, kv2, nxt))
+    kv1.close()
+    kv2.close()
+
+
+def test_error_paths_on_gpu(small):
+    torch = torch_mod()
+    w, orc, gm = small
+    toks = make_tokens(SMALL_BF16.vocab, 2, 8, seed=12)
+    kv, _ = prefill(gm, toks, 9, logits=False)
+    t = torch.zeros(2, dtype=torch.int32, device="cuda")
+    out = torch.empty((2, SMALL_BF16.vocab), device="cuda", dtype=torch.float32)
+    with pytest.raises(nc.NcError) as e:  # prefill into a non-empty cache
+        kv.prefill(torch.zeros((2, 4), dtype=torch.int32, device="cuda"), None)
+    assert e.value.code == nc.NC_ERR_STATE
+    kv.decode(t, out)  # fills position 8 (the last)
+    with pytest.raises(nc.NcError) as e:
+        kv.decode(t, out)
+    assert e.value.code == nc.NC_ERR_CAPACITY
+    assert np.array_equal(kv.lens(), [9, 9])  # unchanged by the failed call
+    with pytest.raises(nc.NcError) as e:
+        nc.nc_decode_step(gm.handle, t, 3, kv.handle, out)
+    assert e.value.code == nc.NC_ERR_INVALID_ARG
+    with pytest.raises(nc.NcError) as e:
+        kv.set_lens([10, 1])  # grow
+    assert e.value.code == nc.NC_ERR_INVALID_ARG
+    kv.close()
+    with pytest.raises(nc.NcError) as e:
+        gm.new_kv(1, SMALL_BF16.max_seq + 1)
+    assert e.value.code == nc.NC_ERR_INVALID_ARG
+
+
+def test_argmax_ties_and_nan():
+    torch = torch_mod()
+    x = torch.zeros((4, 1000), device="cuda", dtype=torch.float32)
+    x[0, 5] = 1.0
+    x[0, 7] = 1.0          # tie -> lowest index
+    x[1, :] = float("nan")
+    x[1, 999] = -3.0       # NaN never wins
+    x[2, 123] = float("inf")
+    x[3, :] = -1.0         # all equal -> 0
+    out = torch.empty(4, dtype=torch.int32, device="cuda")
+    nc.nc_argmax(x, 4, 1000, out)
+    torch.cuda.synchronize()
+    assert out.cpu().tolist() == [5, 999, 123, 0]
