@@ -1,5 +1,5 @@
 // Causal multi-query attention for gfx950: a flash-style prefill kernel and a split-context
-// decode kernel with a combine pass.
+// decode kernel with a combine kernel.
 //
 // Multi-query attention: one K/V head serves every query head (yelogs.com launch write-up,
 // architecture answer).  Causal softmax of q.k/sqrt(hd) over keys at positions <= the
@@ -229,12 +229,13 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 }
 
 // ------------------------------------------------------------------ decode ----------
-// Split phase.  Workgroup (chunk c, row b): 4 waves x 64 keys = keys [256c, 256c + 256)
-// limited to positions 0..lens[b].  All query heads of the row (padded to 16) form the
-// 16 columns of 16x16 MFMA tiles, so each K/V element is read from memory once for the
-// whole head group.  K and V^T operands are loaded straight from the cache into
-// registers.  The four waves' partial softmax states are merged in LDS and the
-// workgroup writes (max, sum, o[16][hd]) for its chunk.
+// Split kernel.  Workgroup (chunk c, row b): 4 waves x 64 keys = keys [256c, 256c + 256)
+// limited to positions 0..lens[b].  All query heads of the row (padded to 16) form the 16
+// columns of 16x16 MFMA tiles, so each K/V element is read from memory once for the whole
+// head group.  Every wave issues all of its K and V^T loads (straight from the cache into
+// registers) before any arithmetic, so a wave keeps 32 KB in flight.  The four waves'
+// softmax states are merged in LDS and the workgroup writes its chunk's partial
+// (max, sum, o[16][hd]); the combine kernel merges the chunks of each row.
 constexpr int DEC_KPW = 64, DEC_CHUNK = 4 * DEC_KPW;
 int attn_decode_chunk() { return DEC_CHUNK; }
 
@@ -247,6 +248,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
     typedef typename Chunk<T>::half HT;
     constexpr int DS = HD / 32;   // 32-deep steps over head dim for S^T
     constexpr int DT = HD / 16;   // 16-row tiles of O^T
+    constexpr int PSZ = 16 * (HD + 2);
 
     __shared__ float sm[4][16], sl[4][16];
     __shared__ float so[4][16][HD + 1];
@@ -263,22 +265,46 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
     const T* kb_base = kc + (long long)b * S * HD;
     const T* vb_base = vtc + (long long)b * HD * S;
 
+    // ---- issue every load of this wave
     CT qf[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s)
         qf[s] = (col < H) ? *(const CT*)(q + ((long long)b * H + col) * HD + 32 * s + 8 * g) : zero_vec<CT>();
+    CT kf[4][DS];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+        const int key = kbeg + 16 * kt + col;
+#pragma unroll
+        for (int s = 0; s < DS; ++s)
+            kf[kt][s] = (key < nkeys) ? *(const CT*)(kb_base + (long long)key * HD + 32 * s + 8 * g) : zero_vec<CT>();
+    }
+    // V^T operands: slot 8g+i of 32-key step u <-> key 32u + 4g + i (i < 4) or
+    // 32u + 16 + 4g + (i - 4) (i >= 4); loaded whole when in range, else element-wise.
+    HT vlo[2][DT], vhi[2][DT];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int ka = kbeg + 32 * u + 4 * g, kb2 = ka + 16;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const T* src = vb_base + (long long)(dt * 16 + col) * S;
+            if (ka + 4 <= nkeys) vlo[u][dt] = *(const HT*)(src + ka);
+            else
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vlo[u][dt][e] = (ka + e < nkeys) ? src[ka + e] : from_f32<T>(0.f);
+            if (kb2 + 4 <= nkeys) vhi[u][dt] = *(const HT*)(src + kb2);
+            else
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vhi[u][dt][e] = (kb2 + e < nkeys) ? src[kb2 + e] : from_f32<T>(0.f);
+        }
+    }
 
-    // S^T tiles for 4 x 16 keys: lane holds head `col`, keys kbeg + 16kt + 4g + j.
+    // ---- scores S^T (lane: head `col`, keys kbeg + 16kt + 4g + j), softmax (base 2)
     f32x4 sacc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
         sacc[kt] = zero_vec<f32x4>();
-        const int key = kbeg + 16 * kt + col;
 #pragma unroll
-        for (int s = 0; s < DS; ++s) {
-            CT kf = (key < nkeys) ? *(const CT*)(kb_base + (long long)key * HD + 32 * s + 8 * g) : zero_vec<CT>();
-            sacc[kt] = mma16(kf, qf[s], sacc[kt]);
-        }
+        for (int s = 0; s < DS; ++s) sacc[kt] = mma16(kf[kt][s], qf[s], sacc[kt]);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -292,8 +318,8 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
         }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float ls = 0.f;
     const float mref = (mx == -INFINITY) ? 0.f : mx;  // a wave past the last key has no mass
+    float ls = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -305,8 +331,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
     ls += __shfl_xor(ls, 16, 64);
     ls += __shfl_xor(ls, 32, 64);
 
-    // O^T[d][head] over 64 keys: two 32-deep steps; slot 8g+i <-> key
-    // 32u + 4g + i (i < 4) or 32u + 16 + 4g + (i - 4) (i >= 4).
+    // ---- O^T[d][head] over the wave's 64 keys (two 32-deep steps)
     f32x4 oacc[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) oacc[i] = zero_vec<f32x4>();
@@ -318,33 +343,21 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
             pf[i] = from_f32<T>(sacc[2 * u][i]);
             pf[4 + i] = from_f32<T>(sacc[2 * u + 1][i]);
         }
-        const int ka = kbeg + 32 * u + 4 * g, kb2 = ka + 16;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const int d = dt * 16 + col;
-            const T* src = vb_base + (long long)d * S;
-            HT lo, hi;
-            if (ka + 4 <= nkeys) lo = *(const HT*)(src + ka);
-            else
-#pragma unroll
-                for (int e = 0; e < 4; ++e) lo[e] = (ka + e < nkeys) ? src[ka + e] : from_f32<T>(0.f);
-            if (kb2 + 4 <= nkeys) hi = *(const HT*)(src + kb2);
-            else
-#pragma unroll
-                for (int e = 0; e < 4; ++e) hi[e] = (kb2 + e < nkeys) ? src[kb2 + e] : from_f32<T>(0.f);
             CT vf;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                vf[i] = lo[i];
-                vf[4 + i] = hi[i];
+                vf[i] = vlo[u][dt][i];
+                vf[4 + i] = vhi[u][dt][i];
             }
             oacc[dt] = mma16(vf, pf, oacc[dt]);
         }
     }
 
-    // Merge the four waves.  Lane holds head `col`, features 16dt + 4g + j.
+    // ---- merge the four waves into this chunk's partial
     if (g == 0) {
-        sm[wave][col] = (mx == -INFINITY) ? -INFINITY : mx;
+        sm[wave][col] = mx;
         sl[wave][col] = ls;
     }
 #pragma unroll
@@ -352,21 +365,19 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) so[wave][col][dt * 16 + 4 * g + j] = oacc[dt][j];
     __syncthreads();
-    float* pb = part + ((long long)b * max_chunks + c) * 16 * (HD + 2);
+    float* pb = part + ((long long)b * max_chunks + c) * PSZ;
     for (int i = tid; i < 16 * HD; i += 256) {
         const int h = i / HD, d = i % HD;
-        float M = fmaxf(fmaxf(sm[0][h], sm[1][h]), fmaxf(sm[2][h], sm[3][h]));
+        const float M = fmaxf(fmaxf(sm[0][h], sm[1][h]), fmaxf(sm[2][h], sm[3][h]));
         float o = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            float mw = sm[w][h];
-            if (mw != -INFINITY) o += fast_exp2((mw == -INFINITY ? 0.f : mw) - M) * so[w][h][d];
-        }
-        pb[16 * 2 + h * HD + d] = o;
+        for (int w = 0; w < 4; ++w)
+            if (sm[w][h] != -INFINITY) o += fast_exp2(sm[w][h] - M) * so[w][h][d];
+        pb[32 + h * HD + d] = o;
     }
     if (tid < 16) {
         const int h = tid;
-        float M = fmaxf(fmaxf(sm[0][h], sm[1][h]), fmaxf(sm[2][h], sm[3][h]));
+        const float M = fmaxf(fmaxf(sm[0][h], sm[1][h]), fmaxf(sm[2][h], sm[3][h]));
         float l = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w)
@@ -374,44 +385,44 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
         pb[h] = M;
         pb[16 + h] = l;
     }
+
 }
 
-// Combine phase: y[b][h][d] = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c.
+// Combine kernel: workgroup (head h, row b), one thread per feature d:
+// y[b][h][d] = sum_c 2^(m_c - M) o_c[d] / sum_c 2^(m_c - M) l_c.
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* __restrict__ part,
-                                                                  const int32_t* __restrict__ lens,
-                                                                  T* __restrict__ y, int H, int S,
-                                                                  int max_chunks) {
-    const int b = blockIdx.x, tid = threadIdx.x;
+__global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __restrict__ part,
+                                                                 const int32_t* __restrict__ lens,
+                                                                 T* __restrict__ y, int H, int S,
+                                                                 int max_chunks) {
+    constexpr int PSZ = 16 * (HD + 2);
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const int nkeys = min(lens[b] + 1, S);
     const int nch = (nkeys + DEC_CHUNK - 1) / DEC_CHUNK;
-    const float* pb = part + (long long)b * max_chunks * 16 * (HD + 2);
-    for (int i = tid; i < H * HD; i += 256) {
-        const int h = i / HD, d = i % HD;
-        float M = -INFINITY;
-        for (int c = 0; c < nch; ++c) M = fmaxf(M, pb[(long long)c * 16 * (HD + 2) + h]);
-        float o = 0.f, l = 0.f;
-        for (int c = 0; c < nch; ++c) {
-            const float* pc = pb + (long long)c * 16 * (HD + 2);
-            float w = fast_exp2(pc[h] - M);
-            l += w * pc[16 + h];
-            o += w * pc[32 + h * HD + d];
-        }
-        y[((long long)b * H + h) * HD + d] = from_f32<T>(o / l);
+    const float* prow = part + (long long)b * max_chunks * PSZ;
+    float M = -INFINITY;
+    for (int cc = 0; cc < nch; ++cc) M = fmaxf(M, prow[(long long)cc * PSZ + h]);
+    float o = 0.f, l = 0.f;
+    for (int cc = 0; cc < nch; ++cc) {
+        const float* pc = prow + (long long)cc * PSZ;
+        const float w = fast_exp2(pc[h] - M);
+        l += w * pc[16 + h];
+        o += w * pc[32 + h * HD + d];
     }
+    y[((long long)b * H + h) * HD + d] = from_f32<T>(o / l);
 }
 
 hipError_t launch_attn_decode(DType dt, int hd, const void* q, const void* kc, const void* vtc,
                               const int32_t* lens, void* y, float* part, int B, int H, int S,
                               int max_chunks, hipStream_t st) {
     const float sl = 1.4426950408889634f / sqrtf((float)hd);
-    dim3 g1(max_chunks, B);
+    dim3 g1(max_chunks, B), g2(H, B);
 #define NC_AD(TT, HDV)                                                                         \
     do {                                                                                       \
         hipLaunchKernelGGL((attn_decode_split_kernel<TT, HDV>), g1, dim3(256), 0, st,          \
                            (const TT*)q, (const TT*)kc, (const TT*)vtc, lens, part, H, S,      \
                            max_chunks, sl);                                                    \
-        hipLaunchKernelGGL((attn_decode_combine_kernel<TT, HDV>), dim3(B), dim3(256), 0, st,   \
+        hipLaunchKernelGGL((attn_decode_combine_kernel<TT, HDV>), g2, dim3(HDV), 0, st,        \
                            (const float*)part, lens, (TT*)y, H, S, max_chunks);                \
     } while (0)
     if (dt == BF16 && hd == 128) NC_AD(bf16, 128);

@@ -45,6 +45,21 @@ __device__ __forceinline__ f32x4 mma16(f32x8 a, f32x8 b, f32x4 c) {
     return c;
 }
 
+// Same-size unsigned vector of a chunk, for branch-free masking of loaded values.
+template <typename T> struct ChunkBits;
+template <> struct ChunkBits<bf16> { typedef uint32_t type __attribute__((ext_vector_type(4))); };
+template <> struct ChunkBits<float> { typedef uint32_t type __attribute__((ext_vector_type(8))); };
+
+// Load a chunk and zero it where `keep` is false, without a branch around the load (the
+// address must be valid either way).
+template <typename T>
+__device__ __forceinline__ typename Chunk<T>::type load_masked(const T* p, bool keep) {
+    typedef typename ChunkBits<T>::type U;
+    U v = *(const U*)p;
+    v &= (U)(keep ? 0xffffffffu : 0u);
+    return __builtin_bit_cast(typename Chunk<T>::type, v);
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }

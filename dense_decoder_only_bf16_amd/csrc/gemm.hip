@@ -1,4 +1,4 @@
-// MFMA matrix product C = A[M,K] B[N,K]^T for gfx950 with fused epilogues.
+// MFMA matrix product C = A[M,K] B[N,K]^T for gfx950 with fused epilogues (prefill).
 //
 // All linear layers of the model are bias-free products with weights stored [out, in]
 // (apidog.com/th "How to train your own ChatGPT for $50", part 3 on precision: the weight
@@ -8,16 +8,32 @@
 // precedes a projection is applied as a row scale in the epilogue, from per-row sums of
 // squares that the producer of x left behind.
 //
-// Tiling: a workgroup computes a BM x BN tile with WM x WN waves; each wave owns a
-// (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  K advances in 128-byte slices
-// (64 bf16 or 32 fp32 per row), staged global -> registers -> LDS with two LDS buffers so
-// the next slice's global loads overlap the current slice's MFMAs.  LDS rows are 128
-// bytes split into 8-element chunks whose position is XOR-swizzled with the row index,
-// so the 32 rows an MFMA operand read touches fall on distinct banks.
+// Tiling: a workgroup computes a 256 x 256 tile with 2 x 2 waves; each wave owns a
+// 128 x 128 sub-tile of 4 x 4 MFMA 32x32 tiles (256 accumulator registers).  Operands are
+// staged in LDS in the MFMA-blocked form [rows/32][K/16][32][16]: one 32x16 block is
+// exactly one wave's 16-deep operand, so every LDS operand read is 1 KB contiguous.
+// Weights arrive in that blocked form from global memory (see kernels.h).
+//
+// Two main loops:
+//  * bf16 (the model's dtype): global -> LDS with the gfx950 direct-to-LDS load
+//    (global_load_lds_dwordx4), a ring of 4 LDS stages of 32 K-columns, loads issued three
+//    stages ahead; no staging registers and no LDS store instructions.  The operand
+//    fragments of the next 16-deep step (also across a K-tile boundary) are read from LDS
+//    while the MFMAs of the current step run (fragments double-buffered in registers,
+//    reads interleaved one per two MFMAs), so with one wave per SIMD neither LDS latency
+//    nor LDS bandwidth stalls the matrix cores.
+//  * fp32 (the small fp32 check model): loads staged through registers into two LDS
+//    buffers (A kept row-major with an XOR swizzle).
+// Workgroups are dealt round-robin to the 8 dies (XCDs), each with its own L2; tiles are
+// renumbered so each die works on a contiguous range, walked in groups of 8 row tiles so
+// tiles running together share A rows and weight columns in the die's L2.
 #include "common.h"
 #include "kernels.h"
 
 namespace nc {
+
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
 
 template <typename T> struct KT {
     static constexpr int BK = 128 / (int)sizeof(T);  // elements per 128-byte row slice
@@ -25,133 +41,66 @@ template <typename T> struct KT {
     static constexpr int KS = BK / 16;               // 16-deep MFMA steps per slice
 };
 
-template <typename T, int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs p) {
-    typedef typename Chunk<T>::type CT;
-    constexpr int NT = WM * WN * 64;
-    constexpr int BK = KT<T>::BK, CPR = KT<T>::CPR, KS = KT<T>::KS;
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int AL = BM * CPR / NT, BL = BN * CPR / NT;
-    static_assert(FM >= 1 && FN >= 1, "wave tile below 32x32");
-    static_assert(AL >= 1 && BL >= 1 && AL * NT == BM * CPR && BL * NT == BN * CPR, "tile/threads");
+constexpr int TBM = 256, TBN = 256;  // workgroup tile
 
-    __shared__ __attribute__((aligned(32))) T As[2][BM * BK];
-    __shared__ __attribute__((aligned(32))) T Bs[2][BN * BK];
-    __shared__ float rs[BM];
-    __shared__ float red[WN][BM];
+// (m0, n0, tile column index) of this workgroup's tile.
+__device__ __forceinline__ void tile_coords(const GemmArgs& p, int& m0, int& n0, int& tn) {
+    constexpr int GM = 8;
+    const int ntn = (p.N + TBN - 1) / TBN, ntm = (p.M + TBM - 1) / TBM;
+    const int total = ntn * ntm;
+    const int pid = blockIdx.x;
+    const int xcd = pid % 8, loc = pid / 8, q8 = total / 8, r8 = total % 8;
+    const int t = (xcd < r8) ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
+    const int grp = t / (GM * ntn), first_m = grp * GM;
+    const int gsize = min(ntm - first_m, GM);
+    const int tm = first_m + (t % (GM * ntn)) % gsize;
+    tn = (t % (GM * ntn)) / gsize;
+    n0 = tn * TBN;
+    m0 = tm * TBM;
+}
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+// Row scales r_m of the tile (RELU2 / SOFTCAP), computed once into LDS.
+__device__ __forceinline__ void tile_row_scales(const GemmArgs& p, int m0, float* rs, int nt) {
+    for (int r = threadIdx.x; r < TBM; r += nt) {
+        const int m = m0 + r;
+        float s = 0.f;
+        if (m < p.M)
+            for (int q = 0; q < p.ss_in_parts; ++q) s += p.ss_in[(long long)q * p.ss_stride + m];
+        rs[r] = 1.0f / sqrtf(s / (float)p.K + p.eps);
+    }
+}
+
+// Epilogue on the accumulators: lane holds column n0 + wn*128 + 32j + l32 and rows
+// m0 + wm*128 + 32i + 8(r/4) + 4hh + (r%4) of acc[i][j][r].
+template <typename T, int EPI>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[4][4], int m0, int n0,
+                                              int tn, const float* rs, float (*red)[TBM]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / 2, wn = wave % 2;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-    const int kspan = p.K / p.k_split;
-    const int kbeg = blockIdx.z * kspan;
-    const int nk = kspan / BK;
-
-    const T* A = (const T*)p.A;
-    const T* B = (const T*)p.B;
-
-    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
-        for (int r = tid; r < BM; r += NT) {
-            int m = m0 + r;
-            float s = 0.f;
-            if (m < p.M)
-                for (int q = 0; q < p.ss_in_parts; ++q) s += p.ss_in[(long long)q * p.ss_stride + m];
-            rs[r] = 1.0f / sqrtf(s / (float)p.K + p.eps);
-        }
-    }
-
-    CT ra[AL], rb[BL];
-    auto gload = [&](int kt) {
-        const int k0 = kbeg + kt * BK;
 #pragma unroll
-        for (int i = 0; i < AL; ++i) {
-            int q = tid + i * NT, r = q / CPR, c = q % CPR;
-            int gm = m0 + r;
-            ra[i] = (gm < p.M) ? *(const CT*)(A + (long long)gm * p.lda + k0 + c * 8) : zero_vec<CT>();
-        }
-#pragma unroll
-        for (int i = 0; i < BL; ++i) {
-            int q = tid + i * NT, r = q / CPR, c = q % CPR;
-            int gn = n0 + r;
-            rb[i] = (gn < p.N) ? *(const CT*)(B + (long long)gn * p.ldb + k0 + c * 8) : zero_vec<CT>();
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < AL; ++i) {
-            int q = tid + i * NT, r = q / CPR, c = q % CPR;
-            *(CT*)(&As[buf][r * BK + ((c ^ (r % CPR)) * 8)]) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < BL; ++i) {
-            int q = tid + i * NT, r = q / CPR, c = q % CPR;
-            *(CT*)(&Bs[buf][r * BK + ((c ^ (r % CPR)) * 8)]) = rb[i];
-        }
-    };
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = zero_vec<f32x16>();
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int c = 2 * s + hh;
-            CT a[FM], b[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                int r = wm * WTM + i * 32 + l32;
-                a[i] = *(const CT*)(&As[buf][r * BK + ((c ^ (r % CPR)) * 8)]);
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                int r = wn * WTN + j * 32 + l32;
-                b[j] = *(const CT*)(&Bs[buf][r * BK + ((c ^ (r % CPR)) * 8)]);
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mma32(a[i], b[j], acc[i][j]);
-        }
-        if (kt + 1 < nk) sstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---------------------------------------------------------------- epilogue ----
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int jr = 0; jr < 16; ++jr) {
-            const int rl = wm * WTM + i * 32 + 8 * (jr / 4) + 4 * hh + (jr % 4);
+            const int rl = wm * 128 + i * 32 + 8 * (jr / 4) + 4 * hh + (jr % 4);
             const int m = m0 + rl;
             float sq = 0.f;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = n0 + wn * WTN + j * 32 + l32;
+            for (int j = 0; j < 4; ++j) {
+                const int n = n0 + wn * 128 + j * 32 + l32;
                 const bool ok = (m < p.M) && (n < p.N);
-                float v = acc[i][j][jr];
+                const float v = acc[i][j][jr];
+                const long long o = (long long)m * p.ldo + n;
                 if (EPI == EPI_STORE) {
-                    if (ok) p.out_f32[(long long)blockIdx.z * p.z_stride + (long long)m * p.ldo + n] = v;
+                    if (ok) p.out_f32[(long long)blockIdx.z * p.z_stride + o] = v;
                 } else if (EPI == EPI_RELU2) {
-                    float t = fmaxf(v * rs[rl], 0.f);
-                    if (ok) ((T*)p.out_t)[(long long)m * p.ldo + n] = from_f32<T>(t * t);
+                    const float t = fmaxf(v * rs[rl], 0.f);
+                    if (ok) ((T*)p.out_t)[o] = from_f32<T>(t * t);
                 } else if (EPI == EPI_SOFTCAP) {
-                    float t = p.cap * tanh_f32(v * rs[rl] / p.cap);
-                    if (ok) p.out_f32[(long long)m * p.ldo + n] = t;
+                    if (ok) p.out_f32[o] = p.cap * tanh_f32(v * rs[rl] / p.cap);
                 } else {  // EPI_RESID
                     if (ok) {
-                        long long o = (long long)m * p.ldo + n;
-                        float xn = p.out_f32[o] + v;
+                        const float xn = p.out_f32[o] + v;
                         p.out_f32[o] = xn;
                         ((T*)p.out_t)[o] = from_f32<T>(xn);
                         sq += xn * xn;
@@ -167,53 +116,248 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs p) {
     }
     if (EPI == EPI_RESID) {
         __syncthreads();
-        for (int r = tid; r < BM; r += NT) {
-            int m = m0 + r;
-            if (m < p.M) {
-                float s = 0.f;
-#pragma unroll
-                for (int w = 0; w < WN; ++w) s += red[w][r];
-                p.ss_out[(long long)blockIdx.x * p.ss_stride + m] = s;
-            }
+        for (int r = tid; r < TBM; r += 256) {
+            const int m = m0 + r;
+            if (m < p.M) p.ss_out[(long long)tn * p.ss_stride + m] = red[0][r] + red[1][r];
         }
     }
 }
 
-// (BM, BN, WM, WN) of each tile shape.
-template <typename T, int EPI>
-static hipError_t launch_t(GemmTile tile, const GemmArgs& a, hipStream_t st) {
-    if (tile == GEMM_BIG) {
-        constexpr int BM = 256, BN = 256;
-        dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, a.k_split);
-        hipLaunchKernelGGL((gemm_kernel<T, BM, BN, 2, 2, EPI>), grid, dim3(256), 0, st, a);
-    } else if constexpr (sizeof(T) == 2) {
-        constexpr int BM = 32, BN = 128;
-        dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, a.k_split);
-        hipLaunchKernelGGL((gemm_kernel<T, BM, BN, 1, 4, EPI>), grid, dim3(256), 0, st, a);
+// ---------------------------------------------------------------------- bf16 ----------
+// vmcnt-only wait (expcnt and lgkmcnt left at their maxima) in the gfx9 s_waitcnt encoding.
+#define NC_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+template <int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_kernel(GemmArgs p) {
+    constexpr int BK = 32, KB = BK / 16, NS = 4;
+    constexpr int STAGE = (TBM + TBN) * BK;       // elements per stage (A then B)
+    __shared__ __attribute__((aligned(1024))) bf16 lds[NS * STAGE];
+    __shared__ float rs[TBM];
+    __shared__ float red[2][TBM];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / 2, wn = wave % 2;
+    const int l32 = lane & 31, hh = lane >> 5;
+    int m0, n0, tn;
+    tile_coords(p, m0, n0, tn);
+    const int ksteps = p.K / 16;
+    const int nk = p.K / BK;
+    const bf16* A = (const bf16*)p.A;
+    const bf16* B = (const bf16*)p.B;
+
+    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) tile_row_scales(p, m0, rs, 256);
+
+    // Stage layout: 16 A blocks (row block rb = b/2, k block b%2) then 16 B blocks.  Wave w
+    // loads A blocks 4w..4w+3 and B blocks 4w..4w+3; lane l fills bytes [16 l, 16 l + 16)
+    // of a 1 KB block, i.e. row l/2, k half l%2.  Rows past M or Npad read a clamped
+    // address; their outputs are masked in the epilogue.
+    auto issue = [&](int kt) {
+        bf16* sbase = lds + (kt % NS) * STAGE;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int b = wave * 4 + u;
+            const int rb = b / KB, kb = b % KB;
+            int m = m0 + rb * 32 + lane / 2;
+            m = m < p.M ? m : p.M - 1;
+            const bf16* src = A + (long long)m * p.lda + k0 + kb * 16 + (lane % 2) * 8;
+            __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(sbase + b * 512), 16, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int b = wave * 4 + u;
+            const int rb = b / KB, kb = b % KB;
+            int nb = n0 / 32 + rb;
+            nb = nb < p.Npad / 32 ? nb : p.Npad / 32 - 1;
+            const bf16* src = B + ((long long)nb * ksteps + k0 / 16 + kb) * 512 + lane * 8;
+            __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(sbase + (16 + b) * 512), 16, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = zero_vec<f32x16>();
+
+    // Operand fragments of one 16-deep step: 4 A blocks and 4 B blocks.
+    typedef bf16x8 Frag[4];
+    auto fload = [&](int kt, int s, Frag& fa, Frag& fb) {
+        const bf16* sa = lds + (kt % NS) * STAGE;
+        const bf16* sb = sa + TBM * BK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fa[i] = *(const bf16x8*)(sa + ((wm * 4 + i) * KB + s) * 512 + l32 * 16 + 8 * hh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            fb[j] = *(const bf16x8*)(sb + ((wn * 4 + j) * KB + s) * 512 + l32 * 16 + 8 * hh);
+    };
+    // 16 MFMAs of one step, with the 8 LDS reads of the next step interleaved (one read
+    // per two MFMAs) so the reads' latency hides behind the matrix cores.
+    auto mfmas = [&](Frag& fa, Frag& fb, bool interleave) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mma32(fa[i], fb[j], acc[i][j]);
+        if (interleave) {
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+            }
+        }
+    };
+
+    // Prologue: tiles 0 .. NS-2 in flight, fragments of tile 0, step 0 in registers.
+#pragma unroll
+    for (int kt = 0; kt < NS - 1; ++kt)
+        if (kt < nk) issue(kt);
+    if (nk > 2) NC_WAIT_VM(16);
+    else if (nk > 1) NC_WAIT_VM(8);
+    else NC_WAIT_VM(0);
+    __builtin_amdgcn_s_barrier();
+    Frag a0, b0, a1, b1;
+    fload(0, 0, a0, b0);
+    for (int kt = 0; kt < nk; ++kt) {
+        // step 0 of tile kt; read step 1 of tile kt meanwhile
+        fload(kt, 1, a1, b1);
+        mfmas(a0, b0, true);
+        // Tile kt+1: own loads done (tile kt+2 may still be in flight), then a barrier:
+        // every wave's loads of kt+1 are in LDS and every wave is done with tile kt-1,
+        // whose stage the next issue overwrites.
+        const bool more = kt + 1 < nk;
+        if (more) {
+            if (kt + 2 < nk) NC_WAIT_VM(8);
+            else NC_WAIT_VM(0);
+            __builtin_amdgcn_s_barrier();
+            if (kt + NS - 1 < nk) issue(kt + NS - 1);
+            fload(kt + 1, 0, a0, b0);  // step 0 of tile kt+1
+        }
+        mfmas(a1, b1, more);
+    }
+    __syncthreads();
+    tile_epilogue<bf16, EPI>(p, acc, m0, n0, tn, rs, red);
+}
+
+// ---------------------------------------------------------------------- fp32 ----------
+template <int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_f32_kernel(GemmArgs p) {
+    typedef float T;
+    typedef typename Chunk<T>::type CT;
+    constexpr int NT = 256;
+    constexpr int BK = KT<T>::BK, CPR = KT<T>::CPR, KS = KT<T>::KS;
+    constexpr int AL = TBM * CPR / NT, BL = TBN * CPR / NT;
+    constexpr int KB16 = BK / 16;
+    __shared__ __attribute__((aligned(32))) T As[2][TBM * BK];
+    __shared__ __attribute__((aligned(32))) T Bs[2][TBN * BK];
+    __shared__ float rs[TBM];
+    __shared__ float red[2][TBM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / 2, wn = wave % 2;
+    const int l32 = lane & 31, hh = lane >> 5;
+    int m0, n0, tn;
+    tile_coords(p, m0, n0, tn);
+    const int kspan = p.K / p.k_split;
+    const int kbeg = blockIdx.z * kspan;
+    const int nk = kspan / BK;
+    const int ksteps = p.K / 16;
+    const T* A = (const T*)p.A;
+    const T* B = (const T*)p.B;
+
+    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) tile_row_scales(p, m0, rs, NT);
+
+    CT ra[AL], rb[BL];
+    auto gload = [&](int kt) {
+        const int k0 = kbeg + kt * BK;
+#pragma unroll
+        for (int i = 0; i < AL; ++i) {
+            int q = tid + i * NT, r = q / CPR, c = q % CPR;
+            int gm = m0 + r;
+            const bool ok = gm < p.M;
+            ra[i] = load_masked(A + (long long)(ok ? gm : 0) * p.lda + k0 + c * 8, ok);
+        }
+#pragma unroll
+        for (int i = 0; i < BL; ++i) {
+            int q = tid + i * NT, bq = q / 64, w = q % 64;
+            int rbk = bq / KB16, kb = bq % KB16;
+            int gn = n0 + 32 * rbk;
+            const bool ok = gn < p.Npad;
+            rb[i] = load_masked(B + ((long long)((ok ? gn : 0) / 32) * ksteps + k0 / 16 + kb) * 512 + w * 8, ok);
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) {
+            int q = tid + i * NT, r = q / CPR, c = q % CPR;
+            *(CT*)(&As[buf][r * BK + ((c ^ (r % CPR)) * 8)]) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < BL; ++i) *(CT*)(&Bs[buf][(tid + i * NT) * 8]) = rb[i];
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = zero_vec<f32x16>();
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int c = 2 * s + hh;
+            CT a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int r = wm * 128 + i * 32 + l32;
+                a[i] = *(const CT*)(&As[buf][r * BK + ((c ^ (r % CPR)) * 8)]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                b[j] = *(const CT*)(&Bs[buf][((wn * 4 + j) * KB16 + s) * 512 + l32 * 16 + 8 * hh]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mma32(a[i], b[j], acc[i][j]);
+        }
+        if (kt + 1 < nk) sstore(buf ^ 1);
+        __syncthreads();
+    }
+    tile_epilogue<T, EPI>(p, acc, m0, n0, tn, rs, red);
+}
+
+template <int EPI>
+static hipError_t launch_e(DType dt, const GemmArgs& a, hipStream_t st) {
+    dim3 grid(((a.N + TBN - 1) / TBN) * ((a.M + TBM - 1) / TBM), 1, a.k_split);
+    if (dt == BF16) {
+        if (a.k_split != 1 || a.K % 32) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gemm_bf16_kernel<EPI>), grid, dim3(256), 0, st, a);
     } else {
-        constexpr int BM = 64, BN = 128;
-        dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, a.k_split);
-        hipLaunchKernelGGL((gemm_kernel<T, BM, BN, 2, 2, EPI>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((gemm_f32_kernel<EPI>), grid, dim3(256), 0, st, a);
     }
     return hipGetLastError();
 }
 
-int gemm_tile_n(GemmTile t) { return t == GEMM_BIG ? 256 : 128; }
-int gemm_tile_k(DType dt) { return dt == BF16 ? KT<bf16>::BK : KT<float>::BK; }
+int gemm_tile_n() { return TBN; }
+int gemm_tile_k(DType dt) { return dt == BF16 ? 32 : KT<float>::BK; }
 
-template <typename T>
-static hipError_t launch_dt(GemmTile tile, Epi epi, const GemmArgs& a, hipStream_t st) {
+hipError_t launch_gemm(DType dt, Epi epi, const GemmArgs& a, hipStream_t st) {
+    if (a.M < 1 || a.N < 1 || a.Npad < a.N || a.Npad % 32) return hipErrorInvalidValue;
     switch (epi) {
-        case EPI_STORE: return launch_t<T, EPI_STORE>(tile, a, st);
-        case EPI_RELU2: return launch_t<T, EPI_RELU2>(tile, a, st);
-        case EPI_RESID: return launch_t<T, EPI_RESID>(tile, a, st);
-        case EPI_SOFTCAP: return launch_t<T, EPI_SOFTCAP>(tile, a, st);
+        case EPI_STORE: return launch_e<EPI_STORE>(dt, a, st);
+        case EPI_RELU2: return launch_e<EPI_RELU2>(dt, a, st);
+        case EPI_RESID: return launch_e<EPI_RESID>(dt, a, st);
+        case EPI_SOFTCAP: return launch_e<EPI_SOFTCAP>(dt, a, st);
+        default: return hipErrorInvalidValue;
     }
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_gemm(DType dt, GemmTile tile, Epi epi, const GemmArgs& a, hipStream_t st) {
-    return dt == BF16 ? launch_dt<bf16>(tile, epi, a, st) : launch_dt<float>(tile, epi, a, st);
 }
 
 }  // namespace nc

@@ -1,0 +1,193 @@
+// Decode projections: C[M, N] = A[M, K] W[N, K]^T for the few rows of one decode step
+// (M = batch <= 128), with the elementwise epilogues of the layer fused.
+//
+// In decode the weights are read once per step and dominate the traffic, so this kernel is
+// built to stream W.  A workgroup owns 32 output columns and all M rows; its waves split K,
+// and each wave loads its W and A operands straight from memory into registers (no LDS
+// staging): the weights are stored MFMA-blocked, so one 16-deep step's W operand is a
+// contiguous 1 KB block, and loads run two groups of steps ahead of the MFMAs.  The eight partial tiles are summed in LDS in a fixed order
+// (deterministic, and no communication between workgroups, whose L2 caches are not
+// coherent with each other), then each wave finishes whole rows:
+//   STORE   raw fp32 product                              (QKV; finished by qkv_post)
+//   RELU2   relu(r_m c)^2 -> dtype                        (MLP up-projection)
+//   RESID   x += c, dtype copy of x, per-row sum of x^2 over the 32 columns
+//   SOFTCAP cap tanh(r_m c / cap) -> fp32 logits          (LM head)
+// with r_m = 1/sqrt(mean(x_m^2) + eps) the parameter-free RMSNorm folded into a row scale.
+// Sources: yelogs.com launch write-up, architecture answer (norms without parameters,
+// ReLU^2, no biases, untied head, logit softcap); apidog.com/th "How to train your own
+// ChatGPT for $50", part 3 (weights cast to the activation dtype for a plain linear map).
+#include "common.h"
+#include "kernels.h"
+
+namespace nc {
+
+constexpr int DEC_BN = 32;  // output columns per workgroup (both tile shapes below)
+
+// Finish one row of the tile: `v` is column n0 + lane of row m (lanes >= tile width hold 0).
+template <typename T, int EPI>
+__device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, int n0, int width,
+                                                 int lane, float v, float r) {
+    const int nn = n0 + lane;
+    const bool ok = lane < width && nn < p.N;
+    const long long o = (long long)m * p.ldo + nn;
+    if (EPI == EPI_STORE) {
+        if (ok) p.out_f32[o] = v;
+    } else if (EPI == EPI_RELU2) {
+        const float t = fmaxf(v * r, 0.f);
+        if (ok) ((T*)p.out_t)[o] = from_f32<T>(t * t);
+    } else if (EPI == EPI_SOFTCAP) {
+        if (ok) p.out_f32[o] = p.cap * tanh_f32(v * r / p.cap);
+    } else {  // EPI_RESID
+        float xn = 0.f;
+        if (ok) {
+            xn = p.out_f32[o] + v;
+            p.out_f32[o] = xn;
+            ((T*)p.out_t)[o] = from_f32<T>(xn);
+        }
+        const float sq = wave_sum(xn * xn);
+        if (lane == 0) p.ss_out[(long long)blockIdx.x * p.ss_stride + m] = sq;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ float dec_row_scale(const DecGemmArgs& p, int m) {
+    float s = 0.f;
+    for (int q = 0; q < p.ss_in_parts; ++q) s += p.ss_in[(long long)q * p.ss_stride + m];
+    return 1.0f / sqrtf(s / (float)p.K + p.eps);
+}
+
+// 32 x 32 MFMA tiles: FM row tiles (M <= 32 FM), 32 columns, NW waves splitting K.
+// Each wave walks its K range in groups of U 16-deep steps with two register buffers: the
+// loads of group g + 1 are issued before the MFMAs of group g, so 2U steps (2U KB of
+// weights per wave for bf16) are in flight.  The weight operand of a step is one
+// contiguous 32x16 block of the blocked layout.
+template <typename T, int FM, int NW, int U, int EPI>
+__global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
+    typedef typename Chunk<T>::type CT;
+    constexpr int BM = 32 * FM, BN = 32, TP = BN + 1;
+    __shared__ float red[NW * BM * TP];
+    __shared__ float rs[BM];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    const int ksteps = p.K / 16;  // K is a multiple of 16 (checked on the host)
+    const int s0 = ksteps * wave / NW, s1 = ksteps * (wave + 1) / NW;
+    const T* A = (const T*)p.A;
+    const T* wb = (const T*)p.W + (long long)(n0 / 32) * ksteps * 512 + l32 * 16 + 8 * hh;
+    const T* arow[FM];
+    bool mok[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + 32 * i + l32;
+        mok[i] = m < p.M;
+        arow[i] = A + (long long)(mok[i] ? m : 0) * p.lda + 8 * hh;
+    }
+
+    f32x16 acc[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[i] = zero_vec<f32x16>();
+    CT wf0[U], wf1[U], af0[U][FM], af1[U][FM];
+    // Loads are unconditional (addresses clamped into valid memory); rows past M are zeroed
+    // with a bit mask and steps past the wave's range (a wave-uniform condition) with a
+    // select, so no load sits behind a divergent branch.
+    auto load = [&](CT (&wf)[U], CT (&af)[U][FM], int sb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = sb + u;
+            const bool ok = s < s1;
+            const int sc = ok ? s : s1 - 1;
+            wf[u] = load_masked(wb + (long long)sc * 512, ok);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[u][i] = load_masked(arow[i] + sc * 16, ok && mok[i]);
+        }
+    };
+    auto mma = [&](CT (&wf)[U], CT (&af)[U][FM]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < FM; ++i) acc[i] = mma32(af[u][i], wf[u], acc[i]);
+    };
+    if (s1 > s0) load(wf0, af0, s0);
+    for (int sb = s0; sb < s1; sb += 2 * U) {
+        load(wf1, af1, sb + U);
+        mma(wf0, af0);
+        if (sb + U >= s1) break;
+        load(wf0, af0, sb + 2 * U);
+        mma(wf1, af1);
+    }
+
+    float* mine = red + wave * BM * TP;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            mine[(32 * i + 8 * (r / 4) + 4 * hh + (r % 4)) * TP + l32] = acc[i][r];
+    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP)
+        for (int r = tid; r < BM; r += NW * 64) rs[r] = (m0 + r < p.M) ? dec_row_scale<T>(p, m0 + r) : 1.f;
+    __syncthreads();
+    const int rows = min(BM, p.M - m0);
+    for (int e = tid; e < rows * BN; e += NW * 64) {
+        const int r = e / BN, c = e % BN;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sum += red[w * BM * TP + r * TP + c];
+        red[r * TP + c] = sum;
+    }
+    __syncthreads();
+    for (int ml = wave; ml < rows; ml += NW)
+        dec_row_epilogue<T, EPI>(p, m0 + ml, n0, BN, lane, lane < BN ? red[ml * TP + lane] : 0.f,
+                                 (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) ? rs[ml] : 1.f);
+}
+
+// Launch shape.  `variant` picks alternative (waves, steps-in-flight) choices for tuning.
+template <typename T, int EPI>
+static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant) {
+    const unsigned gx = (a.N + DEC_BN - 1) / DEC_BN;
+    const int fm = a.M <= 32 ? 1 : (a.M <= 64 ? 2 : 4);
+    const unsigned gy = (a.M + 32 * fm - 1) / (32 * fm);
+    dim3 g(gx, gy);
+#define NC_DG(FMV, NWV, UV) hipLaunchKernelGGL((dec_gemm_kernel<T, FMV, NWV, UV, EPI>), g, dim3(NWV * 64), 0, st, a)
+    if (fm == 1) {
+        if (variant == 1) NC_DG(1, 16, 4);
+        else if (variant == 2) NC_DG(1, 8, 8);
+        else if (variant == 3) NC_DG(1, 4, 16);
+        else if (variant == 4) NC_DG(1, 4, 8);
+        else NC_DG(1, 8, 4);
+    } else if (fm == 2) {
+        if (variant == 1) NC_DG(2, 16, 2);
+        else if (variant == 2) NC_DG(2, 4, 8);
+        else if (variant == 3) NC_DG(2, 4, 4);
+        else if (variant == 4) NC_DG(2, 8, 2);
+        else NC_DG(2, 8, 4);
+    } else {
+        if (variant == 1) NC_DG(4, 4, 4);
+        else if (variant == 2) NC_DG(4, 8, 1);
+        else if (variant == 3) NC_DG(4, 4, 2);
+        else if (variant == 4) NC_DG(4, 2, 4);
+        else NC_DG(4, 8, 2);
+    }
+#undef NC_DG
+    return hipGetLastError();
+}
+
+int dec_gemm_tile_n() { return DEC_BN; }
+
+template <typename T>
+static hipError_t dec_dt(Epi epi, const DecGemmArgs& a, hipStream_t st, int variant) {
+    switch (epi) {
+        case EPI_STORE: return dec_t<T, EPI_STORE>(a, st, variant);
+        case EPI_RELU2: return dec_t<T, EPI_RELU2>(a, st, variant);
+        case EPI_RESID: return dec_t<T, EPI_RESID>(a, st, variant);
+        case EPI_SOFTCAP: return dec_t<T, EPI_SOFTCAP>(a, st, variant);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t st, int variant) {
+    if (a.M < 1 || a.M > 128 || a.K % 16) return hipErrorInvalidValue;
+    return dt == BF16 ? dec_dt<bf16>(epi, a, st, variant) : dec_dt<float>(epi, a, st, variant);
+}
+
+}  // namespace nc

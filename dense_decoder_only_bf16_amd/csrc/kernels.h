@@ -16,10 +16,18 @@ enum DType { F32 = 0, BF16 = 1 };
 //   SOFTCAP out_f32[m][n] = cap tanh(r_m C / cap)
 enum Epi { EPI_STORE = 0, EPI_RELU2 = 1, EPI_RESID = 2, EPI_SOFTCAP = 3 };
 
+// Weight layout used by every projection: MFMA-blocked [Npad/32][K/16][32][16], i.e.
+// element (n, k) of an [N][K] nn.Linear weight sits at
+//   ((n / 32) * (K / 16) + k / 16) * 512 + (n % 32) * 16 + k % 16,
+// with rows n >= N (up to Npad = N rounded up to 32) zero.  A 32x16 block is the operand
+// of one 16-deep MFMA step for one wave.
+__host__ __device__ inline long long blocked_elems(int N, int K) { return (long long)((N + 31) / 32) * 32 * K; }
+hipError_t launch_repack(DType dt, const void* src, void* dst, int N, int K, hipStream_t st);
+
 struct GemmArgs {
     const void* A;  // [M][lda] dtype, K contiguous
-    const void* B;  // [N][ldb] dtype, K contiguous (torch.nn.Linear weight layout)
-    int M, N, K, lda, ldb;
+    const void* B;  // blocked weight (see above), Npad rows
+    int M, N, K, lda, Npad;
     int k_split;        // grid z; K / k_split must be a multiple of the K tile
     float* out_f32;     // STORE / SOFTCAP output, RESID residual x (fp32)
     void* out_t;        // RELU2 output, RESID dtype copy of x
@@ -31,19 +39,25 @@ struct GemmArgs {
     float eps, cap;
 };
 
-// Tile shapes: GEMM_BIG is for M in the thousands (prefill), GEMM_SKINNY for M <= 64.
-enum GemmTile { GEMM_BIG = 0, GEMM_SKINNY = 1 };
-int gemm_tile_n(GemmTile t);   // N extent of one tile (ss_out parts = ceil(N / tile_n))
+// Prefill product (M in the thousands): 256 x 256 tiles.
+int gemm_tile_n();             // N extent of one tile (ss_out parts = ceil(N / tile_n))
 int gemm_tile_k(DType dt);     // K granularity
-hipError_t launch_gemm(DType dt, GemmTile tile, Epi epi, const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm(DType dt, Epi epi, const GemmArgs& a, hipStream_t st);
 
-// Row-wise finish of a K-split product: sums `splits` fp32 slices part[z][m][n] (slice
-// stride z_stride) and applies the RELU2 / RESID / SOFTCAP epilogue of one full row per
-// block.  RESID writes ss_out[m] (one part).
-hipError_t launch_finish(DType dt, Epi epi, const float* part, int splits, long long z_stride,
-                         int M, int N, float* out_f32, void* out_t, int ldo,
-                         const float* ss_in, int ss_in_parts, int ss_stride, int norm_dim,
-                         float* ss_out, float eps, float cap, hipStream_t st);
+// Decode projection (M <= 128 rows, K a multiple of 16) with the epilogue fused
+// (STORE / RELU2 / RESID / SOFTCAP).  Tiles are dec_gemm_tile_n() columns; RESID writes
+// ss_out[tile_n * ss_stride + m] (parts = ceil(N / tile_n)).
+struct DecGemmArgs {
+    const void* A; int lda;     // [M][lda] dtype
+    const void* W;              // blocked weight, Npad = N rounded up to 32 rows
+    int M, N, K;
+    float* out_f32; void* out_t; int ldo;
+    const float* ss_in; int ss_in_parts, ss_stride;
+    float* ss_out;
+    float eps, cap;
+};
+int dec_gemm_tile_n();
+hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t st, int variant = 0);
 
 // x[m] = norm(wte[tok[m]]) (fp32), act[m] = dtype copy, ss[m] = sum(x^2).
 hipError_t launch_embed(DType dt, const int32_t* tok, int M, const void* wte, int vocab, int d,
@@ -73,8 +87,9 @@ hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st);
 hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, const void* vtc,
                                void* y, int B, int T, int H, int S, hipStream_t st);
 
-// Decode attention, one query per row at position lens[b] (keys 0..lens[b]):
-// split phase writes per-chunk partial (max, sum, o) and the combine phase merges them.
+// Decode attention, one query per row at position lens[b] (keys 0..lens[b]): the split
+// kernel reduces each chunk of keys to a partial softmax state, the combine kernel merges a
+// row's partials into y.
 int attn_decode_chunk();
 hipError_t launch_attn_decode(DType dt, int hd, const void* q, const void* kc, const void* vtc,
                               const int32_t* lens, void* y, float* part, int B, int H, int S,

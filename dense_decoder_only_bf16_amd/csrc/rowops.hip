@@ -1,5 +1,5 @@
-// Row-wise kernels: embedding + norm, the QKV finish (RoPE, QK-norm, KV-cache write),
-// the K-split finish of decode projections, greedy argmax and small cache utilities.
+// Row-wise kernels: embedding + norm, the QKV finish of prefill (RoPE, QK-norm, KV-cache
+// write), greedy argmax and small cache utilities.
 //
 // RMSNorm has no learnable parameters and sits after the token embedding (yelogs.com
 // launch write-up, architecture answer); RoPE with precomputed tables (geoz.com.cn
@@ -126,77 +126,6 @@ hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ K-split finish --
-template <typename T, int EPI>
-__global__ __launch_bounds__(256) void finish_kernel(const float* __restrict__ part, int splits,
-                                                     long long zs, int M, int N,
-                                                     float* __restrict__ out_f32, T* __restrict__ out_t,
-                                                     int ldo, const float* __restrict__ ss_in,
-                                                     int ss_parts, int ss_stride, int norm_dim,
-                                                     float* __restrict__ ss_out, float eps, float cap) {
-    __shared__ float red[4];
-    const int m = blockIdx.x;
-    const int tid = threadIdx.x;
-    float r = 1.f;
-    if (EPI != EPI_RESID) {
-        float s = 0.f;
-        for (int q = 0; q < ss_parts; ++q) s += ss_in[(long long)q * ss_stride + m];
-        r = 1.0f / sqrtf(s / (float)norm_dim + eps);
-    }
-    float sq = 0.f;
-    for (int n = tid; n < N; n += 256) {
-        float v = 0.f;
-        for (int z = 0; z < splits; ++z) v += part[(long long)z * zs + (long long)m * N + n];
-        long long o = (long long)m * ldo + n;
-        if (EPI == EPI_RELU2) {
-            float t = fmaxf(v * r, 0.f);
-            out_t[o] = from_f32<T>(t * t);
-        } else if (EPI == EPI_SOFTCAP) {
-            out_f32[o] = cap * tanh_f32(v * r / cap);
-        } else {
-            float xn = out_f32[o] + v;
-            out_f32[o] = xn;
-            out_t[o] = from_f32<T>(xn);
-            sq += xn * xn;
-        }
-    }
-    if (EPI == EPI_RESID) {
-        sq = wave_sum(sq);
-        if ((tid & 63) == 0) red[tid >> 6] = sq;
-        __syncthreads();
-        if (tid == 0) ss_out[m] = red[0] + red[1] + red[2] + red[3];
-    }
-}
-
-template <typename T>
-static hipError_t finish_t(Epi epi, const float* part, int splits, long long zs, int M, int N,
-                           float* out_f32, void* out_t, int ldo, const float* ss_in, int ss_parts,
-                           int ss_stride, int norm_dim, float* ss_out, float eps, float cap,
-                           hipStream_t st) {
-    dim3 grid(M);
-#define NC_FIN(E)                                                                             \
-    hipLaunchKernelGGL((finish_kernel<T, E>), grid, dim3(256), 0, st, part, splits, zs, M, N, \
-                       out_f32, (T*)out_t, ldo, ss_in, ss_parts, ss_stride, norm_dim, ss_out,  \
-                       eps, cap)
-    if (epi == EPI_RELU2) NC_FIN(EPI_RELU2);
-    else if (epi == EPI_SOFTCAP) NC_FIN(EPI_SOFTCAP);
-    else if (epi == EPI_RESID) NC_FIN(EPI_RESID);
-    else return hipErrorInvalidValue;
-#undef NC_FIN
-    return hipGetLastError();
-}
-
-hipError_t launch_finish(DType dt, Epi epi, const float* part, int splits, long long z_stride,
-                         int M, int N, float* out_f32, void* out_t, int ldo, const float* ss_in,
-                         int ss_in_parts, int ss_stride, int norm_dim, float* ss_out, float eps,
-                         float cap, hipStream_t st) {
-    if (dt == BF16)
-        return finish_t<bf16>(epi, part, splits, z_stride, M, N, out_f32, out_t, ldo, ss_in,
-                              ss_in_parts, ss_stride, norm_dim, ss_out, eps, cap, st);
-    return finish_t<float>(epi, part, splits, z_stride, M, N, out_f32, out_t, ldo, ss_in,
-                           ss_in_parts, ss_stride, norm_dim, ss_out, eps, cap, st);
-}
-
 // ------------------------------------------------------------------ argmax ----------
 // Lowest index wins ties; NaN never wins against a number.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
@@ -205,17 +134,30 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-__global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ logits, int V,
-                                                     int32_t* __restrict__ out) {
-    __shared__ float sv[4];
-    __shared__ int si[4];
+// One 1024-thread workgroup per row; 16-byte loads when the row allows it.
+__global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ logits, int V,
+                                                      int32_t* __restrict__ out) {
+    __shared__ float sv[16];
+    __shared__ int si[16];
     const int b = blockIdx.x, tid = threadIdx.x;
     const float* row = logits + (long long)b * V;
     float bv = __builtin_nanf("");
     int bi = 0x7fffffff;
-    for (int i = tid; i < V; i += 256) {
-        float v = row[i];
-        if (better(v, i, bv, bi)) { bv = v; bi = i; }
+    const bool vec = ((V & 3) == 0) && ((((uintptr_t)row) & 15) == 0);
+    if (vec) {
+        const f32x4* r4 = (const f32x4*)row;
+        const int n4 = V >> 2;
+        for (int i = tid; i < n4; i += 1024) {
+            f32x4 v = r4[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (better(v[e], 4 * i + e, bv, bi)) { bv = v[e]; bi = 4 * i + e; }
+        }
+    } else {
+        for (int i = tid; i < V; i += 1024) {
+            float v = row[i];
+            if (better(v, i, bv, bi)) { bv = v; bi = i; }
+        }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -226,14 +168,45 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ l
     if ((tid & 63) == 0) { sv[tid >> 6] = bv; si[tid >> 6] = bi; }
     __syncthreads();
     if (tid == 0) {
-        for (int w = 1; w < 4; ++w)
+        for (int w = 1; w < 16; ++w)
             if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
         out[b] = (bi == 0x7fffffff) ? 0 : bi;
     }
 }
 
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st) {
-    hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(256), 0, st, logits, V, out);
+    hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(1024), 0, st, logits, V, out);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ weight repack ---
+// [N][K] row-major -> MFMA-blocked [Npad/32][K/16][32][16]; one thread per 8 elements.
+template <typename T>
+__global__ __launch_bounds__(256) void repack_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                     int N, int K) {
+    typedef typename Chunk<T>::type CT;
+    const long long c = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long total = blocked_elems(N, K) / 8;
+    if (c >= total) return;
+    const long long blk = c / 64;
+    const int w = (int)(c % 64);
+    const int ksteps = K / 16;
+    const long long rbk = blk / ksteps;
+    const int kb = (int)(blk % ksteps);
+    const long long row = rbk * 32 + w / 2;
+    const int k = kb * 16 + (w % 2) * 8;
+    CT v = zero_vec<CT>();
+    if (row < N) v = *(const CT*)(src + row * K + k);
+    *(CT*)(dst + c * 8) = v;
+}
+
+hipError_t launch_repack(DType dt, const void* src, void* dst, int N, int K, hipStream_t st) {
+    const long long total = blocked_elems(N, K) / 8;
+    dim3 grid((unsigned)((total + 255) / 256));
+    if (dt == BF16)
+        hipLaunchKernelGGL(repack_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)src, (bf16*)dst, N, K);
+    else
+        hipLaunchKernelGGL(repack_kernel<float>, grid, dim3(256), 0, st, (const float*)src, (float*)dst, N, K);
     return hipGetLastError();
 }
 

@@ -8,14 +8,20 @@
 //   O product  + residual epilogue (x += ., dtype copy of x, per-row sum of squares)
 //   FC product + norm scale + ReLU^2 epilogue
 //   PROJ product + residual epilogue
-// then the LM head with norm scale and softcap.  Prefill uses the large MFMA tile with the
-// epilogues fused; decode (M = batch rows) uses the skinny tile with K split across
-// workgroups and a row-wise finish kernel that applies the same epilogues.
+// then the LM head with norm scale and softcap.  Prefill uses the 256x256 MFMA tile with
+// the epilogues fused (the QKV finish is a separate row kernel).  Decode (M = batch rows)
+// uses the weight-streaming decode product (K split over the waves of one workgroup) with
+// the elementwise epilogues fused and the QKV finish as a row kernel; the whole decode step is
+// captured once per (token buffer, logit buffer) pair as a HIP graph and replayed.
+// No kernel communicates with other workgroups of the same launch: the L2 caches of the
+// chip's dies are not coherent with each other, so a device-wide fence costs a write-back
+// and invalidation of the L2; reductions across workgroups are separate launches instead.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -82,28 +88,38 @@ struct nc_kv {
     void* q = nullptr;        // [M][H][hd]
     void* y = nullptr;        // [M][H hd] attention output
     void* u = nullptr;        // [M][d_ff] MLP hidden
-    float* gpart = nullptr;   // [splits][M][N] K-split partial products (decode)
-    long long gpart_elems = 0;
     float* apart = nullptr;   // decode attention partials
     long long apart_elems = 0;
+    // decode step captured as a HIP graph, keyed by the caller's token/logit buffers
+    bool use_graph = true;
+    hipStream_t cap_stream = nullptr;
+    struct Graph {
+        const void* tokens;
+        const void* logits;
+        hipGraphExec_t exec;
+    };
+    std::vector<Graph> graphs;
 };
 
 namespace {
 
+void drop_graphs(nc_kv* kv) {
+    for (auto& g : kv->graphs) (void)hipGraphExecDestroy(g.exec);
+    kv->graphs.clear();
+}
+
 void ws_free(nc_kv* kv) {
-    void* ptrs[] = {kv->x, kv->act, kv->ss_a, kv->ss_b, kv->qkv, kv->q, kv->y, kv->u, kv->gpart, kv->apart};
+    drop_graphs(kv);  // captured graphs point into the workspace
+    void* ptrs[] = {kv->x, kv->act, kv->ss_a, kv->ss_b, kv->qkv, kv->q, kv->y, kv->u, kv->apart};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     kv->x = nullptr; kv->act = nullptr; kv->ss_a = nullptr; kv->ss_b = nullptr; kv->qkv = nullptr;
-    kv->q = nullptr; kv->y = nullptr; kv->u = nullptr; kv->gpart = nullptr; kv->apart = nullptr;
+    kv->q = nullptr; kv->y = nullptr; kv->u = nullptr; kv->apart = nullptr;
     kv->cap_m = 0;
-    kv->gpart_elems = 0;
     kv->apart_elems = 0;
 }
 
-constexpr int kMaxSplit = 16;
-
-// Grow the workspace to hold M token rows (and decode partials when `decode`).
+// Grow the workspace to hold M token rows.
 nc_status ws_ensure(nc_kv* kv, long long M) {
     if (M <= kv->cap_m) return NC_OK;
     const nc_config& c = kv->m->cfg;
@@ -112,9 +128,9 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
     ws_free(kv);
     const long long d = c.d_model, hq = (long long)c.n_head * c.head_dim;
     const long long nqkv = (long long)(c.n_head + 2) * c.head_dim;
-    const long long split_rows = std::min<long long>(M, 128);  // K-split only for small M
-    kv->ss_parts_max = (c.d_model + 127) / 128;
-    const long long qkv_elems = std::max(M * nqkv, kMaxSplit * split_rows * nqkv);
+    // row statistics come in parts of one per output tile of the producing product
+    kv->ss_parts_max = (c.d_model + dec_gemm_tile_n() - 1) / dec_gemm_tile_n();
+    const long long qkv_elems = M * nqkv;
 #define WS_ALLOC(ptr, bytes) HIP_TRY(hipMalloc((void**)&(ptr), (size_t)(bytes)))
     WS_ALLOC(kv->x, M * d * 4);
     WS_ALLOC(kv->act, M * d * es);
@@ -124,8 +140,6 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
     WS_ALLOC(kv->q, M * hq * es);
     WS_ALLOC(kv->y, M * hq * es);
     WS_ALLOC(kv->u, M * c.d_ff * es);
-    kv->gpart_elems = kMaxSplit * split_rows * std::max<long long>(d, c.d_ff);
-    WS_ALLOC(kv->gpart, kv->gpart_elems * 4);
     const int max_chunks = (kv->S + attn_decode_chunk() - 1) / attn_decode_chunk();
     kv->apart_elems = (long long)kv->B * max_chunks * 16 * (c.head_dim + 2);
     WS_ALLOC(kv->apart, kv->apart_elems * 4);
@@ -175,45 +189,66 @@ nc_status launched(hipError_t e, const char* what) {
         if (s_ != NC_OK) return s_;                 \
     } while (0)
 
-// Largest K split <= want that divides K into multiples of the K tile.
-int pick_split(int K, int kt, int want) {
-    int tiles = K / kt;
-    int s = std::max(1, std::min(want, tiles));
-    while (s > 1 && tiles % s) --s;
-    return s;
+nc_status decode_gemm(nc_kv* kv, Epi epi, const DecGemmArgs& a, hipStream_t st) {
+    LAUNCH(launch_dec_gemm(kv->m->dt, epi, a, st));
+    return NC_OK;
 }
 
-// One decode projection: skinny tile, K split sized to fill the GPU, then the epilogue.
-nc_status decode_gemm(nc_kv* kv, Epi epi, const void* A, int lda, const void* W, int N, int K,
-                      float* out_f32, void* out_t, int ldo, const float* ss_in, int ss_parts,
-                      float* ss_out, hipStream_t st, float* qkv_out = nullptr, int* split_out = nullptr) {
-    nc_model* m = kv->m;
-    const int M = kv->B;
-    const int tn = gemm_tile_n(GEMM_SKINNY);
-    const int base = ((N + tn - 1) / tn) * ((M + 31) / 32);
-    const int want = std::max(1, std::min(kMaxSplit, 512 / std::max(1, base)));
-    const int split = pick_split(K, gemm_tile_k(m->dt), want);
-    GemmArgs a{};
-    a.A = A; a.B = W; a.M = M; a.N = N; a.K = K; a.lda = lda; a.ldb = K;
-    a.k_split = split; a.ldo = N; a.eps = m->cfg.norm_eps; a.cap = m->cfg.softcap;
-    if (epi == EPI_STORE) {  // QKV: raw partials consumed by qkv_post
-        a.out_f32 = qkv_out;
-        a.z_stride = (long long)M * N;
-        LAUNCH(launch_gemm(m->dt, GEMM_SKINNY, EPI_STORE, a, st));
-        *split_out = split;
-        return NC_OK;
+// Enqueue one decode step (everything after the host-side checks) on `st`.
+nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* logits, hipStream_t st) {
+    const nc_config& c = m->cfg;
+    const int B = kv->B;
+    const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab;
+    const int nqkv = (H + 2) * hd;
+    const size_t per_layer = (size_t)B * kv->S * hd * m->esz;
+    const int max_chunks = (kv->S + attn_decode_chunk() - 1) / attn_decode_chunk();
+    const int parts_d = (d + dec_gemm_tile_n() - 1) / dec_gemm_tile_n();
+    const int ss = (int)kv->cap_m;
+    nc_status s;
+
+    LAUNCH(launch_embed(m->dt, tokens, B, m->wte, V, d, c.norm_eps, kv->x, kv->act, kv->ss_a, st));
+    int ss_a_parts = 1;
+    for (int l = 0; l < c.n_layer; ++l) {
+        const nc_model::Layer& L = m->layers[l];
+        void* kc = (char*)kv->kcache + l * per_layer;
+        void* vtc = (char*)kv->vcache + l * per_layer;
+        DecGemmArgs a{};
+        a.M = B; a.eps = c.norm_eps; a.cap = c.softcap; a.ss_stride = ss;
+        // QKV raw product, then norm scale + RoPE + QK-norm + cache write at lens[b]
+        a.A = kv->act; a.lda = d; a.W = L.wqkv; a.N = nqkv; a.K = d;
+        a.out_f32 = kv->qkv; a.ldo = nqkv;
+        if ((s = decode_gemm(kv, EPI_STORE, a, st)) != NC_OK) return s;
+        QkvPostArgs qa{};
+        qa.part = kv->qkv; qa.splits = 1; qa.z_stride = 0; qa.M = B; qa.T = 1; qa.H = H; qa.hd = hd;
+        qa.ss_in = kv->ss_a; qa.ss_in_parts = ss_a_parts; qa.ss_stride = ss; qa.norm_dim = d;
+        qa.lens = kv->lens_dev; qa.rope_cos = m->rope_cos; qa.rope_sin = m->rope_sin;
+        qa.q = kv->q; qa.kc = kc; qa.vtc = vtc; qa.S = kv->S; qa.eps = c.norm_eps;
+        LAUNCH(launch_qkv_post(m->dt, qa, st));
+        LAUNCH(launch_attn_decode(m->dt, hd, kv->q, kc, vtc, kv->lens_dev, kv->y, kv->apart, B, H,
+                                  kv->S, max_chunks, st));
+        // O + residual
+        DecGemmArgs o = a;
+        o.A = kv->y; o.lda = H * hd; o.W = L.wo; o.N = d; o.K = H * hd;
+        o.out_f32 = kv->x; o.out_t = kv->act; o.ldo = d; o.ss_out = kv->ss_b;
+        if ((s = decode_gemm(kv, EPI_RESID, o, st)) != NC_OK) return s;
+        // FC + norm scale + relu^2
+        DecGemmArgs f = a;
+        f.A = kv->act; f.lda = d; f.W = L.wfc; f.N = F; f.K = d;
+        f.out_t = kv->u; f.ldo = F; f.ss_in = kv->ss_b; f.ss_in_parts = parts_d;
+        if ((s = decode_gemm(kv, EPI_RELU2, f, st)) != NC_OK) return s;
+        // PROJ + residual
+        DecGemmArgs pj = a;
+        pj.A = kv->u; pj.lda = F; pj.W = L.wproj; pj.N = d; pj.K = F;
+        pj.out_f32 = kv->x; pj.out_t = kv->act; pj.ldo = d; pj.ss_out = kv->ss_a;
+        if ((s = decode_gemm(kv, EPI_RESID, pj, st)) != NC_OK) return s;
+        ss_a_parts = parts_d;
     }
-    if (split == 1 && epi == EPI_SOFTCAP) {
-        a.out_f32 = out_f32; a.ldo = ldo; a.ss_in = ss_in; a.ss_in_parts = ss_parts; a.ss_stride = (int)kv->cap_m;
-        LAUNCH(launch_gemm(m->dt, GEMM_SKINNY, EPI_SOFTCAP, a, st));
-        return NC_OK;
-    }
-    a.out_f32 = kv->gpart;
-    a.z_stride = (long long)M * N;
-    if ((long long)split * M * N > kv->gpart_elems) return fail(NC_ERR_STATE, "decode partial buffer too small");
-    LAUNCH(launch_gemm(m->dt, GEMM_SKINNY, EPI_STORE, a, st));
-    LAUNCH(launch_finish(m->dt, epi, kv->gpart, split, (long long)M * N, M, N, out_f32, out_t, ldo,
-                         ss_in, ss_parts, (int)kv->cap_m, K, ss_out, m->cfg.norm_eps, m->cfg.softcap, st));
+    DecGemmArgs h{};
+    h.M = B; h.eps = c.norm_eps; h.cap = c.softcap; h.ss_stride = ss;
+    h.A = kv->act; h.lda = d; h.W = m->lm; h.N = V; h.K = d;
+    h.out_f32 = logits; h.ldo = V; h.ss_in = kv->ss_a; h.ss_in_parts = ss_a_parts;
+    if ((s = decode_gemm(kv, EPI_SOFTCAP, h, st)) != NC_OK) return s;
+    LAUNCH(launch_lens_add(kv->lens_dev, B, 1, -1, st));
     return NC_OK;
 }
 
@@ -238,6 +273,14 @@ nc_status nc_model_create(const nc_config* cfg, const void* const* weights, nc_m
         int dev = 0;
         s = check_device(&dev);
         if (s != NC_OK) return s;
+        for (int i = 0; i < nw; ++i) {  // kernels read the weights directly: device memory only
+            hipPointerAttribute_t attr;
+            if (hipPointerGetAttributes(&attr, weights[i]) != hipSuccess ||
+                (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)) {
+                (void)hipGetLastError();
+                return fail(NC_ERR_INVALID_ARG, "weight pointer " + std::to_string(i) + " is not device memory");
+            }
+        }
 
         nc_model* m = new nc_model();
         m->cfg = *cfg;
@@ -246,44 +289,47 @@ nc_status nc_model_create(const nc_config* cfg, const void* const* weights, nc_m
         m->device = dev;
         const size_t d = cfg->d_model, hd = cfg->head_dim, H = cfg->n_head, V = cfg->vocab, F = cfg->d_ff;
         const size_t es = m->esz;
+        // projection weights are stored MFMA-blocked (kernels.h); the embedding stays row-major
         const size_t sz_emb = align_up(V * d * es, 256);
-        const size_t sz_qkv = align_up((H + 2) * hd * d * es, 256);
-        const size_t sz_o = align_up(d * H * hd * es, 256);
-        const size_t sz_fc = align_up(F * d * es, 256);
-        const size_t total = 2 * sz_emb + cfg->n_layer * (sz_qkv + sz_o + 2 * sz_fc);
+        const size_t sz_qkv = align_up((size_t)blocked_elems((int)((H + 2) * hd), (int)d) * es, 256);
+        const size_t sz_o = align_up((size_t)blocked_elems((int)d, (int)(H * hd)) * es, 256);
+        const size_t sz_fc = align_up((size_t)blocked_elems((int)F, (int)d) * es, 256);
+        const size_t sz_pj = align_up((size_t)blocked_elems((int)d, (int)F) * es, 256);
+        const size_t sz_lm = align_up((size_t)blocked_elems((int)V, (int)d) * es, 256);
+        const size_t total = sz_emb + sz_lm + cfg->n_layer * (sz_qkv + sz_o + sz_fc + sz_pj);
         hipError_t e = hipMalloc(&m->arena, total);
         if (e != hipSuccess) {
             delete m;
             return fail(NC_ERR_OOM, std::string("weight arena: ") + hipGetErrorString(e));
         }
         char* p = (char*)m->arena;
-        auto cp = [&](void* dst, const void* src, size_t bytes) {
-            return hipMemcpy(dst, src, bytes, hipMemcpyDefault);
-        };
-        hipError_t ce = cp(p, weights[0], V * d * es);
+        hipError_t ce = hipMemcpy(p, weights[0], V * d * es, hipMemcpyDefault);
         m->wte = p;
         p += sz_emb;
         m->layers.resize(cfg->n_layer);
+        const size_t qrows_bytes = (size_t)blocked_elems((int)(H * hd), (int)d) * es;  // H*hd is a multiple of 32
+        const size_t krows_bytes = (size_t)blocked_elems((int)hd, (int)d) * es;
         for (int l = 0; l < cfg->n_layer && ce == hipSuccess; ++l) {
             const void* const* w = weights + 1 + 6 * l;
             nc_model::Layer& L = m->layers[l];
             L.wqkv = p;
-            ce = cp(p, w[0], H * hd * d * es);
-            if (ce == hipSuccess) ce = cp(p + H * hd * d * es, w[1], hd * d * es);
-            if (ce == hipSuccess) ce = cp(p + (H + 1) * hd * d * es, w[2], hd * d * es);
+            ce = launch_repack(m->dt, w[0], p, (int)(H * hd), (int)d, 0);
+            if (ce == hipSuccess) ce = launch_repack(m->dt, w[1], p + qrows_bytes, (int)hd, (int)d, 0);
+            if (ce == hipSuccess) ce = launch_repack(m->dt, w[2], p + qrows_bytes + krows_bytes, (int)hd, (int)d, 0);
             p += sz_qkv;
             L.wo = p;
-            if (ce == hipSuccess) ce = cp(p, w[3], d * H * hd * es);
+            if (ce == hipSuccess) ce = launch_repack(m->dt, w[3], p, (int)d, (int)(H * hd), 0);
             p += sz_o;
             L.wfc = p;
-            if (ce == hipSuccess) ce = cp(p, w[4], F * d * es);
+            if (ce == hipSuccess) ce = launch_repack(m->dt, w[4], p, (int)F, (int)d, 0);
             p += sz_fc;
             L.wproj = p;
-            if (ce == hipSuccess) ce = cp(p, w[5], d * F * es);
-            p += sz_fc;
+            if (ce == hipSuccess) ce = launch_repack(m->dt, w[5], p, (int)d, (int)F, 0);
+            p += sz_pj;
         }
-        if (ce == hipSuccess) ce = cp(p, weights[nw - 1], V * d * es);
+        if (ce == hipSuccess) ce = launch_repack(m->dt, weights[nw - 1], p, (int)V, (int)d, 0);
         m->lm = p;
+        if (ce == hipSuccess) ce = hipDeviceSynchronize();
         // RoPE tables: angle p * base^(-2i/hd), evaluated in double, stored fp32.
         const size_t half = hd / 2, S = cfg->max_seq;
         std::vector<float> hc(S * half), hs(S * half);
@@ -335,6 +381,8 @@ nc_status nc_kv_create(nc_model* m, int32_t batch, int32_t max_seq, nc_kv** out)
         kv->max_seq = max_seq;
         kv->S = (int)align_up(max_seq, 64);
         kv->lens_host.assign(batch, 0);
+        const char* ng = std::getenv("NC_DECODE_GRAPH");
+        kv->use_graph = !(ng && ng[0] == '0');
         const nc_config& c = m->cfg;
         const size_t bytes = (size_t)c.n_layer * batch * kv->S * c.head_dim * m->esz;
         hipError_t e = hipMalloc(&kv->kcache, bytes);
@@ -366,6 +414,7 @@ void nc_kv_free(nc_kv* kv) {
     if (!kv) return;
     (void)hipDeviceSynchronize();
     ws_free(kv);
+    if (kv->cap_stream) (void)hipStreamDestroy(kv->cap_stream);
     if (kv->kcache) (void)hipFree(kv->kcache);
     if (kv->vcache) (void)hipFree(kv->vcache);
     if (kv->lens_dev) (void)hipFree(kv->lens_dev);
@@ -425,7 +474,7 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
         const nc_config& c = m->cfg;
         const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab;
         const int nqkv = (H + 2) * hd;
-        const int tn = gemm_tile_n(GEMM_BIG);
+        const int tn = gemm_tile_n();
         const int parts_d = (d + tn - 1) / tn;
         const size_t per_layer = (size_t)B * kv->S * hd * m->esz;
         const int Mi = (int)M;
@@ -437,9 +486,9 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             GemmArgs g{};
             g.M = Mi; g.lda = d; g.k_split = 1; g.eps = c.norm_eps; g.cap = c.softcap;
             // QKV raw product
-            g.A = kv->act; g.B = L.wqkv; g.N = nqkv; g.K = d; g.ldb = d;
+            g.A = kv->act; g.B = L.wqkv; g.N = nqkv; g.K = d; g.Npad = nqkv;
             g.out_f32 = kv->qkv; g.ldo = nqkv; g.z_stride = 0;
-            LAUNCH(launch_gemm(m->dt, GEMM_BIG, EPI_STORE, g, st));
+            LAUNCH(launch_gemm(m->dt, EPI_STORE, g, st));
             QkvPostArgs qa{};
             qa.part = kv->qkv; qa.splits = 1; qa.z_stride = 0; qa.M = Mi; qa.T = T; qa.H = H; qa.hd = hd;
             qa.ss_in = kv->ss_a; qa.ss_in_parts = ss_a_parts; qa.ss_stride = (int)kv->cap_m; qa.norm_dim = d;
@@ -449,25 +498,25 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             LAUNCH(launch_qkv_post(m->dt, qa, st));
             LAUNCH(launch_attn_prefill(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->y, B, T, H, kv->S, st));
             // O product + residual
-            g.A = kv->y; g.lda = H * hd; g.B = L.wo; g.N = d; g.K = H * hd; g.ldb = H * hd;
+            g.A = kv->y; g.lda = H * hd; g.B = L.wo; g.N = d; g.K = H * hd; g.Npad = d;
             g.out_f32 = kv->x; g.out_t = kv->act; g.ldo = d; g.ss_out = kv->ss_b; g.ss_stride = (int)kv->cap_m;
-            LAUNCH(launch_gemm(m->dt, GEMM_BIG, EPI_RESID, g, st));
+            LAUNCH(launch_gemm(m->dt, EPI_RESID, g, st));
             // FC + norm + relu^2
-            g.A = kv->act; g.lda = d; g.B = L.wfc; g.N = F; g.K = d; g.ldb = d;
+            g.A = kv->act; g.lda = d; g.B = L.wfc; g.N = F; g.K = d; g.Npad = F;
             g.out_t = kv->u; g.ldo = F; g.ss_in = kv->ss_b; g.ss_in_parts = parts_d; g.ss_stride = (int)kv->cap_m;
-            LAUNCH(launch_gemm(m->dt, GEMM_BIG, EPI_RELU2, g, st));
+            LAUNCH(launch_gemm(m->dt, EPI_RELU2, g, st));
             // PROJ + residual
-            g.A = kv->u; g.lda = F; g.B = L.wproj; g.N = d; g.K = F; g.ldb = F;
+            g.A = kv->u; g.lda = F; g.B = L.wproj; g.N = d; g.K = F; g.Npad = d;
             g.out_f32 = kv->x; g.out_t = kv->act; g.ldo = d; g.ss_out = kv->ss_a; g.ss_stride = (int)kv->cap_m;
-            LAUNCH(launch_gemm(m->dt, GEMM_BIG, EPI_RESID, g, st));
+            LAUNCH(launch_gemm(m->dt, EPI_RESID, g, st));
             ss_a_parts = parts_d;
         }
         if (logits) {
             GemmArgs g{};
-            g.A = kv->act; g.lda = d; g.B = m->lm; g.M = Mi; g.N = V; g.K = d; g.ldb = d; g.k_split = 1;
+            g.A = kv->act; g.lda = d; g.B = m->lm; g.M = Mi; g.N = V; g.K = d; g.Npad = (V + 31) / 32 * 32; g.k_split = 1;
             g.out_f32 = logits; g.ldo = V; g.ss_in = kv->ss_a; g.ss_in_parts = ss_a_parts;
             g.ss_stride = (int)kv->cap_m; g.eps = c.norm_eps; g.cap = c.softcap;
-            LAUNCH(launch_gemm(m->dt, GEMM_BIG, EPI_SOFTCAP, g, st));
+            LAUNCH(launch_gemm(m->dt, EPI_SOFTCAP, g, st));
         }
         LAUNCH(launch_lens_add(kv->lens_dev, B, 0, T, st));
         std::fill(kv->lens_host.begin(), kv->lens_host.end(), T);
@@ -483,44 +532,41 @@ nc_status nc_decode_step(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* k
         if (!m || !tokens || !kv || !logits) return fail(NC_ERR_INVALID_ARG, "NULL argument");
         if (kv->m != m) return fail(NC_ERR_INVALID_ARG, "kv belongs to another model");
         if (B != kv->B) return fail(NC_ERR_INVALID_ARG, "B differs from the cache's batch");
+        if (B > 128) return fail(NC_ERR_UNSUPPORTED, "decode supports at most 128 rows");
         for (int b = 0; b < B; ++b)
             if (kv->lens_host[b] + 1 > kv->max_seq) return fail(NC_ERR_CAPACITY, "a row is full (lens + 1 > max_seq)");
         nc_status s = ws_ensure(kv, B);
         if (s != NC_OK) return s;
         hipStream_t st = (hipStream_t)stream;
-        const nc_config& c = m->cfg;
-        const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab;
-        const int nqkv = (H + 2) * hd;
-        const size_t per_layer = (size_t)B * kv->S * hd * m->esz;
-        const int max_chunks = (kv->S + attn_decode_chunk() - 1) / attn_decode_chunk();
-
-        LAUNCH(launch_embed(m->dt, tokens, B, m->wte, V, d, c.norm_eps, kv->x, kv->act, kv->ss_a, st));
-        for (int l = 0; l < c.n_layer; ++l) {
-            const nc_model::Layer& L = m->layers[l];
-            int split = 1;
-            s = decode_gemm(kv, EPI_STORE, kv->act, d, L.wqkv, nqkv, d, nullptr, nullptr, 0, nullptr, 0,
-                            nullptr, st, kv->qkv, &split);
-            if (s != NC_OK) return s;
-            QkvPostArgs qa{};
-            qa.part = kv->qkv; qa.splits = split; qa.z_stride = (long long)B * nqkv; qa.M = B; qa.T = 1;
-            qa.H = H; qa.hd = hd; qa.ss_in = kv->ss_a; qa.ss_in_parts = 1; qa.ss_stride = (int)kv->cap_m;
-            qa.norm_dim = d; qa.lens = kv->lens_dev; qa.rope_cos = m->rope_cos; qa.rope_sin = m->rope_sin;
-            qa.q = kv->q; qa.kc = (char*)kv->kcache + l * per_layer; qa.vtc = (char*)kv->vcache + l * per_layer;
-            qa.S = kv->S; qa.eps = c.norm_eps;
-            LAUNCH(launch_qkv_post(m->dt, qa, st));
-            LAUNCH(launch_attn_decode(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->lens_dev, kv->y, kv->apart, B, H,
-                                      kv->S, max_chunks, st));
-            s = decode_gemm(kv, EPI_RESID, kv->y, H * hd, L.wo, d, H * hd, kv->x, kv->act, d, nullptr, 0,
-                            kv->ss_b, st);
-            if (s != NC_OK) return s;
-            s = decode_gemm(kv, EPI_RELU2, kv->act, d, L.wfc, F, d, nullptr, kv->u, F, kv->ss_b, 1, nullptr, st);
-            if (s != NC_OK) return s;
-            s = decode_gemm(kv, EPI_RESID, kv->u, F, L.wproj, d, F, kv->x, kv->act, d, nullptr, 0, kv->ss_a, st);
-            if (s != NC_OK) return s;
+        if (!kv->use_graph) {
+            s = enqueue_decode(m, kv, tokens, logits, st);
+        } else {
+            hipGraphExec_t exec = nullptr;
+            for (auto& g : kv->graphs)
+                if (g.tokens == tokens && g.logits == logits) exec = g.exec;
+            if (!exec) {
+                if (!kv->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&kv->cap_stream, hipStreamNonBlocking));
+                HIP_TRY(hipStreamBeginCapture(kv->cap_stream, hipStreamCaptureModeThreadLocal));
+                s = enqueue_decode(m, kv, tokens, logits, kv->cap_stream);
+                hipGraph_t graph = nullptr;
+                hipError_t e = hipStreamEndCapture(kv->cap_stream, &graph);
+                if (s != NC_OK) {
+                    if (graph) (void)hipGraphDestroy(graph);
+                    return s;
+                }
+                if (e != hipSuccess) return fail(NC_ERR_DEVICE, std::string("decode capture: ") + hipGetErrorString(e));
+                e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+                (void)hipGraphDestroy(graph);
+                if (e != hipSuccess) return fail(NC_ERR_DEVICE, std::string("graph instantiate: ") + hipGetErrorString(e));
+                if (kv->graphs.size() >= 8) {  // keep a handful of buffer pairs
+                    (void)hipGraphExecDestroy(kv->graphs.front().exec);
+                    kv->graphs.erase(kv->graphs.begin());
+                }
+                kv->graphs.push_back({tokens, logits, exec});
+            }
+            HIP_TRY(hipGraphLaunch(exec, st));
         }
-        s = decode_gemm(kv, EPI_SOFTCAP, kv->act, d, m->lm, V, d, logits, nullptr, V, kv->ss_a, 1, nullptr, st);
         if (s != NC_OK) return s;
-        LAUNCH(launch_lens_add(kv->lens_dev, B, 1, -1, st));
         for (int b = 0; b < B; ++b) kv->lens_host[b] += 1;
         return NC_OK;
     } catch (...) {

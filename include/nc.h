@@ -116,9 +116,12 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens_dev, int32_t B, int32_t 
                      nc_kv* kv, float* logits_dev, void* stream);
 
 /* One decode step: row b takes token tokens_dev[b] at position lens[b] and attends to
- * cache positions 0..lens[b].  Requires B == batch of kv and lens[b] + 1 <= max_seq for
- * every row (NC_ERR_CAPACITY otherwise).  logits_dev: fp32 [B, vocab] (not NULL).
- * On success every length grows by one. */
+ * cache positions 0..lens[b].  Requires B == batch of kv, B <= 128 (NC_ERR_UNSUPPORTED
+ * otherwise) and lens[b] + 1 <= max_seq for every row (NC_ERR_CAPACITY otherwise).
+ * logits_dev: fp32 [B, vocab] (not NULL).  On success every length grows by one.
+ * The step's kernels are captured once per (tokens_dev, logits_dev) pair into a HIP graph
+ * owned by the kv object and replayed on later calls (set NC_DECODE_GRAPH=0 in the
+ * environment before nc_kv_create to launch them one by one instead). */
 nc_status nc_decode_step(nc_model* m, const int32_t* tokens_dev, int32_t B, nc_kv* kv,
                          float* logits_dev, void* stream);
 

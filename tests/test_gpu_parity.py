@@ -188,3 +188,29 @@ def test_argmax_ties_and_nan():
     nc.nc_argmax(x, 4, 1000, out)
     torch.cuda.synchronize()
     assert out.cpu().tolist() == [5, 999, 123, 0]
+
+
+def test_decode_graph_replays_match_eager(small, monkeypatch):
+    """The captured decode graph, replayed step after step with eager work in between,
+    gives bitwise the same logits as launching the kernels one by one."""
+    torch = torch_mod()
+    w, orc, gm = small
+    toks = make_tokens(SMALL_BF16.vocab, 3, 140, seed=13)
+    kv_g, _ = prefill(gm, toks[:, :130], 160, logits=False)
+    monkeypatch.setenv("NC_DECODE_GRAPH", "0")
+    kv_e, _ = prefill(gm, toks[:, :130], 160, logits=False)
+    monkeypatch.delenv("NC_DECODE_GRAPH")
+    tok_buf = torch.zeros(3, dtype=torch.int32, device="cuda")
+    out_g = torch.empty((3, SMALL_BF16.vocab), device="cuda", dtype=torch.float32)
+    want, _ = orc.prefill(toks)
+    for s in range(10):
+        tok_buf.copy_(torch.from_numpy(toks[:, 130 + s].astype(np.int32)))
+        kv_g.decode(tok_buf, out_g)
+        torch.cuda.synchronize()
+        got_g = out_g.cpu().numpy()
+        got_e = decode(gm, kv_e, toks[:, 130 + s])
+        assert np.array_equal(got_g, got_e), s
+        assert np.max(np.abs(got_g - want[:, 130 + s])) <= BF16_TOL
+    assert np.array_equal(kv_g.lens(), [140, 140, 140])
+    kv_g.close()
+    kv_e.close()
