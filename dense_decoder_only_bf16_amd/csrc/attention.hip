@@ -229,76 +229,186 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 }
 
 // ------------------------------------------------------------------ decode ----------
-// Split kernel.  Workgroup (chunk c, row b): 4 waves x 64 keys = keys [256c, 256c + 256)
-// limited to positions 0..lens[b].  All query heads of the row (padded to 16) form the 16
-// columns of 16x16 MFMA tiles, so each K/V element is read from memory once for the whole
-// head group.  Every wave issues all of its K and V^T loads (straight from the cache into
-// registers) before any arithmetic, so a wave keeps 32 KB in flight.  The four waves'
-// softmax states are merged in LDS and the workgroup writes its chunk's partial
-// (max, sum, o[16][hd]); the combine kernel merges the chunks of each row.
-constexpr int DEC_KPW = 64, DEC_CHUNK = 4 * DEC_KPW;
+// Split kernel.  Workgroup (chunk c, row b): 2 waves x 64 keys = keys [128c, 128c + 128)
+// limited to positions 0..lens[b]; each wave writes its own partial softmax state
+// (max, sum, o[16][hd]) to slot 2c + wave.
+//  1. Finish the QKV product of row b for this step (the row's attention-norm scale,
+//     RoPE at position lens[b] and QK-norm of the query heads and the key head; the value
+//     head as is) into LDS.  Every workgroup of the row does this (a few hundred values);
+//     the one whose chunk holds position lens[b] also writes the new key and value into the
+//     cache for later steps.
+//  2. All query heads of the row (padded to 16) form the 16 columns of 16x16 MFMA tiles,
+//     so each cached K/V element is read from memory once for the whole head group.
+//     bf16: each wave stages its 64 keys of K (64 x hd) and V^T (hd x 64) in LDS with
+//     1 KB direct-to-LDS loads issued before step 1, XOR-swizzled so that the MFMA operand
+//     reads are free of bank conflicts.  fp32 (small check model): operands are loaded
+//     straight into registers.  Cached keys at or past lens[b] are masked in the scores;
+//     the new key (position lens[b]) is not read from the cache but added to the wave's
+//     softmax state as one extra term from the values in LDS.
+constexpr int DEC_WAVES = 2, DEC_KPW = 64, DEC_CHUNK = DEC_WAVES * DEC_KPW;
 int attn_decode_chunk() { return DEC_CHUNK; }
+int attn_decode_slots(int S) { return (S + DEC_CHUNK - 1) / DEC_CHUNK * DEC_WAVES; }
 
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_decode_split_kernel(
-    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vtc,
-    const int32_t* __restrict__ lens, float* __restrict__ part, int H, int S, int max_chunks,
-    float scale_log2) {
+__global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_split_kernel(DecAttnArgs a) {
     typedef typename Chunk<T>::type CT;
     typedef typename Chunk<T>::half HT;
+    constexpr bool STAGE = sizeof(T) == 2;  // LDS staging for bf16
+    constexpr int NW = DEC_WAVES;
     constexpr int DS = HD / 32;   // 32-deep steps over head dim for S^T
     constexpr int DT = HD / 16;   // 16-row tiles of O^T
     constexpr int PSZ = 16 * (HD + 2);
+    constexpr int HALF = HD / 2;
+    constexpr int KREG = STAGE ? DEC_KPW * HD * 2 : 16;  // bytes of one wave's K (or V^T) tile
+    constexpr int NSLOT = (18 + NW - 1) / NW;           // QKV-finish slots per wave
 
-    __shared__ float sm[4][16], sl[4][16];
-    __shared__ float so[4][16][HD + 1];
+    __shared__ __attribute__((aligned(1024))) unsigned char buf[NW * 2 * KREG];
+    __shared__ __attribute__((aligned(32))) T qs[16][HD];
+    __shared__ __attribute__((aligned(32))) T kv_new[2][HD];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g = lane >> 4;
     const int c = blockIdx.x, b = blockIdx.y;
-    const int pos = lens[b];  // keys 0..pos are visible
-    const int nkeys = min(pos + 1, S);
-    const int nchunks = (nkeys + DEC_CHUNK - 1) / DEC_CHUNK;
+    const int S = a.S, H = a.H;
+    const int pos = a.lens[b];  // this step's position; keys 0..pos are visible
+    if (pos < 0 || pos >= S) return;  // capacity is checked by the host; stay in bounds
+    const int nchunks = (pos + 1 + DEC_CHUNK - 1) / DEC_CHUNK;
     if (c >= nchunks) return;
     const int kbeg = c * DEC_CHUNK + wave * DEC_KPW;
+    T* kb_base = (T*)a.kc + (long long)b * S * HD;
+    T* vb_base = (T*)a.vtc + (long long)b * HD * S;
+    unsigned char* kl = buf + wave * 2 * KREG;  // K: 64 keys x HD, 16-byte chunks swizzled
+    unsigned char* vl = kl + KREG;               // V^T: HD rows x 64 keys (128 bytes a row)
 
-    const T* kb_base = kc + (long long)b * S * HD;
-    const T* vb_base = vtc + (long long)b * HD * S;
-
-    // ---- issue every load of this wave
-    CT qf[DS];
+    // ---- staging loads of this wave's cached K and V^T (bf16)
+    if constexpr (STAGE) {
+        typedef __attribute__((address_space(1))) void gvoid;
+        typedef __attribute__((address_space(3))) void lvoid;
+        constexpr int KCH = HD / 8;  // 16-byte chunks per K row
+        // K: LDS byte 16 p of the wave's tile holds key p / KCH, chunk (p % KCH) ^ (key % KCH)
 #pragma unroll
-    for (int s = 0; s < DS; ++s)
-        qf[s] = (col < H) ? *(const CT*)(q + ((long long)b * H + col) * HD + 32 * s + 8 * g) : zero_vec<CT>();
-    CT kf[4][DS];
+        for (int j = 0; j < KREG / 1024; ++j) {
+            const int p = j * 64 + lane;
+            const int kidx = p / KCH, cch = (p % KCH) ^ (kidx % KCH);
+            int key = kbeg + kidx;
+            key = key < pos ? key : (pos > 0 ? pos - 1 : 0);  // keys >= pos are masked
+            __builtin_amdgcn_global_load_lds((gvoid*)(kb_base + (long long)key * HD + cch * 8),
+                                             (lvoid*)(kl + j * 1024), 16, 0, 0);
+        }
+        // V^T: LDS byte 16 p holds row d = p / 8, keys 8 ((p % 8) ^ (d % 8)) .. +8
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-        const int key = kbeg + 16 * kt + col;
-#pragma unroll
-        for (int s = 0; s < DS; ++s)
-            kf[kt][s] = (key < nkeys) ? *(const CT*)(kb_base + (long long)key * HD + 32 * s + 8 * g) : zero_vec<CT>();
-    }
-    // V^T operands: slot 8g+i of 32-key step u <-> key 32u + 4g + i (i < 4) or
-    // 32u + 16 + 4g + (i - 4) (i >= 4); loaded whole when in range, else element-wise.
-    HT vlo[2][DT], vhi[2][DT];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int ka = kbeg + 32 * u + 4 * g, kb2 = ka + 16;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const T* src = vb_base + (long long)(dt * 16 + col) * S;
-            if (ka + 4 <= nkeys) vlo[u][dt] = *(const HT*)(src + ka);
-            else
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vlo[u][dt][e] = (ka + e < nkeys) ? src[ka + e] : from_f32<T>(0.f);
-            if (kb2 + 4 <= nkeys) vhi[u][dt] = *(const HT*)(src + kb2);
-            else
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vhi[u][dt][e] = (kb2 + e < nkeys) ? src[kb2 + e] : from_f32<T>(0.f);
+        for (int j = 0; j < KREG / 1024; ++j) {
+            const int p = j * 64 + lane;
+            const int d = p / 8;
+            int k0 = kbeg + 8 * ((p % 8) ^ (d % 8));
+            k0 = k0 <= S - 8 ? k0 : S - 8;  // a chunk starting at or past S is fully masked
+            __builtin_amdgcn_global_load_lds((gvoid*)(vb_base + (long long)d * S + k0),
+                                             (lvoid*)(vl + j * 1024), 16, 0, 0);
         }
     }
 
-    // ---- scores S^T (lane: head `col`, keys kbeg + 16kt + 4g + j), softmax (base 2)
+    // ---- 1. QKV finish for row b: slot j = wave + NW i (0..15 query heads, padding past
+    //         H; 16 the key head; 17 the value head).  All loads first, then arithmetic.
+    {
+        const float* raw = a.qkv + (long long)b * (H + 2) * HD;
+        const bool act = lane < HALF;
+        const int i = act ? lane : 0;
+        float v1[NSLOT], v2[NSLOT];
+#pragma unroll
+        for (int t = 0; t < NSLOT; ++t) {
+            const int j = wave + NW * t;
+            const int src = (j < H) ? j : (j == 16 ? H : (j == 17 ? H + 1 : 0));
+            v1[t] = raw[src * HD + i];
+            v2[t] = raw[src * HD + i + HALF];
+        }
+        const float cs = a.rope_cos[(long long)pos * HALF + i], sn = a.rope_sin[(long long)pos * HALF + i];
+        const float r = row_scale_wave(a.ss_in, a.ss_in_parts, a.ss_stride, b, a.norm_dim, a.eps);
+#pragma unroll
+        for (int t = 0; t < NSLOT; ++t) {
+            const int j = wave + NW * t;
+            if (j >= 18) continue;
+            if (j < H || j == 16) {  // rotate + normalise
+                const float x1 = v1[t] * r, x2 = v2[t] * r;
+                const float o1 = x1 * cs - x2 * sn, o2 = x1 * sn + x2 * cs;
+                const float ss = wave_sum(act ? o1 * o1 + o2 * o2 : 0.f);
+                const float rr = 1.0f / sqrtf(ss / (float)HD + a.eps);
+                T* dst = (j < 16) ? qs[j] : kv_new[0];
+                if (act) {
+                    dst[i] = from_f32<T>(o1 * rr);
+                    dst[i + HALF] = from_f32<T>(o2 * rr);
+                }
+            } else if (j == 17) {
+                if (act) {
+                    kv_new[1][i] = from_f32<T>(v1[t] * r);
+                    kv_new[1][i + HALF] = from_f32<T>(v2[t] * r);
+                }
+            } else {  // padding query slot
+                if (act) {
+                    qs[j][i] = from_f32<T>(0.f);
+                    qs[j][i + HALF] = from_f32<T>(0.f);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (c == nchunks - 1)  // the chunk holding `pos` stores the new key/value
+        for (int e = tid; e < HD; e += NW * 64) {
+            kb_base[(long long)pos * HD + e] = kv_new[0][e];
+            vb_base[(long long)e * S + pos] = kv_new[1][e];
+        }
+
+    // ---- 2. operands
+    CT qf[DS];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qf[s] = *(const CT*)(&qs[col][32 * s + 8 * g]);
+    CT kf[4][DS];
+    // V^T operands: slot 8g+i of 32-key step u <-> key 32u + 4g + i (i < 4) or
+    // 32u + 16 + 4g + (i - 4) (i >= 4).
+    HT vlo[2][DT], vhi[2][DT];
+    if constexpr (STAGE) {
+        constexpr int KCH = HD / 8;
+        NC_WAIT_VM_ALL();  // this wave's staging loads have landed
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const int kidx = 16 * kt + col;
+#pragma unroll
+            for (int s = 0; s < DS; ++s)
+                kf[kt][s] = *(const CT*)(kl + kidx * (HD * 2) + (((4 * s + g) ^ (kidx % KCH)) * 16));
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int d = dt * 16 + col;
+                const int k1 = 32 * u + 4 * g, k2 = k1 + 16;  // first keys (local) of the halves
+                vlo[u][dt] = *(const HT*)(vl + d * 128 + (((k1 / 8) ^ (d % 8)) * 16) + (k1 % 8) * 2);
+                vhi[u][dt] = *(const HT*)(vl + d * 128 + (((k2 / 8) ^ (d % 8)) * 16) + (k2 % 8) * 2);
+            }
+    } else {
+        const int klast = pos > 0 ? pos - 1 : 0;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            int key = kbeg + 16 * kt + col;
+            key = key < pos ? key : klast;
+#pragma unroll
+            for (int s = 0; s < DS; ++s) kf[kt][s] = *(const CT*)(kb_base + (long long)key * HD + 32 * s + 8 * g);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            int ka = kbeg + 32 * u + 4 * g, kb2 = ka + 16;
+            ka = ka <= S - 4 ? ka : S - 4;
+            kb2 = kb2 <= S - 4 ? kb2 : S - 4;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const T* src = vb_base + (long long)(dt * 16 + col) * S;
+                vlo[u][dt] = *(const HT*)(src + ka);
+                vhi[u][dt] = *(const HT*)(src + kb2);
+            }
+        }
+    }
+
+    // ---- scores S^T (lane: head `col`, keys kbeg + 16kt + 4g + j), cached keys < pos
     f32x4 sacc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -312,19 +422,19 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int key = kbeg + 16 * kt + 4 * g + j;
-            float v = (key < nkeys) ? sacc[kt][j] * scale_log2 : -INFINITY;
+            const float v = (key < pos) ? sacc[kt][j] * a.scale_log2 : -INFINITY;
             sacc[kt][j] = v;
             mx = fmaxf(mx, v);
         }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mref = (mx == -INFINITY) ? 0.f : mx;  // a wave past the last key has no mass
+    const float mref = (mx == -INFINITY) ? 0.f : mx;  // no visible cached key: no mass
     float ls = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            float pv = fast_exp2(sacc[kt][j] - mref);
+            const float pv = fast_exp2(sacc[kt][j] - mref);
             sacc[kt][j] = pv;
             ls += pv;
         }
@@ -355,80 +465,99 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
         }
     }
 
-    // ---- merge the four waves into this chunk's partial
-    if (g == 0) {
-        sm[wave][col] = mx;
-        sl[wave][col] = ls;
-    }
+    // ---- the new key (position pos) joins the wave whose range holds it
+    if (pos >= kbeg && pos < kbeg + DEC_KPW) {
+        // score of head `col`: lane group g sums 32 of the hd features
+        float part = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+        for (int e = 0; e < HD / 4; ++e)
+            part += to_f32(qs[col][g * (HD / 4) + e]) * to_f32(kv_new[0][g * (HD / 4) + e]);
+        part += __shfl_xor(part, 16, 64);
+        part += __shfl_xor(part, 32, 64);
+        const float sp = part * a.scale_log2;
+        const float mn = fmaxf(mx, sp);
+        const float al = fast_exp2(mx - mn);  // 0 when no cached key was visible
+        const float be = fast_exp2(sp - mn);
+        ls = ls * al + be;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) so[wave][col][dt * 16 + 4 * g + j] = oacc[dt][j];
-    __syncthreads();
-    float* pb = part + ((long long)b * max_chunks + c) * PSZ;
-    for (int i = tid; i < 16 * HD; i += 256) {
-        const int h = i / HD, d = i % HD;
-        const float M = fmaxf(fmaxf(sm[0][h], sm[1][h]), fmaxf(sm[2][h], sm[3][h]));
-        float o = 0.f;
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-            if (sm[w][h] != -INFINITY) o += fast_exp2(sm[w][h] - M) * so[w][h][d];
-        pb[32 + h * HD + d] = o;
-    }
-    if (tid < 16) {
-        const int h = tid;
-        const float M = fmaxf(fmaxf(sm[0][h], sm[1][h]), fmaxf(sm[2][h], sm[3][h]));
-        float l = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            if (sm[w][h] != -INFINITY) l += fast_exp2(sm[w][h] - M) * sl[w][h];
-        pb[h] = M;
-        pb[16 + h] = l;
+            for (int j = 0; j < 4; ++j)
+                oacc[dt][j] = oacc[dt][j] * al + be * to_f32(kv_new[1][dt * 16 + 4 * g + j]);
+        mx = mn;
     }
 
+    // ---- this wave's partial: slot 2c + wave
+    float* pb = a.part + ((long long)b * a.max_slots + (c * NW + wave)) * PSZ;
+    if (g == 0) {
+        pb[col] = mx;
+        pb[16 + col] = ls;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        f32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = oacc[dt][j];
+        *(f32x4*)(pb + 32 + col * HD + dt * 16 + 4 * g) = o;
+    }
 }
 
 // Combine kernel: workgroup (head h, row b), one thread per feature d:
-// y[b][h][d] = sum_c 2^(m_c - M) o_c[d] / sum_c 2^(m_c - M) l_c.
+// y[b][h][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s over the row's slots.  The
+// slot statistics are loaded lane-parallel (one slot per lane), the weights go through
+// LDS, and the o_s[d] loads of consecutive slots are independent of each other.
 template <typename T, int HD>
 __global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __restrict__ part,
                                                                  const int32_t* __restrict__ lens,
                                                                  T* __restrict__ y, int H, int S,
-                                                                 int max_chunks) {
+                                                                 int max_slots) {
     constexpr int PSZ = 16 * (HD + 2);
+    __shared__ float wts[512];
+    __shared__ float stat[1];
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-    const int nkeys = min(lens[b] + 1, S);
-    const int nch = (nkeys + DEC_CHUNK - 1) / DEC_CHUNK;
-    const float* prow = part + (long long)b * max_chunks * PSZ;
-    float M = -INFINITY;
-    for (int cc = 0; cc < nch; ++cc) M = fmaxf(M, prow[(long long)cc * PSZ + h]);
-    float o = 0.f, l = 0.f;
-    for (int cc = 0; cc < nch; ++cc) {
-        const float* pc = prow + (long long)cc * PSZ;
-        const float w = fast_exp2(pc[h] - M);
-        l += w * pc[16 + h];
-        o += w * pc[32 + h * HD + d];
+    const int pos = min(lens[b], S - 1);
+    const int nsl = min((pos + 1 + DEC_CHUNK - 1) / DEC_CHUNK * DEC_WAVES, 512);
+    const float* prow = part + (long long)b * max_slots * PSZ;
+    if (d < 64) {  // wave 0: max, weights and normaliser
+        float mloc = -INFINITY;
+        for (int sl = d; sl < nsl; sl += 64) mloc = fmaxf(mloc, prow[(long long)sl * PSZ + h]);
+        const float M = wave_max(mloc);
+        float lsum = 0.f;
+        for (int sl = d; sl < nsl; sl += 64) {
+            const float w = fast_exp2(prow[(long long)sl * PSZ + h] - M);  // 0 for empty slots
+            wts[sl] = w;
+            lsum += w * prow[(long long)sl * PSZ + 16 + h];
+        }
+        lsum = wave_sum(lsum);
+        if (d == 0) stat[0] = 1.0f / lsum;
     }
-    y[((long long)b * H + h) * HD + d] = from_f32<T>(o / l);
+    __syncthreads();
+    const float* po = prow + 32 + h * HD + d;
+    float o = 0.f;
+    int sl = 0;
+    for (; sl + 4 <= nsl; sl += 4) {
+        const float o0 = po[(long long)sl * PSZ], o1 = po[(long long)(sl + 1) * PSZ];
+        const float o2 = po[(long long)(sl + 2) * PSZ], o3 = po[(long long)(sl + 3) * PSZ];
+        o += wts[sl] * o0 + wts[sl + 1] * o1 + wts[sl + 2] * o2 + wts[sl + 3] * o3;
+    }
+    for (; sl < nsl; ++sl) o += wts[sl] * po[(long long)sl * PSZ];
+    y[((long long)b * H + h) * HD + d] = from_f32<T>(o * stat[0]);
 }
 
-hipError_t launch_attn_decode(DType dt, int hd, const void* q, const void* kc, const void* vtc,
-                              const int32_t* lens, void* y, float* part, int B, int H, int S,
-                              int max_chunks, hipStream_t st) {
-    const float sl = 1.4426950408889634f / sqrtf((float)hd);
-    dim3 g1(max_chunks, B), g2(H, B);
+hipError_t launch_attn_decode(DType dt, const DecAttnArgs& args, void* y, hipStream_t st) {
+    DecAttnArgs a = args;
+    a.scale_log2 = 1.4426950408889634f / sqrtf((float)a.hd);
+    dim3 g1((a.max_slots + DEC_WAVES - 1) / DEC_WAVES, a.B), g2(a.H, a.B);
 #define NC_AD(TT, HDV)                                                                         \
     do {                                                                                       \
-        hipLaunchKernelGGL((attn_decode_split_kernel<TT, HDV>), g1, dim3(256), 0, st,          \
-                           (const TT*)q, (const TT*)kc, (const TT*)vtc, lens, part, H, S,      \
-                           max_chunks, sl);                                                    \
+        hipLaunchKernelGGL((attn_decode_split_kernel<TT, HDV>), g1, dim3(DEC_WAVES * 64), 0, st, a);     \
         hipLaunchKernelGGL((attn_decode_combine_kernel<TT, HDV>), g2, dim3(HDV), 0, st,        \
-                           (const float*)part, lens, (TT*)y, H, S, max_chunks);                \
+                           (const float*)a.part, a.lens, (TT*)y, a.H, a.S, a.max_slots);      \
     } while (0)
-    if (dt == BF16 && hd == 128) NC_AD(bf16, 128);
-    else if (dt == BF16 && hd == 64) NC_AD(bf16, 64);
-    else if (dt == F32 && hd == 128) NC_AD(float, 128);
-    else if (dt == F32 && hd == 64) NC_AD(float, 64);
+    if (dt == BF16 && a.hd == 128) NC_AD(bf16, 128);
+    else if (dt == BF16 && a.hd == 64) NC_AD(bf16, 64);
+    else if (dt == F32 && a.hd == 128) NC_AD(float, 128);
+    else if (dt == F32 && a.hd == 64) NC_AD(float, 64);
     else return hipErrorInvalidValue;
 #undef NC_AD
     return hipGetLastError();

@@ -86,6 +86,22 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Wait for every outstanding vector-memory load of this wave (including direct-to-LDS
+// loads, which the compiler does not track).
+#define NC_WAIT_VM_ALL() __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8))
+
+// Row scale of the parameter-free RMSNorm, r = 1/sqrt(sum_p ss[p * stride + m] / dim + eps),
+// from `parts` partial sums of squares.  Wave-cooperative: lane q loads parts q, q+64, ...
+// (all loads independent), then a butterfly sum; every lane returns r.  Must be called by
+// all 64 lanes of the wave.
+__device__ __forceinline__ float row_scale_wave(const float* ss, int parts, int stride, int m,
+                                                int dim, float eps) {
+    const int lane = threadIdx.x & 63;
+    float s = 0.f;
+    for (int q = lane; q < parts; q += 64) s += ss[(long long)q * stride + m];
+    return 1.0f / sqrtf(wave_sum(s) / (float)dim + eps);
+}
+
 // 2^x on the hardware exponential unit.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -49,12 +49,6 @@ __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, in
     }
 }
 
-template <typename T>
-__device__ __forceinline__ float dec_row_scale(const DecGemmArgs& p, int m) {
-    float s = 0.f;
-    for (int q = 0; q < p.ss_in_parts; ++q) s += p.ss_in[(long long)q * p.ss_stride + m];
-    return 1.0f / sqrtf(s / (float)p.K + p.eps);
-}
 
 // 32 x 32 MFMA tiles: FM row tiles (M <= 32 FM), 32 columns, NW waves splitting K.
 // Each wave walks its K range in groups of U 16-deep steps with two register buffers: the
@@ -68,6 +62,8 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
     __shared__ float red[NW * BM * TP];
     __shared__ float rs[BM];
 
+    if (p.lens_inc && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int r = threadIdx.x; r < p.M; r += NW * 64) p.lens_inc[r] += 1;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int l32 = lane & 31, hh = lane >> 5;
@@ -125,7 +121,10 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
         for (int r = 0; r < 16; ++r)
             mine[(32 * i + 8 * (r / 4) + 4 * hh + (r % 4)) * TP + l32] = acc[i][r];
     if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP)
-        for (int r = tid; r < BM; r += NW * 64) rs[r] = (m0 + r < p.M) ? dec_row_scale<T>(p, m0 + r) : 1.f;
+        for (int r = wave; r < BM; r += NW) {  // one wave per row, lanes over the parts
+            const float v = (m0 + r < p.M) ? row_scale_wave(p.ss_in, p.ss_in_parts, p.ss_stride, m0 + r, p.K, p.eps) : 1.f;
+            if (lane == 0) rs[r] = v;
+        }
     __syncthreads();
     const int rows = min(BM, p.M - m0);
     for (int e = tid; e < rows * BN; e += NW * 64) {

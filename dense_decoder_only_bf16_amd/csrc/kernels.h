@@ -55,6 +55,7 @@ struct DecGemmArgs {
     const float* ss_in; int ss_in_parts, ss_stride;
     float* ss_out;
     float eps, cap;
+    int32_t* lens_inc;  // if set, workgroup 0 adds one to lens_inc[0..M) (end of a decode step)
 };
 int dec_gemm_tile_n();
 hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t st, int variant = 0);
@@ -87,13 +88,25 @@ hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st);
 hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, const void* vtc,
                                void* y, int B, int T, int H, int S, hipStream_t st);
 
-// Decode attention, one query per row at position lens[b] (keys 0..lens[b]): the split
-// kernel reduces each chunk of keys to a partial softmax state, the combine kernel merges a
-// row's partials into y.
+// Decode attention for one step, one query per row at position lens[b] (keys
+// 0..lens[b]).  The split kernel first finishes the row's raw QKV product (norm scale,
+// RoPE, QK-norm) and stores the new key/value into the cache, then reduces each chunk of
+// keys to a partial softmax state; the combine kernel merges a row's partials into
+// y [B][H][hd].  The combine reads lens[b] to know the chunk count.
+struct DecAttnArgs {
+    const float* qkv;   // raw product [B][(H+2) hd] fp32
+    const float* ss_in; int ss_in_parts, ss_stride, norm_dim;
+    float eps;
+    const float* rope_cos; const float* rope_sin;
+    const int32_t* lens;
+    void* kc; void* vtc;  // this layer's cache: K [B][S][hd], V^T [B][hd][S]
+    float* part;          // [B][max_slots][16 (hd + 2)]
+    int B, H, hd, S, max_slots;  // max_slots = attn_decode_slots(S)
+    float scale_log2;     // set by the launcher
+};
 int attn_decode_chunk();
-hipError_t launch_attn_decode(DType dt, int hd, const void* q, const void* kc, const void* vtc,
-                              const int32_t* lens, void* y, float* part, int B, int H, int S,
-                              int max_chunks, hipStream_t st);
+int attn_decode_slots(int S);  // partial slots per row for a cache of S positions
+hipError_t launch_attn_decode(DType dt, const DecAttnArgs& a, void* y, hipStream_t st);
 
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st);
 hipError_t launch_lens_add(int32_t* lens, int B, int32_t delta, int32_t set_value, hipStream_t st);

@@ -12,30 +12,52 @@
 namespace nc {
 
 // ------------------------------------------------------------------ embedding -------
+// One wave per row; each lane moves 8 consecutive elements per 16/32-byte access.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok, int M,
                                                     const T* __restrict__ wte, int vocab, int d,
                                                     float eps, float* __restrict__ x,
                                                     T* __restrict__ act, float* __restrict__ ss) {
+    typedef typename Chunk<T>::type CT;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= M) return;
     int t = tok[row];
     t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
     const T* e = wte + (long long)t * d;
+    const int nch = d / 8;   // d is a multiple of 64
+    constexpr int MAXC = 8;  // up to 8 chunks per lane: d <= 4096
+    CT v[MAXC];
     float s = 0.f;
-    for (int i = lane; i < d; i += 64) {
-        float v = to_f32(e[i]);
-        s += v * v;
+#pragma unroll
+    for (int u = 0; u < MAXC; ++u) {
+        const int cidx = lane + 64 * u;
+        v[u] = load_masked(e + (cidx < nch ? cidx : 0) * 8, cidx < nch);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float f = to_f32(v[u][k]);
+            s += f * f;
+        }
     }
     s = wave_sum(s);
     const float r = 1.0f / sqrtf(s / (float)d + eps);
     float s2 = 0.f;
-    for (int i = lane; i < d; i += 64) {
-        float v = to_f32(e[i]) * r;
-        x[(long long)row * d + i] = v;
-        act[(long long)row * d + i] = from_f32<T>(v);
-        s2 += v * v;
+#pragma unroll
+    for (int u = 0; u < MAXC; ++u) {
+        const int cidx = lane + 64 * u;
+        if (cidx < nch) {
+            f32x8 xo;
+            CT ao;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float f = to_f32(v[u][k]) * r;
+                xo[k] = f;
+                ao[k] = from_f32<T>(f);
+                s2 += f * f;
+            }
+            *(f32x8*)(x + (long long)row * d + cidx * 8) = xo;
+            *(CT*)(act + (long long)row * d + cidx * 8) = ao;
+        }
     }
     s2 = wave_sum(s2);
     if (lane == 0) ss[row] = s2;

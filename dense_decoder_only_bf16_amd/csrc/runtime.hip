@@ -3,15 +3,17 @@
 //
 // Schedule of one layer (the block structure of the yelogs.com launch write-up's
 // architecture answer; plain pre-norm residual reading):
-//   QKV product (raw, fp32)  -> qkv_post: row norm scale, RoPE, QK-norm, KV-cache write
-//   attention (prefill: flash kernel; decode: split-context + combine)
+//   QKV product (raw, fp32)  -> QKV finish: row norm scale, RoPE, QK-norm, KV-cache write
+//   attention (prefill: flash kernel; decode: split-context + combine, with the QKV
+//   finish done inside the split kernel)
 //   O product  + residual epilogue (x += ., dtype copy of x, per-row sum of squares)
 //   FC product + norm scale + ReLU^2 epilogue
 //   PROJ product + residual epilogue
 // then the LM head with norm scale and softcap.  Prefill uses the 256x256 MFMA tile with
 // the epilogues fused (the QKV finish is a separate row kernel).  Decode (M = batch rows)
 // uses the weight-streaming decode product (K split over the waves of one workgroup) with
-// the elementwise epilogues fused and the QKV finish as a row kernel; the whole decode step is
+// the elementwise epilogues fused and the QKV finish inside the attention kernel; the LM
+// head's launch also advances the row lengths.  The whole decode step is
 // captured once per (token buffer, logit buffer) pair as a HIP graph and replayed.
 // No kernel communicates with other workgroups of the same launch: the L2 caches of the
 // chip's dies are not coherent with each other, so a device-wide fence costs a write-back
@@ -140,8 +142,7 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
     WS_ALLOC(kv->q, M * hq * es);
     WS_ALLOC(kv->y, M * hq * es);
     WS_ALLOC(kv->u, M * c.d_ff * es);
-    const int max_chunks = (kv->S + attn_decode_chunk() - 1) / attn_decode_chunk();
-    kv->apart_elems = (long long)kv->B * max_chunks * 16 * (c.head_dim + 2);
+    kv->apart_elems = (long long)kv->B * attn_decode_slots(kv->S) * 16 * (c.head_dim + 2);
     WS_ALLOC(kv->apart, kv->apart_elems * 4);
 #undef WS_ALLOC
     kv->cap_m = M;
@@ -159,6 +160,7 @@ nc_status check_cfg(const nc_config* c) {
     if ((long long)c->n_head * c->head_dim != c->d_model) return fail(NC_ERR_INVALID_ARG, "d_model must equal n_head * head_dim");
     if (c->n_head > 16) return fail(NC_ERR_UNSUPPORTED, "n_head > 16 is not supported by the decode attention kernel");
     if (c->d_model % 64 || c->d_ff % 64) return fail(NC_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
+    if (c->d_model > 4096) return fail(NC_ERR_UNSUPPORTED, "d_model > 4096 is not supported");
     if (!(c->softcap > 0.f) || !(c->norm_eps >= 0.f) || !(c->rope_base > 0.f))
         return fail(NC_ERR_INVALID_ARG, "softcap and rope_base must be > 0, norm_eps >= 0");
     if (c->max_seq > (1 << 24)) return fail(NC_ERR_INVALID_ARG, "max_seq too large");
@@ -201,7 +203,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
     const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab;
     const int nqkv = (H + 2) * hd;
     const size_t per_layer = (size_t)B * kv->S * hd * m->esz;
-    const int max_chunks = (kv->S + attn_decode_chunk() - 1) / attn_decode_chunk();
+    const int max_slots = attn_decode_slots(kv->S);
     const int parts_d = (d + dec_gemm_tile_n() - 1) / dec_gemm_tile_n();
     const int ss = (int)kv->cap_m;
     nc_status s;
@@ -218,14 +220,13 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         a.A = kv->act; a.lda = d; a.W = L.wqkv; a.N = nqkv; a.K = d;
         a.out_f32 = kv->qkv; a.ldo = nqkv;
         if ((s = decode_gemm(kv, EPI_STORE, a, st)) != NC_OK) return s;
-        QkvPostArgs qa{};
-        qa.part = kv->qkv; qa.splits = 1; qa.z_stride = 0; qa.M = B; qa.T = 1; qa.H = H; qa.hd = hd;
-        qa.ss_in = kv->ss_a; qa.ss_in_parts = ss_a_parts; qa.ss_stride = ss; qa.norm_dim = d;
-        qa.lens = kv->lens_dev; qa.rope_cos = m->rope_cos; qa.rope_sin = m->rope_sin;
-        qa.q = kv->q; qa.kc = kc; qa.vtc = vtc; qa.S = kv->S; qa.eps = c.norm_eps;
-        LAUNCH(launch_qkv_post(m->dt, qa, st));
-        LAUNCH(launch_attn_decode(m->dt, hd, kv->q, kc, vtc, kv->lens_dev, kv->y, kv->apart, B, H,
-                                  kv->S, max_chunks, st));
+        // QKV finish (norm scale, RoPE, QK-norm, cache write) + attention over the cache
+        DecAttnArgs at{};
+        at.qkv = kv->qkv; at.ss_in = kv->ss_a; at.ss_in_parts = ss_a_parts; at.ss_stride = ss;
+        at.norm_dim = d; at.eps = c.norm_eps; at.rope_cos = m->rope_cos; at.rope_sin = m->rope_sin;
+        at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = kv->apart;
+        at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.max_slots = max_slots;
+        LAUNCH(launch_attn_decode(m->dt, at, kv->y, st));
         // O + residual
         DecGemmArgs o = a;
         o.A = kv->y; o.lda = H * hd; o.W = L.wo; o.N = d; o.K = H * hd;
@@ -247,8 +248,8 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
     h.M = B; h.eps = c.norm_eps; h.cap = c.softcap; h.ss_stride = ss;
     h.A = kv->act; h.lda = d; h.W = m->lm; h.N = V; h.K = d;
     h.out_f32 = logits; h.ldo = V; h.ss_in = kv->ss_a; h.ss_in_parts = ss_a_parts;
+    h.lens_inc = kv->lens_dev;  // the step's last kernel also advances every row by one
     if ((s = decode_gemm(kv, EPI_SOFTCAP, h, st)) != NC_OK) return s;
-    LAUNCH(launch_lens_add(kv->lens_dev, B, 1, -1, st));
     return NC_OK;
 }
 
@@ -375,6 +376,7 @@ nc_status nc_kv_create(nc_model* m, int32_t batch, int32_t max_seq, nc_kv** out)
         if (!m) return fail(NC_ERR_INVALID_ARG, "model is NULL");
         if (batch < 1 || max_seq < 1) return fail(NC_ERR_INVALID_ARG, "batch and max_seq must be >= 1");
         if (max_seq > m->cfg.max_seq) return fail(NC_ERR_INVALID_ARG, "max_seq exceeds the model's max_seq");
+        if (max_seq > 32768) return fail(NC_ERR_UNSUPPORTED, "cache capacity above 32768 positions is not supported");
         nc_kv* kv = new nc_kv();
         kv->m = m;
         kv->B = batch;

@@ -58,8 +58,9 @@ typedef int32_t nc_status;
 #define NC_ABI_VERSION 1
 
 /* Model shape.  Requirements: d_model == n_head * head_dim; n_kv_head == 1 (multi-query
- * attention); head_dim in {64, 128}; d_model, d_ff multiples of 64; vocab >= 1;
- * max_seq >= 1 (longest position the RoPE table covers); softcap > 0; norm_eps >= 0. */
+ * attention); head_dim in {64, 128}; n_head <= 16; d_model <= 4096; d_model, d_ff
+ * multiples of 64; vocab >= 1; max_seq >= 1 (longest position the RoPE table covers);
+ * softcap > 0; norm_eps >= 0. */
 typedef struct nc_config {
     int32_t n_layer;
     int32_t d_model;
@@ -91,7 +92,8 @@ nc_status nc_model_create(const nc_config* cfg, const void* const* weights_dev,
                           nc_model** out);
 void nc_model_free(nc_model* m); /* NULL is a no-op; all kv objects must be freed first */
 
-/* KV cache for `batch` rows of up to `max_seq` positions (max_seq <= cfg.max_seq).
+/* KV cache for `batch` rows of up to `max_seq` positions (max_seq <= cfg.max_seq, and at
+ * most 32768: NC_ERR_UNSUPPORTED otherwise).
  * Layout (library-private): K [L][batch][max_seq][hd], V transposed [L][batch][hd][max_seq],
  * both cfg.dtype; keys are stored after RoPE and QK-norm.  All lengths start at 0. */
 nc_status nc_kv_create(nc_model* m, int32_t batch, int32_t max_seq, nc_kv** out);
