@@ -69,6 +69,40 @@ def cpu_baseline(shape, weights, wl, budget_s):
             "prefill_tokens_per_s": round(pre_rate, 2), "decode_tokens_per_s": round(dec_rate, 3)}
 
 
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2516.6  # MI355X dense bf16 matrix peak
+
+
+def roofline(nc, one_step, steps, stream):
+    """Time the decode and prefill projection kernels with HIP events around every launch
+    (library timing mode; graph event nodes for decode) over one more full step, and report
+    the roofline of the one that takes longer.  Decode projections are HBM-bound (bytes:
+    weights + activations + outputs, each once); prefill projections are MFMA-bound."""
+    import torch
+    res = {}
+    for cls, name in ((nc.NC_KC_DECODE_GEMM, "decode_gemm"), (nc.NC_KC_PREFILL_GEMM, "prefill_gemm")):
+        nc.nc_timing_enable(cls)
+        one_step(per_step=lambda: nc.nc_timing_read())
+        torch.cuda.synchronize()
+        launches, ms, byts, flops = nc.nc_timing_read()
+        res[name] = {"launches": int(launches), "ms_total": round(ms, 3),
+                     "avg_us": round(1000.0 * ms / max(launches, 1), 3),
+                     "GB_per_s": round(byts / (ms * 1e-3) / 1e9, 1) if ms > 0 else None,
+                     "TFLOP_per_s": round(flops / (ms * 1e-3) / 1e12, 1) if ms > 0 else None}
+    nc.nc_timing_enable(nc.NC_KC_NONE)
+    dom = max(res, key=lambda k: res[k]["ms_total"])
+    r = res[dom]
+    if dom == "decode_gemm":
+        roof = {"kernel": "dec_gemm_kernel (decode projections)", "bound": "hbm",
+                "achieved": r["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(r["GB_per_s"] / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        roof = {"kernel": "gemm_bf16_kernel (prefill projections)", "bound": "mfma",
+                "achieved": r["TFLOP_per_s"], "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(r["TFLOP_per_s"] / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
+    return roof, res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -99,7 +133,7 @@ def main():
     tok = torch.empty(B, device="cuda", dtype=torch.int32)
     zeros = np.zeros(B, dtype=np.int32)
 
-    def one_step(ev=None):
+    def one_step(ev=None, per_step=None):
         kv.set_lens(zeros)
         if ev:
             ev[0].record(stream)
@@ -111,6 +145,8 @@ def main():
         for _ in range(steps):
             kv.decode(tok, dlog, stream)
             nc.nc_argmax(dlog, B, shape.vocab, tok, stream)
+            if per_step:
+                per_step()
         if ev:
             ev[2].record(stream)
 
@@ -146,6 +182,7 @@ def main():
         "prefill_tokens_per_s": round(B * T / (pre_ms / 1000.0), 1),
         "decode_tokens_per_s": round(B * steps / (dec_ms / 1000.0), 1),
     }
+    out["roofline"], out["kernels"] = roofline(nc, one_step, steps, stream)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(shape, weights, wl, args.cpu_seconds)
     kv.close()

@@ -217,7 +217,7 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
     dim3 grid((T + 255) / 256, H, B);
     const float sl = 1.4426950408889634f / sqrtf((float)hd);
 #define NC_AP(TT, HDV)                                                                        \
-    hipLaunchKernelGGL((attn_prefill_kernel<TT, HDV>), grid, dim3(256), 0, st, (const TT*)q, \
+    NC_TLAUNCH((attn_prefill_kernel<TT, HDV>), grid, dim3(256), 0, st, (const TT*)q, \
                        (const TT*)kc, (const TT*)vtc, (TT*)y, T, H, S, sl)
     if (dt == BF16 && hd == 128) NC_AP(bf16, 128);
     else if (dt == BF16 && hd == 64) NC_AP(bf16, 64);

@@ -339,9 +339,9 @@ static hipError_t launch_e(DType dt, const GemmArgs& a, hipStream_t st) {
     dim3 grid(((a.N + TBN - 1) / TBN) * ((a.M + TBM - 1) / TBM), 1, a.k_split);
     if (dt == BF16) {
         if (a.k_split != 1 || a.K % 32) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((gemm_bf16_kernel<EPI>), grid, dim3(256), 0, st, a);
+        NC_TLAUNCH((gemm_bf16_kernel<EPI>), grid, dim3(256), 0, st, a);
     } else {
-        hipLaunchKernelGGL((gemm_f32_kernel<EPI>), grid, dim3(256), 0, st, a);
+        NC_TLAUNCH((gemm_f32_kernel<EPI>), grid, dim3(256), 0, st, a);
     }
     return hipGetLastError();
 }

@@ -147,7 +147,7 @@ static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant) {
     const int fm = a.M <= 32 ? 1 : (a.M <= 64 ? 2 : 4);
     const unsigned gy = (a.M + 32 * fm - 1) / (32 * fm);
     dim3 g(gx, gy);
-#define NC_DG(FMV, NWV, UV) hipLaunchKernelGGL((dec_gemm_kernel<T, FMV, NWV, UV, EPI>), g, dim3(NWV * 64), 0, st, a)
+#define NC_DG(FMV, NWV, UV) NC_TLAUNCH((dec_gemm_kernel<T, FMV, NWV, UV, EPI>), g, dim3(NWV * 64), 0, st, a)
     if (fm == 1) {
         if (variant == 1) NC_DG(1, 16, 4);
         else if (variant == 2) NC_DG(1, 8, 8);

@@ -2,10 +2,21 @@
 // launcher enqueues on `st` and returns hipGetLastError() of the launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace nc {
+
+// Kernel-timing hook.  While the library times a kernel class it sets these events around
+// a launch helper of that class; the helper launches through hipExtLaunchKernel, which
+// stamps them with the kernel's own start and end (null events: no stamps).
+struct LaunchStamp {
+    hipEvent_t start, stop;
+};
+extern thread_local LaunchStamp t_stamp;
+#define NC_TLAUNCH(K, grid, block, shm, st, ...) \
+    hipExtLaunchKernelGGL(K, grid, block, shm, st, ::nc::t_stamp.start, ::nc::t_stamp.stop, 0, __VA_ARGS__)
 
 enum DType { F32 = 0, BF16 = 1 };
 

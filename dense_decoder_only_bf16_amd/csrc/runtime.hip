@@ -34,6 +34,8 @@
 
 using namespace nc;
 
+thread_local LaunchStamp nc::t_stamp = {nullptr, nullptr};
+
 namespace {
 
 thread_local std::string g_err;
@@ -52,6 +54,27 @@ nc_status fail(nc_status code, const std::string& msg) {
     } while (0)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- kernel timing (diagnostics): every launch of one class of kernels gets a pair of HIP
+// events that its dispatch stamps with the kernel's start and end (hipExtLaunchKernel).
+// While a class is timed, decode steps launch their kernels one by one instead of replaying
+// a captured graph, since stamped launches cannot be captured.
+struct TimingPair {
+    hipEvent_t a, b;
+    double bytes, flops;
+};
+struct Timing {
+    int cls = NC_KC_NONE;
+    std::vector<TimingPair> pending;  // launches not yet read
+    long long launches = 0;
+    double ms = 0, bytes = 0, flops = 0;
+};
+Timing g_tm;
+
+void timing_release(TimingPair& tp) {
+    (void)hipEventDestroy(tp.a);
+    (void)hipEventDestroy(tp.b);
+}
 
 }  // namespace
 
@@ -105,8 +128,12 @@ struct nc_kv {
 
 namespace {
 
+void drop_graph(nc_kv::Graph& g) {
+    (void)hipGraphExecDestroy(g.exec);
+}
+
 void drop_graphs(nc_kv* kv) {
-    for (auto& g : kv->graphs) (void)hipGraphExecDestroy(g.exec);
+    for (auto& g : kv->graphs) drop_graph(g);
     kv->graphs.clear();
 }
 
@@ -191,9 +218,49 @@ nc_status launched(hipError_t e, const char* what) {
         if (s_ != NC_OK) return s_;                 \
     } while (0)
 
+// Launch `fn` (returning hipError_t); if kernel class `cls` is being timed, bracket it with
+// an event pair on `st` that carries its algorithmic bytes and flops.
+template <typename F>
+hipError_t timed(int cls, double bytes, double flops, hipStream_t st, F fn) {
+    if (g_tm.cls != cls) return fn();
+    TimingPair tp{nullptr, nullptr, bytes, flops};
+    hipError_t e = hipEventCreate(&tp.a);
+    if (e == hipSuccess) e = hipEventCreate(&tp.b);
+    if (e == hipSuccess) {
+        t_stamp = {tp.a, tp.b};
+        e = fn();
+        t_stamp = {nullptr, nullptr};
+    }
+    if (e != hipSuccess) {
+        if (tp.a) (void)hipEventDestroy(tp.a);
+        if (tp.b) (void)hipEventDestroy(tp.b);
+        return e;
+    }
+    g_tm.pending.push_back(tp);
+    return hipSuccess;
+}
+
+// Algorithmic bytes of a decode projection: weights, activations, and the epilogue's
+// outputs (RESID also reads x); flops 2 M N K.
 nc_status decode_gemm(nc_kv* kv, Epi epi, const DecGemmArgs& a, hipStream_t st) {
-    LAUNCH(launch_dec_gemm(kv->m->dt, epi, a, st));
+    const double es = (double)kv->m->esz, M = a.M, N = a.N, K = a.K;
+    double out = 0;
+    if (epi == EPI_STORE || epi == EPI_SOFTCAP) out = M * N * 4;
+    else if (epi == EPI_RELU2) out = M * N * es;
+    else out = M * N * (8 + es);
+    const double bytes = N * K * es + M * K * es + out;
+    LAUNCH(timed(NC_KC_DECODE_GEMM, bytes, 2 * M * N * K, st,
+                 [&] { return launch_dec_gemm(kv->m->dt, epi, a, st); }));
     return NC_OK;
+}
+
+// Prefill projection: flops 2 M N K; bytes: A, weights and the output once.
+hipError_t prefill_gemm(nc_model* m, Epi epi, const GemmArgs& g, hipStream_t st) {
+    const double es = (double)m->esz, M = g.M, N = g.N, K = g.K;
+    const double out = (epi == EPI_STORE || epi == EPI_SOFTCAP) ? M * N * 4
+                       : (epi == EPI_RELU2 ? M * N * es : M * N * (8 + es));
+    return timed(NC_KC_PREFILL_GEMM, M * K * es + N * K * es + out, 2 * M * N * K, st,
+                 [&] { return launch_gemm(m->dt, epi, g, st); });
 }
 
 // Enqueue one decode step (everything after the host-side checks) on `st`.
@@ -490,7 +557,7 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             // QKV raw product
             g.A = kv->act; g.B = L.wqkv; g.N = nqkv; g.K = d; g.Npad = nqkv;
             g.out_f32 = kv->qkv; g.ldo = nqkv; g.z_stride = 0;
-            LAUNCH(launch_gemm(m->dt, EPI_STORE, g, st));
+            LAUNCH(prefill_gemm(m, EPI_STORE, g, st));
             QkvPostArgs qa{};
             qa.part = kv->qkv; qa.splits = 1; qa.z_stride = 0; qa.M = Mi; qa.T = T; qa.H = H; qa.hd = hd;
             qa.ss_in = kv->ss_a; qa.ss_in_parts = ss_a_parts; qa.ss_stride = (int)kv->cap_m; qa.norm_dim = d;
@@ -498,19 +565,25 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             qa.q = kv->q; qa.kc = (char*)kv->kcache + l * per_layer; qa.vtc = (char*)kv->vcache + l * per_layer;
             qa.S = kv->S; qa.eps = c.norm_eps;
             LAUNCH(launch_qkv_post(m->dt, qa, st));
-            LAUNCH(launch_attn_prefill(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->y, B, T, H, kv->S, st));
+            {   // causal attention flops: 4 hd per visible (query, key) pair and head
+                const double fl = 4.0 * B * H * hd * (double)T * (T + 1) / 2.0;
+                const double by = (double)B * T * (H + 2 + H) * hd * m->esz;  // q, k, v in; y out
+                LAUNCH(timed(NC_KC_PREFILL_ATTN, by, fl, st, [&] {
+                    return launch_attn_prefill(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->y, B, T, H, kv->S, st);
+                }));
+            }
             // O product + residual
             g.A = kv->y; g.lda = H * hd; g.B = L.wo; g.N = d; g.K = H * hd; g.Npad = d;
             g.out_f32 = kv->x; g.out_t = kv->act; g.ldo = d; g.ss_out = kv->ss_b; g.ss_stride = (int)kv->cap_m;
-            LAUNCH(launch_gemm(m->dt, EPI_RESID, g, st));
+            LAUNCH(prefill_gemm(m, EPI_RESID, g, st));
             // FC + norm + relu^2
             g.A = kv->act; g.lda = d; g.B = L.wfc; g.N = F; g.K = d; g.Npad = F;
             g.out_t = kv->u; g.ldo = F; g.ss_in = kv->ss_b; g.ss_in_parts = parts_d; g.ss_stride = (int)kv->cap_m;
-            LAUNCH(launch_gemm(m->dt, EPI_RELU2, g, st));
+            LAUNCH(prefill_gemm(m, EPI_RELU2, g, st));
             // PROJ + residual
             g.A = kv->u; g.lda = F; g.B = L.wproj; g.N = d; g.K = F; g.Npad = d;
             g.out_f32 = kv->x; g.out_t = kv->act; g.ldo = d; g.ss_out = kv->ss_a; g.ss_stride = (int)kv->cap_m;
-            LAUNCH(launch_gemm(m->dt, EPI_RESID, g, st));
+            LAUNCH(prefill_gemm(m, EPI_RESID, g, st));
             ss_a_parts = parts_d;
         }
         if (logits) {
@@ -518,7 +591,7 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             g.A = kv->act; g.lda = d; g.B = m->lm; g.M = Mi; g.N = V; g.K = d; g.Npad = (V + 31) / 32 * 32; g.k_split = 1;
             g.out_f32 = logits; g.ldo = V; g.ss_in = kv->ss_a; g.ss_in_parts = ss_a_parts;
             g.ss_stride = (int)kv->cap_m; g.eps = c.norm_eps; g.cap = c.softcap;
-            LAUNCH(launch_gemm(m->dt, EPI_SOFTCAP, g, st));
+            LAUNCH(prefill_gemm(m, EPI_SOFTCAP, g, st));
         }
         LAUNCH(launch_lens_add(kv->lens_dev, B, 0, T, st));
         std::fill(kv->lens_host.begin(), kv->lens_host.end(), T);
@@ -540,28 +613,33 @@ nc_status nc_decode_step(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* k
         nc_status s = ws_ensure(kv, B);
         if (s != NC_OK) return s;
         hipStream_t st = (hipStream_t)stream;
-        if (!kv->use_graph) {
+        if (!kv->use_graph || g_tm.cls != NC_KC_NONE) {
             s = enqueue_decode(m, kv, tokens, logits, st);
         } else {
             hipGraphExec_t exec = nullptr;
-            for (auto& g : kv->graphs)
-                if (g.tokens == tokens && g.logits == logits) exec = g.exec;
+            for (const nc_kv::Graph& g : kv->graphs)
+                if (g.tokens == tokens && g.logits == logits) {
+                    exec = g.exec;
+                    break;
+                }
             if (!exec) {
                 if (!kv->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&kv->cap_stream, hipStreamNonBlocking));
                 HIP_TRY(hipStreamBeginCapture(kv->cap_stream, hipStreamCaptureModeThreadLocal));
                 s = enqueue_decode(m, kv, tokens, logits, kv->cap_stream);
                 hipGraph_t graph = nullptr;
                 hipError_t e = hipStreamEndCapture(kv->cap_stream, &graph);
-                if (s != NC_OK) {
+                if (s != NC_OK || e != hipSuccess) {
                     if (graph) (void)hipGraphDestroy(graph);
-                    return s;
+                    if (s != NC_OK) return s;
                 }
                 if (e != hipSuccess) return fail(NC_ERR_DEVICE, std::string("decode capture: ") + hipGetErrorString(e));
                 e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
                 (void)hipGraphDestroy(graph);
-                if (e != hipSuccess) return fail(NC_ERR_DEVICE, std::string("graph instantiate: ") + hipGetErrorString(e));
+                if (e != hipSuccess) {
+                    return fail(NC_ERR_DEVICE, std::string("graph instantiate: ") + hipGetErrorString(e));
+                }
                 if (kv->graphs.size() >= 8) {  // keep a handful of buffer pairs
-                    (void)hipGraphExecDestroy(kv->graphs.front().exec);
+                    drop_graph(kv->graphs.front());
                     kv->graphs.erase(kv->graphs.begin());
                 }
                 kv->graphs.push_back({tokens, logits, exec});
@@ -574,6 +652,45 @@ nc_status nc_decode_step(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* k
     } catch (...) {
         return fail(NC_ERR_DEVICE, "unexpected exception");
     }
+}
+
+nc_status nc_timing_enable(int32_t kernel_class) {
+    if (kernel_class < NC_KC_NONE || kernel_class > NC_KC_PREFILL_ATTN)
+        return fail(NC_ERR_INVALID_ARG, "unknown kernel class");
+    HIP_TRY(hipDeviceSynchronize());
+    for (auto& tp : g_tm.pending) timing_release(tp);
+    g_tm.pending.clear();
+    g_tm.cls = kernel_class;
+    g_tm.launches = 0;
+    g_tm.ms = g_tm.bytes = g_tm.flops = 0;
+    return NC_OK;
+}
+
+nc_status nc_timing_read(nc_timing* out) {
+    if (!out) return fail(NC_ERR_INVALID_ARG, "out is NULL");
+    HIP_TRY(hipDeviceSynchronize());
+    auto add = [](TimingPair& tp) -> hipError_t {
+        float ms = 0.f;
+        hipError_t e = hipEventElapsedTime(&ms, tp.a, tp.b);
+        if (e != hipSuccess) return e;
+        g_tm.launches++;
+        g_tm.ms += ms;
+        g_tm.bytes += tp.bytes;
+        g_tm.flops += tp.flops;
+        return hipSuccess;
+    };
+    hipError_t err = hipSuccess;
+    for (auto& tp : g_tm.pending) {
+        if (err == hipSuccess) err = add(tp);
+        timing_release(tp);
+    }
+    g_tm.pending.clear();
+    if (err != hipSuccess) return fail(NC_ERR_DEVICE, std::string("event timing: ") + hipGetErrorString(err));
+    out->launches = g_tm.launches;
+    out->ms = g_tm.ms;
+    out->bytes = g_tm.bytes;
+    out->flops = g_tm.flops;
+    return NC_OK;
 }
 
 }  // extern "C"

@@ -30,9 +30,14 @@ _CODE_NAMES = {NC_ERR_INVALID_ARG: "NC_ERR_INVALID_ARG", NC_ERR_UNSUPPORTED: "NC
                NC_ERR_OOM: "NC_ERR_OOM", NC_ERR_CAPACITY: "NC_ERR_CAPACITY",
                NC_ERR_STATE: "NC_ERR_STATE", NC_ERR_DEVICE: "NC_ERR_DEVICE"}
 
+NC_KC_NONE = 0
+NC_KC_DECODE_GEMM = 1
+NC_KC_PREFILL_GEMM = 2
+NC_KC_PREFILL_ATTN = 3
+
 EXPORTED = ("nc_model_create", "nc_model_free", "nc_kv_create", "nc_kv_free", "nc_kv_set_lens",
             "nc_kv_get_lens", "nc_kv_export", "nc_prefill", "nc_decode_step", "nc_argmax",
-            "nc_last_error", "nc_abi_version")
+            "nc_timing_enable", "nc_timing_read", "nc_last_error", "nc_abi_version")
 
 
 class NcError(RuntimeError):
@@ -48,6 +53,11 @@ class nc_config(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32),
                 ("rope_base", ctypes.c_float), ("softcap", ctypes.c_float),
                 ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class nc_timing(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64), ("ms", ctypes.c_double),
+                ("bytes", ctypes.c_double), ("flops", ctypes.c_double)]
 
 
 _lib = None
@@ -74,12 +84,15 @@ def lib():
         L.nc_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.nc_decode_step.argtypes = [vp, vp, i32, vp, vp, vp]
         L.nc_argmax.argtypes = [vp, i32, i32, vp, vp]
+        L.nc_timing_enable.argtypes = [i32]
+        L.nc_timing_read.argtypes = [ctypes.POINTER(nc_timing)]
         L.nc_last_error.argtypes = []
         L.nc_last_error.restype = ctypes.c_char_p
         L.nc_abi_version.argtypes = []
         L.nc_abi_version.restype = i32
         for name in ("nc_model_create", "nc_kv_create", "nc_kv_set_lens", "nc_kv_get_lens",
-                     "nc_kv_export", "nc_prefill", "nc_decode_step", "nc_argmax"):
+                     "nc_kv_export", "nc_prefill", "nc_decode_step", "nc_argmax",
+                     "nc_timing_enable", "nc_timing_read"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -172,6 +185,17 @@ def nc_decode_step(m, tokens, B, kv, logits, stream=None):
 
 def nc_argmax(logits, B, V, out, stream=None):
     _check(lib().nc_argmax(_ptr(logits), B, V, _ptr(out), _stream(stream)))
+
+
+def nc_timing_enable(kernel_class):
+    _check(lib().nc_timing_enable(kernel_class))
+
+
+def nc_timing_read():
+    """(launches, ms, bytes, flops) accumulated since nc_timing_enable."""
+    t = nc_timing()
+    _check(lib().nc_timing_read(ctypes.byref(t)))
+    return t.launches, t.ms, t.bytes, t.flops
 
 
 # ------------------------------------------------------------------ convenience -------

@@ -132,6 +132,27 @@ nc_status nc_decode_step(nc_model* m, const int32_t* tokens_dev, int32_t B, nc_k
 nc_status nc_argmax(const float* logits_dev, int32_t B, int32_t V, int32_t* out_dev,
                     void* stream);
 
+/* Kernel timing, for diagnostics and roofline reports.  When a kernel class is enabled,
+ * every launch of that class is bracketed by a pair of HIP events recorded on the launch
+ * stream, and decode steps launch their kernels one by one instead of replaying their
+ * captured graphs (which stay cached for when timing is switched off).  nc_timing_read
+ * synchronises the device and adds the pairs recorded since the last read to running
+ * totals: the number of launches, their summed event-to-event time, and the algorithmic
+ * bytes and flops of those launches.  nc_timing_enable resets the totals.  Process-wide,
+ * not thread-safe. */
+#define NC_KC_NONE 0
+#define NC_KC_DECODE_GEMM 1  /* decode projections: QKV, O, FC, PROJ, LM head            */
+#define NC_KC_PREFILL_GEMM 2 /* prefill projections                                       */
+#define NC_KC_PREFILL_ATTN 3 /* prefill attention                                         */
+typedef struct nc_timing {
+    int64_t launches;
+    double ms;    /* summed event-to-event time of the launches                           */
+    double bytes; /* algorithmic bytes: weights, activations and outputs, each moved once */
+    double flops; /* algorithmic flops: 2 M N K per product, 4 hd per visible score pair  */
+} nc_timing;
+nc_status nc_timing_enable(int32_t kernel_class);
+nc_status nc_timing_read(nc_timing* out);
+
 /* Message of the last error on the calling thread ("" if none). */
 const char* nc_last_error(void);
 int32_t nc_abi_version(void);

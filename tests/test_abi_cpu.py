@@ -38,6 +38,13 @@ def test_abi_version(L):
     assert nc.nc_abi_version() == 1
 
 
+def test_timing_struct_and_bad_class(L):
+    assert ctypes.sizeof(nc.nc_timing) == 32
+    assert L.nc_timing_enable(99) == nc.NC_ERR_INVALID_ARG
+    assert L.nc_timing_enable(-1) == nc.NC_ERR_INVALID_ARG
+    assert L.nc_timing_read(None) == nc.NC_ERR_INVALID_ARG
+
+
 def test_config_struct_layout():
     # 8 int32, 3 float, 1 int32 with no padding
     assert ctypes.sizeof(nc.nc_config) == 48

@@ -214,3 +214,34 @@ def test_decode_graph_replays_match_eager(small, monkeypatch):
     assert np.array_equal(kv_g.lens(), [140, 140, 140])
     kv_g.close()
     kv_e.close()
+
+
+def test_kernel_timing_counts_launches(small):
+    """Timing mode brackets every decode projection (4 per layer + LM head) and every
+    prefill projection (4 per layer + LM head) with events and reports the algorithmic
+    bytes and flops of those launches; decode stays correct while timed (eager launches)."""
+    torch = torch_mod()
+    w, orc, gm = small
+    s = SMALL_BF16
+    toks = make_tokens(s.vocab, 2, 40, seed=14)
+    nc.nc_timing_enable(nc.NC_KC_PREFILL_GEMM)
+    kv, _ = prefill(gm, toks[:, :32], 64)
+    launches, ms, byts, flops = nc.nc_timing_read()
+    assert launches == 4 * s.n_layer + 1 and ms > 0
+    M = 2 * 32
+    want_flops = s.n_layer * 2 * M * s.d_model * ((s.n_head + 2) * s.head_dim + s.d_model + 2 * s.d_ff)
+    want_flops += 2 * M * s.d_model * s.vocab
+    assert abs(flops - want_flops) / want_flops < 1e-9
+    nc.nc_timing_enable(nc.NC_KC_DECODE_GEMM)
+    tok_buf = torch.zeros(2, dtype=torch.int32, device="cuda")
+    out = torch.empty((2, s.vocab), device="cuda", dtype=torch.float32)
+    for step in range(3):
+        tok_buf.copy_(torch.from_numpy(toks[:, 32 + step].astype(np.int32)))
+        kv.decode(tok_buf, out)
+        launches, ms, byts, flops = nc.nc_timing_read()
+        assert launches == (step + 1) * (4 * s.n_layer + 1)
+        assert ms > 0 and byts > 0
+    want = orc.prefill(toks[:, :35], logits_at=[34])[0][:, 0]
+    assert np.max(np.abs(out.cpu().numpy() - want)) <= BF16_TOL  # timed graph still correct
+    nc.nc_timing_enable(nc.NC_KC_NONE)
+    kv.close()
