@@ -8,6 +8,13 @@
 // precedes a projection is applied as a row scale in the epilogue, from per-row sums of
 // squares that the producer of x left behind.
 //
+// Compensated operands: a bf16 operand carries a relative rounding error of up to 2^-9, and
+// in the MLP that error is amplified by the squared ReLU and summed over d_ff terms.  For
+// the MLP products the activation is therefore passed as two bf16 arrays, hi = bf16(a) and
+// lo = bf16(a - hi), and multiplied as hi W^T + lo W^T with fp32 accumulation, which
+// leaves a relative operand error near 2^-17 (the weights are exact bf16 values).  The
+// producing epilogue writes both parts.
+//
 // Tiling: a workgroup computes a 256 x 256 tile with 2 x 2 waves; each wave owns a
 // 128 x 128 sub-tile of 4 x 4 MFMA 32x32 tiles (256 accumulator registers).  Operands are
 // staged in LDS in the MFMA-blocked form [rows/32][K/16][32][16]: one 32x16 block is
@@ -95,14 +102,18 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[4
                     if (ok) p.out_f32[(long long)blockIdx.z * p.z_stride + o] = v;
                 } else if (EPI == EPI_RELU2) {
                     const float t = fmaxf(v * rs[rl], 0.f);
-                    if (ok) ((T*)p.out_t)[o] = from_f32<T>(t * t);
+                    const T hi = from_f32<T>(t * t);
+                    if (ok) ((T*)p.out_t)[o] = hi;
+                    if (ok && p.out_lo) ((T*)p.out_lo)[o] = from_f32<T>(t * t - to_f32(hi));
                 } else if (EPI == EPI_SOFTCAP) {
                     if (ok) p.out_f32[o] = p.cap * tanh_f32(v * rs[rl] / p.cap);
                 } else {  // EPI_RESID
                     if (ok) {
                         const float xn = p.out_f32[o] + v;
                         p.out_f32[o] = xn;
-                        ((T*)p.out_t)[o] = from_f32<T>(xn);
+                        const T hi = from_f32<T>(xn);
+                        ((T*)p.out_t)[o] = hi;
+                        if (p.out_lo) ((T*)p.out_lo)[o] = from_f32<T>(xn - to_f32(hi));
                         sq += xn * xn;
                     }
                 }
@@ -143,8 +154,12 @@ void gemm_bf16_kernel(GemmArgs p) {
     int m0, n0, tn;
     tile_coords(p, m0, n0, tn);
     const int ksteps = p.K / 16;
-    const int nk = p.K / BK;
+    // A compensated product runs twice as many K tiles: tile 2k takes A's columns of tile
+    // k, tile 2k + 1 the same columns of A_lo, both against the same weight block.
+    const bool comp = p.A_lo != nullptr;
+    const int nk = comp ? 2 * (p.K / BK) : p.K / BK;
     const bf16* A = (const bf16*)p.A;
+    const bf16* A_lo = (const bf16*)p.A_lo;
     const bf16* B = (const bf16*)p.B;
 
     if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) tile_row_scales(p, m0, rs, 256);
@@ -155,14 +170,15 @@ void gemm_bf16_kernel(GemmArgs p) {
     // address; their outputs are masked in the epilogue.
     auto issue = [&](int kt) {
         bf16* sbase = lds + (kt % NS) * STAGE;
-        const int k0 = kt * BK;
+        const int k0 = (comp ? kt >> 1 : kt) * BK;
+        const bf16* As = (comp && (kt & 1)) ? A_lo : A;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int b = wave * 4 + u;
             const int rb = b / KB, kb = b % KB;
             int m = m0 + rb * 32 + lane / 2;
             m = m < p.M ? m : p.M - 1;
-            const bf16* src = A + (long long)m * p.lda + k0 + kb * 16 + (lane % 2) * 8;
+            const bf16* src = As + (long long)m * p.lda + k0 + kb * 16 + (lane % 2) * 8;
             __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(sbase + b * 512), 16, 0, 0);
         }
 #pragma unroll
@@ -341,6 +357,7 @@ static hipError_t launch_e(DType dt, const GemmArgs& a, hipStream_t st) {
         if (a.k_split != 1 || a.K % 32) return hipErrorInvalidValue;
         NC_TLAUNCH((gemm_bf16_kernel<EPI>), grid, dim3(256), 0, st, a);
     } else {
+        if (a.A_lo || a.out_lo) return hipErrorInvalidValue;  // fp32 operands need no compensation
         NC_TLAUNCH((gemm_f32_kernel<EPI>), grid, dim3(256), 0, st, a);
     }
     return hipGetLastError();

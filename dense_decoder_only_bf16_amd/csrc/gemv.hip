@@ -34,7 +34,9 @@ __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, in
         if (ok) p.out_f32[o] = v;
     } else if (EPI == EPI_RELU2) {
         const float t = fmaxf(v * r, 0.f);
-        if (ok) ((T*)p.out_t)[o] = from_f32<T>(t * t);
+        const T hi = from_f32<T>(t * t);
+        if (ok) ((T*)p.out_t)[o] = hi;
+        if (ok && p.out_lo) ((T*)p.out_lo)[o] = from_f32<T>(t * t - to_f32(hi));
     } else if (EPI == EPI_SOFTCAP) {
         if (ok) p.out_f32[o] = p.cap * tanh_f32(v * r / p.cap);
     } else {  // EPI_RESID
@@ -42,7 +44,9 @@ __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, in
         if (ok) {
             xn = p.out_f32[o] + v;
             p.out_f32[o] = xn;
-            ((T*)p.out_t)[o] = from_f32<T>(xn);
+            const T hi = from_f32<T>(xn);
+            ((T*)p.out_t)[o] = hi;
+            if (p.out_lo) ((T*)p.out_lo)[o] = from_f32<T>(xn - to_f32(hi));
         }
         const float sq = wave_sum(xn * xn);
         if (lane == 0) p.ss_out[(long long)blockIdx.x * p.ss_stride + m] = sq;
@@ -54,8 +58,9 @@ __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, in
 // Each wave walks its K range in groups of U 16-deep steps with two register buffers: the
 // loads of group g + 1 are issued before the MFMAs of group g, so 2U steps (2U KB of
 // weights per wave for bf16) are in flight.  The weight operand of a step is one
-// contiguous 32x16 block of the blocked layout.
-template <typename T, int FM, int NW, int U, int EPI>
+// contiguous 32x16 block of the blocked layout.  LO: compensated operand (A + A_lo), one
+// more MFMA per step against the same weight registers.
+template <typename T, int FM, int NW, int U, int EPI, bool LO>
 __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
     typedef typename Chunk<T>::type CT;
     constexpr int BM = 32 * FM, BN = 32, TP = BN + 1;
@@ -73,22 +78,26 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
     const T* A = (const T*)p.A;
     const T* wb = (const T*)p.W + (long long)(n0 / 32) * ksteps * 512 + l32 * 16 + 8 * hh;
     const T* arow[FM];
+    const T* lrow[FM];
     bool mok[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int m = m0 + 32 * i + l32;
         mok[i] = m < p.M;
-        arow[i] = A + (long long)(mok[i] ? m : 0) * p.lda + 8 * hh;
+        const long long off = (long long)(mok[i] ? m : 0) * p.lda + 8 * hh;
+        arow[i] = A + off;
+        lrow[i] = LO ? (const T*)p.A_lo + off : arow[i];
     }
 
     f32x16 acc[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) acc[i] = zero_vec<f32x16>();
-    CT wf0[U], wf1[U], af0[U][FM], af1[U][FM];
+    constexpr int NA = LO ? 2 : 1;  // activation parts
+    CT wf0[U], wf1[U], af0[U][NA][FM], af1[U][NA][FM];
     // Loads are unconditional (addresses clamped into valid memory); rows past M are zeroed
     // with a bit mask and steps past the wave's range (a wave-uniform condition) with a
     // select, so no load sits behind a divergent branch.
-    auto load = [&](CT (&wf)[U], CT (&af)[U][FM], int sb) {
+    auto load = [&](CT (&wf)[U], CT (&af)[U][NA][FM], int sb) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int s = sb + u;
@@ -96,14 +105,19 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
             const int sc = ok ? s : s1 - 1;
             wf[u] = load_masked(wb + (long long)sc * 512, ok);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) af[u][i] = load_masked(arow[i] + sc * 16, ok && mok[i]);
+            for (int i = 0; i < FM; ++i) {
+                af[u][0][i] = load_masked(arow[i] + sc * 16, ok && mok[i]);
+                if (LO) af[u][NA - 1][i] = load_masked(lrow[i] + sc * 16, ok && mok[i]);
+            }
         }
     };
-    auto mma = [&](CT (&wf)[U], CT (&af)[U][FM]) {
+    auto mma = [&](CT (&wf)[U], CT (&af)[U][NA][FM]) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int i = 0; i < FM; ++i) acc[i] = mma32(af[u][i], wf[u], acc[i]);
+            for (int h = 0; h < NA; ++h)
+#pragma unroll
+                for (int i = 0; i < FM; ++i) acc[i] = mma32(af[u][h][i], wf[u], acc[i]);
     };
     if (s1 > s0) load(wf0, af0, s0);
     for (int sb = s0; sb < s1; sb += 2 * U) {
@@ -141,13 +155,13 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
 }
 
 // Launch shape.  `variant` picks alternative (waves, steps-in-flight) choices for tuning.
-template <typename T, int EPI>
+template <typename T, int EPI, bool LO>
 static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant) {
     const unsigned gx = (a.N + DEC_BN - 1) / DEC_BN;
     const int fm = a.M <= 32 ? 1 : (a.M <= 64 ? 2 : 4);
     const unsigned gy = (a.M + 32 * fm - 1) / (32 * fm);
     dim3 g(gx, gy);
-#define NC_DG(FMV, NWV, UV) NC_TLAUNCH((dec_gemm_kernel<T, FMV, NWV, UV, EPI>), g, dim3(NWV * 64), 0, st, a)
+#define NC_DG(FMV, NWV, UV) NC_TLAUNCH((dec_gemm_kernel<T, FMV, NWV, UV, EPI, LO>), g, dim3(NWV * 64), 0, st, a)
     if (fm == 1) {
         if (variant == 1) NC_DG(1, 16, 4);
         else if (variant == 2) NC_DG(1, 8, 8);
@@ -175,11 +189,16 @@ int dec_gemm_tile_n() { return DEC_BN; }
 
 template <typename T>
 static hipError_t dec_dt(Epi epi, const DecGemmArgs& a, hipStream_t st, int variant) {
+    // compensated operands exist for the MLP products only (bf16 RELU2 and RESID)
+    const bool lo = a.A_lo != nullptr;
+    if (lo && (sizeof(T) != 2 || (epi != EPI_RELU2 && epi != EPI_RESID))) return hipErrorInvalidValue;
     switch (epi) {
-        case EPI_STORE: return dec_t<T, EPI_STORE>(a, st, variant);
-        case EPI_RELU2: return dec_t<T, EPI_RELU2>(a, st, variant);
-        case EPI_RESID: return dec_t<T, EPI_RESID>(a, st, variant);
-        case EPI_SOFTCAP: return dec_t<T, EPI_SOFTCAP>(a, st, variant);
+        case EPI_STORE: return dec_t<T, EPI_STORE, false>(a, st, variant);
+        case EPI_RELU2:
+            return lo ? dec_t<T, EPI_RELU2, sizeof(T) == 2>(a, st, variant) : dec_t<T, EPI_RELU2, false>(a, st, variant);
+        case EPI_RESID:
+            return lo ? dec_t<T, EPI_RESID, sizeof(T) == 2>(a, st, variant) : dec_t<T, EPI_RESID, false>(a, st, variant);
+        case EPI_SOFTCAP: return dec_t<T, EPI_SOFTCAP, false>(a, st, variant);
         default: return hipErrorInvalidValue;
     }
 }

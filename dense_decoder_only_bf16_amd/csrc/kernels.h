@@ -48,6 +48,12 @@ struct GemmArgs {
     int ss_in_parts, ss_stride;
     float* ss_out;      // RESID: ss_out[tile_n * ss_stride + m]
     float eps, cap;
+    // Compensated operand (bf16 only): A_lo [M][lda] holds a - bf16(a) in bf16, and the
+    // product is taken over both parts (A + A_lo) W^T.  Null: plain A.
+    const void* A_lo;
+    // RELU2 / RESID: also write value - dtype(value) in dtype here (the low part a later
+    // compensated product reads).  Null: not written.
+    void* out_lo;
 };
 
 // Prefill product (M in the thousands): 256 x 256 tiles.
@@ -67,6 +73,8 @@ struct DecGemmArgs {
     float* ss_out;
     float eps, cap;
     int32_t* lens_inc;  // if set, workgroup 0 adds one to lens_inc[0..M) (end of a decode step)
+    const void* A_lo;   // compensated operand, as in GemmArgs (bf16 only; null: plain A)
+    void* out_lo;       // RELU2 / RESID low-part output, as in GemmArgs (null: not written)
 };
 int dec_gemm_tile_n();
 hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t st, int variant = 0);

@@ -113,6 +113,8 @@ struct nc_kv {
     void* q = nullptr;        // [M][H][hd]
     void* y = nullptr;        // [M][H hd] attention output
     void* u = nullptr;        // [M][d_ff] MLP hidden
+    void* act_lo = nullptr;   // bf16 only: low parts of the MLP operands (compensated
+    void* u_lo = nullptr;     // products): x - bf16(x) after attention, u - bf16(u)
     float* apart = nullptr;   // decode attention partials
     long long apart_elems = 0;
     // decode step captured as a HIP graph, keyed by the caller's token/logit buffers
@@ -139,11 +141,13 @@ void drop_graphs(nc_kv* kv) {
 
 void ws_free(nc_kv* kv) {
     drop_graphs(kv);  // captured graphs point into the workspace
-    void* ptrs[] = {kv->x, kv->act, kv->ss_a, kv->ss_b, kv->qkv, kv->q, kv->y, kv->u, kv->apart};
+    void* ptrs[] = {kv->x, kv->act, kv->ss_a, kv->ss_b, kv->qkv, kv->q, kv->y, kv->u, kv->apart,
+                    kv->act_lo, kv->u_lo};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     kv->x = nullptr; kv->act = nullptr; kv->ss_a = nullptr; kv->ss_b = nullptr; kv->qkv = nullptr;
     kv->q = nullptr; kv->y = nullptr; kv->u = nullptr; kv->apart = nullptr;
+    kv->act_lo = nullptr; kv->u_lo = nullptr;
     kv->cap_m = 0;
     kv->apart_elems = 0;
 }
@@ -169,6 +173,10 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
     WS_ALLOC(kv->q, M * hq * es);
     WS_ALLOC(kv->y, M * hq * es);
     WS_ALLOC(kv->u, M * c.d_ff * es);
+    if (kv->m->dt == BF16) {
+        WS_ALLOC(kv->act_lo, M * d * es);
+        WS_ALLOC(kv->u_lo, M * c.d_ff * es);
+    }
     kv->apart_elems = (long long)kv->B * attn_decode_slots(kv->S) * 16 * (c.head_dim + 2);
     WS_ALLOC(kv->apart, kv->apart_elems * 4);
 #undef WS_ALLOC
@@ -240,26 +248,30 @@ hipError_t timed(int cls, double bytes, double flops, hipStream_t st, F fn) {
     return hipSuccess;
 }
 
-// Algorithmic bytes of a decode projection: weights, activations, and the epilogue's
-// outputs (RESID also reads x); flops 2 M N K.
+// Algorithmic bytes of a decode projection: weights, activations (both parts of a
+// compensated operand), and the epilogue's outputs (RESID also reads x; low parts where
+// written); flops 2 M N K of the model (the extra MFMAs of the low part are not counted).
 nc_status decode_gemm(nc_kv* kv, Epi epi, const DecGemmArgs& a, hipStream_t st) {
     const double es = (double)kv->m->esz, M = a.M, N = a.N, K = a.K;
     double out = 0;
     if (epi == EPI_STORE || epi == EPI_SOFTCAP) out = M * N * 4;
     else if (epi == EPI_RELU2) out = M * N * es;
     else out = M * N * (8 + es);
-    const double bytes = N * K * es + M * K * es + out;
+    if (a.out_lo) out += M * N * es;
+    const double bytes = N * K * es + M * K * es * (a.A_lo ? 2 : 1) + out;
     LAUNCH(timed(NC_KC_DECODE_GEMM, bytes, 2 * M * N * K, st,
                  [&] { return launch_dec_gemm(kv->m->dt, epi, a, st); }));
     return NC_OK;
 }
 
-// Prefill projection: flops 2 M N K; bytes: A, weights and the output once.
+// Prefill projection: flops 2 M N K of the model; bytes: A (both parts when compensated),
+// weights and the outputs once.
 hipError_t prefill_gemm(nc_model* m, Epi epi, const GemmArgs& g, hipStream_t st) {
     const double es = (double)m->esz, M = g.M, N = g.N, K = g.K;
-    const double out = (epi == EPI_STORE || epi == EPI_SOFTCAP) ? M * N * 4
-                       : (epi == EPI_RELU2 ? M * N * es : M * N * (8 + es));
-    return timed(NC_KC_PREFILL_GEMM, M * K * es + N * K * es + out, 2 * M * N * K, st,
+    const double out = ((epi == EPI_STORE || epi == EPI_SOFTCAP) ? M * N * 4
+                        : (epi == EPI_RELU2 ? M * N * es : M * N * (8 + es))) +
+                       (g.out_lo ? M * N * es : 0);
+    return timed(NC_KC_PREFILL_GEMM, M * K * es * (g.A_lo ? 2 : 1) + N * K * es + out, 2 * M * N * K, st,
                  [&] { return launch_gemm(m->dt, epi, g, st); });
 }
 
@@ -298,15 +310,16 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         DecGemmArgs o = a;
         o.A = kv->y; o.lda = H * hd; o.W = L.wo; o.N = d; o.K = H * hd;
         o.out_f32 = kv->x; o.out_t = kv->act; o.ldo = d; o.ss_out = kv->ss_b;
+        o.out_lo = kv->act_lo;
         if ((s = decode_gemm(kv, EPI_RESID, o, st)) != NC_OK) return s;
-        // FC + norm scale + relu^2
+        // FC + norm scale + relu^2 (compensated operand)
         DecGemmArgs f = a;
-        f.A = kv->act; f.lda = d; f.W = L.wfc; f.N = F; f.K = d;
-        f.out_t = kv->u; f.ldo = F; f.ss_in = kv->ss_b; f.ss_in_parts = parts_d;
+        f.A = kv->act; f.A_lo = kv->act_lo; f.lda = d; f.W = L.wfc; f.N = F; f.K = d;
+        f.out_t = kv->u; f.out_lo = kv->u_lo; f.ldo = F; f.ss_in = kv->ss_b; f.ss_in_parts = parts_d;
         if ((s = decode_gemm(kv, EPI_RELU2, f, st)) != NC_OK) return s;
-        // PROJ + residual
+        // PROJ + residual (compensated operand)
         DecGemmArgs pj = a;
-        pj.A = kv->u; pj.lda = F; pj.W = L.wproj; pj.N = d; pj.K = F;
+        pj.A = kv->u; pj.A_lo = kv->u_lo; pj.lda = F; pj.W = L.wproj; pj.N = d; pj.K = F;
         pj.out_f32 = kv->x; pj.out_t = kv->act; pj.ldo = d; pj.ss_out = kv->ss_a;
         if ((s = decode_gemm(kv, EPI_RESID, pj, st)) != NC_OK) return s;
         ss_a_parts = parts_d;
@@ -575,15 +588,19 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             // O product + residual
             g.A = kv->y; g.lda = H * hd; g.B = L.wo; g.N = d; g.K = H * hd; g.Npad = d;
             g.out_f32 = kv->x; g.out_t = kv->act; g.ldo = d; g.ss_out = kv->ss_b; g.ss_stride = (int)kv->cap_m;
+            g.A_lo = nullptr; g.out_lo = kv->act_lo;
             LAUNCH(prefill_gemm(m, EPI_RESID, g, st));
-            // FC + norm + relu^2
+            // FC + norm + relu^2 (compensated operand)
             g.A = kv->act; g.lda = d; g.B = L.wfc; g.N = F; g.K = d; g.Npad = F;
             g.out_t = kv->u; g.ldo = F; g.ss_in = kv->ss_b; g.ss_in_parts = parts_d; g.ss_stride = (int)kv->cap_m;
+            g.A_lo = kv->act_lo; g.out_lo = kv->u_lo;
             LAUNCH(prefill_gemm(m, EPI_RELU2, g, st));
-            // PROJ + residual
+            // PROJ + residual (compensated operand)
             g.A = kv->u; g.lda = F; g.B = L.wproj; g.N = d; g.K = F; g.Npad = d;
             g.out_f32 = kv->x; g.out_t = kv->act; g.ldo = d; g.ss_out = kv->ss_a; g.ss_stride = (int)kv->cap_m;
+            g.A_lo = kv->u_lo; g.out_lo = nullptr;
             LAUNCH(prefill_gemm(m, EPI_RESID, g, st));
+            g.A_lo = nullptr;
             ss_a_parts = parts_d;
         }
         if (logits) {
