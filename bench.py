@@ -1,11 +1,15 @@
 """Benchmark of the nanochat GPT forward on one MI355X through libnc.so.
 
 One step = the whole hot path over one batch: prefill of B x T prompt tokens with fp32
-logits at every position, then `decode_steps` greedy decode steps (argmax fed back), on the
-d12 bf16 model (12 layers, d=768, 6x128 heads, one K/V head, MLP 3072, vocab 65536) with
-seeded N(0, 0.02) weights and uniform random token ids.  Prints one JSON line.
+logits at every position, then greedy decode steps (argmax fed back).  Default workload:
+the d12 bf16 model (12 layers, d=768, 6x128 heads, one K/V head, MLP 3072, vocab 65536),
+prefill 8 x 2048 then 256 decode steps of the same 8 rows, seeded N(0, 0.02) weights and
+uniform random token ids.  Other workloads (d20: prefill 32 x 2048 and 128 decode steps of
+64 rows at context 2048; d26: prefill 16 x 2048; d30: 256 decode steps of 128 rows at
+context lengths uniform in [256, 2048]; tiny) build a separate decode context outside the
+timed steps.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload d12|d20|d30|tiny] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload d12|d20|d26|d30|tiny] [--no-cpu]
 """
 
 from __future__ import annotations
@@ -44,7 +48,7 @@ def cpu_baseline(shape, weights, wl, budget_s):
         threads = len(os.sched_getaffinity(0))
     from dense_decoder_only_bf16_amd.inputs import make_tokens
     orc = OracleModel(shape, weights)
-    t_pre = min(wl.prefill_len, 2048)
+    t_pre = min(wl.prefill_len or wl.decode_context, 2048)  # decode-only: its context
     prompt = make_tokens(shape.vocab, 1, t_pre, seed=1)
     t0 = time.perf_counter()
     logits, cache = orc.prefill(prompt, max_seq=t_pre + 64, logits_at=[t_pre - 1])
@@ -60,7 +64,7 @@ def cpu_baseline(shape, weights, wl, budget_s):
     dec_rate = steps / (t3 - t2)
     n_pre = wl.prefill_batch * wl.prefill_len
     n_dec = wl.decode_batch * wl.decode_steps
-    value = (n_pre + n_dec) / (n_pre / pre_rate + n_dec / dec_rate)
+    value = (n_pre + n_dec) / (n_pre / pre_rate + (n_dec / dec_rate if n_dec else 0.0))
     return {"value": round(value, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"fp64 numpy oracle, 1 row: prefill {t_pre} tokens ({t1 - t0:.1f} s, "
                        f"{pre_rate:.1f} tok/s) + {steps} greedy decode steps at context "
@@ -69,37 +73,54 @@ def cpu_baseline(shape, weights, wl, budget_s):
             "prefill_tokens_per_s": round(pre_rate, 2), "decode_tokens_per_s": round(dec_rate, 3)}
 
 
-HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
-MFMA_BF16_PEAK_TFS = 2516.6  # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2516.6  # MI355X dense bf16 matrix peak (256 CUs x 4096 flop/clk x 2.4 GHz)
+FP32_VEC_PEAK_TFS = 157.3    # MI355X fp32 (the tiny fp32 model's products)
+
+CLASSES = (  # (timing class, name, bound); classes without a launch in the workload are skipped
+    ("NC_KC_DECODE_GEMM", "decode_gemm", "hbm"),
+    ("NC_KC_DECODE_ATTN", "decode_attn", "hbm"),
+    ("NC_KC_PREFILL_GEMM", "prefill_gemm", "mfma"),
+    ("NC_KC_PREFILL_ATTN", "prefill_attn", "mfma"),
+)
+KERNEL_NAMES = {"decode_gemm": "dec_gemm_kernel (decode projections)",
+                "decode_attn": "attn_decode_split_kernel + attn_decode_combine_kernel",
+                "prefill_gemm": "gemm_bf16_kernel (prefill projections)",
+                "prefill_attn": "attn_prefill_kernel"}
 
 
-def roofline(nc, one_step, steps, stream):
-    """Time the decode and prefill projection kernels with HIP events around every launch
-    (library timing mode; graph event nodes for decode) over one more full step, and report
-    the roofline of the one that takes longer.  Decode projections are HBM-bound (bytes:
-    weights + activations + outputs, each once); prefill projections are MFMA-bound."""
+def roofline(nc, one_step, dtype):
+    """Kernel timing pass: one more full step per kernel class with the library's timing
+    mode on (every kernel of the class launched with dispatch-stamped start/stop events on
+    its stream; decode launches eager instead of graph replays).  Reports, per class, the
+    launches, the average kernel time per launch and the algorithmic GB/s and TFLOP/s; the
+    roofline object is the class with the largest total kernel time."""
     import torch
     res = {}
-    for cls, name in ((nc.NC_KC_DECODE_GEMM, "decode_gemm"), (nc.NC_KC_PREFILL_GEMM, "prefill_gemm")):
-        nc.nc_timing_enable(cls)
-        one_step(per_step=lambda: nc.nc_timing_read())
+    for cname, name, bound in CLASSES:
+        nc.nc_timing_enable(getattr(nc, cname))
+        one_step(per_decode_step=nc.nc_timing_read)
         torch.cuda.synchronize()
         launches, ms, byts, flops = nc.nc_timing_read()
+        if launches == 0:
+            continue
         res[name] = {"launches": int(launches), "ms_total": round(ms, 3),
-                     "avg_us": round(1000.0 * ms / max(launches, 1), 3),
-                     "GB_per_s": round(byts / (ms * 1e-3) / 1e9, 1) if ms > 0 else None,
-                     "TFLOP_per_s": round(flops / (ms * 1e-3) / 1e12, 1) if ms > 0 else None}
+                     "avg_us": round(1000.0 * ms / launches, 3),
+                     "GB_per_s": round(byts / (ms * 1e-3) / 1e9, 1),
+                     "TFLOP_per_s": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "bytes_per_launch": byts / launches, "flops_per_launch": flops / launches,
+                     "bound": bound}
     nc.nc_timing_enable(nc.NC_KC_NONE)
     dom = max(res, key=lambda k: res[k]["ms_total"])
     r = res[dom]
-    if dom == "decode_gemm":
-        roof = {"kernel": "dec_gemm_kernel (decode projections)", "bound": "hbm",
-                "achieved": r["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(r["GB_per_s"] / HBM_PEAK_GBS, 4), "traffic": None}
+    if r["bound"] == "hbm":
+        ach, peak, unit = r["GB_per_s"], HBM_PEAK_GBS, "GB/s"
     else:
-        roof = {"kernel": "gemm_bf16_kernel (prefill projections)", "bound": "mfma",
-                "achieved": r["TFLOP_per_s"], "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": round(r["TFLOP_per_s"] / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
+        ach, unit = r["TFLOP_per_s"], "TFLOP/s"
+        peak = MFMA_BF16_PEAK_TFS if dtype == "bf16" else FP32_VEC_PEAK_TFS
+    roof = {"kernel": KERNEL_NAMES[dom], "bound": r["bound"], "achieved": ach, "peak": peak,
+            "unit": unit, "frac": round(ach / peak, 4), "traffic": None,
+            "avg_launch_us": r["avg_us"], "launches": r["launches"]}
     return roof, res
 
 
@@ -113,40 +134,61 @@ def main():
     import torch
 
     from dense_decoder_only_bf16_amd import nc
-    from dense_decoder_only_bf16_amd.inputs import WORKLOADS, canonical_list, make_tokens, make_weights
+    from dense_decoder_only_bf16_amd.inputs import (WORKLOADS, canonical_list, make_lens,
+                                                    make_tokens, make_weights)
 
     wl = WORKLOADS[args.workload]
     shape = wl.shape
-    if wl.prefill_batch == 0 or wl.decode_steps == 0 or wl.decode_batch != wl.prefill_batch:
-        print("bench.py times workloads that prefill and then decode the same batch "
-              "(tiny, d12)", file=sys.stderr)
-        sys.exit(2)
-    B, T, steps = wl.prefill_batch, wl.prefill_len, wl.decode_steps
-    max_seq = T + steps
+    Bp, T = wl.prefill_batch, wl.prefill_len
+    Bd, steps = wl.decode_batch, wl.decode_steps
+    shared = Bp > 0 and Bd == Bp  # decode continues the prefilled rows
     weights = make_weights(shape, seed=0)
     model = nc.Model(shape, canonical_list(weights), max_seq=shape.max_seq)
-    kv = model.new_kv(B, max_seq)
     stream = torch.cuda.current_stream()
-    tokens = torch.from_numpy(make_tokens(shape.vocab, B, T, seed=1)).cuda()
-    logits = torch.empty((B, T, shape.vocab), device="cuda", dtype=torch.float32)
-    dlog = torch.empty((B, shape.vocab), device="cuda", dtype=torch.float32)
-    tok = torch.empty(B, device="cuda", dtype=torch.int32)
-    zeros = np.zeros(B, dtype=np.int32)
+    V = shape.vocab
 
-    def one_step(ev=None, per_step=None):
-        kv.set_lens(zeros)
+    kv_p = logits = tokens = None
+    if Bp:
+        kv_p = model.new_kv(Bp, T + (steps if shared else 0))
+        tokens = torch.from_numpy(make_tokens(V, Bp, T, seed=1)).cuda()
+        logits = torch.empty((Bp, T, V), device="cuda", dtype=torch.float32)
+    kv_d = dlog = tok = ctx = None
+    if steps:
+        dlog = torch.empty((Bd, V), device="cuda", dtype=torch.float32)
+        tok = torch.zeros(Bd, device="cuda", dtype=torch.int32)
+        if shared:
+            kv_d = kv_p
+        else:  # decode context built once, outside the timed steps: prefill without logits,
+            # then per-row lengths; every step re-truncates to them (exact, by causality)
+            C = wl.decode_context
+            kv_d = model.new_kv(Bd, C + steps)
+            kv_d.prefill(torch.from_numpy(make_tokens(V, Bd, C, seed=1)).cuda(), None, stream)
+            ctx = (make_lens(Bd, 256, C, seed=2) if wl.mixed_lengths
+                   else np.full(Bd, C, dtype=np.int32))
+            kv_d.set_lens(ctx)
+            first = torch.from_numpy(make_tokens(V, 1, Bd, seed=3)[0]).cuda()
+    zeros = np.zeros(max(Bp, 1), dtype=np.int32)
+
+    def one_step(ev=None, per_decode_step=None):
         if ev:
             ev[0].record(stream)
-        kv.prefill(tokens, logits, stream)
-        for b in range(B):  # greedy pick from each row's last prompt position
-            nc.nc_argmax(logits[b, T - 1], 1, shape.vocab, tok[b:b + 1], stream)
+        if Bp:
+            kv_p.set_lens(zeros[:Bp])
+            kv_p.prefill(tokens, logits, stream)
+            if shared:  # greedy pick from each row's last prompt position
+                for b in range(Bp):
+                    nc.nc_argmax(logits[b, T - 1], 1, V, tok[b:b + 1], stream)
         if ev:
             ev[1].record(stream)
-        for _ in range(steps):
-            kv.decode(tok, dlog, stream)
-            nc.nc_argmax(dlog, B, shape.vocab, tok, stream)
-            if per_step:
-                per_step()
+        if steps:
+            if not shared:
+                kv_d.set_lens(ctx)
+                tok.copy_(first)
+            for _ in range(steps):
+                kv_d.decode(tok, dlog, stream)
+                nc.nc_argmax(dlog, Bd, V, tok, stream)
+                if per_decode_step:
+                    per_decode_step()
         if ev:
             ev[2].record(stream)
 
@@ -163,29 +205,39 @@ def main():
     pre_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
     dec_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
     ms_per_step = wall * 1000.0 / args.steps
-    n_tok = B * T + B * steps
+    n_pre, n_dec = Bp * T, Bd * steps
+    desc = (f"{args.workload} ({shape.n_layer} layers, d {shape.d_model}, {shape.n_head}x"
+            f"{shape.head_dim} query heads, 1 K/V head, MLP {shape.d_ff}, vocab {V}, "
+            f"{shape.dtype}):")
+    if Bp:
+        desc += f" prefill {Bp}x{T} with fp32 logits at every position"
+    if steps:
+        ctxd = ("the prefilled rows" if shared else
+                (f"context lengths U{{256..{wl.decode_context}}} (built untimed)" if wl.mixed_lengths
+                 else f"context {wl.decode_context} (built untimed)"))
+        desc += (", then" if Bp else "") + f" {steps} greedy decode steps of {Bd} rows from {ctxd}"
     out = {
         "metric": "prefill tokens/s + decode tokens/s (1 GPU); % MFMA peak / % HBM BW",
-        "value": round(n_tok / (ms_per_step / 1000.0), 1),
+        "value": round((n_pre + n_dec) / (ms_per_step / 1000.0), 1),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": shape.dtype, "data": "synthetic",
-        "config": {"workload": (f"{args.workload} ({shape.n_layer} layers, d {shape.d_model}, "
-                                f"{shape.n_head}x{shape.head_dim} query heads, 1 K/V head, MLP "
-                                f"{shape.d_ff}, vocab {shape.vocab}, {shape.dtype}): prefill "
-                                f"{B}x{T} with fp32 logits at every position, then {steps} "
-                                f"greedy decode steps of {B} rows"),
-                   "batch": B, "prefill_len": T, "decode_steps": steps},
-        "prefill_ms": round(pre_ms, 3), "decode_ms": round(dec_ms, 3),
-        "prefill_tokens_per_s": round(B * T / (pre_ms / 1000.0), 1),
-        "decode_tokens_per_s": round(B * steps / (dec_ms / 1000.0), 1),
+        "config": {"workload": desc, "prefill_batch": Bp, "prefill_len": T,
+                   "decode_batch": Bd, "decode_steps": steps},
     }
-    out["roofline"], out["kernels"] = roofline(nc, one_step, steps, stream)
+    if Bp:
+        out["prefill_ms"] = round(pre_ms, 3)
+        out["prefill_tokens_per_s"] = round(n_pre / (pre_ms / 1000.0), 1)
+    if steps:
+        out["decode_ms"] = round(dec_ms, 3)
+        out["decode_tokens_per_s"] = round(n_dec / (dec_ms / 1000.0), 1)
+    out["roofline"], out["kernels"] = roofline(nc, one_step, shape.dtype)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(shape, weights, wl, args.cpu_seconds)
-    kv.close()
+    for kv in {id(k): k for k in (kv_p, kv_d) if k is not None}.values():
+        kv.close()
     model.close()
     print(json.dumps(out), flush=True)
 

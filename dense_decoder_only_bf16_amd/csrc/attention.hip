@@ -550,9 +550,9 @@ hipError_t launch_attn_decode(DType dt, const DecAttnArgs& args, void* y, hipStr
     dim3 g1((a.max_slots + DEC_WAVES - 1) / DEC_WAVES, a.B), g2(a.H, a.B);
 #define NC_AD(TT, HDV)                                                                         \
     do {                                                                                       \
-        hipLaunchKernelGGL((attn_decode_split_kernel<TT, HDV>), g1, dim3(DEC_WAVES * 64), 0, st, a);     \
-        hipLaunchKernelGGL((attn_decode_combine_kernel<TT, HDV>), g2, dim3(HDV), 0, st,        \
-                           (const float*)a.part, a.lens, (TT*)y, a.H, a.S, a.max_slots);      \
+        NC_TLAUNCH((attn_decode_split_kernel<TT, HDV>), g1, dim3(DEC_WAVES * 64), 0, st, a);   \
+        NC_TLAUNCH((attn_decode_combine_kernel<TT, HDV>), g2, dim3(HDV), 0, st,                \
+                   (const float*)a.part, a.lens, (TT*)y, a.H, a.S, a.max_slots);              \
     } while (0)
     if (dt == BF16 && a.hd == 128) NC_AD(bf16, 128);
     else if (dt == BF16 && a.hd == 64) NC_AD(bf16, 64);

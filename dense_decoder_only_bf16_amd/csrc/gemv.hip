@@ -23,10 +23,11 @@ namespace nc {
 
 constexpr int DEC_BN = 32;  // output columns per workgroup (both tile shapes below)
 
-// Finish one row of the tile: `v` is column n0 + lane of row m (lanes >= tile width hold 0).
+// Finish one row of the tile: `v` is column n0 + lane of row m (lanes >= tile width hold 0),
+// `r` the row's norm scale (RELU2, SOFTCAP), `x_old` the residual at (m, n0 + lane) (RESID).
 template <typename T, int EPI>
 __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, int n0, int width,
-                                                 int lane, float v, float r) {
+                                                 int lane, float v, float r, float x_old) {
     const int nn = n0 + lane;
     const bool ok = lane < width && nn < p.N;
     const long long o = (long long)m * p.ldo + nn;
@@ -42,7 +43,7 @@ __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, in
     } else {  // EPI_RESID
         float xn = 0.f;
         if (ok) {
-            xn = p.out_f32[o] + v;
+            xn = x_old + v;
             p.out_f32[o] = xn;
             const T hi = from_f32<T>(xn);
             ((T*)p.out_t)[o] = hi;
@@ -65,7 +66,6 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
     typedef typename Chunk<T>::type CT;
     constexpr int BM = 32 * FM, BN = 32, TP = BN + 1;
     __shared__ float red[NW * BM * TP];
-    __shared__ float rs[BM];
 
     if (p.lens_inc && blockIdx.x == 0 && blockIdx.y == 0)
         for (int r = threadIdx.x; r < p.M; r += NW * 64) p.lens_inc[r] += 1;
@@ -73,7 +73,33 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int l32 = lane & 31, hh = lane >> 5;
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    const int rows = min(BM, p.M - m0);  // >= 1
     const int ksteps = p.K / 16;  // K is a multiple of 16 (checked on the host)
+
+    // Wave w finishes rows w, w + NW, ... of the tile.  What their epilogue reads from
+    // memory is loaded now, all rows at once, so the latency hides behind the weight
+    // stream: RELU2 / SOFTCAP this lane's share of the row's partial sums of squares, RESID
+    // the residual x at (row, n0 + lane).  Addresses are clamped into the tile; rows past
+    // the tile are dropped below.
+    constexpr int RPW = (BM + NW - 1) / NW;
+    float pre[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) pre[i] = 0.f;
+    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
+        for (int q = lane; q < p.ss_in_parts; q += 64) {
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+                const int ml = wave + NW * i;
+                const float v = p.ss_in[(long long)q * p.ss_stride + m0 + min(ml, rows - 1)];
+                pre[i] += ml < rows ? v : 0.f;
+            }
+        }
+    } else if (EPI == EPI_RESID) {
+        const int nn = min(n0 + (lane & 31), p.N - 1);
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)
+            pre[i] = p.out_f32[(long long)(m0 + min(wave + NW * i, rows - 1)) * p.ldo + nn];
+    }
     const int s0 = ksteps * wave / NW, s1 = ksteps * (wave + 1) / NW;
     const T* A = (const T*)p.A;
     const T* wb = (const T*)p.W + (long long)(n0 / 32) * ksteps * 512 + l32 * 16 + 8 * hh;
@@ -134,13 +160,7 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             mine[(32 * i + 8 * (r / 4) + 4 * hh + (r % 4)) * TP + l32] = acc[i][r];
-    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP)
-        for (int r = wave; r < BM; r += NW) {  // one wave per row, lanes over the parts
-            const float v = (m0 + r < p.M) ? row_scale_wave(p.ss_in, p.ss_in_parts, p.ss_stride, m0 + r, p.K, p.eps) : 1.f;
-            if (lane == 0) rs[r] = v;
-        }
     __syncthreads();
-    const int rows = min(BM, p.M - m0);
     for (int e = tid; e < rows * BN; e += NW * 64) {
         const int r = e / BN, c = e % BN;
         float sum = 0.f;
@@ -149,9 +169,15 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
         red[r * TP + c] = sum;
     }
     __syncthreads();
-    for (int ml = wave; ml < rows; ml += NW)
-        dec_row_epilogue<T, EPI>(p, m0 + ml, n0, BN, lane, lane < BN ? red[ml * TP + lane] : 0.f,
-                                 (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) ? rs[ml] : 1.f);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int ml = wave + NW * i;
+        if (ml < rows) {  // wave-uniform
+            float r = 1.f;
+            if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) r = 1.0f / sqrtf(wave_sum(pre[i]) / (float)p.K + p.eps);
+            dec_row_epilogue<T, EPI>(p, m0 + ml, n0, BN, lane, lane < BN ? red[ml * TP + lane] : 0.f, r, pre[i]);
+        }
+    }
 }
 
 // Launch shape.  `variant` picks alternative (waves, steps-in-flight) choices for tuning.

@@ -8,15 +8,24 @@
 
 namespace nc {
 
-// Kernel-timing hook.  While the library times a kernel class it sets these events around
-// a launch helper of that class; the helper launches through hipExtLaunchKernel, which
-// stamps them with the kernel's own start and end (null events: no stamps).
+// Kernel-timing hook.  While the library times a kernel class it hands a launch helper of
+// that class up to NC_MAX_STAMPS event pairs; each NC_TLAUNCH in the helper takes the next
+// pair and launches through hipExtLaunchKernel, which stamps the pair with the kernel's
+// own start and end (no pair left: launched without stamps).
+#define NC_MAX_STAMPS 2
 struct LaunchStamp {
-    hipEvent_t start, stop;
+    hipEvent_t ev[NC_MAX_STAMPS][2];
+    int avail, used;
 };
 extern thread_local LaunchStamp t_stamp;
-#define NC_TLAUNCH(K, grid, block, shm, st, ...) \
-    hipExtLaunchKernelGGL(K, grid, block, shm, st, ::nc::t_stamp.start, ::nc::t_stamp.stop, 0, __VA_ARGS__)
+#define NC_TLAUNCH(K, grid, block, shm, st, ...)                                            \
+    do {                                                                                    \
+        ::nc::LaunchStamp& ts_ = ::nc::t_stamp;                                             \
+        const bool on_ = ts_.used < ts_.avail;                                              \
+        hipExtLaunchKernelGGL(K, grid, block, shm, st, on_ ? ts_.ev[ts_.used][0] : nullptr, \
+                              on_ ? ts_.ev[ts_.used][1] : nullptr, 0, __VA_ARGS__);         \
+        ts_.used += on_ ? 1 : 0;                                                            \
+    } while (0)
 
 enum DType { F32 = 0, BF16 = 1 };
 

@@ -34,7 +34,7 @@
 
 using namespace nc;
 
-thread_local LaunchStamp nc::t_stamp = {nullptr, nullptr};
+thread_local LaunchStamp nc::t_stamp = {};
 
 namespace {
 
@@ -59,8 +59,9 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // events that its dispatch stamps with the kernel's start and end (hipExtLaunchKernel).
 // While a class is timed, decode steps launch their kernels one by one instead of replaying
 // a captured graph, since stamped launches cannot be captured.
-struct TimingPair {
-    hipEvent_t a, b;
+struct TimingPair {  // one timed operation: its kernels' event pairs and its work
+    hipEvent_t ev[NC_MAX_STAMPS][2];
+    int n;
     double bytes, flops;
 };
 struct Timing {
@@ -72,8 +73,9 @@ struct Timing {
 Timing g_tm;
 
 void timing_release(TimingPair& tp) {
-    (void)hipEventDestroy(tp.a);
-    (void)hipEventDestroy(tp.b);
+    for (int i = 0; i < NC_MAX_STAMPS; ++i)
+        for (int j = 0; j < 2; ++j)
+            if (tp.ev[i][j]) (void)hipEventDestroy(tp.ev[i][j]);
 }
 
 }  // namespace
@@ -228,20 +230,30 @@ nc_status launched(hipError_t e, const char* what) {
 
 // Launch `fn` (returning hipError_t); if kernel class `cls` is being timed, bracket it with
 // an event pair on `st` that carries its algorithmic bytes and flops.
+// `kernels` = number of kernels `fn` launches through NC_TLAUNCH (at most NC_MAX_STAMPS).
 template <typename F>
-hipError_t timed(int cls, double bytes, double flops, hipStream_t st, F fn) {
+hipError_t timed(int cls, double bytes, double flops, hipStream_t st, F fn, int kernels = 1) {
+    (void)st;
     if (g_tm.cls != cls) return fn();
-    TimingPair tp{nullptr, nullptr, bytes, flops};
-    hipError_t e = hipEventCreate(&tp.a);
-    if (e == hipSuccess) e = hipEventCreate(&tp.b);
+    TimingPair tp = {};
+    tp.bytes = bytes;
+    tp.flops = flops;
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < kernels && e == hipSuccess; ++i)
+        for (int j = 0; j < 2 && e == hipSuccess; ++j) e = hipEventCreate(&tp.ev[i][j]);
     if (e == hipSuccess) {
-        t_stamp = {tp.a, tp.b};
+        t_stamp = {};
+        for (int i = 0; i < kernels; ++i) {
+            t_stamp.ev[i][0] = tp.ev[i][0];
+            t_stamp.ev[i][1] = tp.ev[i][1];
+        }
+        t_stamp.avail = kernels;
         e = fn();
-        t_stamp = {nullptr, nullptr};
+        tp.n = t_stamp.used;
+        t_stamp = {};
     }
     if (e != hipSuccess) {
-        if (tp.a) (void)hipEventDestroy(tp.a);
-        if (tp.b) (void)hipEventDestroy(tp.b);
+        timing_release(tp);
         return e;
     }
     g_tm.pending.push_back(tp);
@@ -305,7 +317,15 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         at.norm_dim = d; at.eps = c.norm_eps; at.rope_cos = m->rope_cos; at.rope_sin = m->rope_sin;
         at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = kv->apart;
         at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.max_slots = max_slots;
-        LAUNCH(launch_attn_decode(m->dt, at, kv->y, st));
+        {   // bytes: the K/V read for every row (positions 0..lens_b, the new one
+            // included), q/k/v in fp32, y out; flops 4 hd per (query head, key) pair
+            const double es = (double)m->esz;
+            double keys = 0;
+            for (int b = 0; b < B; ++b) keys += kv->lens_host[b] + 1;
+            const double by = keys * hd * 2 * es + (double)B * nqkv * 4 + (double)B * H * hd * es;
+            LAUNCH(timed(NC_KC_DECODE_ATTN, by, 4.0 * H * hd * keys, st,
+                         [&] { return launch_attn_decode(m->dt, at, kv->y, st); }, 2));
+        }
         // O + residual
         DecGemmArgs o = a;
         o.A = kv->y; o.lda = H * hd; o.W = L.wo; o.N = d; o.K = H * hd;
@@ -672,7 +692,7 @@ nc_status nc_decode_step(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* k
 }
 
 nc_status nc_timing_enable(int32_t kernel_class) {
-    if (kernel_class < NC_KC_NONE || kernel_class > NC_KC_PREFILL_ATTN)
+    if (kernel_class < NC_KC_NONE || kernel_class > NC_KC_DECODE_ATTN)
         return fail(NC_ERR_INVALID_ARG, "unknown kernel class");
     HIP_TRY(hipDeviceSynchronize());
     for (auto& tp : g_tm.pending) timing_release(tp);
@@ -688,8 +708,12 @@ nc_status nc_timing_read(nc_timing* out) {
     HIP_TRY(hipDeviceSynchronize());
     auto add = [](TimingPair& tp) -> hipError_t {
         float ms = 0.f;
-        hipError_t e = hipEventElapsedTime(&ms, tp.a, tp.b);
-        if (e != hipSuccess) return e;
+        for (int i = 0; i < tp.n; ++i) {
+            float t = 0.f;
+            hipError_t e = hipEventElapsedTime(&t, tp.ev[i][0], tp.ev[i][1]);
+            if (e != hipSuccess) return e;
+            ms += t;
+        }
         g_tm.launches++;
         g_tm.ms += ms;
         g_tm.bytes += tp.bytes;

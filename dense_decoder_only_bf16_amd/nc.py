@@ -34,6 +34,7 @@ NC_KC_NONE = 0
 NC_KC_DECODE_GEMM = 1
 NC_KC_PREFILL_GEMM = 2
 NC_KC_PREFILL_ATTN = 3
+NC_KC_DECODE_ATTN = 4
 
 EXPORTED = ("nc_model_create", "nc_model_free", "nc_kv_create", "nc_kv_free", "nc_kv_set_lens",
             "nc_kv_get_lens", "nc_kv_export", "nc_prefill", "nc_decode_step", "nc_argmax",

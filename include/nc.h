@@ -133,22 +133,25 @@ nc_status nc_argmax(const float* logits_dev, int32_t B, int32_t V, int32_t* out_
                     void* stream);
 
 /* Kernel timing, for diagnostics and roofline reports.  When a kernel class is enabled,
- * every launch of that class is bracketed by a pair of HIP events recorded on the launch
- * stream, and decode steps launch their kernels one by one instead of replaying their
- * captured graphs (which stay cached for when timing is switched off).  nc_timing_read
- * synchronises the device and adds the pairs recorded since the last read to running
- * totals: the number of launches, their summed event-to-event time, and the algorithmic
- * bytes and flops of those launches.  nc_timing_enable resets the totals.  Process-wide,
- * not thread-safe. */
+ * every kernel of that class is launched with a pair of HIP events that the dispatch itself
+ * stamps with the kernel's start and end (hipExtLaunchKernel), on the launch stream; decode
+ * steps then launch their kernels one by one instead of replaying their captured graphs
+ * (which stay cached for when timing is switched off).  nc_timing_read synchronises the
+ * device and adds the operations recorded since the last read to running totals: their
+ * number, their summed kernel time, and their algorithmic bytes and flops.
+ * nc_timing_enable resets the totals.  Process-wide, not thread-safe.  Returns
+ * NC_ERR_INVALID_ARG for an unknown class. */
 #define NC_KC_NONE 0
 #define NC_KC_DECODE_GEMM 1  /* decode projections: QKV, O, FC, PROJ, LM head            */
 #define NC_KC_PREFILL_GEMM 2 /* prefill projections                                       */
 #define NC_KC_PREFILL_ATTN 3 /* prefill attention                                         */
+#define NC_KC_DECODE_ATTN 4  /* decode attention: split + combine kernels, one operation   */
 typedef struct nc_timing {
-    int64_t launches;
-    double ms;    /* summed event-to-event time of the launches                           */
+    int64_t launches; /* timed operations (one decode attention = its two kernels)       */
+    double ms;    /* summed kernel time of the launches (start/stop of each kernel)        */
     double bytes; /* algorithmic bytes: weights, activations and outputs, each moved once */
     double flops; /* algorithmic flops: 2 M N K per product, 4 hd per visible score pair  */
+                  /* (decode attention bytes: K and V rows 0..lens_b of every row, once)  */
 } nc_timing;
 nc_status nc_timing_enable(int32_t kernel_class);
 nc_status nc_timing_read(nc_timing* out);

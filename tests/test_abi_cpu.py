@@ -112,3 +112,15 @@ def test_null_handles_are_rejected(L):
     assert L.nc_kv_export(None, 0, None, None, None) == nc.NC_ERR_INVALID_ARG
     L.nc_model_free(None)
     L.nc_kv_free(None)
+
+
+def test_header_constants_match_binding():
+    """Every #define NC_* integer in the header has the same value in the binding."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    defs = dict(re.findall(r"#define\s+(NC_[A-Z0-9_]+)\s+\(?(-?\d+)\)?", text))
+    assert len(defs) >= 15
+    for name, val in defs.items():
+        if name == "NC_ABI_VERSION":
+            assert nc.nc_abi_version() == int(val) if os.path.exists(nc.LIB_PATH) else True
+            continue
+        assert getattr(nc, name) == int(val), name
