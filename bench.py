@@ -31,6 +31,11 @@ def parse():
     p.add_argument("--workload", default="d12")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--decode-steps", type=int, default=None,
+                   help="override the workload's decode steps (short runs under a profiler)")
+    p.add_argument("--no-roofline", action="store_true", help="skip the kernel-timing pass")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
 
 
@@ -89,7 +94,30 @@ KERNEL_NAMES = {"decode_gemm": "dec_gemm_kernel (decode projections)",
                 "prefill_attn": "attn_prefill_kernel"}
 
 
-def roofline(nc, one_step, dtype):
+# HBM-side bytes per launch of a kernel class, from two rocprofv3 counter passes
+# (FETCH_SIZE, WRITE_SIZE) scaled by a plain-copy calibration, valid only for the kernel
+# sources they were taken with (hash of the listed files); otherwise the report says null.
+TRAFFIC = {
+    ("d12", "decode_gemm"): {"bytes_per_launch": 5.522e6, "profile": "profiles/d12_pmc_traffic.md",
+                             "sources": ("csrc/gemv.hip", "csrc/common.h", "csrc/kernels.h"),
+                             "sha": "6b8dbbe72db6b4ed"},
+}
+
+
+def measured_traffic(workload, name):
+    import hashlib
+    t = TRAFFIC.get((workload, name))
+    if not t:
+        return None
+    h = hashlib.sha256()
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dense_decoder_only_bf16_amd")
+    for f in t["sources"]:
+        with open(os.path.join(base, f), "rb") as fh:
+            h.update(fh.read())
+    return t["bytes_per_launch"] if h.hexdigest()[:16] == t["sha"] else None
+
+
+def roofline(nc, one_step, dtype, workload):
     """Kernel timing pass: one more full step per kernel class with the library's timing
     mode on (every kernel of the class launched with dispatch-stamped start/stop events on
     its stream; decode launches eager instead of graph replays).  Reports, per class, the
@@ -119,13 +147,30 @@ def roofline(nc, one_step, dtype):
         ach, unit = r["TFLOP_per_s"], "TFLOP/s"
         peak = MFMA_BF16_PEAK_TFS if dtype == "bf16" else FP32_VEC_PEAK_TFS
     roof = {"kernel": KERNEL_NAMES[dom], "bound": r["bound"], "achieved": ach, "peak": peak,
-            "unit": unit, "frac": round(ach / peak, 4), "traffic": None,
+            "unit": unit, "frac": round(ach / peak, 4), "traffic": measured_traffic(workload, dom),
+            "bytes_per_launch": r["bytes_per_launch"],
             "avg_launch_us": r["avg_us"], "launches": r["launches"]}
     return roof, res
 
 
+def copy_calibration(mib):
+    """One plain device-to-device copy of `mib` MiB (torch's copy kernel): the reference
+    dispatch whose FETCH_SIZE / WRITE_SIZE counters scale the kernels' counter readings."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4}), flush=True)
+
+
 def main():
     args = parse()
+    if args.copy_mib:
+        copy_calibration(args.copy_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(batch rows are independent, so more GPUs would each run their own rows).",
@@ -141,6 +186,8 @@ def main():
     shape = wl.shape
     Bp, T = wl.prefill_batch, wl.prefill_len
     Bd, steps = wl.decode_batch, wl.decode_steps
+    if args.decode_steps is not None and steps:
+        steps = args.decode_steps
     shared = Bp > 0 and Bd == Bp  # decode continues the prefilled rows
     weights = make_weights(shape, seed=0)
     model = nc.Model(shape, canonical_list(weights), max_seq=shape.max_seq)
@@ -233,7 +280,8 @@ def main():
     if steps:
         out["decode_ms"] = round(dec_ms, 3)
         out["decode_tokens_per_s"] = round(n_dec / (dec_ms / 1000.0), 1)
-    out["roofline"], out["kernels"] = roofline(nc, one_step, shape.dtype)
+    if not args.no_roofline:
+        out["roofline"], out["kernels"] = roofline(nc, one_step, shape.dtype, args.workload)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(shape, weights, wl, args.cpu_seconds)
     for kv in {id(k): k for k in (kv_p, kv_d) if k is not None}.values():

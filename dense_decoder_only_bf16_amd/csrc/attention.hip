@@ -541,7 +541,7 @@ __global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __
         o += wts[sl] * o0 + wts[sl + 1] * o1 + wts[sl + 2] * o2 + wts[sl + 3] * o3;
     }
     for (; sl < nsl; ++sl) o += wts[sl] * po[(long long)sl * PSZ];
-    y[((long long)b * H + h) * HD + d] = from_f32<T>(o * stat[0]);
+    y[blocked_index(b, h * HD + d, H * HD)] = from_f32<T>(o * stat[0]);
 }
 
 hipError_t launch_attn_decode(DType dt, const DecAttnArgs& args, void* y, hipStream_t st) {

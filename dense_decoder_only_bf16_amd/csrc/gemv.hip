@@ -30,14 +30,15 @@ __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, in
                                                  int lane, float v, float r, float x_old) {
     const int nn = n0 + lane;
     const bool ok = lane < width && nn < p.N;
-    const long long o = (long long)m * p.ldo + nn;
+    const long long o = (long long)m * p.ldo + nn;      // fp32 outputs, row-major
+    const long long ob = blocked_index(m, ok ? nn : 0, p.N);  // dtype outputs, blocked
     if (EPI == EPI_STORE) {
         if (ok) p.out_f32[o] = v;
     } else if (EPI == EPI_RELU2) {
         const float t = fmaxf(v * r, 0.f);
         const T hi = from_f32<T>(t * t);
-        if (ok) ((T*)p.out_t)[o] = hi;
-        if (ok && p.out_lo) ((T*)p.out_lo)[o] = from_f32<T>(t * t - to_f32(hi));
+        if (ok) ((T*)p.out_t)[ob] = hi;
+        if (ok && p.out_lo) ((T*)p.out_lo)[ob] = from_f32<T>(t * t - to_f32(hi));
     } else if (EPI == EPI_SOFTCAP) {
         if (ok) p.out_f32[o] = p.cap * tanh_f32(v * r / p.cap);
     } else {  // EPI_RESID
@@ -46,8 +47,8 @@ __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, in
             xn = x_old + v;
             p.out_f32[o] = xn;
             const T hi = from_f32<T>(xn);
-            ((T*)p.out_t)[o] = hi;
-            if (p.out_lo) ((T*)p.out_lo)[o] = from_f32<T>(xn - to_f32(hi));
+            ((T*)p.out_t)[ob] = hi;
+            if (p.out_lo) ((T*)p.out_lo)[ob] = from_f32<T>(xn - to_f32(hi));
         }
         const float sq = wave_sum(xn * xn);
         if (lane == 0) p.ss_out[(long long)blockIdx.x * p.ss_stride + m] = sq;
@@ -103,14 +104,17 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
     const int s0 = ksteps * wave / NW, s1 = ksteps * (wave + 1) / NW;
     const T* A = (const T*)p.A;
     const T* wb = (const T*)p.W + (long long)(n0 / 32) * ksteps * 512 + l32 * 16 + 8 * hh;
+    // A is blocked like W: the operand of step s for row block i is 1 KB at
+    // arow[i] + 512 s.  Lanes of rows past M read row 0 of the block (the same cache lines
+    // as lane 0, so a short last block costs no extra traffic) and zero what they read.
     const T* arow[FM];
     const T* lrow[FM];
     bool mok[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int m = m0 + 32 * i + l32;
-        mok[i] = m < p.M;
-        const long long off = (long long)(mok[i] ? m : 0) * p.lda + 8 * hh;
+        mok[i] = m0 + 32 * i + l32 < p.M;
+        const int rb = min(m0 / 32 + i, (p.M - 1) / 32);  // row block (clamped into the buffer)
+        const long long off = (long long)rb * ksteps * 512 + (mok[i] ? l32 : 0) * 16 + 8 * hh;
         arow[i] = A + off;
         lrow[i] = LO ? (const T*)p.A_lo + off : arow[i];
     }
@@ -132,8 +136,8 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
             wf[u] = load_masked(wb + (long long)sc * 512, ok);
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                af[u][0][i] = load_masked(arow[i] + sc * 16, ok && mok[i]);
-                if (LO) af[u][NA - 1][i] = load_masked(lrow[i] + sc * 16, ok && mok[i]);
+                af[u][0][i] = load_masked(arow[i] + (long long)sc * 512, ok && mok[i]);
+                if (LO) af[u][NA - 1][i] = load_masked(lrow[i] + (long long)sc * 512, ok && mok[i]);
             }
         }
     };

@@ -42,6 +42,11 @@ enum Epi { EPI_STORE = 0, EPI_RELU2 = 1, EPI_RESID = 2, EPI_SOFTCAP = 3 };
 // with rows n >= N (up to Npad = N rounded up to 32) zero.  A 32x16 block is the operand
 // of one 16-deep MFMA step for one wave.
 __host__ __device__ inline long long blocked_elems(int N, int K) { return (long long)((N + 31) / 32) * 32 * K; }
+// Index of element (n, k) in that layout (K a multiple of 16).  Decode activations use the
+// same layout, rows being token rows, so a wave's 16-deep A operand is 1 KB contiguous.
+__host__ __device__ inline long long blocked_index(int n, int k, int K) {
+    return ((long long)(n >> 5) * (K >> 4) + (k >> 4)) * 512 + (n & 31) * 16 + (k & 15);
+}
 hipError_t launch_repack(DType dt, const void* src, void* dst, int N, int K, hipStream_t st);
 
 struct GemmArgs {
@@ -73,8 +78,10 @@ hipError_t launch_gemm(DType dt, Epi epi, const GemmArgs& a, hipStream_t st);
 // Decode projection (M <= 128 rows, K a multiple of 16) with the epilogue fused
 // (STORE / RELU2 / RESID / SOFTCAP).  Tiles are dec_gemm_tile_n() columns; RESID writes
 // ss_out[tile_n * ss_stride + m] (parts = ceil(N / tile_n)).
+// Decode activations (A, A_lo and the dtype outputs out_t, out_lo) are stored blocked with
+// rows rounded up to 32 (blocked_index); the fp32 outputs are row-major with stride ldo.
 struct DecGemmArgs {
-    const void* A; int lda;     // [M][lda] dtype
+    const void* A;              // blocked [ceil(M/32)][K/16][32][16] dtype
     const void* W;              // blocked weight, Npad = N rounded up to 32 rows
     int M, N, K;
     float* out_f32; void* out_t; int ldo;
@@ -88,9 +95,10 @@ struct DecGemmArgs {
 int dec_gemm_tile_n();
 hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t st, int variant = 0);
 
-// x[m] = norm(wte[tok[m]]) (fp32), act[m] = dtype copy, ss[m] = sum(x^2).
+// x[m] = norm(wte[tok[m]]) (fp32, row-major), act[m] = dtype copy (row-major, or blocked
+// with rows rounded up to 32 when `blocked`), ss[m] = sum(x^2).
 hipError_t launch_embed(DType dt, const int32_t* tok, int M, const void* wte, int vocab, int d,
-                        float eps, float* x, void* act, float* ss, hipStream_t st);
+                        float eps, float* x, void* act, float* ss, bool blocked, hipStream_t st);
 
 // Pre-attention finish of the raw QKV product part[z][m][(H+2)*hd]:
 // scale row m by r_m, rotate q heads and the k head at position pos(m), QK-normalise,
@@ -120,7 +128,7 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 // 0..lens[b]).  The split kernel first finishes the row's raw QKV product (norm scale,
 // RoPE, QK-norm) and stores the new key/value into the cache, then reduces each chunk of
 // keys to a partial softmax state; the combine kernel merges a row's partials into
-// y [B][H][hd].  The combine reads lens[b] to know the chunk count.
+// y, [B][H hd] stored blocked (blocked_index, rows rounded up to 32).  The combine reads lens[b] to know the chunk count.
 struct DecAttnArgs {
     const float* qkv;   // raw product [B][(H+2) hd] fp32
     const float* ss_in; int ss_in_parts, ss_stride, norm_dim;

@@ -17,7 +17,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok, int M,
                                                     const T* __restrict__ wte, int vocab, int d,
                                                     float eps, float* __restrict__ x,
-                                                    T* __restrict__ act, float* __restrict__ ss) {
+                                                    T* __restrict__ act, float* __restrict__ ss,
+                                                    bool blocked) {
     typedef typename Chunk<T>::type CT;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
                 s2 += f * f;
             }
             *(f32x8*)(x + (long long)row * d + cidx * 8) = xo;
-            *(CT*)(act + (long long)row * d + cidx * 8) = ao;
+            *(CT*)(act + (blocked ? blocked_index(row, cidx * 8, d) : (long long)row * d + cidx * 8)) = ao;
         }
     }
     s2 = wave_sum(s2);
@@ -64,14 +65,14 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 }
 
 hipError_t launch_embed(DType dt, const int32_t* tok, int M, const void* wte, int vocab, int d,
-                        float eps, float* x, void* act, float* ss, hipStream_t st) {
+                        float eps, float* x, void* act, float* ss, bool blocked, hipStream_t st) {
     dim3 grid((M + 3) / 4);
     if (dt == BF16)
         hipLaunchKernelGGL(embed_kernel<bf16>, grid, dim3(256), 0, st, tok, M, (const bf16*)wte,
-                           vocab, d, eps, x, (bf16*)act, ss);
+                           vocab, d, eps, x, (bf16*)act, ss, blocked);
     else
         hipLaunchKernelGGL(embed_kernel<float>, grid, dim3(256), 0, st, tok, M, (const float*)wte,
-                           vocab, d, eps, x, (float*)act, ss);
+                           vocab, d, eps, x, (float*)act, ss, blocked);
     return hipGetLastError();
 }
 

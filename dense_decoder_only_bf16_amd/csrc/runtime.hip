@@ -166,18 +166,20 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
     // row statistics come in parts of one per output tile of the producing product
     kv->ss_parts_max = (c.d_model + dec_gemm_tile_n() - 1) / dec_gemm_tile_n();
     const long long qkv_elems = M * nqkv;
+    // dtype activations that decode stores blocked hold whole 32-row blocks
+    const long long Mr = (M + 31) / 32 * 32;
 #define WS_ALLOC(ptr, bytes) HIP_TRY(hipMalloc((void**)&(ptr), (size_t)(bytes)))
     WS_ALLOC(kv->x, M * d * 4);
-    WS_ALLOC(kv->act, M * d * es);
+    WS_ALLOC(kv->act, Mr * d * es);
     WS_ALLOC(kv->ss_a, (long long)kv->ss_parts_max * M * 4);
     WS_ALLOC(kv->ss_b, (long long)kv->ss_parts_max * M * 4);
     WS_ALLOC(kv->qkv, qkv_elems * 4);
     WS_ALLOC(kv->q, M * hq * es);
-    WS_ALLOC(kv->y, M * hq * es);
-    WS_ALLOC(kv->u, M * c.d_ff * es);
+    WS_ALLOC(kv->y, Mr * hq * es);
+    WS_ALLOC(kv->u, Mr * c.d_ff * es);
     if (kv->m->dt == BF16) {
-        WS_ALLOC(kv->act_lo, M * d * es);
-        WS_ALLOC(kv->u_lo, M * c.d_ff * es);
+        WS_ALLOC(kv->act_lo, Mr * d * es);
+        WS_ALLOC(kv->u_lo, Mr * c.d_ff * es);
     }
     kv->apart_elems = (long long)kv->B * attn_decode_slots(kv->S) * 16 * (c.head_dim + 2);
     WS_ALLOC(kv->apart, kv->apart_elems * 4);
@@ -299,7 +301,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
     const int ss = (int)kv->cap_m;
     nc_status s;
 
-    LAUNCH(launch_embed(m->dt, tokens, B, m->wte, V, d, c.norm_eps, kv->x, kv->act, kv->ss_a, st));
+    LAUNCH(launch_embed(m->dt, tokens, B, m->wte, V, d, c.norm_eps, kv->x, kv->act, kv->ss_a, true, st));
     int ss_a_parts = 1;
     for (int l = 0; l < c.n_layer; ++l) {
         const nc_model::Layer& L = m->layers[l];
@@ -308,7 +310,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         DecGemmArgs a{};
         a.M = B; a.eps = c.norm_eps; a.cap = c.softcap; a.ss_stride = ss;
         // QKV raw product, then norm scale + RoPE + QK-norm + cache write at lens[b]
-        a.A = kv->act; a.lda = d; a.W = L.wqkv; a.N = nqkv; a.K = d;
+        a.A = kv->act; a.W = L.wqkv; a.N = nqkv; a.K = d;
         a.out_f32 = kv->qkv; a.ldo = nqkv;
         if ((s = decode_gemm(kv, EPI_STORE, a, st)) != NC_OK) return s;
         // QKV finish (norm scale, RoPE, QK-norm, cache write) + attention over the cache
@@ -328,25 +330,25 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         }
         // O + residual
         DecGemmArgs o = a;
-        o.A = kv->y; o.lda = H * hd; o.W = L.wo; o.N = d; o.K = H * hd;
+        o.A = kv->y; o.W = L.wo; o.N = d; o.K = H * hd;
         o.out_f32 = kv->x; o.out_t = kv->act; o.ldo = d; o.ss_out = kv->ss_b;
         o.out_lo = kv->act_lo;
         if ((s = decode_gemm(kv, EPI_RESID, o, st)) != NC_OK) return s;
         // FC + norm scale + relu^2 (compensated operand)
         DecGemmArgs f = a;
-        f.A = kv->act; f.A_lo = kv->act_lo; f.lda = d; f.W = L.wfc; f.N = F; f.K = d;
+        f.A = kv->act; f.A_lo = kv->act_lo; f.W = L.wfc; f.N = F; f.K = d;
         f.out_t = kv->u; f.out_lo = kv->u_lo; f.ldo = F; f.ss_in = kv->ss_b; f.ss_in_parts = parts_d;
         if ((s = decode_gemm(kv, EPI_RELU2, f, st)) != NC_OK) return s;
         // PROJ + residual (compensated operand)
         DecGemmArgs pj = a;
-        pj.A = kv->u; pj.A_lo = kv->u_lo; pj.lda = F; pj.W = L.wproj; pj.N = d; pj.K = F;
+        pj.A = kv->u; pj.A_lo = kv->u_lo; pj.W = L.wproj; pj.N = d; pj.K = F;
         pj.out_f32 = kv->x; pj.out_t = kv->act; pj.ldo = d; pj.ss_out = kv->ss_a;
         if ((s = decode_gemm(kv, EPI_RESID, pj, st)) != NC_OK) return s;
         ss_a_parts = parts_d;
     }
     DecGemmArgs h{};
     h.M = B; h.eps = c.norm_eps; h.cap = c.softcap; h.ss_stride = ss;
-    h.A = kv->act; h.lda = d; h.W = m->lm; h.N = V; h.K = d;
+    h.A = kv->act; h.W = m->lm; h.N = V; h.K = d;
     h.out_f32 = logits; h.ldo = V; h.ss_in = kv->ss_a; h.ss_in_parts = ss_a_parts;
     h.lens_inc = kv->lens_dev;  // the step's last kernel also advances every row by one
     if ((s = decode_gemm(kv, EPI_SOFTCAP, h, st)) != NC_OK) return s;
@@ -581,7 +583,7 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
         const size_t per_layer = (size_t)B * kv->S * hd * m->esz;
         const int Mi = (int)M;
 
-        LAUNCH(launch_embed(m->dt, tokens, Mi, m->wte, V, d, c.norm_eps, kv->x, kv->act, kv->ss_a, st));
+        LAUNCH(launch_embed(m->dt, tokens, Mi, m->wte, V, d, c.norm_eps, kv->x, kv->act, kv->ss_a, false, st));
         int ss_a_parts = 1;
         for (int l = 0; l < c.n_layer; ++l) {
             const nc_model::Layer& L = m->layers[l];
