@@ -283,8 +283,6 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_split_kernel(DecAt
 
     // ---- staging loads of this wave's cached K and V^T (bf16)
     if constexpr (STAGE) {
-        typedef __attribute__((address_space(1))) void gvoid;
-        typedef __attribute__((address_space(3))) void lvoid;
         constexpr int KCH = HD / 8;  // 16-byte chunks per K row
         // K: LDS byte 16 p of the wave's tile holds key p / KCH, chunk (p % KCH) ^ (key % KCH)
 #pragma unroll

@@ -89,6 +89,12 @@ __device__ __forceinline__ float wave_max(float v) {
 // Wait for every outstanding vector-memory load of this wave (including direct-to-LDS
 // loads, which the compiler does not track).
 #define NC_WAIT_VM_ALL() __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8))
+// Wait until at most n (a constant, <= 63) vector-memory loads of this wave are outstanding
+// (expcnt and lgkmcnt left at their maxima), in the gfx9 s_waitcnt encoding.
+#define NC_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+typedef __attribute__((address_space(1))) void gvoid;  // global memory, for direct-to-LDS loads
+typedef __attribute__((address_space(3))) void lvoid;  // LDS
 
 // Row scale of the parameter-free RMSNorm, r = 1/sqrt(sum_p ss[p * stride + m] / dim + eps),
 // from `parts` partial sums of squares.  Wave-cooperative: lane q loads parts q, q+64, ...

@@ -39,8 +39,6 @@
 
 namespace nc {
 
-typedef __attribute__((address_space(1))) void gvoid;
-typedef __attribute__((address_space(3))) void lvoid;
 
 template <typename T> struct KT {
     static constexpr int BK = 128 / (int)sizeof(T);  // elements per 128-byte row slice
@@ -135,8 +133,6 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[4
 }
 
 // ---------------------------------------------------------------------- bf16 ----------
-// vmcnt-only wait (expcnt and lgkmcnt left at their maxima) in the gfx9 s_waitcnt encoding.
-#define NC_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
 template <int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))

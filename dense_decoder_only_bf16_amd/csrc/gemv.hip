@@ -16,6 +16,8 @@
 // Sources: yelogs.com launch write-up, architecture answer (norms without parameters,
 // ReLU^2, no biases, untied head, logit softcap); apidog.com/th "How to train your own
 // ChatGPT for $50", part 3 (weights cast to the activation dtype for a plain linear map).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -215,6 +217,223 @@ static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant) {
     return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------ wide (32 < M <= 128) -------
+// With up to 128 rows, a 32-column workgroup that reads all of A moves several times more
+// activation bytes (out of L2) than weight bytes, and the L2s become the bound.  For bf16
+// and M > 32 a workgroup therefore owns 128 columns (4 waves x one 32-column weight block)
+// and one slice of K, and its waves share the activation operand through LDS: every stage
+// of an LDS ring holds WKC 16-deep steps of the A blocks (both parts when compensated) and
+// of the 4 waves' weight blocks, all filled by direct-to-LDS 1 KB loads issued WNS - 1
+// stages ahead.  The LM head (softcap; N = vocab gives hundreds of column tiles) runs its
+// whole K in one workgroup and its epilogue here.  The other products split K into slices
+// so that there are a few hundred workgroups; their fp32 partial products go to `part` and
+// dec_reduce_kernel adds the slices in a fixed order and runs the epilogue.
+constexpr int WBN = 128;  // columns per workgroup
+constexpr int WKC = 2;    // 16-deep steps per LDS stage
+constexpr int WNS = 6;    // stages in the ring
+
+struct WideShape {
+    int tiles, splits, per;  // column tiles, K slices, 16-deep steps per slice
+};
+// Slices: as many as fill one round of workgroup slots (256 CUs, one or two resident
+// workgroups each by LDS size), at least 2 and each slice at least 2 stages long.  A
+// workgroup's ring runs at a fixed latency-bound rate, so a second round of workgroups
+// costs more than the larger partial sums of a finer split.
+static WideShape wide_shape(Epi epi, int M, bool lo, int N, int K) {
+    WideShape w;
+    const int ksteps = K / 16;  // >= 4 (K >= 64)
+    w.tiles = (N + WBN - 1) / WBN;
+    if (epi == EPI_SOFTCAP) {
+        w.splits = 1;
+        w.per = ksteps;
+        return w;
+    }
+    const int fm = M <= 64 ? 2 : 4;
+    const int stage_kb = WKC * (fm * (lo ? 2 : 1) + 4);
+    const int slots = 256 * std::max(1, 160 / (WNS * stage_kb));
+    int s = slots / w.tiles;
+    s = std::max(2, std::min(s, ksteps / (2 * WKC)));
+    w.per = (ksteps + s - 1) / s;
+    w.splits = (ksteps + w.per - 1) / w.per;  // every slice non-empty, >= 2
+    return w;
+}
+
+template <int FM, bool LO, int EPI>
+__global__ __launch_bounds__(256) void dec_gemm_wide_kernel(DecGemmArgs p, int splits, int per) {
+    constexpr int NA = LO ? 2 : 1;
+    constexpr int ABLK = FM * NA;          // A blocks per 16-deep step
+    constexpr int BPS = WKC * (ABLK + 4);  // 1 KB blocks per stage: A blocks, then W blocks
+    constexpr int BPW = BPS / 4;           // blocks each wave loads per stage
+    static_assert(BPS % 4 == 0, "stage must split evenly over the 4 waves");
+    static_assert((WNS - 2) * BPW <= 63, "vmcnt range");
+    constexpr int STAGE = BPS * 512;       // bf16 elements per stage
+    __shared__ __attribute__((aligned(1024))) bf16 lds[WNS * STAGE];
+    __shared__ float rs[32 * FM];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int n0 = blockIdx.x * WBN;
+    const int ksteps = p.K / 16;
+    const int s0 = blockIdx.y * per, s1 = min(ksteps, s0 + per);  // s0 < s1 (host)
+    const int nstg = (s1 - s0 + WKC - 1) / WKC;
+    const int nblk_w = (p.N + 31) / 32;
+    const int mblk = (p.M + 31) / 32;
+    const bf16* A = (const bf16*)p.A;
+    const bf16* AL = LO ? (const bf16*)p.A_lo : A;
+    const bf16* W = (const bf16*)p.W;
+    (void)splits;
+    if (p.lens_inc && blockIdx.x == 0 && blockIdx.y == 0)  // end of a decode step
+        for (int r = tid; r < p.M; r += 256) p.lens_inc[r] += 1;
+
+    if (EPI == EPI_SOFTCAP) {  // row scales of the final norm
+        for (int r = tid; r < 32 * FM; r += 256) {
+            const int m = min(r, p.M - 1);
+            float s = 0.f;
+            for (int q = 0; q < p.ss_in_parts; ++q) s += p.ss_in[(long long)q * p.ss_stride + m];
+            rs[r] = 1.0f / sqrtf(s / (float)p.K + p.eps);
+        }
+        __syncthreads();
+    }
+
+    // Stage t: block q < WKC ABLK is A (step q / ABLK, row block (q % ABLK) / NA, part
+    // q % NA); the rest are W (step (q - WKC ABLK) / 4, column block of wave
+    // (q - WKC ABLK) % 4).  Steps past the slice and blocks past the matrices load clamped
+    // addresses whose data is never used.
+    auto issue = [&](int t) {
+        bf16* sb = lds + (t % WNS) * STAGE;
+#pragma unroll
+        for (int u = 0; u < BPW; ++u) {
+            const int q = u * 4 + wave;
+            const bf16* src;
+            if (q < WKC * ABLK) {
+                const int kc = q / ABLK, r = q % ABLK;
+                const int step = min(s0 + t * WKC + kc, s1 - 1);
+                const int rb = min(r / NA, mblk - 1);
+                src = ((r % NA) ? AL : A) + ((long long)rb * ksteps + step) * 512 + lane * 8;
+            } else {
+                const int q2 = q - WKC * ABLK;
+                const int step = min(s0 + t * WKC + q2 / 4, s1 - 1);
+                const int nb = min(n0 / 32 + q2 % 4, nblk_w - 1);
+                src = W + ((long long)nb * ksteps + step) * 512 + lane * 8;
+            }
+            __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(sb + q * 512), 16, 0, 0);
+        }
+    };
+
+    f32x16 acc[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[i] = zero_vec<f32x16>();
+#pragma unroll
+    for (int t = 0; t < WNS - 1; ++t) issue(t);
+    for (int t = 0; t < nstg; ++t) {
+        NC_WAIT_VM((WNS - 2) * BPW);  // this wave's share of stage t is in LDS
+        __builtin_amdgcn_s_barrier(); // everyone's share is; everyone is done with stage t-1
+        issue(t + WNS - 1);           // refills the slot of stage t-1
+        const bf16* sb = lds + (t % WNS) * STAGE;
+#pragma unroll
+        for (int kc = 0; kc < WKC; ++kc) {
+            if (s0 + t * WKC + kc < s1) {
+                const bf16x8 wf = *(const bf16x8*)(sb + (WKC * ABLK + kc * 4 + wave) * 512 + l32 * 16 + 8 * hh);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int h = 0; h < NA; ++h) {
+                        const bf16x8 af = *(const bf16x8*)(sb + (kc * ABLK + i * NA + h) * 512 + l32 * 16 + 8 * hh);
+                        acc[i] = mma32(af, wf, acc[i]);
+                    }
+            }
+        }
+    }
+    NC_WAIT_VM_ALL();  // the ring's trailing loads land before the workgroup's LDS is released
+
+    // lane holds column n = n0 + 32 wave + l32 and rows 32 i + 8 (r / 4) + 4 hh + r % 4
+    const int nb = n0 / 32 + wave;
+    const int n = nb * 32 + l32;
+    const bool nok = n < p.N;
+    if constexpr (EPI != EPI_SOFTCAP) {  // split K: this slice's partial product
+        float* dst = p.part + (long long)blockIdx.y * p.M * p.N;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = 32 * i + 8 * (r / 4) + 4 * hh + (r % 4);
+                if (m < p.M && nok) dst[(long long)m * p.N + n] = acc[i][r];
+            }
+    } else {  // whole K: logits = cap tanh(r_m c / cap)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = 32 * i + 8 * (r / 4) + 4 * hh + (r % 4);
+                if (m < p.M && nok) p.out_f32[(long long)m * p.ldo + n] = p.cap * tanh_f32(acc[i][r] * rs[m] / p.cap);
+            }
+    }
+}
+
+// Split-K finish: workgroup (32 columns, 8 rows), wave w finishes rows w and w + 4: the
+// slices' partial products are added in slice order, then the row epilogue runs.
+template <int EPI>
+__global__ __launch_bounds__(256) void dec_reduce_kernel(DecGemmArgs p, int splits) {
+    constexpr int RPW = 2;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 8;
+    const int nn = min(n0 + (lane & 31), p.N - 1);
+    const long long slice = (long long)p.M * p.N;
+    float v[RPW], pre[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        v[i] = 0.f;
+        pre[i] = 0.f;
+    }
+    for (int s = 0; s < splits; ++s)
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int m = min(m0 + wave + 4 * i, p.M - 1);
+            v[i] += p.part[s * slice + (long long)m * p.N + nn];
+        }
+    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
+        for (int q = lane; q < p.ss_in_parts; q += 64)
+#pragma unroll
+            for (int i = 0; i < RPW; ++i)
+                pre[i] += p.ss_in[(long long)q * p.ss_stride + min(m0 + wave + 4 * i, p.M - 1)];
+    } else if (EPI == EPI_RESID) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) pre[i] = p.out_f32[(long long)min(m0 + wave + 4 * i, p.M - 1) * p.ldo + nn];
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int m = m0 + wave + 4 * i;
+        if (m < p.M) {  // wave-uniform
+            float r = 1.f;
+            if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) r = 1.0f / sqrtf(wave_sum(pre[i]) / (float)p.K + p.eps);
+            dec_row_epilogue<bf16, EPI>(p, m, n0, 32, lane, lane < 32 ? v[i] : 0.f, r, pre[i]);
+        }
+    }
+}
+
+template <int EPI, bool LO>
+static hipError_t wide_t(const DecGemmArgs& a, hipStream_t st) {
+    const WideShape w = wide_shape((Epi)EPI, a.M, LO, a.N, a.K);
+    if (w.splits > 1 && !a.part) return hipErrorInvalidValue;
+    dim3 g(w.tiles, w.splits);
+    if (a.M <= 64) NC_TLAUNCH((dec_gemm_wide_kernel<2, LO, EPI>), g, dim3(256), 0, st, a, w.splits, w.per);
+    else NC_TLAUNCH((dec_gemm_wide_kernel<4, LO, EPI>), g, dim3(256), 0, st, a, w.splits, w.per);
+    if (w.splits > 1)
+        NC_TLAUNCH((dec_reduce_kernel<EPI>), dim3((a.N + 31) / 32, (a.M + 7) / 8), dim3(256), 0, st, a, w.splits);
+    return hipGetLastError();
+}
+
+long long dec_gemm_part_elems(DType dt, Epi epi, int M, int N, int K) {
+    if (dt != BF16 || M <= 32) return 0;
+    const bool lo = epi == EPI_RELU2 || epi == EPI_RESID;  // the compensated MLP products
+    const WideShape w = std::max(wide_shape(epi, M, lo, N, K), wide_shape(epi, M, false, N, K),
+                                 [](const WideShape& x, const WideShape& y) { return x.splits < y.splits; });
+    return w.splits > 1 ? (long long)w.splits * M * N : 0;
+}
+
 int dec_gemm_tile_n() { return DEC_BN; }
 
 template <typename T>
@@ -222,6 +441,15 @@ static hipError_t dec_dt(Epi epi, const DecGemmArgs& a, hipStream_t st, int vari
     // compensated operands exist for the MLP products only (bf16 RELU2 and RESID)
     const bool lo = a.A_lo != nullptr;
     if (lo && (sizeof(T) != 2 || (epi != EPI_RELU2 && epi != EPI_RESID))) return hipErrorInvalidValue;
+    if (sizeof(T) == 2 && a.M > 32) {
+        switch (epi) {
+            case EPI_STORE: return wide_t<EPI_STORE, false>(a, st);
+            case EPI_RELU2: return lo ? wide_t<EPI_RELU2, true>(a, st) : wide_t<EPI_RELU2, false>(a, st);
+            case EPI_RESID: return lo ? wide_t<EPI_RESID, true>(a, st) : wide_t<EPI_RESID, false>(a, st);
+            case EPI_SOFTCAP: return wide_t<EPI_SOFTCAP, false>(a, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (epi) {
         case EPI_STORE: return dec_t<T, EPI_STORE, false>(a, st, variant);
         case EPI_RELU2:

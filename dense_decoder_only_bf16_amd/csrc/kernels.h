@@ -91,8 +91,11 @@ struct DecGemmArgs {
     int32_t* lens_inc;  // if set, workgroup 0 adds one to lens_inc[0..M) (end of a decode step)
     const void* A_lo;   // compensated operand, as in GemmArgs (bf16 only; null: plain A)
     void* out_lo;       // RELU2 / RESID low-part output, as in GemmArgs (null: not written)
+    float* part;        // bf16 with M > 32: fp32 split-K partials, dec_gemm_part_elems(M, N, K)
 };
 int dec_gemm_tile_n();
+// Elements of DecGemmArgs::part that a product of this shape needs (0: none).
+long long dec_gemm_part_elems(DType dt, Epi epi, int M, int N, int K);
 hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t st, int variant = 0);
 
 // x[m] = norm(wte[tok[m]]) (fp32, row-major), act[m] = dtype copy (row-major, or blocked

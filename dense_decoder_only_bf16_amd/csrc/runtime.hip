@@ -118,6 +118,8 @@ struct nc_kv {
     void* act_lo = nullptr;   // bf16 only: low parts of the MLP operands (compensated
     void* u_lo = nullptr;     // products): x - bf16(x) after attention, u - bf16(u)
     float* apart = nullptr;   // decode attention partials
+    float* dpart = nullptr;   // decode projections with more than 32 rows: split-K partials
+    long long dpart_elems = 0;
     long long apart_elems = 0;
     // decode step captured as a HIP graph, keyed by the caller's token/logit buffers
     bool use_graph = true;
@@ -144,12 +146,13 @@ void drop_graphs(nc_kv* kv) {
 void ws_free(nc_kv* kv) {
     drop_graphs(kv);  // captured graphs point into the workspace
     void* ptrs[] = {kv->x, kv->act, kv->ss_a, kv->ss_b, kv->qkv, kv->q, kv->y, kv->u, kv->apart,
-                    kv->act_lo, kv->u_lo};
+                    kv->act_lo, kv->u_lo, kv->dpart};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     kv->x = nullptr; kv->act = nullptr; kv->ss_a = nullptr; kv->ss_b = nullptr; kv->qkv = nullptr;
     kv->q = nullptr; kv->y = nullptr; kv->u = nullptr; kv->apart = nullptr;
-    kv->act_lo = nullptr; kv->u_lo = nullptr;
+    kv->act_lo = nullptr; kv->u_lo = nullptr; kv->dpart = nullptr;
+    kv->dpart_elems = 0;
     kv->cap_m = 0;
     kv->apart_elems = 0;
 }
@@ -183,6 +186,18 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
     }
     kv->apart_elems = (long long)kv->B * attn_decode_slots(kv->S) * 16 * (c.head_dim + 2);
     WS_ALLOC(kv->apart, kv->apart_elems * 4);
+    {   // split-K partials of the decode projections (M = batch rows)
+        const int B = kv->B, d = c.d_model, F = c.d_ff, hqv = c.n_head * c.head_dim;
+        const int nq = (c.n_head + 2) * c.head_dim;
+        const DType dt = kv->m->dt;
+        long long e = std::max({dec_gemm_part_elems(dt, EPI_STORE, B, nq, d),
+                                dec_gemm_part_elems(dt, EPI_RESID, B, d, hqv),
+                                dec_gemm_part_elems(dt, EPI_RELU2, B, F, d),
+                                dec_gemm_part_elems(dt, EPI_RESID, B, d, F),
+                                dec_gemm_part_elems(dt, EPI_SOFTCAP, B, c.vocab, d)});
+        if (e > 0) WS_ALLOC(kv->dpart, e * 4);
+        kv->dpart_elems = e;
+    }
 #undef WS_ALLOC
     kv->cap_m = M;
     return NC_OK;
@@ -274,7 +289,7 @@ nc_status decode_gemm(nc_kv* kv, Epi epi, const DecGemmArgs& a, hipStream_t st) 
     if (a.out_lo) out += M * N * es;
     const double bytes = N * K * es + M * K * es * (a.A_lo ? 2 : 1) + out;
     LAUNCH(timed(NC_KC_DECODE_GEMM, bytes, 2 * M * N * K, st,
-                 [&] { return launch_dec_gemm(kv->m->dt, epi, a, st); }));
+                 [&] { return launch_dec_gemm(kv->m->dt, epi, a, st); }, 2));
     return NC_OK;
 }
 
@@ -308,7 +323,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         void* kc = (char*)kv->kcache + l * per_layer;
         void* vtc = (char*)kv->vcache + l * per_layer;
         DecGemmArgs a{};
-        a.M = B; a.eps = c.norm_eps; a.cap = c.softcap; a.ss_stride = ss;
+        a.M = B; a.eps = c.norm_eps; a.cap = c.softcap; a.ss_stride = ss; a.part = kv->dpart;
         // QKV raw product, then norm scale + RoPE + QK-norm + cache write at lens[b]
         a.A = kv->act; a.W = L.wqkv; a.N = nqkv; a.K = d;
         a.out_f32 = kv->qkv; a.ldo = nqkv;
@@ -347,7 +362,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         ss_a_parts = parts_d;
     }
     DecGemmArgs h{};
-    h.M = B; h.eps = c.norm_eps; h.cap = c.softcap; h.ss_stride = ss;
+    h.M = B; h.eps = c.norm_eps; h.cap = c.softcap; h.ss_stride = ss; h.part = kv->dpart;
     h.A = kv->act; h.W = m->lm; h.N = V; h.K = d;
     h.out_f32 = logits; h.ldo = V; h.ss_in = kv->ss_a; h.ss_in_parts = ss_a_parts;
     h.lens_inc = kv->lens_dev;  // the step's last kernel also advances every row by one

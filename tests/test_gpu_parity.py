@@ -99,6 +99,28 @@ def test_bf16_small_decode_teacher_forced(small):
     kv.close()
 
 
+@pytest.mark.parametrize("B", [40, 100])
+def test_bf16_small_decode_many_rows(small, B):
+    """Decode with more than 32 rows (the wide, split-K projection path and its reduce
+    kernel; B not a multiple of 32), rows at different context lengths, 3 teacher-forced
+    steps through the captured graph; every row is checked against the oracle."""
+    w, orc, gm = small
+    T, steps = 40, 3
+    toks = make_tokens(SMALL_BF16.vocab, B, T + steps, seed=20 + B)
+    lens = make_lens(B, 1, T, seed=30 + B)
+    kv, _ = prefill(gm, toks[:, :T], 64, logits=False)
+    kv.set_lens(lens)
+    got = np.stack([decode(gm, kv, toks[:, T + s]) for s in range(steps)], axis=1)  # [B, steps, V]
+    assert np.array_equal(kv.lens(), lens + steps)
+    want = np.empty_like(got, dtype=np.float64)
+    for b in range(B):
+        seq = np.concatenate([toks[b, :lens[b]], toks[b, T:T + steps]])[None]
+        want[b] = orc.prefill(seq, logits_at=np.arange(lens[b], lens[b] + steps))[0][0]
+    err, agr = report(f"small bf16 decode B={B}", got, want)
+    assert err <= BF16_TOL and agr >= AGREE
+    kv.close()
+
+
 def test_bf16_small_truncated_rows(small):
     # prefill, shrink rows to different lengths, decode: equals shorter prefills
     w, orc, gm = small
