@@ -532,13 +532,13 @@ __global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __
     __syncthreads();
     const float* po = prow + 32 + h * HD + d;
     float o = 0.f;
-    int sl = 0;
-    for (; sl + 4 <= nsl; sl += 4) {
-        const float o0 = po[(long long)sl * PSZ], o1 = po[(long long)(sl + 1) * PSZ];
-        const float o2 = po[(long long)(sl + 2) * PSZ], o3 = po[(long long)(sl + 3) * PSZ];
-        o += wts[sl] * o0 + wts[sl + 1] * o1 + wts[sl + 2] * o2 + wts[sl + 3] * o3;
+    for (int s0 = 0; s0 < nsl; s0 += 16) {  // 16 slots per batch of independent loads
+        float t[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) t[u] = po[(long long)min(s0 + u, nsl - 1) * PSZ];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) o += (s0 + u < nsl) ? wts[min(s0 + u, nsl - 1)] * t[u] : 0.f;
     }
-    for (; sl < nsl; ++sl) o += wts[sl] * po[(long long)sl * PSZ];
     y[blocked_index(b, h * HD + d, H * HD)] = from_f32<T>(o * stat[0]);
 }
 

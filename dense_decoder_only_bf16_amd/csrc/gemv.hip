@@ -287,12 +287,19 @@ __global__ __launch_bounds__(256) void dec_gemm_wide_kernel(DecGemmArgs p, int s
     if (p.lens_inc && blockIdx.x == 0 && blockIdx.y == 0)  // end of a decode step
         for (int r = tid; r < p.M; r += 256) p.lens_inc[r] += 1;
 
-    if (EPI == EPI_SOFTCAP) {  // row scales of the final norm
-        for (int r = tid; r < 32 * FM; r += 256) {
-            const int m = min(r, p.M - 1);
-            float s = 0.f;
-            for (int q = 0; q < p.ss_in_parts; ++q) s += p.ss_in[(long long)q * p.ss_stride + m];
-            rs[r] = 1.0f / sqrtf(s / (float)p.K + p.eps);
+    if (EPI == EPI_SOFTCAP) {  // row scales of the final norm: wave w does rows w + 4 j,
+        // lanes over the partial sums, every load of every row issued before any sum
+        constexpr int RW = 8 * FM;
+        float s[RW];
+#pragma unroll
+        for (int j = 0; j < RW; ++j) s[j] = 0.f;
+        for (int q = lane; q < p.ss_in_parts; q += 64)
+#pragma unroll
+            for (int j = 0; j < RW; ++j) s[j] += p.ss_in[(long long)q * p.ss_stride + min(wave + 4 * j, p.M - 1)];
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            const float t = wave_sum(s[j]);
+            if (lane == 0) rs[wave + 4 * j] = 1.0f / sqrtf(t / (float)p.K + p.eps);
         }
         __syncthreads();
     }
@@ -388,12 +395,21 @@ __global__ __launch_bounds__(256) void dec_reduce_kernel(DecGemmArgs p, int spli
         v[i] = 0.f;
         pre[i] = 0.f;
     }
-    for (int s = 0; s < splits; ++s)
+    for (int s0 = 0; s0 < splits; s0 += 8) {  // 8 slices per batch of independent loads
+        float t[8][RPW];
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            const int m = min(m0 + wave + 4 * i, p.M - 1);
-            v[i] += p.part[s * slice + (long long)m * p.N + nn];
-        }
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+                const int m = min(m0 + wave + 4 * i, p.M - 1);
+                const int s = min(s0 + u, splits - 1);
+                t[u][i] = p.part[s * slice + (long long)m * p.N + nn];
+            }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) v[i] += (s0 + u < splits) ? t[u][i] : 0.f;
+    }
     if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
         for (int q = lane; q < p.ss_in_parts; q += 64)
 #pragma unroll

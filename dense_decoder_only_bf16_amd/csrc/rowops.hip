@@ -170,11 +170,19 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
     if (vec) {
         const f32x4* r4 = (const f32x4*)row;
         const int n4 = V >> 2;
-        for (int i = tid; i < n4; i += 1024) {
-            f32x4 v = r4[i];
+        for (int i0 = tid; i0 < n4; i0 += 8 * 1024) {  // 8 independent loads per batch
+            f32x4 v[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (better(v[e], 4 * i + e, bv, bi)) { bv = v[e]; bi = 4 * i + e; }
+            for (int u = 0; u < 8; ++u) v[u] = r4[min(i0 + 1024 * u, n4 - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + 1024 * u;
+                if (i < n4) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (better(v[u][e], 4 * i + e, bv, bi)) { bv = v[u][e]; bi = 4 * i + e; }
+                }
+            }
         }
     } else {
         for (int i = tid; i < V; i += 1024) {
