@@ -15,8 +15,9 @@
 // leaves a relative operand error near 2^-17 (the weights are exact bf16 values).  The
 // producing epilogue writes both parts.
 //
-// Tiling: a workgroup computes a 256 x 256 tile with 2 x 2 waves; each wave owns a
-// 128 x 128 sub-tile of 4 x 4 MFMA 32x32 tiles (256 accumulator registers).  Operands are
+// Tiling: a workgroup computes a 256 x 256 tile.  bf16: 2 x 4 waves (two per SIMD, so one
+// wave's MFMAs cover the other's waits at barriers and LDS reads), each owning a 128 x 64
+// sub-tile of 4 x 2 MFMA 32x32 tiles; fp32: 2 x 2 waves of 128 x 128.  Operands are
 // staged in LDS in the MFMA-blocked form [rows/32][K/16][32][16]: one 32x16 block is
 // exactly one wave's 16-deep operand, so every LDS operand read is 1 KB contiguous.
 // Weights arrive in that blocked form from global memory (see kernels.h).
@@ -27,8 +28,7 @@
 //    stages ahead; no staging registers and no LDS store instructions.  The operand
 //    fragments of the next 16-deep step (also across a K-tile boundary) are read from LDS
 //    while the MFMAs of the current step run (fragments double-buffered in registers,
-//    reads interleaved one per two MFMAs), so with one wave per SIMD neither LDS latency
-//    nor LDS bandwidth stalls the matrix cores.
+//    reads interleaved one per MFMA).
 //  * fp32 (the small fp32 check model): loads staged through registers into two LDS
 //    buffers (A kept row-major with an XOR swizzle).
 // Workgroups are dealt round-robin to the 8 dies (XCDs), each with its own L2; tiles are
@@ -75,24 +75,27 @@ __device__ __forceinline__ void tile_row_scales(const GemmArgs& p, int m0, float
     }
 }
 
-// Epilogue on the accumulators: lane holds column n0 + wn*128 + 32j + l32 and rows
-// m0 + wm*128 + 32i + 8(r/4) + 4hh + (r%4) of acc[i][j][r].
-template <typename T, int EPI>
-__device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[4][4], int m0, int n0,
-                                              int tn, const float* rs, float (*red)[TBM]) {
+// Epilogue on the accumulators of a workgroup of WM x WN waves: wave (wm, wn) owns rows
+// m0 + wm (256/WM) + [0, 256/WM) and columns n0 + wn (256/WN) + [0, 256/WN); its lane holds
+// column n0 + wn (256/WN) + 32 j + l32 and rows ... + 32 i + 8 (r/4) + 4 hh + (r%4) of
+// acc[i][j][r].  RESID leaves one sum of squares per row and tile in ss_out.
+template <typename T, int EPI, int WM, int WN>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[256 / WM / 32][256 / WN / 32],
+                                              int m0, int n0, int tn, const float* rs, float (*red)[TBM]) {
+    constexpr int IM = 256 / WM / 32, JN = 256 / WN / 32, NT = 64 * WM * WN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < IM; ++i) {
 #pragma unroll
         for (int jr = 0; jr < 16; ++jr) {
-            const int rl = wm * 128 + i * 32 + 8 * (jr / 4) + 4 * hh + (jr % 4);
+            const int rl = wm * (256 / WM) + i * 32 + 8 * (jr / 4) + 4 * hh + (jr % 4);
             const int m = m0 + rl;
             float sq = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = n0 + wn * 128 + j * 32 + l32;
+            for (int j = 0; j < JN; ++j) {
+                const int n = n0 + wn * (256 / WN) + j * 32 + l32;
                 const bool ok = (m < p.M) && (n < p.N);
                 const float v = acc[i][j][jr];
                 const long long o = (long long)m * p.ldo + n;
@@ -125,9 +128,12 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[4
     }
     if (EPI == EPI_RESID) {
         __syncthreads();
-        for (int r = tid; r < TBM; r += 256) {
+        for (int r = tid; r < TBM; r += NT) {
             const int m = m0 + r;
-            if (m < p.M) p.ss_out[(long long)tn * p.ss_stride + m] = red[0][r] + red[1][r];
+            float s = 0.f;
+#pragma unroll
+            for (int w = 0; w < WN; ++w) s += red[w][r];
+            if (m < p.M) p.ss_out[(long long)tn * p.ss_stride + m] = s;
         }
     }
 }
@@ -135,17 +141,17 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[4
 // ---------------------------------------------------------------------- bf16 ----------
 
 template <int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_kernel(GemmArgs p) {
     constexpr int BK = 32, KB = BK / 16, NS = 4;
     constexpr int STAGE = (TBM + TBN) * BK;       // elements per stage (A then B)
     __shared__ __attribute__((aligned(1024))) bf16 lds[NS * STAGE];
     __shared__ float rs[TBM];
-    __shared__ float red[2][TBM];
+    __shared__ float red[4][TBM];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / 4, wn = wave % 4;       // 2 x 4 waves, 128 x 64 each
     const int l32 = lane & 31, hh = lane >> 5;
     int m0, n0, tn;
     tile_coords(p, m0, n0, tn);
@@ -158,10 +164,10 @@ void gemm_bf16_kernel(GemmArgs p) {
     const bf16* A_lo = (const bf16*)p.A_lo;
     const bf16* B = (const bf16*)p.B;
 
-    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) tile_row_scales(p, m0, rs, 256);
+    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) tile_row_scales(p, m0, rs, 512);
 
     // Stage layout: 16 A blocks (row block rb = b/2, k block b%2) then 16 B blocks.  Wave w
-    // loads A blocks 4w..4w+3 and B blocks 4w..4w+3; lane l fills bytes [16 l, 16 l + 16)
+    // loads A blocks 2w, 2w+1 and B blocks 2w, 2w+1; lane l fills bytes [16 l, 16 l + 16)
     // of a 1 KB block, i.e. row l/2, k half l%2.  Rows past M or Npad read a clamped
     // address; their outputs are masked in the epilogue.
     auto issue = [&](int kt) {
@@ -169,8 +175,8 @@ void gemm_bf16_kernel(GemmArgs p) {
         const int k0 = (comp ? kt >> 1 : kt) * BK;
         const bf16* As = (comp && (kt & 1)) ? A_lo : A;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int b = wave * 4 + u;
+        for (int u = 0; u < 2; ++u) {
+            const int b = wave * 2 + u;
             const int rb = b / KB, kb = b % KB;
             int m = m0 + rb * 32 + lane / 2;
             m = m < p.M ? m : p.M - 1;
@@ -178,8 +184,8 @@ void gemm_bf16_kernel(GemmArgs p) {
             __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(sbase + b * 512), 16, 0, 0);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int b = wave * 4 + u;
+        for (int u = 0; u < 2; ++u) {
+            const int b = wave * 2 + u;
             const int rb = b / KB, kb = b % KB;
             int nb = n0 / 32 + rb;
             nb = nb < p.Npad / 32 ? nb : p.Npad / 32 - 1;
@@ -188,49 +194,53 @@ void gemm_bf16_kernel(GemmArgs p) {
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = zero_vec<f32x16>();
+        for (int j = 0; j < 2; ++j) acc[i][j] = zero_vec<f32x16>();
 
-    // Operand fragments of one 16-deep step: 4 A blocks and 4 B blocks.
-    typedef bf16x8 Frag[4];
-    auto fload = [&](int kt, int s, Frag& fa, Frag& fb) {
+    // Operand fragments of one 16-deep step: 4 A blocks and 2 B blocks.
+    typedef bf16x8 FragA[4];
+    typedef bf16x8 FragB[2];
+    auto fload = [&](int kt, int s, FragA& fa, FragB& fb) {
         const bf16* sa = lds + (kt % NS) * STAGE;
         const bf16* sb = sa + TBM * BK;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             fa[i] = *(const bf16x8*)(sa + ((wm * 4 + i) * KB + s) * 512 + l32 * 16 + 8 * hh);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            fb[j] = *(const bf16x8*)(sb + ((wn * 4 + j) * KB + s) * 512 + l32 * 16 + 8 * hh);
+        for (int j = 0; j < 2; ++j)
+            fb[j] = *(const bf16x8*)(sb + ((wn * 2 + j) * KB + s) * 512 + l32 * 16 + 8 * hh);
     };
-    // 16 MFMAs of one step, with the 8 LDS reads of the next step interleaved (one read
-    // per two MFMAs) so the reads' latency hides behind the matrix cores.
-    auto mfmas = [&](Frag& fa, Frag& fb, bool interleave) {
+    // 8 MFMAs of one step, with the 6 LDS reads of the next step interleaved (one read per
+    // MFMA) so the reads' latency hides behind the matrix cores.
+    auto mfmas = [&](FragA& fa, FragB& fb, bool interleave) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mma32(fa[i], fb[j], acc[i][j]);
+            for (int j = 0; j < 2; ++j) acc[i][j] = mma32(fa[i], fb[j], acc[i][j]);
         if (interleave) {
 #pragma unroll
-            for (int g = 0; g < 8; ++g) {
+            for (int g = 0; g < 6; ++g) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
     };
 
-    // Prologue: tiles 0 .. NS-2 in flight, fragments of tile 0, step 0 in registers.
+    // Prologue: tiles 0 .. NS-2 in flight (4 loads per wave each), fragments of tile 0,
+    // step 0 in registers.
 #pragma unroll
     for (int kt = 0; kt < NS - 1; ++kt)
         if (kt < nk) issue(kt);
-    if (nk > 2) NC_WAIT_VM(16);
-    else if (nk > 1) NC_WAIT_VM(8);
+    if (nk > 2) NC_WAIT_VM(8);
+    else if (nk > 1) NC_WAIT_VM(4);
     else NC_WAIT_VM(0);
     __builtin_amdgcn_s_barrier();
-    Frag a0, b0, a1, b1;
+    FragA a0, a1;
+    FragB b0, b1;
     fload(0, 0, a0, b0);
     for (int kt = 0; kt < nk; ++kt) {
         // step 0 of tile kt; read step 1 of tile kt meanwhile
@@ -241,7 +251,7 @@ void gemm_bf16_kernel(GemmArgs p) {
         // whose stage the next issue overwrites.
         const bool more = kt + 1 < nk;
         if (more) {
-            if (kt + 2 < nk) NC_WAIT_VM(8);
+            if (kt + 2 < nk) NC_WAIT_VM(4);
             else NC_WAIT_VM(0);
             __builtin_amdgcn_s_barrier();
             if (kt + NS - 1 < nk) issue(kt + NS - 1);
@@ -250,7 +260,7 @@ void gemm_bf16_kernel(GemmArgs p) {
         mfmas(a1, b1, more);
     }
     __syncthreads();
-    tile_epilogue<bf16, EPI>(p, acc, m0, n0, tn, rs, red);
+    tile_epilogue<bf16, EPI, 2, 4>(p, acc, m0, n0, tn, rs, red);
 }
 
 // ---------------------------------------------------------------------- fp32 ----------
@@ -343,7 +353,7 @@ void gemm_f32_kernel(GemmArgs p) {
         if (kt + 1 < nk) sstore(buf ^ 1);
         __syncthreads();
     }
-    tile_epilogue<T, EPI>(p, acc, m0, n0, tn, rs, red);
+    tile_epilogue<T, EPI, 2, 2>(p, acc, m0, n0, tn, rs, red);
 }
 
 template <int EPI>
@@ -351,7 +361,7 @@ static hipError_t launch_e(DType dt, const GemmArgs& a, hipStream_t st) {
     dim3 grid(((a.N + TBN - 1) / TBN) * ((a.M + TBM - 1) / TBM), 1, a.k_split);
     if (dt == BF16) {
         if (a.k_split != 1 || a.K % 32) return hipErrorInvalidValue;
-        NC_TLAUNCH((gemm_bf16_kernel<EPI>), grid, dim3(256), 0, st, a);
+        NC_TLAUNCH((gemm_bf16_kernel<EPI>), grid, dim3(512), 0, st, a);
     } else {
         if (a.A_lo || a.out_lo) return hipErrorInvalidValue;  // fp32 operands need no compensation
         NC_TLAUNCH((gemm_f32_kernel<EPI>), grid, dim3(256), 0, st, a);

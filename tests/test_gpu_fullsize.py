@@ -107,14 +107,14 @@ def test_d20_prefill_32x2048(d20):
     logits = torch.empty((B, T, D20.vocab), device="cuda", dtype=torch.float32)
     kv.prefill(torch.from_numpy(toks).cuda(), logits)
     torch.cuda.synchronize()
-    g0 = logits[0, :384].cpu().numpy()
-    g31 = logits[31, :128].cpu().numpy()
+    g0 = logits[0, :1024].cpu().numpy()
+    g31 = logits[31, :256].cpu().numpy()
     del logits
     kv.close()
-    w0, _ = d20.orc.prefill(toks[0:1, :384])
-    check("d20 prefill row 0 (first 384)", g0, w0[0])
-    w31, _ = d20.orc.prefill(toks[31:32, :128])
-    check("d20 prefill row 31 (first 128)", g31, w31[0])
+    w0, _ = d20.orc.prefill(toks[0:1, :1024])
+    w31, _ = d20.orc.prefill(toks[31:32, :256])
+    check("d20 prefill rows 0 (first 1024) and 31 (first 256)", np.concatenate([g0, g31]),
+          np.concatenate([w0[0], w31[0]]))
 
 
 def test_d20_decode_64_rows_at_2048(d20):
@@ -142,12 +142,12 @@ def test_d26_prefill_16x2048():
     logits = torch.empty((B, T, D26.vocab), device="cuda", dtype=torch.float32)
     kv.prefill(torch.from_numpy(toks).cuda(), logits)
     torch.cuda.synchronize()
-    g = logits[7, :256].cpu().numpy()
+    g = logits[7, :768].cpu().numpy()
     del logits
     kv.close()
     r.close()
-    w, _ = r.orc.prefill(toks[7:8, :256])
-    check("d26 prefill row 7 (first 256)", g, w[0])
+    w, _ = r.orc.prefill(toks[7:8, :768])
+    check("d26 prefill row 7 (first 768)", g, w[0])
 
 
 def test_d30_decode_mixed_lengths():
