@@ -10,10 +10,10 @@
 //
 // Compensated operands: a bf16 operand carries a relative rounding error of up to 2^-9, and
 // in the MLP that error is amplified by the squared ReLU and summed over d_ff terms.  For
-// the MLP products the activation is therefore passed as two bf16 arrays, hi = bf16(a) and
-// lo = bf16(a - hi), and multiplied as hi W^T + lo W^T with fp32 accumulation, which
-// leaves a relative operand error near 2^-17 (the weights are exact bf16 values).  The
-// producing epilogue writes both parts.
+// the MLP products and the LM head the activation is therefore passed as two bf16 arrays,
+// hi = bf16(a) and lo = bf16(a - hi), and multiplied as hi W^T + lo W^T with fp32
+// accumulation, which leaves a relative operand error near 2^-17 (the weights are exact
+// bf16 values).  The producing epilogue writes both parts.
 //
 // Tiling: a workgroup computes a 256 x 256 tile.  bf16: 2 x 4 waves (two per SIMD, so one
 // wave's MFMAs cover the other's waits at barriers and LDS reads), each owning a 128 x 64

@@ -444,7 +444,7 @@ static hipError_t wide_t(const DecGemmArgs& a, hipStream_t st) {
 
 long long dec_gemm_part_elems(DType dt, Epi epi, int M, int N, int K) {
     if (dt != BF16 || M <= 32) return 0;
-    const bool lo = epi == EPI_RELU2 || epi == EPI_RESID;  // the compensated MLP products
+    const bool lo = epi != EPI_STORE;  // compensated operands: MLP products and LM head
     const WideShape w = std::max(wide_shape(epi, M, lo, N, K), wide_shape(epi, M, false, N, K),
                                  [](const WideShape& x, const WideShape& y) { return x.splits < y.splits; });
     return w.splits > 1 ? (long long)w.splits * M * N : 0;
@@ -454,15 +454,15 @@ int dec_gemm_tile_n() { return DEC_BN; }
 
 template <typename T>
 static hipError_t dec_dt(Epi epi, const DecGemmArgs& a, hipStream_t st, int variant) {
-    // compensated operands exist for the MLP products only (bf16 RELU2 and RESID)
+    // compensated operands exist for the MLP products and the LM head (bf16 only)
     const bool lo = a.A_lo != nullptr;
-    if (lo && (sizeof(T) != 2 || (epi != EPI_RELU2 && epi != EPI_RESID))) return hipErrorInvalidValue;
+    if (lo && (sizeof(T) != 2 || epi == EPI_STORE)) return hipErrorInvalidValue;
     if (sizeof(T) == 2 && a.M > 32) {
         switch (epi) {
             case EPI_STORE: return wide_t<EPI_STORE, false>(a, st);
             case EPI_RELU2: return lo ? wide_t<EPI_RELU2, true>(a, st) : wide_t<EPI_RELU2, false>(a, st);
             case EPI_RESID: return lo ? wide_t<EPI_RESID, true>(a, st) : wide_t<EPI_RESID, false>(a, st);
-            case EPI_SOFTCAP: return wide_t<EPI_SOFTCAP, false>(a, st);
+            case EPI_SOFTCAP: return lo ? wide_t<EPI_SOFTCAP, true>(a, st) : wide_t<EPI_SOFTCAP, false>(a, st);
             default: return hipErrorInvalidValue;
         }
     }
@@ -472,7 +472,8 @@ static hipError_t dec_dt(Epi epi, const DecGemmArgs& a, hipStream_t st, int vari
             return lo ? dec_t<T, EPI_RELU2, sizeof(T) == 2>(a, st, variant) : dec_t<T, EPI_RELU2, false>(a, st, variant);
         case EPI_RESID:
             return lo ? dec_t<T, EPI_RESID, sizeof(T) == 2>(a, st, variant) : dec_t<T, EPI_RESID, false>(a, st, variant);
-        case EPI_SOFTCAP: return dec_t<T, EPI_SOFTCAP, false>(a, st, variant);
+        case EPI_SOFTCAP:
+            return lo ? dec_t<T, EPI_SOFTCAP, sizeof(T) == 2>(a, st, variant) : dec_t<T, EPI_SOFTCAP, false>(a, st, variant);
         default: return hipErrorInvalidValue;
     }
 }

@@ -358,12 +358,13 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         DecGemmArgs pj = a;
         pj.A = kv->u; pj.A_lo = kv->u_lo; pj.W = L.wproj; pj.N = d; pj.K = F;
         pj.out_f32 = kv->x; pj.out_t = kv->act; pj.ldo = d; pj.ss_out = kv->ss_a;
+        if (l == c.n_layer - 1) pj.out_lo = kv->act_lo;  // the LM head's operand is compensated
         if ((s = decode_gemm(kv, EPI_RESID, pj, st)) != NC_OK) return s;
         ss_a_parts = parts_d;
     }
     DecGemmArgs h{};
     h.M = B; h.eps = c.norm_eps; h.cap = c.softcap; h.ss_stride = ss; h.part = kv->dpart;
-    h.A = kv->act; h.W = m->lm; h.N = V; h.K = d;
+    h.A = kv->act; h.A_lo = kv->act_lo; h.W = m->lm; h.N = V; h.K = d;
     h.out_f32 = logits; h.ldo = V; h.ss_in = kv->ss_a; h.ss_in_parts = ss_a_parts;
     h.lens_inc = kv->lens_dev;  // the step's last kernel also advances every row by one
     if ((s = decode_gemm(kv, EPI_SOFTCAP, h, st)) != NC_OK) return s;
@@ -635,14 +636,16 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             // PROJ + residual (compensated operand)
             g.A = kv->u; g.lda = F; g.B = L.wproj; g.N = d; g.K = F; g.Npad = d;
             g.out_f32 = kv->x; g.out_t = kv->act; g.ldo = d; g.ss_out = kv->ss_a; g.ss_stride = (int)kv->cap_m;
-            g.A_lo = kv->u_lo; g.out_lo = nullptr;
+            g.A_lo = kv->u_lo;
+            g.out_lo = (l == c.n_layer - 1) ? kv->act_lo : nullptr;  // LM head operand, compensated
             LAUNCH(prefill_gemm(m, EPI_RESID, g, st));
             g.A_lo = nullptr;
             ss_a_parts = parts_d;
         }
         if (logits) {
             GemmArgs g{};
-            g.A = kv->act; g.lda = d; g.B = m->lm; g.M = Mi; g.N = V; g.K = d; g.Npad = (V + 31) / 32 * 32; g.k_split = 1;
+            g.A = kv->act; g.A_lo = kv->act_lo; g.lda = d; g.B = m->lm; g.M = Mi; g.N = V; g.K = d;
+            g.Npad = (V + 31) / 32 * 32; g.k_split = 1;
             g.out_f32 = logits; g.ldo = V; g.ss_in = kv->ss_a; g.ss_in_parts = ss_a_parts;
             g.ss_stride = (int)kv->cap_m; g.eps = c.norm_eps; g.cap = c.softcap;
             LAUNCH(prefill_gemm(m, EPI_SOFTCAP, g, st));
