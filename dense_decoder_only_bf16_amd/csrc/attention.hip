@@ -229,9 +229,11 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 }
 
 // ------------------------------------------------------------------ decode ----------
-// Split kernel.  Workgroup (chunk c, row b): 2 waves x 64 keys = keys [128c, 128c + 128)
-// limited to positions 0..lens[b]; each wave writes its own partial softmax state
-// (max, sum, o[16][hd]) to slot 2c + wave.
+// Split kernel.  Workgroup (chunk c, row b), NW = 2 or 4 waves: the keys [c CK, c CK + CK)
+// of row b, CK = 64 NW R, limited to positions 0..lens[b].  Wave w takes the 64-key blocks
+// (c R + i) NW + w, i < R, one after another and keeps an online-softmax state (running
+// max, sum and o[16][hd]) across them; at the end the NW states are merged in LDS into the
+// chunk's partial state, slot c of row b.
 //  1. Finish the QKV product of row b for this step (the row's attention-norm scale,
 //     RoPE at position lens[b] and QK-norm of the query heads and the key head; the value
 //     head as is) into LDS.  Every workgroup of the row does this (a few hundred values);
@@ -239,30 +241,47 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 //     cache for later steps.
 //  2. All query heads of the row (padded to 16) form the 16 columns of 16x16 MFMA tiles,
 //     so each cached K/V element is read from memory once for the whole head group.
-//     bf16: each wave stages its 64 keys of K (64 x hd) and V^T (hd x 64) in LDS with
-//     1 KB direct-to-LDS loads issued before step 1, XOR-swizzled so that the MFMA operand
-//     reads are free of bank conflicts.  fp32 (small check model): operands are loaded
-//     straight into registers.  Cached keys at or past lens[b] are masked in the scores;
-//     the new key (position lens[b]) is not read from the cache but added to the wave's
-//     softmax state as one extra term from the values in LDS.
-constexpr int DEC_WAVES = 2, DEC_KPW = 64, DEC_CHUNK = DEC_WAVES * DEC_KPW;
-int attn_decode_chunk() { return DEC_CHUNK; }
-int attn_decode_slots(int S) { return (S + DEC_CHUNK - 1) / DEC_CHUNK * DEC_WAVES; }
+//     bf16: a wave stages a block's K (64 x hd) and V^T (hd x 64) in its own LDS region
+//     with 1 KB direct-to-LDS loads, XOR-swizzled so that the MFMA operand reads are free
+//     of bank conflicts; once the block's operands are in registers, the next block's
+//     loads are issued and overlap this block's arithmetic.  fp32 (small check model):
+//     operands are loaded straight into registers.  Cached keys at or past lens[b] are
+//     masked in the scores; the new key (position lens[b]) is not read from the cache but
+//     added to the state of the wave whose block holds it, as one extra term from the
+//     values in LDS.
+constexpr int DEC_KPW = 64;
+// Waves per workgroup: 4, or 2 when the rows are few (more, smaller workgroups then).
+int attn_decode_waves(int B, int S) { return (long long)B * ((S + 255) / 256) >= 128 ? 4 : 2; }
+int attn_decode_iters(int B, int S) {
+    // The largest R in {1, 2, 4} that still leaves 128 workgroups or more: a wave's blocks
+    // run one after another at about one memory latency each, so longer chunks amortize
+    // the QKV finish and the merge until too few workgroups are left to fill the chip
+    // (measured at d12, d20 and d30 decode shapes).
+    const int nw = attn_decode_waves(B, S);
+    int r = 1;
+    while (r < 4 && (long long)B * ((S + nw * 64 * 2 * r - 1) / (nw * 64 * 2 * r)) >= 128) r *= 2;
+    return r;
+}
+int attn_decode_slots(int B, int S) {
+    const int ck = attn_decode_waves(B, S) * DEC_KPW * attn_decode_iters(B, S);
+    return (S + ck - 1) / ck;
+}
 
-template <typename T, int HD>
-__global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_split_kernel(DecAttnArgs a) {
+template <typename T, int HD, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs a) {
     typedef typename Chunk<T>::type CT;
     typedef typename Chunk<T>::half HT;
     constexpr bool STAGE = sizeof(T) == 2;  // LDS staging for bf16
-    constexpr int NW = DEC_WAVES;
     constexpr int DS = HD / 32;   // 32-deep steps over head dim for S^T
     constexpr int DT = HD / 16;   // 16-row tiles of O^T
     constexpr int PSZ = 16 * (HD + 2);
     constexpr int HALF = HD / 2;
-    constexpr int KREG = STAGE ? DEC_KPW * HD * 2 : 16;  // bytes of one wave's K (or V^T) tile
-    constexpr int NSLOT = (18 + NW - 1) / NW;           // QKV-finish slots per wave
+    constexpr int KREG = DEC_KPW * HD * 2;  // bytes of one block's K (and of its V^T), bf16
+    constexpr int WREG = 2 * KREG;          // a wave's region: staging, then its final state
+    static_assert(WREG >= PSZ * 4, "a wave's state fits its region");
+    constexpr int NSLOT = (18 + NW - 1) / NW;  // QKV-finish slots per wave
 
-    __shared__ __attribute__((aligned(1024))) unsigned char buf[NW * 2 * KREG];
+    __shared__ __attribute__((aligned(1024))) unsigned char buf[NW * WREG];
     __shared__ __attribute__((aligned(32))) T qs[16][HD];
     __shared__ __attribute__((aligned(32))) T kv_new[2][HD];
 
@@ -270,41 +289,47 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_split_kernel(DecAt
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g = lane >> 4;
     const int c = blockIdx.x, b = blockIdx.y;
-    const int S = a.S, H = a.H;
+    const int S = a.S, H = a.H, R = a.iters;
+    const int CK = NW * DEC_KPW * R;
     const int pos = a.lens[b];  // this step's position; keys 0..pos are visible
     if (pos < 0 || pos >= S) return;  // capacity is checked by the host; stay in bounds
-    const int nchunks = (pos + 1 + DEC_CHUNK - 1) / DEC_CHUNK;
+    const int nchunks = (pos + 1 + CK - 1) / CK;
     if (c >= nchunks) return;
-    const int kbeg = c * DEC_CHUNK + wave * DEC_KPW;
     T* kb_base = (T*)a.kc + (long long)b * S * HD;
     T* vb_base = (T*)a.vtc + (long long)b * HD * S;
-    unsigned char* kl = buf + wave * 2 * KREG;  // K: 64 keys x HD, 16-byte chunks swizzled
-    unsigned char* vl = kl + KREG;               // V^T: HD rows x 64 keys (128 bytes a row)
+    unsigned char* kl = buf + wave * WREG;  // K: 64 keys x HD, 16-byte chunks swizzled
+    unsigned char* vl = kl + KREG;           // V^T: HD rows x 64 keys (128 bytes a row)
+    // first key of this wave's i-th block; a block starting past pos holds no visible key
+    auto kbeg_of = [&](int i) { return ((c * R + i) * NW + wave) * DEC_KPW; };
 
-    // ---- staging loads of this wave's cached K and V^T (bf16)
-    if constexpr (STAGE) {
-        constexpr int KCH = HD / 8;  // 16-byte chunks per K row
-        // K: LDS byte 16 p of the wave's tile holds key p / KCH, chunk (p % KCH) ^ (key % KCH)
+    // ---- staging loads of one block of cached K and V^T (bf16)
+    auto issue = [&](int kbeg) {
+        if constexpr (STAGE) {
+            constexpr int KCH = HD / 8;  // 16-byte chunks per K row
+            // K: LDS byte 16 p holds key p / KCH, chunk (p % KCH) ^ (key % KCH)
 #pragma unroll
-        for (int j = 0; j < KREG / 1024; ++j) {
-            const int p = j * 64 + lane;
-            const int kidx = p / KCH, cch = (p % KCH) ^ (kidx % KCH);
-            int key = kbeg + kidx;
-            key = key < pos ? key : (pos > 0 ? pos - 1 : 0);  // keys >= pos are masked
-            __builtin_amdgcn_global_load_lds((gvoid*)(kb_base + (long long)key * HD + cch * 8),
-                                             (lvoid*)(kl + j * 1024), 16, 0, 0);
-        }
-        // V^T: LDS byte 16 p holds row d = p / 8, keys 8 ((p % 8) ^ (d % 8)) .. +8
+            for (int j = 0; j < KREG / 1024; ++j) {
+                const int p = j * 64 + lane;
+                const int kidx = p / KCH, cch = (p % KCH) ^ (kidx % KCH);
+                int key = kbeg + kidx;
+                key = key < pos ? key : (pos > 0 ? pos - 1 : 0);  // keys >= pos are masked
+                __builtin_amdgcn_global_load_lds((gvoid*)(kb_base + (long long)key * HD + cch * 8),
+                                                 (lvoid*)(kl + j * 1024), 16, 0, 0);
+            }
+            // V^T: LDS byte 16 p holds row d = p / 8, keys 8 ((p % 8) ^ (d % 8)) .. +8
 #pragma unroll
-        for (int j = 0; j < KREG / 1024; ++j) {
-            const int p = j * 64 + lane;
-            const int d = p / 8;
-            int k0 = kbeg + 8 * ((p % 8) ^ (d % 8));
-            k0 = k0 <= S - 8 ? k0 : S - 8;  // a chunk starting at or past S is fully masked
-            __builtin_amdgcn_global_load_lds((gvoid*)(vb_base + (long long)d * S + k0),
-                                             (lvoid*)(vl + j * 1024), 16, 0, 0);
+            for (int j = 0; j < KREG / 1024; ++j) {
+                const int p = j * 64 + lane;
+                const int d = p / 8;
+                int k0 = kbeg + 8 * ((p % 8) ^ (d % 8));
+                k0 = k0 <= S - 8 ? k0 : S - 8;  // a chunk starting at or past S is fully masked
+                __builtin_amdgcn_global_load_lds((gvoid*)(vb_base + (long long)d * S + k0),
+                                                 (lvoid*)(vl + j * 1024), 16, 0, 0);
+            }
         }
-    }
+    };
+    const bool first_live = kbeg_of(0) <= pos;
+    if (first_live) issue(kbeg_of(0));
 
     // ---- 1. QKV finish for row b: slot j = wave + NW i (0..15 query heads, padding past
     //         H; 16 the key head; 17 the value head).  All loads first, then arithmetic.
@@ -355,152 +380,191 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_split_kernel(DecAt
             kb_base[(long long)pos * HD + e] = kv_new[0][e];
             vb_base[(long long)e * S + pos] = kv_new[1][e];
         }
-
-    // ---- 2. operands
     CT qf[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[s] = *(const CT*)(&qs[col][32 * s + 8 * g]);
-    CT kf[4][DS];
-    // V^T operands: slot 8g+i of 32-key step u <-> key 32u + 4g + i (i < 4) or
-    // 32u + 16 + 4g + (i - 4) (i >= 4).
-    HT vlo[2][DT], vhi[2][DT];
-    if constexpr (STAGE) {
-        constexpr int KCH = HD / 8;
-        NC_WAIT_VM_ALL();  // this wave's staging loads have landed
+
+    // ---- 2. the wave's blocks, online softmax over them.  State per lane: head `col`;
+    //         o_run[dt][j] holds O^T[d = 16 dt + 4 g + j][col].
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 o_run[DT];
+#pragma unroll
+    for (int i = 0; i < DT; ++i) o_run[i] = zero_vec<f32x4>();
+    for (int it = 0; it < R; ++it) {
+        const int kbeg = kbeg_of(it);
+        if (kbeg > pos) break;  // wave-uniform: this and later blocks hold no visible key
+        CT kf[4][DS];
+        // V^T operands: slot 8g+i of 32-key step u <-> key 32u + 4g + i (i < 4) or
+        // 32u + 16 + 4g + (i - 4) (i >= 4).
+        HT vlo[2][DT], vhi[2][DT];
+        if constexpr (STAGE) {
+            constexpr int KCH = HD / 8;
+            NC_WAIT_VM_ALL();  // this wave's staging loads of the block have landed
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                const int kidx = 16 * kt + col;
+#pragma unroll
+                for (int s = 0; s < DS; ++s)
+                    kf[kt][s] = *(const CT*)(kl + kidx * (HD * 2) + (((4 * s + g) ^ (kidx % KCH)) * 16));
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int d = dt * 16 + col;
+                    const int k1 = 32 * u + 4 * g, k2 = k1 + 16;  // first keys (local) of the halves
+                    vlo[u][dt] = *(const HT*)(vl + d * 128 + (((k1 / 8) ^ (d % 8)) * 16) + (k1 % 8) * 2);
+                    vhi[u][dt] = *(const HT*)(vl + d * 128 + (((k2 / 8) ^ (d % 8)) * 16) + (k2 % 8) * 2);
+                }
+            // the operand reads are complete before the region is refilled
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            __builtin_amdgcn_sched_barrier(0);
+            if (it + 1 < R && kbeg_of(it + 1) <= pos) issue(kbeg_of(it + 1));
+        } else {
+            const int klast = pos > 0 ? pos - 1 : 0;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                int key = kbeg + 16 * kt + col;
+                key = key < pos ? key : klast;
+#pragma unroll
+                for (int s = 0; s < DS; ++s) kf[kt][s] = *(const CT*)(kb_base + (long long)key * HD + 32 * s + 8 * g);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                int ka = kbeg + 32 * u + 4 * g, kb2 = ka + 16;
+                ka = ka <= S - 4 ? ka : S - 4;
+                kb2 = kb2 <= S - 4 ? kb2 : S - 4;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const T* src = vb_base + (long long)(dt * 16 + col) * S;
+                    vlo[u][dt] = *(const HT*)(src + ka);
+                    vhi[u][dt] = *(const HT*)(src + kb2);
+                }
+            }
+        }
+
+        // scores S^T (lane: head `col`, keys kbeg + 16kt + 4g + j), cached keys < pos
+        f32x4 sacc[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-            const int kidx = 16 * kt + col;
+            sacc[kt] = zero_vec<f32x4>();
 #pragma unroll
-            for (int s = 0; s < DS; ++s)
-                kf[kt][s] = *(const CT*)(kl + kidx * (HD * 2) + (((4 * s + g) ^ (kidx % KCH)) * 16));
+            for (int s = 0; s < DS; ++s) sacc[kt] = mma16(kf[kt][s], qf[s], sacc[kt]);
         }
+        float mb = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int d = dt * 16 + col;
-                const int k1 = 32 * u + 4 * g, k2 = k1 + 16;  // first keys (local) of the halves
-                vlo[u][dt] = *(const HT*)(vl + d * 128 + (((k1 / 8) ^ (d % 8)) * 16) + (k1 % 8) * 2);
-                vhi[u][dt] = *(const HT*)(vl + d * 128 + (((k2 / 8) ^ (d % 8)) * 16) + (k2 % 8) * 2);
+            for (int j = 0; j < 4; ++j) {
+                const int key = kbeg + 16 * kt + 4 * g + j;
+                const float v = (key < pos) ? sacc[kt][j] * a.scale_log2 : -INFINITY;
+                sacc[kt][j] = v;
+                mb = fmaxf(mb, v);
             }
-    } else {
-        const int klast = pos > 0 ? pos - 1 : 0;
+        mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+        const float mn = fmaxf(m_run, mb);
+        const float mref = (mn == -INFINITY) ? 0.f : mn;  // nothing visible yet: no mass
+        const float al = fast_exp2(m_run - mref);           // 0 while the state is empty
+        float ls = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            int key = kbeg + 16 * kt + col;
-            key = key < pos ? key : klast;
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int s = 0; s < DS; ++s) kf[kt][s] = *(const CT*)(kb_base + (long long)key * HD + 32 * s + 8 * g);
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            int ka = kbeg + 32 * u + 4 * g, kb2 = ka + 16;
-            ka = ka <= S - 4 ? ka : S - 4;
-            kb2 = kb2 <= S - 4 ? kb2 : S - 4;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const T* src = vb_base + (long long)(dt * 16 + col) * S;
-                vlo[u][dt] = *(const HT*)(src + ka);
-                vhi[u][dt] = *(const HT*)(src + kb2);
+            for (int j = 0; j < 4; ++j) {
+                const float pv = fast_exp2(sacc[kt][j] - mref);
+                sacc[kt][j] = pv;
+                ls += pv;
             }
-        }
-    }
-
-    // ---- scores S^T (lane: head `col`, keys kbeg + 16kt + 4g + j), cached keys < pos
-    f32x4 sacc[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-        sacc[kt] = zero_vec<f32x4>();
-#pragma unroll
-        for (int s = 0; s < DS; ++s) sacc[kt] = mma16(kf[kt][s], qf[s], sacc[kt]);
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int key = kbeg + 16 * kt + 4 * g + j;
-            const float v = (key < pos) ? sacc[kt][j] * a.scale_log2 : -INFINITY;
-            sacc[kt][j] = v;
-            mx = fmaxf(mx, v);
-        }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mref = (mx == -INFINITY) ? 0.f : mx;  // no visible cached key: no mass
-    float ls = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float pv = fast_exp2(sacc[kt][j] - mref);
-            sacc[kt][j] = pv;
-            ls += pv;
-        }
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-
-    // ---- O^T[d][head] over the wave's 64 keys (two 32-deep steps)
-    f32x4 oacc[DT];
-#pragma unroll
-    for (int i = 0; i < DT; ++i) oacc[i] = zero_vec<f32x4>();
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        CT pf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pf[i] = from_f32<T>(sacc[2 * u][i]);
-            pf[4 + i] = from_f32<T>(sacc[2 * u + 1][i]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            CT vf;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                vf[i] = vlo[u][dt][i];
-                vf[4 + i] = vhi[u][dt][i];
-            }
-            oacc[dt] = mma16(vf, pf, oacc[dt]);
-        }
-    }
-
-    // ---- the new key (position pos) joins the wave whose range holds it
-    if (pos >= kbeg && pos < kbeg + DEC_KPW) {
-        // score of head `col`: lane group g sums 32 of the hd features
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < HD / 4; ++e)
-            part += to_f32(qs[col][g * (HD / 4) + e]) * to_f32(kv_new[0][g * (HD / 4) + e]);
-        part += __shfl_xor(part, 16, 64);
-        part += __shfl_xor(part, 32, 64);
-        const float sp = part * a.scale_log2;
-        const float mn = fmaxf(mx, sp);
-        const float al = fast_exp2(mx - mn);  // 0 when no cached key was visible
-        const float be = fast_exp2(sp - mn);
-        ls = ls * al + be;
+        ls += __shfl_xor(ls, 16, 64);
+        ls += __shfl_xor(ls, 32, 64);
+        l_run = l_run * al + ls;
+        m_run = mn;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                oacc[dt][j] = oacc[dt][j] * al + be * to_f32(kv_new[1][dt * 16 + 4 * g + j]);
-        mx = mn;
+            for (int j = 0; j < 4; ++j) o_run[dt][j] *= al;
+        // O^T[d][head] += V^T P over the block's 64 keys (two 32-deep steps)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            CT pf;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pf[i] = from_f32<T>(sacc[2 * u][i]);
+                pf[4 + i] = from_f32<T>(sacc[2 * u + 1][i]);
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                CT vf;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    vf[i] = vlo[u][dt][i];
+                    vf[4 + i] = vhi[u][dt][i];
+                }
+                o_run[dt] = mma16(vf, pf, o_run[dt]);
+            }
+        }
+        // the new key (position pos) joins the wave whose block holds it
+        if (pos >= kbeg && pos < kbeg + DEC_KPW) {
+            // score of head `col`: lane group g sums a quarter of the hd features
+            float part = 0.f;
+#pragma unroll
+            for (int e = 0; e < HD / 4; ++e)
+                part += to_f32(qs[col][g * (HD / 4) + e]) * to_f32(kv_new[0][g * (HD / 4) + e]);
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            const float sp = part * a.scale_log2;
+            const float mn2 = fmaxf(m_run, sp);
+            const float al2 = fast_exp2(m_run - mn2);  // 0 when no cached key was visible
+            const float be = fast_exp2(sp - mn2);
+            l_run = l_run * al2 + be;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o_run[dt][j] = o_run[dt][j] * al2 + be * to_f32(kv_new[1][dt * 16 + 4 * g + j]);
+            m_run = mn2;
+        }
     }
 
-    // ---- this wave's partial: slot 2c + wave
-    float* pb = a.part + ((long long)b * a.max_slots + (c * NW + wave)) * PSZ;
+    // ---- 3. merge the 4 waves' states into the chunk's partial (slot c of row b)
+    if constexpr (STAGE) NC_WAIT_VM_ALL();  // no staging load still in flight into the region
+    __syncthreads();                        // every wave is done with its region
+    float* st = (float*)(buf + wave * WREG);
     if (g == 0) {
-        pb[col] = mx;
-        pb[16 + col] = ls;
+        st[col] = m_run;
+        st[16 + col] = l_run;
     }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        f32x4 o;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = oacc[dt][j];
-        *(f32x4*)(pb + 32 + col * HD + dt * 16 + 4 * g) = o;
+        for (int j = 0; j < 4; ++j) st[32 + col * HD + dt * 16 + 4 * g + j] = o_run[dt][j];
+    __syncthreads();
+    float* pb = a.part + ((long long)b * a.max_slots + c) * PSZ;
+    for (int e = tid; e < 16 * HD; e += NW * 64) {
+        const int h = e / HD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, ((const float*)(buf + w * WREG))[h]);
+        const float mref = (M == -INFINITY) ? 0.f : M;
+        float o = 0.f, l = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float* sw = (const float*)(buf + w * WREG);
+            const float f = fast_exp2(sw[h] - mref);
+            o += f * sw[32 + e];
+            l += f * sw[16 + h];
+        }
+        pb[32 + e] = o;
+        if (e % HD == 0) {
+            pb[h] = M;
+            pb[16 + h] = l;
+        }
     }
 }
 
-// Combine kernel: workgroup (head h, row b), one thread per feature d:
+// Combine kernel: workgroup (head h, row b), one thread per feature d, over the row's
+// chunks (slots) of `chunk` keys:
 // y[b][h][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s over the row's slots.  The
 // slot statistics are loaded lane-parallel (one slot per lane), the weights go through
 // LDS, and the o_s[d] loads of consecutive slots are independent of each other.
@@ -508,13 +572,13 @@ template <typename T, int HD>
 __global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __restrict__ part,
                                                                  const int32_t* __restrict__ lens,
                                                                  T* __restrict__ y, int H, int S,
-                                                                 int max_slots) {
+                                                                 int max_slots, int chunk) {
     constexpr int PSZ = 16 * (HD + 2);
     __shared__ float wts[512];
     __shared__ float stat[1];
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const int pos = min(lens[b], S - 1);
-    const int nsl = min((pos + 1 + DEC_CHUNK - 1) / DEC_CHUNK * DEC_WAVES, 512);
+    const int nsl = min((pos + 1 + chunk - 1) / chunk, 512);
     const float* prow = part + (long long)b * max_slots * PSZ;
     if (d < 64) {  // wave 0: max, weights and normaliser
         float mloc = -INFINITY;
@@ -545,12 +609,17 @@ __global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __
 hipError_t launch_attn_decode(DType dt, const DecAttnArgs& args, void* y, hipStream_t st) {
     DecAttnArgs a = args;
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)a.hd);
-    dim3 g1((a.max_slots + DEC_WAVES - 1) / DEC_WAVES, a.B), g2(a.H, a.B);
+    dim3 g1(a.max_slots, a.B), g2(a.H, a.B);
+    const int nw = attn_decode_waves(a.B, a.S);
+    if (a.iters != attn_decode_iters(a.B, a.S) || a.max_slots != attn_decode_slots(a.B, a.S))
+        return hipErrorInvalidValue;
+    const int chunk = nw * DEC_KPW * a.iters;
 #define NC_AD(TT, HDV)                                                                         \
     do {                                                                                       \
-        NC_TLAUNCH((attn_decode_split_kernel<TT, HDV>), g1, dim3(DEC_WAVES * 64), 0, st, a);   \
+        if (nw == 4) NC_TLAUNCH((attn_decode_split_kernel<TT, HDV, 4>), g1, dim3(256), 0, st, a); \
+        else NC_TLAUNCH((attn_decode_split_kernel<TT, HDV, 2>), g1, dim3(128), 0, st, a);     \
         NC_TLAUNCH((attn_decode_combine_kernel<TT, HDV>), g2, dim3(HDV), 0, st,                \
-                   (const float*)a.part, a.lens, (TT*)y, a.H, a.S, a.max_slots);              \
+                   (const float*)a.part, a.lens, (TT*)y, a.H, a.S, a.max_slots, chunk);       \
     } while (0)
     if (dt == BF16 && a.hd == 128) NC_AD(bf16, 128);
     else if (dt == BF16 && a.hd == 64) NC_AD(bf16, 64);

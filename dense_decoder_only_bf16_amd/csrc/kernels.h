@@ -140,11 +140,13 @@ struct DecAttnArgs {
     const int32_t* lens;
     void* kc; void* vtc;  // this layer's cache: K [B][S][hd], V^T [B][hd][S]
     float* part;          // [B][max_slots][16 (hd + 2)]
-    int B, H, hd, S, max_slots;  // max_slots = attn_decode_slots(S)
+    int B, H, hd, S;
+    int iters;            // 64-key blocks per wave: attn_decode_iters(B, S)
+    int max_slots;        // attn_decode_slots(B, S)
     float scale_log2;     // set by the launcher
 };
-int attn_decode_chunk();
-int attn_decode_slots(int S);  // partial slots per row for a cache of S positions
+int attn_decode_iters(int B, int S);  // chunk of a workgroup = 256 x iters keys
+int attn_decode_slots(int B, int S);  // partial slots (chunks) per row, cache of S positions
 hipError_t launch_attn_decode(DType dt, const DecAttnArgs& a, void* y, hipStream_t st);
 
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st);

@@ -184,7 +184,7 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
         WS_ALLOC(kv->act_lo, Mr * d * es);
         WS_ALLOC(kv->u_lo, Mr * c.d_ff * es);
     }
-    kv->apart_elems = (long long)kv->B * attn_decode_slots(kv->S) * 16 * (c.head_dim + 2);
+    kv->apart_elems = (long long)kv->B * attn_decode_slots(kv->B, kv->S) * 16 * (c.head_dim + 2);
     WS_ALLOC(kv->apart, kv->apart_elems * 4);
     {   // split-K partials of the decode projections (M = batch rows)
         const int B = kv->B, d = c.d_model, F = c.d_ff, hqv = c.n_head * c.head_dim;
@@ -311,7 +311,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
     const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab;
     const int nqkv = (H + 2) * hd;
     const size_t per_layer = (size_t)B * kv->S * hd * m->esz;
-    const int max_slots = attn_decode_slots(kv->S);
+    const int max_slots = attn_decode_slots(B, kv->S);
     const int parts_d = (d + dec_gemm_tile_n() - 1) / dec_gemm_tile_n();
     const int ss = (int)kv->cap_m;
     nc_status s;
@@ -334,6 +334,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         at.norm_dim = d; at.eps = c.norm_eps; at.rope_cos = m->rope_cos; at.rope_sin = m->rope_sin;
         at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = kv->apart;
         at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.max_slots = max_slots;
+        at.iters = attn_decode_iters(B, kv->S);
         {   // bytes: the K/V read for every row (positions 0..lens_b, the new one
             // included), q/k/v in fp32, y out; flops 4 hd per (query head, key) pair
             const double es = (double)m->esz;
