@@ -79,13 +79,15 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
     constexpr int VCH = HD * (KB / 8) / 256;
     static_assert(KCH >= 1 && VCH >= 1, "block too small for 256 threads");
 
-    for (int kbi = 0; kbi < nkb; ++kbi) {
-        const int k0 = kbi * KB;
-        CT rk[KCH], rv[VCH];
+    // K/V block k0 into registers (zeros past Tn); the next block's loads are issued right
+    // after the current block is in LDS, so they are in flight during its arithmetic.
+    CT rk[KCH], rv[VCH];
+    auto gload = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
             int c = tid + i * 256, key = c / CPRK, ch = c % CPRK;
-            rk[i] = (k0 + key < Tn) ? *(const CT*)(kb_base + (long long)(k0 + key) * HD + ch * 8) : zero_vec<CT>();
+            const int kk = min(k0 + key, Tn - 1);
+            rk[i] = load_masked(kb_base + (long long)kk * HD + ch * 8, k0 + key < Tn);
         }
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
@@ -101,6 +103,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
                 rv[i] = t;
             }
         }
+    };
+    gload(0);
+    for (int kbi = 0; kbi < nkb; ++kbi) {
+        const int k0 = kbi * KB;
         __syncthreads();  // previous block's LDS reads are complete
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
@@ -113,6 +119,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
             *(CT*)(&Vs[d * KB + ((ch ^ (d & 7)) * 8)]) = rv[i];
         }
         __syncthreads();
+        if (kbi + 1 < nkb) gload(k0 + KB);
 
         if (k0 > q0w + 63) continue;  // every query of this wave precedes the block
 
