@@ -79,8 +79,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
     constexpr int VCH = HD * (KB / 8) / 256;
     static_assert(KCH >= 1 && VCH >= 1, "block too small for 256 threads");
 
-    // K/V block k0 into registers (zeros past Tn); the next block's loads are issued right
-    // after the current block is in LDS, so they are in flight during its arithmetic.
+    // K/V block k0 into registers (zeros past Tn), then into LDS.
     CT rk[KCH], rv[VCH];
     auto gload = [&](int k0) {
 #pragma unroll
@@ -104,9 +103,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
             }
         }
     };
-    gload(0);
     for (int kbi = 0; kbi < nkb; ++kbi) {
         const int k0 = kbi * KB;
+        gload(k0);
         __syncthreads();  // previous block's LDS reads are complete
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
@@ -119,7 +118,6 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
             *(CT*)(&Vs[d * KB + ((ch ^ (d & 7)) * 8)]) = rv[i];
         }
         __syncthreads();
-        if (kbi + 1 < nkb) gload(k0 + KB);
 
         if (k0 > q0w + 63) continue;  // every query of this wave precedes the block
 
@@ -137,31 +135,41 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
             }
         }
 
-        // Online softmax (base 2).  Row index of register r in a 32x32 output tile:
-        // 8*(r/4) + 4*hh + (r%4).
+        // Online softmax in base 2 on unscaled scores: the running max m is kept unscaled and
+        // p = 2^(c s - c m) with c = log2(e)/sqrt(hd), one FMA per score.  Only a block that
+        // reaches past a query of this wave (the diagonal) or past Tn needs the mask.  Row
+        // index of register r in a 32x32 output tile: 8*(r/4) + 4*hh + (r%4).
+        const bool need_mask = (k0 + KB - 1 > q0w) || (k0 + KB > Tn);  // wave-uniform
 #pragma unroll
         for (int jn = 0; jn < 2; ++jn) {
             const int qi = q0w + jn * 32 + l32;
             float mx = -INFINITY;
+            if (need_mask) {
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+                for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + mt * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
-                    float v = sacc[mt][jn][r] * scale_log2;
-                    v = (key <= qi && key < Tn) ? v : -INFINITY;
-                    sacc[mt][jn][r] = v;
-                    mx = fmaxf(mx, v);
-                }
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + mt * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
+                        const float v = (key <= qi && key < Tn) ? sacc[mt][jn][r] : -INFINITY;
+                        sacc[mt][jn][r] = v;
+                        mx = fmaxf(mx, v);
+                    }
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][jn][r]);
+            }
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
             const float m_new = fmaxf(m_run[jn], mx);
-            const float alpha = fast_exp2(m_run[jn] - m_new);
+            const float cm = scale_log2 * m_new;
+            const float alpha = fast_exp2(scale_log2 * m_run[jn] - cm);  // 0 on the first block
             float ls = 0.f;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float pv = fast_exp2(sacc[mt][jn][r] - m_new);
+                    const float pv = fast_exp2(fmaf(sacc[mt][jn][r], scale_log2, -cm));
                     sacc[mt][jn][r] = pv;
                     ls += pv;
                 }
