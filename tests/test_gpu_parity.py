@@ -267,3 +267,40 @@ def test_kernel_timing_counts_launches(small):
     assert np.max(np.abs(out.cpu().numpy() - want)) <= BF16_TOL  # timed graph still correct
     nc.nc_timing_enable(nc.NC_KC_NONE)
     kv.close()
+
+
+# head_dim 64 in bf16 (the other bf16 models use 128), vocab not a multiple of 32
+SMALL_HD64 = Shape("small-hd64", n_layer=2, d_model=256, n_head=4, head_dim=64, d_ff=1024,
+                   vocab=777, dtype="bf16", max_seq=200)
+# the most query heads the decode kernel takes (16: no padded head slots)
+WIDE_H16 = Shape("h16", n_layer=1, d_model=2048, n_head=16, head_dim=128, d_ff=2048,
+                 vocab=512, dtype="bf16", max_seq=96)
+
+
+@pytest.mark.parametrize("shape", [SMALL_HD64, WIDE_H16], ids=lambda s: s.name)
+def test_bf16_other_head_shapes(shape):
+    """Prefill of ragged rows, then decode from rows truncated to 0 (empty context: the new
+    key is the only one), 1 and a middle length, compared with the oracle everywhere."""
+    w = make_weights(shape, seed=8)
+    orc = OracleModel(shape, w)
+    gm = gpu_model(shape, w)
+    T = 70
+    toks = make_tokens(shape.vocab, 3, T + 4, seed=9)
+    want, _ = orc.prefill(toks[:, :T])
+    kv, got = prefill(gm, toks[:, :T], shape.max_seq)
+    err, agr = report(f"{shape.name} prefill", got, want)
+    assert err <= BF16_TOL and agr >= AGREE
+    lens = np.array([0, 1, 41], dtype=np.int32)
+    kv.set_lens(lens)
+    got = np.stack([decode(gm, kv, toks[:, T + s]) for s in range(4)], axis=1)
+    for b in range(3):
+        seq = np.concatenate([toks[b, :lens[b]], toks[b, T:T + 4]])[None]
+        ref, _ = orc.prefill(seq, logits_at=np.arange(lens[b], lens[b] + 4))
+        err, agr = report(f"{shape.name} decode row {b} from length {lens[b]}", got[b], ref[0])
+        assert err <= BF16_TOL
+        srt = np.sort(ref[0], -1)  # any argmax disagreement must be a near tie
+        flip = np.argmax(got[b], -1) != np.argmax(ref[0], -1)
+        assert not np.any(flip & (srt[:, -1] - srt[:, -2] >= 2 * err))
+    assert np.array_equal(kv.lens(), lens + 4)
+    kv.close()
+    gm.close()
