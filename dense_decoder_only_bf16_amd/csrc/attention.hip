@@ -248,7 +248,8 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 // of row b, CK = 64 NW R, limited to positions 0..lens[b].  Wave w takes the 64-key blocks
 // (c R + i) NW + w, i < R, one after another and keeps an online-softmax state (running
 // max, sum and o[16][hd]) across them; at the end the NW states are merged in LDS into the
-// chunk's partial state, slot c of row b.
+// chunk's partial state, slot c of row b (with R = 1 each wave's state is a partial of its
+// own, slot NW c + w, and the merge is left to the combine kernel).
 //  1. Finish the QKV product of row b for this step (the row's attention-norm scale,
 //     RoPE at position lens[b] and QK-norm of the query heads and the key head; the value
 //     head as is) into LDS.  Every workgroup of the row does this (a few hundred values);
@@ -278,8 +279,9 @@ int attn_decode_iters(int B, int S) {
     return r;
 }
 int attn_decode_slots(int B, int S) {
-    const int ck = attn_decode_waves(B, S) * DEC_KPW * attn_decode_iters(B, S);
-    return (S + ck - 1) / ck;
+    const int nw = attn_decode_waves(B, S), r = attn_decode_iters(B, S);
+    const int ck = nw * DEC_KPW * r;
+    return (S + ck - 1) / ck * (r == 1 ? nw : 1);  // one block per wave: a slot per wave
 }
 
 template <typename T, int HD, int NW>
@@ -542,7 +544,19 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
         }
     }
 
-    // ---- 3. merge the 4 waves' states into the chunk's partial (slot c of row b)
+    // ---- 3a. one block per wave (R == 1): each wave's state is its own partial, slot
+    //          NW c + w of row b; the combine kernel merges them with the other chunks'.
+    if (R == 1) {
+        float* pw = a.part + ((long long)b * a.max_slots + NW * c + wave) * PSZ;
+        if (g == 0) {
+            pw[col] = m_run;
+            pw[16 + col] = l_run;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(pw + 32 + col * HD + dt * 16 + 4 * g) = o_run[dt];
+        return;
+    }
+    // ---- 3b. merge the waves' states into the chunk's partial (slot c of row b)
     if constexpr (STAGE) NC_WAIT_VM_ALL();  // no staging load still in flight into the region
     __syncthreads();                        // every wave is done with its region
     float* st = (float*)(buf + wave * WREG);
@@ -624,11 +638,12 @@ __global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __
 hipError_t launch_attn_decode(DType dt, const DecAttnArgs& args, void* y, hipStream_t st) {
     DecAttnArgs a = args;
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)a.hd);
-    dim3 g1(a.max_slots, a.B), g2(a.H, a.B);
+    dim3 g1(a.iters == 1 ? a.max_slots / attn_decode_waves(a.B, a.S) : a.max_slots, a.B), g2(a.H, a.B);
     const int nw = attn_decode_waves(a.B, a.S);
     if (a.iters != attn_decode_iters(a.B, a.S) || a.max_slots != attn_decode_slots(a.B, a.S))
         return hipErrorInvalidValue;
-    const int chunk = nw * DEC_KPW * a.iters;
+    // the combine sees slots of `chunk` keys: a wave's block when R == 1, else a chunk
+    const int chunk = a.iters == 1 ? DEC_KPW : nw * DEC_KPW * a.iters;
 #define NC_AD(TT, HDV)                                                                         \
     do {                                                                                       \
         if (nw == 4) NC_TLAUNCH((attn_decode_split_kernel<TT, HDV, 4>), g1, dim3(256), 0, st, a); \

@@ -170,12 +170,12 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
     if (vec) {
         const f32x4* r4 = (const f32x4*)row;
         const int n4 = V >> 2;
-        for (int i0 = tid; i0 < n4; i0 += 8 * 1024) {  // 8 independent loads per batch
-            f32x4 v[8];
+        for (int i0 = tid; i0 < n4; i0 += 16 * 1024) {  // 16 independent loads per batch
+            f32x4 v[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = r4[min(i0 + 1024 * u, n4 - 1)];
+            for (int u = 0; u < 16; ++u) v[u] = r4[min(i0 + 1024 * u, n4 - 1)];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 16; ++u) {
                 const int i = i0 + 1024 * u;
                 if (i < n4) {
 #pragma unroll
