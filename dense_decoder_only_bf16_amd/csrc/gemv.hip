@@ -194,6 +194,9 @@ static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant) {
     const unsigned gy = (a.M + 32 * fm - 1) / (32 * fm);
     dim3 g(gx, gy);
 #define NC_DG(FMV, NWV, UV) NC_TLAUNCH((dec_gemm_kernel<T, FMV, NWV, UV, EPI, LO>), g, dim3(NWV * 64), 0, st, a)
+    // one row block and at most 8 steps per wave (K <= 1024): all of a wave's weight
+    // steps in flight at once (one memory round trip), except for the wide LM head
+    if (fm == 1 && variant == 0 && a.K <= 1024 && a.N <= 16384) variant = 2;
     if (fm == 1) {
         if (variant == 1) NC_DG(1, 16, 4);
         else if (variant == 2) NC_DG(1, 8, 8);
