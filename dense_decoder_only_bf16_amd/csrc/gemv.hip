@@ -197,6 +197,9 @@ static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant) {
     // one row block and at most 8 steps per wave (K <= 1024): all of a wave's weight
     // steps in flight at once (one memory round trip), except for the wide LM head
     if (fm == 1 && variant == 0 && a.K <= 1024 && a.N <= 16384) variant = 2;
+    // one row block, long K and few column blocks (the MLP down-projection): 16 waves
+    // split K, halving each wave's chain of loads
+    if (fm == 1 && variant == 0 && a.K > 1024 && a.N <= 2048) variant = 1;
     if (fm == 1) {
         if (variant == 1) NC_DG(1, 16, 4);
         else if (variant == 2) NC_DG(1, 8, 8);
