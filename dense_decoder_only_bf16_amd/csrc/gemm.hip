@@ -24,8 +24,8 @@
 //
 // Two main loops:
 //  * bf16 (the model's dtype): global -> LDS with the gfx950 direct-to-LDS load
-//    (global_load_lds_dwordx4), a ring of 4 LDS stages of 32 K-columns, loads issued three
-//    stages ahead; no staging registers and no LDS store instructions.  The operand
+//    (global_load_lds_dwordx4), a ring of 5 LDS stages of 32 K-columns (all 160 KB), loads
+//    issued four stages ahead; no staging registers and no LDS store instructions.  The operand
 //    fragments of the next 16-deep step (also across a K-tile boundary) are read from LDS
 //    while the MFMAs of the current step run (fragments double-buffered in registers,
 //    reads interleaved one per MFMA).
@@ -143,11 +143,13 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[2
 template <int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_kernel(GemmArgs p) {
-    constexpr int BK = 32, KB = BK / 16, NS = 4;
+    constexpr int BK = 32, KB = BK / 16, NS = 5;
     constexpr int STAGE = (TBM + TBN) * BK;       // elements per stage (A then B)
+    // The ring takes all 160 KB of LDS; after the main loop it holds the row scales and the
+    // RESID row sums instead.
     __shared__ __attribute__((aligned(1024))) bf16 lds[NS * STAGE];
-    __shared__ float rs[TBM];
-    __shared__ float red[4][TBM];
+    float* rs = (float*)lds;
+    float (*red)[TBM] = (float (*)[TBM])((float*)lds + TBM);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -164,7 +166,18 @@ void gemm_bf16_kernel(GemmArgs p) {
     const bf16* A_lo = (const bf16*)p.A_lo;
     const bf16* B = (const bf16*)p.B;
 
-    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) tile_row_scales(p, m0, rs, 512);
+    // RELU2 / SOFTCAP: the partial sums of squares of row m0 + (tid % 256) are loaded now and
+    // reduced to the row scale after the main loop, so their latency overlaps it.
+    constexpr int MAXP = 16;  // partial sums per row: one per 256 columns of d <= 4096
+    float ssp[MAXP];
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) ssp[q] = 0.f;
+    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
+        const int m = min(m0 + (tid & (TBM - 1)), p.M - 1);
+#pragma unroll
+        for (int q = 0; q < MAXP; ++q)
+            if (q < p.ss_in_parts) ssp[q] = p.ss_in[(long long)q * p.ss_stride + m];
+    }
 
     // Stage layout: 16 A blocks (row block rb = b/2, k block b%2) then 16 B blocks.  Wave w
     // loads A blocks 2w, 2w+1 and B blocks 2w, 2w+1; lane l fills bytes [16 l, 16 l + 16)
@@ -235,7 +248,8 @@ void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
     for (int kt = 0; kt < NS - 1; ++kt)
         if (kt < nk) issue(kt);
-    if (nk > 2) NC_WAIT_VM(8);
+    if (nk > 3) NC_WAIT_VM(12);
+    else if (nk > 2) NC_WAIT_VM(8);
     else if (nk > 1) NC_WAIT_VM(4);
     else NC_WAIT_VM(0);
     __builtin_amdgcn_s_barrier();
@@ -246,12 +260,13 @@ void gemm_bf16_kernel(GemmArgs p) {
         // step 0 of tile kt; read step 1 of tile kt meanwhile
         fload(kt, 1, a1, b1);
         mfmas(a0, b0, true);
-        // Tile kt+1: own loads done (tile kt+2 may still be in flight), then a barrier:
-        // every wave's loads of kt+1 are in LDS and every wave is done with tile kt-1,
-        // whose stage the next issue overwrites.
+        // Tile kt+1: own loads done (tiles kt+2, kt+3 may still be in flight), then a
+        // barrier: every wave's loads of kt+1 are in LDS and every wave is done with tile
+        // kt-1, whose stage the next issue overwrites.
         const bool more = kt + 1 < nk;
         if (more) {
-            if (kt + 2 < nk) NC_WAIT_VM(4);
+            if (kt + 3 < nk) NC_WAIT_VM(8);
+            else if (kt + 2 < nk) NC_WAIT_VM(4);
             else NC_WAIT_VM(0);
             __builtin_amdgcn_s_barrier();
             if (kt + NS - 1 < nk) issue(kt + NS - 1);
@@ -259,7 +274,16 @@ void gemm_bf16_kernel(GemmArgs p) {
         }
         mfmas(a1, b1, more);
     }
-    __syncthreads();
+    __syncthreads();  // every wave is done with the ring (all its loads have landed)
+    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
+        if (tid < TBM) {
+            float s = 0.f;
+#pragma unroll
+            for (int q = 0; q < MAXP; ++q) s += ssp[q];
+            rs[tid] = 1.0f / sqrtf(s / (float)p.K + p.eps);
+        }
+        __syncthreads();
+    }
     tile_epilogue<bf16, EPI, 2, 4>(p, acc, m0, n0, tn, rs, red);
 }
 
