@@ -20,7 +20,10 @@
  * norm(z) = z / sqrt(mean(z^2) + eps) has no parameters.  RoPE rotates the pair
  * (i, i + hd/2) by pos * base^(-2i/hd).  Linear layers have no bias; weights are stored
  * [out, in] as in torch.nn.Linear.  Matrix products take dtype operands (bf16 or fp32)
- * with fp32 accumulation; the residual stream, norms, softmax and logits are fp32.
+ * with fp32 accumulation; the residual stream, norms, softmax and logits are fp32.  With
+ * bf16, the inputs of the MLP products and of the LM head are carried as two bf16 parts
+ * (a = hi + lo) and multiplied part by part, so their operand rounding error is about
+ * 2^-17 instead of 2^-9; the KV cache and the other operands are bf16.
  *
  * Conventions for every call:
  *  - Every pointer named *_dev is device memory on the current HIP device; pointers named
