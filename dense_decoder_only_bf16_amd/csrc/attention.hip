@@ -32,7 +32,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
                                                            const T* __restrict__ kc,
                                                            const T* __restrict__ vtc,
                                                            T* __restrict__ y, int Tn, int H,
-                                                           int S, float scale_log2) {
+                                                           int nkv, int S, float scale_log2) {
     typedef typename Chunk<T>::type CT;
     typedef typename Chunk<T>::half HT;
     constexpr int BQ = 256, KB = 64, NT = 64 * 8 / JN;
@@ -50,8 +50,9 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
     const int q0 = qb * BQ;
     const int q0w = q0 + wave * 32 * JN;
 
-    const T* kb_base = kc + (long long)b * S * HD;
-    const T* vb_base = vtc + (long long)b * HD * S;
+    const int kvh = head / (H / nkv);  // the K/V head this query head reads
+    const T* kb_base = kc + ((long long)b * nkv + kvh) * S * HD;
+    const T* vb_base = vtc + ((long long)b * nkv + kvh) * HD * S;
 
     // Query operands: B operand of S^T, lane holds query (q0w + jn*32 + l32), dims 16s+8hh..
     CT qf[JN][KSTEPS];
@@ -232,12 +233,13 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 }
 
 hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, const void* vtc,
-                               void* y, int B, int T, int H, int S, hipStream_t st) {
+                               void* y, int B, int T, int H, int nkv, int S, hipStream_t st) {
+    if (nkv < 1 || H % nkv) return hipErrorInvalidValue;
     dim3 grid((T + 255) / 256, H, B);
     const float sl = 1.4426950408889634f / sqrtf((float)hd);
 #define NC_AP(TT, HDV)                                                                          \
     NC_TLAUNCH((attn_prefill_kernel<TT, HDV, 1>), grid, dim3(512), 0, st, (const TT*)q,        \
-               (const TT*)kc, (const TT*)vtc, (TT*)y, T, H, S, sl)
+               (const TT*)kc, (const TT*)vtc, (TT*)y, T, H, nkv, S, sl)
     if (dt == BF16 && hd == 128) NC_AP(bf16, 128);
     else if (dt == BF16 && hd == 64) NC_AP(bf16, 64);
     else if (dt == F32 && hd == 128) NC_AP(float, 128);
@@ -248,15 +250,16 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 }
 
 // ------------------------------------------------------------------ decode ----------
-// Split kernel.  Workgroup (chunk c, row b), NW = 2 or 4 waves: the keys [c CK, c CK + CK)
-// of row b, CK = 64 NW R, limited to positions 0..lens[b].  Wave w takes the 64-key blocks
+// Split kernel.  Workgroup (chunk c, unit u = (row b, K/V head kvh)), NW = 2 or 4 waves: the
+// keys [c CK, c CK + CK) of K/V head kvh of row b, CK = 64 NW R, limited to positions
+// 0..lens[b], against the G = H / nkv query heads kvh G .. kvh G + G - 1 (G <= 16).  Wave w takes the 64-key blocks
 // (c R + i) NW + w, i < R, one after another and keeps an online-softmax state (running
 // max, sum and o[16][hd]) across them; at the end the NW states are merged in LDS into the
 // chunk's partial state, slot c of row b (with R = 1 each wave's state is a partial of its
 // own, slot NW c + w, and the merge is left to the combine kernel).
 //  1. Finish the QKV product of row b for this step (the row's attention-norm scale,
-//     RoPE at position lens[b] and QK-norm of the query heads and the key head; the value
-//     head as is) into LDS.  Every workgroup of the row does this (a few hundred values);
+//     RoPE at position lens[b] and QK-norm of the group's query heads and of key head kvh;
+//     value head kvh as is) into LDS.  Every workgroup of the row does this (a few hundred values);
 //     the one whose chunk holds position lens[b] also writes the new key and value into the
 //     cache for later steps.
 //  2. All query heads of the row (padded to 16) form the 16 columns of 16x16 MFMA tiles,
@@ -272,6 +275,7 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 constexpr int DEC_KPW = 64;
 // Waves per workgroup: 4, or 2 when the rows are few (more, smaller workgroups then).
 int attn_decode_waves(int B, int S) { return (long long)B * ((S + 255) / 256) >= 128 ? 4 : 2; }
+// (B here and below counts (row, K/V head) units.)
 int attn_decode_iters(int B, int S) {
     // The largest R in {1, 2, 4} that still leaves 128 workgroups or more: a wave's blocks
     // run one after another at about one memory latency each, so longer chunks amortize
@@ -309,15 +313,17 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g = lane >> 4;
-    const int c = blockIdx.x, b = blockIdx.y;
+    const int c = blockIdx.x, u = blockIdx.y;  // unit u = b nkv + kvh
+    const int b = u / a.nkv, kvh = u % a.nkv;
     const int S = a.S, H = a.H, R = a.iters;
+    const int G = H / a.nkv;
     const int CK = NW * DEC_KPW * R;
     const int pos = a.lens[b];  // this step's position; keys 0..pos are visible
     if (pos < 0 || pos >= S) return;  // capacity is checked by the host; stay in bounds
     const int nchunks = (pos + 1 + CK - 1) / CK;
     if (c >= nchunks) return;
-    T* kb_base = (T*)a.kc + (long long)b * S * HD;
-    T* vb_base = (T*)a.vtc + (long long)b * HD * S;
+    T* kb_base = (T*)a.kc + (long long)u * S * HD;
+    T* vb_base = (T*)a.vtc + (long long)u * HD * S;
     unsigned char* kl = buf + wave * WREG;  // K: 64 keys x HD, 16-byte chunks swizzled
     unsigned char* vl = kl + KREG;           // V^T: HD rows x 64 keys (128 bytes a row)
     // first key of this wave's i-th block; a block starting past pos holds no visible key
@@ -352,17 +358,18 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
     const bool first_live = kbeg_of(0) <= pos;
     if (first_live) issue(kbeg_of(0));
 
-    // ---- 1. QKV finish for row b: slot j = wave + NW i (0..15 query heads, padding past
-    //         H; 16 the key head; 17 the value head).  All loads first, then arithmetic.
+    // ---- 1. QKV finish for row b: slot j = wave + NW i (0..15 the group's query heads,
+    //         padding past G; 16 key head kvh; 17 value head kvh).  All loads first, then
+    //         arithmetic.
     {
-        const float* raw = a.qkv + (long long)b * (H + 2) * HD;
+        const float* raw = a.qkv + (long long)b * (H + 2 * a.nkv) * HD;
         const bool act = lane < HALF;
         const int i = act ? lane : 0;
         float v1[NSLOT], v2[NSLOT];
 #pragma unroll
         for (int t = 0; t < NSLOT; ++t) {
             const int j = wave + NW * t;
-            const int src = (j < H) ? j : (j == 16 ? H : (j == 17 ? H + 1 : 0));
+            const int src = (j < G) ? kvh * G + j : (j == 16 ? H + kvh : (j == 17 ? H + a.nkv + kvh : 0));
             v1[t] = raw[src * HD + i];
             v2[t] = raw[src * HD + i + HALF];
         }
@@ -372,7 +379,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
         for (int t = 0; t < NSLOT; ++t) {
             const int j = wave + NW * t;
             if (j >= 18) continue;
-            if (j < H || j == 16) {  // rotate + normalise
+            if (j < G || j == 16) {  // rotate + normalise
                 const float x1 = v1[t] * r, x2 = v2[t] * r;
                 const float o1 = x1 * cs - x2 * sn, o2 = x1 * sn + x2 * cs;
                 const float ss = wave_sum(act ? o1 * o1 + o2 * o2 : 0.f);
@@ -551,7 +558,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
     // ---- 3a. one block per wave (R == 1): each wave's state is its own partial, slot
     //          NW c + w of row b; the combine kernel merges them with the other chunks'.
     if (R == 1) {
-        float* pw = a.part + ((long long)b * a.max_slots + NW * c + wave) * PSZ;
+        float* pw = a.part + ((long long)u * a.max_slots + NW * c + wave) * PSZ;
         if (g == 0) {
             pw[col] = m_run;
             pw[16 + col] = l_run;
@@ -573,7 +580,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
 #pragma unroll
         for (int j = 0; j < 4; ++j) st[32 + col * HD + dt * 16 + 4 * g + j] = o_run[dt][j];
     __syncthreads();
-    float* pb = a.part + ((long long)b * a.max_slots + c) * PSZ;
+    float* pb = a.part + ((long long)u * a.max_slots + c) * PSZ;
     for (int e = tid; e < 16 * HD; e += NW * 64) {
         const int h = e / HD;
         float M = -INFINITY;
@@ -604,30 +611,31 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
 template <typename T, int HD>
 __global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __restrict__ part,
                                                                  const int32_t* __restrict__ lens,
-                                                                 T* __restrict__ y, int H, int S,
-                                                                 int max_slots, int chunk) {
+                                                                 T* __restrict__ y, int H, int nkv,
+                                                                 int S, int max_slots, int chunk) {
     constexpr int PSZ = 16 * (HD + 2);
     __shared__ float wts[512];
     __shared__ float stat[1];
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int G = H / nkv, hg = h % G;  // query head h is head hg of K/V head h / G's group
     const int pos = min(lens[b], S - 1);
     const int nsl = min((pos + 1 + chunk - 1) / chunk, 512);
-    const float* prow = part + (long long)b * max_slots * PSZ;
+    const float* prow = part + ((long long)b * nkv + h / G) * max_slots * PSZ;
     if (d < 64) {  // wave 0: max, weights and normaliser
         float mloc = -INFINITY;
-        for (int sl = d; sl < nsl; sl += 64) mloc = fmaxf(mloc, prow[(long long)sl * PSZ + h]);
+        for (int sl = d; sl < nsl; sl += 64) mloc = fmaxf(mloc, prow[(long long)sl * PSZ + hg]);
         const float M = wave_max(mloc);
         float lsum = 0.f;
         for (int sl = d; sl < nsl; sl += 64) {
-            const float w = fast_exp2(prow[(long long)sl * PSZ + h] - M);  // 0 for empty slots
+            const float w = fast_exp2(prow[(long long)sl * PSZ + hg] - M);  // 0 for empty slots
             wts[sl] = w;
-            lsum += w * prow[(long long)sl * PSZ + 16 + h];
+            lsum += w * prow[(long long)sl * PSZ + 16 + hg];
         }
         lsum = wave_sum(lsum);
         if (d == 0) stat[0] = 1.0f / lsum;
     }
     __syncthreads();
-    const float* po = prow + 32 + h * HD + d;
+    const float* po = prow + 32 + hg * HD + d;
     float o = 0.f;
     for (int s0 = 0; s0 < nsl; s0 += 16) {  // 16 slots per batch of independent loads
         float t[16];
@@ -642,10 +650,12 @@ __global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __
 hipError_t launch_attn_decode(DType dt, const DecAttnArgs& args, void* y, hipStream_t st) {
     DecAttnArgs a = args;
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)a.hd);
-    dim3 g1(a.iters == 1 ? a.max_slots / attn_decode_waves(a.B, a.S) : a.max_slots, a.B), g2(a.H, a.B);
-    const int nw = attn_decode_waves(a.B, a.S);
-    if (a.iters != attn_decode_iters(a.B, a.S) || a.max_slots != attn_decode_slots(a.B, a.S))
+    if (a.nkv < 1 || a.H % a.nkv || a.H / a.nkv > 16) return hipErrorInvalidValue;
+    const int units = a.B * a.nkv;  // (row, K/V head) pairs
+    const int nw = attn_decode_waves(units, a.S);
+    if (a.iters != attn_decode_iters(units, a.S) || a.max_slots != attn_decode_slots(units, a.S))
         return hipErrorInvalidValue;
+    dim3 g1(a.iters == 1 ? a.max_slots / nw : a.max_slots, units), g2(a.H, a.B);
     // the combine sees slots of `chunk` keys: a wave's block when R == 1, else a chunk
     const int chunk = a.iters == 1 ? DEC_KPW : nw * DEC_KPW * a.iters;
 #define NC_AD(TT, HDV)                                                                         \
@@ -653,7 +663,7 @@ hipError_t launch_attn_decode(DType dt, const DecAttnArgs& args, void* y, hipStr
         if (nw == 4) NC_TLAUNCH((attn_decode_split_kernel<TT, HDV, 4>), g1, dim3(256), 0, st, a); \
         else NC_TLAUNCH((attn_decode_split_kernel<TT, HDV, 2>), g1, dim3(128), 0, st, a);     \
         NC_TLAUNCH((attn_decode_combine_kernel<TT, HDV>), g2, dim3(HDV), 0, st,                \
-                   (const float*)a.part, a.lens, (TT*)y, a.H, a.S, a.max_slots, chunk);       \
+                   (const float*)a.part, a.lens, (TT*)y, a.H, a.nkv, a.S, a.max_slots, chunk); \
     } while (0)
     if (dt == BF16 && a.hd == 128) NC_AD(bf16, 128);
     else if (dt == BF16 && a.hd == 64) NC_AD(bf16, 64);

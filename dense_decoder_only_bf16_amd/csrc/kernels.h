@@ -103,29 +103,29 @@ hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t 
 hipError_t launch_embed(DType dt, const int32_t* tok, int M, const void* wte, int vocab, int d,
                         float eps, float* x, void* act, float* ss, bool blocked, hipStream_t st);
 
-// Pre-attention finish of the raw QKV product part[z][m][(H+2)*hd]:
-// scale row m by r_m, rotate q heads and the k head at position pos(m), QK-normalise,
-// write q [m][H][hd] and k, v into the cache of layer `layer`.
+// Pre-attention finish of the raw QKV product part[z][m][(H+2 nkv)*hd] (H query heads, then
+// nkv key heads, then nkv value heads): scale row m by r_m, rotate the q and k heads at
+// position pos(m), QK-normalise, write q [m][H][hd] and k, v into the cache of the layer.
 // Position of row m: prefill (lens == nullptr) pos = m % T, row b = m / T;
 // decode (lens != nullptr) b = m, pos = lens[b].
 struct QkvPostArgs {
     const float* part; int splits; long long z_stride;
-    int M, T, H, hd;
+    int M, T, H, hd, nkv;
     const float* ss_in; int ss_in_parts, ss_stride, norm_dim;
     const int32_t* lens;
     const float* rope_cos; const float* rope_sin; // [max_seq][hd/2]
     void* q;          // [M][H][hd]
-    void* kc;         // K cache of this layer: [B][S][hd]
-    void* vtc;        // V cache of this layer, transposed: [B][hd][S]
+    void* kc;         // K cache of this layer: [B][nkv][S][hd]
+    void* vtc;        // V cache of this layer, transposed: [B][nkv][hd][S]
     int S;            // cache capacity (positions)
     float eps;
 };
 hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st);
 
-// Causal multi-query attention over a full prefill: q [B*T][H][hd], K/V of this layer in
-// the cache (positions 0..T-1), y [B*T][H*hd].
+// Causal attention over a full prefill: q [B*T][H][hd], K/V of this layer in the cache
+// (positions 0..T-1, nkv heads; query head h reads K/V head h / (H / nkv)), y [B*T][H*hd].
 hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, const void* vtc,
-                               void* y, int B, int T, int H, int S, hipStream_t st);
+                               void* y, int B, int T, int H, int nkv, int S, hipStream_t st);
 
 // Decode attention for one step, one query per row at position lens[b] (keys
 // 0..lens[b]).  The split kernel first finishes the row's raw QKV product (norm scale,
@@ -133,20 +133,21 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 // keys to a partial softmax state; the combine kernel merges a row's partials into
 // y, [B][H hd] stored blocked (blocked_index, rows rounded up to 32).  The combine reads lens[b] to know the chunk count.
 struct DecAttnArgs {
-    const float* qkv;   // raw product [B][(H+2) hd] fp32
+    const float* qkv;   // raw product [B][(H+2 nkv) hd] fp32
     const float* ss_in; int ss_in_parts, ss_stride, norm_dim;
     float eps;
     const float* rope_cos; const float* rope_sin;
     const int32_t* lens;
-    void* kc; void* vtc;  // this layer's cache: K [B][S][hd], V^T [B][hd][S]
-    float* part;          // [B][max_slots][16 (hd + 2)]
-    int B, H, hd, S;
-    int iters;            // 64-key blocks per wave: attn_decode_iters(B, S)
-    int max_slots;        // attn_decode_slots(B, S)
+    void* kc; void* vtc;  // this layer's cache: K [B][nkv][S][hd], V^T [B][nkv][hd][S]
+    float* part;          // [B nkv][max_slots][16 (hd + 2)]
+    int B, H, hd, S, nkv; // query heads H = nkv G, G <= 16 per K/V head
+    int iters;            // 64-key blocks per wave: attn_decode_iters(B nkv, S)
+    int max_slots;        // attn_decode_slots(B nkv, S)
     float scale_log2;     // set by the launcher
 };
-int attn_decode_iters(int B, int S);  // chunk of a workgroup = 256 x iters keys
-int attn_decode_slots(int B, int S);  // partial slots (chunks) per row, cache of S positions
+// For `rows` (row, K/V head) units over a cache of S positions:
+int attn_decode_iters(int rows, int S);  // 64-key blocks per wave
+int attn_decode_slots(int rows, int S);  // partial slots per unit
 hipError_t launch_attn_decode(DType dt, const DecAttnArgs& a, void* y, hipStream_t st);
 
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st);

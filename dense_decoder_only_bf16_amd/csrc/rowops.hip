@@ -77,13 +77,13 @@ hipError_t launch_embed(DType dt, const int32_t* tok, int M, const void* wte, in
 }
 
 // ------------------------------------------------------------------ QKV finish ------
-// One wave per (row, head slot); slots 0..H-1 are query heads, H the key head, H+1 the
-// value head.  Lane i < hd/2 holds the RoPE pair (i, i + hd/2).
+// One wave per (row, head slot); slots 0..H-1 are query heads, H..H+nkv-1 the key heads,
+// H+nkv..H+2nkv-1 the value heads.  Lane i < hd/2 holds the RoPE pair (i, i + hd/2).
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
     const int lane = threadIdx.x & 63;
     const long long gw = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int slots = a.H + 2;
+    const int slots = a.H + 2 * a.nkv;
     if (gw >= (long long)a.M * slots) return;
     const int m = (int)(gw / slots), j = (int)(gw % slots);
     const int half = a.hd / 2;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
         v1 *= r;
         v2 *= r;
     }
-    if (j <= a.H) {
+    if (j < a.H + a.nkv) {
         float c = 0.f, sn = 0.f;
         if (act) {
             c = a.rope_cos[(long long)pos * half + lane];
@@ -128,19 +128,20 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
             if (j < a.H)
                 dst = (T*)a.q + ((long long)m * a.H + j) * a.hd;
             else
-                dst = (T*)a.kc + ((long long)b * a.S + pos) * a.hd;
+                dst = (T*)a.kc + (((long long)b * a.nkv + (j - a.H)) * a.S + pos) * a.hd;
             dst[lane] = from_f32<T>(o1);
             dst[lane + half] = from_f32<T>(o2);
         }
     } else if (act) {
-        T* vt = (T*)a.vtc + (long long)b * a.hd * a.S;
+        T* vt = (T*)a.vtc + ((long long)b * a.nkv + (j - a.H - a.nkv)) * a.hd * a.S;
         vt[(long long)lane * a.S + pos] = from_f32<T>(v1);
         vt[(long long)(lane + half) * a.S + pos] = from_f32<T>(v2);
     }
 }
 
 hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st) {
-    long long waves = (long long)a.M * (a.H + 2);
+    if (a.nkv < 1 || a.H % a.nkv) return hipErrorInvalidValue;
+    long long waves = (long long)a.M * (a.H + 2 * a.nkv);
     dim3 grid((unsigned)((waves + 3) / 4));
     if (dt == BF16)
         hipLaunchKernelGGL(qkv_post_kernel<bf16>, grid, dim3(256), 0, st, a);

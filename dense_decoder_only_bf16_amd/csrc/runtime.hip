@@ -165,7 +165,7 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
     HIP_TRY(hipDeviceSynchronize());
     ws_free(kv);
     const long long d = c.d_model, hq = (long long)c.n_head * c.head_dim;
-    const long long nqkv = (long long)(c.n_head + 2) * c.head_dim;
+    const long long nqkv = (long long)(c.n_head + 2 * c.n_kv_head) * c.head_dim;
     // row statistics come in parts of one per output tile of the producing product
     kv->ss_parts_max = (c.d_model + dec_gemm_tile_n() - 1) / dec_gemm_tile_n();
     const long long qkv_elems = M * nqkv;
@@ -184,11 +184,14 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
         WS_ALLOC(kv->act_lo, Mr * d * es);
         WS_ALLOC(kv->u_lo, Mr * c.d_ff * es);
     }
-    kv->apart_elems = (long long)kv->B * attn_decode_slots(kv->B, kv->S) * 16 * (c.head_dim + 2);
+    {
+        const int units = kv->B * c.n_kv_head;  // (row, K/V head) pairs of decode attention
+        kv->apart_elems = (long long)units * attn_decode_slots(units, kv->S) * 16 * (c.head_dim + 2);
+    }
     WS_ALLOC(kv->apart, kv->apart_elems * 4);
     {   // split-K partials of the decode projections (M = batch rows)
         const int B = kv->B, d = c.d_model, F = c.d_ff, hqv = c.n_head * c.head_dim;
-        const int nq = (c.n_head + 2) * c.head_dim;
+        const int nq = (c.n_head + 2 * c.n_kv_head) * c.head_dim;
         const DType dt = kv->m->dt;
         long long e = std::max({dec_gemm_part_elems(dt, EPI_STORE, B, nq, d),
                                 dec_gemm_part_elems(dt, EPI_RESID, B, d, hqv),
@@ -209,10 +212,12 @@ nc_status check_cfg(const nc_config* c) {
         c->vocab < 1 || c->max_seq < 1)
         return fail(NC_ERR_INVALID_ARG, "all sizes must be positive");
     if (c->dtype != NC_F32 && c->dtype != NC_BF16) return fail(NC_ERR_INVALID_ARG, "dtype must be NC_F32 or NC_BF16");
-    if (c->n_kv_head != 1) return fail(NC_ERR_UNSUPPORTED, "only n_kv_head == 1 (multi-query attention) is supported");
+    if (c->n_kv_head < 1 || c->n_head % c->n_kv_head)
+        return fail(NC_ERR_INVALID_ARG, "n_kv_head must be >= 1 and divide n_head");
+    if (c->n_head / c->n_kv_head > 16)
+        return fail(NC_ERR_UNSUPPORTED, "more than 16 query heads per K/V head is not supported by the decode attention kernel");
     if (c->head_dim != 64 && c->head_dim != 128) return fail(NC_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     if ((long long)c->n_head * c->head_dim != c->d_model) return fail(NC_ERR_INVALID_ARG, "d_model must equal n_head * head_dim");
-    if (c->n_head > 16) return fail(NC_ERR_UNSUPPORTED, "n_head > 16 is not supported by the decode attention kernel");
     if (c->d_model % 64 || c->d_ff % 64) return fail(NC_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
     if (c->d_model > 4096) return fail(NC_ERR_UNSUPPORTED, "d_model > 4096 is not supported");
     if (!(c->softcap > 0.f) || !(c->norm_eps >= 0.f) || !(c->rope_base > 0.f))
@@ -308,10 +313,10 @@ hipError_t prefill_gemm(nc_model* m, Epi epi, const GemmArgs& g, hipStream_t st)
 nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* logits, hipStream_t st) {
     const nc_config& c = m->cfg;
     const int B = kv->B;
-    const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab;
-    const int nqkv = (H + 2) * hd;
-    const size_t per_layer = (size_t)B * kv->S * hd * m->esz;
-    const int max_slots = attn_decode_slots(B, kv->S);
+    const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab, nkv = c.n_kv_head;
+    const int nqkv = (H + 2 * nkv) * hd;
+    const size_t per_layer = (size_t)B * nkv * kv->S * hd * m->esz;
+    const int max_slots = attn_decode_slots(B * nkv, kv->S);
     const int parts_d = (d + dec_gemm_tile_n() - 1) / dec_gemm_tile_n();
     const int ss = (int)kv->cap_m;
     nc_status s;
@@ -333,14 +338,15 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         at.qkv = kv->qkv; at.ss_in = kv->ss_a; at.ss_in_parts = ss_a_parts; at.ss_stride = ss;
         at.norm_dim = d; at.eps = c.norm_eps; at.rope_cos = m->rope_cos; at.rope_sin = m->rope_sin;
         at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = kv->apart;
-        at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.max_slots = max_slots;
-        at.iters = attn_decode_iters(B, kv->S);
+        at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.nkv = nkv; at.max_slots = max_slots;
+        at.iters = attn_decode_iters(B * nkv, kv->S);
         {   // bytes: the K/V read for every row (positions 0..lens_b, the new one
-            // included), q/k/v in fp32, y out; flops 4 hd per (query head, key) pair
+            // included) of each K/V head, q/k/v in fp32, y out; flops 4 hd per
+            // (query head, key) pair
             const double es = (double)m->esz;
             double keys = 0;
             for (int b = 0; b < B; ++b) keys += kv->lens_host[b] + 1;
-            const double by = keys * hd * 2 * es + (double)B * nqkv * 4 + (double)B * H * hd * es;
+            const double by = keys * nkv * hd * 2 * es + (double)B * nqkv * 4 + (double)B * H * hd * es;
             LAUNCH(timed(NC_KC_DECODE_ATTN, by, 4.0 * H * hd * keys, st,
                          [&] { return launch_attn_decode(m->dt, at, kv->y, st); }, 2));
         }
@@ -408,10 +414,11 @@ nc_status nc_model_create(const nc_config* cfg, const void* const* weights, nc_m
         m->esz = cfg->dtype == NC_BF16 ? 2 : 4;
         m->device = dev;
         const size_t d = cfg->d_model, hd = cfg->head_dim, H = cfg->n_head, V = cfg->vocab, F = cfg->d_ff;
+        const size_t nkv = cfg->n_kv_head;
         const size_t es = m->esz;
         // projection weights are stored MFMA-blocked (kernels.h); the embedding stays row-major
         const size_t sz_emb = align_up(V * d * es, 256);
-        const size_t sz_qkv = align_up((size_t)blocked_elems((int)((H + 2) * hd), (int)d) * es, 256);
+        const size_t sz_qkv = align_up((size_t)blocked_elems((int)((H + 2 * nkv) * hd), (int)d) * es, 256);
         const size_t sz_o = align_up((size_t)blocked_elems((int)d, (int)(H * hd)) * es, 256);
         const size_t sz_fc = align_up((size_t)blocked_elems((int)F, (int)d) * es, 256);
         const size_t sz_pj = align_up((size_t)blocked_elems((int)d, (int)F) * es, 256);
@@ -428,14 +435,15 @@ nc_status nc_model_create(const nc_config* cfg, const void* const* weights, nc_m
         p += sz_emb;
         m->layers.resize(cfg->n_layer);
         const size_t qrows_bytes = (size_t)blocked_elems((int)(H * hd), (int)d) * es;  // H*hd is a multiple of 32
-        const size_t krows_bytes = (size_t)blocked_elems((int)hd, (int)d) * es;
+        const size_t krows_bytes = (size_t)blocked_elems((int)(nkv * hd), (int)d) * es;  // hd is too
         for (int l = 0; l < cfg->n_layer && ce == hipSuccess; ++l) {
             const void* const* w = weights + 1 + 6 * l;
             nc_model::Layer& L = m->layers[l];
             L.wqkv = p;
             ce = launch_repack(m->dt, w[0], p, (int)(H * hd), (int)d, 0);
-            if (ce == hipSuccess) ce = launch_repack(m->dt, w[1], p + qrows_bytes, (int)hd, (int)d, 0);
-            if (ce == hipSuccess) ce = launch_repack(m->dt, w[2], p + qrows_bytes + krows_bytes, (int)hd, (int)d, 0);
+            if (ce == hipSuccess) ce = launch_repack(m->dt, w[1], p + qrows_bytes, (int)(nkv * hd), (int)d, 0);
+            if (ce == hipSuccess)
+                ce = launch_repack(m->dt, w[2], p + qrows_bytes + krows_bytes, (int)(nkv * hd), (int)d, 0);
             p += sz_qkv;
             L.wo = p;
             if (ce == hipSuccess) ce = launch_repack(m->dt, w[3], p, (int)d, (int)(H * hd), 0);
@@ -505,7 +513,7 @@ nc_status nc_kv_create(nc_model* m, int32_t batch, int32_t max_seq, nc_kv** out)
         const char* ng = std::getenv("NC_DECODE_GRAPH");
         kv->use_graph = !(ng && ng[0] == '0');
         const nc_config& c = m->cfg;
-        const size_t bytes = (size_t)c.n_layer * batch * kv->S * c.head_dim * m->esz;
+        const size_t bytes = (size_t)c.n_layer * batch * c.n_kv_head * kv->S * c.head_dim * m->esz;
         hipError_t e = hipMalloc(&kv->kcache, bytes);
         if (e == hipSuccess) e = hipMalloc(&kv->vcache, bytes);
         if (e == hipSuccess) e = hipMalloc((void**)&kv->lens_dev, batch * sizeof(int32_t));
@@ -564,10 +572,11 @@ nc_status nc_kv_export(nc_kv* kv, int32_t layer, void* k_out, void* v_out, void*
     if (!kv || !k_out || !v_out) return fail(NC_ERR_INVALID_ARG, "NULL argument");
     const nc_config& c = kv->m->cfg;
     if (layer < 0 || layer >= c.n_layer) return fail(NC_ERR_INVALID_ARG, "layer out of range");
-    const size_t per_layer = (size_t)kv->B * kv->S * c.head_dim * kv->m->esz;
+    const size_t per_layer = (size_t)kv->B * c.n_kv_head * kv->S * c.head_dim * kv->m->esz;
     const char* kc = (const char*)kv->kcache + layer * per_layer;
     const char* vc = (const char*)kv->vcache + layer * per_layer;
-    LAUNCH(launch_kv_export(kv->m->dt, c.head_dim, kc, vc, k_out, v_out, kv->B, kv->S, kv->max_seq,
+    // the cache is [B][n_kv_head][...] per layer: export (row, K/V head) pairs as rows
+    LAUNCH(launch_kv_export(kv->m->dt, c.head_dim, kc, vc, k_out, v_out, kv->B * c.n_kv_head, kv->S, kv->max_seq,
                             (hipStream_t)stream));
     return NC_OK;
 }
@@ -593,11 +602,11 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
         if (s != NC_OK) return s;
         hipStream_t st = (hipStream_t)stream;
         const nc_config& c = m->cfg;
-        const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab;
-        const int nqkv = (H + 2) * hd;
+        const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab, nkv = c.n_kv_head;
+        const int nqkv = (H + 2 * nkv) * hd;
         const int tn = gemm_tile_n();
         const int parts_d = (d + tn - 1) / tn;
-        const size_t per_layer = (size_t)B * kv->S * hd * m->esz;
+        const size_t per_layer = (size_t)B * nkv * kv->S * hd * m->esz;
         const int Mi = (int)M;
 
         LAUNCH(launch_embed(m->dt, tokens, Mi, m->wte, V, d, c.norm_eps, kv->x, kv->act, kv->ss_a, false, st));
@@ -611,7 +620,7 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             g.out_f32 = kv->qkv; g.ldo = nqkv; g.z_stride = 0;
             LAUNCH(prefill_gemm(m, EPI_STORE, g, st));
             QkvPostArgs qa{};
-            qa.part = kv->qkv; qa.splits = 1; qa.z_stride = 0; qa.M = Mi; qa.T = T; qa.H = H; qa.hd = hd;
+            qa.part = kv->qkv; qa.splits = 1; qa.z_stride = 0; qa.M = Mi; qa.T = T; qa.H = H; qa.hd = hd; qa.nkv = nkv;
             qa.ss_in = kv->ss_a; qa.ss_in_parts = ss_a_parts; qa.ss_stride = (int)kv->cap_m; qa.norm_dim = d;
             qa.lens = nullptr; qa.rope_cos = m->rope_cos; qa.rope_sin = m->rope_sin;
             qa.q = kv->q; qa.kc = (char*)kv->kcache + l * per_layer; qa.vtc = (char*)kv->vcache + l * per_layer;
@@ -619,9 +628,9 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             LAUNCH(launch_qkv_post(m->dt, qa, st));
             {   // causal attention flops: 4 hd per visible (query, key) pair and head
                 const double fl = 4.0 * B * H * hd * (double)T * (T + 1) / 2.0;
-                const double by = (double)B * T * (H + 2 + H) * hd * m->esz;  // q, k, v in; y out
+                const double by = (double)B * T * (H + 2 * nkv + H) * hd * m->esz;  // q, k, v in; y out
                 LAUNCH(timed(NC_KC_PREFILL_ATTN, by, fl, st, [&] {
-                    return launch_attn_prefill(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->y, B, T, H, kv->S, st);
+                    return launch_attn_prefill(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->y, B, T, H, nkv, kv->S, st);
                 }));
             }
             // O product + residual

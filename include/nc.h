@@ -11,8 +11,9 @@
  *   per layer l:
  *     h    = norm(x)
  *     q    = norm(rope(h Wq^T, pos)) per head,  k = norm(rope(h Wk^T, pos)),  v = h Wv^T
- *     y_h  = softmax(q_h k^T / sqrt(hd) + causal mask) v   (one K/V head shared by all
- *            query heads: multi-query attention)
+ *     y_h  = softmax(q_h k_g^T / sqrt(hd) + causal mask) v_g,  g = h / (n_head / n_kv_head)
+ *            (n_kv_head K/V heads, each shared by a group of query heads: n_kv_head == 1
+ *            is multi-query attention, n_kv_head == n_head plain multi-head attention)
  *     x   += concat_h(y_h) Wo^T
  *     x   += relu(norm(x) Wfc^T)^2 Wproj^T
  *   logits = cap * tanh(norm(x) Wlm^T / cap)                   (fp32)
@@ -60,8 +61,9 @@ typedef int32_t nc_status;
 
 #define NC_ABI_VERSION 1
 
-/* Model shape.  Requirements: d_model == n_head * head_dim; n_kv_head == 1 (multi-query
- * attention); head_dim in {64, 128}; n_head <= 16; d_model <= 4096; d_model, d_ff
+/* Model shape.  Requirements: d_model == n_head * head_dim; n_kv_head >= 1 divides n_head
+ * (NC_ERR_INVALID_ARG otherwise) with at most 16 query heads per K/V head
+ * (NC_ERR_UNSUPPORTED otherwise); head_dim in {64, 128}; d_model <= 4096; d_model, d_ff
  * multiples of 64; vocab >= 1; max_seq >= 1 (longest position the RoPE table covers);
  * softcap > 0; norm_eps >= 0. */
 typedef struct nc_config {
@@ -85,7 +87,8 @@ typedef struct nc_kv nc_kv;       /* KV cache + per-row lengths + workspace, lib
 /* Build a model from 6*n_layer + 2 device tensors of cfg->dtype elements, row-major
  * [out, in], in canonical order:
  *   wte [vocab, d_model],
- *   per layer: Wq [n_head*hd, d], Wk [hd, d], Wv [hd, d], Wo [d, n_head*hd],
+ *   per layer: Wq [n_head*hd, d], Wk [n_kv_head*hd, d], Wv [n_kv_head*hd, d],
+ *              Wo [d, n_head*hd],
  *              Wfc [d_ff, d], Wproj [d, d_ff],
  *   lm_head [vocab, d_model].
  * The library copies (and repacks) them into memory it owns, synchronously; the caller may
@@ -97,7 +100,8 @@ void nc_model_free(nc_model* m); /* NULL is a no-op; all kv objects must be free
 
 /* KV cache for `batch` rows of up to `max_seq` positions (max_seq <= cfg.max_seq, and at
  * most 32768: NC_ERR_UNSUPPORTED otherwise).
- * Layout (library-private): K [L][batch][max_seq][hd], V transposed [L][batch][hd][max_seq],
+ * Layout (library-private): K [L][batch][n_kv_head][max_seq][hd], V transposed
+ * [L][batch][n_kv_head][hd][max_seq],
  * both cfg.dtype; keys are stored after RoPE and QK-norm.  All lengths start at 0. */
 nc_status nc_kv_create(nc_model* m, int32_t batch, int32_t max_seq, nc_kv** out);
 void nc_kv_free(nc_kv* kv); /* NULL is a no-op; synchronises the device first */
@@ -110,7 +114,8 @@ nc_status nc_kv_set_lens(nc_kv* kv, const int32_t* lens_host);
 nc_status nc_kv_get_lens(const nc_kv* kv, int32_t* lens_host);
 
 /* Copy layer `layer` of the cache out in plain layout: k_dev and v_dev are
- * [batch][max_seq][hd] of cfg.dtype (rows past each length hold stale values). */
+ * [batch][n_kv_head][max_seq][hd] of cfg.dtype (positions past each length hold stale
+ * values). */
 nc_status nc_kv_export(nc_kv* kv, int32_t layer, void* k_dev, void* v_dev, void* stream);
 
 /* Prefill: tokens_dev int32 [B, T] at positions 0..T-1 of every row.  Requires every

@@ -59,7 +59,8 @@ def _bad_cfg(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(n_kv_head=2), nc.NC_ERR_UNSUPPORTED),
+    (dict(n_kv_head=0), nc.NC_ERR_INVALID_ARG),
+    (dict(n_kv_head=3), nc.NC_ERR_INVALID_ARG),  # does not divide n_head = 2
     (dict(head_dim=96, d_model=192), nc.NC_ERR_UNSUPPORTED),
     (dict(d_model=100), nc.NC_ERR_INVALID_ARG),
     (dict(n_layer=0), nc.NC_ERR_INVALID_ARG),

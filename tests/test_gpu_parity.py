@@ -275,9 +275,18 @@ SMALL_HD64 = Shape("small-hd64", n_layer=2, d_model=256, n_head=4, head_dim=64, 
 # the most query heads the decode kernel takes (16: no padded head slots)
 WIDE_H16 = Shape("h16", n_layer=1, d_model=2048, n_head=16, head_dim=128, d_ff=2048,
                  vocab=512, dtype="bf16", max_seq=96)
+# grouped-query attention: 8 query heads over 2 K/V heads (groups of 4)
+GQA_8_2 = Shape("gqa8x2", n_layer=2, d_model=1024, n_head=8, head_dim=128, d_ff=2048,
+                vocab=640, dtype="bf16", max_seq=160, n_kv_head=2)
+# plain multi-head attention (a K/V head per query head), head_dim 64
+MHA_4 = Shape("mha4", n_layer=2, d_model=256, n_head=4, head_dim=64, d_ff=512,
+              vocab=300, dtype="bf16", max_seq=100, n_kv_head=4)
+# the widest group with more than one K/V head: 32 query heads over 2 (groups of 16)
+GQA_32_2 = Shape("gqa32x2", n_layer=1, d_model=2048, n_head=32, head_dim=64, d_ff=1024,
+                 vocab=256, dtype="bf16", max_seq=96, n_kv_head=2)
 
 
-@pytest.mark.parametrize("shape", [SMALL_HD64, WIDE_H16], ids=lambda s: s.name)
+@pytest.mark.parametrize("shape", [SMALL_HD64, WIDE_H16, GQA_8_2, MHA_4, GQA_32_2], ids=lambda s: s.name)
 def test_bf16_other_head_shapes(shape):
     """Prefill of ragged rows, then decode from rows truncated to 0 (empty context: the new
     key is the only one), 1 and a middle length, compared with the oracle everywhere."""
@@ -302,5 +311,68 @@ def test_bf16_other_head_shapes(shape):
         flip = np.argmax(got[b], -1) != np.argmax(ref[0], -1)
         assert not np.any(flip & (srt[:, -1] - srt[:, -2] >= 2 * err))
     assert np.array_equal(kv.lens(), lens + 4)
+    kv.close()
+    gm.close()
+
+
+# fp32 grouped-query model: 4 query heads over 2 K/V heads, checked at the fp32 bar
+TINY_GQA = replace(TINY, name="tiny-gqa", d_model=256, n_head=4, n_kv_head=2, d_ff=512)
+
+
+def test_fp32_gqa_prefill_decode_and_cache():
+    """Grouped-query attention in fp32: prefill logits, teacher-forced decode logits and
+    every K/V head of the cache against the oracle at the fp32 bar."""
+    torch = torch_mod()
+    shape = TINY_GQA
+    w = make_weights(shape, seed=40)
+    orc = OracleModel(shape, w)
+    gm = gpu_model(shape, w)
+    B, T, steps = 2, 50, 6
+    toks = make_tokens(shape.vocab, B, T + steps, seed=41)
+    want, cache = orc.prefill(toks, max_seq=shape.max_seq)
+    kv, got = prefill(gm, toks[:, :T], shape.max_seq)
+    err, _ = report("tiny-gqa prefill", got, want[:, :T])
+    assert err <= F32_TOL
+    nkv, hd, S = shape.n_kv_head, shape.head_dim, shape.max_seq
+    for layer in range(shape.n_layer):
+        k = torch.empty((B, nkv, S, hd), device="cuda", dtype=torch.float32)
+        v = torch.empty_like(k)
+        kv.export(layer, k, v)
+        torch.cuda.synchronize()
+        k, v = k.cpu().numpy(), v.cpu().numpy()
+        # oracle cache: [layer][row][position][K/V head][hd]
+        ck = np.transpose(cache["k"][layer, :, :T], (0, 2, 1, 3))
+        cv = np.transpose(cache["v"][layer, :, :T], (0, 2, 1, 3))
+        assert np.max(np.abs(k[:, :, :T] - ck)) < 1e-5
+        assert np.max(np.abs(v[:, :, :T] - cv)) < 1e-5
+    got = np.stack([decode(gm, kv, toks[:, T + s]) for s in range(steps)], axis=1)
+    err, _ = report("tiny-gqa decode", got, want[:, T:T + steps])
+    assert err <= F32_TOL
+    kv.close()
+    gm.close()
+
+
+@pytest.mark.parametrize("B", [3, 40])
+def test_bf16_gqa_decode_many_rows(B):
+    """Grouped-query decode at mixed context lengths up to 600 (B = 40: 80 (row, K/V head)
+    units, so the split kernel runs 4 waves and merges them in LDS; B = 3: one block per
+    wave), 2 teacher-forced steps; every row is checked against the oracle."""
+    shape = replace(GQA_8_2, n_layer=1, max_seq=640)
+    w = make_weights(shape, seed=42)
+    orc = OracleModel(shape, w)
+    gm = gpu_model(shape, w)
+    T, steps = 600, 2
+    toks = make_tokens(shape.vocab, B, T + steps, seed=43 + B)
+    lens = make_lens(B, 1, T, seed=44 + B)
+    kv, _ = prefill(gm, toks[:, :T], shape.max_seq, logits=False)
+    kv.set_lens(lens)
+    got = np.stack([decode(gm, kv, toks[:, T + s]) for s in range(steps)], axis=1)
+    assert np.array_equal(kv.lens(), lens + steps)
+    want = np.empty_like(got, dtype=np.float64)
+    for b in range(B):
+        seq = np.concatenate([toks[b, :lens[b]], toks[b, T:T + steps]])[None]
+        want[b] = orc.prefill(seq, logits_at=np.arange(lens[b], lens[b] + steps))[0][0]
+    err, agr = report(f"gqa decode B={B}", got, want)
+    assert err <= BF16_TOL and agr >= AGREE
     kv.close()
     gm.close()
