@@ -22,5 +22,6 @@ from .model import (  # noqa: F401
     softcap,
     linear,
     causal_attention,
+    layer_windows,
     param_count,
 )

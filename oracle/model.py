@@ -20,6 +20,11 @@ What is computed, and where the pages say so:
     extracted text); geoz.com.cn development tricks; apidog.com part 1];
   * no bias in any linear layer [yelogs.com architecture answer];
   * multi-query attention, one K/V head shared by every query head [yelogs.com answer];
+    grouped-query attention, fewer K/V heads than query heads, in the later version
+    [apidog.com part 1, architecture features];
+  * sliding-window attention with a configurable per-layer pattern of short and long
+    windows ("SSSL"), passed to the attention call as a window size [apidog.com part 1,
+    architecture features; part 5, the flash-attention call with window_size];
   * a softcap on the logits [yelogs.com architecture answer];
   * inference with a KV cache: prefill of the prompt, then one token per decode step
     [szyisi.cn, section on the base model and the Engine class; apidog.com part 6,
@@ -34,7 +39,12 @@ Readings where the pages are silent (each is listed with its reason in the desig
   * attention: scale 1/sqrt(hd), causal including the diagonal, full max-subtracted softmax;
   * MLP: d -> d_ff -> d, activation relu(x)^2, no gate;
   * residual: plain x <- x + f(norm(x));
-  * softcap: cap * tanh(z / cap).
+  * softcap: cap * tanh(z / cap);
+  * sliding window w >= 0: a query at position p sees keys p - w .. p (w + 1 keys, the
+    left extent of the window_size argument of the pages' flash-attention call; its
+    right extent is 0 under causality); w < 0 means the whole causal context;
+  * window pattern: character l mod len(pattern) of the pattern gives layer l's window,
+    'S' the short window and 'L' the whole context.
 
 Everything is evaluated in float64 with plain numpy operations: no tiling, no online
 softmax, no fusion.  Weights may arrive in any float dtype; they are widened to float64
@@ -98,11 +108,12 @@ def linear(x, w):
     return np.asarray(x, dtype=F64) @ np.asarray(w, dtype=F64).T
 
 
-def causal_attention(q, k, v, q_pos):
+def causal_attention(q, k, v, q_pos, window=-1):
     """Causal softmax attention with shared K/V heads.
 
     q: [Tq, H, hd]; k, v: [Tk, n_kv, hd] holding key positions 0..Tk-1;
-    q_pos: [Tq] absolute position of each query.  Query t sees keys j <= q_pos[t].
+    q_pos: [Tq] absolute position of each query.  Query t sees keys j <= q_pos[t], and
+    with window >= 0 only those with j >= q_pos[t] - window.
     Query head h reads K/V head h // (H / n_kv); with n_kv = 1 every query head shares
     the single K/V head (multi-query attention)."""
     q = np.asarray(q, dtype=F64)
@@ -111,7 +122,11 @@ def causal_attention(q, k, v, q_pos):
     tq, n_head, hd = q.shape
     tk, n_kv, _ = k.shape
     group = n_head // n_kv
-    hidden = np.arange(tk)[None, :] > np.asarray(q_pos)[:, None]
+    j = np.arange(tk)[None, :]
+    qp = np.asarray(q_pos)[:, None]
+    hidden = j > qp
+    if window >= 0:
+        hidden = hidden | (j < qp - window)
     y = np.empty((tq, n_head, hd), dtype=F64)
     for h in range(n_head):
         g = h // group
@@ -122,6 +137,21 @@ def causal_attention(q, k, v, q_pos):
         p = p / np.sum(p, axis=1, keepdims=True)
         y[:, h, :] = p @ v[:, g, :]
     return y
+
+
+def layer_windows(pattern, n_layer, short_window):
+    """Per-layer windows from a pattern of 'S' (short window) and 'L' (whole context)
+    characters, repeated over the layers: layer l takes character l mod len(pattern)."""
+    out = []
+    for layer in range(n_layer):
+        ch = pattern[layer % len(pattern)]
+        if ch == "S":
+            out.append(int(short_window))
+        elif ch == "L":
+            out.append(-1)
+        else:
+            raise ValueError(f"window pattern character {ch!r} is not S or L")
+    return out
 
 
 def param_count(n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, vocab):
@@ -147,9 +177,11 @@ class OracleModel:
     weights: {"wte": [V, d], "layers": [{"wq": [H*hd, d], "wk": [n_kv*hd, d],
     "wv": [n_kv*hd, d], "wo": [d, H*hd], "wfc": [d_ff, d], "wproj": [d, d_ff]}, ...],
     "lm_head": [V, d]}.
+    windows: per-layer attention windows (see causal_attention), or None for the whole
+    causal context in every layer.
     """
 
-    def __init__(self, cfg, weights):
+    def __init__(self, cfg, weights, windows=None):
         for f in _CFG_FIELDS:
             setattr(self, f, getattr(cfg, f))
         assert self.n_head % self.n_kv_head == 0
@@ -158,6 +190,8 @@ class OracleModel:
         self.layers = [{k: np.asarray(lw[k], dtype=F64) for k in _LAYER_KEYS}
                        for lw in weights["layers"]]
         assert len(self.layers) == self.n_layer
+        self.windows = [-1] * self.n_layer if windows is None else [int(w) for w in windows]
+        assert len(self.windows) == self.n_layer
         self._cos = np.zeros((0, self.head_dim // 2))
         self._sin = self._cos
 
@@ -215,7 +249,7 @@ class OracleModel:
                 q, k, v = self._qkv(lw, x, pos)
                 cache["k"][li, b, :t_len] = k
                 cache["v"][li, b, :t_len] = v
-                y = causal_attention(q, k, v, pos)
+                y = causal_attention(q, k, v, pos, self.windows[li])
                 x = x + linear(y.reshape(t_len, -1), lw["wo"])
                 x = x + self._mlp(lw, x)
             logits[b] = self._head(x[at])
@@ -240,7 +274,7 @@ class OracleModel:
                 cache["k"][li, b, p] = k[0]
                 cache["v"][li, b, p] = v[0]
                 y = causal_attention(q, cache["k"][li, b, :p + 1], cache["v"][li, b, :p + 1],
-                                     pos)
+                                     pos, self.windows[li])
                 x = x + linear(y.reshape(1, -1), lw["wo"])
                 x = x + self._mlp(lw, x)
             logits[b] = self._head(x)[0]

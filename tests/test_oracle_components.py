@@ -6,7 +6,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import (causal_attention, linear, relu2, rms_norm, rope, rope_tables,
+from oracle import (causal_attention, layer_windows, linear, relu2, rms_norm, rope, rope_tables,
                     softcap)
 
 
@@ -147,16 +147,19 @@ def test_linear_matches_loop():
 
 
 # ---------------------------------------------------------------- attention ---------
-def brute_attention(q, k, v, q_pos):
-    """Triple loop from the definition: softmax over visible keys of q.k/sqrt(hd)."""
+def brute_attention(q, k, v, q_pos, window=-1):
+    """Triple loop from the definition: softmax over visible keys of q.k/sqrt(hd); with a
+    window w >= 0 the visible keys of a query at position p are max(0, p - w) .. p."""
     tq, n_head, hd = q.shape
     n_kv = k.shape[1]
     out = np.zeros_like(q)
     for t in range(tq):
         for h in range(n_head):
             g = h * n_kv // n_head
+            first = 0 if window < 0 else max(0, q_pos[t] - window)
+            keys = list(range(first, q_pos[t] + 1))
             scores = []
-            for j in range(q_pos[t] + 1):
+            for j in keys:
                 s = 0.0
                 for c in range(hd):
                     s += q[t, h, c] * k[j, g, c]
@@ -165,7 +168,7 @@ def brute_attention(q, k, v, q_pos):
             w = [math.exp(s - m) for s in scores]
             z = sum(w)
             for c in range(hd):
-                out[t, h, c] = sum(w[j] * v[j, g, c] for j in range(len(w))) / z
+                out[t, h, c] = sum(w[i] * v[j, g, c] for i, j in enumerate(keys)) / z
     return out
 
 
@@ -184,6 +187,54 @@ def test_attention_brute_force(n_head, n_kv):
     pos2 = np.array([3, 5])
     assert np.allclose(causal_attention(q2, k, v, pos2), brute_attention(q2, k, v, pos2),
                        rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("window", [0, 1, 3])
+@pytest.mark.parametrize("n_head,n_kv", [(3, 1), (4, 2)])
+def test_windowed_attention_brute_force(n_head, n_kv, window):
+    r = rng(11)
+    t, hd = 7, 8
+    q = r.standard_normal((t, n_head, hd))
+    k = r.standard_normal((t, n_kv, hd))
+    v = r.standard_normal((t, n_kv, hd))
+    pos = np.arange(t)
+    assert np.allclose(causal_attention(q, k, v, pos, window),
+                       brute_attention(q, k, v, pos, window), rtol=0, atol=1e-13)
+    q2 = r.standard_normal((2, n_head, hd))
+    pos2 = np.array([4, 6])
+    assert np.allclose(causal_attention(q2, k, v, pos2, window),
+                       brute_attention(q2, k, v, pos2, window), rtol=0, atol=1e-13)
+
+
+def test_window_special_cases():
+    r = rng(12)
+    t, hd = 6, 8
+    q = r.standard_normal((t, 4, hd))
+    k = r.standard_normal((t, 2, hd))
+    v = r.standard_normal((t, 2, hd))
+    pos = np.arange(t)
+    # window 0: a query sees only its own key, so the output is its group's value
+    y = causal_attention(q, k, v, pos, 0)
+    assert np.allclose(y, np.repeat(v, 2, axis=1), rtol=0, atol=1e-15)
+    # a window reaching past position 0 changes nothing
+    full = causal_attention(q, k, v, pos)
+    assert np.array_equal(causal_attention(q, k, v, pos, t - 1), full)
+    assert np.array_equal(causal_attention(q, k, v, pos, 10 * t), full)
+    # window 1 at position p: the two-key softmax in closed form
+    y1 = causal_attention(q, k, v, pos, 1)
+    p, h, g = 4, 3, 1
+    s0 = q[p, h] @ k[p - 1, g] / math.sqrt(hd)
+    s1 = q[p, h] @ k[p, g] / math.sqrt(hd)
+    a = 1.0 / (1.0 + math.exp(s1 - s0))
+    assert np.allclose(y1[p, h], a * v[p - 1, g] + (1 - a) * v[p, g], rtol=0, atol=1e-14)
+
+
+def test_layer_windows_pattern():
+    assert layer_windows("SSSL", 6, 128) == [128, 128, 128, -1, 128, 128]
+    assert layer_windows("L", 3, 64) == [-1, -1, -1]
+    assert layer_windows("SL", 3, 0) == [0, -1, 0]
+    with pytest.raises(ValueError):
+        layer_windows("SXL", 3, 8)
 
 
 def test_attention_special_cases():

@@ -208,6 +208,44 @@ def test_mqa_equals_mha_with_replicated_kv():
     assert np.allclose(mqa, mha, rtol=0, atol=1e-12)
 
 
+# ------------------------------------------------------- sliding windows --------------
+def test_one_layer_window_equals_suffix_prefill():
+    """One layer with window w: RoPE scores depend only on the distance between positions,
+    so the logits at position i equal those of the whole-context model run on tokens
+    i - w .. i alone (its last position)."""
+    shape = replace(MICRO, n_layer=1)
+    w = micro_weights(shape, seed=22)
+    toks = make_tokens(shape.vocab, 1, 12, seed=23)
+    for win in (0, 2, 5):
+        got, _ = OracleModel(shape, w, windows=[win]).prefill(toks)
+        full = OracleModel(shape, w)
+        for i in range(win, 12):
+            ref, _ = full.prefill(toks[:, i - win:i + 1], logits_at=[win])
+            assert np.allclose(got[0, i], ref[0, 0], rtol=0, atol=1e-11), (win, i)
+
+
+def test_window_receptive_field_and_decode():
+    """L layers of window w: position i depends on tokens i - L w .. i only (a suffix run
+    reproduces it), and decode steps reproduce the prefill logits."""
+    shape = replace(MICRO, n_layer=2, n_kv_head=1)
+    w = micro_weights(shape, seed=24)
+    wins = [2, 1]
+    m = OracleModel(shape, w, windows=wins)
+    toks = make_tokens(shape.vocab, 2, 12, seed=25)
+    full, _ = m.prefill(toks)
+    reach = sum(wins)
+    for i in range(reach, 12):
+        ref, _ = m.prefill(toks[:, i - reach:i + 1], logits_at=[reach])
+        assert np.allclose(full[:, i], ref[:, 0], rtol=0, atol=1e-11)
+    # a longer reach would matter: the whole-context model differs
+    whole, _ = OracleModel(shape, w).prefill(toks)
+    assert np.max(np.abs(whole[:, 8:] - full[:, 8:])) > 1e-3
+    _, cache = m.prefill(toks[:, :5], max_seq=12)
+    for t in range(5, 12):
+        step = m.decode_step(cache, toks[:, t])
+        assert np.allclose(step, full[:, t], rtol=0, atol=1e-11)
+
+
 def test_embedding_and_qk_scale_invariance_at_eps0():
     shape = replace(MICRO, norm_eps=0.0)
     w = micro_weights(shape, seed=18)
