@@ -25,14 +25,17 @@ namespace nc {
 // queries as JN 32-column MFMA tiles.  The launcher uses JN = 1: 8 waves whose registers
 // leave room for two waves per SIMD, so one wave's MFMAs overlap another's softmax
 // (measured 1.35x faster than 4 waves of 64 queries at the d12 and d20 prefill shapes).  K/V advance in blocks of 64 keys staged in
-// LDS; blocks past the last query of the workgroup are never loaded, and a wave whose
-// queries all precede a block skips its MFMAs.
+// LDS; blocks past the last query of the workgroup, or before the window of its first
+// query, are never loaded, and a wave whose queries all precede a block, or whose windows
+// all start after it, skips its MFMAs.  Sliding window: a query at position p sees keys
+// p - win .. p (win >= Tn: the whole causal context).
 template <typename T, int HD, int JN>
 __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __restrict__ q,
                                                            const T* __restrict__ kc,
                                                            const T* __restrict__ vtc,
                                                            T* __restrict__ y, int Tn, int H,
-                                                           int nkv, int S, float scale_log2) {
+                                                           int nkv, int S, int win,
+                                                           float scale_log2) {
     typedef typename Chunk<T>::type CT;
     typedef typename Chunk<T>::half HT;
     constexpr int BQ = 256, KB = 64, NT = 64 * 8 / JN;
@@ -80,6 +83,8 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 
     const int kend = min(Tn, q0 + BQ);
     const int nkb = (kend + KB - 1) / KB;
+    const int kb_first = max(0, q0 - win) / KB;  // earliest key any query here sees
+    const int qlast_w = q0w + 32 * JN - 1;        // last query of this wave
     constexpr int KCH = KB * CPRK / NT;  // K chunks per thread
     constexpr int VCH = HD * (KB / 8) / NT;
     static_assert(KCH >= 1 && VCH >= 1, "block too small for the workgroup");
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
             }
         }
     };
-    for (int kbi = 0; kbi < nkb; ++kbi) {
+    for (int kbi = kb_first; kbi < nkb; ++kbi) {
         const int k0 = kbi * KB;
         gload(k0);
         __syncthreads();  // previous block's LDS reads are complete
@@ -124,7 +129,8 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
         }
         __syncthreads();
 
-        if (k0 > q0w + 32 * JN - 1) continue;  // every query of this wave precedes the block
+        // every query of this wave precedes the block, or its window starts after it
+        if (k0 > qlast_w || k0 + KB - 1 < q0w - win) continue;
 
         f32x16 sacc[2][JN];
 #pragma unroll
@@ -142,9 +148,11 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 
         // Online softmax in base 2 on unscaled scores: the running max m is kept unscaled and
         // p = 2^(c s - c m) with c = log2(e)/sqrt(hd), one FMA per score.  Only a block that
-        // reaches past a query of this wave (the diagonal) or past Tn needs the mask.  Row
-        // index of register r in a 32x32 output tile: 8*(r/4) + 4*hh + (r%4).
-        const bool need_mask = (k0 + KB - 1 > q0w) || (k0 + KB > Tn);  // wave-uniform
+        // reaches past a query of this wave (the diagonal), past Tn, or before the window
+        // start of a query of this wave needs the mask.  A query whose keys in the blocks
+        // so far are all masked keeps an empty state (m = -inf, reference 0).  Row index of
+        // register r in a 32x32 output tile: 8*(r/4) + 4*hh + (r%4).
+        const bool need_mask = (k0 + KB - 1 > q0w) || (k0 + KB > Tn) || (k0 < qlast_w - win);  // wave-uniform
 #pragma unroll
         for (int jn = 0; jn < JN; ++jn) {
             const int qi = q0w + jn * 32 + l32;
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = k0 + mt * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
-                        const float v = (key <= qi && key < Tn) ? sacc[mt][jn][r] : -INFINITY;
+                        const float v = (key <= qi && key < Tn && key >= qi - win) ? sacc[mt][jn][r] : -INFINITY;
                         sacc[mt][jn][r] = v;
                         mx = fmaxf(mx, v);
                     }
@@ -167,7 +175,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
             }
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
             const float m_new = fmaxf(m_run[jn], mx);
-            const float cm = scale_log2 * m_new;
+            const float cm = (m_new == -INFINITY) ? 0.f : scale_log2 * m_new;
             const float alpha = fast_exp2(scale_log2 * m_run[jn] - cm);  // 0 on the first block
             float ls = 0.f;
 #pragma unroll
@@ -233,13 +241,15 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 }
 
 hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, const void* vtc,
-                               void* y, int B, int T, int H, int nkv, int S, hipStream_t st) {
+                               void* y, int B, int T, int H, int nkv, int S, int window,
+                               hipStream_t st) {
     if (nkv < 1 || H % nkv) return hipErrorInvalidValue;
+    const int win = (window < 0 || window >= T) ? T : window;  // T: the whole causal context
     dim3 grid((T + 255) / 256, H, B);
     const float sl = 1.4426950408889634f / sqrtf((float)hd);
 #define NC_AP(TT, HDV)                                                                          \
     NC_TLAUNCH((attn_prefill_kernel<TT, HDV, 1>), grid, dim3(512), 0, st, (const TT*)q,        \
-               (const TT*)kc, (const TT*)vtc, (TT*)y, T, H, nkv, S, sl)
+               (const TT*)kc, (const TT*)vtc, (TT*)y, T, H, nkv, S, win, sl)
     if (dt == BF16 && hd == 128) NC_AP(bf16, 128);
     else if (dt == BF16 && hd == 64) NC_AP(bf16, 64);
     else if (dt == F32 && hd == 128) NC_AP(float, 128);
@@ -251,8 +261,11 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 
 // ------------------------------------------------------------------ decode ----------
 // Split kernel.  Workgroup (chunk c, unit u = (row b, K/V head kvh)), NW = 2 or 4 waves: the
-// keys [c CK, c CK + CK) of K/V head kvh of row b, CK = 64 NW R, limited to positions
-// 0..lens[b], against the G = H / nkv query heads kvh G .. kvh G + G - 1 (G <= 16).  Wave w takes the 64-key blocks
+// keys [c CK, c CK + CK) of K/V head kvh of row b, CK = 64 NW R, limited to the visible
+// positions lo..lens[b] (lo = lens[b] - window with a window, else 0), against the
+// G = H / nkv query heads kvh G .. kvh G + G - 1 (G <= 16).  The grid's x index counts
+// chunks from the one holding lo, so only chunks with visible keys are launched work;
+// a wave's blocks wholly before lo are skipped.  Wave w takes the 64-key blocks
 // (c R + i) NW + w, i < R, one after another and keeps an online-softmax state (running
 // max, sum and o[16][hd]) across them; at the end the NW states are merged in LDS into the
 // chunk's partial state, slot c of row b (with R = 1 each wave's state is a partial of its
@@ -273,21 +286,23 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 //     added to the state of the wave whose block holds it, as one extra term from the
 //     values in LDS.
 constexpr int DEC_KPW = 64;
-// Waves per workgroup: 4, or 2 when the rows are few (more, smaller workgroups then).
-int attn_decode_waves(int B, int S) { return (long long)B * ((S + 255) / 256) >= 128 ? 4 : 2; }
-// (B here and below counts (row, K/V head) units.)
-int attn_decode_iters(int B, int S) {
+int attn_decode_span(int S, int window) { return (window < 0 || window >= S) ? S : window + 1; }
+// Waves per workgroup: 4, or 2 when the work is small (more, smaller workgroups then).
+// B here and below counts (row, K/V head) units; `span` bounds the keys a query sees.
+int attn_decode_waves(int B, int span) { return (long long)B * ((span + 255) / 256) >= 128 ? 4 : 2; }
+int attn_decode_iters(int B, int span) {
     // The largest R in {1, 2, 4} that still leaves 128 workgroups or more: a wave's blocks
     // run one after another at about one memory latency each, so longer chunks amortize
     // the QKV finish and the merge until too few workgroups are left to fill the chip
     // (measured at d12, d20 and d30 decode shapes).
-    const int nw = attn_decode_waves(B, S);
+    const int nw = attn_decode_waves(B, span);
     int r = 1;
-    while (r < 4 && (long long)B * ((S + nw * 64 * 2 * r - 1) / (nw * 64 * 2 * r)) >= 128) r *= 2;
+    while (r < 4 && (long long)B * ((span + nw * 64 * 2 * r - 1) / (nw * 64 * 2 * r)) >= 128) r *= 2;
     return r;
 }
-int attn_decode_slots(int B, int S) {
-    const int nw = attn_decode_waves(B, S), r = attn_decode_iters(B, S);
+// Slots are indexed by absolute chunk, so a unit needs as many as the whole cache has.
+int attn_decode_slots(int B, int S, int span) {
+    const int nw = attn_decode_waves(B, span), r = attn_decode_iters(B, span);
     const int ck = nw * DEC_KPW * r;
     return (S + ck - 1) / ck * (r == 1 ? nw : 1);  // one block per wave: a slot per wave
 }
@@ -313,13 +328,15 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g = lane >> 4;
-    const int c = blockIdx.x, u = blockIdx.y;  // unit u = b nkv + kvh
+    const int u = blockIdx.y;  // unit u = b nkv + kvh
     const int b = u / a.nkv, kvh = u % a.nkv;
     const int S = a.S, H = a.H, R = a.iters;
     const int G = H / a.nkv;
     const int CK = NW * DEC_KPW * R;
-    const int pos = a.lens[b];  // this step's position; keys 0..pos are visible
+    const int pos = a.lens[b];  // this step's position; keys lo..pos are visible
     if (pos < 0 || pos >= S) return;  // capacity is checked by the host; stay in bounds
+    const int lo = (a.window < 0 || a.window >= pos) ? 0 : pos - a.window;
+    const int c = blockIdx.x + lo / CK;
     const int nchunks = (pos + 1 + CK - 1) / CK;
     if (c >= nchunks) return;
     T* kb_base = (T*)a.kc + (long long)u * S * HD;
@@ -355,8 +372,11 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
             }
         }
     };
-    const bool first_live = kbeg_of(0) <= pos;
-    if (first_live) issue(kbeg_of(0));
+    // first block of this wave that reaches lo (blocks are R apart in NW 64-key steps)
+    int i0 = 0;
+    while (i0 < R && kbeg_of(i0) + DEC_KPW <= lo) ++i0;
+    const bool first_live = i0 < R && kbeg_of(i0) <= pos;
+    if (first_live) issue(kbeg_of(i0));
 
     // ---- 1. QKV finish for row b: slot j = wave + NW i (0..15 the group's query heads,
     //         padding past G; 16 key head kvh; 17 value head kvh).  All loads first, then
@@ -418,7 +438,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
     f32x4 o_run[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) o_run[i] = zero_vec<f32x4>();
-    for (int it = 0; it < R; ++it) {
+    for (int it = i0; it < R; ++it) {
         const int kbeg = kbeg_of(it);
         if (kbeg > pos) break;  // wave-uniform: this and later blocks hold no visible key
         CT kf[4][DS];
@@ -486,7 +506,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int key = kbeg + 16 * kt + 4 * g + j;
-                const float v = (key < pos) ? sacc[kt][j] * a.scale_log2 : -INFINITY;
+                const float v = (key < pos && key >= lo) ? sacc[kt][j] * a.scale_log2 : -INFINITY;
                 sacc[kt][j] = v;
                 mb = fmaxf(mb, v);
             }
@@ -604,7 +624,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
 }
 
 // Combine kernel: workgroup (head h, row b), one thread per feature d, over the row's
-// chunks (slots) of `chunk` keys:
+// chunks (slots) of `chunk` keys that hold visible keys (from the one holding lo):
 // y[b][h][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s over the row's slots.  The
 // slot statistics are loaded lane-parallel (one slot per lane), the weights go through
 // LDS, and the o_s[d] loads of consecutive slots are independent of each other.
@@ -612,7 +632,8 @@ template <typename T, int HD>
 __global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __restrict__ part,
                                                                  const int32_t* __restrict__ lens,
                                                                  T* __restrict__ y, int H, int nkv,
-                                                                 int S, int max_slots, int chunk) {
+                                                                 int S, int window, int max_slots,
+                                                                 int chunk) {
     constexpr int PSZ = 16 * (HD + 2);
     __shared__ float wts[512];
     __shared__ float stat[1];
@@ -620,13 +641,14 @@ __global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __
     const int G = H / nkv, hg = h % G;  // query head h is head hg of K/V head h / G's group
     const int pos = min(lens[b], S - 1);
     const int nsl = min((pos + 1 + chunk - 1) / chunk, 512);
+    const int s_lo = ((window < 0 || window >= pos) ? 0 : pos - window) / chunk;
     const float* prow = part + ((long long)b * nkv + h / G) * max_slots * PSZ;
     if (d < 64) {  // wave 0: max, weights and normaliser
         float mloc = -INFINITY;
-        for (int sl = d; sl < nsl; sl += 64) mloc = fmaxf(mloc, prow[(long long)sl * PSZ + hg]);
+        for (int sl = s_lo + d; sl < nsl; sl += 64) mloc = fmaxf(mloc, prow[(long long)sl * PSZ + hg]);
         const float M = wave_max(mloc);
         float lsum = 0.f;
-        for (int sl = d; sl < nsl; sl += 64) {
+        for (int sl = s_lo + d; sl < nsl; sl += 64) {
             const float w = fast_exp2(prow[(long long)sl * PSZ + hg] - M);  // 0 for empty slots
             wts[sl] = w;
             lsum += w * prow[(long long)sl * PSZ + 16 + hg];
@@ -637,7 +659,7 @@ __global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __
     __syncthreads();
     const float* po = prow + 32 + hg * HD + d;
     float o = 0.f;
-    for (int s0 = 0; s0 < nsl; s0 += 16) {  // 16 slots per batch of independent loads
+    for (int s0 = s_lo; s0 < nsl; s0 += 16) {  // 16 slots per batch of independent loads
         float t[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) t[u] = po[(long long)min(s0 + u, nsl - 1) * PSZ];
@@ -652,18 +674,24 @@ hipError_t launch_attn_decode(DType dt, const DecAttnArgs& args, void* y, hipStr
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)a.hd);
     if (a.nkv < 1 || a.H % a.nkv || a.H / a.nkv > 16) return hipErrorInvalidValue;
     const int units = a.B * a.nkv;  // (row, K/V head) pairs
-    const int nw = attn_decode_waves(units, a.S);
-    if (a.iters != attn_decode_iters(units, a.S) || a.max_slots != attn_decode_slots(units, a.S))
+    const int span = attn_decode_span(a.S, a.window);
+    const int nw = attn_decode_waves(units, span);
+    if (a.iters != attn_decode_iters(units, span) || a.max_slots < attn_decode_slots(units, a.S, span))
         return hipErrorInvalidValue;
-    dim3 g1(a.iters == 1 ? a.max_slots / nw : a.max_slots, units), g2(a.H, a.B);
+    const int ck = nw * DEC_KPW * a.iters;
+    // chunks with visible keys: all of them, or those a window of span keys can touch
+    const int all = (a.S + ck - 1) / ck;
+    const int live = span == a.S ? all : std::min(all, (span - 1 + ck - 1) / ck + 1);
+    dim3 g1(live, units), g2(a.H, a.B);
     // the combine sees slots of `chunk` keys: a wave's block when R == 1, else a chunk
-    const int chunk = a.iters == 1 ? DEC_KPW : nw * DEC_KPW * a.iters;
+    const int chunk = a.iters == 1 ? DEC_KPW : ck;
 #define NC_AD(TT, HDV)                                                                         \
     do {                                                                                       \
         if (nw == 4) NC_TLAUNCH((attn_decode_split_kernel<TT, HDV, 4>), g1, dim3(256), 0, st, a); \
         else NC_TLAUNCH((attn_decode_split_kernel<TT, HDV, 2>), g1, dim3(128), 0, st, a);     \
         NC_TLAUNCH((attn_decode_combine_kernel<TT, HDV>), g2, dim3(HDV), 0, st,                \
-                   (const float*)a.part, a.lens, (TT*)y, a.H, a.nkv, a.S, a.max_slots, chunk); \
+                   (const float*)a.part, a.lens, (TT*)y, a.H, a.nkv, a.S,              \
+                   span == a.S ? -1 : a.window, a.max_slots, chunk);                          \
     } while (0)
     if (dt == BF16 && a.hd == 128) NC_AD(bf16, 128);
     else if (dt == BF16 && a.hd == 64) NC_AD(bf16, 64);

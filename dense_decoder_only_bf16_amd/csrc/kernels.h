@@ -124,11 +124,13 @@ hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st);
 
 // Causal attention over a full prefill: q [B*T][H][hd], K/V of this layer in the cache
 // (positions 0..T-1, nkv heads; query head h reads K/V head h / (H / nkv)), y [B*T][H*hd].
+// window >= 0: a query at position p sees keys p - window .. p; window < 0: keys 0..p.
 hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, const void* vtc,
-                               void* y, int B, int T, int H, int nkv, int S, hipStream_t st);
+                               void* y, int B, int T, int H, int nkv, int S, int window,
+                               hipStream_t st);
 
 // Decode attention for one step, one query per row at position lens[b] (keys
-// 0..lens[b]).  The split kernel first finishes the row's raw QKV product (norm scale,
+// 0..lens[b], or lens[b] - window .. lens[b] with a window >= 0).  The split kernel first finishes the row's raw QKV product (norm scale,
 // RoPE, QK-norm) and stores the new key/value into the cache, then reduces each chunk of
 // keys to a partial softmax state; the combine kernel merges a row's partials into
 // y, [B][H hd] stored blocked (blocked_index, rows rounded up to 32).  The combine reads lens[b] to know the chunk count.
@@ -141,13 +143,17 @@ struct DecAttnArgs {
     void* kc; void* vtc;  // this layer's cache: K [B][nkv][S][hd], V^T [B][nkv][hd][S]
     float* part;          // [B nkv][max_slots][16 (hd + 2)]
     int B, H, hd, S, nkv; // query heads H = nkv G, G <= 16 per K/V head
-    int iters;            // 64-key blocks per wave: attn_decode_iters(B nkv, S)
-    int max_slots;        // attn_decode_slots(B nkv, S)
+    int window;           // sliding window (< 0: the whole causal context)
+    int iters;            // 64-key blocks per wave: attn_decode_iters(B nkv, span)
+    int max_slots;        // partial slots per unit, >= attn_decode_slots(B nkv, S, span)
     float scale_log2;     // set by the launcher
 };
-// For `rows` (row, K/V head) units over a cache of S positions:
-int attn_decode_iters(int rows, int S);  // 64-key blocks per wave
-int attn_decode_slots(int rows, int S);  // partial slots per unit
+// Keys a query can see at most: min(S, window + 1), or S without a window.
+int attn_decode_span(int S, int window);
+// For `rows` (row, K/V head) units over a cache of S positions of which at most `span`
+// are visible to a query:
+int attn_decode_iters(int rows, int span);         // 64-key blocks per wave
+int attn_decode_slots(int rows, int S, int span);  // partial slots per unit
 hipError_t launch_attn_decode(DType dt, const DecAttnArgs& a, void* y, hipStream_t st);
 
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st);

@@ -94,14 +94,15 @@ struct nc_model {
     std::vector<Layer> layers;
     float* rope_cos = nullptr;
     float* rope_sin = nullptr;
+    std::vector<int> windows;  // per-layer sliding window, -1: the whole causal context
     int live_kv = 0;
 };
 
 struct nc_kv {
     nc_model* m;
     int B, max_seq, S;  // S: allocated positions per row (stride), multiple of 64
-    void* kcache = nullptr;  // [L][B][S][hd]
-    void* vcache = nullptr;  // [L][B][hd][S]
+    void* kcache = nullptr;  // [L][B][nkv][S][hd]
+    void* vcache = nullptr;  // [L][B][nkv][hd][S]
     int32_t* lens_dev = nullptr;
     std::vector<int32_t> lens_host;
     // workspace, sized for `cap_m` token rows
@@ -111,7 +112,7 @@ struct nc_kv {
     void* act = nullptr;      // [M][d] dtype copy of x
     float* ss_a = nullptr;    // [parts][M] sums of squares feeding the QKV / LM-head norm
     float* ss_b = nullptr;    // [parts][M] sums of squares feeding the MLP norm
-    float* qkv = nullptr;     // [splits][M][(H+2) hd] raw products
+    float* qkv = nullptr;     // [M][(H+2 nkv) hd] raw products
     void* q = nullptr;        // [M][H][hd]
     void* y = nullptr;        // [M][H hd] attention output
     void* u = nullptr;        // [M][d_ff] MLP hidden
@@ -121,6 +122,7 @@ struct nc_kv {
     float* dpart = nullptr;   // decode projections with more than 32 rows: split-K partials
     long long dpart_elems = 0;
     long long apart_elems = 0;
+    int apart_slots = 0;      // partial slots per (row, K/V head) unit, the most any layer needs
     // decode step captured as a HIP graph, keyed by the caller's token/logit buffers
     bool use_graph = true;
     hipStream_t cap_stream = nullptr;
@@ -186,7 +188,11 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
     }
     {
         const int units = kv->B * c.n_kv_head;  // (row, K/V head) pairs of decode attention
-        kv->apart_elems = (long long)units * attn_decode_slots(units, kv->S) * 16 * (c.head_dim + 2);
+        int slots = 0;
+        for (int l = 0; l < c.n_layer; ++l)
+            slots = std::max(slots, attn_decode_slots(units, kv->S, attn_decode_span(kv->S, kv->m->windows[l])));
+        kv->apart_slots = slots;
+        kv->apart_elems = (long long)units * slots * 16 * (c.head_dim + 2);
     }
     WS_ALLOC(kv->apart, kv->apart_elems * 4);
     {   // split-K partials of the decode projections (M = batch rows)
@@ -316,7 +322,6 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
     const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab, nkv = c.n_kv_head;
     const int nqkv = (H + 2 * nkv) * hd;
     const size_t per_layer = (size_t)B * nkv * kv->S * hd * m->esz;
-    const int max_slots = attn_decode_slots(B * nkv, kv->S);
     const int parts_d = (d + dec_gemm_tile_n() - 1) / dec_gemm_tile_n();
     const int ss = (int)kv->cap_m;
     nc_status s;
@@ -338,14 +343,16 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         at.qkv = kv->qkv; at.ss_in = kv->ss_a; at.ss_in_parts = ss_a_parts; at.ss_stride = ss;
         at.norm_dim = d; at.eps = c.norm_eps; at.rope_cos = m->rope_cos; at.rope_sin = m->rope_sin;
         at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = kv->apart;
-        at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.nkv = nkv; at.max_slots = max_slots;
-        at.iters = attn_decode_iters(B * nkv, kv->S);
-        {   // bytes: the K/V read for every row (positions 0..lens_b, the new one
+        at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.nkv = nkv; at.max_slots = kv->apart_slots;
+        at.window = m->windows[l];
+        at.iters = attn_decode_iters(B * nkv, attn_decode_span(kv->S, at.window));
+        {   // bytes: the K/V read for every row (its visible positions, the new one
             // included) of each K/V head, q/k/v in fp32, y out; flops 4 hd per
             // (query head, key) pair
             const double es = (double)m->esz;
             double keys = 0;
-            for (int b = 0; b < B; ++b) keys += kv->lens_host[b] + 1;
+            for (int b = 0; b < B; ++b)
+                keys += at.window < 0 ? kv->lens_host[b] + 1 : std::min(kv->lens_host[b], at.window) + 1;
             const double by = keys * nkv * hd * 2 * es + (double)B * nqkv * 4 + (double)B * H * hd * es;
             LAUNCH(timed(NC_KC_DECODE_ATTN, by, 4.0 * H * hd * keys, st,
                          [&] { return launch_attn_decode(m->dt, at, kv->y, st); }, 2));
@@ -410,6 +417,7 @@ nc_status nc_model_create(const nc_config* cfg, const void* const* weights, nc_m
 
         nc_model* m = new nc_model();
         m->cfg = *cfg;
+        m->windows.assign(cfg->n_layer, -1);
         m->dt = cfg->dtype == NC_BF16 ? BF16 : F32;
         m->esz = cfg->dtype == NC_BF16 ? 2 : 4;
         m->device = dev;
@@ -494,6 +502,19 @@ void nc_model_free(nc_model* m) {
     if (m->rope_cos) (void)hipFree(m->rope_cos);
     if (m->rope_sin) (void)hipFree(m->rope_sin);
     delete m;
+}
+
+nc_status nc_model_set_windows(nc_model* m, const int32_t* windows) {
+    try {
+        if (!m || !windows) return fail(NC_ERR_INVALID_ARG, "NULL argument");
+        if (m->live_kv != 0) return fail(NC_ERR_STATE, "windows can only change while the model has no kv object");
+        std::vector<int> w(windows, windows + m->cfg.n_layer);
+        for (int& x : w) x = x < 0 ? -1 : x;
+        m->windows = std::move(w);
+        return NC_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(NC_ERR_OOM, "host allocation failed");
+    }
 }
 
 nc_status nc_kv_create(nc_model* m, int32_t batch, int32_t max_seq, nc_kv** out) {
@@ -627,10 +648,14 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             qa.S = kv->S; qa.eps = c.norm_eps;
             LAUNCH(launch_qkv_post(m->dt, qa, st));
             {   // causal attention flops: 4 hd per visible (query, key) pair and head
-                const double fl = 4.0 * B * H * hd * (double)T * (T + 1) / 2.0;
+                const int w = m->windows[l];
+                const double Td = T, vis = (w < 0 || w + 1 >= T)
+                                               ? Td * (Td + 1) / 2.0
+                                               : (w + 1.0) * (w + 2.0) / 2.0 + (Td - w - 1.0) * (w + 1.0);
+                const double fl = 4.0 * B * H * hd * vis;
                 const double by = (double)B * T * (H + 2 * nkv + H) * hd * m->esz;  // q, k, v in; y out
                 LAUNCH(timed(NC_KC_PREFILL_ATTN, by, fl, st, [&] {
-                    return launch_attn_prefill(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->y, B, T, H, nkv, kv->S, st);
+                    return launch_attn_prefill(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->y, B, T, H, nkv, kv->S, w, st);
                 }));
             }
             // O product + residual

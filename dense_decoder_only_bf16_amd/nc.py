@@ -36,7 +36,7 @@ NC_KC_PREFILL_GEMM = 2
 NC_KC_PREFILL_ATTN = 3
 NC_KC_DECODE_ATTN = 4
 
-EXPORTED = ("nc_model_create", "nc_model_free", "nc_kv_create", "nc_kv_free", "nc_kv_set_lens",
+EXPORTED = ("nc_model_create", "nc_model_free", "nc_model_set_windows", "nc_kv_create", "nc_kv_free", "nc_kv_set_lens",
             "nc_kv_get_lens", "nc_kv_export", "nc_prefill", "nc_decode_step", "nc_argmax",
             "nc_timing_enable", "nc_timing_read", "nc_last_error", "nc_abi_version")
 
@@ -76,6 +76,7 @@ def lib():
         L.nc_model_create.argtypes = [ctypes.POINTER(nc_config), ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.nc_model_free.argtypes = [vp]
         L.nc_model_free.restype = None
+        L.nc_model_set_windows.argtypes = [vp, ctypes.POINTER(i32)]
         L.nc_kv_create.argtypes = [vp, i32, i32, ctypes.POINTER(vp)]
         L.nc_kv_free.argtypes = [vp]
         L.nc_kv_free.restype = None
@@ -91,7 +92,7 @@ def lib():
         L.nc_last_error.restype = ctypes.c_char_p
         L.nc_abi_version.argtypes = []
         L.nc_abi_version.restype = i32
-        for name in ("nc_model_create", "nc_kv_create", "nc_kv_set_lens", "nc_kv_get_lens",
+        for name in ("nc_model_create", "nc_model_set_windows", "nc_kv_create", "nc_kv_set_lens", "nc_kv_get_lens",
                      "nc_kv_export", "nc_prefill", "nc_decode_step", "nc_argmax",
                      "nc_timing_enable", "nc_timing_read"):
             getattr(L, name).restype = st
@@ -149,6 +150,20 @@ def nc_model_create(cfg, weights):
 
 def nc_model_free(m):
     lib().nc_model_free(m)
+
+
+def nc_model_set_windows(m, windows):
+    a = np.ascontiguousarray(windows, dtype=np.int32)
+    _check(lib().nc_model_set_windows(m, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+
+
+def layer_windows(pattern, n_layer, short_window):
+    """Per-layer windows for nc_model_set_windows from a pattern such as "SSSL": layer l
+    takes pattern[l % len(pattern)], 'S' = short_window, 'L' = -1 (whole context)."""
+    table = {"S": int(short_window), "L": -1}
+    if not pattern or any(ch not in table for ch in pattern):
+        raise ValueError(f"window pattern {pattern!r} must be a non-empty string of S and L")
+    return [table[pattern[i % len(pattern)]] for i in range(n_layer)]
 
 
 def nc_kv_create(m, batch, max_seq):
@@ -210,12 +225,14 @@ def upload_weights(weights_list, dtype, device="cuda"):
 class Model:
     """Owning wrapper: model handle + its KV caches."""
 
-    def __init__(self, shape, weights_list, max_seq=None, device="cuda"):
+    def __init__(self, shape, weights_list, max_seq=None, device="cuda", windows=None):
         self.shape = shape
         self.cfg = make_config(shape, max_seq)
         dev = upload_weights(weights_list, shape.dtype, device)
         self.handle = nc_model_create(self.cfg, dev)
         del dev
+        if windows is not None:
+            nc_model_set_windows(self.handle, windows)
 
     def new_kv(self, batch, max_seq):
         return KV(self, batch, max_seq)

@@ -98,6 +98,14 @@ nc_status nc_model_create(const nc_config* cfg, const void* const* weights_dev,
                           nc_model** out);
 void nc_model_free(nc_model* m); /* NULL is a no-op; all kv objects must be freed first */
 
+/* Sliding-window attention per layer (the later version's configurable pattern of short
+ * and long windows, apidog.com/th guide, part 1 architecture features; the window size
+ * argument of the attention call, part 5).  windows_host: n_layer int32 values; for
+ * w >= 0 a query at position p of that layer attends to keys p - w .. p only, w < 0 to
+ * the whole causal context 0..p (the default of a new model).  Allowed only while the
+ * model has no nc_kv object (NC_ERR_STATE otherwise); copies the values. */
+nc_status nc_model_set_windows(nc_model* m, const int32_t* windows_host);
+
 /* KV cache for `batch` rows of up to `max_seq` positions (max_seq <= cfg.max_seq, and at
  * most 32768: NC_ERR_UNSUPPORTED otherwise).
  * Layout (library-private): K [L][batch][n_kv_head][max_seq][hd], V transposed

@@ -12,8 +12,8 @@ def torch_mod():
     return torch
 
 
-def gpu_model(shape, weights, max_seq=None):
-    return nc.Model(shape, canonical_list(weights), max_seq=max_seq)
+def gpu_model(shape, weights, max_seq=None, windows=None):
+    return nc.Model(shape, canonical_list(weights), max_seq=max_seq, windows=windows)
 
 
 def prefill(model, tokens, max_seq, logits=True):
@@ -46,3 +46,12 @@ def report(tag, got, want):
     agr = agreement(got, want)
     print(f"[{tag}] max_abs={err:.3e} argmax_agree={agr:.4f} n={got.shape[:-1]}", flush=True)
     return err, agr
+
+
+def assert_flips_are_near_ties(got, want, err):
+    """Every argmax disagreement must be a near tie of the reference: its top two logits
+    closer than twice the measured error, so rounding within the bound explains it (used
+    where too few positions are checked for a percentage bar to mean anything)."""
+    srt = np.sort(want, -1)
+    flip = np.argmax(got, -1) != np.argmax(want, -1)
+    assert not np.any(flip & (srt[..., -1] - srt[..., -2] >= 2 * err)), "argmax flip beyond the error"

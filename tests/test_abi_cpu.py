@@ -111,6 +111,7 @@ def test_null_handles_are_rejected(L):
     assert L.nc_kv_set_lens(None, None) == nc.NC_ERR_INVALID_ARG
     assert L.nc_kv_get_lens(None, None) == nc.NC_ERR_INVALID_ARG
     assert L.nc_kv_export(None, 0, None, None, None) == nc.NC_ERR_INVALID_ARG
+    assert L.nc_model_set_windows(None, None) == nc.NC_ERR_INVALID_ARG
     L.nc_model_free(None)
     L.nc_kv_free(None)
 
@@ -125,3 +126,11 @@ def test_header_constants_match_binding():
             assert nc.nc_abi_version() == int(val) if os.path.exists(nc.LIB_PATH) else True
             continue
         assert getattr(nc, name) == int(val), name
+
+
+def test_layer_windows_helper():
+    assert nc.layer_windows("SSSL", 5, 256) == [256, 256, 256, -1, 256]
+    with pytest.raises(ValueError):
+        nc.layer_windows("SQ", 2, 8)
+    with pytest.raises(ValueError):
+        nc.layer_windows("", 2, 8)

@@ -15,7 +15,8 @@ from dense_decoder_only_bf16_amd.inputs import (TINY, Shape, make_tokens, make_w
                                                 make_lens)
 from oracle import OracleModel
 
-from gpu_helpers import agreement, decode, gpu_model, prefill, report, torch_mod
+from gpu_helpers import (agreement, assert_flips_are_near_ties, decode, gpu_model, prefill,
+                         report, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -373,6 +374,88 @@ def test_bf16_gqa_decode_many_rows(B):
         seq = np.concatenate([toks[b, :lens[b]], toks[b, T:T + steps]])[None]
         want[b] = orc.prefill(seq, logits_at=np.arange(lens[b], lens[b] + steps))[0][0]
     err, agr = report(f"gqa decode B={B}", got, want)
+    assert err <= BF16_TOL  # 2 B positions: each argmax disagreement must be a near tie
+    assert_flips_are_near_ties(got, want, err)
+    kv.close()
+    gm.close()
+
+
+# ---------------------------------------------------------------- sliding windows ------
+def test_fp32_windows_prefill_and_decode():
+    """Sliding windows in fp32 (layer 0: 7 keys back, layer 1: the whole context) over a
+    prefill that spans several 64-key blocks, then decode steps, at the fp32 bar."""
+    shape = replace(TINY, max_seq=160)
+    wins = [7, -1]
+    w = make_weights(shape, seed=50)
+    orc = OracleModel(shape, w, windows=wins)
+    gm = gpu_model(shape, w, windows=wins)
+    B, T, steps = 2, 150, 6
+    toks = make_tokens(shape.vocab, B, T + steps, seed=51)
+    want, _ = orc.prefill(toks)
+    kv, got = prefill(gm, toks[:, :T], shape.max_seq)
+    err, _ = report("tiny windows prefill", got, want[:, :T])
+    assert err <= F32_TOL
+    got = np.stack([decode(gm, kv, toks[:, T + s]) for s in range(steps)], axis=1)
+    err, _ = report("tiny windows decode", got, want[:, T:T + steps])
+    assert err <= F32_TOL
+    kv.close()
+    gm.close()
+
+
+SSSL = Shape("sssl", n_layer=4, d_model=512, n_head=4, head_dim=128, d_ff=1024, vocab=500,
+             dtype="bf16", max_seq=640, n_kv_head=2)
+
+
+@pytest.mark.parametrize("short", [0, 70, 300])
+def test_bf16_window_pattern_prefill(short):
+    """Pattern SSSL with short windows of 0 keys back (each query sees itself only), 70
+    (not a block multiple) and 300 (longer than a 256-query tile) over a 520-token prefill."""
+    wins = nc.layer_windows("SSSL", SSSL.n_layer, short)
+    w = make_weights(SSSL, seed=52)
+    orc = OracleModel(SSSL, w, windows=wins)
+    gm = gpu_model(SSSL, w, windows=wins)
+    toks = make_tokens(SSSL.vocab, 2, 520, seed=53)
+    want, _ = orc.prefill(toks)
+    kv, got = prefill(gm, toks, SSSL.max_seq)
+    err, agr = report(f"sssl w={short} prefill", got, want)
     assert err <= BF16_TOL and agr >= AGREE
     kv.close()
+    gm.close()
+
+
+@pytest.mark.parametrize("B", [3, 40])
+def test_bf16_window_pattern_decode_many_rows(B):
+    """SSSL decode with a 100-key short window at mixed context lengths up to 600: the
+    split kernel launches only the chunks the window touches (B = 40: 80 units, 4 waves
+    merged in LDS; B = 3: one block per wave); every row is checked."""
+    wins = nc.layer_windows("SSSL", SSSL.n_layer, 100)
+    w = make_weights(SSSL, seed=54)
+    orc = OracleModel(SSSL, w, windows=wins)
+    gm = gpu_model(SSSL, w, windows=wins)
+    T, steps = 600, 2
+    toks = make_tokens(SSSL.vocab, B, T + steps, seed=55 + B)
+    lens = make_lens(B, 1, T, seed=56 + B)
+    kv, _ = prefill(gm, toks[:, :T], SSSL.max_seq, logits=False)
+    kv.set_lens(lens)
+    got = np.stack([decode(gm, kv, toks[:, T + s]) for s in range(steps)], axis=1)
+    want = np.empty_like(got, dtype=np.float64)
+    for b in range(B):
+        seq = np.concatenate([toks[b, :lens[b]], toks[b, T:T + steps]])[None]
+        want[b] = orc.prefill(seq, logits_at=np.arange(lens[b], lens[b] + steps))[0][0]
+    err, agr = report(f"sssl decode B={B}", got, want)
+    assert err <= BF16_TOL  # 2 B positions: each argmax disagreement must be a near tie
+    assert_flips_are_near_ties(got, want, err)
+    kv.close()
+    gm.close()
+
+
+def test_windows_only_change_without_kv():
+    w = make_weights(SMALL_BF16, seed=57)
+    gm = gpu_model(SMALL_BF16, w)
+    kv = gm.new_kv(1, 16)
+    with pytest.raises(nc.NcError) as e:
+        nc.nc_model_set_windows(gm.handle, [4, -1])
+    assert e.value.code == nc.NC_ERR_STATE
+    kv.close()
+    nc.nc_model_set_windows(gm.handle, [4, -1])
     gm.close()
