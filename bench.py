@@ -9,7 +9,11 @@ uniform random token ids.  Other workloads (d20: prefill 32 x 2048 and 128 decod
 context lengths uniform in [256, 2048]; tiny) build a separate decode context outside the
 timed steps.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload d12|d20|d26|d30|tiny] [--no-cpu]
+Workloads d20-gqa (5 K/V heads) and d20-sssl (an SSSL pattern of 512-key sliding
+windows) run the d20 step with the later version's attention options.
+
+    python bench.py [--steps K] [--warmup W] [--workload d12|d20|d26|d30|d20-gqa|d20-sssl|tiny]
+                    [--no-cpu]
 """
 
 from __future__ import annotations
@@ -39,7 +43,7 @@ def parse():
     return p.parse_args()
 
 
-def cpu_baseline(shape, weights, wl, budget_s):
+def cpu_baseline(shape, weights, wl, budget_s, windows=None):
     """Time the fp64 oracle on the host on a bounded sample of the same workload.
 
     Sample: one row; prefill of min(T, 2048) tokens, then greedy decode steps until the
@@ -52,7 +56,7 @@ def cpu_baseline(shape, weights, wl, budget_s):
     except Exception:  # noqa: BLE001
         threads = len(os.sched_getaffinity(0))
     from dense_decoder_only_bf16_amd.inputs import make_tokens
-    orc = OracleModel(shape, weights)
+    orc = OracleModel(shape, weights, windows=windows)
     t_pre = min(wl.prefill_len or wl.decode_context, 2048)  # decode-only: its context
     prompt = make_tokens(shape.vocab, 1, t_pre, seed=1)
     t0 = time.perf_counter()
@@ -190,7 +194,9 @@ def main():
         steps = args.decode_steps
     shared = Bp > 0 and Bd == Bp  # decode continues the prefilled rows
     weights = make_weights(shape, seed=0)
-    model = nc.Model(shape, canonical_list(weights), max_seq=shape.max_seq)
+    windows = (nc.layer_windows(wl.window_pattern, shape.n_layer, wl.short_window)
+               if wl.window_pattern else None)
+    model = nc.Model(shape, canonical_list(weights), max_seq=shape.max_seq, windows=windows)
     stream = torch.cuda.current_stream()
     V = shape.vocab
 
@@ -253,9 +259,12 @@ def main():
     dec_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
     ms_per_step = wall * 1000.0 / args.steps
     n_pre, n_dec = Bp * T, Bd * steps
+    kvh = f"{shape.n_kv_head} K/V head" + ("s" if shape.n_kv_head > 1 else "")
+    win = (f", windows {wl.window_pattern} with {wl.short_window}-key short windows"
+           if wl.window_pattern else "")
     desc = (f"{args.workload} ({shape.n_layer} layers, d {shape.d_model}, {shape.n_head}x"
-            f"{shape.head_dim} query heads, 1 K/V head, MLP {shape.d_ff}, vocab {V}, "
-            f"{shape.dtype}):")
+            f"{shape.head_dim} query heads, {kvh}, MLP {shape.d_ff}, vocab {V}, "
+            f"{shape.dtype}{win}):")
     if Bp:
         desc += f" prefill {Bp}x{T} with fp32 logits at every position"
     if steps:
@@ -283,7 +292,7 @@ def main():
     if not args.no_roofline:
         out["roofline"], out["kernels"] = roofline(nc, one_step, shape.dtype, args.workload)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(shape, weights, wl, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(shape, weights, wl, args.cpu_seconds, windows)
     for kv in {id(k): k for k in (kv_p, kv_d) if k is not None}.values():
         kv.close()
     model.close()

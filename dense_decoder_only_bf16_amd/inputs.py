@@ -48,6 +48,8 @@ class Workload:
     decode_steps: int
     decode_context: int          # context length before the first decode step
     mixed_lengths: bool = False  # per-row context lengths drawn from U{256..2048}
+    window_pattern: str = ""     # per-layer sliding windows, e.g. "SSSL" ("" = none)
+    short_window: int = 0        # window of the pattern's S layers (keys back)
 
 
 def from_depth(depth, vocab=65536, dtype="bf16", max_seq=2048, name=None):
@@ -68,6 +70,11 @@ WORKLOADS = {
     "d20": Workload(D20, 32, 2048, 64, 128, 2048),
     "d26": Workload(D26, 16, 2048, 0, 0, 0),
     "d30": Workload(D30, 0, 0, 128, 256, 2048, mixed_lengths=True),
+    # the later version's attention options on the d20 model and run: 5 K/V heads (groups
+    # of 2 query heads), and an SSSL window pattern with 512-key short windows
+    "d20-gqa": Workload(replace(D20, name="d20-gqa", n_kv_head=5), 32, 2048, 64, 128, 2048),
+    "d20-sssl": Workload(replace(D20, name="d20-sssl"), 32, 2048, 64, 128, 2048,
+                         window_pattern="SSSL", short_window=512),
 }
 
 

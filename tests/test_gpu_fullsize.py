@@ -15,8 +15,8 @@ import numpy as np
 import pytest
 
 from dense_decoder_only_bf16_amd import nc
-from dense_decoder_only_bf16_amd.inputs import (D12, D20, D26, D30, canonical_list, make_lens,
-                                                make_tokens, make_weights)
+from dense_decoder_only_bf16_amd.inputs import (D12, D20, D26, D30, WORKLOADS, canonical_list,
+                                                make_lens, make_tokens, make_weights)
 from oracle import OracleModel
 
 from gpu_helpers import torch_mod
@@ -46,11 +46,11 @@ def check(tag, got, want):
 
 
 class Run:
-    def __init__(self, shape):
+    def __init__(self, shape, windows=None):
         self.shape = shape
         self.w = make_weights(shape, seed=0)
-        self.model = nc.Model(shape, canonical_list(self.w), max_seq=shape.max_seq)
-        self.orc = OracleModel(shape, self.w)
+        self.model = nc.Model(shape, canonical_list(self.w), max_seq=shape.max_seq, windows=windows)
+        self.orc = OracleModel(shape, self.w, windows=windows)
 
     def close(self):
         self.model.close()
@@ -175,3 +175,39 @@ def test_d30_decode_mixed_lengths():
         seq = np.concatenate([toks[b, :n], toks[b, T:T + steps]])[None]
         want, _ = r.orc.prefill(seq, logits_at=np.arange(n, n + steps))
         check(f"d30 decode row {b} (context {n})", np.stack(got[b]), want[0])
+
+
+@pytest.mark.parametrize("name", ["d20-gqa", "d20-sssl"])
+def test_d20_attention_variants(name):
+    """The d20 step with 5 K/V heads, or with SSSL 512-key windows: prefill 32 x 2048 in the
+    benchmark's launch shape (row 0 checked over its first 768 positions, past the first
+    window), then the rows truncated to lengths in 600..900 and two decode steps."""
+    torch = torch_mod()
+    wl = WORKLOADS[name]
+    shape = wl.shape
+    wins = (nc.layer_windows(wl.window_pattern, shape.n_layer, wl.short_window)
+            if wl.window_pattern else None)
+    r = Run(shape, wins)
+    B, T, steps = 32, 2048, 2
+    toks = make_tokens(shape.vocab, B, T + steps, seed=3)
+    kv = r.model.new_kv(B, shape.max_seq)
+    logits = torch.empty((B, T, shape.vocab), device="cuda", dtype=torch.float32)
+    kv.prefill(torch.from_numpy(np.ascontiguousarray(toks[:, :T])).cuda(), logits)
+    torch.cuda.synchronize()
+    g0 = logits[0, :768].cpu().numpy()
+    del logits
+    lens = make_lens(B, 600, 900, seed=4)
+    kv.set_lens(lens)
+    dec = torch.empty((B, shape.vocab), device="cuda", dtype=torch.float32)
+    got = []
+    for s in range(steps):
+        kv.decode(torch.from_numpy(np.ascontiguousarray(toks[:, T + s])).cuda(), dec)
+        got.append(dec[17].cpu().numpy())
+    kv.close()
+    r.close()
+    w0, _ = r.orc.prefill(toks[0:1, :768])
+    check(f"{name} prefill row 0 (first 768)", g0, w0[0])
+    n = int(lens[17])
+    seq = np.concatenate([toks[17, :n], toks[17, T:T + steps]])[None]
+    want, _ = r.orc.prefill(seq, logits_at=np.arange(n, n + steps))
+    check(f"{name} decode row 17 (context {n})", np.stack(got), want[0])
