@@ -27,14 +27,17 @@ namespace nc {
 // (measured 1.35x faster than 4 waves of 64 queries at the d12 and d20 prefill shapes).  K/V advance in blocks of 64 keys staged in
 // LDS; blocks past the last query of the workgroup, or before the window of its first
 // query, are never loaded, and a wave whose queries all precede a block, or whose windows
-// all start after it, skips its MFMAs.  Sliding window: a query at position p sees keys
-// p - win .. p (win >= Tn: the whole causal context).
+// all start after it, skips its MFMAs.  Query i of row b sits at position off + i (off =
+// offs[b]: the tokens already in the row's cache, 0 for a first prefill) and keys are
+// cache positions.  Sliding window: a query at position p sees keys p - win .. p (win
+// = 2^30: the whole causal context).
 template <typename T, int HD, int JN>
 __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __restrict__ q,
                                                            const T* __restrict__ kc,
                                                            const T* __restrict__ vtc,
                                                            T* __restrict__ y, int Tn, int H,
                                                            int nkv, int S, int win,
+                                                           const int32_t* __restrict__ offs,
                                                            float scale_log2) {
     typedef typename Chunk<T>::type CT;
     typedef typename Chunk<T>::half HT;
@@ -52,6 +55,8 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
     const int head = blockIdx.y, b = blockIdx.z;
     const int q0 = qb * BQ;
     const int q0w = q0 + wave * 32 * JN;
+    const int off = offs ? offs[b] : 0;  // position of query 0
+    const int Kn = off + Tn;             // keys in the cache after this prefill
 
     const int kvh = head / (H / nkv);  // the K/V head this query head reads
     const T* kb_base = kc + ((long long)b * nkv + kvh) * S * HD;
@@ -81,34 +86,35 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
         l_run[jn] = 0.f;
     }
 
-    const int kend = min(Tn, q0 + BQ);
+    const int kend = off + min(Tn, q0 + BQ);
     const int nkb = (kend + KB - 1) / KB;
-    const int kb_first = max(0, q0 - win) / KB;  // earliest key any query here sees
-    const int qlast_w = q0w + 32 * JN - 1;        // last query of this wave
+    const int kb_first = max(0, off + q0 - win) / KB;  // earliest key any query here sees
+    const int p0w = off + q0w;                          // position of this wave's first query
+    const int plast_w = p0w + 32 * JN - 1;              // and of its last
     constexpr int KCH = KB * CPRK / NT;  // K chunks per thread
     constexpr int VCH = HD * (KB / 8) / NT;
     static_assert(KCH >= 1 && VCH >= 1, "block too small for the workgroup");
 
-    // K/V block k0 into registers (zeros past Tn), then into LDS.
+    // K/V block k0 into registers (zeros past Kn), then into LDS.
     CT rk[KCH], rv[VCH];
     auto gload = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
             int c = tid + i * NT, key = c / CPRK, ch = c % CPRK;
-            const int kk = min(k0 + key, Tn - 1);
-            rk[i] = load_masked(kb_base + (long long)kk * HD + ch * 8, k0 + key < Tn);
+            const int kk = min(k0 + key, Kn - 1);
+            rk[i] = load_masked(kb_base + (long long)kk * HD + ch * 8, k0 + key < Kn);
         }
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             int c = tid + i * NT, d = c / (KB / 8), ch = c % (KB / 8);
             const T* src = vb_base + (long long)d * S + k0 + ch * 8;
-            if (k0 + ch * 8 + 8 <= Tn) {
+            if (k0 + ch * 8 + 8 <= Kn) {
                 rv[i] = *(const CT*)src;
             } else {
                 CT t = zero_vec<CT>();
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    if (k0 + ch * 8 + e < Tn) t[e] = src[e];
+                    if (k0 + ch * 8 + e < Kn) t[e] = src[e];
                 rv[i] = t;
             }
         }
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
         __syncthreads();
 
         // every query of this wave precedes the block, or its window starts after it
-        if (k0 > qlast_w || k0 + KB - 1 < q0w - win) continue;
+        if (k0 > plast_w || k0 + KB - 1 < p0w - win) continue;
 
         f32x16 sacc[2][JN];
 #pragma unroll
@@ -148,14 +154,14 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 
         // Online softmax in base 2 on unscaled scores: the running max m is kept unscaled and
         // p = 2^(c s - c m) with c = log2(e)/sqrt(hd), one FMA per score.  Only a block that
-        // reaches past a query of this wave (the diagonal), past Tn, or before the window
+        // reaches past a query of this wave (the diagonal), past Kn, or before the window
         // start of a query of this wave needs the mask.  A query whose keys in the blocks
         // so far are all masked keeps an empty state (m = -inf, reference 0).  Row index of
         // register r in a 32x32 output tile: 8*(r/4) + 4*hh + (r%4).
-        const bool need_mask = (k0 + KB - 1 > q0w) || (k0 + KB > Tn) || (k0 < qlast_w - win);  // wave-uniform
+        const bool need_mask = (k0 + KB - 1 > p0w) || (k0 + KB > Kn) || (k0 < plast_w - win);  // wave-uniform
 #pragma unroll
         for (int jn = 0; jn < JN; ++jn) {
-            const int qi = q0w + jn * 32 + l32;
+            const int qp = p0w + jn * 32 + l32;  // the query's position
             float mx = -INFINITY;
             if (need_mask) {
 #pragma unroll
@@ -163,7 +169,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = k0 + mt * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
-                        const float v = (key <= qi && key < Tn && key >= qi - win) ? sacc[mt][jn][r] : -INFINITY;
+                        const float v = (key <= qp && key < Kn && key >= qp - win) ? sacc[mt][jn][r] : -INFINITY;
                         sacc[mt][jn][r] = v;
                         mx = fmaxf(mx, v);
                     }
@@ -242,14 +248,14 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 
 hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, const void* vtc,
                                void* y, int B, int T, int H, int nkv, int S, int window,
-                               hipStream_t st) {
+                               const int32_t* offs, hipStream_t st) {
     if (nkv < 1 || H % nkv) return hipErrorInvalidValue;
-    const int win = (window < 0 || window >= T) ? T : window;  // T: the whole causal context
+    const int win = (window < 0 || window >= S) ? (1 << 30) : window;  // 2^30: whole context
     dim3 grid((T + 255) / 256, H, B);
     const float sl = 1.4426950408889634f / sqrtf((float)hd);
 #define NC_AP(TT, HDV)                                                                          \
     NC_TLAUNCH((attn_prefill_kernel<TT, HDV, 1>), grid, dim3(512), 0, st, (const TT*)q,        \
-               (const TT*)kc, (const TT*)vtc, (TT*)y, T, H, nkv, S, win, sl)
+               (const TT*)kc, (const TT*)vtc, (TT*)y, T, H, nkv, S, win, offs, sl)
     if (dt == BF16 && hd == 128) NC_AP(bf16, 128);
     else if (dt == BF16 && hd == 64) NC_AP(bf16, 64);
     else if (dt == F32 && hd == 128) NC_AP(float, 128);

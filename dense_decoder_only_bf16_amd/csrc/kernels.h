@@ -106,8 +106,8 @@ hipError_t launch_embed(DType dt, const int32_t* tok, int M, const void* wte, in
 // Pre-attention finish of the raw QKV product part[z][m][(H+2 nkv)*hd] (H query heads, then
 // nkv key heads, then nkv value heads): scale row m by r_m, rotate the q and k heads at
 // position pos(m), QK-normalise, write q [m][H][hd] and k, v into the cache of the layer.
-// Position of row m: prefill (lens == nullptr) pos = m % T, row b = m / T;
-// decode (lens != nullptr) b = m, pos = lens[b].
+// Token m is token m % T of batch row b = m / T, at position pos = lens[b] + m % T (the
+// row's current length, 0 when lens is null).
 struct QkvPostArgs {
     const float* part; int splits; long long z_stride;
     int M, T, H, hd, nkv;
@@ -122,12 +122,14 @@ struct QkvPostArgs {
 };
 hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st);
 
-// Causal attention over a full prefill: q [B*T][H][hd], K/V of this layer in the cache
-// (positions 0..T-1, nkv heads; query head h reads K/V head h / (H / nkv)), y [B*T][H*hd].
-// window >= 0: a query at position p sees keys p - window .. p; window < 0: keys 0..p.
+// Causal attention of a prefill of T tokens per row: q [B*T][H][hd], the queries of row b
+// at positions off_b .. off_b + T - 1 (off_b = offs[b], or 0 when offs is null), the K/V
+// of this layer in the cache (positions 0 .. off_b + T - 1, nkv heads; query head h reads
+// K/V head h / (H / nkv)), y [B*T][H*hd].  window >= 0: a query at position p sees keys
+// p - window .. p; window < 0: keys 0..p.
 hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, const void* vtc,
                                void* y, int B, int T, int H, int nkv, int S, int window,
-                               hipStream_t st);
+                               const int32_t* offs, hipStream_t st);
 
 // Decode attention for one step, one query per row at position lens[b] (keys
 // 0..lens[b], or lens[b] - window .. lens[b] with a window >= 0).  The split kernel first finishes the row's raw QKV product (norm scale,

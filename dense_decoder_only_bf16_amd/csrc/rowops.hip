@@ -87,14 +87,8 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
     if (gw >= (long long)a.M * slots) return;
     const int m = (int)(gw / slots), j = (int)(gw % slots);
     const int half = a.hd / 2;
-    int b, pos;
-    if (a.lens) {
-        b = m;
-        pos = a.lens[b];
-    } else {
-        b = m / a.T;
-        pos = m % a.T;
-    }
+    const int b = m / a.T;
+    const int pos = m % a.T + (a.lens ? a.lens[b] : 0);
     if (pos < 0 || pos >= a.S) return;  // capacity is checked by the host; stay in bounds
     float s = 0.f;
     for (int q = 0; q < a.ss_in_parts; ++q) s += a.ss_in[(long long)q * a.ss_stride + m];

@@ -288,6 +288,14 @@ hipError_t timed(int cls, double bytes, double flops, hipStream_t st, F fn, int 
     return hipSuccess;
 }
 
+// (query, key) pairs a prefill of T tokens at positions off .. off + T - 1 attends to:
+// sum over positions p of min(p + 1, w + 1) (w < 0: p + 1).
+double visible_pairs(long long off, long long T, int w) {
+    if (w < 0) return (double)T * off + (double)T * (T + 1) / 2.0;
+    const long long n1 = std::min(std::max((long long)w - off, 0LL), T);  // positions p < w
+    return (double)n1 * off + (double)n1 * (n1 + 1) / 2.0 + (double)(T - n1) * (w + 1.0);
+}
+
 // Algorithmic bytes of a decode projection: weights, activations (both parts of a
 // compensated operand), and the epilogue's outputs (RESID also reads x; low parts where
 // written); flops 2 M N K of the model (the extra MFMAs of the low part are not counted).
@@ -615,9 +623,10 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
         if (!m || !tokens || !kv) return fail(NC_ERR_INVALID_ARG, "NULL argument");
         if (kv->m != m) return fail(NC_ERR_INVALID_ARG, "kv belongs to another model");
         if (B != kv->B) return fail(NC_ERR_INVALID_ARG, "B differs from the cache's batch");
-        if (T < 1 || T > kv->max_seq) return fail(NC_ERR_CAPACITY, "T must be in [1, kv max_seq]");
+        if (T < 1) return fail(NC_ERR_INVALID_ARG, "T must be >= 1");
         for (int b = 0; b < B; ++b)
-            if (kv->lens_host[b] != 0) return fail(NC_ERR_STATE, "prefill needs an empty cache (all lengths 0)");
+            if ((long long)kv->lens_host[b] + T > kv->max_seq)
+                return fail(NC_ERR_CAPACITY, "a row's length + T exceeds the cache's max_seq");
         const long long M = (long long)B * T;
         nc_status s = ws_ensure(kv, M);
         if (s != NC_OK) return s;
@@ -643,19 +652,24 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             QkvPostArgs qa{};
             qa.part = kv->qkv; qa.splits = 1; qa.z_stride = 0; qa.M = Mi; qa.T = T; qa.H = H; qa.hd = hd; qa.nkv = nkv;
             qa.ss_in = kv->ss_a; qa.ss_in_parts = ss_a_parts; qa.ss_stride = (int)kv->cap_m; qa.norm_dim = d;
-            qa.lens = nullptr; qa.rope_cos = m->rope_cos; qa.rope_sin = m->rope_sin;
+            qa.lens = kv->lens_dev; qa.rope_cos = m->rope_cos; qa.rope_sin = m->rope_sin;
             qa.q = kv->q; qa.kc = (char*)kv->kcache + l * per_layer; qa.vtc = (char*)kv->vcache + l * per_layer;
             qa.S = kv->S; qa.eps = c.norm_eps;
             LAUNCH(launch_qkv_post(m->dt, qa, st));
-            {   // causal attention flops: 4 hd per visible (query, key) pair and head
+            {   // causal attention flops: 4 hd per visible (query, key) pair and head; bytes:
+                // q in, y out, and every key/value a query of the row sees, read once
                 const int w = m->windows[l];
-                const double Td = T, vis = (w < 0 || w + 1 >= T)
-                                               ? Td * (Td + 1) / 2.0
-                                               : (w + 1.0) * (w + 2.0) / 2.0 + (Td - w - 1.0) * (w + 1.0);
-                const double fl = 4.0 * B * H * hd * vis;
-                const double by = (double)B * T * (H + 2 * nkv + H) * hd * m->esz;  // q, k, v in; y out
+                double vis = 0, keys = 0;
+                for (int b = 0; b < B; ++b) {
+                    const long long off = kv->lens_host[b];
+                    vis += visible_pairs(off, T, w);
+                    keys += (double)(off + T - (w < 0 ? 0 : std::max(0LL, off - w)));
+                }
+                const double fl = 4.0 * H * hd * vis;
+                const double by = ((double)B * T * 2 * H + keys * 2 * nkv) * hd * m->esz;
                 LAUNCH(timed(NC_KC_PREFILL_ATTN, by, fl, st, [&] {
-                    return launch_attn_prefill(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->y, B, T, H, nkv, kv->S, w, st);
+                    return launch_attn_prefill(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->y, B, T, H, nkv, kv->S, w,
+                                               kv->lens_dev, st);
                 }));
             }
             // O product + residual
@@ -685,8 +699,8 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             g.ss_stride = (int)kv->cap_m; g.eps = c.norm_eps; g.cap = c.softcap;
             LAUNCH(prefill_gemm(m, EPI_SOFTCAP, g, st));
         }
-        LAUNCH(launch_lens_add(kv->lens_dev, B, 0, T, st));
-        std::fill(kv->lens_host.begin(), kv->lens_host.end(), T);
+        LAUNCH(launch_lens_add(kv->lens_dev, B, T, -1, st));
+        for (int32_t& n : kv->lens_host) n += T;
         return NC_OK;
     } catch (...) {
         return fail(NC_ERR_DEVICE, "unexpected exception");

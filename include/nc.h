@@ -126,9 +126,14 @@ nc_status nc_kv_get_lens(const nc_kv* kv, int32_t* lens_host);
  * values). */
 nc_status nc_kv_export(nc_kv* kv, int32_t layer, void* k_dev, void* v_dev, void* stream);
 
-/* Prefill: tokens_dev int32 [B, T] at positions 0..T-1 of every row.  Requires every
- * length 0, B == batch of kv, 1 <= T <= kv max_seq.  logits_dev: fp32 [B, T, vocab] for
- * every position, or NULL to fill the cache only.  On success lengths become T.
+/* Prefill: tokens_dev int32 [B, T]; row b's tokens go to positions lens[b] .. lens[b]+T-1
+ * and attend to the row's cached positions as well (0..lens[b]-1): on an empty cache this
+ * is the prompt prefill, on a filled one it appends a chunk (a long prompt in pieces, or
+ * forced tokens in the middle of a generation), with the same results as a single prefill
+ * of the whole sequence or as T decode steps.  Requires B == batch of kv, T >= 1
+ * (NC_ERR_INVALID_ARG) and lens[b] + T <= max_seq for every row (NC_ERR_CAPACITY).
+ * logits_dev: fp32 [B, T, vocab] for every new position, or NULL to fill the cache only.
+ * On success every length grows by T.
  * Token ids outside [0, vocab) are clamped (memory-safe; their outputs are meaningless). */
 nc_status nc_prefill(nc_model* m, const int32_t* tokens_dev, int32_t B, int32_t T,
                      nc_kv* kv, float* logits_dev, void* stream);

@@ -281,6 +281,14 @@ class OracleModel:
         cache["lens"] += 1
         return logits
 
+    def extend(self, cache, tokens):
+        """Append tokens [B, T]: row b takes them at positions lens[b] .. lens[b] + T - 1.
+        Returns logits [B, T, V].  By causality this is T decode steps, which is how it is
+        computed."""
+        tokens = np.asarray(tokens)
+        return np.stack([self.decode_step(cache, tokens[:, t]) for t in range(tokens.shape[1])],
+                        axis=1)
+
     def truncate(self, cache, lens):
         """Shrink the cached length of each row (keys beyond the new length are dropped)."""
         lens = np.asarray(lens, dtype=np.int64)

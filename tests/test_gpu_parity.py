@@ -178,9 +178,9 @@ def test_error_paths_on_gpu(small):
     kv, _ = prefill(gm, toks, 9, logits=False)
     t = torch.zeros(2, dtype=torch.int32, device="cuda")
     out = torch.empty((2, SMALL_BF16.vocab), device="cuda", dtype=torch.float32)
-    with pytest.raises(nc.NcError) as e:  # prefill into a non-empty cache
+    with pytest.raises(nc.NcError) as e:  # an appended chunk past max_seq (8 + 4 > 9)
         kv.prefill(torch.zeros((2, 4), dtype=torch.int32, device="cuda"), None)
-    assert e.value.code == nc.NC_ERR_STATE
+    assert e.value.code == nc.NC_ERR_CAPACITY
     kv.decode(t, out)  # fills position 8 (the last)
     with pytest.raises(nc.NcError) as e:
         kv.decode(t, out)
@@ -458,4 +458,66 @@ def test_windows_only_change_without_kv():
     assert e.value.code == nc.NC_ERR_STATE
     kv.close()
     nc.nc_model_set_windows(gm.handle, [4, -1])
+    gm.close()
+
+
+# ---------------------------------------------------------------- appended prefill -----
+def test_fp32_append_chunks_with_windows():
+    """A prompt prefilled in three chunks (37, 64 and 1 tokens after the first 48) equals
+    one prefill of the whole, with a 20-key window in layer 0, at the fp32 bar; then a
+    decode step continues from the appended cache."""
+    torch = torch_mod()
+    shape = replace(TINY, max_seq=160)
+    wins = [20, -1]
+    w = make_weights(shape, seed=60)
+    orc = OracleModel(shape, w, windows=wins)
+    gm = gpu_model(shape, w, windows=wins)
+    B = 2
+    toks = make_tokens(shape.vocab, B, 151, seed=61)
+    want, _ = orc.prefill(toks)
+    kv, got0 = prefill(gm, toks[:, :48], shape.max_seq)
+    parts = [got0]
+    for a, b in ((48, 85), (85, 149), (149, 150)):
+        out = torch.empty((B, b - a, shape.vocab), device="cuda", dtype=torch.float32)
+        kv.prefill(torch.from_numpy(np.ascontiguousarray(toks[:, a:b])).cuda(), out)
+        torch.cuda.synchronize()
+        parts.append(out.cpu().numpy())
+    assert np.array_equal(kv.lens(), [150, 150])
+    err, _ = report("tiny append chunks", np.concatenate(parts, 1), want[:, :150])
+    assert err <= F32_TOL
+    got = decode(gm, kv, toks[:, 150])
+    err, _ = report("tiny decode after append", got, want[:, 150])
+    assert err <= F32_TOL
+    kv.close()
+    gm.close()
+
+
+def test_bf16_append_at_ragged_lengths():
+    """Rows truncated to lengths 0, 1, 77 and 260, then a 300-token chunk appended to all
+    of them (queries at different positions per row, two query tiles), then one decode
+    step: every row equals the oracle's prefill of its own concatenated sequence."""
+    torch = torch_mod()
+    shape = replace(SMALL_BF16, max_seq=600)
+    w = make_weights(shape, seed=64)
+    orc = OracleModel(shape, w)
+    gm = gpu_model(shape, w)
+    B, T0, T = 4, 260, 300
+    toks = make_tokens(shape.vocab, B, T0, seed=62)
+    more = make_tokens(shape.vocab, B, T + 1, seed=63)
+    lens = np.array([0, 1, 77, 260], dtype=np.int32)
+    kv, _ = prefill(gm, toks, 600, logits=False)
+    kv.set_lens(lens)
+    out = torch.empty((B, T, shape.vocab), device="cuda", dtype=torch.float32)
+    kv.prefill(torch.from_numpy(np.ascontiguousarray(more[:, :T])).cuda(), out)
+    got = out.cpu().numpy()
+    dec = decode(gm, kv, more[:, T])
+    assert np.array_equal(kv.lens(), lens + T + 1)
+    for b in range(B):
+        seq = np.concatenate([toks[b, :lens[b]], more[b]])[None]
+        ref, _ = orc.prefill(seq, logits_at=np.arange(lens[b], lens[b] + T + 1))
+        err, agr = report(f"small append row {b} from length {lens[b]}", got[b], ref[0, :T])
+        assert err <= BF16_TOL and agr >= AGREE
+        err = np.max(np.abs(dec[b] - ref[0, T]))
+        assert err <= BF16_TOL
+    kv.close()
     gm.close()

@@ -208,6 +208,20 @@ def test_mqa_equals_mha_with_replicated_kv():
     assert np.allclose(mqa, mha, rtol=0, atol=1e-12)
 
 
+def test_extend_equals_prefill_of_the_whole():
+    """Appending chunks to a cache gives the logits a single prefill of the whole sequence
+    gives at those positions (decode steps against the batched causal prefill)."""
+    w = micro_weights(seed=26)
+    m = OracleModel(MICRO, w, windows=[3, -1])
+    toks = make_tokens(MICRO.vocab, 2, 12, seed=27)
+    whole, _ = m.prefill(toks)
+    _, cache = m.prefill(toks[:, :5], max_seq=12)
+    a = m.extend(cache, toks[:, 5:9])
+    b = m.extend(cache, toks[:, 9:12])
+    assert np.allclose(np.concatenate([a, b], 1), whole[:, 5:], rtol=0, atol=1e-11)
+    assert np.array_equal(cache["lens"], [12, 12])
+
+
 # ------------------------------------------------------- sliding windows --------------
 def test_one_layer_window_equals_suffix_prefill():
     """One layer with window w: RoPE scores depend only on the distance between positions,
