@@ -163,4 +163,17 @@ hipError_t launch_lens_add(int32_t* lens, int B, int32_t delta, int32_t set_valu
 hipError_t launch_kv_export(DType dt, int hd, const void* kc, const void* vtc, void* k_out,
                             void* v_out, int B, int S, int S_out, hipStream_t st);
 
+// Copy rows between two caches of one model (K [L][B][nkv][S][hd], V^T [L][B][nkv][hd][S],
+// es bytes per element): pair i copies positions 0..len[i]-1 of source row src[i] into
+// destination row dst[i] and sets lens_dst[dst[i]] = len[i].  The pairs' rows must not
+// overlap when both caches are the same.
+struct KvRowCopy {
+    static constexpr int MAX = 128;
+    int n;
+    int32_t dst[MAX], src[MAX], len[MAX];
+};
+hipError_t launch_kv_copy_rows(const KvRowCopy& rc, const void* ksrc, const void* vsrc, void* kdst,
+                               void* vdst, int L, int nkv, int hd, int es, int Bsrc, int Ssrc, int Bdst,
+                               int Sdst, int32_t* lens_dst, hipStream_t st);
+
 }  // namespace nc

@@ -275,4 +275,46 @@ hipError_t launch_kv_export(DType dt, int hd, const void* kc, const void* vtc, v
     return hipGetLastError();
 }
 
+// Row copy between caches of one model: workgroup (pair i, layer and K/V head, K or V).
+// K of a (row, head) is len hd contiguous elements; V^T is hd rows of len positions with
+// the cache's row stride.  Copies go in 16-byte units (the tail of a V^T row is rounded up
+// to 16 bytes, which stays inside the row: S is a multiple of 64 positions).
+__global__ __launch_bounds__(256) void kv_copy_rows_kernel(KvRowCopy rc, const char* __restrict__ ksrc,
+                                                          const char* __restrict__ vsrc,
+                                                          char* __restrict__ kdst, char* __restrict__ vdst,
+                                                          int nkv, int hd, int es, int Bsrc, int Ssrc,
+                                                          int Bdst, int Sdst, int32_t* lens_dst) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const int i = blockIdx.x, l = blockIdx.y / nkv, kvh = blockIdx.y % nkv;
+    const int len = rc.len[i];
+    const long long us = ((long long)l * Bsrc + rc.src[i]) * nkv + kvh;  // (layer, row, head) unit
+    const long long ud = ((long long)l * Bdst + rc.dst[i]) * nkv + kvh;
+    if (blockIdx.z == 0) {
+        const u4* s = (const u4*)(ksrc + us * Ssrc * hd * es);
+        u4* d = (u4*)(kdst + ud * Sdst * hd * es);
+        const long long n = (long long)len * hd * es / 16;
+        for (long long e = threadIdx.x; e < n; e += 256) d[e] = s[e];
+        if (l == 0 && kvh == 0 && threadIdx.x == 0) lens_dst[rc.dst[i]] = len;
+    } else {
+        const int per_row = (len * es + 15) / 16;
+        const long long n = (long long)per_row * hd;
+        for (long long e = threadIdx.x; e < n; e += 256) {
+            const int row = (int)(e / per_row), c = (int)(e % per_row);
+            const u4* s = (const u4*)(vsrc + ((us * hd + row) * Ssrc) * es) + c;
+            u4* d = (u4*)(vdst + ((ud * hd + row) * Sdst) * es) + c;
+            *d = *s;
+        }
+    }
+}
+
+hipError_t launch_kv_copy_rows(const KvRowCopy& rc, const void* ksrc, const void* vsrc, void* kdst,
+                               void* vdst, int L, int nkv, int hd, int es, int Bsrc, int Ssrc, int Bdst,
+                               int Sdst, int32_t* lens_dst, hipStream_t st) {
+    if (rc.n < 1 || rc.n > KvRowCopy::MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kv_copy_rows_kernel, dim3(rc.n, L * nkv, 2), dim3(256), 0, st, rc,
+                       (const char*)ksrc, (const char*)vsrc, (char*)kdst, (char*)vdst, nkv, hd, es,
+                       Bsrc, Ssrc, Bdst, Sdst, lens_dst);
+    return hipGetLastError();
+}
+
 }  // namespace nc

@@ -610,6 +610,49 @@ nc_status nc_kv_export(nc_kv* kv, int32_t layer, void* k_out, void* v_out, void*
     return NC_OK;
 }
 
+nc_status nc_kv_copy_rows(nc_kv* dst, const int32_t* dst_rows, nc_kv* src, const int32_t* src_rows,
+                          int32_t n, void* stream) {
+    try {
+        if (!dst || !src) return fail(NC_ERR_INVALID_ARG, "NULL argument");
+        if (dst->m != src->m) return fail(NC_ERR_INVALID_ARG, "the caches belong to different models");
+        if (n < 0) return fail(NC_ERR_INVALID_ARG, "n must be >= 0");
+        if (n == 0) return NC_OK;
+        if (!dst_rows || !src_rows) return fail(NC_ERR_INVALID_ARG, "NULL row list");
+        std::vector<char> is_dst(dst->B, 0);
+        for (int i = 0; i < n; ++i) {
+            if (dst_rows[i] < 0 || dst_rows[i] >= dst->B || src_rows[i] < 0 || src_rows[i] >= src->B)
+                return fail(NC_ERR_INVALID_ARG, "row index out of range");
+            if (is_dst[dst_rows[i]]) return fail(NC_ERR_INVALID_ARG, "a destination row appears twice");
+            is_dst[dst_rows[i]] = 1;
+            if (src->lens_host[src_rows[i]] > dst->max_seq)
+                return fail(NC_ERR_CAPACITY, "a source row is longer than the destination's max_seq");
+        }
+        if (dst == src)
+            for (int i = 0; i < n; ++i)
+                if (is_dst[src_rows[i]]) return fail(NC_ERR_INVALID_ARG, "a row is both a source and a destination");
+        const nc_config& c = dst->m->cfg;
+        hipStream_t st = (hipStream_t)stream;
+        for (int i0 = 0; i0 < n; i0 += KvRowCopy::MAX) {
+            KvRowCopy rc{};
+            rc.n = std::min(n - i0, KvRowCopy::MAX);
+            for (int i = 0; i < rc.n; ++i) {
+                rc.dst[i] = dst_rows[i0 + i];
+                rc.src[i] = src_rows[i0 + i];
+                rc.len[i] = src->lens_host[src_rows[i0 + i]];
+            }
+            LAUNCH(launch_kv_copy_rows(rc, src->kcache, src->vcache, dst->kcache, dst->vcache, c.n_layer,
+                                       c.n_kv_head, c.head_dim, (int)dst->m->esz, src->B, src->S, dst->B,
+                                       dst->S, dst->lens_dev, st));
+        }
+        for (int i = 0; i < n; ++i) dst->lens_host[dst_rows[i]] = src->lens_host[src_rows[i]];
+        return NC_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(NC_ERR_OOM, "host allocation failed");
+    } catch (...) {
+        return fail(NC_ERR_DEVICE, "unexpected exception");
+    }
+}
+
 nc_status nc_argmax(const float* logits, int32_t B, int32_t V, int32_t* out, void* stream) {
     if (!logits || !out) return fail(NC_ERR_INVALID_ARG, "NULL argument");
     if (B < 1 || V < 1) return fail(NC_ERR_INVALID_ARG, "B and V must be >= 1");

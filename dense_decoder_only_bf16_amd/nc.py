@@ -37,7 +37,7 @@ NC_KC_PREFILL_ATTN = 3
 NC_KC_DECODE_ATTN = 4
 
 EXPORTED = ("nc_model_create", "nc_model_free", "nc_model_set_windows", "nc_kv_create", "nc_kv_free", "nc_kv_set_lens",
-            "nc_kv_get_lens", "nc_kv_export", "nc_prefill", "nc_decode_step", "nc_argmax",
+            "nc_kv_get_lens", "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step", "nc_argmax",
             "nc_timing_enable", "nc_timing_read", "nc_last_error", "nc_abi_version")
 
 
@@ -83,6 +83,7 @@ def lib():
         L.nc_kv_set_lens.argtypes = [vp, ctypes.POINTER(i32)]
         L.nc_kv_get_lens.argtypes = [vp, ctypes.POINTER(i32)]
         L.nc_kv_export.argtypes = [vp, i32, vp, vp, vp]
+        L.nc_kv_copy_rows.argtypes = [vp, ctypes.POINTER(i32), vp, ctypes.POINTER(i32), i32, vp]
         L.nc_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.nc_decode_step.argtypes = [vp, vp, i32, vp, vp, vp]
         L.nc_argmax.argtypes = [vp, i32, i32, vp, vp]
@@ -93,7 +94,7 @@ def lib():
         L.nc_abi_version.argtypes = []
         L.nc_abi_version.restype = i32
         for name in ("nc_model_create", "nc_model_set_windows", "nc_kv_create", "nc_kv_set_lens", "nc_kv_get_lens",
-                     "nc_kv_export", "nc_prefill", "nc_decode_step", "nc_argmax",
+                     "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step", "nc_argmax",
                      "nc_timing_enable", "nc_timing_read"):
             getattr(L, name).restype = st
         _lib = L
@@ -191,6 +192,16 @@ def nc_kv_export(kv, layer, k_out, v_out, stream=None):
     _check(lib().nc_kv_export(kv, layer, _ptr(k_out), _ptr(v_out), _stream(stream)))
 
 
+def nc_kv_copy_rows(dst, dst_rows, src, src_rows, stream=None):
+    d = np.ascontiguousarray(dst_rows, dtype=np.int32)
+    s = np.ascontiguousarray(src_rows, dtype=np.int32)
+    if d.shape != s.shape or d.ndim != 1:
+        raise ValueError("dst_rows and src_rows must be 1-D of the same length")
+    p = ctypes.POINTER(ctypes.c_int32)
+    _check(lib().nc_kv_copy_rows(dst, d.ctypes.data_as(p), src, s.ctypes.data_as(p), d.shape[0],
+                                 _stream(stream)))
+
+
 def nc_prefill(m, tokens, B, T, kv, logits, stream=None):
     _check(lib().nc_prefill(m, _ptr(tokens), B, T, kv, _ptr(logits), _stream(stream)))
 
@@ -263,6 +274,10 @@ class KV:
 
     def export(self, layer, k_out, v_out, stream=None):
         nc_kv_export(self.handle, layer, k_out, v_out, stream)
+
+    def copy_rows_from(self, src, src_rows, dst_rows, stream=None):
+        """Rows dst_rows of this cache take rows src_rows of cache `src` (same model)."""
+        nc_kv_copy_rows(self.handle, dst_rows, src.handle, src_rows, stream)
 
     def close(self):
         if self.handle is not None:

@@ -126,6 +126,18 @@ nc_status nc_kv_get_lens(const nc_kv* kv, int32_t* lens_host);
  * values). */
 nc_status nc_kv_export(nc_kv* kv, int32_t layer, void* k_dev, void* v_dev, void* stream);
 
+/* Copy cache rows: for i < n, row dst_rows_host[i] of dst takes the keys and values (every
+ * layer) and the length of row src_rows_host[i] of src, as src holds them once its
+ * enqueued work completes.  This is the batch generation of the pages' inference engine
+ * (apidog.com/th guide, part 6: the KV cache cloned for parallel sampling): a prompt is
+ * prefilled once and its row copied to the rows that then sample independently.  src and
+ * dst belong to the same model and may be the same object; destination rows must be
+ * distinct and, within one cache, disjoint from the source rows (NC_ERR_INVALID_ARG); a
+ * source length above dst's max_seq gives NC_ERR_CAPACITY.  n == 0 is a no-op.  Enqueued
+ * on `stream` (both caches are then in use on that stream). */
+nc_status nc_kv_copy_rows(nc_kv* dst, const int32_t* dst_rows_host, nc_kv* src,
+                          const int32_t* src_rows_host, int32_t n, void* stream);
+
 /* Prefill: tokens_dev int32 [B, T]; row b's tokens go to positions lens[b] .. lens[b]+T-1
  * and attend to the row's cached positions as well (0..lens[b]-1): on an empty cache this
  * is the prompt prefill, on a filled one it appends a chunk (a long prompt in pieces, or

@@ -289,6 +289,23 @@ class OracleModel:
         return np.stack([self.decode_step(cache, tokens[:, t]) for t in range(tokens.shape[1])],
                         axis=1)
 
+    @staticmethod
+    def copy_rows(dst_cache, dst_rows, src_cache, src_rows):
+        """Row dst_rows[i] of dst_cache takes the keys, values and length of row
+        src_rows[i] of src_cache (batch generation: one prefilled prompt copied to the rows
+        that sample from it)."""
+        n = min(dst_cache["max_seq"], src_cache["max_seq"])
+        k = src_cache["k"][:, list(src_rows), :n].copy()
+        v = src_cache["v"][:, list(src_rows), :n].copy()
+        lens = src_cache["lens"][list(src_rows)].copy()
+        assert np.all(lens <= dst_cache["max_seq"])
+        for i, d in enumerate(dst_rows):
+            dst_cache["k"][:, d] = 0.0
+            dst_cache["v"][:, d] = 0.0
+            dst_cache["k"][:, d, :n] = k[:, i]
+            dst_cache["v"][:, d, :n] = v[:, i]
+            dst_cache["lens"][d] = lens[i]
+
     def truncate(self, cache, lens):
         """Shrink the cached length of each row (keys beyond the new length are dropped)."""
         lens = np.asarray(lens, dtype=np.int64)

@@ -521,3 +521,93 @@ def test_bf16_append_at_ragged_lengths():
         assert err <= BF16_TOL
     kv.close()
     gm.close()
+
+
+# ---------------------------------------------------------------- cache row copies -----
+def test_copy_rows_bit_exact_and_lengths():
+    """Copied rows hold exactly the source's keys and values (every layer and K/V head,
+    across caches of different capacity, and within one cache) and take its length."""
+    torch = torch_mod()
+    shape = replace(TINY_GQA, max_seq=200)
+    w = make_weights(shape, seed=70)
+    gm = gpu_model(shape, w)
+    toks = make_tokens(shape.vocab, 3, 90, seed=71)
+    src, _ = prefill(gm, toks, 120, logits=False)
+    src.set_lens([90, 17, 64])
+    dst = gm.new_kv(5, 200)
+    dst.copy_rows_from(src, [1, 0, 2, 0], [4, 0, 1, 3])
+    assert np.array_equal(dst.lens(), [90, 64, 0, 90, 17])
+    nkv, hd = shape.n_kv_head, shape.head_dim
+
+    def export(kv, rows, cap):
+        out = []
+        for layer in range(shape.n_layer):
+            k = torch.empty((rows, nkv, cap, hd), device="cuda", dtype=torch.float32)
+            v = torch.empty_like(k)
+            kv.export(layer, k, v)
+            torch.cuda.synchronize()
+            out.append((k.cpu().numpy(), v.cpu().numpy()))
+        return out
+
+    before, copied = export(src, 3, 120), export(dst, 5, 200)
+    src.copy_rows_from(src, [0], [1])  # within one cache
+    assert np.array_equal(src.lens(), [90, 90, 64])
+    after = export(src, 3, 120)
+    for layer in range(shape.n_layer):
+        (ks, vs), (kd, vd), (ka, va) = before[layer], copied[layer], after[layer]
+        for d, s, n in ((4, 1, 17), (0, 0, 90), (1, 2, 64), (3, 0, 90)):
+            assert np.array_equal(kd[d, :, :n], ks[s, :, :n]), (layer, d)
+            assert np.array_equal(vd[d, :, :n], vs[s, :, :n]), (layer, d)
+        assert np.array_equal(ka[1, :, :90], ks[0, :, :90])
+        assert np.array_equal(va[1, :, :90], vs[0, :, :90])
+        assert np.array_equal(ka[2], ks[2]) and np.array_equal(ka[0], ks[0])  # others untouched
+    dst.close()
+    src.close()
+    gm.close()
+
+
+def test_copy_rows_then_sample_independently(small):
+    """Batch generation: one prompt prefilled once, copied to four rows, each continued
+    with its own tokens (decode steps and an appended chunk) against the oracle."""
+    torch = torch_mod()
+    w, orc, gm = small
+    prompt = make_tokens(SMALL_BF16.vocab, 1, 100, seed=72)
+    one, _ = prefill(gm, prompt, 101, logits=False)
+    many = gm.new_kv(4, 200)
+    many.copy_rows_from(one, [0, 0, 0, 0], [3, 0, 2, 1])
+    one.close()
+    nxt = make_tokens(SMALL_BF16.vocab, 4, 8, seed=73)
+    got = [decode(gm, many, nxt[:, s]) for s in range(3)]
+    out = torch.empty((4, 5, SMALL_BF16.vocab), device="cuda", dtype=torch.float32)
+    many.prefill(torch.from_numpy(np.ascontiguousarray(nxt[:, 3:])).cuda(), out)
+    got = np.concatenate([np.stack(got, 1), out.cpu().numpy()], 1)  # [4, 8, V]
+    assert np.array_equal(many.lens(), [108] * 4)
+    for b in range(4):
+        seq = np.concatenate([prompt[0], nxt[b]])[None]
+        ref, _ = orc.prefill(seq, logits_at=np.arange(100, 108))
+        err, agr = report(f"copied row {b}", got[b], ref[0])
+        assert err <= BF16_TOL
+        assert_flips_are_near_ties(got[b], ref[0], err)
+    many.close()
+
+
+def test_copy_rows_errors(small):
+    w, orc, gm = small
+    a = gm.new_kv(3, 50)
+    b = gm.new_kv(2, 10)
+    toks = make_tokens(SMALL_BF16.vocab, 3, 20, seed=74)
+    a.prefill(torch_mod().from_numpy(toks).cuda(), None)
+    for dst, src, code in (
+        ([0, 0], [1, 2], nc.NC_ERR_INVALID_ARG),   # a destination twice
+        ([2], [3], nc.NC_ERR_INVALID_ARG),         # source row out of range
+        ([0], [1], nc.NC_ERR_CAPACITY),            # 20 positions into a 10-position cache
+    ):
+        with pytest.raises(nc.NcError) as e:
+            (a if code != nc.NC_ERR_CAPACITY else b).copy_rows_from(a, src, dst)
+        assert e.value.code == code
+    with pytest.raises(nc.NcError) as e:  # within one cache, a row both read and written
+        a.copy_rows_from(a, [0, 1], [1, 2])
+    assert e.value.code == nc.NC_ERR_INVALID_ARG
+    assert np.array_equal(a.lens(), [20, 20, 20]) and np.array_equal(b.lens(), [0, 0])
+    a.close()
+    b.close()

@@ -222,6 +222,24 @@ def test_extend_equals_prefill_of_the_whole():
     assert np.array_equal(cache["lens"], [12, 12])
 
 
+def test_copied_rows_continue_like_their_source():
+    """A prompt prefilled in one row and copied to three rows of a larger cache: each copy
+    then decodes exactly like a fresh prefill of the prompt followed by its own tokens."""
+    w = micro_weights(seed=28)
+    m = OracleModel(MICRO, w)
+    prompt = make_tokens(MICRO.vocab, 1, 5, seed=29)
+    _, one = m.prefill(prompt, max_seq=6)
+    many = m.new_cache(3, 9)
+    m.copy_rows(many, [2, 0, 1], one, [0, 0, 0])
+    assert np.array_equal(many["lens"], [5, 5, 5])
+    nxt = make_tokens(MICRO.vocab, 3, 2, seed=30)
+    got = m.extend(many, nxt)
+    for b in range(3):
+        seq = np.concatenate([prompt[0], nxt[b]])[None]
+        ref, _ = m.prefill(seq, logits_at=[5, 6])
+        assert np.allclose(got[b], ref[0], rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------- sliding windows --------------
 def test_one_layer_window_equals_suffix_prefill():
     """One layer with window w: RoPE scores depend only on the distance between positions,
