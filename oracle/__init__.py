@@ -23,5 +23,6 @@ from .model import (  # noqa: F401
     linear,
     causal_attention,
     layer_windows,
+    sample,
     param_count,
 )

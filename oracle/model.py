@@ -28,7 +28,9 @@ What is computed, and where the pages say so:
   * a softcap on the logits [yelogs.com architecture answer];
   * inference with a KV cache: prefill of the prompt, then one token per decode step
     [szyisi.cn, section on the base model and the Engine class; apidog.com part 6,
-    inference engine].
+    inference engine];
+  * batch generation: the prompt's cache copied to several rows that are sampled in
+    parallel [apidog.com part 6].
 
 Readings where the pages are silent (each is listed with its reason in the design notes):
   * norm placement: pre-norm before attention and before the MLP, one norm right after the
@@ -44,7 +46,12 @@ Readings where the pages are silent (each is listed with its reason in the desig
     left extent of the window_size argument of the pages' flash-attention call; its
     right extent is 0 under causality); w < 0 means the whole causal context;
   * window pattern: character l mod len(pattern) of the pattern gives layer l's window,
-    'S' the short window and 'L' the whole context.
+    'S' the short window and 'L' the whole context;
+  * sampling (the pages name parallel sampling but give no formula): keep the logits at
+    or above the k-th largest (all with top_k <= 0), take probabilities proportional to
+    exp(logit / temperature), and return the smallest token index whose cumulative
+    probability exceeds a uniform number u in [0, 1) given by the caller; temperature <= 0
+    is the greedy argmax.  NaN logits have probability 0.
 
 Everything is evaluated in float64 with plain numpy operations: no tiling, no online
 softmax, no fusion.  Weights may arrive in any float dtype; they are widened to float64
@@ -151,6 +158,30 @@ def layer_windows(pattern, n_layer, short_window):
             out.append(-1)
         else:
             raise ValueError(f"window pattern character {ch!r} is not S or L")
+    return out
+
+
+def sample(logits, temperature, top_k, u):
+    """One token per row of logits [B, V] (see the sampling reading above); u: [B]."""
+    logits = np.asarray(logits, dtype=F64)
+    out = np.empty(logits.shape[0], dtype=np.int64)
+    for b, row in enumerate(logits):
+        z = np.where(np.isnan(row), -np.inf, row)
+        if temperature <= 0:
+            out[b] = int(np.argmax(z))  # first maximum
+            continue
+        if 0 < top_k < z.shape[0]:
+            kth = np.sort(z)[::-1][top_k - 1]
+            z = np.where(z >= kth, z, -np.inf)
+        m = np.max(z)
+        if not np.isfinite(m):
+            out[b] = 0
+            continue
+        p = np.exp((z - m) / temperature)
+        cdf = np.cumsum(p) / np.sum(p)
+        out[b] = min(int(np.searchsorted(cdf, u[b], side="right")), z.shape[0] - 1)
+        while p[out[b]] == 0:  # cdf flat at the end: the last token with mass
+            out[b] -= 1
     return out
 
 

@@ -6,7 +6,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import (causal_attention, layer_windows, linear, relu2, rms_norm, rope, rope_tables,
+from oracle import (causal_attention, layer_windows, linear, relu2, rms_norm, rope, rope_tables, sample,
                     softcap)
 
 
@@ -265,3 +265,49 @@ def test_attention_mqa_equals_replicated_mha():
     mqa = causal_attention(q, k, v, pos)
     mha = causal_attention(q, np.repeat(k, h, axis=1), np.repeat(v, h, axis=1), pos)
     assert np.allclose(mqa, mha, rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------- sampling ----------
+def test_sample_greedy_limits():
+    r = rng(13)
+    logits = r.standard_normal((6, 40)) * 3
+    greedy = np.argmax(logits, -1)
+    u = r.random(6)
+    assert np.array_equal(sample(logits, 0.0, 0, u), greedy)        # temperature 0
+    assert np.array_equal(sample(logits, 1.0, 1, u), greedy)        # top-1
+    assert np.array_equal(sample(logits, 1e-4, 0, u), greedy)       # vanishing temperature
+    assert np.array_equal(sample(logits, 0.7, 40, u), sample(logits, 0.7, 0, u))  # k = V
+
+
+def test_sample_two_tokens_closed_form():
+    l0, l1, t = 0.3, 1.1, 0.8
+    p0 = 1.0 / (1.0 + math.exp((l1 - l0) / t))
+    logits = np.array([[l0, l1]])
+    for u in (0.0, p0 - 1e-9, p0 + 1e-9, 0.999):
+        assert sample(logits, t, 0, np.array([u]))[0] == (0 if u < p0 else 1)
+
+
+def test_sample_frequencies_on_a_grid():
+    """u on a uniform grid of N points: token i is drawn for the points inside its slice of
+    the cumulative distribution, so its count is N p_i within one."""
+    r = rng(14)
+    z = r.standard_normal(12)
+    t, k, n = 1.3, 5, 20000
+    keep = np.argsort(z)[::-1][:k]
+    e = np.exp(z[keep] / t)
+    probs = np.zeros(12)
+    probs[keep] = e / e.sum()
+    u = (np.arange(n) + 0.5) / n
+    got = sample(np.broadcast_to(z, (n, 12)), t, k, u)
+    counts = np.bincount(got, minlength=12)
+    assert np.all(np.abs(counts - n * probs) <= 1.0)
+
+
+def test_sample_ties_nan_and_inf():
+    row = np.array([[1.0, 2.0, 2.0, 2.0, -np.inf, np.nan, 0.5]])
+    # top-2 keeps every logit tied with the 2nd largest: three equal tokens
+    drawn = {int(sample(row, 1.0, 2, np.array([u]))[0]) for u in (0.1, 0.5, 0.9)}
+    assert drawn == {1, 2, 3}
+    # NaN and -inf never drawn, even at the top of the distribution
+    assert sample(row, 5.0, 0, np.array([0.999999]))[0] == 6
+    assert sample(np.array([[-np.inf, np.nan]]), 1.0, 0, np.array([0.5]))[0] == 0
