@@ -159,6 +159,11 @@ int attn_decode_slots(int rows, int S, int span);  // partial slots per unit
 hipError_t launch_attn_decode(DType dt, const DecAttnArgs& a, void* y, hipStream_t st);
 
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st);
+// Token per row drawn with probabilities proportional to 2^(logit scale) over the logits at
+// or above the top_k-th largest (top_k <= 0 or >= V: all), by the inverse of the
+// cumulative distribution in token order at u[b] in [0, 1).
+hipError_t launch_sample(const float* logits, int B, int V, float scale, int top_k, const float* u,
+                         int32_t* out, hipStream_t st);
 hipError_t launch_lens_add(int32_t* lens, int B, int32_t delta, int32_t set_value, hipStream_t st);
 hipError_t launch_kv_export(DType dt, int hd, const void* kc, const void* vtc, void* k_out,
                             void* v_out, int B, int S, int S_out, hipStream_t st);

@@ -205,6 +205,141 @@ hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, hipStr
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ sampling --------
+// Order-preserving map of a float to an unsigned key (larger float, larger key); NaN maps
+// to 0, below every number.
+__device__ __forceinline__ uint32_t order_key(float x) {
+    if (x != x) return 0u;
+    const uint32_t b = __float_as_uint(x);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// One 1024-thread workgroup per row.
+//  1. Threshold: the key of the top_k-th largest logit, by a radix select over the keys,
+//     8 bits at a time from the top (an LDS histogram of the candidates that match the
+//     digits chosen so far); top_k <= 0 or >= V keeps every logit.
+//  2. m = the row's largest logit (always kept).
+//  3. Weights w_i = 2^((x_i - m) scale) for kept, non-NaN logits (scale = log2(e) / T).
+//     Thread t owns the contiguous segment [t seg, (t + 1) seg) of the row, so the block's
+//     exclusive scan of segment sums orders them by token index.  With target = u Z (Z the
+//     total), the last thread whose scan value is <= target and whose segment has mass
+//     walks its segment, summing in the same order as its segment sum, to the first
+//     token whose running sum exceeds target - (its scan value); if rounding carries the
+//     target past its end, its last token with mass is taken.
+__global__ __launch_bounds__(1024) void sample_kernel(const float* __restrict__ logits, int V,
+                                                      float scale, int top_k,
+                                                      const float* __restrict__ u,
+                                                      int32_t* __restrict__ out) {
+    __shared__ uint32_t hist[256];
+    __shared__ int sel[2];
+    __shared__ float wred[16];
+    __shared__ int wbest[16];
+    __shared__ int picks[1024];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float* row = logits + (long long)b * V;
+
+    uint32_t thresh = 0;
+    if (top_k > 0 && top_k < V) {
+        uint32_t prefix = 0, mask = 0;
+        int kk = top_k;  // rank still wanted among the candidates
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            if (tid < 256) hist[tid] = 0;
+            __syncthreads();
+            for (int i = tid; i < V; i += 1024) {
+                const uint32_t k = order_key(row[i]);
+                if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                int cum = 0, d = 255;
+                for (; d > 0; --d) {
+                    if (cum + (int)hist[d] >= kk) break;
+                    cum += (int)hist[d];
+                }
+                sel[0] = d;
+                sel[1] = kk - cum;
+            }
+            __syncthreads();
+            prefix |= (uint32_t)sel[0] << shift;
+            mask |= 0xFFu << shift;
+            kk = sel[1];
+            __syncthreads();  // sel and hist are rewritten in the next round
+        }
+        thresh = prefix;
+    }
+
+    float m = -INFINITY;
+    for (int i = tid; i < V; i += 1024) m = fmaxf(m, row[i]);  // fmaxf skips NaN
+    m = wave_max(m);
+    if (lane == 0) wred[wave] = m;
+    __syncthreads();
+    m = wred[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) m = fmaxf(m, wred[w]);
+    if (m == -INFINITY) {  // no logit with mass
+        if (tid == 0) out[b] = 0;
+        return;
+    }
+    __syncthreads();  // wred is reused below
+
+    auto weight = [&](float x) {
+        return (x == x && order_key(x) >= thresh) ? exp2f((x - m) * scale) : 0.f;
+    };
+    const int seg = (V + 1023) / 1024;
+    const int i0 = min(V, tid * seg), i1 = min(V, i0 + seg);
+    float s = 0.f;
+    for (int i = i0; i < i1; ++i) s += weight(row[i]);
+    float incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wred[wave] = incl;
+    __syncthreads();
+    float wpre = 0.f, Z = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        wpre += (w < wave) ? wred[w] : 0.f;
+        Z += wred[w];
+    }
+    const float excl = wpre + (incl - s);
+    float uu = u[b];
+    uu = (uu >= 0.f) ? (uu < 1.f ? uu : 0x1.fffffep-1f) : 0.f;  // into [0, 1); NaN -> 0
+    const float r = uu * Z - excl;
+    const bool valid = r >= 0.f && s > 0.f;
+    int pick = -1;
+    if (valid) {
+        float loc = 0.f;
+        for (int i = i0; i < i1; ++i) {
+            const float w = weight(row[i]);
+            loc += w;
+            if (w > 0.f) {
+                pick = i;
+                if (loc > r) break;
+            }
+        }
+    }
+    picks[tid] = pick;
+    int best = valid ? tid : -1;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o, 64));
+    if (lane == 0) wbest[wave] = best;
+    __syncthreads();
+    if (tid == 0) {
+        int t = -1;
+        for (int w = 0; w < 16; ++w) t = max(t, wbest[w]);
+        const int p = t >= 0 ? picks[t] : 0;
+        out[b] = min(max(p, 0), V - 1);
+    }
+}
+
+hipError_t launch_sample(const float* logits, int B, int V, float scale, int top_k, const float* u,
+                         int32_t* out, hipStream_t st) {
+    hipLaunchKernelGGL(sample_kernel, dim3(B), dim3(1024), 0, st, logits, V, scale, top_k, u, out);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ weight repack ---
 // [N][K] row-major -> MFMA-blocked [Npad/32][K/16][32][16]; one thread per 8 elements.
 template <typename T>

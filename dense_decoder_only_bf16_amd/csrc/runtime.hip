@@ -610,6 +610,21 @@ nc_status nc_kv_export(nc_kv* kv, int32_t layer, void* k_out, void* v_out, void*
     return NC_OK;
 }
 
+nc_status nc_sample(const float* logits, int32_t B, int32_t V, float temperature, int32_t top_k,
+                    const float* u, int32_t* out, void* stream) {
+    if (!logits || !out) return fail(NC_ERR_INVALID_ARG, "NULL argument");
+    if (B < 1 || V < 1) return fail(NC_ERR_INVALID_ARG, "B and V must be >= 1");
+    if (!(temperature > 0.f)) {
+        LAUNCH(launch_argmax(logits, B, V, out, (hipStream_t)stream));
+        return NC_OK;
+    }
+    if (!u) return fail(NC_ERR_INVALID_ARG, "u is NULL");
+    const double scale = 1.4426950408889634 / (double)temperature;
+    if (!(scale < 3.0e38)) return fail(NC_ERR_INVALID_ARG, "temperature too small");
+    LAUNCH(launch_sample(logits, B, V, (float)scale, top_k, u, out, (hipStream_t)stream));
+    return NC_OK;
+}
+
 nc_status nc_kv_copy_rows(nc_kv* dst, const int32_t* dst_rows, nc_kv* src, const int32_t* src_rows,
                           int32_t n, void* stream) {
     try {

@@ -38,7 +38,7 @@ NC_KC_DECODE_ATTN = 4
 
 EXPORTED = ("nc_model_create", "nc_model_free", "nc_model_set_windows", "nc_kv_create", "nc_kv_free", "nc_kv_set_lens",
             "nc_kv_get_lens", "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step", "nc_argmax",
-            "nc_timing_enable", "nc_timing_read", "nc_last_error", "nc_abi_version")
+            "nc_sample", "nc_timing_enable", "nc_timing_read", "nc_last_error", "nc_abi_version")
 
 
 class NcError(RuntimeError):
@@ -87,6 +87,7 @@ def lib():
         L.nc_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.nc_decode_step.argtypes = [vp, vp, i32, vp, vp, vp]
         L.nc_argmax.argtypes = [vp, i32, i32, vp, vp]
+        L.nc_sample.argtypes = [vp, i32, i32, ctypes.c_float, i32, vp, vp, vp]
         L.nc_timing_enable.argtypes = [i32]
         L.nc_timing_read.argtypes = [ctypes.POINTER(nc_timing)]
         L.nc_last_error.argtypes = []
@@ -95,7 +96,7 @@ def lib():
         L.nc_abi_version.restype = i32
         for name in ("nc_model_create", "nc_model_set_windows", "nc_kv_create", "nc_kv_set_lens", "nc_kv_get_lens",
                      "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step", "nc_argmax",
-                     "nc_timing_enable", "nc_timing_read"):
+                     "nc_sample", "nc_timing_enable", "nc_timing_read"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -212,6 +213,11 @@ def nc_decode_step(m, tokens, B, kv, logits, stream=None):
 
 def nc_argmax(logits, B, V, out, stream=None):
     _check(lib().nc_argmax(_ptr(logits), B, V, _ptr(out), _stream(stream)))
+
+
+def nc_sample(logits, B, V, temperature, top_k, u, out, stream=None):
+    _check(lib().nc_sample(_ptr(logits), B, V, float(temperature), int(top_k), _ptr(u), _ptr(out),
+                           _stream(stream)))
 
 
 def nc_timing_enable(kernel_class):

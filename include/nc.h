@@ -165,6 +165,19 @@ nc_status nc_decode_step(nc_model* m, const int32_t* tokens_dev, int32_t B, nc_k
 nc_status nc_argmax(const float* logits_dev, int32_t B, int32_t V, int32_t* out_dev,
                     void* stream);
 
+/* Sampled pick, the engine's parallel sampling (apidog.com/th guide, part 6; the pages give
+ * no formula, so this is the plain temperature / top-k reading): over the logits of row b
+ * at or above its top_k-th largest value (every logit when top_k <= 0 or top_k >= V; ties
+ * with that value are all kept), probabilities proportional to exp(logit / temperature);
+ * out_dev[b] = the smallest token index whose cumulative probability, in token order,
+ * exceeds u_dev[b].  u_dev: fp32 [B] uniform numbers in [0, 1) drawn by the caller (values
+ * outside are clamped into it), so a draw is reproducible.  NaN logits have probability 0;
+ * logits must not be +inf.  temperature <= 0 (or NaN) is the greedy pick of nc_argmax and
+ * u_dev may then be NULL.  fp32 arithmetic: where u_dev[b] lies within about 1e-5 of a
+ * boundary of the cumulative distribution, the neighbouring token may be returned. */
+nc_status nc_sample(const float* logits_dev, int32_t B, int32_t V, float temperature,
+                    int32_t top_k, const float* u_dev, int32_t* out_dev, void* stream);
+
 /* Kernel timing, for diagnostics and roofline reports.  When a kernel class is enabled,
  * every kernel of that class is launched with a pair of HIP events that the dispatch itself
  * stamps with the kernel's start and end (hipExtLaunchKernel), on the launch stream; decode

@@ -113,6 +113,7 @@ def test_null_handles_are_rejected(L):
     assert L.nc_kv_export(None, 0, None, None, None) == nc.NC_ERR_INVALID_ARG
     assert L.nc_model_set_windows(None, None) == nc.NC_ERR_INVALID_ARG
     assert L.nc_kv_copy_rows(None, None, None, None, 0, None) == nc.NC_ERR_INVALID_ARG
+    assert L.nc_sample(None, 1, 1, 1.0, 0, None, None, None) == nc.NC_ERR_INVALID_ARG
     L.nc_model_free(None)
     L.nc_kv_free(None)
 

@@ -611,3 +611,80 @@ def test_copy_rows_errors(small):
     assert np.array_equal(a.lens(), [20, 20, 20]) and np.array_equal(b.lens(), [0, 0])
     a.close()
     b.close()
+
+
+# ---------------------------------------------------------------- sampling -------------
+def _check_samples(logits, temperature, top_k, u, got, tol=1e-4):
+    """Every pick equals the oracle's, or u lies within tol of the boundary between the two
+    picks in the oracle's fp64 cumulative distribution; every pick has probability > 0."""
+    from oracle import sample
+    want = sample(logits, temperature, top_k, u.astype(np.float64))
+    z = np.where(np.isnan(logits), -np.inf, logits.astype(np.float64))
+    n_diff = 0
+    for b in range(z.shape[0]):
+        if got[b] == want[b]:
+            continue
+        n_diff += 1
+        row = z[b]
+        if 0 < top_k < row.shape[0]:
+            kth = np.sort(row)[::-1][top_k - 1]
+            row = np.where(row >= kth, row, -np.inf)
+        p = np.exp((row - np.max(row)) / temperature)
+        cdf = np.cumsum(p) / np.sum(p)
+        g = int(got[b])
+        assert p[g] > 0, (b, g)
+        lo = cdf[g - 1] if g > 0 else 0.0
+        assert lo - tol <= u[b] <= cdf[g] + tol, (b, g, int(want[b]), float(u[b]), lo, cdf[g])
+    return n_diff
+
+
+@pytest.mark.parametrize("V", [65536, 1000, 1])
+def test_sampling_against_oracle(V):
+    torch = torch_mod()
+    rng = np.random.default_rng(80 + V)
+    B = 64
+    logits = (rng.standard_normal((B, V)) * 2.0).astype(np.float32)
+    if V > 1:
+        logits[:8] = np.round(logits[:8] * 4) / 4  # rows with many ties
+        logits[8, ::3] = -np.inf
+        logits[9, 1::5] = np.nan
+    u = rng.random(B).astype(np.float32)
+    u[0], u[1] = 0.0, np.nextafter(np.float32(1), np.float32(0))
+    dl = torch.from_numpy(logits).cuda()
+    du = torch.from_numpy(u).cuda()
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    diffs = 0
+    for temperature in (0.7, 1.0, 1.8):
+        for top_k in (0, 1, 7, 50, V):
+            nc.nc_sample(dl, B, V, temperature, top_k, du, out)
+            got = out.cpu().numpy()
+            diffs += _check_samples(logits, temperature, top_k, u, got)
+    print(f"[sampling V={V}] picks differing from the oracle (near a boundary): {diffs}", flush=True)
+    assert diffs <= 3
+    # temperature 0: the greedy pick, u not needed
+    nc.nc_sample(dl, B, V, 0.0, 0, None, out)
+    ref = torch.empty_like(out)
+    nc.nc_argmax(dl, B, V, ref)
+    assert torch.equal(out, ref)
+
+
+def test_sampling_frequencies_on_a_grid():
+    """u on a grid of 4096 points over one row: the picks reproduce the distribution's
+    slices (counts within 1 of N p_i, up to boundary rounding)."""
+    torch = torch_mod()
+    rng = np.random.default_rng(90)
+    V, N, t, k = 300, 4096, 1.2, 20
+    z = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    logits = np.ascontiguousarray(np.broadcast_to(z, (N, V)))
+    u = ((np.arange(N) + 0.5) / N).astype(np.float32)
+    out = torch.empty(N, dtype=torch.int32, device="cuda")
+    nc.nc_sample(torch.from_numpy(logits).cuda(), N, V, t, k, torch.from_numpy(u).cuda(), out)
+    got = out.cpu().numpy()
+    _check_samples(logits, t, k, u, got)
+    keep = np.argsort(z.astype(np.float64))[::-1][:k]
+    e = np.exp(z[keep].astype(np.float64) / t)
+    probs = np.zeros(V)
+    probs[keep] = e / e.sum()
+    counts = np.bincount(got, minlength=V)
+    assert np.all(np.abs(counts - N * probs) <= 2.0)
+    assert set(np.nonzero(counts)[0]) <= set(keep)
