@@ -10,9 +10,12 @@ context lengths uniform in [256, 2048]; tiny) build a separate decode context ou
 timed steps.  Prints one JSON line.
 
 Workloads d20-gqa (5 K/V heads) and d20-sssl (an SSSL pattern of 512-key sliding
-windows) run the d20 step with the later version's attention options.
+windows) run the d20 step with the later version's attention options; d12-sample runs
+the d12 step with sampled decode picks (temperature 1, top-50; the uniforms are drawn
+before the timed region).
 
-    python bench.py [--steps K] [--warmup W] [--workload d12|d20|d26|d30|d20-gqa|d20-sssl|tiny]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload d12|d20|d26|d30|d20-gqa|d20-sssl|d12-sample|tiny]
                     [--no-cpu]
 """
 
@@ -102,9 +105,9 @@ KERNEL_NAMES = {"decode_gemm": "dec_gemm_kernel (decode projections)",
 # (FETCH_SIZE, WRITE_SIZE) scaled by a plain-copy calibration, valid only for the kernel
 # sources they were taken with (hash of the listed files); otherwise the report says null.
 TRAFFIC = {
-    ("d12", "decode_gemm"): {"bytes_per_launch": 5.523e6, "profile": "profiles/d12_pmc_traffic.md",
+    ("d12", "decode_gemm"): {"bytes_per_launch": 5.529e6, "profile": "profiles/d12_pmc_traffic.md",
                              "sources": ("csrc/gemv.hip", "csrc/common.h", "csrc/kernels.h"),
-                             "sha": "4f1c0552b9b98811"},
+                             "sha": "58d2b198addfe82d"},
 }
 
 
@@ -221,6 +224,9 @@ def main():
             kv_d.set_lens(ctx)
             first = torch.from_numpy(make_tokens(V, 1, Bd, seed=3)[0]).cuda()
     zeros = np.zeros(max(Bp, 1), dtype=np.int32)
+    u_all = None
+    if steps and wl.temperature > 0:  # one uniform per row and step, drawn untimed
+        u_all = torch.from_numpy(np.random.default_rng(4).random((steps, Bd)).astype(np.float32)).cuda()
 
     def one_step(ev=None, per_decode_step=None):
         if ev:
@@ -237,9 +243,12 @@ def main():
             if not shared:
                 kv_d.set_lens(ctx)
                 tok.copy_(first)
-            for _ in range(steps):
+            for s in range(steps):
                 kv_d.decode(tok, dlog, stream)
-                nc.nc_argmax(dlog, Bd, V, tok, stream)
+                if u_all is None:
+                    nc.nc_argmax(dlog, Bd, V, tok, stream)
+                else:
+                    nc.nc_sample(dlog, Bd, V, wl.temperature, wl.top_k, u_all[s], tok, stream)
                 if per_decode_step:
                     per_decode_step()
         if ev:
@@ -271,7 +280,9 @@ def main():
         ctxd = ("the prefilled rows" if shared else
                 (f"context lengths U{{256..{wl.decode_context}}} (built untimed)" if wl.mixed_lengths
                  else f"context {wl.decode_context} (built untimed)"))
-        desc += (", then" if Bp else "") + f" {steps} greedy decode steps of {Bd} rows from {ctxd}"
+        pick = (f"sampled (temperature {wl.temperature}, top-{wl.top_k})" if wl.temperature > 0
+                else "greedy")
+        desc += (", then" if Bp else "") + f" {steps} {pick} decode steps of {Bd} rows from {ctxd}"
     out = {
         "metric": "prefill tokens/s + decode tokens/s (1 GPU); % MFMA peak / % HBM BW",
         "value": round((n_pre + n_dec) / (ms_per_step / 1000.0), 1),

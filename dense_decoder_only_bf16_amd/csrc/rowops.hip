@@ -214,129 +214,227 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// One 1024-thread workgroup per row.
-//  1. Threshold: the key of the top_k-th largest logit, by a radix select over the keys,
-//     8 bits at a time from the top (an LDS histogram of the candidates that match the
-//     digits chosen so far); top_k <= 0 or >= V keeps every logit.
+// One 1024-thread workgroup per row.  The row is taken in tiles of 65536 tokens held in
+// registers: thread t holds the 16 four-token chunks j 1024 + t of the tile (64 values),
+// loaded with independent 16-byte loads; a row of at most one tile is loaded once and
+// every pass runs on registers (longer rows reload their tiles per pass).  Tokens past V
+// are masked by index.
+//  1. Threshold: the key of the top_k-th largest logit (keys: order_key), found bit by
+//     bit from the top by counting the keys at or above each candidate (32 steps of one
+//     comparison per value); top_k <= 0 or >= V keeps every logit.
 //  2. m = the row's largest logit (always kept).
 //  3. Weights w_i = 2^((x_i - m) scale) for kept, non-NaN logits (scale = log2(e) / T).
-//     Thread t owns the contiguous segment [t seg, (t + 1) seg) of the row, so the block's
-//     exclusive scan of segment sums orders them by token index.  With target = u Z (Z the
-//     total), the last thread whose scan value is <= target and whose segment has mass
-//     walks its segment, summing in the same order as its segment sum, to the first
-//     token whose running sum exceeds target - (its scan value); if rounding carries the
-//     target past its end, its last token with mass is taken.
+//     Range (tile, j) is the 4096 contiguous tokens of chunk column j; with the range
+//     totals in token order and target = u Z, the last range with mass whose preceding
+//     total is <= target is scanned over its threads (4 tokens each, in token order), and
+//     the last thread with mass whose preceding sum is <= the remainder walks its 4
+//     tokens to the first whose running sum exceeds it (rounding past the end: its last
+//     token with mass).
+constexpr int SMP_J = 16;                  // four-token chunks per thread in a tile
+constexpr int SMP_TILE = SMP_J * 1024 * 4; // tokens per tile
+constexpr int SMP_MAX_TILES = 16;          // rows up to 2^20 tokens
+
+__device__ __forceinline__ void sample_load(const float* row, int V, int t0, bool vec, int tid,
+                                            f32x4 (&v)[SMP_J]) {
+#pragma unroll
+    for (int j = 0; j < SMP_J; ++j) {
+        const int i = t0 + 4 * (j * 1024 + tid);
+        if (vec && i + 3 < V) {
+            v[j] = *(const f32x4*)(row + i);
+        } else {
+            f32x4 t;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[e] = (i + e < V) ? row[i + e] : __builtin_nanf("");
+            v[j] = t;
+        }
+    }
+}
+
+template <bool MT>  // MT: more than one tile (V > 65536)
 __global__ __launch_bounds__(1024) void sample_kernel(const float* __restrict__ logits, int V,
                                                       float scale, int top_k,
                                                       const float* __restrict__ u,
                                                       int32_t* __restrict__ out) {
-    __shared__ uint32_t hist[256];
-    __shared__ int sel[2];
-    __shared__ float wred[16];
+    __shared__ int cntbuf[2][16];
+    __shared__ float wred[16][SMP_J];
+    __shared__ float rtot[SMP_MAX_TILES * SMP_J];
+    __shared__ float wsc[16];
     __shared__ int wbest[16];
-    __shared__ int picks[1024];
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* row = logits + (long long)b * V;
+    const bool vec = ((V & 3) == 0) && ((((uintptr_t)row) & 15) == 0);
+    const int ntiles = MT ? (V + SMP_TILE - 1) / SMP_TILE : 1;
+    f32x4 v[SMP_J];
+    sample_load(row, V, 0, vec, tid, v);
+    auto valid = [&](int t0, int j, int e) { return t0 + 4 * (j * 1024 + tid) + e < V; };
 
     uint32_t thresh = 0;
     if (top_k > 0 && top_k < V) {
-        uint32_t prefix = 0, mask = 0;
-        int kk = top_k;  // rank still wanted among the candidates
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            if (tid < 256) hist[tid] = 0;
-            __syncthreads();
-            for (int i = tid; i < V; i += 1024) {
-                const uint32_t k = order_key(row[i]);
-                if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
-            }
-            __syncthreads();
-            if (tid == 0) {
-                int cum = 0, d = 255;
-                for (; d > 0; --d) {
-                    if (cum + (int)hist[d] >= kk) break;
-                    cum += (int)hist[d];
+        // The largest key t with at least top_k keys >= t, one bit at a time from the top
+        // (per-lane counts, one wave sum per step).  The values are
+        // turned into keys in place (padding and NaN: key 0, never counted) and back after.
+        if (ntiles == 1) {
+#pragma unroll
+            for (int j = 0; j < SMP_J; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[j][e] = __uint_as_float(valid(0, j, e) ? order_key(v[j][e]) : 0u);
+        }
+        uint32_t prefix = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = prefix | (1u << bit);
+            int cnt = 0;
+            for (int tl = 0; tl < ntiles; ++tl) {
+                if (ntiles > 1) {
+                    sample_load(row, V, tl * SMP_TILE, vec, tid, v);
+#pragma unroll
+                    for (int j = 0; j < SMP_J; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            v[j][e] = __uint_as_float(valid(tl * SMP_TILE, j, e) ? order_key(v[j][e]) : 0u);
                 }
-                sel[0] = d;
-                sel[1] = kk - cum;
+#pragma unroll
+                for (int j = 0; j < SMP_J; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cnt += (__float_as_uint(v[j][e]) >= cand) ? 1 : 0;
             }
-            __syncthreads();
-            prefix |= (uint32_t)sel[0] << shift;
-            mask |= 0xFFu << shift;
-            kk = sel[1];
-            __syncthreads();  // sel and hist are rewritten in the next round
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+            if (lane == 0) cntbuf[bit & 1][wave] = cnt;
+            __syncthreads();  // one barrier a step: the two parities alternate
+            int total = 0;
+#pragma unroll
+            for (int w = 0; w < 16; ++w) total += cntbuf[bit & 1][w];
+            if (total >= top_k) prefix = cand;
         }
         thresh = prefix;
+        if (ntiles == 1) {  // keys back to values (key 0 -> a NaN)
+#pragma unroll
+            for (int j = 0; j < SMP_J; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t k = __float_as_uint(v[j][e]);
+                    v[j][e] = __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+                }
+        } else {
+            sample_load(row, V, 0, vec, tid, v);
+        }
     }
 
-    float m = -INFINITY;
-    for (int i = tid; i < V; i += 1024) m = fmaxf(m, row[i]);  // fmaxf skips NaN
-    m = wave_max(m);
-    if (lane == 0) wred[wave] = m;
-    __syncthreads();
-    m = wred[0];
+    float m = -INFINITY;  // fmaxf skips NaN (padding included)
+    for (int tl = 0; tl < ntiles; ++tl) {
+        if (ntiles > 1) sample_load(row, V, tl * SMP_TILE, vec, tid, v);
 #pragma unroll
-    for (int w = 1; w < 16; ++w) m = fmaxf(m, wred[w]);
+        for (int j = 0; j < SMP_J; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, v[j][e]);
+    }
+    m = wave_max(m);
+    if (lane == 0) wsc[wave] = m;
+    __syncthreads();
+    m = wsc[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) m = fmaxf(m, wsc[w]);
     if (m == -INFINITY) {  // no logit with mass
         if (tid == 0) out[b] = 0;
         return;
     }
-    __syncthreads();  // wred is reused below
-
     auto weight = [&](float x) {
         return (x == x && order_key(x) >= thresh) ? exp2f((x - m) * scale) : 0.f;
     };
-    const int seg = (V + 1023) / 1024;
-    const int i0 = min(V, tid * seg), i1 = min(V, i0 + seg);
-    float s = 0.f;
-    for (int i = i0; i < i1; ++i) s += weight(row[i]);
-    float incl = s;
+    // range totals (tile, j), in token order
+    for (int tl = 0; tl < ntiles; ++tl) {
+        if (ntiles > 1) sample_load(row, V, tl * SMP_TILE, vec, tid, v);
+        __syncthreads();  // wred of the previous tile has been read
+#pragma unroll
+        for (int j = 0; j < SMP_J; ++j) {
+            float t = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t += weight(v[j][e]);
+            t = wave_sum(t);
+            if (lane == 0) wred[wave][j] = t;
+        }
+        __syncthreads();
+        if (tid < SMP_J) {
+            float t = 0.f;
+            for (int w = 0; w < 16; ++w) t += wred[w][tid];
+            rtot[tl * SMP_J + tid] = t;
+        }
+    }
+    __syncthreads();
+    const int nr = ntiles * SMP_J;
+    float Z = 0.f;
+    for (int r = 0; r < nr; ++r) Z += rtot[r];
+    float uu = u[b];
+    uu = (uu >= 0.f) ? (uu < 1.f ? uu : 0x1.fffffep-1f) : 0.f;  // into [0, 1); NaN -> 0
+    const float target = uu * Z;
+    float pre = 0.f, rem = 0.f;
+    int rsel = 0;
+    for (int r = 0; r < nr; ++r) {
+        if (rtot[r] > 0.f && pre <= target) {
+            rsel = r;
+            rem = target - pre;
+        }
+        pre += rtot[r];
+    }
+    const int tl = rsel / SMP_J, js = rsel % SMP_J;
+    if (ntiles > 1) sample_load(row, V, tl * SMP_TILE, vec, tid, v);
+    float w4[4], st = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f32x4 c = v[0];
+#pragma unroll
+        for (int j = 1; j < SMP_J; ++j) c = (j == js) ? v[j] : c;
+        w4[e] = weight(c[e]);
+        st += w4[e];
+    }
+    // exclusive scan of the threads' sums over the range (thread order = token order)
+    float incl = st;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const float t = __shfl_up(incl, o, 64);
         if (lane >= o) incl += t;
     }
-    if (lane == 63) wred[wave] = incl;
+    if (lane == 63) wsc[wave] = incl;
     __syncthreads();
-    float wpre = 0.f, Z = 0.f;
+    float wpre = 0.f;
 #pragma unroll
-    for (int w = 0; w < 16; ++w) {
-        wpre += (w < wave) ? wred[w] : 0.f;
-        Z += wred[w];
-    }
-    const float excl = wpre + (incl - s);
-    float uu = u[b];
-    uu = (uu >= 0.f) ? (uu < 1.f ? uu : 0x1.fffffep-1f) : 0.f;  // into [0, 1); NaN -> 0
-    const float r = uu * Z - excl;
-    const bool valid = r >= 0.f && s > 0.f;
-    int pick = -1;
-    if (valid) {
-        float loc = 0.f;
-        for (int i = i0; i < i1; ++i) {
-            const float w = weight(row[i]);
-            loc += w;
-            if (w > 0.f) {
-                pick = i;
-                if (loc > r) break;
-            }
-        }
-    }
-    picks[tid] = pick;
-    int best = valid ? tid : -1;
+    for (int w = 0; w < 16; ++w) wpre += (w < wave) ? wsc[w] : 0.f;
+    const float r = rem - (wpre + (incl - st));
+    const bool ok = r >= 0.f && st > 0.f;
+    int best = ok ? tid : -1;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o, 64));
     if (lane == 0) wbest[wave] = best;
     __syncthreads();
-    if (tid == 0) {
-        int t = -1;
-        for (int w = 0; w < 16; ++w) t = max(t, wbest[w]);
-        const int p = t >= 0 ? picks[t] : 0;
-        out[b] = min(max(p, 0), V - 1);
+    int tbest = -1;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) tbest = max(tbest, wbest[w]);
+    if (tid == tbest) {
+        const int base = tl * SMP_TILE + 4 * (js * 1024 + tid);
+        int pick = -1, last = -1;
+        float loc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            loc += w4[e];
+            if (w4[e] > 0.f) {
+                last = base + e;
+                if (pick < 0 && loc > r) pick = base + e;
+            }
+        }
+        out[b] = min(max(pick >= 0 ? pick : last, 0), V - 1);
+    } else if (tbest < 0 && tid == 0) {
+        out[b] = 0;
     }
 }
 
 hipError_t launch_sample(const float* logits, int B, int V, float scale, int top_k, const float* u,
                          int32_t* out, hipStream_t st) {
-    hipLaunchKernelGGL(sample_kernel, dim3(B), dim3(1024), 0, st, logits, V, scale, top_k, u, out);
+    if (V > SMP_MAX_TILES * SMP_TILE) return hipErrorInvalidValue;
+    if (V <= SMP_TILE)
+        hipLaunchKernelGGL(sample_kernel<false>, dim3(B), dim3(1024), 0, st, logits, V, scale, top_k, u, out);
+    else
+        hipLaunchKernelGGL(sample_kernel<true>, dim3(B), dim3(1024), 0, st, logits, V, scale, top_k, u, out);
     return hipGetLastError();
 }
 

@@ -619,6 +619,7 @@ nc_status nc_sample(const float* logits, int32_t B, int32_t V, float temperature
         return NC_OK;
     }
     if (!u) return fail(NC_ERR_INVALID_ARG, "u is NULL");
+    if (V > (1 << 20)) return fail(NC_ERR_UNSUPPORTED, "sampling supports V <= 2^20");
     const double scale = 1.4426950408889634 / (double)temperature;
     if (!(scale < 3.0e38)) return fail(NC_ERR_INVALID_ARG, "temperature too small");
     LAUNCH(launch_sample(logits, B, V, (float)scale, top_k, u, out, (hipStream_t)stream));

@@ -50,6 +50,8 @@ class Workload:
     mixed_lengths: bool = False  # per-row context lengths drawn from U{256..2048}
     window_pattern: str = ""     # per-layer sliding windows, e.g. "SSSL" ("" = none)
     short_window: int = 0        # window of the pattern's S layers (keys back)
+    temperature: float = 0.0     # decode picks: > 0 samples (with top_k), else greedy
+    top_k: int = 0
 
 
 def from_depth(depth, vocab=65536, dtype="bf16", max_seq=2048, name=None):
@@ -75,6 +77,8 @@ WORKLOADS = {
     "d20-gqa": Workload(replace(D20, name="d20-gqa", n_kv_head=5), 32, 2048, 64, 128, 2048),
     "d20-sssl": Workload(replace(D20, name="d20-sssl"), 32, 2048, 64, 128, 2048,
                          window_pattern="SSSL", short_window=512),
+    # the d12 run with sampled instead of greedy decode picks (temperature 1, top-50)
+    "d12-sample": Workload(D12, 8, 2048, 8, 256, 2048, temperature=1.0, top_k=50),
 }
 
 

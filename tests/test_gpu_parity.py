@@ -638,7 +638,7 @@ def _check_samples(logits, temperature, top_k, u, got, tol=1e-4):
     return n_diff
 
 
-@pytest.mark.parametrize("V", [65536, 1000, 1])
+@pytest.mark.parametrize("V", [65536, 1000, 1, 100003])  # 100003: two register tiles
 def test_sampling_against_oracle(V):
     torch = torch_mod()
     rng = np.random.default_rng(80 + V)
