@@ -30,7 +30,13 @@ What is computed, and where the pages say so:
     [szyisi.cn, section on the base model and the Engine class; apidog.com part 6,
     inference engine];
   * batch generation: the prompt's cache copied to several rows that are sampled in
-    parallel [apidog.com part 6].
+    parallel [apidog.com part 6];
+  * later-version blocks [apidog.com part 1, architecture features and the three learned
+    mechanisms after them]: value embeddings on some layers, added to v through a gate of
+    3 sigmoid(...) per K/V head that reads the first channels of the attention input;
+    per-layer scaling of the residual stream against the first layer's input x0;
+    "smear", a gated copy of the previous token's embedding added to the current one;
+    "backout", a multiple of a middle layer's residual stream subtracted at the end.
 
 Readings where the pages are silent (each is listed with its reason in the design notes):
   * norm placement: pre-norm before attention and before the MLP, one norm right after the
@@ -47,6 +53,16 @@ Readings where the pages are silent (each is listed with its reason in the desig
     right extent is 0 under causality); w < 0 means the whole causal context;
   * window pattern: character l mod len(pattern) of the pattern gives layer l's window,
     'S' the short window and 'L' the whole context;
+  * later-version blocks, where the pages give only their update rules:
+      - smear: x_t = e_t + smear_lambda sigmoid(e_t[:C_s] . smear_gate) e_{t-1}, with e the
+        normalised token embedding, t the position in the row (position 0: x_0 = e_0);
+      - x0 = the stream after smear; layer l starts with
+        x <- resid_lambda[l] x + x0_lambda[l] x0;
+      - backout: xb = the stream at the start of layer backout_layer (after its scaling),
+        and x <- x - backout_lambda xb after the last layer, before the final norm;
+      - value embedding of layer l (where given): for K/V head j,
+        v_j += 3 sigmoid(h[:C_v] . ve_gate[l][j]) ve[l][token][j hd:(j + 1) hd], with h the
+        attention input norm(x);
   * sampling (the pages name parallel sampling but give no formula): keep the logits at
     or above the k-th largest (all with top_k <= 0), take probabilities proportional to
     exp(logit / temperature), and return the smallest token index whose cumulative
@@ -210,9 +226,13 @@ class OracleModel:
     "lm_head": [V, d]}.
     windows: per-layer attention windows (see causal_attention), or None for the whole
     causal context in every layer.
+    extras: the later-version blocks (see the readings above), a dict with any of
+    "resid_lambda", "x0_lambda" (n_layer floats each), "smear_gate" ([C_s]) with
+    "smear_lambda", "backout_layer" (-1: none) with "backout_lambda", and "ve", "ve_gate"
+    (dicts layer -> [V, n_kv*hd] and [n_kv, C_v]); None or missing keys: the plain model.
     """
 
-    def __init__(self, cfg, weights, windows=None):
+    def __init__(self, cfg, weights, windows=None, extras=None):
         for f in _CFG_FIELDS:
             setattr(self, f, getattr(cfg, f))
         assert self.n_head % self.n_kv_head == 0
@@ -223,6 +243,17 @@ class OracleModel:
         assert len(self.layers) == self.n_layer
         self.windows = [-1] * self.n_layer if windows is None else [int(w) for w in windows]
         assert len(self.windows) == self.n_layer
+        ex = extras or {}
+        self.resid_lambda = [float(a) for a in ex.get("resid_lambda", [1.0] * self.n_layer)]
+        self.x0_lambda = [float(a) for a in ex.get("x0_lambda", [0.0] * self.n_layer)]
+        g = ex.get("smear_gate")
+        self.smear_gate = None if g is None else np.asarray(g, dtype=F64)
+        self.smear_lambda = float(ex.get("smear_lambda", 0.0))
+        self.backout_layer = int(ex.get("backout_layer", -1))
+        self.backout_lambda = float(ex.get("backout_lambda", 0.0))
+        self.ve = {int(k): np.asarray(v, dtype=F64) for k, v in ex.get("ve", {}).items()}
+        self.ve_gate = {int(k): np.asarray(v, dtype=F64) for k, v in ex.get("ve_gate", {}).items()}
+        assert set(self.ve) == set(self.ve_gate)
         self._cos = np.zeros((0, self.head_dim // 2))
         self._sin = self._cos
 
@@ -233,13 +264,32 @@ class OracleModel:
                                                self.head_dim, self.rope_base)
         return self._cos, self._sin
 
-    def _qkv(self, lw, x, pos):
-        """Pre-attention norm, projections, RoPE and QK-norm for rows x at positions pos."""
+    def _embed(self, toks, prev):
+        """Stream entering layer 0 (before its scaling) for tokens toks [T] of one row;
+        prev is the row's token before toks[0], or None at position 0."""
+        e = rms_norm(self.wte[toks], self.norm_eps)
+        if self.smear_gate is None:
+            return e
+        c = self.smear_gate.shape[0]
+        gate = self.smear_lambda / (1.0 + np.exp(-(e[:, :c] @ self.smear_gate)))
+        before = np.zeros_like(e)
+        before[1:] = e[:-1]
+        if prev is not None:
+            before[0] = rms_norm(self.wte[prev], self.norm_eps)
+        return e + gate[:, None] * before
+
+    def _qkv(self, lw, x, pos, li=None, toks=None):
+        """Pre-attention norm, projections, RoPE and QK-norm for rows x at positions pos
+        (layer li's value embedding of tokens toks added to v where the layer has one)."""
         t = x.shape[0]
         h = rms_norm(x, self.norm_eps)
         q = linear(h, lw["wq"]).reshape(t, self.n_head, self.head_dim)
         k = linear(h, lw["wk"]).reshape(t, self.n_kv_head, self.head_dim)
         v = linear(h, lw["wv"]).reshape(t, self.n_kv_head, self.head_dim)
+        if li in self.ve:
+            c = self.ve_gate[li].shape[1]
+            gate = 3.0 / (1.0 + np.exp(-(h[:, :c] @ self.ve_gate[li].T)))  # [t, n_kv]
+            v = v + gate[:, :, None] * self.ve[li][toks].reshape(t, self.n_kv_head, self.head_dim)
         cos, sin = self._tables(int(np.max(pos)) + 1)
         q = rms_norm(rope(q, pos[:, None], cos, sin), self.norm_eps)
         k = rms_norm(rope(k, pos[:, None], cos, sin), self.norm_eps)
@@ -255,7 +305,22 @@ class OracleModel:
     def new_cache(self, batch, max_seq):
         shape = (self.n_layer, batch, max_seq, self.n_kv_head, self.head_dim)
         return {"k": np.zeros(shape, dtype=F64), "v": np.zeros(shape, dtype=F64),
+                "tok": np.zeros((batch, max_seq), dtype=np.int64),
                 "lens": np.zeros(batch, dtype=np.int64), "max_seq": max_seq}
+
+    def _layers(self, x, on_layer):
+        """The layers over stream x (from _embed); on_layer(li, lw, x) runs attention and MLP
+        of layer li on its (scaled) input and returns the new stream."""
+        x0 = x
+        xb = None
+        for li, lw in enumerate(self.layers):
+            x = self.resid_lambda[li] * x + self.x0_lambda[li] * x0
+            if li == self.backout_layer:
+                xb = x
+            x = on_layer(li, lw, x)
+        if xb is not None:
+            x = x - self.backout_lambda * xb
+        return x
 
     # -- prefill ---------------------------------------------------------------------
     def prefill(self, tokens, max_seq=None, logits_at=None, cache=None):
@@ -275,15 +340,16 @@ class OracleModel:
         logits = np.empty((b_sz, at.shape[0], self.vocab), dtype=F64)
         pos = np.arange(t_len)
         for b in range(b_sz):
-            x = rms_norm(self.wte[tokens[b]], self.norm_eps)
-            for li, lw in enumerate(self.layers):
-                q, k, v = self._qkv(lw, x, pos)
+            def layer(li, lw, x, b=b):
+                q, k, v = self._qkv(lw, x, pos, li, tokens[b])
                 cache["k"][li, b, :t_len] = k
                 cache["v"][li, b, :t_len] = v
                 y = causal_attention(q, k, v, pos, self.windows[li])
                 x = x + linear(y.reshape(t_len, -1), lw["wo"])
-                x = x + self._mlp(lw, x)
+                return x + self._mlp(lw, x)
+            x = self._layers(self._embed(tokens[b], None), layer)
             logits[b] = self._head(x[at])
+        cache["tok"][:, :t_len] = tokens
         cache["lens"][:] = t_len
         return logits, cache
 
@@ -299,15 +365,18 @@ class OracleModel:
         for b in range(b_sz):
             p = int(cache["lens"][b])
             pos = np.array([p])
-            x = rms_norm(self.wte[tokens[b:b + 1]], self.norm_eps)
-            for li, lw in enumerate(self.layers):
-                q, k, v = self._qkv(lw, x, pos)
+
+            def layer(li, lw, x, b=b, p=p, pos=pos):
+                q, k, v = self._qkv(lw, x, pos, li, tokens[b:b + 1])
                 cache["k"][li, b, p] = k[0]
                 cache["v"][li, b, p] = v[0]
                 y = causal_attention(q, cache["k"][li, b, :p + 1], cache["v"][li, b, :p + 1],
                                      pos, self.windows[li])
                 x = x + linear(y.reshape(1, -1), lw["wo"])
-                x = x + self._mlp(lw, x)
+                return x + self._mlp(lw, x)
+            prev = int(cache["tok"][b, p - 1]) if p > 0 else None
+            x = self._layers(self._embed(tokens[b:b + 1], prev), layer)
+            cache["tok"][b, p] = tokens[b]
             logits[b] = self._head(x)[0]
         cache["lens"] += 1
         return logits
@@ -328,6 +397,7 @@ class OracleModel:
         n = min(dst_cache["max_seq"], src_cache["max_seq"])
         k = src_cache["k"][:, list(src_rows), :n].copy()
         v = src_cache["v"][:, list(src_rows), :n].copy()
+        tk = src_cache["tok"][list(src_rows), :n].copy()
         lens = src_cache["lens"][list(src_rows)].copy()
         assert np.all(lens <= dst_cache["max_seq"])
         for i, d in enumerate(dst_rows):
@@ -335,6 +405,8 @@ class OracleModel:
             dst_cache["v"][:, d] = 0.0
             dst_cache["k"][:, d, :n] = k[:, i]
             dst_cache["v"][:, d, :n] = v[:, i]
+            dst_cache["tok"][d] = 0
+            dst_cache["tok"][d, :n] = tk[i]
             dst_cache["lens"][d] = lens[i]
 
     def truncate(self, cache, lens):

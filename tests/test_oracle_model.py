@@ -340,3 +340,161 @@ def test_param_count_matches_pages():
     from dense_decoder_only_bf16_amd.inputs import weight_shapes
     tot = sum(a * b for _, (a, b) in weight_shapes(sh))
     assert tot == param_count(20, d, 10, 1, 128, 4 * d, 65536) == 502_005_760
+
+
+# ------------------------------------------------------- later-version blocks ---------
+def _sig(z):
+    return 1.0 / (1.0 + math.exp(-z))
+
+
+def scalar_forward_extras(shape, w, tokens, ex):
+    """scalar_forward with the later-version blocks, from their update rules: smear on the
+    embeddings, per-layer residual scaling against x0, value embeddings through a
+    3 sigmoid gate per K/V head, and backout of a layer's input at the end."""
+    eps, hd, nh, nkv = shape.norm_eps, shape.head_dim, shape.n_head, shape.n_kv_head
+    wl = lambda a: np.asarray(a, dtype=float).tolist()  # noqa: E731
+    es = [_norm(wl(w["wte"][t]), eps) for t in tokens]
+    sg = wl(ex["smear_gate"])
+    xs = []
+    for p, e in enumerate(es):
+        if p == 0:
+            xs.append(list(e))
+        else:
+            g = ex["smear_lambda"] * _sig(sum(a * b for a, b in zip(e[:len(sg)], sg)))
+            xs.append([a + g * b for a, b in zip(e, es[p - 1])])
+    x0s = [list(x) for x in xs]
+    xb = None
+    for li, lw in enumerate(w["layers"]):
+        lam, mu = ex["resid_lambda"][li], ex["x0_lambda"][li]
+        xs = [[lam * a + mu * b for a, b in zip(x, x0)] for x, x0 in zip(xs, x0s)]
+        if li == ex["backout_layer"]:
+            xb = [list(x) for x in xs]
+        wq, wk, wv, wo = wl(lw["wq"]), wl(lw["wk"]), wl(lw["wv"]), wl(lw["wo"])
+        wfc, wproj = wl(lw["wfc"]), wl(lw["wproj"])
+        qs, ks, vs = [], [], []
+        for p, x in enumerate(xs):
+            h = _norm(x, eps)
+            q, k, v = _matvec(wq, h), _matvec(wk, h), _matvec(wv, h)
+            if li in ex["ve"]:
+                gw, table = wl(ex["ve_gate"][li]), wl(ex["ve"][li])
+                for j in range(nkv):
+                    g = 3.0 * _sig(sum(a * b for a, b in zip(h[:len(gw[j])], gw[j])))
+                    for c in range(hd):
+                        v[j * hd + c] += g * table[tokens[p]][j * hd + c]
+            qs.append([_norm(_rot(q[i * hd:(i + 1) * hd], p, shape.rope_base), eps)
+                       for i in range(nh)])
+            ks.append([_norm(_rot(k[i * hd:(i + 1) * hd], p, shape.rope_base), eps)
+                       for i in range(nkv)])
+            vs.append([v[i * hd:(i + 1) * hd] for i in range(nkv)])
+        new = []
+        for p, x in enumerate(xs):
+            y = []
+            for hh in range(nh):
+                g = hh * nkv // nh
+                sc = [sum(qs[p][hh][c] * ks[j][g][c] for c in range(hd)) / math.sqrt(hd)
+                      for j in range(p + 1)]
+                m = max(sc)
+                e = [math.exp(s - m) for s in sc]
+                z = sum(e)
+                y += [sum(e[j] * vs[j][g][c] for j in range(p + 1)) / z for c in range(hd)]
+            x = [a + b for a, b in zip(x, _matvec(wo, y))]
+            u = [max(a, 0.0) ** 2 for a in _matvec(wfc, _norm(x, eps))]
+            x = [a + b for a, b in zip(x, _matvec(wproj, u))]
+            new.append(x)
+        xs = new
+    if xb is not None:
+        xs = [[a - ex["backout_lambda"] * b for a, b in zip(x, xbb)] for x, xbb in zip(xs, xb)]
+    lm = wl(w["lm_head"])
+    return [[shape.softcap * math.tanh(z / shape.softcap)
+             for z in _matvec(lm, _norm(x, eps))] for x in xs]
+
+
+def micro_extras(shape, seed, ve_layers=(1,), c_s=3, c_v=5):
+    r = np.random.default_rng(seed)
+    kvd = shape.n_kv_head * shape.head_dim
+    return {"resid_lambda": list(r.uniform(0.6, 1.4, shape.n_layer)),
+            "x0_lambda": list(r.uniform(-0.3, 0.5, shape.n_layer)),
+            "smear_gate": r.standard_normal(c_s), "smear_lambda": 0.7,
+            "backout_layer": shape.n_layer // 2, "backout_lambda": 0.4,
+            "ve": {l: r.standard_normal((shape.vocab, kvd)) * 0.5 for l in ve_layers},
+            "ve_gate": {l: r.standard_normal((shape.n_kv_head, c_v)) for l in ve_layers}}
+
+
+@pytest.mark.parametrize("n_kv", [1, 2])
+def test_extras_match_scalar_loops(n_kv):
+    shape = replace(MICRO, n_layer=3, n_kv_head=n_kv)
+    w = micro_weights(shape, seed=31)
+    ex = micro_extras(shape, 32, ve_layers=(0, 2))
+    toks = make_tokens(shape.vocab, 2, 6, seed=33)
+    logits, _ = OracleModel(shape, w, extras=ex).prefill(toks)
+    for b in range(2):
+        ref = np.array(scalar_forward_extras(shape, w, toks[b].tolist(), ex))
+        assert np.allclose(logits[b], ref, rtol=0, atol=1e-12)
+
+
+def test_neutral_extras_are_the_plain_model():
+    shape = replace(MICRO, n_layer=2)
+    w = micro_weights(shape, seed=34)
+    ex = micro_extras(shape, 35)
+    ex.update(resid_lambda=[1.0, 1.0], x0_lambda=[0.0, 0.0], smear_lambda=0.0,
+              backout_lambda=0.0, ve={1: np.zeros_like(ex["ve"][1])})
+    toks = make_tokens(shape.vocab, 2, 7, seed=36)
+    a, _ = OracleModel(shape, w, extras=ex).prefill(toks)
+    b, _ = OracleModel(shape, w).prefill(toks)
+    assert np.array_equal(a, b)
+
+
+def test_backout_and_lambdas_closed_form():
+    """Blocks that add nothing (Wo = Wproj = 0): the final stream is
+    (1 - b) (l1 (l0 + m0) + m1) e, so at eps = 0 the logits are those of the plain model
+    with the sign of that factor (here negative: the softcapped logits flip sign)."""
+    shape = replace(MICRO, n_layer=2, norm_eps=0.0)
+    w = micro_weights(shape, seed=37)
+    for lw in w["layers"]:
+        lw["wo"][:] = 0.0
+        lw["wproj"][:] = 0.0
+    ex = {"resid_lambda": [0.9, 1.2], "x0_lambda": [0.3, -0.2], "backout_layer": 1,
+          "backout_lambda": 1.5}
+    toks = make_tokens(shape.vocab, 1, 5, seed=38)
+    got, _ = OracleModel(shape, w, extras=ex).prefill(toks)
+    plain, _ = OracleModel(shape, w).prefill(toks)
+    factor = (1 - 1.5) * (1.2 * (0.9 + 0.3) - 0.2)
+    assert factor < 0
+    assert np.allclose(got, -plain, rtol=0, atol=1e-12)
+
+
+def test_extras_decode_truncate_extend_copy():
+    """With every block on: decode steps reproduce prefill (smear reads the cached previous
+    token), a truncated row continues like a shorter prefill, appended chunks and copied
+    rows continue like one prefill of their whole sequence; position 0 is untouched by
+    smear (no previous token)."""
+    shape = replace(MICRO, n_layer=3, n_kv_head=2)
+    w = micro_weights(shape, seed=39)
+    ex = micro_extras(shape, 40, ve_layers=(1,))
+    m = OracleModel(shape, w, extras=ex)
+    toks = make_tokens(shape.vocab, 2, 10, seed=41)
+    full, _ = m.prefill(toks)
+    _, cache = m.prefill(toks[:, :4], max_seq=12)
+    steps = np.stack([m.decode_step(cache, toks[:, t]) for t in range(4, 10)], 1)
+    assert np.allclose(steps, full[:, 4:], rtol=0, atol=1e-11)
+    m.truncate(cache, [3, 6])
+    got = m.decode_step(cache, toks[:, 9])
+    for b, n in enumerate((3, 6)):
+        seq = np.concatenate([toks[b, :n], toks[b, 9:10]])[None]
+        ref, _ = m.prefill(seq, logits_at=[n])
+        assert np.allclose(got[b], ref[0, 0], rtol=0, atol=1e-11)
+    _, cache = m.prefill(toks[:, :5], max_seq=12)
+    ext = m.extend(cache, toks[:, 5:10])
+    assert np.allclose(ext, full[:, 5:], rtol=0, atol=1e-11)
+    many = m.new_cache(2, 12)
+    m.copy_rows(many, [1, 0], cache, [0, 0])
+    more = make_tokens(shape.vocab, 2, 1, seed=42)
+    got = m.decode_step(many, more[:, 0])
+    for b in range(2):
+        seq = np.concatenate([toks[0], more[b]])[None]
+        ref, _ = m.prefill(seq, logits_at=[10])
+        assert np.allclose(got[b], ref[0, 0], rtol=0, atol=1e-11)
+    no_smear = dict(ex, smear_lambda=0.0)
+    z, _ = OracleModel(shape, w, extras=no_smear).prefill(toks)
+    assert np.allclose(z[:, 0], full[:, 0], rtol=0, atol=1e-13)
+    assert np.max(np.abs(z[:, 1:] - full[:, 1:])) > 1e-3
