@@ -108,6 +108,16 @@ __device__ __forceinline__ float row_scale_wave(const float* ss, int parts, int 
     return 1.0f / sqrtf(wave_sum(s) / (float)dim + eps);
 }
 
+// Gate of a value embedding for value head j of a row (every lane of the wave calls it):
+// 3 sigmoid(r xin[:ch] . gate[j]).
+template <typename T>
+__device__ __forceinline__ float value_embed_gate(const T* __restrict__ gate, int j, int ch,
+                                                  const float* __restrict__ xin, float r, int lane) {
+    float dot = lane < ch ? to_f32(gate[(long long)j * ch + lane]) * xin[lane] : 0.f;
+    dot = wave_sum(dot) * r;
+    return 3.0f / (1.0f + expf(-dot));
+}
+
 // 2^x on the hardware exponential unit.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

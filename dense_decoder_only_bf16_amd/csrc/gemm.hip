@@ -110,7 +110,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[2
                     if (ok) p.out_f32[o] = p.cap * tanh_f32(v * rs[rl] / p.cap);
                 } else {  // EPI_RESID
                     if (ok) {
-                        const float xn = p.out_f32[o] + v;
+                        const float xn = resid_value(p.rx, o, p.out_f32[o], v);
                         p.out_f32[o] = xn;
                         const T hi = from_f32<T>(xn);
                         ((T*)p.out_t)[o] = hi;

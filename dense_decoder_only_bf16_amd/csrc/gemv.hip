@@ -46,7 +46,7 @@ __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, in
     } else {  // EPI_RESID
         float xn = 0.f;
         if (ok) {
-            xn = x_old + v;
+            xn = resid_value(p.rx, o, x_old, v);
             p.out_f32[o] = xn;
             const T hi = from_f32<T>(xn);
             ((T*)p.out_t)[ob] = hi;

@@ -49,6 +49,21 @@ __host__ __device__ inline long long blocked_index(int n, int k, int K) {
 }
 hipError_t launch_repack(DType dt, const void* src, void* dst, int N, int K, hipStream_t st);
 
+// RESID with the later version's blocks (x0 non-null): the new residual is
+//   x = ra (x_old + C) + rb x0 + rc xb        (xb null: no last term)
+// with x0, xb fp32 [M][ldo] like x; xb_out (if set) receives a copy of the new x.
+struct ResidExtra {
+    const float* x0; const float* xb; float* xb_out;
+    float ra, rb, rc;
+};
+__host__ __device__ inline float resid_value(const ResidExtra& e, long long o, float x_old, float c) {
+    if (!e.x0) return x_old + c;
+    float x = e.ra * (x_old + c) + e.rb * e.x0[o];
+    if (e.xb) x += e.rc * e.xb[o];
+    if (e.xb_out) e.xb_out[o] = x;
+    return x;
+}
+
 struct GemmArgs {
     const void* A;  // [M][lda] dtype, K contiguous
     const void* B;  // blocked weight (see above), Npad rows
@@ -68,6 +83,7 @@ struct GemmArgs {
     // RELU2 / RESID: also write value - dtype(value) in dtype here (the low part a later
     // compensated product reads).  Null: not written.
     void* out_lo;
+    ResidExtra rx;  // RESID: the later version's residual scaling and backout
 };
 
 // Prefill product (M in the thousands): 256 x 256 tiles.
@@ -92,22 +108,45 @@ struct DecGemmArgs {
     const void* A_lo;   // compensated operand, as in GemmArgs (bf16 only; null: plain A)
     void* out_lo;       // RELU2 / RESID low-part output, as in GemmArgs (null: not written)
     float* part;        // bf16 with M > 32: fp32 split-K partials, dec_gemm_part_elems(M, N, K)
+    ResidExtra rx;      // RESID: as in GemmArgs (x0, xb row-major with stride ldo)
 };
 int dec_gemm_tile_n();
 // Elements of DecGemmArgs::part that a product of this shape needs (0: none).
 long long dec_gemm_part_elems(DType dt, Epi epi, int M, int N, int K);
 hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t st, int variant = 0);
 
-// x[m] = norm(wte[tok[m]]) (fp32, row-major), act[m] = dtype copy (row-major, or blocked
-// with rows rounded up to 32 when `blocked`), ss[m] = sum(x^2).
-hipError_t launch_embed(DType dt, const int32_t* tok, int M, const void* wte, int vocab, int d,
-                        float eps, float* x, void* act, float* ss, bool blocked, hipStream_t st);
+// x[m] = scale0 norm(wte[tok[m]]) (fp32, row-major), act[m] = dtype copy (row-major, or
+// blocked with rows rounded up to 32 when `blocked`), ss[m] = sum(x^2); with the later
+// version's smear, the previous token's normalised embedding is mixed in first (row m is
+// token m % T of batch row m / T at position lens[b] + m % T; hist [B][S] holds each row's
+// tokens by position), and the unscaled result is x0.
+struct EmbedArgs {
+    const int32_t* tok; int M, T;
+    const void* wte; int vocab, d;
+    float eps, scale0;
+    float* x; void* act; float* ss; bool blocked;
+    const int32_t* lens;          // positions of each row's first token (null: 0)
+    int32_t* hist; int S;         // token history (null: none)
+    const void* smear_gate; int smear_ch; float smear_lambda;  // null gate: no smear
+    float* x0;                    // stream before the layer-0 scaling (null: not written)
+    float* xb;                    // copy of x (backout source at layer 0; null: none)
+};
+hipError_t launch_embed(DType dt, const EmbedArgs& a, hipStream_t st);
 
 // Pre-attention finish of the raw QKV product part[z][m][(H+2 nkv)*hd] (H query heads, then
 // nkv key heads, then nkv value heads): scale row m by r_m, rotate the q and k heads at
 // position pos(m), QK-normalise, write q [m][H][hd] and k, v into the cache of the layer.
 // Token m is token m % T of batch row b = m / T, at position pos = lens[b] + m % T (the
 // row's current length, 0 when lens is null).
+// Value embedding of a layer (the later version's blocks; ve null: none): value head j of
+// row m gains 3 sigmoid(r_m xin[m][:ve_ch] . ve_gate[j]) ve[tok[m]][j hd .. (j + 1) hd),
+// r_m xin the row's attention input (xin fp32 with row stride xin_stride, ve_ch <= 64);
+// ve [vocab][nkv hd] and ve_gate [nkv][ve_ch] in the model dtype.
+struct ValueEmbed {
+    const void* ve; const void* ve_gate; int ve_ch, vocab;
+    const int32_t* tok; const float* xin; int xin_stride;
+};
+
 struct QkvPostArgs {
     const float* part; int splits; long long z_stride;
     int M, T, H, hd, nkv;
@@ -119,6 +158,7 @@ struct QkvPostArgs {
     void* vtc;        // V cache of this layer, transposed: [B][nkv][hd][S]
     int S;            // cache capacity (positions)
     float eps;
+    ValueEmbed vemb;  // tok[m], xin row m
 };
 hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st);
 
@@ -149,6 +189,7 @@ struct DecAttnArgs {
     int iters;            // 64-key blocks per wave: attn_decode_iters(B nkv, span)
     int max_slots;        // partial slots per unit, >= attn_decode_slots(B nkv, S, span)
     float scale_log2;     // set by the launcher
+    ValueEmbed vemb;      // tok[b], xin row b
 };
 // Keys a query can see at most: min(S, window + 1), or S without a window.
 int attn_decode_span(int S, int window);
@@ -177,8 +218,10 @@ struct KvRowCopy {
     int n;
     int32_t dst[MAX], src[MAX], len[MAX];
 };
+// hsrc / hdst: token histories [B][S] (both null: none), copied like the keys.
 hipError_t launch_kv_copy_rows(const KvRowCopy& rc, const void* ksrc, const void* vsrc, void* kdst,
                                void* vdst, int L, int nkv, int hd, int es, int Bsrc, int Ssrc, int Bdst,
-                               int Sdst, int32_t* lens_dst, hipStream_t st);
+                               int Sdst, int32_t* lens_dst, const int32_t* hsrc, int32_t* hdst,
+                               hipStream_t st);
 
 }  // namespace nc

@@ -13,25 +13,15 @@ namespace nc {
 
 // ------------------------------------------------------------------ embedding -------
 // One wave per row; each lane moves 8 consecutive elements per 16/32-byte access.
+// Normalised embedding e of a token: chunks in v[], returned scale r (e = r wte[tok]).
 template <typename T>
-__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok, int M,
-                                                    const T* __restrict__ wte, int vocab, int d,
-                                                    float eps, float* __restrict__ x,
-                                                    T* __restrict__ act, float* __restrict__ ss,
-                                                    bool blocked) {
+__device__ __forceinline__ float embed_row(const T* __restrict__ wte, int t, int nch, int d, float eps,
+                                           int lane, typename Chunk<T>::type (&v)[8]) {
     typedef typename Chunk<T>::type CT;
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= M) return;
-    int t = tok[row];
-    t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
     const T* e = wte + (long long)t * d;
-    const int nch = d / 8;   // d is a multiple of 64
-    constexpr int MAXC = 8;  // up to 8 chunks per lane: d <= 4096
-    CT v[MAXC];
     float s = 0.f;
 #pragma unroll
-    for (int u = 0; u < MAXC; ++u) {
+    for (int u = 0; u < 8; ++u) {
         const int cidx = lane + 64 * u;
         v[u] = load_masked(e + (cidx < nch ? cidx : 0) * 8, cidx < nch);
 #pragma unroll
@@ -41,38 +31,91 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
         }
     }
     s = wave_sum(s);
-    const float r = 1.0f / sqrtf(s / (float)d + eps);
+    return 1.0f / sqrtf(s / (float)d + eps);
+}
+
+// Row m is token m % T of batch row b = m / T at position pos = lens[b] + m % T (lens null:
+// 0).  x = scale0 e' with e' = e, or with smear e + lambda sigmoid(e[:C] . g) e_prev (e_prev
+// the normalised embedding of the row's previous token: the chunk's previous token, else
+// hist[b][pos - 1]; none at position 0); x0 = e' and xb = x where requested; hist[b][pos] =
+// token.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
+    typedef typename Chunk<T>::type CT;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= a.M) return;
+    auto clamp_tok = [&](int t) { return t < 0 ? 0 : (t >= a.vocab ? a.vocab - 1 : t); };
+    const int t = clamp_tok(a.tok[row]);
+    const int nch = a.d / 8;  // d is a multiple of 64; up to 8 chunks per lane: d <= 4096
+    const T* wte = (const T*)a.wte;
+    CT v[8];
+    const float r = embed_row<T>(wte, t, nch, a.d, a.eps, lane, v);
+    float xs[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) xs[u][k] = to_f32(v[u][k]) * r;
+    const int T_ = a.T > 0 ? a.T : 1;
+    const int b = row / T_, ti = row % T_;
+    const int pos = ti + (a.lens ? a.lens[b] : 0);
+    const bool in_cache = a.hist && pos >= 0 && pos < a.S;
+    if (a.smear_gate) {
+        const int prev = ti > 0 ? clamp_tok(a.tok[row - 1])
+                                : ((in_cache && pos > 0) ? clamp_tok(a.hist[(long long)b * a.S + pos - 1]) : -1);
+        if (prev >= 0) {  // wave-uniform
+            const T* g = (const T*)a.smear_gate;
+            float dot = 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int c = (lane + 64 * u) * 8 + k;
+                    dot += c < a.smear_ch ? xs[u][k] * to_f32(g[c]) : 0.f;
+                }
+            dot = wave_sum(dot);
+            const float gate = a.smear_lambda / (1.0f + expf(-dot));
+            const float rp = embed_row<T>(wte, prev, nch, a.d, a.eps, lane, v);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) xs[u][k] += gate * to_f32(v[u][k]) * rp;
+        }
+    }
+    if (in_cache && lane == 0) a.hist[(long long)b * a.S + pos] = t;
     float s2 = 0.f;
 #pragma unroll
-    for (int u = 0; u < MAXC; ++u) {
+    for (int u = 0; u < 8; ++u) {
         const int cidx = lane + 64 * u;
         if (cidx < nch) {
-            f32x8 xo;
+            f32x8 xo, x0o;
             CT ao;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const float f = to_f32(v[u][k]) * r;
+                const float f = xs[u][k] * a.scale0;
+                x0o[k] = xs[u][k];
                 xo[k] = f;
                 ao[k] = from_f32<T>(f);
                 s2 += f * f;
             }
-            *(f32x8*)(x + (long long)row * d + cidx * 8) = xo;
-            *(CT*)(act + (blocked ? blocked_index(row, cidx * 8, d) : (long long)row * d + cidx * 8)) = ao;
+            const long long o = (long long)row * a.d + cidx * 8;
+            *(f32x8*)(a.x + o) = xo;
+            if (a.x0) *(f32x8*)(a.x0 + o) = x0o;
+            if (a.xb) *(f32x8*)(a.xb + o) = xo;
+            *(CT*)((T*)a.act + (a.blocked ? blocked_index(row, cidx * 8, a.d) : o)) = ao;
         }
     }
     s2 = wave_sum(s2);
-    if (lane == 0) ss[row] = s2;
+    if (lane == 0) a.ss[row] = s2;
 }
 
-hipError_t launch_embed(DType dt, const int32_t* tok, int M, const void* wte, int vocab, int d,
-                        float eps, float* x, void* act, float* ss, bool blocked, hipStream_t st) {
-    dim3 grid((M + 3) / 4);
+hipError_t launch_embed(DType dt, const EmbedArgs& a, hipStream_t st) {
+    if (a.d % 64 || a.d > 4096 || a.smear_ch > a.d) return hipErrorInvalidValue;
+    dim3 grid((a.M + 3) / 4);
     if (dt == BF16)
-        hipLaunchKernelGGL(embed_kernel<bf16>, grid, dim3(256), 0, st, tok, M, (const bf16*)wte,
-                           vocab, d, eps, x, (bf16*)act, ss, blocked);
+        hipLaunchKernelGGL(embed_kernel<bf16>, grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL(embed_kernel<float>, grid, dim3(256), 0, st, tok, M, (const float*)wte,
-                           vocab, d, eps, x, (float*)act, ss, blocked);
+        hipLaunchKernelGGL(embed_kernel<float>, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -104,6 +147,19 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
         }
         v1 *= r;
         v2 *= r;
+    }
+    if (j >= a.H + a.nkv && a.vemb.ve) {  // wave-uniform
+        const ValueEmbed& ve = a.vemb;
+        const int jj = j - a.H - a.nkv;
+        const float g = value_embed_gate<T>((const T*)ve.ve_gate, jj, ve.ve_ch,
+                                            ve.xin + (long long)m * ve.xin_stride, r, lane);
+        int tk = ve.tok[m];
+        tk = tk < 0 ? 0 : (tk >= ve.vocab ? ve.vocab - 1 : tk);
+        const T* e = (const T*)ve.ve + ((long long)tk * a.nkv + jj) * a.hd;
+        if (act) {
+            v1 += g * to_f32(e[lane]);
+            v2 += g * to_f32(e[lane + half]);
+        }
     }
     if (j < a.H + a.nkv) {
         float c = 0.f, sn = 0.f;
@@ -516,7 +572,9 @@ __global__ __launch_bounds__(256) void kv_copy_rows_kernel(KvRowCopy rc, const c
                                                           const char* __restrict__ vsrc,
                                                           char* __restrict__ kdst, char* __restrict__ vdst,
                                                           int nkv, int hd, int es, int Bsrc, int Ssrc,
-                                                          int Bdst, int Sdst, int32_t* lens_dst) {
+                                                          int Bdst, int Sdst, int32_t* lens_dst,
+                                                          const int32_t* __restrict__ hsrc,
+                                                          int32_t* __restrict__ hdst) {
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
     const int i = blockIdx.x, l = blockIdx.y / nkv, kvh = blockIdx.y % nkv;
     const int len = rc.len[i];
@@ -528,6 +586,10 @@ __global__ __launch_bounds__(256) void kv_copy_rows_kernel(KvRowCopy rc, const c
         const long long n = (long long)len * hd * es / 16;
         for (long long e = threadIdx.x; e < n; e += 256) d[e] = s[e];
         if (l == 0 && kvh == 0 && threadIdx.x == 0) lens_dst[rc.dst[i]] = len;
+    } else if (blockIdx.z == 2) {  // token history, once per pair
+        if (l == 0 && kvh == 0)
+            for (int e = threadIdx.x; e < len; e += 256)
+                hdst[(long long)rc.dst[i] * Sdst + e] = hsrc[(long long)rc.src[i] * Ssrc + e];
     } else {
         const int per_row = (len * es + 15) / 16;
         const long long n = (long long)per_row * hd;
@@ -542,11 +604,12 @@ __global__ __launch_bounds__(256) void kv_copy_rows_kernel(KvRowCopy rc, const c
 
 hipError_t launch_kv_copy_rows(const KvRowCopy& rc, const void* ksrc, const void* vsrc, void* kdst,
                                void* vdst, int L, int nkv, int hd, int es, int Bsrc, int Ssrc, int Bdst,
-                               int Sdst, int32_t* lens_dst, hipStream_t st) {
-    if (rc.n < 1 || rc.n > KvRowCopy::MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kv_copy_rows_kernel, dim3(rc.n, L * nkv, 2), dim3(256), 0, st, rc,
+                               int Sdst, int32_t* lens_dst, const int32_t* hsrc, int32_t* hdst,
+                               hipStream_t st) {
+    if (rc.n < 1 || rc.n > KvRowCopy::MAX || (!hsrc) != (!hdst)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kv_copy_rows_kernel, dim3(rc.n, L * nkv, hsrc ? 3 : 2), dim3(256), 0, st, rc,
                        (const char*)ksrc, (const char*)vsrc, (char*)kdst, (char*)vdst, nkv, hd, es,
-                       Bsrc, Ssrc, Bdst, Sdst, lens_dst);
+                       Bsrc, Ssrc, Bdst, Sdst, lens_dst, hsrc, hdst);
     return hipGetLastError();
 }
 

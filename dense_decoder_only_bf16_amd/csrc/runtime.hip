@@ -95,6 +95,17 @@ struct nc_model {
     float* rope_cos = nullptr;
     float* rope_sin = nullptr;
     std::vector<int> windows;  // per-layer sliding window, -1: the whole causal context
+    struct Extras {            // the later version's blocks (nc_model_set_extras)
+        bool on = false;
+        std::vector<float> lam, mu;  // residual scaling per layer
+        void* smear_gate = nullptr;
+        int smear_ch = 0;
+        float smear_lambda = 0.f;
+        int backout_layer = -1;
+        float backout_lambda = 0.f;
+        std::vector<void*> ve, ve_gate;  // per layer (null: none)
+        int ve_ch = 0;
+    } ex;
     int live_kv = 0;
 };
 
@@ -105,6 +116,7 @@ struct nc_kv {
     void* vcache = nullptr;  // [L][B][nkv][hd][S]
     int32_t* lens_dev = nullptr;
     std::vector<int32_t> lens_host;
+    int32_t* hist = nullptr;  // [B][S] tokens by position (only with smear)
     // workspace, sized for `cap_m` token rows
     long long cap_m = 0;
     int ss_parts_max = 0;
@@ -120,6 +132,8 @@ struct nc_kv {
     void* u_lo = nullptr;     // products): x - bf16(x) after attention, u - bf16(u)
     float* apart = nullptr;   // decode attention partials
     float* dpart = nullptr;   // decode projections with more than 32 rows: split-K partials
+    float* x0 = nullptr;      // later-version blocks: stream before layer 0's scaling [M][d]
+    float* xb = nullptr;      // and the backout source [M][d]
     long long dpart_elems = 0;
     long long apart_elems = 0;
     int apart_slots = 0;      // partial slots per (row, K/V head) unit, the most any layer needs
@@ -148,12 +162,12 @@ void drop_graphs(nc_kv* kv) {
 void ws_free(nc_kv* kv) {
     drop_graphs(kv);  // captured graphs point into the workspace
     void* ptrs[] = {kv->x, kv->act, kv->ss_a, kv->ss_b, kv->qkv, kv->q, kv->y, kv->u, kv->apart,
-                    kv->act_lo, kv->u_lo, kv->dpart};
+                    kv->act_lo, kv->u_lo, kv->dpart, kv->x0, kv->xb};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     kv->x = nullptr; kv->act = nullptr; kv->ss_a = nullptr; kv->ss_b = nullptr; kv->qkv = nullptr;
     kv->q = nullptr; kv->y = nullptr; kv->u = nullptr; kv->apart = nullptr;
-    kv->act_lo = nullptr; kv->u_lo = nullptr; kv->dpart = nullptr;
+    kv->act_lo = nullptr; kv->u_lo = nullptr; kv->dpart = nullptr; kv->x0 = nullptr; kv->xb = nullptr;
     kv->dpart_elems = 0;
     kv->cap_m = 0;
     kv->apart_elems = 0;
@@ -186,6 +200,8 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
         WS_ALLOC(kv->act_lo, Mr * d * es);
         WS_ALLOC(kv->u_lo, Mr * c.d_ff * es);
     }
+    if (kv->m->ex.on) WS_ALLOC(kv->x0, M * d * 4);
+    if (kv->m->ex.on && kv->m->ex.backout_layer >= 0) WS_ALLOC(kv->xb, M * d * 4);
     {
         const int units = kv->B * c.n_kv_head;  // (row, K/V head) pairs of decode attention
         int slots = 0;
@@ -323,6 +339,52 @@ hipError_t prefill_gemm(nc_model* m, Epi epi, const GemmArgs& g, hipStream_t st)
                  [&] { return launch_gemm(m->dt, epi, g, st); });
 }
 
+// Embedding of M = B T token rows (positions lens[b] + t), with the later-version blocks'
+// smear, x0 and layer-0 scaling when they are on.
+EmbedArgs embed_args(nc_model* m, nc_kv* kv, const int32_t* tokens, int M, int T, bool blocked) {
+    const nc_config& c = m->cfg;
+    const nc_model::Extras& ex = m->ex;
+    EmbedArgs e{};
+    e.tok = tokens; e.M = M; e.T = T; e.wte = m->wte; e.vocab = c.vocab; e.d = c.d_model;
+    e.eps = c.norm_eps; e.scale0 = 1.f;
+    e.x = kv->x; e.act = kv->act; e.ss = kv->ss_a; e.blocked = blocked;
+    e.lens = kv->lens_dev; e.hist = kv->hist; e.S = kv->S;
+    if (ex.on) {
+        e.scale0 = ex.lam[0] + ex.mu[0];
+        e.x0 = kv->x0;
+        if (ex.backout_layer == 0) e.xb = kv->xb;
+        e.smear_gate = ex.smear_gate; e.smear_ch = ex.smear_ch; e.smear_lambda = ex.smear_lambda;
+    }
+    return e;
+}
+
+// RESID extras of layer l's MLP residual (PROJ): the next layer's scaling, the backout
+// source when the next layer is the backout layer, the backout itself after the last.
+ResidExtra proj_resid_extra(const nc_model* m, const nc_kv* kv, int l) {
+    const nc_model::Extras& ex = m->ex;
+    ResidExtra r{};
+    r.ra = 1.f;
+    if (!ex.on) return r;
+    r.x0 = kv->x0;
+    if (l + 1 < m->cfg.n_layer) {
+        r.ra = ex.lam[l + 1];
+        r.rb = ex.mu[l + 1];
+        if (l + 1 == ex.backout_layer) r.xb_out = kv->xb;
+    } else if (ex.backout_layer >= 0) {
+        r.xb = kv->xb;
+        r.rc = -ex.backout_lambda;
+    }
+    return r;
+}
+
+ValueEmbed value_embed(const nc_model* m, const nc_kv* kv, int l, const int32_t* tokens) {
+    ValueEmbed v{};
+    if (!m->ex.on || !m->ex.ve[l]) return v;
+    v.ve = m->ex.ve[l]; v.ve_gate = m->ex.ve_gate[l]; v.ve_ch = m->ex.ve_ch; v.vocab = m->cfg.vocab;
+    v.tok = tokens; v.xin = kv->x; v.xin_stride = m->cfg.d_model;
+    return v;
+}
+
 // Enqueue one decode step (everything after the host-side checks) on `st`.
 nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* logits, hipStream_t st) {
     const nc_config& c = m->cfg;
@@ -334,7 +396,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
     const int ss = (int)kv->cap_m;
     nc_status s;
 
-    LAUNCH(launch_embed(m->dt, tokens, B, m->wte, V, d, c.norm_eps, kv->x, kv->act, kv->ss_a, true, st));
+    LAUNCH(launch_embed(m->dt, embed_args(m, kv, tokens, B, 1, true), st));
     int ss_a_parts = 1;
     for (int l = 0; l < c.n_layer; ++l) {
         const nc_model::Layer& L = m->layers[l];
@@ -353,6 +415,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = kv->apart;
         at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.nkv = nkv; at.max_slots = kv->apart_slots;
         at.window = m->windows[l];
+        at.vemb = value_embed(m, kv, l, tokens);
         at.iters = attn_decode_iters(B * nkv, attn_decode_span(kv->S, at.window));
         {   // bytes: the K/V read for every row (its visible positions, the new one
             // included) of each K/V head, q/k/v in fp32, y out; flops 4 hd per
@@ -380,6 +443,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         DecGemmArgs pj = a;
         pj.A = kv->u; pj.A_lo = kv->u_lo; pj.W = L.wproj; pj.N = d; pj.K = F;
         pj.out_f32 = kv->x; pj.out_t = kv->act; pj.ldo = d; pj.ss_out = kv->ss_a;
+        pj.rx = proj_resid_extra(m, kv, l);
         if (l == c.n_layer - 1) pj.out_lo = kv->act_lo;  // the LM head's operand is compensated
         if ((s = decode_gemm(kv, EPI_RESID, pj, st)) != NC_OK) return s;
         ss_a_parts = parts_d;
@@ -503,9 +567,37 @@ nc_status nc_model_create(const nc_config* cfg, const void* const* weights, nc_m
     }
 }
 
+namespace {
+void extras_free(nc_model::Extras& ex) {
+    if (ex.smear_gate) (void)hipFree(ex.smear_gate);
+    for (void* p : ex.ve)
+        if (p) (void)hipFree(p);
+    for (void* p : ex.ve_gate)
+        if (p) (void)hipFree(p);
+    ex = nc_model::Extras{};
+}
+
+bool is_device_ptr(const void* p) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+}
+
+// Library-owned copy of `bytes` of device memory.
+hipError_t dev_copy(const void* src, size_t bytes, void** dst) {
+    hipError_t e = hipMalloc(dst, bytes);
+    if (e == hipSuccess) e = hipMemcpy(*dst, src, bytes, hipMemcpyDeviceToDevice);
+    return e;
+}
+}  // namespace
+
 void nc_model_free(nc_model* m) {
     if (!m) return;
     (void)hipDeviceSynchronize();
+    extras_free(m->ex);
     if (m->arena) (void)hipFree(m->arena);
     if (m->rope_cos) (void)hipFree(m->rope_cos);
     if (m->rope_sin) (void)hipFree(m->rope_sin);
@@ -521,6 +613,73 @@ nc_status nc_model_set_windows(nc_model* m, const int32_t* windows) {
         m->windows = std::move(w);
         return NC_OK;
     } catch (const std::bad_alloc&) {
+        return fail(NC_ERR_OOM, "host allocation failed");
+    }
+}
+
+nc_status nc_model_set_extras(nc_model* m, const nc_extras* x) {
+    try {
+        if (!m) return fail(NC_ERR_INVALID_ARG, "model is NULL");
+        if (m->live_kv != 0) return fail(NC_ERR_STATE, "extras can only change while the model has no kv object");
+        const nc_config& c = m->cfg;
+        const int L = c.n_layer, lim = std::min(64, c.d_model);
+        if (x) {
+            if (x->smear_gate_dev && (x->smear_channels < 1 || x->smear_channels > lim))
+                return fail(NC_ERR_INVALID_ARG, "smear_channels must be in [1, min(64, d_model)]");
+            if (x->backout_layer < -1 || x->backout_layer >= L) return fail(NC_ERR_INVALID_ARG, "backout_layer out of range");
+            if (x->smear_gate_dev && !is_device_ptr(x->smear_gate_dev))
+                return fail(NC_ERR_INVALID_ARG, "smear_gate_dev is not device memory");
+            if (x->ve_dev) {
+                if (!x->ve_gate_dev) return fail(NC_ERR_INVALID_ARG, "ve_gate_dev is NULL");
+                bool any = false;
+                for (int l = 0; l < L; ++l) {
+                    if (!x->ve_dev[l]) continue;
+                    any = true;
+                    if (!is_device_ptr(x->ve_dev[l]) || !x->ve_gate_dev[l] || !is_device_ptr(x->ve_gate_dev[l]))
+                        return fail(NC_ERR_INVALID_ARG, "value embedding of layer " + std::to_string(l) +
+                                                            ": table or gate is not device memory");
+                }
+                if (any && (x->ve_channels < 1 || x->ve_channels > lim))
+                    return fail(NC_ERR_INVALID_ARG, "ve_channels must be in [1, min(64, d_model)]");
+            }
+        }
+        (void)hipDeviceSynchronize();
+        extras_free(m->ex);
+        if (!x) return NC_OK;
+        nc_model::Extras& ex = m->ex;
+        ex.on = true;
+        ex.lam.assign(L, 1.f);
+        ex.mu.assign(L, 0.f);
+        if (x->resid_lambda_host) ex.lam.assign(x->resid_lambda_host, x->resid_lambda_host + L);
+        if (x->x0_lambda_host) ex.mu.assign(x->x0_lambda_host, x->x0_lambda_host + L);
+        ex.backout_layer = x->backout_layer;
+        ex.backout_lambda = x->backout_lambda;
+        ex.ve.assign(L, nullptr);
+        ex.ve_gate.assign(L, nullptr);
+        hipError_t e = hipSuccess;
+        if (x->smear_gate_dev) {
+            ex.smear_ch = x->smear_channels;
+            ex.smear_lambda = x->smear_lambda;
+            e = dev_copy(x->smear_gate_dev, (size_t)ex.smear_ch * m->esz, &ex.smear_gate);
+        }
+        if (x->ve_dev) {
+            ex.ve_ch = x->ve_channels;
+            const size_t tb = (size_t)c.vocab * c.n_kv_head * c.head_dim * m->esz;
+            const size_t gb = (size_t)c.n_kv_head * ex.ve_ch * m->esz;
+            for (int l = 0; l < L && e == hipSuccess; ++l) {
+                if (!x->ve_dev[l]) continue;
+                e = dev_copy(x->ve_dev[l], tb, &ex.ve[l]);
+                if (e == hipSuccess) e = dev_copy(x->ve_gate_dev[l], gb, &ex.ve_gate[l]);
+            }
+        }
+        if (e != hipSuccess) {
+            extras_free(m->ex);
+            return fail(e == hipErrorOutOfMemory ? NC_ERR_OOM : NC_ERR_DEVICE,
+                        std::string("extras copy: ") + hipGetErrorString(e));
+        }
+        return NC_OK;
+    } catch (const std::bad_alloc&) {
+        extras_free(m->ex);
         return fail(NC_ERR_OOM, "host allocation failed");
     }
 }
@@ -549,11 +708,16 @@ nc_status nc_kv_create(nc_model* m, int32_t batch, int32_t max_seq, nc_kv** out)
         if (e == hipSuccess) e = hipMemset(kv->kcache, 0, bytes);
         if (e == hipSuccess) e = hipMemset(kv->vcache, 0, bytes);
         if (e == hipSuccess) e = hipMemset(kv->lens_dev, 0, batch * sizeof(int32_t));
+        if (e == hipSuccess && m->ex.smear_gate) {
+            e = hipMalloc((void**)&kv->hist, (size_t)batch * kv->S * sizeof(int32_t));
+            if (e == hipSuccess) e = hipMemset(kv->hist, 0, (size_t)batch * kv->S * sizeof(int32_t));
+        }
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) {
             if (kv->kcache) (void)hipFree(kv->kcache);
             if (kv->vcache) (void)hipFree(kv->vcache);
             if (kv->lens_dev) (void)hipFree(kv->lens_dev);
+            if (kv->hist) (void)hipFree(kv->hist);
             delete kv;
             return fail(e == hipErrorOutOfMemory ? NC_ERR_OOM : NC_ERR_DEVICE,
                         std::string("kv allocation: ") + hipGetErrorString(e));
@@ -576,6 +740,7 @@ void nc_kv_free(nc_kv* kv) {
     if (kv->kcache) (void)hipFree(kv->kcache);
     if (kv->vcache) (void)hipFree(kv->vcache);
     if (kv->lens_dev) (void)hipFree(kv->lens_dev);
+    if (kv->hist) (void)hipFree(kv->hist);
     kv->m->live_kv--;
     delete kv;
 }
@@ -658,7 +823,7 @@ nc_status nc_kv_copy_rows(nc_kv* dst, const int32_t* dst_rows, nc_kv* src, const
             }
             LAUNCH(launch_kv_copy_rows(rc, src->kcache, src->vcache, dst->kcache, dst->vcache, c.n_layer,
                                        c.n_kv_head, c.head_dim, (int)dst->m->esz, src->B, src->S, dst->B,
-                                       dst->S, dst->lens_dev, st));
+                                       dst->S, dst->lens_dev, src->hist, dst->hist, st));
         }
         for (int i = 0; i < n; ++i) dst->lens_host[dst_rows[i]] = src->lens_host[src_rows[i]];
         return NC_OK;
@@ -698,7 +863,7 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
         const size_t per_layer = (size_t)B * nkv * kv->S * hd * m->esz;
         const int Mi = (int)M;
 
-        LAUNCH(launch_embed(m->dt, tokens, Mi, m->wte, V, d, c.norm_eps, kv->x, kv->act, kv->ss_a, false, st));
+        LAUNCH(launch_embed(m->dt, embed_args(m, kv, tokens, Mi, T, false), st));
         int ss_a_parts = 1;
         for (int l = 0; l < c.n_layer; ++l) {
             const nc_model::Layer& L = m->layers[l];
@@ -714,6 +879,7 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             qa.lens = kv->lens_dev; qa.rope_cos = m->rope_cos; qa.rope_sin = m->rope_sin;
             qa.q = kv->q; qa.kc = (char*)kv->kcache + l * per_layer; qa.vtc = (char*)kv->vcache + l * per_layer;
             qa.S = kv->S; qa.eps = c.norm_eps;
+            qa.vemb = value_embed(m, kv, l, tokens);
             LAUNCH(launch_qkv_post(m->dt, qa, st));
             {   // causal attention flops: 4 hd per visible (query, key) pair and head; bytes:
                 // q in, y out, and every key/value a query of the row sees, read once
@@ -746,8 +912,10 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             g.out_f32 = kv->x; g.out_t = kv->act; g.ldo = d; g.ss_out = kv->ss_a; g.ss_stride = (int)kv->cap_m;
             g.A_lo = kv->u_lo;
             g.out_lo = (l == c.n_layer - 1) ? kv->act_lo : nullptr;  // LM head operand, compensated
+            g.rx = proj_resid_extra(m, kv, l);
             LAUNCH(prefill_gemm(m, EPI_RESID, g, st));
             g.A_lo = nullptr;
+            g.rx = ResidExtra{};
             ss_a_parts = parts_d;
         }
         if (logits) {

@@ -131,6 +131,29 @@ def canonical_list(weights):
     return out
 
 
+def make_extras(s: Shape, seed=5, ve_layers=None, smear_ch=24, ve_ch=32, ve_std=0.5):
+    """Seeded parameters of the later version's blocks (value embeddings, residual lambdas,
+    smear, backout) in the dict form both sides take: per-layer lambdas as float32 values,
+    tables and gates as float32 arrays holding exact values of the storage dtype.  Value
+    embeddings sit on the odd layers unless ve_layers says otherwise; backout takes the
+    middle layer."""
+    rng = np.random.default_rng(seed)
+    L, kvd = s.n_layer, s.n_kv_head * s.head_dim
+    rnd = (lambda a: round_bf16(a)) if s.dtype == "bf16" else (lambda a: a)
+    ve_layers = list(range(1, L, 2)) if ve_layers is None else list(ve_layers)
+    f32 = lambda a: np.asarray(a, dtype=np.float32)  # noqa: E731
+    ex = {"resid_lambda": [float(v) for v in f32(rng.uniform(0.8, 1.2, L))],
+          "x0_lambda": [float(v) for v in f32(rng.uniform(0.0, 0.3, L))],
+          "smear_gate": rnd(f32(rng.standard_normal(smear_ch) * 0.3)),
+          "smear_lambda": float(np.float32(0.5)),
+          "backout_layer": L // 2, "backout_lambda": float(np.float32(0.3)),
+          "ve": {}, "ve_gate": {}}
+    for l in ve_layers:
+        ex["ve"][l] = rnd(f32(rng.standard_normal((s.vocab, kvd)) * ve_std))
+        ex["ve_gate"][l] = rnd(f32(rng.standard_normal((s.n_kv_head, ve_ch)) * 0.3))
+    return ex
+
+
 def make_tokens(vocab, batch, length, seed=1):
     """Uniform random token ids in [0, vocab), int32 [batch, length]."""
     return np.random.default_rng(seed).integers(0, vocab, (batch, length)).astype(np.int32)

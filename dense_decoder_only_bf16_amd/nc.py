@@ -36,7 +36,8 @@ NC_KC_PREFILL_GEMM = 2
 NC_KC_PREFILL_ATTN = 3
 NC_KC_DECODE_ATTN = 4
 
-EXPORTED = ("nc_model_create", "nc_model_free", "nc_model_set_windows", "nc_kv_create", "nc_kv_free", "nc_kv_set_lens",
+EXPORTED = ("nc_model_create", "nc_model_free", "nc_model_set_windows", "nc_model_set_extras",
+            "nc_kv_create", "nc_kv_free", "nc_kv_set_lens",
             "nc_kv_get_lens", "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step", "nc_argmax",
             "nc_sample", "nc_timing_enable", "nc_timing_read", "nc_last_error", "nc_abi_version")
 
@@ -54,6 +55,16 @@ class nc_config(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32),
                 ("rope_base", ctypes.c_float), ("softcap", ctypes.c_float),
                 ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class nc_extras(ctypes.Structure):
+    _fields_ = [("resid_lambda_host", ctypes.POINTER(ctypes.c_float)),
+                ("x0_lambda_host", ctypes.POINTER(ctypes.c_float)),
+                ("smear_gate_dev", ctypes.c_void_p), ("smear_channels", ctypes.c_int32),
+                ("smear_lambda", ctypes.c_float), ("backout_layer", ctypes.c_int32),
+                ("backout_lambda", ctypes.c_float),
+                ("ve_dev", ctypes.POINTER(ctypes.c_void_p)),
+                ("ve_gate_dev", ctypes.POINTER(ctypes.c_void_p)), ("ve_channels", ctypes.c_int32)]
 
 
 class nc_timing(ctypes.Structure):
@@ -77,6 +88,7 @@ def lib():
         L.nc_model_free.argtypes = [vp]
         L.nc_model_free.restype = None
         L.nc_model_set_windows.argtypes = [vp, ctypes.POINTER(i32)]
+        L.nc_model_set_extras.argtypes = [vp, ctypes.POINTER(nc_extras)]
         L.nc_kv_create.argtypes = [vp, i32, i32, ctypes.POINTER(vp)]
         L.nc_kv_free.argtypes = [vp]
         L.nc_kv_free.restype = None
@@ -94,7 +106,7 @@ def lib():
         L.nc_last_error.restype = ctypes.c_char_p
         L.nc_abi_version.argtypes = []
         L.nc_abi_version.restype = i32
-        for name in ("nc_model_create", "nc_model_set_windows", "nc_kv_create", "nc_kv_set_lens", "nc_kv_get_lens",
+        for name in ("nc_model_create", "nc_model_set_windows", "nc_model_set_extras", "nc_kv_create", "nc_kv_set_lens", "nc_kv_get_lens",
                      "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step", "nc_argmax",
                      "nc_sample", "nc_timing_enable", "nc_timing_read"):
             getattr(L, name).restype = st
@@ -157,6 +169,53 @@ def nc_model_free(m):
 def nc_model_set_windows(m, windows):
     a = np.ascontiguousarray(windows, dtype=np.int32)
     _check(lib().nc_model_set_windows(m, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+
+
+def nc_model_set_extras(m, extras, n_layer, dtype, device="cuda"):
+    """extras: None (blocks off) or a dict with any of "resid_lambda", "x0_lambda" (n_layer
+    floats), "smear_gate" ([Cs] array) with "smear_lambda", "backout_layer" with
+    "backout_lambda", "ve" / "ve_gate" (dicts layer -> [V, n_kv*hd] / [n_kv, Cv] arrays).
+    Arrays are uploaded in the model dtype for the call (the library copies them)."""
+    if extras is None:
+        _check(lib().nc_model_set_extras(m, None))
+        return
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    keep = []
+
+    def dev(a):
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device=device).to(tdt)
+        keep.append(t)
+        return t.data_ptr()
+
+    def host(vals):
+        a = (ctypes.c_float * n_layer)(*[float(v) for v in vals])
+        keep.append(a)
+        return ctypes.cast(a, ctypes.POINTER(ctypes.c_float))
+
+    ex = nc_extras()
+    if "resid_lambda" in extras:
+        ex.resid_lambda_host = host(extras["resid_lambda"])
+    if "x0_lambda" in extras:
+        ex.x0_lambda_host = host(extras["x0_lambda"])
+    if extras.get("smear_gate") is not None:
+        g = np.asarray(extras["smear_gate"])
+        ex.smear_gate_dev = dev(g)
+        ex.smear_channels = g.shape[0]
+        ex.smear_lambda = float(extras.get("smear_lambda", 0.0))
+    ex.backout_layer = int(extras.get("backout_layer", -1))
+    ex.backout_lambda = float(extras.get("backout_lambda", 0.0))
+    ve = extras.get("ve") or {}
+    if ve:
+        tabs = (ctypes.c_void_p * n_layer)(*[dev(ve[l]) if l in ve else None for l in range(n_layer)])
+        gates = (ctypes.c_void_p * n_layer)(*[dev(extras["ve_gate"][l]) if l in ve else None
+                                              for l in range(n_layer)])
+        keep += [tabs, gates]
+        ex.ve_dev = ctypes.cast(tabs, ctypes.POINTER(ctypes.c_void_p))
+        ex.ve_gate_dev = ctypes.cast(gates, ctypes.POINTER(ctypes.c_void_p))
+        ex.ve_channels = np.asarray(extras["ve_gate"][next(iter(ve))]).shape[1]
+    _check(lib().nc_model_set_extras(m, ctypes.byref(ex)))
+    del keep
 
 
 def layer_windows(pattern, n_layer, short_window):
@@ -242,7 +301,7 @@ def upload_weights(weights_list, dtype, device="cuda"):
 class Model:
     """Owning wrapper: model handle + its KV caches."""
 
-    def __init__(self, shape, weights_list, max_seq=None, device="cuda", windows=None):
+    def __init__(self, shape, weights_list, max_seq=None, device="cuda", windows=None, extras=None):
         self.shape = shape
         self.cfg = make_config(shape, max_seq)
         dev = upload_weights(weights_list, shape.dtype, device)
@@ -250,6 +309,8 @@ class Model:
         del dev
         if windows is not None:
             nc_model_set_windows(self.handle, windows)
+        if extras is not None:
+            nc_model_set_extras(self.handle, extras, shape.n_layer, shape.dtype, device)
 
     def new_kv(self, batch, max_seq):
         return KV(self, batch, max_seq)

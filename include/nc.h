@@ -106,6 +106,36 @@ void nc_model_free(nc_model* m); /* NULL is a no-op; all kv objects must be free
  * model has no nc_kv object (NC_ERR_STATE otherwise); copies the values. */
 nc_status nc_model_set_windows(nc_model* m, const int32_t* windows_host);
 
+/* The later version's learned blocks (apidog.com/th guide, part 1: value embeddings on some
+ * layers with an input-dependent gate, per-layer residual scaling against x0, smear and
+ * backout; the pages give their update rules only, so these are the readings):
+ *   e_t    = norm(wte[token_t]);  smear: x_t = e_t + smear_lambda sigmoid(e_t[:Cs] . g) e_{t-1}
+ *            (e_{t-1} the row's previous token's; none at position 0); x0 = x;
+ *   layer l starts with x <- resid_lambda[l] x + x0_lambda[l] x0;
+ *   layers with a value embedding: value head j gains
+ *            3 sigmoid(h[:Cv] . ve_gate[l][j]) ve[l][token][j hd .. (j+1) hd), h = norm(x)
+ *            the attention input;
+ *   backout: xb = x at the start of layer backout_layer; after the last layer
+ *            x <- x - backout_lambda xb, before the final norm.
+ * Tables are device memory of cfg.dtype, copied by the library; scalars are host values.
+ * ex == NULL switches every block off (the default).  Allowed only while the model has no
+ * nc_kv object (NC_ERR_STATE); NC_ERR_INVALID_ARG for channels outside [1, min(64, d_model)],
+ * a backout layer outside [-1, n_layer) or tables that are not device memory. */
+typedef struct nc_extras {
+    const float* resid_lambda_host;   /* n_layer values, or NULL: all 1 */
+    const float* x0_lambda_host;      /* n_layer values, or NULL: all 0 */
+    const void* smear_gate_dev;       /* [smear_channels], or NULL: no smear */
+    int32_t smear_channels;
+    float smear_lambda;
+    int32_t backout_layer;            /* -1: no backout */
+    float backout_lambda;
+    const void* const* ve_dev;        /* n_layer pointers (NULL entries: no value embedding in
+                                         that layer) to [vocab][n_kv_head * head_dim], or NULL */
+    const void* const* ve_gate_dev;   /* n_layer pointers to [n_kv_head][ve_channels] */
+    int32_t ve_channels;
+} nc_extras;
+nc_status nc_model_set_extras(nc_model* m, const nc_extras* ex);
+
 /* KV cache for `batch` rows of up to `max_seq` positions (max_seq <= cfg.max_seq, and at
  * most 32768: NC_ERR_UNSUPPORTED otherwise).
  * Layout (library-private): K [L][batch][n_kv_head][max_seq][hd], V transposed

@@ -12,8 +12,8 @@ def torch_mod():
     return torch
 
 
-def gpu_model(shape, weights, max_seq=None, windows=None):
-    return nc.Model(shape, canonical_list(weights), max_seq=max_seq, windows=windows)
+def gpu_model(shape, weights, max_seq=None, windows=None, extras=None):
+    return nc.Model(shape, canonical_list(weights), max_seq=max_seq, windows=windows, extras=extras)
 
 
 def prefill(model, tokens, max_seq, logits=True):

@@ -114,6 +114,7 @@ def test_null_handles_are_rejected(L):
     assert L.nc_model_set_windows(None, None) == nc.NC_ERR_INVALID_ARG
     assert L.nc_kv_copy_rows(None, None, None, None, 0, None) == nc.NC_ERR_INVALID_ARG
     assert L.nc_sample(None, 1, 1, 1.0, 0, None, None, None) == nc.NC_ERR_INVALID_ARG
+    assert L.nc_model_set_extras(None, None) == nc.NC_ERR_INVALID_ARG
     L.nc_model_free(None)
     L.nc_kv_free(None)
 
@@ -136,3 +137,9 @@ def test_layer_windows_helper():
         nc.layer_windows("SQ", 2, 8)
     with pytest.raises(ValueError):
         nc.layer_windows("", 2, 8)
+
+
+def test_extras_struct_layout():
+    assert ctypes.sizeof(nc.nc_extras) == 64
+    assert nc.nc_extras.smear_gate_dev.offset == 16 and nc.nc_extras.ve_dev.offset == 40
+    assert nc.nc_extras.ve_channels.offset == 56

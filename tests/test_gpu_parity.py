@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from dense_decoder_only_bf16_amd import nc
-from dense_decoder_only_bf16_amd.inputs import (TINY, Shape, make_tokens, make_weights,
+from dense_decoder_only_bf16_amd.inputs import (TINY, Shape, make_extras, make_tokens, make_weights,
                                                 make_lens)
 from oracle import OracleModel
 
@@ -688,3 +688,100 @@ def test_sampling_frequencies_on_a_grid():
     counts = np.bincount(got, minlength=V)
     assert np.all(np.abs(counts - N * probs) <= 2.0)
     assert set(np.nonzero(counts)[0]) <= set(keep)
+
+
+# ---------------------------------------------------------------- later-version blocks -
+EXTRAS_TINY = replace(TINY, name="tiny-extras", n_layer=3, d_model=256, n_head=4, n_kv_head=2,
+                      max_seq=96)
+
+
+def test_fp32_extras_prefill_decode_append_copy():
+    """Value embeddings (layers 0 and 2), residual lambdas, smear and backout in fp32: a
+    prefill, decode steps (smear reading the cached previous token), a truncated row, an
+    appended chunk and a copied row, all against the oracle at the fp32 bar."""
+    torch = torch_mod()
+    shape = EXTRAS_TINY
+    w = make_weights(shape, seed=100)
+    ex = make_extras(shape, seed=101, ve_layers=(0, 2), smear_ch=24, ve_ch=40)
+    orc = OracleModel(shape, w, extras=ex)
+    gm = gpu_model(shape, w, extras=ex)
+    B, T = 2, 60
+    toks = make_tokens(shape.vocab, B, 80, seed=102)
+    want, _ = orc.prefill(toks)
+    kv, got = prefill(gm, toks[:, :T], shape.max_seq)
+    err, _ = report("tiny extras prefill", got, want[:, :T])
+    assert err <= F32_TOL
+    got = np.stack([decode(gm, kv, toks[:, T + s]) for s in range(4)], axis=1)
+    err, _ = report("tiny extras decode", got, want[:, T:T + 4])
+    assert err <= F32_TOL
+    kv.set_lens([30, 64])
+    out = torch.empty((B, 5, shape.vocab), device="cuda", dtype=torch.float32)
+    kv.prefill(torch.from_numpy(np.ascontiguousarray(toks[:, 70:75])).cuda(), out)
+    got = out.cpu().numpy()
+    for b, n in enumerate((30, 64)):
+        seq = np.concatenate([toks[b, :n], toks[b, 70:75]])[None]
+        ref, _ = orc.prefill(seq, logits_at=np.arange(n, n + 5))
+        err, _ = report(f"tiny extras append row {b} at {n}", got[b], ref[0])
+        assert err <= F32_TOL
+    other = gm.new_kv(3, shape.max_seq)
+    other.copy_rows_from(kv, [1], [2])
+    got = decode(gm, other, np.array([0, 0, toks[1, 75]], dtype=np.int32))[2]
+    seq = np.concatenate([toks[1, :64], toks[1, 70:76]])[None]
+    ref, _ = orc.prefill(seq, logits_at=[69])
+    err = float(np.max(np.abs(got - ref[0, 0])))
+    print(f"[tiny extras copied row] max_abs={err:.3e}", flush=True)
+    assert err <= F32_TOL
+    other.close()
+    kv.close()
+    gm.close()
+
+
+@pytest.mark.parametrize("B", [3, 40])
+def test_bf16_extras_prefill_and_decode(B):
+    """The blocks on a bf16 model (4 layers, value embeddings on the odd ones): ragged
+    prefill, then decode of B rows at mixed lengths (B = 40: the split-K decode path, whose
+    reduce kernel runs the residual epilogue)."""
+    shape = replace(SMALL_BF16, name="small-extras", n_layer=4, n_kv_head=2, max_seq=400)
+    w = make_weights(shape, seed=103)
+    ex = make_extras(shape, seed=104)
+    orc = OracleModel(shape, w, extras=ex)
+    gm = gpu_model(shape, w, extras=ex)
+    T = 300
+    toks = make_tokens(shape.vocab, B, T + 2, seed=105 + B)
+    kv, got = prefill(gm, toks[:, :T], shape.max_seq)
+    want, _ = orc.prefill(toks[:2, :T])
+    err, agr = report(f"small extras prefill B={B}", got[:2], want)
+    assert err <= BF16_TOL and agr >= AGREE
+    lens = make_lens(B, 1, T, seed=106 + B)
+    kv.set_lens(lens)
+    got = np.stack([decode(gm, kv, toks[:, T + s]) for s in range(2)], axis=1)
+    want = np.empty_like(got, dtype=np.float64)
+    for b in range(B):
+        seq = np.concatenate([toks[b, :lens[b]], toks[b, T:T + 2]])[None]
+        want[b] = orc.prefill(seq, logits_at=np.arange(lens[b], lens[b] + 2))[0][0]
+    err, agr = report(f"small extras decode B={B}", got, want)
+    assert err <= BF16_TOL
+    assert_flips_are_near_ties(got, want, err)
+    kv.close()
+    gm.close()
+
+
+def test_extras_switch_off_and_errors(small):
+    """Setting the blocks requires no live cache; clearing them gives the plain model."""
+    w, orc, gm = small
+    kv = gm.new_kv(1, 8)
+    ex = make_extras(SMALL_BF16, seed=107)
+    with pytest.raises(nc.NcError) as e:
+        nc.nc_model_set_extras(gm.handle, ex, SMALL_BF16.n_layer, "bf16")
+    assert e.value.code == nc.NC_ERR_STATE
+    kv.close()
+    bad = dict(ex, backout_layer=SMALL_BF16.n_layer)
+    with pytest.raises(nc.NcError) as e:
+        nc.nc_model_set_extras(gm.handle, bad, SMALL_BF16.n_layer, "bf16")
+    assert e.value.code == nc.NC_ERR_INVALID_ARG
+    nc.nc_model_set_extras(gm.handle, ex, SMALL_BF16.n_layer, "bf16")
+    nc.nc_model_set_extras(gm.handle, None, SMALL_BF16.n_layer, "bf16")
+    toks = make_tokens(SMALL_BF16.vocab, 1, 20, seed=108)
+    _, got = prefill(gm, toks, 20)
+    want, _ = orc.prefill(toks)
+    assert np.max(np.abs(got - want)) <= BF16_TOL
