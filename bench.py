@@ -10,12 +10,13 @@ context lengths uniform in [256, 2048]; tiny) build a separate decode context ou
 timed steps.  Prints one JSON line.
 
 Workloads d20-gqa (5 K/V heads) and d20-sssl (an SSSL pattern of 512-key sliding
-windows) run the d20 step with the later version's attention options; d12-sample runs
+windows) run the d20 step with the later version's attention options, d20-blocks with its
+learned blocks (value embeddings, residual lambdas, smear, backout); d12-sample runs
 the d12 step with sampled decode picks (temperature 1, top-50; the uniforms are drawn
 before the timed region).
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload d12|d20|d26|d30|d20-gqa|d20-sssl|d12-sample|tiny]
+                    [--workload d12|d20|d26|d30|d20-gqa|d20-sssl|d20-blocks|d12-sample|tiny]
                     [--no-cpu]
 """
 
@@ -46,7 +47,7 @@ def parse():
     return p.parse_args()
 
 
-def cpu_baseline(shape, weights, wl, budget_s, windows=None):
+def cpu_baseline(shape, weights, wl, budget_s, windows=None, extras=None):
     """Time the fp64 oracle on the host on a bounded sample of the same workload.
 
     Sample: one row; prefill of min(T, 2048) tokens, then greedy decode steps until the
@@ -59,7 +60,7 @@ def cpu_baseline(shape, weights, wl, budget_s, windows=None):
     except Exception:  # noqa: BLE001
         threads = len(os.sched_getaffinity(0))
     from dense_decoder_only_bf16_amd.inputs import make_tokens
-    orc = OracleModel(shape, weights, windows=windows)
+    orc = OracleModel(shape, weights, windows=windows, extras=extras)
     t_pre = min(wl.prefill_len or wl.decode_context, 2048)  # decode-only: its context
     prompt = make_tokens(shape.vocab, 1, t_pre, seed=1)
     t0 = time.perf_counter()
@@ -186,8 +187,8 @@ def main():
     import torch
 
     from dense_decoder_only_bf16_amd import nc
-    from dense_decoder_only_bf16_amd.inputs import (WORKLOADS, canonical_list, make_lens,
-                                                    make_tokens, make_weights)
+    from dense_decoder_only_bf16_amd.inputs import (WORKLOADS, canonical_list, make_extras,
+                                                    make_lens, make_tokens, make_weights)
 
     wl = WORKLOADS[args.workload]
     shape = wl.shape
@@ -199,7 +200,9 @@ def main():
     weights = make_weights(shape, seed=0)
     windows = (nc.layer_windows(wl.window_pattern, shape.n_layer, wl.short_window)
                if wl.window_pattern else None)
-    model = nc.Model(shape, canonical_list(weights), max_seq=shape.max_seq, windows=windows)
+    extras = make_extras(shape, seed=wl.extras_seed) if wl.extras_seed >= 0 else None
+    model = nc.Model(shape, canonical_list(weights), max_seq=shape.max_seq, windows=windows,
+                     extras=extras)
     stream = torch.cuda.current_stream()
     V = shape.vocab
 
@@ -271,6 +274,9 @@ def main():
     kvh = f"{shape.n_kv_head} K/V head" + ("s" if shape.n_kv_head > 1 else "")
     win = (f", windows {wl.window_pattern} with {wl.short_window}-key short windows"
            if wl.window_pattern else "")
+    if extras is not None:
+        win += (f", value embeddings on layers {sorted(extras['ve'])}, residual lambdas, smear, "
+                f"backout at layer {extras['backout_layer']}")
     desc = (f"{args.workload} ({shape.n_layer} layers, d {shape.d_model}, {shape.n_head}x"
             f"{shape.head_dim} query heads, {kvh}, MLP {shape.d_ff}, vocab {V}, "
             f"{shape.dtype}{win}):")
@@ -303,7 +309,7 @@ def main():
     if not args.no_roofline:
         out["roofline"], out["kernels"] = roofline(nc, one_step, shape.dtype, args.workload)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(shape, weights, wl, args.cpu_seconds, windows)
+        out["cpu_baseline"] = cpu_baseline(shape, weights, wl, args.cpu_seconds, windows, extras)
     for kv in {id(k): k for k in (kv_p, kv_d) if k is not None}.values():
         kv.close()
     model.close()

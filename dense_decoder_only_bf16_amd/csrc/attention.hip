@@ -417,13 +417,11 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs 
                 }
             } else if (j == 17) {
                 float w1 = v1[t] * r, w2 = v2[t] * r;
-                if (a.vemb.ve) {  // the layer's value embedding (wave-uniform)
-                    const ValueEmbed& ve = a.vemb;
+                if (a.vemb) {  // the layer's value embedding (wave-uniform)
+                    const ValueEmbed& ve = *a.vemb;
                     const float g = value_embed_gate<T>((const T*)ve.ve_gate, kvh, ve.ve_ch,
                                                         ve.xin + (long long)b * ve.xin_stride, r, lane);
-                    int tk = ve.tok[b];
-                    tk = tk < 0 ? 0 : (tk >= ve.vocab ? ve.vocab - 1 : tk);
-                    const T* e = (const T*)ve.ve + ((long long)tk * a.nkv + kvh) * HD;
+                    const T* e = (const T*)ve.ve + ((long long)ve.tok[b] * a.nkv + kvh) * HD;
                     w1 += g * to_f32(e[i]);
                     w2 += g * to_f32(e[i + HALF]);
                 }

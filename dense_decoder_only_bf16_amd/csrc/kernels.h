@@ -63,6 +63,11 @@ __host__ __device__ inline float resid_value(const ResidExtra& e, long long o, f
     if (e.xb_out) e.xb_out[o] = x;
     return x;
 }
+// Decode kernels take these blocks by pointer (device memory, null: off): their argument
+// blocks stay small, which measurably shortens these few-microsecond kernels.
+__device__ inline float resid_value(const ResidExtra* e, long long o, float x_old, float c) {
+    return e ? resid_value(*e, o, x_old, c) : x_old + c;
+}
 
 struct GemmArgs {
     const void* A;  // [M][lda] dtype, K contiguous
@@ -96,19 +101,20 @@ hipError_t launch_gemm(DType dt, Epi epi, const GemmArgs& a, hipStream_t st);
 // ss_out[tile_n * ss_stride + m] (parts = ceil(N / tile_n)).
 // Decode activations (A, A_lo and the dtype outputs out_t, out_lo) are stored blocked with
 // rows rounded up to 32 (blocked_index); the fp32 outputs are row-major with stride ldo.
-struct DecGemmArgs {
+struct DecGemmArgs {  // pointers first, then 4-byte fields: no padding (120 bytes)
     const void* A;              // blocked [ceil(M/32)][K/16][32][16] dtype
     const void* W;              // blocked weight, Npad = N rounded up to 32 rows
-    int M, N, K;
-    float* out_f32; void* out_t; int ldo;
-    const float* ss_in; int ss_in_parts, ss_stride;
+    float* out_f32; void* out_t;
+    const float* ss_in;
     float* ss_out;
-    float eps, cap;
     int32_t* lens_inc;  // if set, workgroup 0 adds one to lens_inc[0..M) (end of a decode step)
     const void* A_lo;   // compensated operand, as in GemmArgs (bf16 only; null: plain A)
     void* out_lo;       // RELU2 / RESID low-part output, as in GemmArgs (null: not written)
     float* part;        // bf16 with M > 32: fp32 split-K partials, dec_gemm_part_elems(M, N, K)
-    ResidExtra rx;      // RESID: as in GemmArgs (x0, xb row-major with stride ldo)
+    const ResidExtra* rx;  // RESID: as in GemmArgs, in device memory (null: plain residual)
+    int M, N, K, ldo;
+    int ss_in_parts, ss_stride;
+    float eps, cap;
 };
 int dec_gemm_tile_n();
 // Elements of DecGemmArgs::part that a product of this shape needs (0: none).
@@ -130,6 +136,7 @@ struct EmbedArgs {
     const void* smear_gate; int smear_ch; float smear_lambda;  // null gate: no smear
     float* x0;                    // stream before the layer-0 scaling (null: not written)
     float* xb;                    // copy of x (backout source at layer 0; null: none)
+    int32_t* tok_out;             // the clamped token of each row (null: not written)
 };
 hipError_t launch_embed(DType dt, const EmbedArgs& a, hipStream_t st);
 
@@ -141,7 +148,8 @@ hipError_t launch_embed(DType dt, const EmbedArgs& a, hipStream_t st);
 // Value embedding of a layer (the later version's blocks; ve null: none): value head j of
 // row m gains 3 sigmoid(r_m xin[m][:ve_ch] . ve_gate[j]) ve[tok[m]][j hd .. (j + 1) hd),
 // r_m xin the row's attention input (xin fp32 with row stride xin_stride, ve_ch <= 64);
-// ve [vocab][nkv hd] and ve_gate [nkv][ve_ch] in the model dtype.
+// ve [vocab][nkv hd] and ve_gate [nkv][ve_ch] in the model dtype; tok[m] the row's token
+// (clamped into the vocabulary by the embedding kernel that writes it).
 struct ValueEmbed {
     const void* ve; const void* ve_gate; int ve_ch, vocab;
     const int32_t* tok; const float* xin; int xin_stride;
@@ -189,7 +197,7 @@ struct DecAttnArgs {
     int iters;            // 64-key blocks per wave: attn_decode_iters(B nkv, span)
     int max_slots;        // partial slots per unit, >= attn_decode_slots(B nkv, S, span)
     float scale_log2;     // set by the launcher
-    ValueEmbed vemb;      // tok[b], xin row b
+    const ValueEmbed* vemb;  // device memory (null: none); tok[b], xin row b
 };
 // Keys a query can see at most: min(S, window + 1), or S without a window.
 int attn_decode_span(int S, int window);

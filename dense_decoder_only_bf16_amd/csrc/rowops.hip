@@ -83,6 +83,7 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
         }
     }
     if (in_cache && lane == 0) a.hist[(long long)b * a.S + pos] = t;
+    if (a.tok_out && lane == 0) a.tok_out[row] = t;
     float s2 = 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -153,9 +154,7 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
         const int jj = j - a.H - a.nkv;
         const float g = value_embed_gate<T>((const T*)ve.ve_gate, jj, ve.ve_ch,
                                             ve.xin + (long long)m * ve.xin_stride, r, lane);
-        int tk = ve.tok[m];
-        tk = tk < 0 ? 0 : (tk >= ve.vocab ? ve.vocab - 1 : tk);
-        const T* e = (const T*)ve.ve + ((long long)tk * a.nkv + jj) * a.hd;
+        const T* e = (const T*)ve.ve + ((long long)ve.tok[m] * a.nkv + jj) * a.hd;
         if (act) {
             v1 += g * to_f32(e[lane]);
             v2 += g * to_f32(e[lane + half]);

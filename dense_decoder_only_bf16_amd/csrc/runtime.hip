@@ -134,6 +134,9 @@ struct nc_kv {
     float* dpart = nullptr;   // decode projections with more than 32 rows: split-K partials
     float* x0 = nullptr;      // later-version blocks: stream before layer 0's scaling [M][d]
     float* xb = nullptr;      // and the backout source [M][d]
+    int32_t* tokbuf = nullptr;   // the rows' clamped tokens (value embeddings) [M]
+    ResidExtra* rx_dev = nullptr;  // per layer: the PROJ residual's blocks (decode)
+    ValueEmbed* ve_dev = nullptr;  // per layer: the value embedding (decode)
     long long dpart_elems = 0;
     long long apart_elems = 0;
     int apart_slots = 0;      // partial slots per (row, K/V head) unit, the most any layer needs
@@ -162,15 +165,45 @@ void drop_graphs(nc_kv* kv) {
 void ws_free(nc_kv* kv) {
     drop_graphs(kv);  // captured graphs point into the workspace
     void* ptrs[] = {kv->x, kv->act, kv->ss_a, kv->ss_b, kv->qkv, kv->q, kv->y, kv->u, kv->apart,
-                    kv->act_lo, kv->u_lo, kv->dpart, kv->x0, kv->xb};
+                    kv->act_lo, kv->u_lo, kv->dpart, kv->x0, kv->xb, kv->tokbuf, kv->rx_dev, kv->ve_dev};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     kv->x = nullptr; kv->act = nullptr; kv->ss_a = nullptr; kv->ss_b = nullptr; kv->qkv = nullptr;
     kv->q = nullptr; kv->y = nullptr; kv->u = nullptr; kv->apart = nullptr;
     kv->act_lo = nullptr; kv->u_lo = nullptr; kv->dpart = nullptr; kv->x0 = nullptr; kv->xb = nullptr;
+    kv->tokbuf = nullptr; kv->rx_dev = nullptr; kv->ve_dev = nullptr;
     kv->dpart_elems = 0;
     kv->cap_m = 0;
     kv->apart_elems = 0;
+}
+
+// RESID extras of layer l's MLP residual (PROJ): the next layer's scaling, the backout
+// source when the next layer is the backout layer, the backout itself after the last.
+ResidExtra proj_resid_extra(const nc_model* m, const nc_kv* kv, int l) {
+    const nc_model::Extras& ex = m->ex;
+    ResidExtra r{};
+    r.ra = 1.f;
+    if (!ex.on) return r;
+    r.x0 = kv->x0;
+    if (l + 1 < m->cfg.n_layer) {
+        r.ra = ex.lam[l + 1];
+        r.rb = ex.mu[l + 1];
+        if (l + 1 == ex.backout_layer) r.xb_out = kv->xb;
+    } else if (ex.backout_layer >= 0) {
+        r.xb = kv->xb;
+        r.rc = -ex.backout_lambda;
+    }
+    return r;
+}
+
+// Value embedding of layer l (ve null: none); the tokens are those the embedding kernel
+// recorded for the rows of the current call.
+ValueEmbed value_embed(const nc_model* m, const nc_kv* kv, int l) {
+    ValueEmbed v{};
+    if (!m->ex.on || !m->ex.ve[l]) return v;
+    v.ve = m->ex.ve[l]; v.ve_gate = m->ex.ve_gate[l]; v.ve_ch = m->ex.ve_ch; v.vocab = m->cfg.vocab;
+    v.tok = kv->tokbuf; v.xin = kv->x; v.xin_stride = m->cfg.d_model;
+    return v;
 }
 
 // Grow the workspace to hold M token rows.
@@ -200,8 +233,14 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
         WS_ALLOC(kv->act_lo, Mr * d * es);
         WS_ALLOC(kv->u_lo, Mr * c.d_ff * es);
     }
-    if (kv->m->ex.on) WS_ALLOC(kv->x0, M * d * 4);
-    if (kv->m->ex.on && kv->m->ex.backout_layer >= 0) WS_ALLOC(kv->xb, M * d * 4);
+    const nc_model::Extras& ex = kv->m->ex;
+    if (ex.on) {
+        WS_ALLOC(kv->x0, M * d * 4);
+        if (ex.backout_layer >= 0) WS_ALLOC(kv->xb, M * d * 4);
+        WS_ALLOC(kv->tokbuf, M * 4);
+        WS_ALLOC(kv->rx_dev, c.n_layer * sizeof(ResidExtra));
+        WS_ALLOC(kv->ve_dev, c.n_layer * sizeof(ValueEmbed));
+    }
     {
         const int units = kv->B * c.n_kv_head;  // (row, K/V head) pairs of decode attention
         int slots = 0;
@@ -225,6 +264,16 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
     }
 #undef WS_ALLOC
     kv->cap_m = M;
+    if (ex.on) {  // the per-layer blocks that decode kernels read through pointers
+        std::vector<ResidExtra> rx(c.n_layer);
+        std::vector<ValueEmbed> ve(c.n_layer);
+        for (int l = 0; l < c.n_layer; ++l) {
+            rx[l] = proj_resid_extra(kv->m, kv, l);
+            ve[l] = value_embed(kv->m, kv, l);
+        }
+        HIP_TRY(hipMemcpy(kv->rx_dev, rx.data(), rx.size() * sizeof(ResidExtra), hipMemcpyHostToDevice));
+        HIP_TRY(hipMemcpy(kv->ve_dev, ve.data(), ve.size() * sizeof(ValueEmbed), hipMemcpyHostToDevice));
+    }
     return NC_OK;
 }
 
@@ -354,35 +403,9 @@ EmbedArgs embed_args(nc_model* m, nc_kv* kv, const int32_t* tokens, int M, int T
         e.x0 = kv->x0;
         if (ex.backout_layer == 0) e.xb = kv->xb;
         e.smear_gate = ex.smear_gate; e.smear_ch = ex.smear_ch; e.smear_lambda = ex.smear_lambda;
+        e.tok_out = kv->tokbuf;
     }
     return e;
-}
-
-// RESID extras of layer l's MLP residual (PROJ): the next layer's scaling, the backout
-// source when the next layer is the backout layer, the backout itself after the last.
-ResidExtra proj_resid_extra(const nc_model* m, const nc_kv* kv, int l) {
-    const nc_model::Extras& ex = m->ex;
-    ResidExtra r{};
-    r.ra = 1.f;
-    if (!ex.on) return r;
-    r.x0 = kv->x0;
-    if (l + 1 < m->cfg.n_layer) {
-        r.ra = ex.lam[l + 1];
-        r.rb = ex.mu[l + 1];
-        if (l + 1 == ex.backout_layer) r.xb_out = kv->xb;
-    } else if (ex.backout_layer >= 0) {
-        r.xb = kv->xb;
-        r.rc = -ex.backout_lambda;
-    }
-    return r;
-}
-
-ValueEmbed value_embed(const nc_model* m, const nc_kv* kv, int l, const int32_t* tokens) {
-    ValueEmbed v{};
-    if (!m->ex.on || !m->ex.ve[l]) return v;
-    v.ve = m->ex.ve[l]; v.ve_gate = m->ex.ve_gate[l]; v.ve_ch = m->ex.ve_ch; v.vocab = m->cfg.vocab;
-    v.tok = tokens; v.xin = kv->x; v.xin_stride = m->cfg.d_model;
-    return v;
 }
 
 // Enqueue one decode step (everything after the host-side checks) on `st`.
@@ -415,7 +438,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = kv->apart;
         at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.nkv = nkv; at.max_slots = kv->apart_slots;
         at.window = m->windows[l];
-        at.vemb = value_embed(m, kv, l, tokens);
+        at.vemb = (m->ex.on && m->ex.ve[l]) ? kv->ve_dev + l : nullptr;
         at.iters = attn_decode_iters(B * nkv, attn_decode_span(kv->S, at.window));
         {   // bytes: the K/V read for every row (its visible positions, the new one
             // included) of each K/V head, q/k/v in fp32, y out; flops 4 hd per
@@ -443,7 +466,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         DecGemmArgs pj = a;
         pj.A = kv->u; pj.A_lo = kv->u_lo; pj.W = L.wproj; pj.N = d; pj.K = F;
         pj.out_f32 = kv->x; pj.out_t = kv->act; pj.ldo = d; pj.ss_out = kv->ss_a;
-        pj.rx = proj_resid_extra(m, kv, l);
+        pj.rx = m->ex.on ? kv->rx_dev + l : nullptr;
         if (l == c.n_layer - 1) pj.out_lo = kv->act_lo;  // the LM head's operand is compensated
         if ((s = decode_gemm(kv, EPI_RESID, pj, st)) != NC_OK) return s;
         ss_a_parts = parts_d;
@@ -879,7 +902,7 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             qa.lens = kv->lens_dev; qa.rope_cos = m->rope_cos; qa.rope_sin = m->rope_sin;
             qa.q = kv->q; qa.kc = (char*)kv->kcache + l * per_layer; qa.vtc = (char*)kv->vcache + l * per_layer;
             qa.S = kv->S; qa.eps = c.norm_eps;
-            qa.vemb = value_embed(m, kv, l, tokens);
+            qa.vemb = value_embed(m, kv, l);
             LAUNCH(launch_qkv_post(m->dt, qa, st));
             {   // causal attention flops: 4 hd per visible (query, key) pair and head; bytes:
                 // q in, y out, and every key/value a query of the row sees, read once

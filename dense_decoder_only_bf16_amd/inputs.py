@@ -52,6 +52,7 @@ class Workload:
     short_window: int = 0        # window of the pattern's S layers (keys back)
     temperature: float = 0.0     # decode picks: > 0 samples (with top_k), else greedy
     top_k: int = 0
+    extras_seed: int = -1        # >= 0: the later version's blocks from make_extras(seed)
 
 
 def from_depth(depth, vocab=65536, dtype="bf16", max_seq=2048, name=None):
@@ -77,6 +78,9 @@ WORKLOADS = {
     "d20-gqa": Workload(replace(D20, name="d20-gqa", n_kv_head=5), 32, 2048, 64, 128, 2048),
     "d20-sssl": Workload(replace(D20, name="d20-sssl"), 32, 2048, 64, 128, 2048,
                          window_pattern="SSSL", short_window=512),
+    # the later version's learned blocks on the d20 model and run (value embeddings on the
+    # odd layers, residual lambdas, smear, backout at layer 10)
+    "d20-blocks": Workload(replace(D20, name="d20-blocks"), 32, 2048, 64, 128, 2048, extras_seed=5),
     # the d12 run with sampled instead of greedy decode picks (temperature 1, top-50)
     "d12-sample": Workload(D12, 8, 2048, 8, 256, 2048, temperature=1.0, top_k=50),
 }

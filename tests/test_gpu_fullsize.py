@@ -16,7 +16,7 @@ import pytest
 
 from dense_decoder_only_bf16_amd import nc
 from dense_decoder_only_bf16_amd.inputs import (D12, D20, D26, D30, WORKLOADS, canonical_list,
-                                                make_lens, make_tokens, make_weights)
+                                                make_extras, make_lens, make_tokens, make_weights)
 from oracle import OracleModel
 
 from gpu_helpers import torch_mod
@@ -46,11 +46,12 @@ def check(tag, got, want):
 
 
 class Run:
-    def __init__(self, shape, windows=None):
+    def __init__(self, shape, windows=None, extras=None):
         self.shape = shape
         self.w = make_weights(shape, seed=0)
-        self.model = nc.Model(shape, canonical_list(self.w), max_seq=shape.max_seq, windows=windows)
-        self.orc = OracleModel(shape, self.w, windows=windows)
+        self.model = nc.Model(shape, canonical_list(self.w), max_seq=shape.max_seq, windows=windows,
+                              extras=extras)
+        self.orc = OracleModel(shape, self.w, windows=windows, extras=extras)
 
     def close(self):
         self.model.close()
@@ -177,17 +178,18 @@ def test_d30_decode_mixed_lengths():
         check(f"d30 decode row {b} (context {n})", np.stack(got[b]), want[0])
 
 
-@pytest.mark.parametrize("name", ["d20-gqa", "d20-sssl"])
+@pytest.mark.parametrize("name", ["d20-gqa", "d20-sssl", "d20-blocks"])
 def test_d20_attention_variants(name):
-    """The d20 step with 5 K/V heads, or with SSSL 512-key windows: prefill 32 x 2048 in the
-    benchmark's launch shape (row 0 checked over its first 768 positions, past the first
-    window), then the rows truncated to lengths in 600..900 and two decode steps."""
+    """The d20 step with 5 K/V heads, with SSSL 512-key windows, or with the learned blocks:
+    prefill 32 x 2048 in the benchmark's launch shape (row 0 checked over its first 768
+    positions, past the first window), then the rows truncated to lengths in 600..900 and
+    two decode steps."""
     torch = torch_mod()
     wl = WORKLOADS[name]
     shape = wl.shape
     wins = (nc.layer_windows(wl.window_pattern, shape.n_layer, wl.short_window)
             if wl.window_pattern else None)
-    r = Run(shape, wins)
+    r = Run(shape, wins, make_extras(shape, seed=wl.extras_seed) if wl.extras_seed >= 0 else None)
     B, T, steps = 32, 2048, 2
     toks = make_tokens(shape.vocab, B, T + steps, seed=3)
     kv = r.model.new_kv(B, shape.max_seq)
