@@ -1,5 +1,7 @@
 // Causal multi-query attention for gfx950: a flash-style prefill kernel and a split-context
-// decode kernel with a combine kernel.
+// decode kernel with a combine kernel.  Both write the attention output y in the layout the
+// O product reads: MFMA-blocked (kernels.h, blocked_index) for bf16, row-major for fp32
+// prefill.
 //
 // Multi-query attention: one K/V head serves every query head (yelogs.com launch write-up,
 // architecture answer).  Causal softmax of q.k/sqrt(hd) over keys at positions <= the
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
         const int qi = q0w + jn * 32 + l32;
         if (qi >= Tn) continue;
         const float inv = 1.0f / l_run[jn];
-        T* dst = y + (((long long)b * Tn + qi) * H + head) * HD;
+        const long long row = (long long)b * Tn + qi;
 #pragma unroll
         for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -241,7 +243,10 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
                 HT o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(oacc[md][jn][4 * g + e] * inv);
-                *(HT*)(dst + md * 32 + 8 * g + 4 * hh) = o;
+                const int c = head * HD + md * 32 + 8 * g + 4 * hh;  // 4 features, 4-aligned
+                // bf16: the O product's operand layout (blocked); fp32: row-major
+                const long long o_idx = sizeof(T) == 2 ? blocked_index((int)row, c, H * HD) : row * H * HD + c;
+                *(HT*)(y + o_idx) = o;
             }
     }
 }

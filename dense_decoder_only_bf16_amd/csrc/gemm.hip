@@ -104,8 +104,9 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[2
                 } else if (EPI == EPI_RELU2) {
                     const float t = fmaxf(v * rs[rl], 0.f);
                     const T hi = from_f32<T>(t * t);
-                    if (ok) ((T*)p.out_t)[o] = hi;
-                    if (ok && p.out_lo) ((T*)p.out_lo)[o] = from_f32<T>(t * t - to_f32(hi));
+                    const long long ot = sizeof(T) == 2 ? blocked_index(m, n, p.ldo) : o;
+                    if (ok) ((T*)p.out_t)[ot] = hi;
+                    if (ok && p.out_lo) ((T*)p.out_lo)[ot] = from_f32<T>(t * t - to_f32(hi));
                 } else if (EPI == EPI_SOFTCAP) {
                     if (ok) p.out_f32[o] = p.cap * tanh_f32(v * rs[rl] / p.cap);
                 } else {  // EPI_RESID
@@ -113,8 +114,9 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[2
                         const float xn = resid_value(p.rx, o, p.out_f32[o], v);
                         p.out_f32[o] = xn;
                         const T hi = from_f32<T>(xn);
-                        ((T*)p.out_t)[o] = hi;
-                        if (p.out_lo) ((T*)p.out_lo)[o] = from_f32<T>(xn - to_f32(hi));
+                        const long long ot = sizeof(T) == 2 ? blocked_index(m, n, p.ldo) : o;
+                        ((T*)p.out_t)[ot] = hi;
+                        if (p.out_lo) ((T*)p.out_lo)[ot] = from_f32<T>(xn - to_f32(hi));
                         sq += xn * xn;
                     }
                 }
@@ -181,8 +183,11 @@ void gemm_bf16_kernel(GemmArgs p) {
 
     // Stage layout: 16 A blocks (row block rb = b/2, k block b%2) then 16 B blocks.  Wave w
     // loads A blocks 2w, 2w+1 and B blocks 2w, 2w+1; lane l fills bytes [16 l, 16 l + 16)
-    // of a 1 KB block, i.e. row l/2, k half l%2.  Rows past M or Npad read a clamped
-    // address; their outputs are masked in the epilogue.
+    // of a 1 KB block, i.e. row l/2, k half l%2.  A and B are both stored blocked, so each
+    // block is one contiguous 1 KB load (8 cache lines, fully used).  A holds ceil(M/32)
+    // whole 32-row blocks (rows past M are padding); a tile's row blocks past the last one
+    // and weight blocks past Npad read a clamped block.  Their outputs are masked in the
+    // epilogue.
     auto issue = [&](int kt) {
         bf16* sbase = lds + (kt % NS) * STAGE;
         const int k0 = (comp ? kt >> 1 : kt) * BK;
@@ -191,9 +196,9 @@ void gemm_bf16_kernel(GemmArgs p) {
         for (int u = 0; u < 2; ++u) {
             const int b = wave * 2 + u;
             const int rb = b / KB, kb = b % KB;
-            int m = m0 + rb * 32 + lane / 2;
-            m = m < p.M ? m : p.M - 1;
-            const bf16* src = As + (long long)m * p.lda + k0 + kb * 16 + (lane % 2) * 8;
+            int mb = m0 / 32 + rb;
+            mb = mb < (p.M + 31) / 32 ? mb : (p.M + 31) / 32 - 1;  // tiles reach past the last block
+            const bf16* src = As + ((long long)mb * (p.K / 16) + (k0 / 16 + kb)) * 512 + lane * 8;
             __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(sbase + b * 512), 16, 0, 0);
         }
 #pragma unroll

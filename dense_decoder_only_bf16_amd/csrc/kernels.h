@@ -70,7 +70,10 @@ __device__ inline float resid_value(const ResidExtra* e, long long o, float x_ol
 }
 
 struct GemmArgs {
-    const void* A;  // [M][lda] dtype, K contiguous
+    // bf16: blocked [ceil(M/32)][K/16][32][16] (whole 32-row blocks; lda unused);
+    // fp32: [M][lda], K contiguous.  The same holds for A_lo and for the dtype outputs
+    // out_t / out_lo of RELU2 and RESID (blocked with K = ldo for bf16).
+    const void* A;
     const void* B;  // blocked weight (see above), Npad rows
     int M, N, K, lda, Npad;
     int k_split;        // grid z; K / k_split must be a multiple of the K tile
@@ -82,7 +85,7 @@ struct GemmArgs {
     int ss_in_parts, ss_stride;
     float* ss_out;      // RESID: ss_out[tile_n * ss_stride + m]
     float eps, cap;
-    // Compensated operand (bf16 only): A_lo [M][lda] holds a - bf16(a) in bf16, and the
+    // Compensated operand (bf16 only): A_lo (laid out like A) holds a - bf16(a) in bf16, and the
     // product is taken over both parts (A + A_lo) W^T.  Null: plain A.
     const void* A_lo;
     // RELU2 / RESID: also write value - dtype(value) in dtype here (the low part a later

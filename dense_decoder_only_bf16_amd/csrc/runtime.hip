@@ -886,7 +886,8 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
         const size_t per_layer = (size_t)B * nkv * kv->S * hd * m->esz;
         const int Mi = (int)M;
 
-        LAUNCH(launch_embed(m->dt, embed_args(m, kv, tokens, Mi, T, false), st));
+        // bf16 activations of prefill are stored blocked, the layout the products read
+        LAUNCH(launch_embed(m->dt, embed_args(m, kv, tokens, Mi, T, m->dt == BF16), st));
         int ss_a_parts = 1;
         for (int l = 0; l < c.n_layer; ++l) {
             const nc_model::Layer& L = m->layers[l];
