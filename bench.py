@@ -308,6 +308,17 @@ def main():
         out["decode_tokens_per_s"] = round(n_dec / (dec_ms / 1000.0), 1)
     if not args.no_roofline:
         out["roofline"], out["kernels"] = roofline(nc, one_step, shape.dtype, args.workload)
+        # what this GPU sustains with plain kernels, beside the published peaks
+        rnd = nc.nc_diag_mfma_rate(True)
+        const = nc.nc_diag_mfma_rate(False)
+        hbm = nc.nc_diag_hbm_read_rate()
+        out["sustained"] = {
+            "mfma_bf16_random_operands_tflops": round(rnd, 1),
+            "mfma_bf16_constant_operands_tflops": round(const, 1),
+            "hbm_read_stream_tbps": round(hbm, 3),
+            "roofline_frac_of_sustained": round(
+                out["roofline"]["achieved"] / (rnd if out["roofline"]["unit"] == "TFLOP/s" else hbm * 1000.0), 4),
+        }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(shape, weights, wl, args.cpu_seconds, windows, extras)
     for kv in {id(k): k for k in (kv_p, kv_d) if k is not None}.values():

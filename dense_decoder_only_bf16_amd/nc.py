@@ -39,7 +39,8 @@ NC_KC_DECODE_ATTN = 4
 EXPORTED = ("nc_model_create", "nc_model_free", "nc_model_set_windows", "nc_model_set_extras",
             "nc_kv_create", "nc_kv_free", "nc_kv_set_lens",
             "nc_kv_get_lens", "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step", "nc_argmax",
-            "nc_sample", "nc_timing_enable", "nc_timing_read", "nc_last_error", "nc_abi_version")
+            "nc_sample", "nc_timing_enable", "nc_timing_read", "nc_last_error", "nc_abi_version",
+            "nc_diag_mfma_rate", "nc_diag_hbm_read_rate")
 
 
 class NcError(RuntimeError):
@@ -104,11 +105,14 @@ def lib():
         L.nc_timing_read.argtypes = [ctypes.POINTER(nc_timing)]
         L.nc_last_error.argtypes = []
         L.nc_last_error.restype = ctypes.c_char_p
+        L.nc_diag_mfma_rate.argtypes = [i32, ctypes.POINTER(ctypes.c_double)]
+        L.nc_diag_hbm_read_rate.argtypes = [ctypes.POINTER(ctypes.c_double)]
         L.nc_abi_version.argtypes = []
         L.nc_abi_version.restype = i32
         for name in ("nc_model_create", "nc_model_set_windows", "nc_model_set_extras", "nc_kv_create", "nc_kv_set_lens", "nc_kv_get_lens",
                      "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step", "nc_argmax",
-                     "nc_sample", "nc_timing_enable", "nc_timing_read"):
+                     "nc_sample", "nc_timing_enable", "nc_timing_read", "nc_diag_mfma_rate",
+                     "nc_diag_hbm_read_rate"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -288,6 +292,18 @@ def nc_timing_read():
     t = nc_timing()
     _check(lib().nc_timing_read(ctypes.byref(t)))
     return t.launches, t.ms, t.bytes, t.flops
+
+
+def nc_diag_mfma_rate(random_operands=True):
+    v = ctypes.c_double()
+    _check(lib().nc_diag_mfma_rate(1 if random_operands else 0, ctypes.byref(v)))
+    return v.value
+
+
+def nc_diag_hbm_read_rate():
+    v = ctypes.c_double()
+    _check(lib().nc_diag_hbm_read_rate(ctypes.byref(v)))
+    return v.value
 
 
 # ------------------------------------------------------------------ convenience -------

@@ -232,6 +232,16 @@ typedef struct nc_timing {
 nc_status nc_timing_enable(int32_t kernel_class);
 nc_status nc_timing_read(nc_timing* out);
 
+/* Diagnostics (measurement context, not part of the forward): what the current GPU
+ * sustains with plain kernels, synchronous, about a second each.
+ * nc_diag_mfma_rate: dense bf16 32x32x16 MFMA throughput in TFLOP/s, with operands that
+ *   keep toggling (random_operands != 0) or stay fixed; the matrix cores' power draw, and
+ *   so the clock they hold, depends on the data.
+ * nc_diag_hbm_read_rate: a 1 GiB device-memory read stream in TB/s.
+ * NC_ERR_INVALID_ARG for a NULL output, NC_ERR_DEVICE on a HIP error. */
+nc_status nc_diag_mfma_rate(int32_t random_operands, double* tflops_out);
+nc_status nc_diag_hbm_read_rate(double* tbps_out);
+
 /* Message of the last error on the calling thread ("" if none). */
 const char* nc_last_error(void);
 int32_t nc_abi_version(void);

@@ -785,3 +785,12 @@ def test_extras_switch_off_and_errors(small):
     _, got = prefill(gm, toks, 20)
     want, _ = orc.prefill(toks)
     assert np.max(np.abs(got - want)) <= BF16_TOL
+
+
+def test_diagnostic_rates_are_physical():
+    """The sustained-rate probes return values below MI355X's published peaks."""
+    rnd, const = nc.nc_diag_mfma_rate(True), nc.nc_diag_mfma_rate(False)
+    hbm = nc.nc_diag_hbm_read_rate()
+    print(f"[diag] mfma random {rnd:.0f} constant {const:.0f} TFLOP/s, hbm read {hbm:.2f} TB/s", flush=True)
+    assert 100.0 < rnd <= 2516.6 * 1.05 and 100.0 < const <= 2516.6 * 1.05
+    assert 0.5 < hbm <= 8.0 * 1.05
