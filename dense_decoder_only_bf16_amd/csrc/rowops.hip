@@ -134,20 +134,30 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
     const int b = m / a.T;
     const int pos = m % a.T + (a.lens ? a.lens[b] : 0);
     if (pos < 0 || pos >= a.S) return;  // capacity is checked by the host; stay in bounds
-    float s = 0.f;
-    for (int q = 0; q < a.ss_in_parts; ++q) s += a.ss_in[(long long)q * a.ss_stride + m];
-    const float r = 1.0f / sqrtf(s / (float)a.norm_dim + a.eps);
+    // row scale: the lanes share the row's partial sums of squares
+    const float r = row_scale_wave(a.ss_in, a.ss_in_parts, a.ss_stride, m, a.norm_dim, a.eps);
     const int N = slots * a.hd;
     const bool act = lane < half;
+    const int i = act ? lane : 0;
     float v1 = 0.f, v2 = 0.f;
-    if (act) {
+    {   // the K-split slices, in order, 8 independent loads per batch
         const float* src = a.part + (long long)m * N + j * a.hd;
-        for (int z = 0; z < a.splits; ++z) {
-            v1 += src[(long long)z * a.z_stride + lane];
-            v2 += src[(long long)z * a.z_stride + lane + half];
+        for (int z0 = 0; z0 < a.splits; z0 += 8) {
+            float t1[8], t2[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const long long o = (long long)min(z0 + u, a.splits - 1) * a.z_stride;
+                t1[u] = src[o + i];
+                t2[u] = src[o + i + half];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                v1 += (z0 + u < a.splits) ? t1[u] : 0.f;
+                v2 += (z0 + u < a.splits) ? t2[u] : 0.f;
+            }
         }
-        v1 *= r;
-        v2 *= r;
+        v1 = act ? v1 * r : 0.f;
+        v2 = act ? v2 * r : 0.f;
     }
     if (j >= a.H + a.nkv && a.vemb.ve) {  // wave-uniform
         const ValueEmbed& ve = a.vemb;
