@@ -88,6 +88,21 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[2
     const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
     for (int i = 0; i < IM; ++i) {
+        // RESID: the old residual of this row tile, all loaded before any store (the stores
+        // write the same array, so the compiler could not move a later load above them and
+        // every element would wait a full memory round trip)
+        float xold[16][JN];
+        if (EPI == EPI_RESID) {
+#pragma unroll
+            for (int jr = 0; jr < 16; ++jr) {
+                const int m = min(m0 + wm * (256 / WM) + i * 32 + 8 * (jr / 4) + 4 * hh + (jr % 4), p.M - 1);
+#pragma unroll
+                for (int j = 0; j < JN; ++j) {
+                    const int n = min(n0 + wn * (256 / WN) + j * 32 + l32, p.N - 1);
+                    xold[jr][j] = p.out_f32[(long long)m * p.ldo + n];
+                }
+            }
+        }
 #pragma unroll
         for (int jr = 0; jr < 16; ++jr) {
             const int rl = wm * (256 / WM) + i * 32 + 8 * (jr / 4) + 4 * hh + (jr % 4);
@@ -111,7 +126,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[2
                     if (ok) p.out_f32[o] = p.cap * tanh_f32(v * rs[rl] / p.cap);
                 } else {  // EPI_RESID
                     if (ok) {
-                        const float xn = resid_value(p.rx, o, p.out_f32[o], v);
+                        const float xn = resid_value(p.rx, o, xold[jr][j], v);
                         p.out_f32[o] = xn;
                         const T hi = from_f32<T>(xn);
                         const long long ot = sizeof(T) == 2 ? blocked_index(m, n, p.ldo) : o;
