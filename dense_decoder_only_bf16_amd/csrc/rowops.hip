@@ -121,87 +121,142 @@ hipError_t launch_embed(DType dt, const EmbedArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------------ QKV finish ------
-// One wave per (row, head slot); slots 0..H-1 are query heads, H..H+nkv-1 the key heads,
-// H+nkv..H+2nkv-1 the value heads.  Lane i < hd/2 holds the RoPE pair (i, i + hd/2).
+// Workgroup (head slot j, 64 consecutive tokens of one batch row); slots 0..H-1 are query
+// heads, H..H+nkv-1 the key heads, H+nkv..H+2nkv-1 the value heads.  Wave w takes tokens
+// 16 w .. 16 w + 15 of the tile one after another; lane i < hd/2 holds the RoPE pair
+// (i, i + hd/2).  The 16 row scales of a wave are computed up front, one token per lane.
+// Value heads go through LDS so that each row d of the transposed V cache is written as
+// 64 consecutive positions.
+constexpr int QP_TILE = 64;
+
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs a) {
-    const int lane = threadIdx.x & 63;
-    const long long gw = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int slots = a.H + 2 * a.nkv;
-    if (gw >= (long long)a.M * slots) return;
-    const int m = (int)(gw / slots), j = (int)(gw % slots);
+    __shared__ T vs[128][QP_TILE];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = blockIdx.x;
+    const int tpr = (a.T + QP_TILE - 1) / QP_TILE;
+    const int b = blockIdx.y / tpr, t0 = (blockIdx.y % tpr) * QP_TILE;
+    const int off = a.lens ? a.lens[b] : 0;  // position of the row's token 0
     const int half = a.hd / 2;
-    const int b = m / a.T;
-    const int pos = m % a.T + (a.lens ? a.lens[b] : 0);
-    if (pos < 0 || pos >= a.S) return;  // capacity is checked by the host; stay in bounds
-    // row scale: the lanes share the row's partial sums of squares
-    const float r = row_scale_wave(a.ss_in, a.ss_in_parts, a.ss_stride, m, a.norm_dim, a.eps);
+    const int slots = a.H + 2 * a.nkv;
     const int N = slots * a.hd;
     const bool act = lane < half;
     const int i = act ? lane : 0;
-    float v1 = 0.f, v2 = 0.f;
-    {   // the K-split slices, in order, 8 independent loads per batch
-        const float* src = a.part + (long long)m * N + j * a.hd;
-        for (int z0 = 0; z0 < a.splits; z0 += 8) {
-            float t1[8], t2[8];
+    const bool is_v = j >= a.H + a.nkv;
+
+    // row scales of this wave's 16 tokens: lane k < 16 takes token 16 wave + k
+    float rl = 1.f;
+    {
+        const int tk = t0 + 16 * wave + (lane & 15);
+        const int m = b * a.T + min(tk, a.T - 1);
+        constexpr int MAXP = 16;  // partial sums per row (prefill: one per 256 columns)
+        float sp[MAXP];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const long long o = (long long)min(z0 + u, a.splits - 1) * a.z_stride;
-                t1[u] = src[o + i];
-                t2[u] = src[o + i + half];
-            }
+        for (int q = 0; q < MAXP; ++q)
+            sp[q] = q < a.ss_in_parts ? a.ss_in[(long long)q * a.ss_stride + m] : 0.f;
+        float ssum = 0.f;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                v1 += (z0 + u < a.splits) ? t1[u] : 0.f;
-                v2 += (z0 + u < a.splits) ? t2[u] : 0.f;
+        for (int q = 0; q < MAXP; ++q) ssum += sp[q];
+        for (int q = MAXP; q < a.ss_in_parts; ++q) ssum += a.ss_in[(long long)q * a.ss_stride + m];
+        rl = 1.0f / sqrtf(ssum / (float)a.norm_dim + a.eps);
+    }
+    // One product slice (prefill): the 16 tokens' values and rotation tables are all loaded
+    // before any arithmetic (rows past the tile's last token read a clamped row).
+    const bool one = a.splits == 1;
+    float pv1[16], pv2[16], pc[16], ps[16];
+    if (one) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int t = min(t0 + 16 * wave + k, a.T - 1);
+            const float* src = a.part + (long long)(b * a.T + t) * N + j * a.hd;
+            pv1[k] = src[i];
+            pv2[k] = src[i + half];
+            const int pos = min(max(off + t, 0), a.S - 1);
+            pc[k] = a.rope_cos[(long long)pos * half + i];
+            ps[k] = a.rope_sin[(long long)pos * half + i];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int tl = 16 * wave + k, t = t0 + tl;
+        const float r = __shfl(rl, k, 64);
+        if (t >= a.T) break;  // wave-uniform
+        const int m = b * a.T + t;
+        const int pos = off + t;
+        float v1 = 0.f, v2 = 0.f;
+        if (one) {
+            v1 = act ? pv1[k] * r : 0.f;
+            v2 = act ? pv2[k] * r : 0.f;
+        } else {   // the K-split slices, in order, 8 independent loads per batch
+            const float* src = a.part + (long long)m * N + j * a.hd;
+            for (int z0 = 0; z0 < a.splits; z0 += 8) {
+                float t1[8], t2[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const long long o = (long long)min(z0 + u, a.splits - 1) * a.z_stride;
+                    t1[u] = src[o + i];
+                    t2[u] = src[o + i + half];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    v1 += (z0 + u < a.splits) ? t1[u] : 0.f;
+                    v2 += (z0 + u < a.splits) ? t2[u] : 0.f;
+                }
             }
+            v1 = act ? v1 * r : 0.f;
+            v2 = act ? v2 * r : 0.f;
         }
-        v1 = act ? v1 * r : 0.f;
-        v2 = act ? v2 * r : 0.f;
-    }
-    if (j >= a.H + a.nkv && a.vemb.ve) {  // wave-uniform
-        const ValueEmbed& ve = a.vemb;
-        const int jj = j - a.H - a.nkv;
-        const float g = value_embed_gate<T>((const T*)ve.ve_gate, jj, ve.ve_ch,
-                                            ve.xin + (long long)m * ve.xin_stride, r, lane);
-        const T* e = (const T*)ve.ve + ((long long)ve.tok[m] * a.nkv + jj) * a.hd;
-        if (act) {
-            v1 += g * to_f32(e[lane]);
-            v2 += g * to_f32(e[lane + half]);
+        if (is_v) {
+            if (a.vemb.ve) {  // the layer's value embedding
+                const ValueEmbed& ve = a.vemb;
+                const int jj = j - a.H - a.nkv;
+                const float g = value_embed_gate<T>((const T*)ve.ve_gate, jj, ve.ve_ch,
+                                                    ve.xin + (long long)m * ve.xin_stride, r, lane);
+                const T* e = (const T*)ve.ve + ((long long)ve.tok[m] * a.nkv + jj) * a.hd;
+                v1 += act ? g * to_f32(e[i]) : 0.f;
+                v2 += act ? g * to_f32(e[i + half]) : 0.f;
+            }
+            if (act) {
+                vs[i][tl] = from_f32<T>(v1);
+                vs[i + half][tl] = from_f32<T>(v2);
+            }
+            continue;
         }
-    }
-    if (j < a.H + a.nkv) {
+        if (pos < 0 || pos >= a.S) continue;  // capacity is checked by the host
         float c = 0.f, sn = 0.f;
         if (act) {
-            c = a.rope_cos[(long long)pos * half + lane];
-            sn = a.rope_sin[(long long)pos * half + lane];
+            c = one ? pc[k] : a.rope_cos[(long long)pos * half + i];
+            sn = one ? ps[k] : a.rope_sin[(long long)pos * half + i];
         }
         float o1 = v1 * c - v2 * sn;
         float o2 = v1 * sn + v2 * c;
-        float ms = wave_sum(o1 * o1 + o2 * o2) / (float)a.hd;
-        float rr = 1.0f / sqrtf(ms + a.eps);
-        o1 *= rr;
-        o2 *= rr;
+        const float ms = wave_sum(o1 * o1 + o2 * o2) / (float)a.hd;
+        const float rr = 1.0f / sqrtf(ms + a.eps);
         if (act) {
             T* dst;
             if (j < a.H)
                 dst = (T*)a.q + ((long long)m * a.H + j) * a.hd;
             else
                 dst = (T*)a.kc + (((long long)b * a.nkv + (j - a.H)) * a.S + pos) * a.hd;
-            dst[lane] = from_f32<T>(o1);
-            dst[lane + half] = from_f32<T>(o2);
+            dst[i] = from_f32<T>(o1 * rr);
+            dst[i + half] = from_f32<T>(o2 * rr);
         }
-    } else if (act) {
+    }
+    if (is_v) {  // workgroup-uniform: V^T rows, 64 consecutive positions each
+        __syncthreads();
         T* vt = (T*)a.vtc + ((long long)b * a.nkv + (j - a.H - a.nkv)) * a.hd * a.S;
-        vt[(long long)lane * a.S + pos] = from_f32<T>(v1);
-        vt[(long long)(lane + half) * a.S + pos] = from_f32<T>(v2);
+        for (int e = threadIdx.x; e < a.hd * QP_TILE; e += 256) {
+            const int d = e / QP_TILE, p = e % QP_TILE;
+            const int pos = off + t0 + p;
+            if (t0 + p < a.T && pos >= 0 && pos < a.S) vt[(long long)d * a.S + pos] = vs[d][p];
+        }
     }
 }
 
 hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st) {
-    if (a.nkv < 1 || a.H % a.nkv) return hipErrorInvalidValue;
-    long long waves = (long long)a.M * (a.H + 2 * a.nkv);
-    dim3 grid((unsigned)((waves + 3) / 4));
+    if (a.nkv < 1 || a.H % a.nkv || a.hd > 128 || a.T < 1 || a.M % a.T) return hipErrorInvalidValue;
+    const int B = a.M / a.T, tpr = (a.T + QP_TILE - 1) / QP_TILE;
+    dim3 grid(a.H + 2 * a.nkv, B * tpr);
     if (dt == BF16)
         hipLaunchKernelGGL(qkv_post_kernel<bf16>, grid, dim3(256), 0, st, a);
     else
