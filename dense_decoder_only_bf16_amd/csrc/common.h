@@ -93,6 +93,23 @@ __device__ __forceinline__ float wave_max(float v) {
 // (expcnt and lgkmcnt left at their maxima), in the gfx9 s_waitcnt encoding.
 #define NC_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
+// Device-scope plain accesses (relaxed atomics at agent scope): the store is written
+// through to the level where the dies' L2 caches are coherent and the load reads from it,
+// so data passed between workgroups on different dies needs no cache-wide fence.
+__device__ __forceinline__ void store_device(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_device(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory access this wave has issued is complete (device-scope stores
+// have reached the coherent level); the compiler may move no memory access across it.
+__device__ __forceinline__ void wait_stores_complete() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    NC_WAIT_VM_ALL();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 typedef __attribute__((address_space(1))) void gvoid;  // global memory, for direct-to-LDS loads
 typedef __attribute__((address_space(3))) void lvoid;  // LDS
 

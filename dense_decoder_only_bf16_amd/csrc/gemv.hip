@@ -64,13 +64,23 @@ __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, in
 // weights per wave for bf16) are in flight.  The weight operand of a step is one
 // contiguous 32x16 block of the blocked layout.  LO: compensated operand (A + A_lo), one
 // more MFMA per step against the same weight registers.
+// K slices: with gridDim.z = KS > 1, workgroup z covers the z-th of KS equal ranges of K
+// and stores its tile sum to `part`; the workgroup that finds itself the last of the tile
+// to arrive (a counter per tile in `done`, which it sets back to zero) adds the KS slices
+// in slice order and runs the epilogue.  Every other workgroup only stores and leaves,
+// so no workgroup ever waits on another.  The slice sums are stored and loaded with
+// device-scope accesses (written through to, and read from, the level where the dies'
+// caches are coherent), and each workgroup waits for its stores to complete before it
+// counts itself, so no cache-wide write-back or invalidation is needed; such fences
+// would flush the whole L2 of a die under the other workgroups' weight streams.
 template <typename T, int FM, int NW, int U, int EPI, bool LO>
 __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
     typedef typename Chunk<T>::type CT;
     constexpr int BM = 32 * FM, BN = 32, TP = BN + 1;
     __shared__ float red[NW * BM * TP];
+    __shared__ int last_in;
 
-    if (p.lens_inc && blockIdx.x == 0 && blockIdx.y == 0)
+    if (p.lens_inc && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
         for (int r = threadIdx.x; r < p.M; r += NW * 64) p.lens_inc[r] += 1;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -103,7 +113,9 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
         for (int i = 0; i < RPW; ++i)
             pre[i] = p.out_f32[(long long)(m0 + min(wave + NW * i, rows - 1)) * p.ldo + nn];
     }
-    const int s0 = ksteps * wave / NW, s1 = ksteps * (wave + 1) / NW;
+    const int KS = gridDim.z;
+    const int z0 = (int)((long long)ksteps * blockIdx.z / KS), z1 = (int)((long long)ksteps * (blockIdx.z + 1) / KS);
+    const int s0 = z0 + (z1 - z0) * wave / NW, s1 = z0 + (z1 - z0) * (wave + 1) / NW;
     const T* A = (const T*)p.A;
     const T* wb = (const T*)p.W + (long long)(n0 / 32) * ksteps * 512 + l32 * 16 + 8 * hh;
     // A is blocked like W: the operand of step s for row block i is 1 KB at
@@ -174,6 +186,32 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
         for (int w = 0; w < NW; ++w) sum += red[w * BM * TP + r * TP + c];
         red[r * TP + c] = sum;
     }
+    if (KS > 1) {
+        const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+        float* pt = p.part + (long long)tile * KS * BM * BN;  // [tile][slice][BM][BN]
+        for (int e = tid; e < rows * BN; e += NW * 64)
+            store_device(pt + blockIdx.z * BM * BN + e, red[(e / BN) * TP + e % BN]);
+        wait_stores_complete();  // this slice is visible device-wide before it is counted
+        __syncthreads();
+        if (tid == 0) {
+            const int before = __hip_atomic_fetch_add(p.done + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_in = before == KS - 1;
+            if (before == KS - 1) __hip_atomic_store(p.done + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!last_in) return;  // workgroup-uniform
+        for (int e = tid; e < rows * BN; e += NW * 64) {
+            float sum = 0.f;
+            for (int zb = 0; zb < KS; zb += 8) {  // 8 independent loads at a time
+                float t[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) t[u] = load_device(pt + min(zb + u, KS - 1) * BM * BN + e);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) sum += zb + u < KS ? t[u] : 0.f;
+            }
+            red[(e / BN) * TP + e % BN] = sum;
+        }
+    }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -186,20 +224,30 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
     }
 }
 
+// K slices of the one-row-block kernel: a product with long K and few column tiles (the
+// MLP down-projection: d_model columns, K = d_ff) is split so that each workgroup takes
+// 64 16-deep steps, 8 per wave, all of a wave's loads in flight at once (d12, 8 rows:
+// 8.0 us against 10.3 us for 16 waves with 12 steps each in one workgroup per tile; 32
+// or 16 steps per workgroup measured no faster).
+static int dec_ksplit(int M, int N, int K) {
+    if (M > 32 || K <= 1024 || N > 2048) return 1;
+    return (K / 16 + 63) / 64;
+}
+
 // Launch shape.  `variant` picks alternative (waves, steps-in-flight) choices for tuning.
 template <typename T, int EPI, bool LO>
 static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant) {
     const unsigned gx = (a.N + DEC_BN - 1) / DEC_BN;
     const int fm = a.M <= 32 ? 1 : (a.M <= 64 ? 2 : 4);
     const unsigned gy = (a.M + 32 * fm - 1) / (32 * fm);
-    dim3 g(gx, gy);
+    const int ks = dec_ksplit(a.M, a.N, a.K);
+    if (ks > 1 && (!a.part || !a.done)) return hipErrorInvalidValue;
+    dim3 g(gx, gy, ks);
 #define NC_DG(FMV, NWV, UV) NC_TLAUNCH((dec_gemm_kernel<T, FMV, NWV, UV, EPI, LO>), g, dim3(NWV * 64), 0, st, a)
-    // one row block and at most 8 steps per wave (K <= 1024): all of a wave's weight
-    // steps in flight at once (one memory round trip), except for the wide LM head
-    if (fm == 1 && variant == 0 && a.K <= 1024 && a.N <= 16384) variant = 2;
-    // one row block, long K and few column blocks (the MLP down-projection): 16 waves
-    // split K, halving each wave's chain of loads
-    if (fm == 1 && variant == 0 && a.K > 1024 && a.N <= 2048) variant = 1;
+    // one row block and at most 8 steps per wave (K <= 1024, or a K slice): all of a
+    // wave's weight steps in flight at once (one memory round trip), except for the wide
+    // LM head
+    if (fm == 1 && variant == 0 && (ks > 1 || a.K <= 1024) && a.N <= 16384) variant = 2;
     if (fm == 1) {
         if (variant == 1) NC_DG(1, 16, 4);
         else if (variant == 2) NC_DG(1, 8, 8);
@@ -449,7 +497,11 @@ static hipError_t wide_t(const DecGemmArgs& a, hipStream_t st) {
 }
 
 long long dec_gemm_part_elems(DType dt, Epi epi, int M, int N, int K) {
-    if (dt != BF16 || M <= 32) return 0;
+    if (M <= 32) {
+        const int ks = dec_ksplit(M, N, K);
+        return ks > 1 ? (long long)ks * ((N + DEC_BN - 1) / DEC_BN) * 32 * DEC_BN : 0;
+    }
+    if (dt != BF16) return 0;
     const bool lo = epi != EPI_STORE;  // compensated operands: MLP products and LM head
     const WideShape w = std::max(wide_shape(epi, M, lo, N, K), wide_shape(epi, M, false, N, K),
                                  [](const WideShape& x, const WideShape& y) { return x.splits < y.splits; });

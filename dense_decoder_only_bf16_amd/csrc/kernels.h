@@ -104,7 +104,7 @@ hipError_t launch_gemm(DType dt, Epi epi, const GemmArgs& a, hipStream_t st);
 // ss_out[tile_n * ss_stride + m] (parts = ceil(N / tile_n)).
 // Decode activations (A, A_lo and the dtype outputs out_t, out_lo) are stored blocked with
 // rows rounded up to 32 (blocked_index); the fp32 outputs are row-major with stride ldo.
-struct DecGemmArgs {  // pointers first, then 4-byte fields: no padding (120 bytes)
+struct DecGemmArgs {  // pointers first, then 4-byte fields: no padding (128 bytes)
     const void* A;              // blocked [ceil(M/32)][K/16][32][16] dtype
     const void* W;              // blocked weight, Npad = N rounded up to 32 rows
     float* out_f32; void* out_t;
@@ -113,7 +113,8 @@ struct DecGemmArgs {  // pointers first, then 4-byte fields: no padding (120 byt
     int32_t* lens_inc;  // if set, workgroup 0 adds one to lens_inc[0..M) (end of a decode step)
     const void* A_lo;   // compensated operand, as in GemmArgs (bf16 only; null: plain A)
     void* out_lo;       // RELU2 / RESID low-part output, as in GemmArgs (null: not written)
-    float* part;        // bf16 with M > 32: fp32 split-K partials, dec_gemm_part_elems(M, N, K)
+    float* part;        // fp32 split-K partials, dec_gemm_part_elems(M, N, K) elements
+    int32_t* done;      // split-K arrival counters, one per output tile, zero between launches
     const ResidExtra* rx;  // RESID: as in GemmArgs, in device memory (null: plain residual)
     int M, N, K, ldo;
     int ss_in_parts, ss_stride;

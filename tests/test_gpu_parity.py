@@ -353,6 +353,52 @@ def test_fp32_gqa_prefill_decode_and_cache():
     gm.close()
 
 
+# MLP width 2880: decode's down-projection (K = 2880, 180 16-deep steps) is split over 3
+# workgroups per column tile, 60 steps each (7 or 8 per wave)
+TINY_WIDE_MLP = replace(TINY, name="tiny-mlp2880", d_ff=2880)
+SMALL_WIDE_MLP = replace(SMALL_BF16, name="small-mlp2880", d_ff=2880)
+
+
+def test_fp32_split_k_decode():
+    """Decode with the down-projection split over workgroups (the last of a tile to finish
+    adds the slices), 8 teacher-forced steps at the fp32 bar; the slice counters return to
+    zero, so every step (graph replays included) sees the same result as the oracle."""
+    shape = TINY_WIDE_MLP
+    w = make_weights(shape, seed=44)
+    orc = OracleModel(shape, w)
+    gm = gpu_model(shape, w)
+    B, T, steps = 2, 20, 8
+    toks = make_tokens(shape.vocab, B, T + steps, seed=45)
+    want, _ = orc.prefill(toks)
+    kv, got = prefill(gm, toks[:, :T], shape.max_seq)
+    err, _ = report("tiny-mlp2880 prefill", got, want[:, :T])
+    assert err <= F32_TOL
+    got = np.stack([decode(gm, kv, toks[:, T + s]) for s in range(steps)], axis=1)
+    err, _ = report("tiny-mlp2880 decode", got, want[:, T:T + steps])
+    assert err <= F32_TOL
+    kv.close()
+    gm.close()
+
+
+@pytest.mark.parametrize("B", [1, 32])
+def test_bf16_split_k_decode(B):
+    """The split down-projection in bf16 at 1 row and at a full 32-row block, 3 steps."""
+    shape = SMALL_WIDE_MLP
+    w = make_weights(shape, seed=46)
+    orc = OracleModel(shape, w)
+    gm = gpu_model(shape, w)
+    T, steps = 33, 3
+    toks = make_tokens(shape.vocab, B, T + steps, seed=47)
+    want, _ = orc.prefill(toks, logits_at=np.arange(T, T + steps))
+    kv, _ = prefill(gm, toks[:, :T], shape.max_seq)
+    got = np.stack([decode(gm, kv, toks[:, T + s]) for s in range(steps)], axis=1)
+    err, agr = report(f"small-mlp2880 decode B={B}", got, want)
+    assert err <= BF16_TOL
+    assert_flips_are_near_ties(got, want, err)
+    kv.close()
+    gm.close()
+
+
 @pytest.mark.parametrize("B", [3, 40])
 def test_bf16_gqa_decode_many_rows(B):
     """Grouped-query decode at mixed context lengths up to 600 (B = 40: 80 (row, K/V head)
