@@ -66,7 +66,7 @@ __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, in
 // more MFMA per step against the same weight registers.
 // K slices: with gridDim.z = KS > 1, workgroup z covers the z-th of KS equal ranges of K
 // and stores its tile sum to `part`; the workgroup that finds itself the last of the tile
-// to arrive (a counter per tile in `done`, which it sets back to zero) adds the KS slices
+// to arrive (a counter per tile at the head of `part`, which it sets back to zero) adds the KS slices
 // in slice order and runs the epilogue.  Every other workgroup only stores and leaves,
 // so no workgroup ever waits on another.  The slice sums are stored and loaded with
 // device-scope accesses (written through to, and read from, the level where the dies'
@@ -187,16 +187,17 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
         red[r * TP + c] = sum;
     }
     if (KS > 1) {
-        const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-        float* pt = p.part + (long long)tile * KS * BM * BN;  // [tile][slice][BM][BN]
+        const int tile = blockIdx.y * gridDim.x + blockIdx.x;  // < DEC_PART_CTRS (host check)
+        int32_t* done = (int32_t*)p.part;
+        float* pt = p.part + DEC_PART_CTRS + (long long)tile * KS * BM * BN;  // [tile][slice][BM][BN]
         for (int e = tid; e < rows * BN; e += NW * 64)
             store_device(pt + blockIdx.z * BM * BN + e, red[(e / BN) * TP + e % BN]);
         wait_stores_complete();  // this slice is visible device-wide before it is counted
         __syncthreads();
         if (tid == 0) {
-            const int before = __hip_atomic_fetch_add(p.done + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int before = __hip_atomic_fetch_add(done + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             last_in = before == KS - 1;
-            if (before == KS - 1) __hip_atomic_store(p.done + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (before == KS - 1) __hip_atomic_store(done + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
         if (!last_in) return;  // workgroup-uniform
@@ -241,7 +242,7 @@ static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant) {
     const int fm = a.M <= 32 ? 1 : (a.M <= 64 ? 2 : 4);
     const unsigned gy = (a.M + 32 * fm - 1) / (32 * fm);
     const int ks = dec_ksplit(a.M, a.N, a.K);
-    if (ks > 1 && (!a.part || !a.done)) return hipErrorInvalidValue;
+    if (ks > 1 && (!a.part || (int)(gx * gy) > DEC_PART_CTRS)) return hipErrorInvalidValue;
     dim3 g(gx, gy, ks);
 #define NC_DG(FMV, NWV, UV) NC_TLAUNCH((dec_gemm_kernel<T, FMV, NWV, UV, EPI, LO>), g, dim3(NWV * 64), 0, st, a)
     // one row block and at most 8 steps per wave (K <= 1024, or a K slice): all of a
@@ -485,9 +486,11 @@ __global__ __launch_bounds__(256) void dec_reduce_kernel(DecGemmArgs p, int spli
 }
 
 template <int EPI, bool LO>
-static hipError_t wide_t(const DecGemmArgs& a, hipStream_t st) {
-    const WideShape w = wide_shape((Epi)EPI, a.M, LO, a.N, a.K);
-    if (w.splits > 1 && !a.part) return hipErrorInvalidValue;
+static hipError_t wide_t(const DecGemmArgs& args, hipStream_t st) {
+    const WideShape w = wide_shape((Epi)EPI, args.M, LO, args.N, args.K);
+    if (w.splits > 1 && !args.part) return hipErrorInvalidValue;
+    DecGemmArgs a = args;
+    if (a.part) a.part += DEC_PART_CTRS;  // the partials follow the counters
     dim3 g(w.tiles, w.splits);
     if (a.M <= 64) NC_TLAUNCH((dec_gemm_wide_kernel<2, LO, EPI>), g, dim3(256), 0, st, a, w.splits, w.per);
     else NC_TLAUNCH((dec_gemm_wide_kernel<4, LO, EPI>), g, dim3(256), 0, st, a, w.splits, w.per);
@@ -499,13 +502,13 @@ static hipError_t wide_t(const DecGemmArgs& a, hipStream_t st) {
 long long dec_gemm_part_elems(DType dt, Epi epi, int M, int N, int K) {
     if (M <= 32) {
         const int ks = dec_ksplit(M, N, K);
-        return ks > 1 ? (long long)ks * ((N + DEC_BN - 1) / DEC_BN) * 32 * DEC_BN : 0;
+        return ks > 1 ? DEC_PART_CTRS + (long long)ks * ((N + DEC_BN - 1) / DEC_BN) * 32 * DEC_BN : 0;
     }
     if (dt != BF16) return 0;
     const bool lo = epi != EPI_STORE;  // compensated operands: MLP products and LM head
     const WideShape w = std::max(wide_shape(epi, M, lo, N, K), wide_shape(epi, M, false, N, K),
                                  [](const WideShape& x, const WideShape& y) { return x.splits < y.splits; });
-    return w.splits > 1 ? (long long)w.splits * M * N : 0;
+    return w.splits > 1 ? DEC_PART_CTRS + (long long)w.splits * M * N : 0;
 }
 
 int dec_gemm_tile_n() { return DEC_BN; }

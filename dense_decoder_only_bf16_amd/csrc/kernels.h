@@ -104,7 +104,7 @@ hipError_t launch_gemm(DType dt, Epi epi, const GemmArgs& a, hipStream_t st);
 // ss_out[tile_n * ss_stride + m] (parts = ceil(N / tile_n)).
 // Decode activations (A, A_lo and the dtype outputs out_t, out_lo) are stored blocked with
 // rows rounded up to 32 (blocked_index); the fp32 outputs are row-major with stride ldo.
-struct DecGemmArgs {  // pointers first, then 4-byte fields: no padding (128 bytes)
+struct DecGemmArgs {  // pointers first, then 4-byte fields: no padding (120 bytes)
     const void* A;              // blocked [ceil(M/32)][K/16][32][16] dtype
     const void* W;              // blocked weight, Npad = N rounded up to 32 rows
     float* out_f32; void* out_t;
@@ -113,14 +113,17 @@ struct DecGemmArgs {  // pointers first, then 4-byte fields: no padding (128 byt
     int32_t* lens_inc;  // if set, workgroup 0 adds one to lens_inc[0..M) (end of a decode step)
     const void* A_lo;   // compensated operand, as in GemmArgs (bf16 only; null: plain A)
     void* out_lo;       // RELU2 / RESID low-part output, as in GemmArgs (null: not written)
-    float* part;        // fp32 split-K partials, dec_gemm_part_elems(M, N, K) elements
-    int32_t* done;      // split-K arrival counters, one per output tile, zero between launches
+    // split-K workspace, dec_gemm_part_elems(M, N, K) elements: DEC_PART_CTRS int32 arrival
+    // counters (zero before the first launch; every launch leaves them at zero), then the
+    // fp32 partial products
+    float* part;
     const ResidExtra* rx;  // RESID: as in GemmArgs, in device memory (null: plain residual)
     int M, N, K, ldo;
     int ss_in_parts, ss_stride;
     float eps, cap;
 };
 int dec_gemm_tile_n();
+constexpr int DEC_PART_CTRS = 64;
 // Elements of DecGemmArgs::part that a product of this shape needs (0: none).
 long long dec_gemm_part_elems(DType dt, Epi epi, int M, int N, int K);
 hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t st, int variant = 0);

@@ -132,7 +132,6 @@ struct nc_kv {
     void* u_lo = nullptr;     // products): x - bf16(x) after attention, u - bf16(u)
     float* apart = nullptr;   // decode attention partials
     float* dpart = nullptr;   // decode projections: split-K partials
-    int32_t* done = nullptr;  // decode split-K arrival counters (zero between launches)
     float* x0 = nullptr;      // later-version blocks: stream before layer 0's scaling [M][d]
     float* xb = nullptr;      // and the backout source [M][d]
     int32_t* tokbuf = nullptr;   // the rows' clamped tokens (value embeddings) [M]
@@ -166,14 +165,13 @@ void drop_graphs(nc_kv* kv) {
 void ws_free(nc_kv* kv) {
     drop_graphs(kv);  // captured graphs point into the workspace
     void* ptrs[] = {kv->x, kv->act, kv->ss_a, kv->ss_b, kv->qkv, kv->q, kv->y, kv->u, kv->apart,
-                    kv->act_lo, kv->u_lo, kv->dpart, kv->x0, kv->xb, kv->tokbuf, kv->rx_dev, kv->ve_dev,
-                    kv->done};
+                    kv->act_lo, kv->u_lo, kv->dpart, kv->x0, kv->xb, kv->tokbuf, kv->rx_dev, kv->ve_dev};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     kv->x = nullptr; kv->act = nullptr; kv->ss_a = nullptr; kv->ss_b = nullptr; kv->qkv = nullptr;
     kv->q = nullptr; kv->y = nullptr; kv->u = nullptr; kv->apart = nullptr;
     kv->act_lo = nullptr; kv->u_lo = nullptr; kv->dpart = nullptr; kv->x0 = nullptr; kv->xb = nullptr;
-    kv->tokbuf = nullptr; kv->rx_dev = nullptr; kv->ve_dev = nullptr; kv->done = nullptr;
+    kv->tokbuf = nullptr; kv->rx_dev = nullptr; kv->ve_dev = nullptr;
     kv->dpart_elems = 0;
     kv->cap_m = 0;
     kv->apart_elems = 0;
@@ -261,13 +259,12 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
                                 dec_gemm_part_elems(dt, EPI_RELU2, B, F, d),
                                 dec_gemm_part_elems(dt, EPI_RESID, B, d, F),
                                 dec_gemm_part_elems(dt, EPI_SOFTCAP, B, c.vocab, d)});
-        if (e > 0) WS_ALLOC(kv->dpart, e * 4);
+        if (e > 0) {
+            WS_ALLOC(kv->dpart, e * 4);
+            // the arrival counters at its head start at zero; every launch leaves them so
+            HIP_TRY(hipMemset(kv->dpart, 0, DEC_PART_CTRS * 4));
+        }
         kv->dpart_elems = e;
-        // one arrival counter per output tile of the widest product (the LM head), set to
-        // zero once here; every split-K launch leaves them at zero
-        const long long tiles = 4LL * ((std::max({nq, d, F, c.vocab}) + dec_gemm_tile_n() - 1) / dec_gemm_tile_n());
-        WS_ALLOC(kv->done, tiles * 4);
-        HIP_TRY(hipMemset(kv->done, 0, (size_t)tiles * 4));
     }
 #undef WS_ALLOC
     kv->cap_m = M;
@@ -434,7 +431,6 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         void* vtc = (char*)kv->vcache + l * per_layer;
         DecGemmArgs a{};
         a.M = B; a.eps = c.norm_eps; a.cap = c.softcap; a.ss_stride = ss; a.part = kv->dpart;
-        a.done = kv->done;
         // QKV raw product, then norm scale + RoPE + QK-norm + cache write at lens[b]
         a.A = kv->act; a.W = L.wqkv; a.N = nqkv; a.K = d;
         a.out_f32 = kv->qkv; a.ldo = nqkv;
@@ -481,7 +477,6 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
     }
     DecGemmArgs h{};
     h.M = B; h.eps = c.norm_eps; h.cap = c.softcap; h.ss_stride = ss; h.part = kv->dpart;
-    h.done = kv->done;
     h.A = kv->act; h.A_lo = kv->act_lo; h.W = m->lm; h.N = V; h.K = d;
     h.out_f32 = logits; h.ldo = V; h.ss_in = kv->ss_a; h.ss_in_parts = ss_a_parts;
     h.lens_inc = kv->lens_dev;  // the step's last kernel also advances every row by one
