@@ -197,12 +197,16 @@ void gemm_bf16_kernel(GemmArgs p) {
     }
 
     // Stage layout: 16 A blocks (row block rb = b/2, k block b%2) then 16 B blocks.  Wave w
-    // loads A blocks 2w, 2w+1 and B blocks 2w, 2w+1; lane l fills bytes [16 l, 16 l + 16)
-    // of a 1 KB block, i.e. row l/2, k half l%2.  A and B are both stored blocked, so each
-    // block is one contiguous 1 KB load (8 cache lines, fully used).  A holds ceil(M/32)
+    // loads A blocks 2w, 2w+1 and B blocks 2w, 2w+1.  A and B are both stored blocked, so
+    // each block is one contiguous 1 KB load (8 cache lines, fully used).  In LDS a block is
+    // held in MFMA lane order: bytes [16 l, 16 l + 16) are what lane l of an operand read
+    // takes, row l % 32, k half l / 32 (memory chunk 2 (l % 32) + l / 32), so each group of
+    // 8 lanes that LDS serves together reads 128 contiguous bytes from all 32 banks (the
+    // memory order would put two lanes of a group on the same banks).  A holds ceil(M/32)
     // whole 32-row blocks (rows past M are padding); a tile's row blocks past the last one
     // and weight blocks past Npad read a clamped block.  Their outputs are masked in the
     // epilogue.
+    const int lchunk = 2 * l32 + hh;  // the memory chunk this lane moves into LDS chunk `lane`
     auto issue = [&](int kt) {
         bf16* sbase = lds + (kt % NS) * STAGE;
         const int k0 = (comp ? kt >> 1 : kt) * BK;
@@ -213,7 +217,7 @@ void gemm_bf16_kernel(GemmArgs p) {
             const int rb = b / KB, kb = b % KB;
             int mb = m0 / 32 + rb;
             mb = mb < (p.M + 31) / 32 ? mb : (p.M + 31) / 32 - 1;  // tiles reach past the last block
-            const bf16* src = As + ((long long)mb * (p.K / 16) + (k0 / 16 + kb)) * 512 + lane * 8;
+            const bf16* src = As + ((long long)mb * (p.K / 16) + (k0 / 16 + kb)) * 512 + lchunk * 8;
             __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(sbase + b * 512), 16, 0, 0);
         }
 #pragma unroll
@@ -222,7 +226,7 @@ void gemm_bf16_kernel(GemmArgs p) {
             const int rb = b / KB, kb = b % KB;
             int nb = n0 / 32 + rb;
             nb = nb < p.Npad / 32 ? nb : p.Npad / 32 - 1;
-            const bf16* src = B + ((long long)nb * ksteps + k0 / 16 + kb) * 512 + lane * 8;
+            const bf16* src = B + ((long long)nb * ksteps + k0 / 16 + kb) * 512 + lchunk * 8;
             __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(sbase + (16 + b) * 512), 16, 0, 0);
         }
     };
@@ -240,11 +244,9 @@ void gemm_bf16_kernel(GemmArgs p) {
         const bf16* sa = lds + (kt % NS) * STAGE;
         const bf16* sb = sa + TBM * BK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            fa[i] = *(const bf16x8*)(sa + ((wm * 4 + i) * KB + s) * 512 + l32 * 16 + 8 * hh);
+        for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(sa + ((wm * 4 + i) * KB + s) * 512 + lane * 8);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            fb[j] = *(const bf16x8*)(sb + ((wn * 2 + j) * KB + s) * 512 + l32 * 16 + 8 * hh);
+        for (int j = 0; j < 2; ++j) fb[j] = *(const bf16x8*)(sb + ((wn * 2 + j) * KB + s) * 512 + lane * 8);
     };
     // 8 MFMAs of one step, with the 6 LDS reads of the next step interleaved (one read per
     // MFMA) so the reads' latency hides behind the matrix cores.
@@ -293,6 +295,142 @@ void gemm_bf16_kernel(GemmArgs p) {
             fload(kt + 1, 0, a0, b0);  // step 0 of tile kt+1
         }
         mfmas(a1, b1, more);
+    }
+    __syncthreads();  // every wave is done with the ring (all its loads have landed)
+    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
+        if (tid < TBM) {
+            float s = 0.f;
+#pragma unroll
+            for (int q = 0; q < MAXP; ++q) s += ssp[q];
+            rs[tid] = 1.0f / sqrtf(s / (float)p.K + p.eps);
+        }
+        __syncthreads();
+    }
+    tile_epilogue<bf16, EPI, 2, 4>(p, acc, m0, n0, tn, rs, red);
+}
+
+// Compensated products (A + A_lo against one weight: the MLP products and the LM head).  A
+// stage is one 16-deep step holding the tile's 8 A blocks, its 8 A_lo blocks and its 8
+// weight blocks (24 KB; wave w loads block w of each), so a weight block is brought into
+// LDS once for both MFMAs that use it: 24 KB of loads per 16 MFMAs of each wave, where
+// running A_lo as extra K tiles of the kernel above loads 32 KB (the weight twice).  The
+// loads into LDS, not the matrix cores, bound these products.  Six stages (144 KB), five
+// in flight; a stage's 8 hi MFMAs come before its 8 lo MFMAs, so the two updates of an
+// accumulator are 8 MFMAs apart, and the next stage's 10 fragment reads are interleaved
+// with them.
+template <int EPI>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_bf16_comp_kernel(GemmArgs p) {
+    constexpr int NS = 6, BPS = 24;   // stages, 1 KB blocks per stage
+    constexpr int STAGE = BPS * 512;  // elements per stage
+    __shared__ __attribute__((aligned(1024))) bf16 lds[NS * STAGE];
+    float* rs = (float*)lds;
+    float (*red)[TBM] = (float (*)[TBM])((float*)lds + TBM);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / 4, wn = wave % 4;  // 2 x 4 waves, 128 x 64 each
+    const int l32 = lane & 31, hh = lane >> 5;
+    int m0, n0, tn;
+    tile_coords(p, m0, n0, tn);
+    const int nk = p.K / 16;  // stages
+
+    constexpr int MAXP = 16;
+    float ssp[MAXP];
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) ssp[q] = 0.f;
+    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
+        const int m = min(m0 + (tid & (TBM - 1)), p.M - 1);
+#pragma unroll
+        for (int q = 0; q < MAXP; ++q)
+            if (q < p.ss_in_parts) ssp[q] = p.ss_in[(long long)q * p.ss_stride + m];
+    }
+
+    // Wave w moves row block w of A and A_lo and weight block w; lane l takes memory chunk
+    // 2 (l % 32) + l / 32 of a block into LDS chunk l (MFMA lane order, as above).  Row
+    // blocks past A's last and weight blocks past Npad read a clamped block; their outputs
+    // are masked in the epilogue.
+    const int lchunk = 2 * l32 + hh;
+    const int mb = min(m0 / 32 + wave, (p.M + 31) / 32 - 1);
+    const int nb = min(n0 / 32 + wave, p.Npad / 32 - 1);
+    const bf16* srcA = (const bf16*)p.A + (long long)mb * nk * 512 + lchunk * 8;
+    const bf16* srcL = (const bf16*)p.A_lo + (long long)mb * nk * 512 + lchunk * 8;
+    const bf16* srcB = (const bf16*)p.B + (long long)nb * nk * 512 + lchunk * 8;
+    auto issue = [&](int kt) {
+        bf16* s = lds + (kt % NS) * STAGE;
+        __builtin_amdgcn_global_load_lds((gvoid*)(srcA + (long long)kt * 512), (lvoid*)(s + wave * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gvoid*)(srcL + (long long)kt * 512), (lvoid*)(s + (8 + wave) * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gvoid*)(srcB + (long long)kt * 512), (lvoid*)(s + (16 + wave) * 512), 16, 0, 0);
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = zero_vec<f32x16>();
+
+    typedef bf16x8 Frag[10];  // A blocks 0..3, A_lo blocks 4..7, weight blocks 8..9
+    auto fload = [&](int kt, Frag& f) {
+        const bf16* s = lds + (kt % NS) * STAGE + lane * 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(s + (wm * 4 + i) * 512);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[4 + i] = *(const bf16x8*)(s + (8 + wm * 4 + i) * 512);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) f[8 + j] = *(const bf16x8*)(s + (16 + wn * 2 + j) * 512);
+    };
+    auto mfmas = [&](Frag& f, bool interleave) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mma32(f[i], f[8 + j], acc[i][j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mma32(f[4 + i], f[8 + j], acc[i][j]);
+        if (interleave) {
+#pragma unroll
+            for (int g = 0; g < 10; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+        }
+    };
+    // One stage: wait until this wave's loads of stage kt + 1 have landed (later stages,
+    // at most 3, may stay in flight), barrier (every wave's loads of kt + 1 are in LDS and
+    // every wave is done with stage kt - 1, whose slot the next issue refills), refill, then
+    // the MFMAs of stage kt with the fragment reads of stage kt + 1.
+    auto step = [&](int kt, Frag& cur, Frag& nxt) {
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const int ahead = min(NS - 3, nk - 2 - kt);
+            if (ahead >= 3) NC_WAIT_VM(9);
+            else if (ahead == 2) NC_WAIT_VM(6);
+            else if (ahead == 1) NC_WAIT_VM(3);
+            else NC_WAIT_VM(0);
+            __builtin_amdgcn_s_barrier();
+            if (kt + NS - 1 < nk) issue(kt + NS - 1);
+            fload(kt + 1, nxt);
+        }
+        mfmas(cur, more);
+    };
+
+    // Prologue: stages 0 .. NS-2 in flight (3 loads per wave each), stage 0's fragments.
+#pragma unroll
+    for (int kt = 0; kt < NS - 1; ++kt)
+        if (kt < nk) issue(kt);
+    if (nk > 4) NC_WAIT_VM(12);
+    else if (nk > 3) NC_WAIT_VM(9);
+    else if (nk > 2) NC_WAIT_VM(6);
+    else if (nk > 1) NC_WAIT_VM(3);
+    else NC_WAIT_VM(0);
+    __builtin_amdgcn_s_barrier();
+    Frag f0, f1;
+    fload(0, f0);
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, f0, f1);
+        if (kt + 1 < nk) step(kt + 1, f1, f0);
     }
     __syncthreads();  // every wave is done with the ring (all its loads have landed)
     if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
@@ -405,6 +543,12 @@ static hipError_t launch_e(DType dt, const GemmArgs& a, hipStream_t st) {
     dim3 grid(((a.N + TBN - 1) / TBN) * ((a.M + TBM - 1) / TBM), 1, a.k_split);
     if (dt == BF16) {
         if (a.k_split != 1 || a.K % 32) return hipErrorInvalidValue;
+        if constexpr (EPI != EPI_STORE) {
+            if (a.A_lo) {
+                NC_TLAUNCH((gemm_bf16_comp_kernel<EPI>), grid, dim3(512), 0, st, a);
+                return hipGetLastError();
+            }
+        }
         NC_TLAUNCH((gemm_bf16_kernel<EPI>), grid, dim3(512), 0, st, a);
     } else {
         if (a.A_lo || a.out_lo) return hipErrorInvalidValue;  // fp32 operands need no compensation
