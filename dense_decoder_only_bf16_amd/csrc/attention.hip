@@ -130,10 +130,15 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
             int c = tid + i * NT, key = c / CPRK, ch = c % CPRK;
             *(CT*)(&Ks[key * HD + ((ch ^ (key & 7)) * 8)]) = rk[i];
         }
+        // V^T row d (KB keys) in 4-key units: unit u sits at unit position u ^ (d % 16), so
+        // the 16 rows that one LDS cycle of 4-key reads serves (consecutive d, the same u)
+        // land on 16 different bank pairs; an 8-key chunk (two units) is written whole, its
+        // units swapped for odd d.
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             int c = tid + i * NT, d = c / (KB / 8), ch = c % (KB / 8);
-            *(CT*)(&Vs[d * KB + ((ch ^ (d & 7)) * 8)]) = rv[i];
+            const CT sv = __builtin_shufflevector(rv[i], rv[i], 4, 5, 6, 7, 0, 1, 2, 3);
+            *(CT*)(&Vs[d * KB + ((ch ^ ((d >> 1) & 7)) * 8)]) = (d & 1) ? sv : rv[i];
         }
         __syncthreads();
 
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
             for (int md = 0; md < MD; ++md) {
                 const int d = md * 32 + l32;
                 const int u1 = 4 * t + hh, u2 = 4 * t + 2 + hh;  // 4-key units of this lane
-                const int sw = 2 * (d & 7);
+                const int sw = d & 15;
                 HT lo = *(const HT*)(&Vs[d * KB + ((u1 ^ sw) * 4)]);
                 HT hi = *(const HT*)(&Vs[d * KB + ((u2 ^ sw) * 4)]);
                 CT vf;
