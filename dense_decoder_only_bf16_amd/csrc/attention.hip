@@ -48,8 +48,11 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
     constexpr int KSTEPS = HD / 16;   // 16-deep steps over the head dim
     constexpr int MD = HD / 32;       // 32-row tiles of O^T
 
-    __shared__ __attribute__((aligned(32))) T Ks[KB * HD];
-    __shared__ __attribute__((aligned(32))) T Vs[HD * KB];
+    // bf16: two buffers of a K block and a V^T block, filled by direct-to-LDS loads; fp32:
+    // one buffer, filled through registers.  Both take 8 KB HD bytes.
+    constexpr bool DIRECT = sizeof(T) == 2;
+    constexpr int BUF_T = 2 * KB * HD;  // elements of one buffer (K block, then V^T block)
+    __shared__ __attribute__((aligned(1024))) T smem[DIRECT ? 2 * BUF_T : BUF_T];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -97,7 +100,36 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
     constexpr int VCH = HD * (KB / 8) / NT;
     static_assert(KCH >= 1 && VCH >= 1, "block too small for the workgroup");
 
-    // K/V block k0 into registers (zeros past Kn), then into LDS.
+    // LDS layouts (16-byte chunks): K row `key` holds chunk ch at chunk position
+    // ch ^ (key % 8); V^T row d (KB keys) holds chunk ch at position ch ^ (d % 8), so that
+    // the operand reads below are spread over the banks.
+    // bf16: block kbi goes straight into buffer `bufi` with 1 KB direct-to-LDS loads; lane l
+    // of a load writes chunk position l of its 1 KB and so fetches the chunk that the
+    // swizzle puts there.  Rows past Kn are loaded as they are (the cache holds finite
+    // values everywhere): their scores are masked, so they weigh 0.
+    constexpr int NWV = 8 / JN;                    // waves
+    constexpr int KJ = KB * CPRK / 64 / NWV;       // 1 KB K loads per wave
+    constexpr int VJ = HD * (KB / 8) / 64 / NWV;   // 1 KB V^T loads per wave
+    auto issue = [&](int kbi, int bufi) {
+        const int k0 = kbi * KB;
+        T* kl = smem + bufi * BUF_T;
+        T* vl = kl + KB * HD;
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) {
+            const int p = (wave * KJ + j) * 64 + lane;
+            const int key = p / CPRK, ch = (p % CPRK) ^ (key & 7);
+            __builtin_amdgcn_global_load_lds((gvoid*)(kb_base + (long long)(k0 + key) * HD + ch * 8),
+                                             (lvoid*)(kl + (wave * KJ + j) * 512), 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) {
+            const int p = (wave * VJ + j) * 64 + lane;
+            const int d = p / (KB / 8), ch = (p % (KB / 8)) ^ (d & 7);
+            __builtin_amdgcn_global_load_lds((gvoid*)(vb_base + (long long)d * S + k0 + ch * 8),
+                                             (lvoid*)(vl + (wave * VJ + j) * 512), 16, 0, 0);
+        }
+    };
+    // fp32: K/V block k0 into registers (zeros past Kn), then into LDS.
     CT rk[KCH], rv[VCH];
     auto gload = [&](int k0) {
 #pragma unroll
@@ -121,26 +153,37 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
             }
         }
     };
+    // bf16: block kbi + 1 streams into the other buffer while block kbi is worked on, with
+    // one barrier per block.
+    if (DIRECT && kb_first < nkb) issue(kb_first, 0);
     for (int kbi = kb_first; kbi < nkb; ++kbi) {
         const int k0 = kbi * KB;
-        gload(k0);
-        __syncthreads();  // previous block's LDS reads are complete
+        const T* Ks;
+        const T* Vs;
+        if constexpr (DIRECT) {
+            const int bufi = (kbi - kb_first) & 1;
+            NC_WAIT_VM_ALL();  // this wave's loads of block kbi have landed
+            __syncthreads();   // every wave's have, and every wave is done with the other buffer
+            if (kbi + 1 < nkb) issue(kbi + 1, bufi ^ 1);
+            Ks = smem + bufi * BUF_T;
+            Vs = Ks + KB * HD;
+        } else {
+            gload(k0);
+            __syncthreads();  // previous block's LDS reads are complete
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            int c = tid + i * NT, key = c / CPRK, ch = c % CPRK;
-            *(CT*)(&Ks[key * HD + ((ch ^ (key & 7)) * 8)]) = rk[i];
-        }
-        // V^T row d (KB keys) in 4-key units: unit u sits at unit position u ^ (d % 16), so
-        // the 16 rows that one LDS cycle of 4-key reads serves (consecutive d, the same u)
-        // land on 16 different bank pairs; an 8-key chunk (two units) is written whole, its
-        // units swapped for odd d.
+            for (int i = 0; i < KCH; ++i) {
+                int c = tid + i * NT, key = c / CPRK, ch = c % CPRK;
+                *(CT*)(&smem[key * HD + ((ch ^ (key & 7)) * 8)]) = rk[i];
+            }
 #pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            int c = tid + i * NT, d = c / (KB / 8), ch = c % (KB / 8);
-            const CT sv = __builtin_shufflevector(rv[i], rv[i], 4, 5, 6, 7, 0, 1, 2, 3);
-            *(CT*)(&Vs[d * KB + ((ch ^ ((d >> 1) & 7)) * 8)]) = (d & 1) ? sv : rv[i];
+            for (int i = 0; i < VCH; ++i) {
+                int c = tid + i * NT, d = c / (KB / 8), ch = c % (KB / 8);
+                *(CT*)(&smem[KB * HD + d * KB + ((ch ^ (d & 7)) * 8)]) = rv[i];
+            }
+            __syncthreads();
+            Ks = smem;
+            Vs = smem + KB * HD;
         }
-        __syncthreads();
 
         // every query of this wave precedes the block, or its window starts after it
         if (k0 > plast_w || k0 + KB - 1 < p0w - win) continue;
@@ -219,7 +262,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
             for (int md = 0; md < MD; ++md) {
                 const int d = md * 32 + l32;
                 const int u1 = 4 * t + hh, u2 = 4 * t + 2 + hh;  // 4-key units of this lane
-                const int sw = d & 15;
+                const int sw = 2 * (d & 7);
                 HT lo = *(const HT*)(&Vs[d * KB + ((u1 ^ sw) * 4)]);
                 HT hi = *(const HT*)(&Vs[d * KB + ((u2 ^ sw) * 4)]);
                 CT vf;
