@@ -74,16 +74,31 @@ template <typename V> __device__ __forceinline__ V zero_vec() {
     return v;
 }
 
-// Butterfly sum / max over the 64 lanes of a wave (every lane gets the result).
+// Sum / max over the 64 lanes of a wave, the same value in every lane (call with the whole
+// wave active).  Inside each 16-lane row, four DPP lane exchanges (quad xor 1, quad xor 2,
+// half-row mirror, row mirror) leave the row's result in all its lanes; these are VALU
+// operand modifiers, with none of the LDS round trips of a shuffle.  The four row results
+// are then read as scalars.
+template <int CTRL> __device__ __forceinline__ float dpp_lane(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float read_lane(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_lane<DPP_QUAD_XOR1>(v);
+    v += dpp_lane<DPP_QUAD_XOR2>(v);
+    v += dpp_lane<DPP_HALF_MIRROR>(v);
+    v += dpp_lane<DPP_MIRROR>(v);
+    return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_lane<DPP_QUAD_XOR1>(v));
+    v = fmaxf(v, dpp_lane<DPP_QUAD_XOR2>(v));
+    v = fmaxf(v, dpp_lane<DPP_HALF_MIRROR>(v));
+    v = fmaxf(v, dpp_lane<DPP_MIRROR>(v));
+    return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
 }
 
 // Wait for every outstanding vector-memory load of this wave (including direct-to-LDS
