@@ -86,11 +86,23 @@ __device__ __forceinline__ float read_lane(float v, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
-__device__ __forceinline__ float wave_sum(float v) {
+constexpr int DPP_ROW_BCAST15 = 0x142;
+// sum over the 16 lanes of each row, in every lane of the row
+__device__ __forceinline__ float row_sum(float v) {
     v += dpp_lane<DPP_QUAD_XOR1>(v);
     v += dpp_lane<DPP_QUAD_XOR2>(v);
     v += dpp_lane<DPP_HALF_MIRROR>(v);
-    v += dpp_lane<DPP_MIRROR>(v);
+    return v + dpp_lane<DPP_MIRROR>(v);
+}
+// sum over each 32-lane half, valid in lanes 16..31 (first half) and 48..63 (second half):
+// the row sums of rows 0 and 2 are broadcast from their lane 15 into rows 1 and 3
+__device__ __forceinline__ float half_sum_hi_rows(float v) {
+    v = row_sum(v);
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), DPP_ROW_BCAST15,
+                                                                     0xA, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row_sum(v);
     return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {

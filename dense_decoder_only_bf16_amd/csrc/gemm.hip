@@ -136,10 +136,9 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[2
                     }
                 }
             }
-            if (EPI == EPI_RESID) {
-#pragma unroll
-                for (int o = 16; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
-                if (l32 == 0) red[wn][rl] = sq;
+            if (EPI == EPI_RESID) {  // the row's sum over the wave's 32 columns: lanes 16, 48
+                sq = half_sum_hi_rows(sq);
+                if (l32 == 16) red[wn][rl] = sq;
             }
         }
     }
