@@ -230,9 +230,14 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][jn][r]);
             }
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run[jn], mx);
+            // Lazy rescaling: the reference max moves only when the block's max exceeds it by
+            // more than 8 in the base-2 exponent (or no key was visible yet), so p <= 2^8 and
+            // the state is rescaled (64 multiplies) only when some lane of the wave moved.
+            const float m_cand = fmaxf(m_run[jn], mx);
+            const bool move = m_run[jn] == -INFINITY || scale_log2 * (m_cand - m_run[jn]) > 8.f;
+            const float m_new = move ? m_cand : m_run[jn];
             const float cm = (m_new == -INFINITY) ? 0.f : scale_log2 * m_new;
-            const float alpha = fast_exp2(scale_log2 * m_run[jn] - cm);  // 0 on the first block
+            const float alpha = move ? fast_exp2(scale_log2 * m_run[jn] - cm) : 1.f;  // 0 on the first block
             float ls = 0.f;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
@@ -245,8 +250,10 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
             ls += __shfl_xor(ls, 32, 64);
             l_run[jn] = l_run[jn] * alpha + ls;
             m_run[jn] = m_new;
+            if (__any(move)) {  // wave-uniform
 #pragma unroll
-            for (int md = 0; md < MD; ++md) oacc[md][jn] *= alpha;
+                for (int md = 0; md < MD; ++md) oacc[md][jn] *= alpha;
+            }
         }
 
         // O^T += V^T P^T over the block's 64 keys in four 16-deep steps.
