@@ -225,6 +225,78 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
     }
 }
 
+// LM head of a decode step with at most 32 rows (softcap epilogue).  One wave per 32-column
+// tile over the whole K, 4 waves (4 independent tiles) per workgroup: the vocabulary's
+// tiles then run as one round of independent waves, each streaming its weight column
+// block with 2U steps of loads in flight, with no reduction across waves and no barrier.
+// (With 8 waves splitting K per tile, the head ran as four rounds of whole workgroups,
+// each round a full latency chain: d12, 8 rows, 1 ms more per 256 steps; U = 8 measured
+// the same as U = 4.)
+template <typename T, bool LO, int U>
+__global__ __launch_bounds__(256) void dec_head_kernel(DecGemmArgs p) {
+    typedef typename Chunk<T>::type CT;
+    __shared__ float rsc[4][32];  // each wave's copy of the rows' norm scales
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+    if (p.lens_inc && blockIdx.x == 0)
+        for (int r = threadIdx.x; r < p.M; r += 256) p.lens_inc[r] += 1;
+    const int n0 = (blockIdx.x * 4 + wave) * 32;
+    if (n0 >= p.N) return;  // wave-uniform; no barrier follows
+    const int ksteps = p.K / 16;
+
+    // norm scale of row `lane` (< M): its partial sums of squares, loads issued together
+    float s = 0.f;
+    if (lane < p.M)
+        for (int q = 0; q < p.ss_in_parts; ++q) s += p.ss_in[(long long)q * p.ss_stride + lane];
+    if (lane < 32) rsc[wave][lane] = 1.0f / sqrtf(s / (float)p.K + p.eps);
+
+    // A and W blocked; lanes of rows past M read row 0 of the block (its cache lines) and
+    // zero what they read
+    const bool mok = l32 < p.M;
+    const long long aoff = (long long)(mok ? l32 : 0) * 16 + 8 * hh;
+    const T* arow = (const T*)p.A + aoff;
+    const T* lrow = LO ? (const T*)p.A_lo + aoff : arow;
+    const T* wb = (const T*)p.W + (long long)(n0 / 32) * ksteps * 512 + l32 * 16 + 8 * hh;
+    constexpr int NA = LO ? 2 : 1;
+    f32x16 acc = zero_vec<f32x16>();
+    CT wf0[U], wf1[U], af0[U][NA], af1[U][NA];
+    auto load = [&](CT (&wf)[U], CT (&af)[U][NA], int sb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int st = sb + u;
+            const bool ok = st < ksteps;
+            const int sc = ok ? st : ksteps - 1;
+            wf[u] = load_masked(wb + (long long)sc * 512, ok);
+            af[u][0] = load_masked(arow + (long long)sc * 512, ok && mok);
+            if (LO) af[u][NA - 1] = load_masked(lrow + (long long)sc * 512, ok && mok);
+        }
+    };
+    auto mma = [&](CT (&wf)[U], CT (&af)[U][NA]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int h = 0; h < NA; ++h) acc = mma32(af[u][h], wf[u], acc);
+    };
+    load(wf0, af0, 0);
+    for (int sb = 0; sb < ksteps; sb += 2 * U) {
+        load(wf1, af1, sb + U);
+        mma(wf0, af0);
+        if (sb + U >= ksteps) break;
+        load(wf0, af0, sb + 2 * U);
+        mma(wf1, af1);
+    }
+
+    // lane holds column n0 + l32 of rows 8 (r / 4) + 4 hh + r % 4
+    const int n = n0 + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int m = 8 * (r / 4) + 4 * hh + (r % 4);
+        if (m < p.M && n < p.N)
+            p.out_f32[(long long)m * p.ldo + n] = p.cap * tanh_f32(acc[r] * rsc[wave][m] / p.cap);
+    }
+}
+
 // K slices of the one-row-block kernel: a product with long K and few column tiles (the
 // MLP down-projection: d_model columns, K = d_ff) is split so that each workgroup takes
 // 64 16-deep steps, 8 per wave, all of a wave's loads in flight at once (d12, 8 rows:
@@ -244,6 +316,10 @@ static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant) {
     const int ks = dec_ksplit(a.M, a.N, a.K);
     if (ks > 1 && (!a.part || (int)(gx * gy) > DEC_PART_CTRS)) return hipErrorInvalidValue;
     dim3 g(gx, gy, ks);
+    if (EPI == EPI_SOFTCAP && fm == 1 && variant == 0) {
+        NC_TLAUNCH((dec_head_kernel<T, LO, 4>), dim3((gx + 3) / 4), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
 #define NC_DG(FMV, NWV, UV) NC_TLAUNCH((dec_gemm_kernel<T, FMV, NWV, UV, EPI, LO>), g, dim3(NWV * 64), 0, st, a)
     // one row block and at most 8 steps per wave (K <= 1024, or a K slice): all of a
     // wave's weight steps in flight at once (one memory round trip), except for the wide
