@@ -247,10 +247,10 @@ def main():
                 kv_d.set_lens(ctx)
                 tok.copy_(first)
             for s in range(steps):
-                kv_d.decode(tok, dlog, stream)
-                if u_all is None:
-                    nc.nc_argmax(dlog, Bd, V, tok, stream)
+                if u_all is None:  # decode step and greedy pick in one graph
+                    kv_d.decode_greedy(tok, dlog, tok, stream)
                 else:
+                    kv_d.decode(tok, dlog, stream)
                     nc.nc_sample(dlog, Bd, V, wl.temperature, wl.top_k, u_all[s], tok, stream)
                 if per_decode_step:
                     per_decode_step()

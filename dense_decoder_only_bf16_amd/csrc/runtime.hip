@@ -146,6 +146,7 @@ struct nc_kv {
     struct Graph {
         const void* tokens;
         const void* logits;
+        const void* next;  // greedy picks written in the same graph (null: none)
         hipGraphExec_t exec;
     };
     std::vector<Graph> graphs;
@@ -962,8 +963,13 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
     }
 }
 
-nc_status nc_decode_step(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* kv, float* logits,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+// One decode step, with the greedy picks of its logits into `next` when next is not null,
+// eager or as a replay of the graph captured for (tokens, logits, next).
+nc_status decode_impl(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* kv, float* logits,
+                      int32_t* next, void* stream) {
     try {
         if (!m || !tokens || !kv || !logits) return fail(NC_ERR_INVALID_ARG, "NULL argument");
         if (kv->m != m) return fail(NC_ERR_INVALID_ARG, "kv belongs to another model");
@@ -974,19 +980,27 @@ nc_status nc_decode_step(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* k
         nc_status s = ws_ensure(kv, B);
         if (s != NC_OK) return s;
         hipStream_t st = (hipStream_t)stream;
+        auto enqueue = [&](hipStream_t q) {
+            nc_status r = enqueue_decode(m, kv, tokens, logits, q);
+            if (r == NC_OK && next) {
+                const hipError_t e = launch_argmax(logits, B, m->cfg.vocab, next, q);
+                if (e != hipSuccess) r = fail(NC_ERR_DEVICE, std::string("argmax: ") + hipGetErrorString(e));
+            }
+            return r;
+        };
         if (!kv->use_graph || g_tm.cls != NC_KC_NONE) {
-            s = enqueue_decode(m, kv, tokens, logits, st);
+            s = enqueue(st);
         } else {
             hipGraphExec_t exec = nullptr;
             for (const nc_kv::Graph& g : kv->graphs)
-                if (g.tokens == tokens && g.logits == logits) {
+                if (g.tokens == tokens && g.logits == logits && g.next == next) {
                     exec = g.exec;
                     break;
                 }
             if (!exec) {
                 if (!kv->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&kv->cap_stream, hipStreamNonBlocking));
                 HIP_TRY(hipStreamBeginCapture(kv->cap_stream, hipStreamCaptureModeThreadLocal));
-                s = enqueue_decode(m, kv, tokens, logits, kv->cap_stream);
+                s = enqueue(kv->cap_stream);
                 hipGraph_t graph = nullptr;
                 hipError_t e = hipStreamEndCapture(kv->cap_stream, &graph);
                 if (s != NC_OK || e != hipSuccess) {
@@ -1003,7 +1017,7 @@ nc_status nc_decode_step(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* k
                     drop_graph(kv->graphs.front());
                     kv->graphs.erase(kv->graphs.begin());
                 }
-                kv->graphs.push_back({tokens, logits, exec});
+                kv->graphs.push_back({tokens, logits, next, exec});
             }
             HIP_TRY(hipGraphLaunch(exec, st));
         }
@@ -1013,6 +1027,20 @@ nc_status nc_decode_step(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* k
     } catch (...) {
         return fail(NC_ERR_DEVICE, "unexpected exception");
     }
+}
+}  // namespace
+
+extern "C" {
+
+nc_status nc_decode_step(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* kv, float* logits,
+                         void* stream) {
+    return decode_impl(m, tokens, B, kv, logits, nullptr, stream);
+}
+
+nc_status nc_decode_greedy(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* kv, float* logits,
+                           int32_t* next, void* stream) {
+    if (!next) return fail(NC_ERR_INVALID_ARG, "next is NULL");
+    return decode_impl(m, tokens, B, kv, logits, next, stream);
 }
 
 nc_status nc_timing_enable(int32_t kernel_class) {

@@ -38,7 +38,8 @@ NC_KC_DECODE_ATTN = 4
 
 EXPORTED = ("nc_model_create", "nc_model_free", "nc_model_set_windows", "nc_model_set_extras",
             "nc_kv_create", "nc_kv_free", "nc_kv_set_lens",
-            "nc_kv_get_lens", "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step", "nc_argmax",
+            "nc_kv_get_lens", "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step",
+            "nc_decode_greedy", "nc_argmax",
             "nc_sample", "nc_timing_enable", "nc_timing_read", "nc_last_error", "nc_abi_version",
             "nc_diag_mfma_rate", "nc_diag_hbm_read_rate")
 
@@ -99,6 +100,7 @@ def lib():
         L.nc_kv_copy_rows.argtypes = [vp, ctypes.POINTER(i32), vp, ctypes.POINTER(i32), i32, vp]
         L.nc_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.nc_decode_step.argtypes = [vp, vp, i32, vp, vp, vp]
+        L.nc_decode_greedy.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.nc_argmax.argtypes = [vp, i32, i32, vp, vp]
         L.nc_sample.argtypes = [vp, i32, i32, ctypes.c_float, i32, vp, vp, vp]
         L.nc_timing_enable.argtypes = [i32]
@@ -110,7 +112,8 @@ def lib():
         L.nc_abi_version.argtypes = []
         L.nc_abi_version.restype = i32
         for name in ("nc_model_create", "nc_model_set_windows", "nc_model_set_extras", "nc_kv_create", "nc_kv_set_lens", "nc_kv_get_lens",
-                     "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step", "nc_argmax",
+                     "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step", "nc_decode_greedy",
+                     "nc_argmax",
                      "nc_sample", "nc_timing_enable", "nc_timing_read", "nc_diag_mfma_rate",
                      "nc_diag_hbm_read_rate"):
             getattr(L, name).restype = st
@@ -274,6 +277,10 @@ def nc_decode_step(m, tokens, B, kv, logits, stream=None):
     _check(lib().nc_decode_step(m, _ptr(tokens), B, kv, _ptr(logits), _stream(stream)))
 
 
+def nc_decode_greedy(m, tokens, B, kv, logits, next_tokens, stream=None):
+    _check(lib().nc_decode_greedy(m, _ptr(tokens), B, kv, _ptr(logits), _ptr(next_tokens), _stream(stream)))
+
+
 def nc_argmax(logits, B, V, out, stream=None):
     _check(lib().nc_argmax(_ptr(logits), B, V, _ptr(out), _stream(stream)))
 
@@ -348,6 +355,10 @@ class KV:
 
     def decode(self, tokens, logits, stream=None):
         nc_decode_step(self.model.handle, tokens, self.batch, self.handle, logits, stream)
+
+    def decode_greedy(self, tokens, logits, next_tokens, stream=None):
+        """decode + argmax of the logits into next_tokens (may be tokens), one graph."""
+        nc_decode_greedy(self.model.handle, tokens, self.batch, self.handle, logits, next_tokens, stream)
 
     def set_lens(self, lens):
         nc_kv_set_lens(self.handle, lens)

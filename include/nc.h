@@ -190,6 +190,15 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens_dev, int32_t B, int32_t 
 nc_status nc_decode_step(nc_model* m, const int32_t* tokens_dev, int32_t B, nc_kv* kv,
                          float* logits_dev, void* stream);
 
+/* Greedy decode step, the engine's generation loop with argmax picks (apidog.com/th guide,
+ * part 6): nc_decode_step followed by nc_argmax of its logits into next_dev (int32 [B]),
+ * both in one captured graph: one call per generated token.  next_dev may be
+ * tokens_dev itself (the step reads its tokens before it writes the picks).  Same
+ * requirements and errors as nc_decode_step; next_dev must not be NULL.  The graph is
+ * keyed by (tokens_dev, logits_dev, next_dev). */
+nc_status nc_decode_greedy(nc_model* m, const int32_t* tokens_dev, int32_t B, nc_kv* kv,
+                           float* logits_dev, int32_t* next_dev, void* stream);
+
 /* Greedy pick: out_dev[b] = argmax_v logits_dev[b, v] over fp32 [B, V]; ties go to the
  * lowest index; NaN compares below every number. */
 nc_status nc_argmax(const float* logits_dev, int32_t B, int32_t V, int32_t* out_dev,

@@ -107,6 +107,7 @@ def test_null_handles_are_rejected(L):
     assert L.nc_kv_create(None, 1, 8, ctypes.byref(out)) == nc.NC_ERR_INVALID_ARG
     assert L.nc_prefill(None, None, 1, 1, None, None, None) == nc.NC_ERR_INVALID_ARG
     assert L.nc_decode_step(None, None, 1, None, None, None) == nc.NC_ERR_INVALID_ARG
+    assert L.nc_decode_greedy(None, None, 1, None, None, None, None) == nc.NC_ERR_INVALID_ARG
     assert L.nc_argmax(None, 1, 1, None, None) == nc.NC_ERR_INVALID_ARG
     assert L.nc_kv_set_lens(None, None) == nc.NC_ERR_INVALID_ARG
     assert L.nc_kv_get_lens(None, None) == nc.NC_ERR_INVALID_ARG

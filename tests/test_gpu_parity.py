@@ -239,6 +239,39 @@ def test_decode_graph_replays_match_eager(small, monkeypatch):
     kv_e.close()
 
 
+@pytest.mark.parametrize("in_place", [True, False])
+def test_decode_greedy_matches_step_then_argmax(small, in_place):
+    """nc_decode_greedy (decode step and argmax in one graph) against nc_decode_step then
+    nc_argmax on a second cache: the same picks and bitwise the same logits over 12 greedy
+    steps (graph replays), the picks fed back; picks written in place or to another buffer."""
+    torch = torch_mod()
+    w, orc, gm = small
+    B = 4
+    toks = make_tokens(SMALL_BF16.vocab, B, 120, seed=17)
+    kv_a, _ = prefill(gm, toks, 160, logits=False)
+    kv_b, _ = prefill(gm, toks, 160, logits=False)
+    V = SMALL_BF16.vocab
+    start = torch.from_numpy(make_tokens(V, 1, B, seed=18)[0]).cuda()
+    tok_a, tok_b = start.clone(), start.clone()
+    nxt_a = tok_a if in_place else torch.empty_like(tok_a)
+    log_a = torch.empty((B, V), device="cuda", dtype=torch.float32)
+    log_b = torch.empty_like(log_a)
+    for s in range(12):
+        kv_a.decode_greedy(tok_a, log_a, nxt_a)
+        kv_b.decode(tok_b, log_b)
+        nc.nc_argmax(log_b, B, V, tok_b)
+        torch.cuda.synchronize()
+        assert torch.equal(log_a, log_b), s
+        assert torch.equal(nxt_a, tok_b), s
+        if not in_place:
+            tok_a.copy_(nxt_a)
+    assert np.array_equal(kv_a.lens(), [132] * B)
+    with pytest.raises(nc.NcError):
+        nc.nc_decode_greedy(gm.handle, tok_a, B, kv_a.handle, log_a, None)
+    kv_a.close()
+    kv_b.close()
+
+
 def test_kernel_timing_counts_launches(small):
     """Timing mode brackets every decode projection (4 per layer + LM head) and every
     prefill projection (4 per layer + LM head) with events and reports the algorithmic
