@@ -166,18 +166,19 @@ __device__ __forceinline__ float value_embed_gate(const T* __restrict__ gate, in
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // tanh from the identity tanh(y) = sign(y) (1 - e^(-2|y|)) / (1 + e^(-2|y|)), with the
-// exponential taken as 2^(-2|y| log2 e).  Relative error a few ulp away from 0; for
-// |y| < 2^-4 the odd Taylor series y - y^3/3 + 2y^5/15 is used instead, which avoids the
+// exponential taken as 2^(-2|y| log2 e) and the quotient through the hardware reciprocal
+// (1 ulp).  Relative error a few ulp away from 0; for |y| < 2^-4 the odd Taylor series
+// y - y^3/3 + 2y^5/15 is taken instead (a select, no branch), which avoids the
 // cancellation in 1 - e^(-2|y|).
 __device__ __forceinline__ float tanh_f32(float y) {
-    float a = fabsf(y);
-    float r;
-    if (a < 0.0625f) {
-        float y2 = y * y;
-        r = y * (1.0f + y2 * (-1.0f / 3.0f + y2 * (2.0f / 15.0f)));
-    } else {
-        float e = fast_exp2(-2.8853900817779268f * a);  // e^(-2a)
-        r = copysignf((1.0f - e) / (1.0f + e), y);
-    }
-    return r;
+    const float a = fabsf(y);
+    const float y2 = y * y;
+    const float series = y * (1.0f + y2 * (-1.0f / 3.0f + y2 * (2.0f / 15.0f)));
+    const float e = fast_exp2(-2.8853900817779268f * a);  // e^(-2a)
+    const float q = copysignf((1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), y);
+    return a < 0.0625f ? series : q;
+}
+// The logit softcap cap tanh(x / cap), with inv_cap = 1 / cap computed once by the caller.
+__device__ __forceinline__ float softcap_f32(float x, float cap, float inv_cap) {
+    return cap * tanh_f32(x * inv_cap);
 }

@@ -83,6 +83,7 @@ template <typename T, int EPI, int WM, int WN>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[256 / WM / 32][256 / WN / 32],
                                               int m0, int n0, int tn, const float* rs, float (*red)[TBM]) {
     constexpr int IM = 256 / WM / 32, JN = 256 / WN / 32, NT = 64 * WM * WN;
+    const float inv_cap = 1.0f / p.cap;  // SOFTCAP
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -123,7 +124,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[2
                     if (ok) ((T*)p.out_t)[ot] = hi;
                     if (ok && p.out_lo) ((T*)p.out_lo)[ot] = from_f32<T>(t * t - to_f32(hi));
                 } else if (EPI == EPI_SOFTCAP) {
-                    if (ok) p.out_f32[o] = p.cap * tanh_f32(v * rs[rl] / p.cap);
+                    if (ok) p.out_f32[o] = softcap_f32(v * rs[rl], p.cap, inv_cap);
                 } else {  // EPI_RESID
                     if (ok) {
                         const float xn = resid_value(p.rx, o, xold[jr][j], v);

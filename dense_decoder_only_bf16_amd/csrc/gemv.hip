@@ -42,7 +42,7 @@ __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, in
         if (ok) ((T*)p.out_t)[ob] = hi;
         if (ok && p.out_lo) ((T*)p.out_lo)[ob] = from_f32<T>(t * t - to_f32(hi));
     } else if (EPI == EPI_SOFTCAP) {
-        if (ok) p.out_f32[o] = p.cap * tanh_f32(v * r / p.cap);
+        if (ok) p.out_f32[o] = softcap_f32(v * r, p.cap, 1.0f / p.cap);
     } else {  // EPI_RESID
         float xn = 0.f;
         if (ok) {
@@ -289,11 +289,12 @@ __global__ __launch_bounds__(256) void dec_head_kernel(DecGemmArgs p) {
 
     // lane holds column n0 + l32 of rows 8 (r / 4) + 4 hh + r % 4
     const int n = n0 + l32;
+    const float inv_cap = 1.0f / p.cap;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int m = 8 * (r / 4) + 4 * hh + (r % 4);
         if (m < p.M && n < p.N)
-            p.out_f32[(long long)m * p.ldo + n] = p.cap * tanh_f32(acc[r] * rsc[wave][m] / p.cap);
+            p.out_f32[(long long)m * p.ldo + n] = softcap_f32(acc[r] * rsc[wave][m], p.cap, inv_cap);
     }
 }
 
@@ -500,12 +501,13 @@ __global__ __launch_bounds__(256) void dec_gemm_wide_kernel(DecGemmArgs p, int s
                 if (m < p.M && nok) dst[(long long)m * p.N + n] = acc[i][r];
             }
     } else {  // whole K: logits = cap tanh(r_m c / cap)
+        const float inv_cap = 1.0f / p.cap;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = 32 * i + 8 * (r / 4) + 4 * hh + (r % 4);
-                if (m < p.M && nok) p.out_f32[(long long)m * p.ldo + n] = p.cap * tanh_f32(acc[i][r] * rs[m] / p.cap);
+                if (m < p.M && nok) p.out_f32[(long long)m * p.ldo + n] = softcap_f32(acc[i][r] * rs[m], p.cap, inv_cap);
             }
     }
 }
