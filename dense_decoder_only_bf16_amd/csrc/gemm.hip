@@ -22,13 +22,15 @@
 // exactly one wave's 16-deep operand, so every LDS operand read is 1 KB contiguous.
 // Weights arrive in that blocked form from global memory (see kernels.h).
 //
-// Two main loops:
+// Three main loops:
 //  * bf16 (the model's dtype): global -> LDS with the gfx950 direct-to-LDS load
 //    (global_load_lds_dwordx4), a ring of 5 LDS stages of 32 K-columns (all 160 KB), loads
 //    issued four stages ahead; no staging registers and no LDS store instructions.  The operand
 //    fragments of the next 16-deep step (also across a K-tile boundary) are read from LDS
 //    while the MFMAs of the current step run (fragments double-buffered in registers,
 //    reads interleaved one per MFMA).
+//  * bf16 with a compensated operand (gemm_bf16_comp_kernel): 6 stages of one 16-deep step
+//    holding A, A_lo and the weight block, so each weight block is loaded once.
 //  * fp32 (the small fp32 check model): loads staged through registers into two LDS
 //    buffers (A kept row-major with an XOR swizzle).
 // Workgroups are dealt round-robin to the 8 dies (XCDs), each with its own L2; tiles are

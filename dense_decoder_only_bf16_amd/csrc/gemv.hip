@@ -5,9 +5,10 @@
 // built to stream W.  A workgroup owns 32 output columns and all M rows; its waves split K,
 // and each wave loads its W and A operands straight from memory into registers (no LDS
 // staging): the weights are stored MFMA-blocked, so one 16-deep step's W operand is a
-// contiguous 1 KB block, and loads run two groups of steps ahead of the MFMAs.  The eight partial tiles are summed in LDS in a fixed order
-// (deterministic, and no communication between workgroups, whose L2 caches are not
-// coherent with each other), then each wave finishes whole rows:
+// contiguous 1 KB block, and loads run two groups of steps ahead of the MFMAs.  The waves'
+// partial tiles are summed in LDS in a fixed order (deterministic; a product with long K
+// and few column tiles also splits K over workgroups, see dec_gemm_kernel), then each
+// wave finishes whole rows:
 //   STORE   raw fp32 product                              (QKV; finished by qkv_post)
 //   RELU2   relu(r_m c)^2 -> dtype                        (MLP up-projection)
 //   RESID   x += c, dtype copy of x, per-row sum of x^2 over the 32 columns

@@ -15,9 +15,10 @@
 // the elementwise epilogues fused and the QKV finish inside the attention kernel; the LM
 // head's launch also advances the row lengths.  The whole decode step is
 // captured once per (token buffer, logit buffer) pair as a HIP graph and replayed.
-// No kernel communicates with other workgroups of the same launch: the L2 caches of the
-// chip's dies are not coherent with each other, so a device-wide fence costs a write-back
-// and invalidation of the L2; reductions across workgroups are separate launches instead.
+// The L2 caches of the chip's dies are not coherent with each other, so a device-wide
+// fence costs a write-back and invalidation of a die's L2.  Reductions across workgroups
+// are separate launches, except the decode down-projection's K slices, which pass through
+// device-scope stores and loads and an arrival counter, with no fence and no waiting.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
