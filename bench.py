@@ -108,7 +108,7 @@ KERNEL_NAMES = {"decode_gemm": "dec_gemm_kernel (decode projections)",
 TRAFFIC = {
     ("d12", "decode_gemm"): {"bytes_per_launch": 5.602e6, "profile": "profiles/d12_pmc_traffic.md",
                              "sources": ("csrc/gemv.hip", "csrc/common.h", "csrc/kernels.h"),
-                             "sha": "9c7a1c2907787d23"},
+                             "sha": "cbc11e4fb6d22557"},
 }
 
 
