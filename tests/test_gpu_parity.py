@@ -386,6 +386,38 @@ def test_fp32_gqa_prefill_decode_and_cache():
     gm.close()
 
 
+# The narrowest model the library takes: d_model 64 (one 64-wide head), so the QKV, FC and
+# LM-head products have K = 64, four 16-deep steps: the prefill GEMMs' short pipeline
+# paths (prologue and drain with fewer stages than the ring holds).
+NARROW = Shape("narrow", n_layer=2, d_model=64, n_head=1, head_dim=64, d_ff=256, vocab=300,
+               dtype="bf16", max_seq=140)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_narrow_model_prefill_and_decode(dtype):
+    """K = 64 products end to end: ragged prefill of 3 rows (T = 70), then 4 teacher-forced
+    decode steps, against the oracle at the bar of the dtype."""
+    shape = replace(NARROW, name=f"narrow-{dtype}", dtype=dtype)
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    w = make_weights(shape, seed=50)
+    orc = OracleModel(shape, w)
+    gm = gpu_model(shape, w)
+    B, T, steps = 3, 70, 4
+    toks = make_tokens(shape.vocab, B, T + steps, seed=51)
+    want, _ = orc.prefill(toks)
+    kv, got = prefill(gm, toks[:, :T], shape.max_seq)
+    err, agr = report(f"{shape.name} prefill", got, want[:, :T])
+    assert err <= tol
+    if dtype == "bf16":
+        assert agr >= AGREE
+    got = np.stack([decode(gm, kv, toks[:, T + s]) for s in range(steps)], axis=1)
+    err, _ = report(f"{shape.name} decode", got, want[:, T:T + steps])
+    assert err <= tol
+    assert_flips_are_near_ties(got, want[:, T:T + steps], err)
+    kv.close()
+    gm.close()
+
+
 # MLP width 2880: decode's down-projection (K = 2880, 180 16-deep steps) is split over 3
 # workgroups per column tile, 60 steps each (7 or 8 per wave)
 TINY_WIDE_MLP = replace(TINY, name="tiny-mlp2880", d_ff=2880)
