@@ -1,23 +1,24 @@
 """Benchmark of the nanochat GPT forward on one MI355X through libnc.so.
 
 One step = the whole hot path over one batch: prefill of B x T prompt tokens with fp32
-logits at every position, then greedy decode steps (argmax fed back).  Default workload:
-the d12 bf16 model (12 layers, d=768, 6x128 heads, one K/V head, MLP 3072, vocab 65536),
-prefill 8 x 2048 then 256 decode steps of the same 8 rows, seeded N(0, 0.02) weights and
-uniform random token ids.  Other workloads (d20: prefill 32 x 2048 and 128 decode steps of
-64 rows at context 2048; d26: prefill 16 x 2048; d30: 256 decode steps of 128 rows at
-context lengths uniform in [256, 2048]; tiny) build a separate decode context outside the
-timed steps.  Prints one JSON line.
+logits at every position, then greedy decode steps (argmax fed back).  Default line: the d20
+bf16 model (20 layers, d=1280, 10x128 query heads, one K/V head, MLP 5120, vocab 65536),
+prefill 32 x 2048 (the pages' 32 rows of 2048 tokens per GPU) and 128 decode steps of 64
+rows at context 2048, seeded N(0, 0.02) weights and uniform random token ids.  Beside it, on
+the same JSON line, the two stress runs of the other configs, each graded against its own
+roof: "d26" (prefill 16 x 2048, the prefill products against the bf16 MFMA peak) and "d30"
+(256 decode steps of 128 rows at context lengths uniform in [256, 2048], the decode
+attention graded alone against HBM bandwidth).  Decode contexts that differ from the
+prefill batch are built outside the timed steps.
 
-Workloads d20-gqa (5 K/V heads) and d20-sssl (an SSSL pattern of 512-key sliding
-windows) run the d20 step with the later version's attention options, d20-blocks with its
-learned blocks (value embeddings, residual lambdas, smear, backout); d12-sample runs
-the d12 step with sampled decode picks (temperature 1, top-50; the uniforms are drawn
-before the timed region).
+Other workloads run alone with --workload (d12: prefill 8 x 2048 then 256 decode steps of
+the same rows; d26; d30; tiny; d20-gqa with 5 K/V heads; d20-sssl with an SSSL pattern of
+512-key sliding windows; d20-blocks with the later version's learned blocks; d12-sample
+with sampled decode picks, temperature 1 and top-50, uniforms drawn before timing).
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload d12|d20|d26|d30|d20-gqa|d20-sssl|d20-blocks|d12-sample|tiny]
-                    [--no-cpu]
+                    [--workload d20|d12|d26|d30|d20-gqa|d20-sssl|d20-blocks|d12-sample|tiny]
+                    [--no-extra] [--no-cpu] [--no-roofline]
 """
 
 from __future__ import annotations
@@ -36,7 +37,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--workload", default="d12")
+    p.add_argument("--workload", default="d20")
+    p.add_argument("--no-extra", action="store_true",
+                   help="default line only: skip the d26 prefill and d30 decode runs beside it")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--decode-steps", type=int, default=None,
@@ -54,11 +57,16 @@ def cpu_baseline(shape, weights, wl, budget_s, windows=None, extras=None):
     time budget is spent.  The per-phase rates are combined with the workload's own mix of
     prefill and decode tokens into one tokens/s figure."""
     from oracle import OracleModel
+    cores = len(os.sched_getaffinity(0))  # host cores this process may run on
+    blas = {"vendor": "unknown", "threads": None}
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = {"vendor": f"{info[0].get('internal_api')} {info[0].get('version')}",
+                    "threads": int(info[0].get("num_threads", 1))}
     except Exception:  # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
+        pass
     from dense_decoder_only_bf16_amd.inputs import make_tokens
     orc = OracleModel(shape, weights, windows=windows, extras=extras)
     t_pre = min(wl.prefill_len or wl.decode_context, 2048)  # decode-only: its context
@@ -78,7 +86,8 @@ def cpu_baseline(shape, weights, wl, budget_s, windows=None, extras=None):
     n_pre = wl.prefill_batch * wl.prefill_len
     n_dec = wl.decode_batch * wl.decode_steps
     value = (n_pre + n_dec) / (n_pre / pre_rate + (n_dec / dec_rate if n_dec else 0.0))
-    return {"value": round(value, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(value, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "blas": blas,
             "sample": (f"fp64 numpy oracle, 1 row: prefill {t_pre} tokens ({t1 - t0:.1f} s, "
                        f"{pre_rate:.1f} tok/s) + {steps} greedy decode steps at context "
                        f"{t_pre} ({t3 - t2:.1f} s, {dec_rate:.2f} tok/s); combined with the "
@@ -125,15 +134,18 @@ def measured_traffic(workload, name):
     return t["bytes_per_launch"] if h.hexdigest()[:16] == t["sha"] else None
 
 
-def roofline(nc, one_step, dtype, workload):
+def roofline(nc, one_step, dtype, workload, classes=None, grade=None):
     """Kernel timing pass: one more full step per kernel class with the library's timing
     mode on (every kernel of the class launched with dispatch-stamped start/stop events on
     its stream; decode launches eager instead of graph replays).  Reports, per class, the
-    launches, the average kernel time per launch and the algorithmic GB/s and TFLOP/s; the
-    roofline object is the class with the largest total kernel time."""
+    launches, the average kernel time per launch and the algorithmic GB/s and TFLOP/s.  The
+    roofline object is the class `grade` names, or else the class with the largest total
+    kernel time."""
     import torch
     res = {}
     for cname, name, bound in CLASSES:
+        if classes is not None and name not in classes:
+            continue
         nc.nc_timing_enable(getattr(nc, cname))
         one_step(per_decode_step=nc.nc_timing_read)
         torch.cuda.synchronize()
@@ -147,15 +159,22 @@ def roofline(nc, one_step, dtype, workload):
                      "bytes_per_launch": byts / launches, "flops_per_launch": flops / launches,
                      "bound": bound}
     nc.nc_timing_enable(nc.NC_KC_NONE)
-    dom = max(res, key=lambda k: res[k]["ms_total"])
+    for r in res.values():  # every class against its own roof
+        if r["bound"] == "hbm":
+            r["frac"] = round(r["GB_per_s"] / HBM_PEAK_GBS, 4)
+        else:
+            peak = MFMA_BF16_PEAK_TFS if dtype == "bf16" else FP32_VEC_PEAK_TFS
+            r["frac"] = round(r["TFLOP_per_s"] / peak, 4)
+    dom = grade if grade in res else max(res, key=lambda k: res[k]["ms_total"])
     r = res[dom]
     if r["bound"] == "hbm":
         ach, peak, unit = r["GB_per_s"], HBM_PEAK_GBS, "GB/s"
     else:
         ach, unit = r["TFLOP_per_s"], "TFLOP/s"
         peak = MFMA_BF16_PEAK_TFS if dtype == "bf16" else FP32_VEC_PEAK_TFS
-    roof = {"kernel": KERNEL_NAMES[dom], "bound": r["bound"], "achieved": ach, "peak": peak,
-            "unit": unit, "frac": round(ach / peak, 4), "traffic": measured_traffic(workload, dom),
+    roof = {"kernel": KERNEL_NAMES[dom], "class": dom, "bound": r["bound"], "achieved": ach,
+            "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+            "traffic": measured_traffic(workload, dom),
             "bytes_per_launch": r["bytes_per_launch"],
             "avg_launch_us": r["avg_us"], "launches": r["launches"]}
     return roof, res
@@ -174,35 +193,37 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes": n * 4}), flush=True)
 
 
-def main():
-    args = parse()
-    if args.copy_mib:
-        copy_calibration(args.copy_mib)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(batch rows are independent, so more GPUs would each run their own rows).",
-              file=sys.stderr)
-        sys.exit(2)
+def progress(msg):
+    """A progress line on stderr (stdout carries only the JSON result)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def run_workload(name, args, cpu=True, roof_classes=None, grade=None):
+    """Time one workload: warmup steps, then exactly args.steps steps bracketed by device
+    synchronisation; then the kernel-timing pass and, if asked, the oracle on the host.
+    Returns the report dict of this workload (its value = its tokens per second)."""
     import torch
 
     from dense_decoder_only_bf16_amd import nc
     from dense_decoder_only_bf16_amd.inputs import (WORKLOADS, canonical_list, make_extras,
                                                     make_lens, make_tokens, make_weights)
 
-    wl = WORKLOADS[args.workload]
+    wl = WORKLOADS[name]
     shape = wl.shape
     Bp, T = wl.prefill_batch, wl.prefill_len
     Bd, steps = wl.decode_batch, wl.decode_steps
     if args.decode_steps is not None and steps:
         steps = args.decode_steps
     shared = Bp > 0 and Bd == Bp  # decode continues the prefilled rows
+    progress(f"{name}: drawing weights")
     weights = make_weights(shape, seed=0)
     windows = (nc.layer_windows(wl.window_pattern, shape.n_layer, wl.short_window)
                if wl.window_pattern else None)
     extras = make_extras(shape, seed=wl.extras_seed) if wl.extras_seed >= 0 else None
     model = nc.Model(shape, canonical_list(weights), max_seq=shape.max_seq, windows=windows,
                      extras=extras)
+    if not cpu:
+        del weights
     stream = torch.cuda.current_stream()
     V = shape.vocab
 
@@ -211,7 +232,7 @@ def main():
         kv_p = model.new_kv(Bp, T + (steps if shared else 0))
         tokens = torch.from_numpy(make_tokens(V, Bp, T, seed=1)).cuda()
         logits = torch.empty((Bp, T, V), device="cuda", dtype=torch.float32)
-    kv_d = dlog = tok = ctx = None
+    kv_d = dlog = tok = ctx = first = None
     if steps:
         dlog = torch.empty((Bd, V), device="cuda", dtype=torch.float32)
         tok = torch.zeros(Bd, device="cuda", dtype=torch.int32)
@@ -257,9 +278,11 @@ def main():
         if ev:
             ev[2].record(stream)
 
+    progress(f"{name}: model on the GPU, {args.warmup} warmup steps")
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
+    progress(f"{name}: {args.steps} timed steps")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -277,7 +300,7 @@ def main():
     if extras is not None:
         win += (f", value embeddings on layers {sorted(extras['ve'])}, residual lambdas, smear, "
                 f"backout at layer {extras['backout_layer']}")
-    desc = (f"{args.workload} ({shape.n_layer} layers, d {shape.d_model}, {shape.n_head}x"
+    desc = (f"{name} ({shape.n_layer} layers, d {shape.d_model}, {shape.n_head}x"
             f"{shape.head_dim} query heads, {kvh}, MLP {shape.d_ff}, vocab {V}, "
             f"{shape.dtype}{win}):")
     if Bp:
@@ -289,17 +312,10 @@ def main():
         pick = (f"sampled (temperature {wl.temperature}, top-{wl.top_k})" if wl.temperature > 0
                 else "greedy")
         desc += (", then" if Bp else "") + f" {steps} {pick} decode steps of {Bd} rows from {ctxd}"
-    out = {
-        "metric": "prefill tokens/s + decode tokens/s (1 GPU); % MFMA peak / % HBM BW",
-        "value": round((n_pre + n_dec) / (ms_per_step / 1000.0), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": shape.dtype, "data": "synthetic",
-        "config": {"workload": desc, "prefill_batch": Bp, "prefill_len": T,
-                   "decode_batch": Bd, "decode_steps": steps},
-    }
+    out = {"value": round((n_pre + n_dec) / (ms_per_step / 1000.0), 1), "unit": "tokens/s",
+           "ms_per_step": round(ms_per_step, 3),
+           "config": {"workload": desc, "prefill_batch": Bp, "prefill_len": T,
+                      "decode_batch": Bd, "decode_steps": steps}}
     if Bp:
         out["prefill_ms"] = round(pre_ms, 3)
         out["prefill_tokens_per_s"] = round(n_pre / (pre_ms / 1000.0), 1)
@@ -307,7 +323,69 @@ def main():
         out["decode_ms"] = round(dec_ms, 3)
         out["decode_tokens_per_s"] = round(n_dec / (dec_ms / 1000.0), 1)
     if not args.no_roofline:
-        out["roofline"], out["kernels"] = roofline(nc, one_step, shape.dtype, args.workload)
+        progress(f"{name}: kernel-timing pass")
+        out["roofline"], out["kernels"] = roofline(nc, one_step, shape.dtype, name,
+                                                   roof_classes, grade)
+    if cpu and not args.no_cpu:
+        progress(f"{name}: oracle on the host cores")
+        out["cpu_baseline"] = cpu_baseline(shape, weights, wl, args.cpu_seconds, windows, extras)
+    for kv in {id(k): k for k in (kv_p, kv_d) if k is not None}.values():
+        kv.close()
+    model.close()
+    del logits, dlog, tokens
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+# Runs reported beside the default line: (workload, kernel classes timed, class graded).
+EXTRA = (("d26", ("prefill_gemm", "prefill_attn"), "prefill_gemm"),
+         ("d30", ("decode_attn", "decode_gemm"), "decode_attn"))
+
+
+def main():
+    args = parse()
+    if args.copy_mib:
+        copy_calibration(args.copy_mib)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(batch rows are independent, so more GPUs would each run their own rows).",
+              file=sys.stderr)
+        sys.exit(2)
+    from dense_decoder_only_bf16_amd.inputs import WORKLOADS
+    if args.workload not in WORKLOADS:
+        print(f"unknown workload {args.workload}; one of {sorted(WORKLOADS)}", file=sys.stderr)
+        sys.exit(2)
+    from dense_decoder_only_bf16_amd import nc
+
+    main_run = run_workload(args.workload, args)
+    out = {
+        "metric": "prefill tokens/s + decode tokens/s (1 GPU); % MFMA peak / % HBM BW",
+        "value": main_run.pop("value"),
+        "unit": main_run.pop("unit"),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": main_run.pop("ms_per_step"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": WORKLOADS[args.workload].shape.dtype, "data": "synthetic",
+        "config": main_run.pop("config"),
+    }
+    cpu = main_run.pop("cpu_baseline", None)
+    out.update(main_run)
+    if args.workload == "d20" and not args.no_extra:
+        for name, classes, grade in EXTRA:
+            r = run_workload(name, args, cpu=False, roof_classes=classes, grade=grade)
+            r["graded"] = grade
+            out[name] = r
+        # the two targets side by side: prefill products vs MFMA peak, decode attention vs HBM
+        targets = {}
+        for name, cls, need in (("d20", "prefill_gemm", 0.60), ("d26", "prefill_gemm", 0.60),
+                                ("d20", "decode_attn", 0.70), ("d30", "decode_attn", 0.70)):
+            k = (out if name == "d20" else out.get(name, {})).get("kernels", {}).get(cls)
+            if k:
+                targets[f"{name}_{cls}"] = {"frac": k["frac"], "target": need}
+        out["targets"] = targets
+    if not args.no_roofline:
         # what this GPU sustains with plain kernels, beside the published peaks
         rnd = nc.nc_diag_mfma_rate(True)
         const = nc.nc_diag_mfma_rate(False)
@@ -319,11 +397,8 @@ def main():
             "roofline_frac_of_sustained": round(
                 out["roofline"]["achieved"] / (rnd if out["roofline"]["unit"] == "TFLOP/s" else hbm * 1000.0), 4),
         }
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(shape, weights, wl, args.cpu_seconds, windows, extras)
-    for kv in {id(k): k for k in (kv_p, kv_d) if k is not None}.values():
-        kv.close()
-    model.close()
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -1015,6 +1015,13 @@ nc_status decode_impl(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* kv, 
                     return fail(NC_ERR_DEVICE, std::string("graph instantiate: ") + hipGetErrorString(e));
                 }
                 if (kv->graphs.size() >= 8) {  // keep a handful of buffer pairs
+                    // the oldest graph may still be queued or running on some stream:
+                    // let the device drain before its executable is destroyed
+                    e = hipDeviceSynchronize();
+                    if (e != hipSuccess) {
+                        (void)hipGraphExecDestroy(exec);
+                        return fail(NC_ERR_DEVICE, std::string("graph eviction: ") + hipGetErrorString(e));
+                    }
                     drop_graph(kv->graphs.front());
                     kv->graphs.erase(kv->graphs.begin());
                 }

@@ -135,6 +135,32 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _arg(t, dtype, elems, name):
+    """Device address of a tensor argument, after checking what the library cannot: a
+    torch tensor must be a contiguous CUDA tensor of `dtype` ("int32" or "float32") with at
+    least `elems` elements (NcError NC_ERR_INVALID_ARG otherwise).  None and raw integer
+    addresses pass through unchecked."""
+    if t is None or isinstance(t, int):
+        return t
+    want = {"int32": "torch.int32", "float32": "torch.float32"}[dtype]
+    if str(t.dtype) != want:
+        raise NcError(NC_ERR_INVALID_ARG, f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise NcError(NC_ERR_INVALID_ARG, f"{name} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise NcError(NC_ERR_INVALID_ARG, f"{name} must be contiguous")
+    if t.numel() < elems:
+        raise NcError(NC_ERR_INVALID_ARG, f"{name} holds {t.numel()} elements, {elems} needed")
+    return t.data_ptr()
+
+
+def _vocab(m):
+    return _MODEL_VOCAB.get(m.value if isinstance(m, ctypes.c_void_p) else m, 0)
+
+
+_MODEL_VOCAB = {}  # model handle -> vocab, for the logits size checks
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -166,10 +192,12 @@ def nc_model_create(cfg, weights):
     arr = (ctypes.c_void_p * len(weights))(*[_ptr(w) for w in weights])
     out = ctypes.c_void_p()
     _check(lib().nc_model_create(ctypes.byref(cfg), arr, ctypes.byref(out)))
+    _MODEL_VOCAB[out.value] = cfg.vocab
     return out
 
 
 def nc_model_free(m):
+    _MODEL_VOCAB.pop(m.value if isinstance(m, ctypes.c_void_p) else m, None)
     lib().nc_model_free(m)
 
 
@@ -270,24 +298,40 @@ def nc_kv_copy_rows(dst, dst_rows, src, src_rows, stream=None):
 
 
 def nc_prefill(m, tokens, B, T, kv, logits, stream=None):
-    _check(lib().nc_prefill(m, _ptr(tokens), B, T, kv, _ptr(logits), _stream(stream)))
+    """tokens int32 [B, T]; logits float32 [B, T, V] or None."""
+    n = max(B, 0) * max(T, 0)
+    _check(lib().nc_prefill(m, _arg(tokens, "int32", n, "tokens"), B, T, kv,
+                            _arg(logits, "float32", n * _vocab(m), "logits"), _stream(stream)))
 
 
 def nc_decode_step(m, tokens, B, kv, logits, stream=None):
-    _check(lib().nc_decode_step(m, _ptr(tokens), B, kv, _ptr(logits), _stream(stream)))
+    """tokens int32 [B]; logits float32 [B, V]."""
+    _check(lib().nc_decode_step(m, _arg(tokens, "int32", max(B, 0), "tokens"), B, kv,
+                                _arg(logits, "float32", max(B, 0) * _vocab(m), "logits"),
+                                _stream(stream)))
 
 
 def nc_decode_greedy(m, tokens, B, kv, logits, next_tokens, stream=None):
-    _check(lib().nc_decode_greedy(m, _ptr(tokens), B, kv, _ptr(logits), _ptr(next_tokens), _stream(stream)))
+    """tokens int32 [B]; logits float32 [B, V]; next_tokens int32 [B] (may be tokens)."""
+    _check(lib().nc_decode_greedy(m, _arg(tokens, "int32", max(B, 0), "tokens"), B, kv,
+                                  _arg(logits, "float32", max(B, 0) * _vocab(m), "logits"),
+                                  _arg(next_tokens, "int32", max(B, 0), "next_tokens"),
+                                  _stream(stream)))
 
 
 def nc_argmax(logits, B, V, out, stream=None):
-    _check(lib().nc_argmax(_ptr(logits), B, V, _ptr(out), _stream(stream)))
+    """logits float32 [B, V]; out int32 [B]."""
+    n = max(B, 0)
+    _check(lib().nc_argmax(_arg(logits, "float32", n * max(V, 0), "logits"), B, V,
+                           _arg(out, "int32", n, "out"), _stream(stream)))
 
 
 def nc_sample(logits, B, V, temperature, top_k, u, out, stream=None):
-    _check(lib().nc_sample(_ptr(logits), B, V, float(temperature), int(top_k), _ptr(u), _ptr(out),
-                           _stream(stream)))
+    """logits float32 [B, V]; u float32 [B] (or None for greedy); out int32 [B]."""
+    n = max(B, 0)
+    _check(lib().nc_sample(_arg(logits, "float32", n * max(V, 0), "logits"), B, V,
+                           float(temperature), int(top_k), _arg(u, "float32", n, "u"),
+                           _arg(out, "int32", n, "out"), _stream(stream)))
 
 
 def nc_timing_enable(kernel_class):
@@ -349,15 +393,27 @@ class KV:
         self.model, self.batch, self.max_seq = model, batch, max_seq
         self.handle = nc_kv_create(model.handle, batch, max_seq)
 
+    def _shape(self, t, shape, name):
+        if t is not None and tuple(t.shape) != tuple(shape):
+            raise NcError(NC_ERR_INVALID_ARG, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
     def prefill(self, tokens, logits, stream=None):
+        """tokens int32 [B, T]; logits float32 [B, T, V] or None (cache only)."""
         B, T = tokens.shape
+        self._shape(logits, (B, T, self.model.shape.vocab), "logits")
         nc_prefill(self.model.handle, tokens, B, T, self.handle, logits, stream)
 
     def decode(self, tokens, logits, stream=None):
+        """tokens int32 [B]; logits float32 [B, V]."""
+        self._shape(tokens, (self.batch,), "tokens")
+        self._shape(logits, (self.batch, self.model.shape.vocab), "logits")
         nc_decode_step(self.model.handle, tokens, self.batch, self.handle, logits, stream)
 
     def decode_greedy(self, tokens, logits, next_tokens, stream=None):
         """decode + argmax of the logits into next_tokens (may be tokens), one graph."""
+        self._shape(tokens, (self.batch,), "tokens")
+        self._shape(logits, (self.batch, self.model.shape.vocab), "logits")
+        self._shape(next_tokens, (self.batch,), "next_tokens")
         nc_decode_greedy(self.model.handle, tokens, self.batch, self.handle, logits, next_tokens, stream)
 
     def set_lens(self, lens):

@@ -137,7 +137,12 @@ typedef struct nc_extras {
 nc_status nc_model_set_extras(nc_model* m, const nc_extras* ex);
 
 /* KV cache for `batch` rows of up to `max_seq` positions (max_seq <= cfg.max_seq, and at
- * most 32768: NC_ERR_UNSUPPORTED otherwise).
+ * most 32768: NC_ERR_UNSUPPORTED otherwise).  The cache of the pages' inference engine:
+ * keys and values of every processed position kept per layer so that each new token
+ * attends to them without recomputation (szyisi.cn launch article, section on the base
+ * model's evaluation: an Engine class with a KV cache and the two inference stages,
+ * prefill and decode; apidog.com/th guide, part 6: the prompt's cache filled once, then
+ * read by flash_attn_with_kvcache).
  * Layout (library-private): K [L][batch][n_kv_head][max_seq][hd], V transposed
  * [L][batch][n_kv_head][hd][max_seq],
  * both cfg.dtype; keys are stored after RoPE and QK-norm.  All lengths start at 0. */
@@ -168,7 +173,12 @@ nc_status nc_kv_export(nc_kv* kv, int32_t layer, void* k_dev, void* v_dev, void*
 nc_status nc_kv_copy_rows(nc_kv* dst, const int32_t* dst_rows_host, nc_kv* src,
                           const int32_t* src_rows_host, int32_t n, void* stream);
 
-/* Prefill: tokens_dev int32 [B, T]; row b's tokens go to positions lens[b] .. lens[b]+T-1
+/* Prefill, the engine's first inference stage (szyisi.cn launch article, base-model
+ * evaluation section: prefill then decode over a KV cache; apidog.com/th guide, part 5: the
+ * causal attention call over a whole sequence, part 6: the prompt's cache filled once).
+ * Computes the forward pass above for T tokens per row in one batched pass and stores
+ * their keys and values.
+ * tokens_dev int32 [B, T]; row b's tokens go to positions lens[b] .. lens[b]+T-1
  * and attend to the row's cached positions as well (0..lens[b]-1): on an empty cache this
  * is the prompt prefill, on a filled one it appends a chunk (a long prompt in pieces, or
  * forced tokens in the middle of a generation), with the same results as a single prefill
@@ -180,7 +190,11 @@ nc_status nc_kv_copy_rows(nc_kv* dst, const int32_t* dst_rows_host, nc_kv* src,
 nc_status nc_prefill(nc_model* m, const int32_t* tokens_dev, int32_t B, int32_t T,
                      nc_kv* kv, float* logits_dev, void* stream);
 
-/* One decode step: row b takes token tokens_dev[b] at position lens[b] and attends to
+/* One decode step, the engine's second inference stage (szyisi.cn launch article,
+ * base-model evaluation section; apidog.com/th guide, part 6: one new token per row whose
+ * query attends to the cached keys and values, flash_attn_with_kvcache).  Computes the
+ * forward pass above for one token per row and appends its key and value to the cache.
+ * Row b takes token tokens_dev[b] at position lens[b] and attends to
  * cache positions 0..lens[b].  Requires B == batch of kv, B <= 128 (NC_ERR_UNSUPPORTED
  * otherwise) and lens[b] + 1 <= max_seq for every row (NC_ERR_CAPACITY otherwise).
  * logits_dev: fp32 [B, vocab] (not NULL).  On success every length grows by one.
@@ -199,8 +213,12 @@ nc_status nc_decode_step(nc_model* m, const int32_t* tokens_dev, int32_t B, nc_k
 nc_status nc_decode_greedy(nc_model* m, const int32_t* tokens_dev, int32_t B, nc_kv* kv,
                            float* logits_dev, int32_t* next_dev, void* stream);
 
-/* Greedy pick: out_dev[b] = argmax_v logits_dev[b, v] over fp32 [B, V]; ties go to the
- * lowest index; NaN compares below every number. */
+/* Greedy pick, the deterministic choice of the engine's generation loop (the pages show
+ * base-model completions of prompts, szyisi.cn launch article, base-model evaluation
+ * section, and give no sampling formula for them; the greedy reading takes the most
+ * likely token): out_dev[b] = argmax_v logits_dev[b, v] over fp32 [B, V] (row-major,
+ * caller-owned device memory; out_dev int32 [B]); ties go to the lowest index; NaN compares
+ * below every number.  NC_ERR_INVALID_ARG for NULL pointers or B, V < 1. */
 nc_status nc_argmax(const float* logits_dev, int32_t B, int32_t V, int32_t* out_dev,
                     void* stream);
 

@@ -151,7 +151,13 @@ def test_d26_prefill_16x2048():
     check("d26 prefill row 7 (first 768)", g, w[0])
 
 
-def test_d30_decode_mixed_lengths():
+@pytest.fixture(scope="module")
+def d30_decode():
+    """The d30 decode run: 128 rows prefilled to 2048, truncated to lengths uniform in
+    [256, 2048], then 3 teacher-forced steps in one launch shape.  Returns the oracle
+    model, the tokens, the lengths and the logits of the checked rows: the shortest, the
+    25th percentile and the two longest (contexts past 1024 keys, so their keys span several
+    chunks of the split decode attention while the short rows of the same launch end early)."""
     torch = torch_mod()
     r = Run(D30)
     B, T, steps = 128, 2048, 3
@@ -161,7 +167,8 @@ def test_d30_decode_mixed_lengths():
     kv.prefill(torch.from_numpy(np.ascontiguousarray(toks[:, :T])).cuda(), None)
     kv.set_lens(lens)
     dec = torch.empty((B, D30.vocab), device="cuda", dtype=torch.float32)
-    rows = [int(np.argmin(lens)), int(np.argsort(lens)[B // 4])]
+    order = np.argsort(lens, kind="stable")
+    rows = [int(order[0]), int(order[B // 4]), int(order[-2]), int(order[-1])]
     got = {b: [] for b in rows}
     for s in range(steps):
         kv.decode(torch.from_numpy(np.ascontiguousarray(toks[:, T + s])).cuda(), dec)
@@ -171,11 +178,27 @@ def test_d30_decode_mixed_lengths():
     assert np.array_equal(kv.lens(), lens + steps)
     kv.close()
     r.close()
-    for b in rows:
+    yield r.orc, toks, lens, rows, got
+
+
+def _check_d30_rows(d30_decode, which):
+    orc, toks, lens, rows, got = d30_decode
+    T, steps = 2048, len(next(iter(got.values())))
+    for b in [rows[i] for i in which]:
         n = int(lens[b])
         seq = np.concatenate([toks[b, :n], toks[b, T:T + steps]])[None]
-        want, _ = r.orc.prefill(seq, logits_at=np.arange(n, n + steps))
+        want, _ = orc.prefill(seq, logits_at=np.arange(n, n + steps))
         check(f"d30 decode row {b} (context {n})", np.stack(got[b]), want[0])
+
+
+def test_d30_decode_mixed_lengths(d30_decode):
+    _check_d30_rows(d30_decode, [0, 1])
+
+
+def test_d30_decode_longest_rows(d30_decode):
+    orc, toks, lens, rows, got = d30_decode
+    assert min(int(lens[rows[2]]), int(lens[rows[3]])) > 1024
+    _check_d30_rows(d30_decode, [2, 3])
 
 
 @pytest.mark.parametrize("name", ["d20-gqa", "d20-sssl", "d20-blocks"])

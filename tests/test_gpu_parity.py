@@ -186,9 +186,22 @@ def test_error_paths_on_gpu(small):
         kv.decode(t, out)
     assert e.value.code == nc.NC_ERR_CAPACITY
     assert np.array_equal(kv.lens(), [9, 9])  # unchanged by the failed call
+    t3 = torch.zeros(3, dtype=torch.int32, device="cuda")
+    out3 = torch.empty((3, SMALL_BF16.vocab), device="cuda", dtype=torch.float32)
+    with pytest.raises(nc.NcError) as e:  # the library's check: B differs from the cache's
+        nc.nc_decode_step(gm.handle, t3, 3, kv.handle, out3)
+    assert e.value.code == nc.NC_ERR_INVALID_ARG and "batch" in str(e.value)
+    # the binding's checks: buffers too small, wrong dtype, not contiguous, not on the GPU
+    bad = [(t, 3, out3), (t.long(), 2, out), (t, 2, out.double()), (t, 2, out.t()),
+           (t.cpu(), 2, out)]
+    for tt, bb, oo in bad:
+        with pytest.raises(nc.NcError) as e:
+            nc.nc_decode_step(gm.handle, tt, bb, kv.handle, oo)
+        assert e.value.code == nc.NC_ERR_INVALID_ARG
     with pytest.raises(nc.NcError) as e:
-        nc.nc_decode_step(gm.handle, t, 3, kv.handle, out)
+        kv.decode(t, out[:, :10].contiguous())
     assert e.value.code == nc.NC_ERR_INVALID_ARG
+    assert np.array_equal(kv.lens(), [9, 9])
     with pytest.raises(nc.NcError) as e:
         kv.set_lens([10, 1])  # grow
     assert e.value.code == nc.NC_ERR_INVALID_ARG
@@ -235,6 +248,31 @@ def test_decode_graph_replays_match_eager(small, monkeypatch):
         assert np.array_equal(got_g, got_e), s
         assert np.max(np.abs(got_g - want[:, 130 + s])) <= BF16_TOL
     assert np.array_equal(kv_g.lens(), [140, 140, 140])
+    kv_g.close()
+    kv_e.close()
+
+
+def test_decode_graph_eviction_without_host_syncs(small, monkeypatch):
+    """Eleven decode steps, each with its own (tokens, logits) buffer pair, enqueued back to
+    back with no host synchronisation: the cache of captured graphs (eight) evicts its oldest
+    while earlier replays may still be queued.  Every step's logits equal the eager ones."""
+    torch = torch_mod()
+    w, orc, gm = small
+    B, T, n = 3, 100, 11
+    toks = make_tokens(SMALL_BF16.vocab, B, T + n, seed=19)
+    kv_g, _ = prefill(gm, toks[:, :T], 128, logits=False)
+    monkeypatch.setenv("NC_DECODE_GRAPH", "0")
+    kv_e, _ = prefill(gm, toks[:, :T], 128, logits=False)
+    monkeypatch.delenv("NC_DECODE_GRAPH")
+    tok_bufs = [torch.from_numpy(np.ascontiguousarray(toks[:, T + s])).cuda() for s in range(n)]
+    outs = [torch.empty((B, SMALL_BF16.vocab), device="cuda", dtype=torch.float32) for _ in range(n)]
+    torch.cuda.synchronize()
+    for s in range(n):
+        kv_g.decode(tok_bufs[s], outs[s])
+    torch.cuda.synchronize()
+    for s in range(n):
+        assert np.array_equal(outs[s].cpu().numpy(), decode(gm, kv_e, toks[:, T + s])), s
+    assert np.array_equal(kv_g.lens(), [T + n] * B)
     kv_g.close()
     kv_e.close()
 
