@@ -106,7 +106,7 @@ CLASSES = (  # (timing class, name, bound); classes without a launch in the work
     ("NC_KC_PREFILL_ATTN", "prefill_attn", "mfma"),
 )
 KERNEL_NAMES = {"decode_gemm": "dec_gemm_kernel (decode projections)",
-                "decode_attn": "attn_decode_split_kernel + attn_decode_combine_kernel",
+                "decode_attn": "attn_decode_kernel (decode attention)",
                 "prefill_gemm": "gemm_bf16_kernel (prefill projections)",
                 "prefill_attn": "attn_prefill_kernel"}
 

@@ -326,448 +326,653 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 }
 
 // ------------------------------------------------------------------ decode ----------
-// Split kernel.  Workgroup (chunk c, unit u = (row b, K/V head kvh)), NW = 2 or 4 waves: the
-// keys [c CK, c CK + CK) of K/V head kvh of row b, CK = 64 NW R, limited to the visible
-// positions lo..lens[b] (lo = lens[b] - window with a window, else 0), against the
-// G = H / nkv query heads kvh G .. kvh G + G - 1 (G <= 16).  The grid's x index counts
-// chunks from the one holding lo, so only chunks with visible keys are launched work;
-// a wave's blocks wholly before lo are skipped.  Wave w takes the 64-key blocks
-// (c R + i) NW + w, i < R, one after another and keeps an online-softmax state (running
-// max, sum and o[16][hd]) across them; at the end the NW states are merged in LDS into the
-// chunk's partial state, slot c of row b (with R = 1 each wave's state is a partial of its
-// own, slot NW c + w, and the merge is left to the combine kernel).
-//  1. Finish the QKV product of row b for this step (the row's attention-norm scale,
-//     RoPE at position lens[b] and QK-norm of the group's query heads and of key head kvh;
-//     value head kvh as is) into LDS.  Every workgroup of the row does this (a few hundred values);
-//     the one whose chunk holds position lens[b] also writes the new key and value into the
-//     cache for later steps.
-//  2. All query heads of the row (padded to 16) form the 16 columns of 16x16 MFMA tiles,
-//     so each cached K/V element is read from memory once for the whole head group.
-//     bf16: a wave stages a block's K (64 x hd) and V^T (hd x 64) in its own LDS region
-//     with 1 KB direct-to-LDS loads, XOR-swizzled so that the MFMA operand reads are free
-//     of bank conflicts; once the block's operands are in registers, the next block's
-//     loads are issued and overlap this block's arithmetic.  fp32 (small check model):
-//     operands are loaded straight into registers.  Cached keys at or past lens[b] are
-//     masked in the scores; the new key (position lens[b]) is not read from the cache but
-//     added to the state of the wave whose block holds it, as one extra term from the
-//     values in LDS.
-constexpr int DEC_KPW = 64;
+// One query per row at position pos_b = lens[b] against the row's cached keys lo_b..pos_b
+// (lo_b = pos_b - window with a window, else 0) of each K/V head, all query heads of a K/V
+// head's group together, so each cached K/V element is read from memory once per step
+// (multi-query attention, yelogs.com launch write-up, architecture answer; decode against
+// the cache, apidog.com/th guide, part 6, flash_attn_with_kvcache).
+//
+// Work split.  A unit is (row b, K/V head g); unit u = b nkv + g covers the 64-key blocks
+// lo_b / 64 .. pos_b / 64 of its cache.  The blocks of all units, unit after unit, form one
+// sequence, cut into equal contiguous runs, one per workgroup, whatever the row lengths:
+// the launch stays balanced when the rows' lengths differ (d30's mixed lengths), and a
+// run that ends inside a unit leaves a partial softmax state (max m, sum l, o[hd] per
+// query head) for the workgroup that finishes the unit.  The cut is computed in the kernel
+// from the device lengths, so a captured step stays valid as the rows grow.
+//
+// Workgroup: 4 waves.  Its blocks stream through a ring of NS LDS stages (bf16: 64 keys of
+// K rows and of V^T rows, 1 KB direct-to-LDS loads, NS - 1 stages in flight); wave w takes
+// keys 16 w .. 16 w + 15 of every block: S^T = K Q^T by 16x16x32 MFMAs (keys = rows, the
+// group's <= 16 query heads = columns), online softmax in base 2 per head, then
+// O^T += V^T P^T by 16x16x16 MFMAs whose B operand is the score tile as it stands (each lane
+// already holds the 4 keys of its column).  fp32 (small check models) loads the same
+// fragments straight from memory.
+//
+// QKV finish.  While the first stages load, the workgroup finishes the raw QKV product for
+// the units of its run (row norm scale, RoPE at pos_b and QK-norm of the group's query heads;
+// for the unit whose last block it holds, also the new key and value, which it writes into
+// the cache).  The new key is not read back from the cache: the wave whose keys hold
+// position pos_b takes its K and V operands for that key from the finished values.
+//
+// End of a unit's run: the 4 waves' states merge in LDS; a unit inside one run is
+// normalised and stored to y; otherwise the state goes to the unit's partial slot and, at
+// the end of the run, the workgroup counts itself on the unit's arrival counter (device-
+// scope stores completed first, no cache-wide fence); the last to arrive merges the unit's
+// partials into y and resets the counter.  y is [B][H hd] stored blocked (blocked_index).
+constexpr int DEC_KB = 64;       // keys per block (one ring stage)
+constexpr int DEC_QSEG = 4;      // units whose finished q the prologue prepares
+constexpr int DEC_PER_MIN = 2;   // at least this many blocks per workgroup
+constexpr int DEC_MAX_WG = 256;  // workgroups per launch (one per CU)
+constexpr int DEC_MAX_B = 128;
+
 int attn_decode_span(int S, int window) { return (window < 0 || window >= S) ? S : window + 1; }
-// Waves per workgroup: 4, or 2 when the work is small (more, smaller workgroups then).
-// B here and below counts (row, K/V head) units; `span` bounds the keys a query sees.
-int attn_decode_waves(int B, int span) { return (long long)B * ((span + 255) / 256) >= 128 ? 4 : 2; }
-int attn_decode_iters(int B, int span) {
-    // The largest R in {1, 2, 4} that still leaves 128 workgroups or more: a wave's blocks
-    // run one after another at about one memory latency each, so longer chunks amortize
-    // the QKV finish and the merge until too few workgroups are left to fill the chip
-    // (measured at d12, d20 and d30 decode shapes).
-    const int nw = attn_decode_waves(B, span);
-    int r = 1;
-    while (r < 4 && (long long)B * ((span + nw * 64 * 2 * r - 1) / (nw * 64 * 2 * r)) >= 128) r *= 2;
-    return r;
+int attn_decode_workgroups(int units, int S) {
+    const long long most = (long long)units * (S / DEC_KB);  // every unit at full length
+    return (int)std::max(1LL, std::min((long long)DEC_MAX_WG, most / DEC_PER_MIN));
 }
-// Slots are indexed by absolute chunk, so a unit needs as many as the whole cache has.
-int attn_decode_slots(int B, int S, int span) {
-    const int nw = attn_decode_waves(B, span), r = attn_decode_iters(B, span);
-    const int ck = nw * DEC_KPW * r;
-    return (S + ck - 1) / ck * (r == 1 ? nw : 1);  // one block per wave: a slot per wave
+int attn_decode_slots(int units, int S) {
+    (void)units;
+    return std::min(DEC_MAX_WG, (S / DEC_KB + DEC_PER_MIN - 1) / DEC_PER_MIN + 2);
 }
 
-template <typename T, int HD, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecAttnArgs a) {
-    typedef typename Chunk<T>::type CT;
-    typedef typename Chunk<T>::half HT;
-    constexpr bool STAGE = sizeof(T) == 2;  // LDS staging for bf16
-    constexpr int DS = HD / 32;   // 32-deep steps over head dim for S^T
-    constexpr int DT = HD / 16;   // 16-row tiles of O^T
-    constexpr int PSZ = 16 * (HD + 2);
+__device__ __forceinline__ f32x4 mma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c, 0, 0, 0);
+}
+// O^T += V^T P^T over 4 keys: bf16 one 16x16x16 MFMA; fp32 four 16x16x4 MFMAs, key j of
+// every lane contracted in MFMA j (the same key assignment on both operands).
+__device__ __forceinline__ f32x4 pv_step(bf16x4 v, f32x4 p, f32x4 c) {
+    bf16x4 pb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pb[j] = (bf16)p[j];
+    return mma16x16x16(v, pb, c);
+}
+__device__ __forceinline__ f32x4 pv_step(f32x4 v, f32x4 p, f32x4 c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(v[j], p[j], c, 0, 0, 0);
+    return c;
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
+    typedef typename Chunk<T>::type CT;     // 8 elements
+    typedef typename Chunk<T>::half HT;     // 4 elements
+    constexpr bool STAGE = sizeof(T) == 2;  // LDS ring for bf16
+    constexpr int NS = STAGE ? (HD == 128 ? 3 : 5) : 1;
+    constexpr int NSW = 4;                                  // streaming waves; wave 4 does I/O
+    constexpr int KBYTES = DEC_KB * HD * 2;                 // a block's K rows (bf16)
+    constexpr int SBYTES = STAGE ? 2 * KBYTES : 16;         // a stage: K, then V^T
+    constexpr int LK = KBYTES / 1024 / NSW;                 // 1 KB loads per wave, K (and V^T)
+    constexpr int KCH = HD / 8;                             // 16-byte chunks of a K row
+    constexpr int DS = HD / 32;                             // 32-deep steps of S^T
+    constexpr int DT = HD / 16;                             // 16-row tiles of O^T
+    constexpr int OP = HD + 4;                              // padded merge row
     constexpr int HALF = HD / 2;
-    constexpr int KREG = DEC_KPW * HD * 2;  // bytes of one block's K (and of its V^T), bf16
-    constexpr int WREG = 2 * KREG;          // a wave's region: staging, then its final state
-    static_assert(WREG >= PSZ * 4, "a wave's state fits its region");
-    constexpr int NSLOT = (18 + NW - 1) / NW;  // QKV-finish slots per wave
+    constexpr int PSZ = 16 * (HD + 2);
+    constexpr int TPH = HD / 8;                             // merge threads per head, 8 features each
+    constexpr int FSL = 5;                                  // finish slots per streaming wave (18 / 4)
+    static_assert(!STAGE || LK >= 1, "stage split");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char buf[NW * WREG];
-    __shared__ __attribute__((aligned(32))) T qs[16][HD];
-    __shared__ __attribute__((aligned(32))) T kv_new[2][HD];
+    // One LDS array, carved into regions (a single LDS object leaves the compiler's wait
+    // insertion no alias scopes to track, so reads of a landed ring stage do not wait for
+    // the stages still in flight; the explicit waits below order them):
+    //   ring  NS stages of SBYTES (K rows, then V^T rows)
+    //   mrg   per streaming wave: o[16][OP], m[16], l[16] (fp32)
+    //   outb  a unit's merged state: m[16], l[16], o[16][HD] (fp32)
+    //   qsl   DEC_QSEG x 18 x HD elements: q heads 0..15, new key, new value
+    //   pre / jlo / posr / flag / desc  int tables
+    constexpr int MRG_FL = 16 * OP + 32;
+    constexpr int MRG_OFF = NS * SBYTES;
+    constexpr int OUT_OFF = MRG_OFF + NSW * MRG_FL * 4;
+    constexpr int QSL_OFF = OUT_OFF + PSZ * 4;
+    constexpr int INT_OFF = QSL_OFF + DEC_QSEG * 18 * HD * (int)sizeof(T);
+    constexpr int LDS_BYTES = INT_OFF + (3 * DEC_MAX_B + 1 + 1 + 4) * 4;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
+    unsigned char* const ring = lds;
+    float (*const mrg)[MRG_FL] = (float (*)[MRG_FL])(lds + MRG_OFF);
+    float* const outb = (float*)(lds + OUT_OFF);
+    T (*const qsl)[18][HD] = (T (*)[18][HD])(lds + QSL_OFF);
+    int* const pre = (int*)(lds + INT_OFF);  // DEC_MAX_B + 1
+    int* const jlo = pre + DEC_MAX_B + 1;     // DEC_MAX_B
+    int* const posr = jlo + DEC_MAX_B;        // DEC_MAX_B
+    int* const flag = posr + DEC_MAX_B;       // 1
+    int* const desc = flag + 1;               // 4: first unit, its block; last unit, its block
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int col = lane & 15, g = lane >> 4;
-    const int u = blockIdx.y;  // unit u = b nkv + kvh
-    const int b = u / a.nkv, kvh = u % a.nkv;
-    const int S = a.S, H = a.H, R = a.iters;
-    const int G = H / a.nkv;
-    const int CK = NW * DEC_KPW * R;
-    const int pos = a.lens[b];  // this step's position; keys lo..pos are visible
-    if (pos < 0 || pos >= S) return;  // capacity is checked by the host; stay in bounds
-    const int lo = (a.window < 0 || a.window >= pos) ? 0 : pos - a.window;
-    const int c = blockIdx.x + lo / CK;
-    const int nchunks = (pos + 1 + CK - 1) / CK;
-    if (c >= nchunks) return;
-    T* kb_base = (T*)a.kc + (long long)u * S * HD;
-    T* vb_base = (T*)a.vtc + (long long)u * HD * S;
-    unsigned char* kl = buf + wave * WREG;  // K: 64 keys x HD, 16-byte chunks swizzled
-    unsigned char* vl = kl + KREG;           // V^T: HD rows x 64 keys (128 bytes a row)
-    // first key of this wave's i-th block; a block starting past pos holds no visible key
-    auto kbeg_of = [&](int i) { return ((c * R + i) * NW + wave) * DEC_KPW; };
+    const bool io = wave == NSW;  // wave-uniform
+    const int col = lane & 15, grp = lane >> 4;
+    const int B = a.B, nkv = a.nkv, S = a.S, H = a.H, G = H / nkv;
 
-    // ---- staging loads of one block of cached K and V^T (bf16)
-    auto issue = [&](int kbeg) {
-        if constexpr (STAGE) {
-            constexpr int KCH = HD / 8;  // 16-byte chunks per K row
-            // K: LDS byte 16 p holds key p / KCH, chunk (p % KCH) ^ (key % KCH)
+    // ---- block counts per row and their prefix (I/O wave; B <= 128, two rows per lane)
+    if (io) {
+        int nb[2];
 #pragma unroll
-            for (int j = 0; j < KREG / 1024; ++j) {
-                const int p = j * 64 + lane;
-                const int kidx = p / KCH, cch = (p % KCH) ^ (kidx % KCH);
-                int key = kbeg + kidx;
-                key = key < pos ? key : (pos > 0 ? pos - 1 : 0);  // keys >= pos are masked
-                __builtin_amdgcn_global_load_lds((gvoid*)(kb_base + (long long)key * HD + cch * 8),
-                                                 (lvoid*)(kl + j * 1024), 16, 0, 0);
-            }
-            // V^T: LDS byte 16 p holds row d = p / 8, keys 8 ((p % 8) ^ (d % 8)) .. +8
-#pragma unroll
-            for (int j = 0; j < KREG / 1024; ++j) {
-                const int p = j * 64 + lane;
-                const int d = p / 8;
-                int k0 = kbeg + 8 * ((p % 8) ^ (d % 8));
-                k0 = k0 <= S - 8 ? k0 : S - 8;  // a chunk starting at or past S is fully masked
-                __builtin_amdgcn_global_load_lds((gvoid*)(vb_base + (long long)d * S + k0),
-                                                 (lvoid*)(vl + j * 1024), 16, 0, 0);
+        for (int i = 0; i < 2; ++i) {
+            const int r = 2 * lane + i;
+            nb[i] = 0;
+            if (r < B) {
+                const int pos = min(max(a.lens[r], 0), S - 1);  // capacity is checked by the host
+                const int lo = (a.window < 0 || a.window >= pos) ? 0 : pos - a.window;
+                nb[i] = pos / DEC_KB - lo / DEC_KB + 1;
+                jlo[r] = lo / DEC_KB;
+                posr[r] = pos;
             }
         }
-    };
-    // first block of this wave that reaches lo (blocks are R apart in NW 64-key steps)
-    int i0 = 0;
-    while (i0 < R && kbeg_of(i0) + DEC_KPW <= lo) ++i0;
-    const bool first_live = i0 < R && kbeg_of(i0) <= pos;
-    if (first_live) issue(kbeg_of(i0));
-
-    // ---- 1. QKV finish for row b: slot j = wave + NW i (0..15 the group's query heads,
-    //         padding past G; 16 key head kvh; 17 value head kvh).  All loads first, then
-    //         arithmetic.
-    {
-        const float* raw = a.qkv + (long long)b * (H + 2 * a.nkv) * HD;
-        const bool act = lane < HALF;
-        const int i = act ? lane : 0;
-        float v1[NSLOT], v2[NSLOT];
+        int s = nb[0] + nb[1];
 #pragma unroll
-        for (int t = 0; t < NSLOT; ++t) {
-            const int j = wave + NW * t;
-            const int src = (j < G) ? kvh * G + j : (j == 16 ? H + kvh : (j == 17 ? H + a.nkv + kvh : 0));
-            v1[t] = raw[src * HD + i];
-            v2[t] = raw[src * HD + i + HALF];
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(s, d, 64);
+            if (lane >= d) s += t;
         }
-        const float cs = a.rope_cos[(long long)pos * HALF + i], sn = a.rope_sin[(long long)pos * HALF + i];
-        const float r = row_scale_wave(a.ss_in, a.ss_in_parts, a.ss_stride, b, a.norm_dim, a.eps);
+        if (2 * lane < B) pre[2 * lane] = s - nb[0] - nb[1];
+        if (2 * lane + 1 < B) pre[2 * lane + 1] = s - nb[1];
+        const int tot = __shfl(s, 63, 64);
+        if (lane == 0) {
+            pre[B] = tot;
+            flag[0] = 0;
+        }
+        // this workgroup's run (the same formulas as below) and the units holding its first
+        // and last block: the lane whose two rows hold block q answers, found by a ballot
+        const int total = nkv * tot;
+        const int nwg = max(1, min((int)gridDim.x, total / DEC_PER_MIN));
+        const int w = blockIdx.x;
+        if (w < nwg) {
+            const int q_at[2] = {(int)((long long)w * total / nwg), (int)((long long)(w + 1) * total / nwg) - 1};
+            const int p0 = nkv * (s - nb[0] - nb[1]), p1 = nkv * (s - nb[1]), p2 = nkv * s;
 #pragma unroll
-        for (int t = 0; t < NSLOT; ++t) {
-            const int j = wave + NW * t;
-            if (j >= 18) continue;
-            if (j < G || j == 16) {  // rotate + normalise
-                const float x1 = v1[t] * r, x2 = v2[t] * r;
-                const float o1 = x1 * cs - x2 * sn, o2 = x1 * sn + x2 * cs;
-                const float ss = wave_sum(act ? o1 * o1 + o2 * o2 : 0.f);
-                const float rr = 1.0f / sqrtf(ss / (float)HD + a.eps);
-                T* dst = (j < 16) ? qs[j] : kv_new[0];
-                if (act) {
-                    dst[i] = from_f32<T>(o1 * rr);
-                    dst[i + HALF] = from_f32<T>(o2 * rr);
-                }
-            } else if (j == 17) {
-                float w1 = v1[t] * r, w2 = v2[t] * r;
-                if (a.vemb) {  // the layer's value embedding (wave-uniform)
-                    const ValueEmbed& ve = *a.vemb;
-                    const float g = value_embed_gate<T>((const T*)ve.ve_gate, kvh, ve.ve_ch,
-                                                        ve.xin + (long long)b * ve.xin_stride, r, lane);
-                    const T* e = (const T*)ve.ve + ((long long)ve.tok[b] * a.nkv + kvh) * HD;
-                    w1 += g * to_f32(e[i]);
-                    w2 += g * to_f32(e[i + HALF]);
-                }
-                if (act) {
-                    kv_new[1][i] = from_f32<T>(w1);
-                    kv_new[1][i + HALF] = from_f32<T>(w2);
-                }
-            } else {  // padding query slot
-                if (act) {
-                    qs[j][i] = from_f32<T>(0.f);
-                    qs[j][i + HALF] = from_f32<T>(0.f);
+            for (int e = 0; e < 2; ++e) {
+                const int q = q_at[e];
+                const unsigned long long m = __ballot(p0 <= q && q < p2);
+                const int L = __builtin_ctzll(m);
+                const bool second = q >= p1;
+                const int row = 2 * lane + (second ? 1 : 0);
+                const int n = second ? nb[1] : nb[0];
+                const int rel = q - (second ? p1 : p0);
+                if (lane == L) {
+                    desc[2 * e] = row * nkv + rel / n;  // unit
+                    desc[2 * e + 1] = rel % n;          // block within the unit
                 }
             }
         }
     }
     __syncthreads();
-    if (c == nchunks - 1)  // the chunk holding `pos` stores the new key/value
-        for (int e = tid; e < HD; e += NW * 64) {
-            kb_base[(long long)pos * HD + e] = kv_new[0][e];
-            vb_base[(long long)e * S + pos] = kv_new[1][e];
-        }
-    CT qf[DS];
-#pragma unroll
-    for (int s = 0; s < DS; ++s) qf[s] = *(const CT*)(&qs[col][32 * s + 8 * g]);
+    // (LDS values are the same in every lane: read them as scalars, so that addresses built
+    // from them stay in scalar registers)
+    auto lds_s = [](const int* p) { return __builtin_amdgcn_readfirstlane(*p); };
+    const int total = nkv * lds_s(&pre[B]);
+    const int nwg = max(1, min((int)gridDim.x, total / DEC_PER_MIN));
+    const int w = blockIdx.x;
+    if (w >= nwg) return;  // workgroup-uniform
+    // run of workgroup x: blocks [start(x), start(x + 1)), start(x) = floor(x total / nwg)
+    auto start_of = [&](int x) { return (int)((long long)x * total / nwg); };
+    auto wg_of = [&](int q) { return (int)(((long long)(q + 1) * nwg - 1) / total); };  // run holding block q
+    const int g0 = start_of(w), g1 = start_of(w + 1);
+    const int nblk = g1 - g0;  // >= 1
 
-    // ---- 2. the wave's blocks, online softmax over them.  State per lane: head `col`;
-    //         o_run[dt][j] holds O^T[d = 16 dt + 4 g + j][col].
+    // ---- processing order.  The run's blocks are F | M | X (F: blocks of its first unit,
+    // which may continue a unit of earlier runs; X: blocks of its last unit, which may
+    // continue into later runs; M: whole units).  They are processed as X, M, F: a unit
+    // that continues into later runs leaves its partial state early, and the run that holds
+    // a unit's last block (its owner, which merges the others' partial states into y) gets
+    // to it last.  Segment k of the order is one unit's blocks [j, jend); units are linear
+    // indices u = b nkv + g, consecutive in the run.
+    const int u_first = lds_s(&desc[0]), jf = lds_s(&desc[1]);
+    const int u_last = lds_s(&desc[2]), jl = lds_s(&desc[3]);
+    const int nseg = u_last - u_first + 1;
+    struct Cur { int k, u, b, g, j, jend, nb; };
+    auto unit_nb = [&](int bb) { return lds_s(&pre[bb + 1]) - lds_s(&pre[bb]); };
+    auto seg_begin = [&](Cur& c, int k) {
+        c.k = k;
+        int j0, je;
+        if (nseg == 1) {
+            c.u = u_first; j0 = jf; je = jl + 1;
+        } else if (k == 0) {
+            c.u = u_last; j0 = 0; je = jl + 1;
+        } else if (k < nseg - 1) {
+            c.u = u_first + k; j0 = 0; je = -1;
+        } else {
+            c.u = u_first; j0 = jf; je = -1;
+        }
+        c.b = c.u / nkv;
+        c.g = c.u - c.b * nkv;
+        c.nb = unit_nb(c.b);
+        c.j = j0;
+        c.jend = je < 0 ? c.nb : je;
+    };
+    auto cstart = [&]() { Cur c; seg_begin(c, 0); return c; };
+    auto cadvance = [&](Cur& c) {  // next block in processing order
+        if (++c.j == c.jend && c.k + 1 < nseg) seg_begin(c, c.k + 1);
+    };
+    // first block (global index) of unit (b, g)
+    auto unit_first = [&](const Cur& c) { return nkv * lds_s(&pre[c.b]) + c.g * c.nb; };
+    // the segment reaches the unit's last block: this run owns the unit
+    auto owns = [&](const Cur& c) { return c.jend == c.nb; };
+
+    // ---- QKV finish, split in a load phase and an arithmetic phase so that its loads go
+    //      out before the ring's first stages and overlap them.  Segment k (processing
+    //      order, k < DEC_QSEG) of unit (b, g): slots 0..15 its query heads (zero past G),
+    //      16 the new key, 17 the new value (only for an owned unit).  Streaming wave w takes
+    //      slots w, w + 4, ...; lane i < hd/2 holds the RoPE pair (i, i + hd/2).
+    const int nq = min(nseg, DEC_QSEG);
+    int fb[DEC_QSEG], fg[DEC_QSEG];
+    bool fown[DEC_QSEG];
+#pragma unroll
+    for (int k = 0; k < DEC_QSEG; ++k) {
+        Cur c;
+        seg_begin(c, min(k, nq - 1));
+        fb[k] = c.b; fg[k] = c.g; fown[k] = k < nq && owns(c);
+    }
+    const bool act = lane < HALF;
+    const int fi = act ? lane : 0;
+    float fv1[DEC_QSEG][FSL], fv2[DEC_QSEG][FSL], fcs[DEC_QSEG], fsn[DEC_QSEG], fss[DEC_QSEG][2];
+    auto finish_load = [&](int k) {
+        const float* raw = a.qkv + (long long)fb[k] * (H + 2 * nkv) * HD;
+#pragma unroll
+        for (int x = 0; x < FSL; ++x) {
+            const int j = wave + NSW * x;
+            const int src = j < G ? fg[k] * G + j : (j == 16 ? H + fg[k] : (j == 17 ? H + nkv + fg[k] : 0));
+            fv1[k][x] = raw[src * HD + fi];
+            fv2[k][x] = raw[src * HD + fi + HALF];
+        }
+        const int pos = lds_s(&posr[fb[k]]);
+        fcs[k] = a.rope_cos[(long long)pos * HALF + fi];
+        fsn[k] = a.rope_sin[(long long)pos * HALF + fi];
+        // this lane's share of the row's partial sums of squares (<= 128 parts: d_model <= 4096
+        // in 32-column tiles), two fixed loads, summed in the arithmetic phase
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int q = lane + 64 * x;
+            fss[k][x] = a.ss_in[(long long)min(q, a.ss_in_parts - 1) * a.ss_stride + fb[k]];
+        }
+    };
+    auto finish_compute = [&](int k, int sl) {
+        const int b = fb[k], g = fg[k];
+        const float ssl = (lane < a.ss_in_parts ? fss[k][0] : 0.f) + (lane + 64 < a.ss_in_parts ? fss[k][1] : 0.f);
+        const float r = 1.0f / sqrtf(wave_sum(ssl) / (float)a.norm_dim + a.eps);
+#pragma unroll
+        for (int x = 0; x < FSL; ++x) {
+            const int j = wave + NSW * x;
+            if (j >= 18 || (j >= 16 && !fown[k])) continue;  // wave-uniform
+            T* dst = qsl[sl][j];
+            if (j < G || j == 16) {  // rotate, then normalise over the head
+                const float x1 = fv1[k][x] * r, x2 = fv2[k][x] * r;
+                const float o1 = x1 * fcs[k] - x2 * fsn[k], o2 = x1 * fsn[k] + x2 * fcs[k];
+                const float ss = wave_sum(act ? o1 * o1 + o2 * o2 : 0.f);
+                const float rr = 1.0f / sqrtf(ss / (float)HD + a.eps);
+                if (act) {
+                    const T t1 = from_f32<T>(o1 * rr), t2 = from_f32<T>(o2 * rr);
+                    dst[fi] = t1;
+                    dst[fi + HALF] = t2;
+                    if (j == 16) {  // the new key into the cache
+                        T* kd = (T*)a.kc + (((long long)b * nkv + g) * S + lds_s(&posr[b])) * HD;
+                        kd[fi] = t1;
+                        kd[fi + HALF] = t2;
+                    }
+                }
+            } else if (j == 17) {
+                float w1 = fv1[k][x] * r, w2 = fv2[k][x] * r;
+                if (a.vemb) {  // the layer's value embedding (wave-uniform)
+                    const ValueEmbed& ve = *a.vemb;
+                    const float gt = value_embed_gate<T>((const T*)ve.ve_gate, g, ve.ve_ch,
+                                                         ve.xin + (long long)b * ve.xin_stride, r, lane);
+                    const T* e = (const T*)ve.ve + ((long long)ve.tok[b] * nkv + g) * HD;
+                    w1 += gt * to_f32(e[fi]);
+                    w2 += gt * to_f32(e[fi + HALF]);
+                }
+                if (act) {
+                    const T t1 = from_f32<T>(w1), t2 = from_f32<T>(w2);
+                    dst[fi] = t1;
+                    dst[fi + HALF] = t2;
+                    // the new value into the (transposed) cache
+                    T* vd = (T*)a.vtc + ((long long)b * nkv + g) * HD * S + lds_s(&posr[b]);
+                    vd[(long long)fi * S] = t1;
+                    vd[(long long)(fi + HALF) * S] = t2;
+                }
+            } else if (act) {  // padding head
+                dst[fi] = from_f32<T>(0.f);
+                dst[fi + HALF] = from_f32<T>(0.f);
+            }
+        }
+    };
+    // ---- ring: stage t (t-th block in processing order) into slot t % NS.  A stage is 4 LK
+    // chunks of 1 KB for K and as many for V^T; chunk c goes to LDS bytes 1024 c .. and lane
+    // l of its load fetches the 16 bytes that land at 16 l (K: LDS chunk p = 64 c + l holds
+    // key p / KCH, chunk (p % KCH) ^ (key % KCH); V^T: row d = p / 8, keys
+    // 8 ((p % 8) ^ (d % 8)) .. + 8).  Streaming wave w loads chunks w LK .. w LK + LK - 1 of
+    // the stages it issues; the I/O wave loads all chunks of the first NS - 1 stages, so the
+    // streaming waves' own load counters hold only the QKV finish's loads meanwhile.
+    auto issue = [&](int t, const Cur& c, int c0, int nc) {
+        if constexpr (STAGE) {
+            unsigned char* sb = ring + (t % NS) * SBYTES;
+            const long long u = (long long)c.b * nkv + c.g;
+            const int kbeg = (lds_s(&jlo[c.b]) + c.j) * DEC_KB;
+            const unsigned char* kb = (const unsigned char*)a.kc + (u * S + kbeg) * HD * 2;
+            const unsigned char* vb = (const unsigned char*)a.vtc + (u * HD * S + kbeg) * 2;
+            for (int ch = c0; ch < c0 + nc; ++ch) {
+                const int p = ch * 64 + lane;
+                const int key = p / KCH, kch = (p % KCH) ^ (key % KCH);
+                __builtin_amdgcn_global_load_lds((gvoid*)(kb + (unsigned)(key * HD + kch * 8) * 2u),
+                                                 (lvoid*)(sb + ch * 1024), 16, 0, 0);
+            }
+            for (int ch = c0; ch < c0 + nc; ++ch) {
+                const int p = ch * 64 + lane;
+                const int d = p / 8, vch = (p % 8) ^ (d % 8);
+                __builtin_amdgcn_global_load_lds((gvoid*)(vb + (unsigned)(d * S + vch * 8) * 2u),
+                                                 (lvoid*)(sb + KBYTES + ch * 1024), 16, 0, 0);
+            }
+        }
+    };
+    // prologue: the streaming waves issue the QKV finish's loads of the first units; then
+    // (a CU returns its loads in order) the I/O wave issues the first NS - 1 stages while the
+    // streaming waves finish (their new keys and values go to the cache)
+    if (!io) {
+#pragma unroll
+        for (int k = 0; k < DEC_QSEG; ++k)
+            if (k < nq) finish_load(k);
+    }
+    __builtin_amdgcn_s_barrier();
+    Cur ci = cstart();
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+        if (t < nblk) {
+            if (io) issue(t, ci, 0, NSW * LK);
+            cadvance(ci);
+        }
+    if (!io) {
+#pragma unroll
+        for (int k = 0; k < DEC_QSEG; ++k)
+            if (k < nq) finish_compute(k, k);
+    }
+    __syncthreads();
+
+    // ---- main loop
+    const float scale = a.scale_log2;
+    Cur cc = cstart();
+    int seg = 0;
+    int b = cc.b, g = cc.g, pos = lds_s(&posr[b]);
+    int lo = (a.window < 0 || a.window >= pos) ? 0 : pos - a.window;
+    CT qf[DS];
+    auto load_q = [&](int sl) {
+#pragma unroll
+        for (int s = 0; s < DS; ++s) qf[s] = *(const CT*)(&qsl[sl][col][8 * (4 * s + grp)]);
+    };
+    if (!io) load_q(0);
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 o_run[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) o_run[i] = zero_vec<f32x4>();
-    for (int it = i0; it < R; ++it) {
-        const int kbeg = kbeg_of(it);
-        if (kbeg > pos) break;  // wave-uniform: this and later blocks hold no visible key
-        CT kf[4][DS];
-        // V^T operands: slot 8g+i of 32-key step u <-> key 32u + 4g + i (i < 4) or
-        // 32u + 16 + 4g + (i - 4) (i >= 4).
-        HT vlo[2][DT], vhi[2][DT];
-        if constexpr (STAGE) {
-            constexpr int KCH = HD / 8;
-            NC_WAIT_VM_ALL();  // this wave's staging loads of the block have landed
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                const int kidx = 16 * kt + col;
-#pragma unroll
-                for (int s = 0; s < DS; ++s)
-                    kf[kt][s] = *(const CT*)(kl + kidx * (HD * 2) + (((4 * s + g) ^ (kidx % KCH)) * 16));
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const int d = dt * 16 + col;
-                    const int k1 = 32 * u + 4 * g, k2 = k1 + 16;  // first keys (local) of the halves
-                    vlo[u][dt] = *(const HT*)(vl + d * 128 + (((k1 / 8) ^ (d % 8)) * 16) + (k1 % 8) * 2);
-                    vhi[u][dt] = *(const HT*)(vl + d * 128 + (((k2 / 8) ^ (d % 8)) * 16) + (k2 % 8) * 2);
-                }
-            // the operand reads are complete before the region is refilled
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-            __builtin_amdgcn_sched_barrier(0);
-            if (it + 1 < R && kbeg_of(it + 1) <= pos) issue(kbeg_of(it + 1));
-        } else {
-            const int klast = pos > 0 ? pos - 1 : 0;
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                int key = kbeg + 16 * kt + col;
-                key = key < pos ? key : klast;
-#pragma unroll
-                for (int s = 0; s < DS; ++s) kf[kt][s] = *(const CT*)(kb_base + (long long)key * HD + 32 * s + 8 * g);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                int ka = kbeg + 32 * u + 4 * g, kb2 = ka + 16;
-                ka = ka <= S - 4 ? ka : S - 4;
-                kb2 = kb2 <= S - 4 ? kb2 : S - 4;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const T* src = vb_base + (long long)(dt * 16 + col) * S;
-                    vlo[u][dt] = *(const HT*)(src + ka);
-                    vhi[u][dt] = *(const HT*)(src + kb2);
-                }
-            }
-        }
+    int own_u = -1, own_ws0 = 0, own_n = 0;  // an owned unit shared with earlier runs (the last one processed)
+    // I/O wave: a partial state stored, its flag not yet set (the flag waits until the
+    // stores have completed, checked two blocks later so that the wave does not stall the
+    // streaming waves at the next barrier)
+    long long pend_flag = -1;
+    int pend_t = 0;
+    auto set_flag = [&]() {
+        wait_stores_complete();
+        if (lane == 0) __hip_atomic_store(a.flags + pend_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pend_flag = -1;
+    };
 
-        // scores S^T (lane: head `col`, keys kbeg + 16kt + 4g + j), cached keys < pos
-        f32x4 sacc[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            sacc[kt] = zero_vec<f32x4>();
-#pragma unroll
-            for (int s = 0; s < DS; ++s) sacc[kt] = mma16(kf[kt][s], qf[s], sacc[kt]);
+    for (int t = 0; t < nblk; ++t) {
+        if (io && pend_flag >= 0 && t >= pend_t + 2) set_flag();
+        if constexpr (STAGE) {
+            // wait for this wave's loads of stage t: the I/O wave issued stages 0 .. NS - 2,
+            // the streaming waves the later ones (later stages of the same issuer may stay
+            // in flight)
+            if (t <= NS - 2) {
+                if (io) {
+                    constexpr int PIO = 2 * NSW * LK;  // loads of a whole stage
+                    const int ahead = min(NS - 2, nblk - 1) - t;
+                    if (ahead >= 3) NC_WAIT_VM(3 * PIO);
+                    else if (ahead == 2) NC_WAIT_VM(2 * PIO);
+                    else if (ahead == 1) NC_WAIT_VM(PIO);
+                    else NC_WAIT_VM(0);
+                }
+            } else if (!io) {
+                const int ahead = min(NS - 2, nblk - 1 - t);
+                if (ahead >= 3) NC_WAIT_VM(3 * 2 * LK);
+                else if (ahead == 2) NC_WAIT_VM(2 * 2 * LK);
+                else if (ahead == 1) NC_WAIT_VM(2 * LK);
+                else NC_WAIT_VM(0);
+            }
+            __syncthreads();  // stage t is in LDS; every wave is done with stage t - 1
+            if (t + NS - 1 < nblk) {
+                if (!io) issue(t + NS - 1, ci, wave * LK, LK);
+                cadvance(ci);
+            }
         }
-        float mb = -INFINITY;
+        const long long u = (long long)b * nkv + g;
+        if (!io) {
+            const int kbeg = (lds_s(&jlo[b]) + cc.j) * DEC_KB;
+            const int kw = kbeg + 16 * wave;          // first key of this wave
+            const bool has_new = pos >= kw && pos < kw + 16;  // wave-uniform
+            const int sl = seg % DEC_QSEG;
+            // operands: K rows of keys kw + col (A of S^T), V^T rows d = 16 dt + col at keys
+            // kw + 4 grp .. + 3 (A of O^T)
+            CT kf[DS];
+            HT vf[DT];
+            if constexpr (STAGE) {
+                const unsigned char* kl = ring + (t % NS) * SBYTES;
+                const unsigned char* vl = kl + KBYTES;
+                const int key = 16 * wave + col;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+                for (int s = 0; s < DS; ++s) kf[s] = *(const CT*)(kl + key * HD * 2 + (((4 * s + grp) ^ (key % KCH)) * 16));
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int d = 16 * dt + col, ch = 2 * wave + (grp >> 1);
+                    vf[dt] = *(const HT*)(vl + d * 128 + ((ch ^ (d % 8)) * 16) + (grp & 1) * 8);
+                }
+            } else {
+                const T* kb = (const T*)a.kc + (u * S + kw + col) * HD;
+#pragma unroll
+                for (int s = 0; s < DS; ++s) kf[s] = *(const CT*)(kb + 8 * (4 * s + grp));
+                const T* vb = (const T*)a.vtc + u * HD * S + kw + 4 * grp;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) vf[dt] = *(const HT*)(vb + (long long)(16 * dt + col) * S);
+            }
+            if (has_new) {  // the new key and value from the finish, not from the cache
+                if (kw + col == pos) {
+#pragma unroll
+                    for (int s = 0; s < DS; ++s) kf[s] = *(const CT*)(&qsl[sl][16][8 * (4 * s + grp)]);
+                }
+                const int jn = pos - kw - 4 * grp;
+                if (jn >= 0 && jn < 4) {
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) vf[dt][jn] = qsl[sl][17][16 * dt + col];
+                }
+            }
+            // scores S^T: lane holds head col, keys kw + 4 grp + j
+            f32x4 sc = zero_vec<f32x4>();
+#pragma unroll
+            for (int s = 0; s < DS; ++s) sc = mma16(kf[s], qf[s], sc);
+            float mb = -INFINITY;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int key = kbeg + 16 * kt + 4 * g + j;
-                const float v = (key < pos && key >= lo) ? sacc[kt][j] * a.scale_log2 : -INFINITY;
-                sacc[kt][j] = v;
+                const int key = kw + 4 * grp + j;
+                const float v = (key <= pos && key >= lo) ? sc[j] * scale : -INFINITY;
+                sc[j] = v;
                 mb = fmaxf(mb, v);
             }
-        mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-        const float mn = fmaxf(m_run, mb);
-        const float mref = (mn == -INFINITY) ? 0.f : mn;  // nothing visible yet: no mass
-        const float al = fast_exp2(m_run - mref);           // 0 while the state is empty
-        float ls = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+            mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+            mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+            const float mn = fmaxf(m_run, mb);
+            const float mref = (mn == -INFINITY) ? 0.f : mn;  // nothing visible yet: no mass
+            const float al = fast_exp2(m_run - mref);           // 0 while the state is empty
+            float ls = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float pv = fast_exp2(sacc[kt][j] - mref);
-                sacc[kt][j] = pv;
-                ls += pv;
+                sc[j] = fast_exp2(sc[j] - mref);
+                ls += sc[j];
             }
-        ls += __shfl_xor(ls, 16, 64);
-        ls += __shfl_xor(ls, 32, 64);
-        l_run = l_run * al + ls;
-        m_run = mn;
+            ls += __shfl_xor(ls, 16, 64);
+            ls += __shfl_xor(ls, 32, 64);
+            l_run = l_run * al + ls;
+            m_run = mn;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o_run[dt][j] *= al;
-        // O^T[d][head] += V^T P over the block's 64 keys (two 32-deep steps)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            CT pf;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pf[i] = from_f32<T>(sacc[2 * u][i]);
-                pf[4 + i] = from_f32<T>(sacc[2 * u + 1][i]);
-            }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                CT vf;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    vf[i] = vlo[u][dt][i];
-                    vf[4 + i] = vhi[u][dt][i];
+            for (int dt = 0; dt < DT; ++dt) o_run[dt] = pv_step(vf[dt], sc, o_run[dt] * al);
+        }
+
+        // ---- end of the unit's blocks in this run (workgroup-uniform)
+        const bool unit_end = cc.j == cc.jend - 1;
+        if (unit_end) {
+            if (!io) {
+                float* mw = mrg[wave];
+                if (grp == 0) {
+                    mw[16 * OP + col] = m_run;
+                    mw[16 * OP + 16 + col] = l_run;
                 }
-                o_run[dt] = mma16(vf, pf, o_run[dt]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) *(f32x4*)(&mw[col * OP + 16 * dt + 4 * grp]) = o_run[dt];
+            }
+            __syncthreads();
+            const int q0 = unit_first(cc);
+            const int ws0 = wg_of(q0), ws1 = wg_of(q0 + cc.nb - 1);
+            const int nsu = ws1 - ws0 + 1;  // runs holding blocks of this unit
+            // the streaming waves merge their 4 states into outb (y values when the whole
+            // unit is in this run, else this run's state)
+            const int hh = tid / TPH, d0 = 8 * (tid % TPH);
+            if (!io && hh < G) {
+                float M = -INFINITY;
+#pragma unroll
+                for (int x = 0; x < NSW; ++x) M = fmaxf(M, mrg[x][16 * OP + hh]);
+                const float mr = (M == -INFINITY) ? 0.f : M;
+                float o[8], l = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+                for (int x = 0; x < NSW; ++x) {
+                    const float f = fast_exp2(mrg[x][16 * OP + hh] - mr);
+                    l += f * mrg[x][16 * OP + 16 + hh];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[e] += f * mrg[x][hh * OP + d0 + e];
+                }
+                const float inv = nsu == 1 ? 1.0f / l : 1.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) outb[32 + hh * HD + d0 + e] = o[e] * inv;
+                if (d0 == 0) {
+                    outb[hh] = M;
+                    outb[16 + hh] = l;
+                }
+            }
+            __syncthreads();  // outb is complete; the merge area is free again
+            if (nsu > 1 && w == ws1) {  // owned, shared with earlier runs: merged after the loop
+                own_u = (int)u;
+                own_ws0 = ws0;
+                own_n = nsu;
+            } else if (io) {  // the stores: y, or this run's partial state in slot (unit, run - first run)
+                if (nsu == 1) {
+                    for (int e = lane; e < G * TPH; e += 64) {
+                        const int h2 = e / TPH, f0 = 8 * (e % TPH);
+                        CT yo;
+#pragma unroll
+                        for (int x = 0; x < 8; ++x) yo[x] = from_f32<T>(outb[32 + h2 * HD + f0 + x]);
+                        *(CT*)((T*)a.y + blocked_index(b, (g * G + h2) * HD + f0, H * HD)) = yo;
+                    }
+                } else {
+                    float* ps = a.part + (u * a.max_slots + (w - ws0)) * PSZ;
+                    for (int e = lane; e < 32 + G * HD; e += 64) store_device(ps + e, outb[e]);
+                    if (pend_flag >= 0) set_flag();  // (a run shares at most two units)
+                    pend_flag = u * a.max_slots + (w - ws0);
+                    pend_t = t;
+                }
+            }
+            // next unit
+            if (t + 1 < nblk) {
+                ++seg;
+                m_run = -INFINITY;
+                l_run = 0.f;
+#pragma unroll
+                for (int i = 0; i < DT; ++i) o_run[i] = zero_vec<f32x4>();
+                cadvance(cc);
+                b = cc.b;
+                g = cc.g;
+                pos = lds_s(&posr[b]);
+                lo = (a.window < 0 || a.window >= pos) ? 0 : pos - a.window;
+                if (seg >= DEC_QSEG) {  // finish this unit now (more units than q slots)
+                    fb[0] = b; fg[0] = g; fown[0] = owns(cc);
+                    if (!io) {
+                        finish_load(0);
+                        finish_compute(0, seg % DEC_QSEG);
+                    }
+                    __syncthreads();
+                }
+                if (!io) load_q(seg % DEC_QSEG);
+            }
+            continue;
+        }
+        cadvance(cc);
+    }
+
+    // ---- an owned unit shared with earlier runs: wait for their partial states (flags set
+    // once each state is visible; they were written at the start of those runs), merge them
+    // with this run's state (outb) into y, and clear the flags for the next launch
+    if (io && pend_flag >= 0) set_flag();  // the state is visible device-wide before its flag
+    if (own_u < 0) return;  // workgroup-uniform
+    if (io) return;
+    const long long u = own_u;
+    const int nprev = own_n - 1;  // slots 0 .. nprev - 1
+    int32_t* fl = a.flags + u * a.max_slots;
+    if (tid < nprev) {  // bounded wait: the states were written long before, in practice at once
+        int v = 0;
+        for (int it = 0; it < (1 << 22); ++it) {
+            v = __hip_atomic_load(fl + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (v) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (!v) flag[0] = 1;  // never set: the output is made NaN rather than wrong
+    }
+    __syncthreads();
+    const bool bad = flag[0] != 0;
+    const int hh = tid / TPH, d0 = 8 * (tid % TPH);
+    if (hh < G) {
+        const int bb = (int)(u / nkv), gg = (int)(u % nkv);
+        const float* pu = a.part + u * a.max_slots * PSZ;
+        float M = outb[hh];
+        for (int s = 0; s < nprev; ++s) M = fmaxf(M, load_device(pu + (long long)s * PSZ + hh));
+        const float mr = (M == -INFINITY) ? 0.f : M;
+        float o[8];
+        const float f_own = fast_exp2(outb[hh] - mr);
+        float l = f_own * outb[16 + hh];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = f_own * outb[32 + hh * HD + d0 + e];
+        for (int s0 = 0; s0 < nprev; s0 += 4) {  // 4 slots per batch of independent loads
+            float mt[4], lt[4], ot[4][8];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const float* ps = pu + (long long)min(s0 + x, nprev - 1) * PSZ;
+                mt[x] = load_device(ps + hh);
+                lt[x] = load_device(ps + 16 + hh);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ot[x][e] = load_device(ps + 32 + hh * HD + d0 + e);
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const float f = s0 + x < nprev ? fast_exp2(mt[x] - mr) : 0.f;
+                l += f * lt[x];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] += f * ot[x][e];
             }
         }
-        // the new key (position pos) joins the wave whose block holds it
-        if (pos >= kbeg && pos < kbeg + DEC_KPW) {
-            // score of head `col`: lane group g sums a quarter of the hd features
-            float part = 0.f;
+        const float inv = bad ? __builtin_nanf("") : 1.0f / l;
+        CT yo;
 #pragma unroll
-            for (int e = 0; e < HD / 4; ++e)
-                part += to_f32(qs[col][g * (HD / 4) + e]) * to_f32(kv_new[0][g * (HD / 4) + e]);
-            part += __shfl_xor(part, 16, 64);
-            part += __shfl_xor(part, 32, 64);
-            const float sp = part * a.scale_log2;
-            const float mn2 = fmaxf(m_run, sp);
-            const float al2 = fast_exp2(m_run - mn2);  // 0 when no cached key was visible
-            const float be = fast_exp2(sp - mn2);
-            l_run = l_run * al2 + be;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    o_run[dt][j] = o_run[dt][j] * al2 + be * to_f32(kv_new[1][dt * 16 + 4 * g + j]);
-            m_run = mn2;
-        }
+        for (int e = 0; e < 8; ++e) yo[e] = from_f32<T>(o[e] * inv);
+        *(CT*)((T*)a.y + blocked_index(bb, (gg * G + hh) * HD + d0, H * HD)) = yo;
     }
-
-    // ---- 3a. one block per wave (R == 1): each wave's state is its own partial, slot
-    //          NW c + w of row b; the combine kernel merges them with the other chunks'.
-    if (R == 1) {
-        float* pw = a.part + ((long long)u * a.max_slots + NW * c + wave) * PSZ;
-        if (g == 0) {
-            pw[col] = m_run;
-            pw[16 + col] = l_run;
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(pw + 32 + col * HD + dt * 16 + 4 * g) = o_run[dt];
-        return;
-    }
-    // ---- 3b. merge the waves' states into the chunk's partial (slot c of row b)
-    if constexpr (STAGE) NC_WAIT_VM_ALL();  // no staging load still in flight into the region
-    __syncthreads();                        // every wave is done with its region
-    float* st = (float*)(buf + wave * WREG);
-    if (g == 0) {
-        st[col] = m_run;
-        st[16 + col] = l_run;
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) st[32 + col * HD + dt * 16 + 4 * g + j] = o_run[dt][j];
-    __syncthreads();
-    float* pb = a.part + ((long long)u * a.max_slots + c) * PSZ;
-    for (int e = tid; e < 16 * HD; e += NW * 64) {
-        const int h = e / HD;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, ((const float*)(buf + w * WREG))[h]);
-        const float mref = (M == -INFINITY) ? 0.f : M;
-        float o = 0.f, l = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float* sw = (const float*)(buf + w * WREG);
-            const float f = fast_exp2(sw[h] - mref);
-            o += f * sw[32 + e];
-            l += f * sw[16 + h];
-        }
-        pb[32 + e] = o;
-        if (e % HD == 0) {
-            pb[h] = M;
-            pb[16 + h] = l;
-        }
-    }
+    if (tid < nprev) __hip_atomic_store(fl + tid, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Combine kernel: workgroup (head h, row b), one thread per feature d, over the row's
-// chunks (slots) of `chunk` keys that hold visible keys (from the one holding lo):
-// y[b][h][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s over the row's slots.  The
-// slot statistics are loaded lane-parallel (one slot per lane), the weights go through
-// LDS, and the o_s[d] loads of consecutive slots are independent of each other.
-template <typename T, int HD>
-__global__ __launch_bounds__(HD) void attn_decode_combine_kernel(const float* __restrict__ part,
-                                                                 const int32_t* __restrict__ lens,
-                                                                 T* __restrict__ y, int H, int nkv,
-                                                                 int S, int window, int max_slots,
-                                                                 int chunk) {
-    constexpr int PSZ = 16 * (HD + 2);
-    __shared__ float wts[512];
-    __shared__ float stat[1];
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-    const int G = H / nkv, hg = h % G;  // query head h is head hg of K/V head h / G's group
-    const int pos = min(lens[b], S - 1);
-    const int nsl = min((pos + 1 + chunk - 1) / chunk, 512);
-    const int s_lo = ((window < 0 || window >= pos) ? 0 : pos - window) / chunk;
-    const float* prow = part + ((long long)b * nkv + h / G) * max_slots * PSZ;
-    if (d < 64) {  // wave 0: max, weights and normaliser
-        float mloc = -INFINITY;
-        for (int sl = s_lo + d; sl < nsl; sl += 64) mloc = fmaxf(mloc, prow[(long long)sl * PSZ + hg]);
-        const float M = wave_max(mloc);
-        float lsum = 0.f;
-        for (int sl = s_lo + d; sl < nsl; sl += 64) {
-            const float w = fast_exp2(prow[(long long)sl * PSZ + hg] - M);  // 0 for empty slots
-            wts[sl] = w;
-            lsum += w * prow[(long long)sl * PSZ + 16 + hg];
-        }
-        lsum = wave_sum(lsum);
-        if (d == 0) stat[0] = 1.0f / lsum;
-    }
-    __syncthreads();
-    const float* po = prow + 32 + hg * HD + d;
-    float o = 0.f;
-    for (int s0 = s_lo; s0 < nsl; s0 += 16) {  // 16 slots per batch of independent loads
-        float t[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) t[u] = po[(long long)min(s0 + u, nsl - 1) * PSZ];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) o += (s0 + u < nsl) ? wts[min(s0 + u, nsl - 1)] * t[u] : 0.f;
-    }
-    y[blocked_index(b, h * HD + d, H * HD)] = from_f32<T>(o * stat[0]);
-}
-
-hipError_t launch_attn_decode(DType dt, const DecAttnArgs& args, void* y, hipStream_t st) {
+hipError_t launch_attn_decode(DType dt, const DecAttnArgs& args, hipStream_t st) {
     DecAttnArgs a = args;
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)a.hd);
-    if (a.nkv < 1 || a.H % a.nkv || a.H / a.nkv > 16) return hipErrorInvalidValue;
-    const int units = a.B * a.nkv;  // (row, K/V head) pairs
-    const int span = attn_decode_span(a.S, a.window);
-    const int nw = attn_decode_waves(units, span);
-    if (a.iters != attn_decode_iters(units, span) || a.max_slots < attn_decode_slots(units, a.S, span))
+    const int units = a.B * a.nkv;
+    if (a.nkv < 1 || a.H % a.nkv || a.H / a.nkv > 16 || a.B < 1 || a.B > DEC_MAX_B || a.S % DEC_KB ||
+        a.max_slots < attn_decode_slots(units, a.S) || !a.part || !a.flags || !a.y)
         return hipErrorInvalidValue;
-    const int ck = nw * DEC_KPW * a.iters;
-    // chunks with visible keys: all of them, or those a window of span keys can touch
-    const int all = (a.S + ck - 1) / ck;
-    const int live = span == a.S ? all : std::min(all, (span - 1 + ck - 1) / ck + 1);
-    dim3 g1(live, units), g2(a.H, a.B);
-    // the combine sees slots of `chunk` keys: a wave's block when R == 1, else a chunk
-    const int chunk = a.iters == 1 ? DEC_KPW : ck;
-#define NC_AD(TT, HDV)                                                                         \
-    do {                                                                                       \
-        if (nw == 4) NC_TLAUNCH((attn_decode_split_kernel<TT, HDV, 4>), g1, dim3(256), 0, st, a); \
-        else NC_TLAUNCH((attn_decode_split_kernel<TT, HDV, 2>), g1, dim3(128), 0, st, a);     \
-        NC_TLAUNCH((attn_decode_combine_kernel<TT, HDV>), g2, dim3(HDV), 0, st,                \
-                   (const float*)a.part, a.lens, (TT*)y, a.H, a.nkv, a.S,              \
-                   span == a.S ? -1 : a.window, a.max_slots, chunk);                          \
-    } while (0)
+    const dim3 grid(attn_decode_workgroups(units, a.S));
+#define NC_AD(TT, HDV) NC_TLAUNCH((attn_decode_kernel<TT, HDV>), grid, dim3(320), 0, st, a)
     if (dt == BF16 && a.hd == 128) NC_AD(bf16, 128);
     else if (dt == BF16 && a.hd == 64) NC_AD(bf16, 64);
     else if (dt == F32 && a.hd == 128) NC_AD(float, 128);

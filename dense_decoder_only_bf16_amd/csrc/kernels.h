@@ -186,11 +186,13 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
                                void* y, int B, int T, int H, int nkv, int S, int window,
                                const int32_t* offs, hipStream_t st);
 
-// Decode attention for one step, one query per row at position lens[b] (keys
-// 0..lens[b], or lens[b] - window .. lens[b] with a window >= 0).  The split kernel first finishes the row's raw QKV product (norm scale,
-// RoPE, QK-norm) and stores the new key/value into the cache, then reduces each chunk of
-// keys to a partial softmax state; the combine kernel merges a row's partials into
-// y, [B][H hd] stored blocked (blocked_index, rows rounded up to 32).  The combine reads lens[b] to know the chunk count.
+// Decode attention for one step: one query per row at position lens[b] against keys
+// 0..lens[b] (or lens[b] - window .. lens[b] with a window >= 0) of each K/V head.  The
+// kernel first finishes the row's raw QKV product (norm scale, RoPE, QK-norm) and stores the
+// new key/value into the cache; the 64-key blocks of all (row, K/V head) units are split
+// into equal runs, one per workgroup; a unit cut by run boundaries leaves partial softmax
+// states that the run holding its last block merges.  y: [B][H hd] stored blocked
+// (blocked_index, rows rounded up to 32).
 struct DecAttnArgs {
     const float* qkv;   // raw product [B][(H+2 nkv) hd] fp32
     const float* ss_in; int ss_in_parts, ss_stride, norm_dim;
@@ -198,21 +200,21 @@ struct DecAttnArgs {
     const float* rope_cos; const float* rope_sin;
     const int32_t* lens;
     void* kc; void* vtc;  // this layer's cache: K [B][nkv][S][hd], V^T [B][nkv][hd][S]
-    float* part;          // [B nkv][max_slots][16 (hd + 2)]
-    int B, H, hd, S, nkv; // query heads H = nkv G, G <= 16 per K/V head
+    float* part;          // partial states [B nkv][max_slots][16 (hd + 2)]
+    int32_t* flags;       // ready flags of the partial states [B nkv][max_slots]: zero before
+                          // the first launch, and every launch leaves them zero
+    void* y;              // attention output, blocked
+    int B, H, hd, S, nkv; // query heads H = nkv G, G <= 16 per K/V head; B <= 128; S % 64 == 0
     int window;           // sliding window (< 0: the whole causal context)
-    int iters;            // 64-key blocks per wave: attn_decode_iters(B nkv, span)
-    int max_slots;        // partial slots per unit, >= attn_decode_slots(B nkv, S, span)
+    int max_slots;        // partial slots per unit, >= attn_decode_slots(B nkv, S)
     float scale_log2;     // set by the launcher
     const ValueEmbed* vemb;  // device memory (null: none); tok[b], xin row b
 };
 // Keys a query can see at most: min(S, window + 1), or S without a window.
 int attn_decode_span(int S, int window);
-// For `rows` (row, K/V head) units over a cache of S positions of which at most `span`
-// are visible to a query:
-int attn_decode_iters(int rows, int span);         // 64-key blocks per wave
-int attn_decode_slots(int rows, int S, int span);  // partial slots per unit
-hipError_t launch_attn_decode(DType dt, const DecAttnArgs& a, void* y, hipStream_t st);
+int attn_decode_workgroups(int units, int S);  // grid of a launch over `units` (row, K/V head) units
+int attn_decode_slots(int units, int S);       // partial slots per unit
+hipError_t launch_attn_decode(DType dt, const DecAttnArgs& a, hipStream_t st);
 
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, hipStream_t st);
 // Token per row drawn with probabilities proportional to 2^(logit scale) over the logits at

@@ -131,7 +131,8 @@ struct nc_kv {
     void* u = nullptr;        // [M][d_ff] MLP hidden
     void* act_lo = nullptr;   // bf16 only: low parts of the MLP operands (compensated
     void* u_lo = nullptr;     // products): x - bf16(x) after attention, u - bf16(u)
-    float* apart = nullptr;   // decode attention partials
+    float* apart = nullptr;   // decode attention partial states
+    int32_t* actr = nullptr;  // decode attention ready flags, one per (row, K/V head) and slot
     float* dpart = nullptr;   // decode projections: split-K partials
     float* x0 = nullptr;      // later-version blocks: stream before layer 0's scaling [M][d]
     float* xb = nullptr;      // and the backout source [M][d]
@@ -166,12 +167,12 @@ void drop_graphs(nc_kv* kv) {
 
 void ws_free(nc_kv* kv) {
     drop_graphs(kv);  // captured graphs point into the workspace
-    void* ptrs[] = {kv->x, kv->act, kv->ss_a, kv->ss_b, kv->qkv, kv->q, kv->y, kv->u, kv->apart,
+    void* ptrs[] = {kv->x, kv->act, kv->ss_a, kv->ss_b, kv->qkv, kv->q, kv->y, kv->u, kv->apart, kv->actr,
                     kv->act_lo, kv->u_lo, kv->dpart, kv->x0, kv->xb, kv->tokbuf, kv->rx_dev, kv->ve_dev};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     kv->x = nullptr; kv->act = nullptr; kv->ss_a = nullptr; kv->ss_b = nullptr; kv->qkv = nullptr;
-    kv->q = nullptr; kv->y = nullptr; kv->u = nullptr; kv->apart = nullptr;
+    kv->q = nullptr; kv->y = nullptr; kv->u = nullptr; kv->apart = nullptr; kv->actr = nullptr;
     kv->act_lo = nullptr; kv->u_lo = nullptr; kv->dpart = nullptr; kv->x0 = nullptr; kv->xb = nullptr;
     kv->tokbuf = nullptr; kv->rx_dev = nullptr; kv->ve_dev = nullptr;
     kv->dpart_elems = 0;
@@ -245,13 +246,13 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
     }
     {
         const int units = kv->B * c.n_kv_head;  // (row, K/V head) pairs of decode attention
-        int slots = 0;
-        for (int l = 0; l < c.n_layer; ++l)
-            slots = std::max(slots, attn_decode_slots(units, kv->S, attn_decode_span(kv->S, kv->m->windows[l])));
-        kv->apart_slots = slots;
-        kv->apart_elems = (long long)units * slots * 16 * (c.head_dim + 2);
+        kv->apart_slots = attn_decode_slots(units, kv->S);
+        kv->apart_elems = (long long)units * kv->apart_slots * 16 * (c.head_dim + 2);
+        WS_ALLOC(kv->apart, kv->apart_elems * 4);
+        // ready flags of the partial states: zero now, and every launch leaves them zero
+        WS_ALLOC(kv->actr, (long long)units * kv->apart_slots * 4);
+        HIP_TRY(hipMemset(kv->actr, 0, (size_t)units * kv->apart_slots * 4));
     }
-    WS_ALLOC(kv->apart, kv->apart_elems * 4);
     {   // split-K partials of the decode projections (M = batch rows)
         const int B = kv->B, d = c.d_model, F = c.d_ff, hqv = c.n_head * c.head_dim;
         const int nq = (c.n_head + 2 * c.n_kv_head) * c.head_dim;
@@ -441,11 +442,11 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         DecAttnArgs at{};
         at.qkv = kv->qkv; at.ss_in = kv->ss_a; at.ss_in_parts = ss_a_parts; at.ss_stride = ss;
         at.norm_dim = d; at.eps = c.norm_eps; at.rope_cos = m->rope_cos; at.rope_sin = m->rope_sin;
-        at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = kv->apart;
+        at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = kv->apart; at.flags = kv->actr;
+        at.y = kv->y;
         at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.nkv = nkv; at.max_slots = kv->apart_slots;
         at.window = m->windows[l];
         at.vemb = (m->ex.on && m->ex.ve[l]) ? kv->ve_dev + l : nullptr;
-        at.iters = attn_decode_iters(B * nkv, attn_decode_span(kv->S, at.window));
         {   // bytes: the K/V read for every row (its visible positions, the new one
             // included) of each K/V head, q/k/v in fp32, y out; flops 4 hd per
             // (query head, key) pair
@@ -455,7 +456,7 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
                 keys += at.window < 0 ? kv->lens_host[b] + 1 : std::min(kv->lens_host[b], at.window) + 1;
             const double by = keys * nkv * hd * 2 * es + (double)B * nqkv * 4 + (double)B * H * hd * es;
             LAUNCH(timed(NC_KC_DECODE_ATTN, by, 4.0 * H * hd * keys, st,
-                         [&] { return launch_attn_decode(m->dt, at, kv->y, st); }, 2));
+                         [&] { return launch_attn_decode(m->dt, at, st); }));
         }
         // O + residual
         DecGemmArgs o = a;
