@@ -223,6 +223,8 @@ hipError_t launch_argmax(const float* logits, int B, int V, int32_t* out, hipStr
 hipError_t launch_sample(const float* logits, int B, int V, float scale, int top_k, const float* u,
                          int32_t* out, hipStream_t st);
 hipError_t launch_lens_add(int32_t* lens, int B, int32_t delta, int32_t set_value, hipStream_t st);
+// p[0..n) = 0 (a fill kernel: no memset node when the caller captures the stream)
+hipError_t launch_zero_i32(int32_t* p, long long n, hipStream_t st);
 hipError_t launch_kv_export(DType dt, int hd, const void* kc, const void* vtc, void* k_out,
                             void* v_out, int B, int S, int S_out, hipStream_t st);
 

@@ -6,6 +6,8 @@
 // development-tricks section) and QK-norm (yelogs.com architecture answer; apidog.com/th
 // part 1) finish the query and key projections.  Each of these is one wave per row (or
 // per row and head) with wavefront reductions for the sums of squares.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -597,6 +599,18 @@ __global__ void lens_kernel(int32_t* lens, int B, int32_t delta, int32_t set_val
 
 hipError_t launch_lens_add(int32_t* lens, int B, int32_t delta, int32_t set_value, hipStream_t st) {
     hipLaunchKernelGGL(lens_kernel, dim3((B + 255) / 256), dim3(256), 0, st, lens, B, delta, set_value);
+    return hipGetLastError();
+}
+
+__global__ void zero_i32_kernel(int32_t* p, long long n) {
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+hipError_t launch_zero_i32(int32_t* p, long long n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const long long blocks = std::min<long long>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
     return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -110,17 +111,14 @@ struct nc_model {
     int live_kv = 0;
 };
 
-struct nc_kv {
-    nc_model* m;
-    int B, max_seq, S;  // S: allocated positions per row (stride), multiple of 64
-    void* kcache = nullptr;  // [L][B][nkv][S][hd]
-    void* vcache = nullptr;  // [L][B][nkv][hd][S]
-    int32_t* lens_dev = nullptr;
-    std::vector<int32_t> lens_host;
-    int32_t* hist = nullptr;  // [B][S] tokens by position (only with smear)
-    // workspace, sized for `cap_m` token rows
+// Workspace of the forward: every buffer the kernels use beyond the inputs, the outputs,
+// the weights and the cache.  One block, laid out by ws_layout for `cap_m` token rows; the
+// same layout is carved from library-allocated memory (nc_kv) or from the static array of
+// the allocation-free decode entry point.
+struct Ws {
     long long cap_m = 0;
     int ss_parts_max = 0;
+    void* base = nullptr;     // the block (null: none)
     float* x = nullptr;       // [M][d] fp32 residual
     void* act = nullptr;      // [M][d] dtype copy of x
     float* ss_a = nullptr;    // [parts][M] sums of squares feeding the QKV / LM-head norm
@@ -133,7 +131,7 @@ struct nc_kv {
     void* u_lo = nullptr;     // products): x - bf16(x) after attention, u - bf16(u)
     float* apart = nullptr;   // decode attention partial states
     int32_t* actr = nullptr;  // decode attention ready flags, one per (row, K/V head) and slot
-    float* dpart = nullptr;   // decode projections: split-K partials
+    float* dpart = nullptr;   // decode projections: split-K arrival counters, then partials
     float* x0 = nullptr;      // later-version blocks: stream before layer 0's scaling [M][d]
     float* xb = nullptr;      // and the backout source [M][d]
     int32_t* tokbuf = nullptr;   // the rows' clamped tokens (value embeddings) [M]
@@ -141,7 +139,20 @@ struct nc_kv {
     ValueEmbed* ve_dev = nullptr;  // per layer: the value embedding (decode)
     long long dpart_elems = 0;
     long long apart_elems = 0;
-    int apart_slots = 0;      // partial slots per (row, K/V head) unit, the most any layer needs
+    long long actr_elems = 0;
+    int apart_slots = 0;      // partial slots per (row, K/V head) unit
+    size_t bytes = 0;         // size of the block
+};
+
+struct nc_kv {
+    nc_model* m;
+    int B, max_seq, S;  // S: allocated positions per row (stride), multiple of 64
+    void* kcache = nullptr;  // [L][B][nkv][S][hd]
+    void* vcache = nullptr;  // [L][B][nkv][hd][S]
+    int32_t* lens_dev = nullptr;
+    std::vector<int32_t> lens_host;
+    int32_t* hist = nullptr;  // [B][S] tokens by position (only with smear)
+    Ws ws;  // workspace, library-allocated (grown on demand)
     // decode step captured as a HIP graph, keyed by the caller's token/logit buffers
     bool use_graph = true;
     hipStream_t cap_stream = nullptr;
@@ -167,33 +178,24 @@ void drop_graphs(nc_kv* kv) {
 
 void ws_free(nc_kv* kv) {
     drop_graphs(kv);  // captured graphs point into the workspace
-    void* ptrs[] = {kv->x, kv->act, kv->ss_a, kv->ss_b, kv->qkv, kv->q, kv->y, kv->u, kv->apart, kv->actr,
-                    kv->act_lo, kv->u_lo, kv->dpart, kv->x0, kv->xb, kv->tokbuf, kv->rx_dev, kv->ve_dev};
-    for (void* p : ptrs)
-        if (p) (void)hipFree(p);
-    kv->x = nullptr; kv->act = nullptr; kv->ss_a = nullptr; kv->ss_b = nullptr; kv->qkv = nullptr;
-    kv->q = nullptr; kv->y = nullptr; kv->u = nullptr; kv->apart = nullptr; kv->actr = nullptr;
-    kv->act_lo = nullptr; kv->u_lo = nullptr; kv->dpart = nullptr; kv->x0 = nullptr; kv->xb = nullptr;
-    kv->tokbuf = nullptr; kv->rx_dev = nullptr; kv->ve_dev = nullptr;
-    kv->dpart_elems = 0;
-    kv->cap_m = 0;
-    kv->apart_elems = 0;
+    if (kv->ws.base) (void)hipFree(kv->ws.base);
+    kv->ws = Ws{};
 }
 
 // RESID extras of layer l's MLP residual (PROJ): the next layer's scaling, the backout
 // source when the next layer is the backout layer, the backout itself after the last.
-ResidExtra proj_resid_extra(const nc_model* m, const nc_kv* kv, int l) {
+ResidExtra proj_resid_extra(const nc_model* m, const Ws& ws, int l) {
     const nc_model::Extras& ex = m->ex;
     ResidExtra r{};
     r.ra = 1.f;
     if (!ex.on) return r;
-    r.x0 = kv->x0;
+    r.x0 = ws.x0;
     if (l + 1 < m->cfg.n_layer) {
         r.ra = ex.lam[l + 1];
         r.rb = ex.mu[l + 1];
-        if (l + 1 == ex.backout_layer) r.xb_out = kv->xb;
+        if (l + 1 == ex.backout_layer) r.xb_out = ws.xb;
     } else if (ex.backout_layer >= 0) {
-        r.xb = kv->xb;
+        r.xb = ws.xb;
         r.rc = -ex.backout_lambda;
     }
     return r;
@@ -201,86 +203,103 @@ ResidExtra proj_resid_extra(const nc_model* m, const nc_kv* kv, int l) {
 
 // Value embedding of layer l (ve null: none); the tokens are those the embedding kernel
 // recorded for the rows of the current call.
-ValueEmbed value_embed(const nc_model* m, const nc_kv* kv, int l) {
+ValueEmbed value_embed(const nc_model* m, const Ws& ws, int l) {
     ValueEmbed v{};
     if (!m->ex.on || !m->ex.ve[l]) return v;
     v.ve = m->ex.ve[l]; v.ve_gate = m->ex.ve_gate[l]; v.ve_ch = m->ex.ve_ch; v.vocab = m->cfg.vocab;
-    v.tok = kv->tokbuf; v.xin = kv->x; v.xin_stride = m->cfg.d_model;
+    v.tok = ws.tokbuf; v.xin = ws.x; v.xin_stride = m->cfg.d_model;
     return v;
+}
+
+// Layout of the workspace for M token rows of a cache of B rows and S positions, carved
+// from `base` (null: sizes only, every pointer offset from 0).  Each buffer starts at a
+// 256-byte boundary; ws.bytes is the total.
+Ws ws_layout(const nc_model* m, int B, int S, long long M, void* base) {
+    const nc_config& c = m->cfg;
+    const size_t es = m->esz;
+    Ws w{};
+    w.cap_m = M;
+    const long long d = c.d_model, hq = (long long)c.n_head * c.head_dim;
+    const long long nqkv = (long long)(c.n_head + 2 * c.n_kv_head) * c.head_dim;
+    // row statistics come in parts of one per output tile of the producing product
+    w.ss_parts_max = (c.d_model + dec_gemm_tile_n() - 1) / dec_gemm_tile_n();
+    // dtype activations that decode stores blocked hold whole 32-row blocks
+    const long long Mr = (M + 31) / 32 * 32;
+    size_t off = 0;
+    auto take = [&](long long bytes) -> void* {
+        void* p = (char*)base + off;
+        off += align_up((size_t)std::max(bytes, 0LL), 256);
+        return p;
+    };
+    w.x = (float*)take(M * d * 4);
+    w.act = take(Mr * d * es);
+    w.ss_a = (float*)take((long long)w.ss_parts_max * M * 4);
+    w.ss_b = (float*)take((long long)w.ss_parts_max * M * 4);
+    w.qkv = (float*)take(M * nqkv * 4);
+    w.q = take(M * hq * es);
+    w.y = take(Mr * hq * es);
+    w.u = take(Mr * c.d_ff * es);
+    if (m->dt == BF16) {
+        w.act_lo = take(Mr * d * es);
+        w.u_lo = take(Mr * c.d_ff * es);
+    }
+    const nc_model::Extras& ex = m->ex;
+    if (ex.on) {
+        w.x0 = (float*)take(M * d * 4);
+        if (ex.backout_layer >= 0) w.xb = (float*)take(M * d * 4);
+        w.tokbuf = (int32_t*)take(M * 4);
+        w.rx_dev = (ResidExtra*)take(c.n_layer * (long long)sizeof(ResidExtra));
+        w.ve_dev = (ValueEmbed*)take(c.n_layer * (long long)sizeof(ValueEmbed));
+    }
+    const int units = B * c.n_kv_head;  // (row, K/V head) pairs of decode attention
+    w.apart_slots = attn_decode_slots(units, S);
+    w.apart_elems = (long long)units * w.apart_slots * 16 * (c.head_dim + 2);
+    w.apart = (float*)take(w.apart_elems * 4);
+    w.actr_elems = (long long)units * w.apart_slots;
+    w.actr = (int32_t*)take(w.actr_elems * 4);
+    {   // split-K partials of the decode projections (M = batch rows)
+        const int hqv = c.n_head * c.head_dim, nq = (c.n_head + 2 * c.n_kv_head) * c.head_dim;
+        w.dpart_elems = std::max({dec_gemm_part_elems(m->dt, EPI_STORE, B, nq, c.d_model),
+                                  dec_gemm_part_elems(m->dt, EPI_RESID, B, c.d_model, hqv),
+                                  dec_gemm_part_elems(m->dt, EPI_RELU2, B, c.d_ff, c.d_model),
+                                  dec_gemm_part_elems(m->dt, EPI_RESID, B, c.d_model, c.d_ff),
+                                  dec_gemm_part_elems(m->dt, EPI_SOFTCAP, B, c.vocab, c.d_model)});
+        w.dpart = w.dpart_elems > 0 ? (float*)take(w.dpart_elems * 4) : nullptr;
+    }
+    w.bytes = off;
+    w.base = base;
+    return w;
 }
 
 // Grow the workspace to hold M token rows.
 nc_status ws_ensure(nc_kv* kv, long long M) {
-    if (M <= kv->cap_m) return NC_OK;
-    const nc_config& c = kv->m->cfg;
-    const size_t es = kv->m->esz;
+    if (M <= kv->ws.cap_m) return NC_OK;
     HIP_TRY(hipDeviceSynchronize());
     ws_free(kv);
-    const long long d = c.d_model, hq = (long long)c.n_head * c.head_dim;
-    const long long nqkv = (long long)(c.n_head + 2 * c.n_kv_head) * c.head_dim;
-    // row statistics come in parts of one per output tile of the producing product
-    kv->ss_parts_max = (c.d_model + dec_gemm_tile_n() - 1) / dec_gemm_tile_n();
-    const long long qkv_elems = M * nqkv;
-    // dtype activations that decode stores blocked hold whole 32-row blocks
-    const long long Mr = (M + 31) / 32 * 32;
-#define WS_ALLOC(ptr, bytes) HIP_TRY(hipMalloc((void**)&(ptr), (size_t)(bytes)))
-    WS_ALLOC(kv->x, M * d * 4);
-    WS_ALLOC(kv->act, Mr * d * es);
-    WS_ALLOC(kv->ss_a, (long long)kv->ss_parts_max * M * 4);
-    WS_ALLOC(kv->ss_b, (long long)kv->ss_parts_max * M * 4);
-    WS_ALLOC(kv->qkv, qkv_elems * 4);
-    WS_ALLOC(kv->q, M * hq * es);
-    WS_ALLOC(kv->y, Mr * hq * es);
-    WS_ALLOC(kv->u, Mr * c.d_ff * es);
-    if (kv->m->dt == BF16) {
-        WS_ALLOC(kv->act_lo, Mr * d * es);
-        WS_ALLOC(kv->u_lo, Mr * c.d_ff * es);
-    }
-    const nc_model::Extras& ex = kv->m->ex;
-    if (ex.on) {
-        WS_ALLOC(kv->x0, M * d * 4);
-        if (ex.backout_layer >= 0) WS_ALLOC(kv->xb, M * d * 4);
-        WS_ALLOC(kv->tokbuf, M * 4);
-        WS_ALLOC(kv->rx_dev, c.n_layer * sizeof(ResidExtra));
-        WS_ALLOC(kv->ve_dev, c.n_layer * sizeof(ValueEmbed));
-    }
-    {
-        const int units = kv->B * c.n_kv_head;  // (row, K/V head) pairs of decode attention
-        kv->apart_slots = attn_decode_slots(units, kv->S);
-        kv->apart_elems = (long long)units * kv->apart_slots * 16 * (c.head_dim + 2);
-        WS_ALLOC(kv->apart, kv->apart_elems * 4);
-        // ready flags of the partial states: zero now, and every launch leaves them zero
-        WS_ALLOC(kv->actr, (long long)units * kv->apart_slots * 4);
-        HIP_TRY(hipMemset(kv->actr, 0, (size_t)units * kv->apart_slots * 4));
-    }
-    {   // split-K partials of the decode projections (M = batch rows)
-        const int B = kv->B, d = c.d_model, F = c.d_ff, hqv = c.n_head * c.head_dim;
-        const int nq = (c.n_head + 2 * c.n_kv_head) * c.head_dim;
-        const DType dt = kv->m->dt;
-        long long e = std::max({dec_gemm_part_elems(dt, EPI_STORE, B, nq, d),
-                                dec_gemm_part_elems(dt, EPI_RESID, B, d, hqv),
-                                dec_gemm_part_elems(dt, EPI_RELU2, B, F, d),
-                                dec_gemm_part_elems(dt, EPI_RESID, B, d, F),
-                                dec_gemm_part_elems(dt, EPI_SOFTCAP, B, c.vocab, d)});
-        if (e > 0) {
-            WS_ALLOC(kv->dpart, e * 4);
-            // the arrival counters at its head start at zero; every launch leaves them so
-            HIP_TRY(hipMemset(kv->dpart, 0, DEC_PART_CTRS * 4));
-        }
-        kv->dpart_elems = e;
-    }
-#undef WS_ALLOC
-    kv->cap_m = M;
-    if (ex.on) {  // the per-layer blocks that decode kernels read through pointers
+    const size_t bytes = ws_layout(kv->m, kv->B, kv->S, M, nullptr).bytes;
+    void* base = nullptr;
+    HIP_TRY(hipMalloc(&base, bytes));
+    Ws w = ws_layout(kv->m, kv->B, kv->S, M, base);
+    // the attention ready flags and the split-K arrival counters start at zero, and every
+    // launch leaves them so
+    hipError_t e = hipMemset(w.actr, 0, (size_t)w.actr_elems * 4);
+    if (e == hipSuccess && w.dpart) e = hipMemset(w.dpart, 0, DEC_PART_CTRS * 4);
+    if (e == hipSuccess && kv->m->ex.on) {  // the per-layer blocks that decode kernels read through pointers
+        const nc_config& c = kv->m->cfg;
         std::vector<ResidExtra> rx(c.n_layer);
         std::vector<ValueEmbed> ve(c.n_layer);
         for (int l = 0; l < c.n_layer; ++l) {
-            rx[l] = proj_resid_extra(kv->m, kv, l);
-            ve[l] = value_embed(kv->m, kv, l);
+            rx[l] = proj_resid_extra(kv->m, w, l);
+            ve[l] = value_embed(kv->m, w, l);
         }
-        HIP_TRY(hipMemcpy(kv->rx_dev, rx.data(), rx.size() * sizeof(ResidExtra), hipMemcpyHostToDevice));
-        HIP_TRY(hipMemcpy(kv->ve_dev, ve.data(), ve.size() * sizeof(ValueEmbed), hipMemcpyHostToDevice));
+        e = hipMemcpy(w.rx_dev, rx.data(), rx.size() * sizeof(ResidExtra), hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(w.ve_dev, ve.data(), ve.size() * sizeof(ValueEmbed), hipMemcpyHostToDevice);
     }
+    if (e != hipSuccess) {
+        (void)hipFree(base);
+        return fail(NC_ERR_DEVICE, std::string("workspace setup: ") + hipGetErrorString(e));
+    }
+    kv->ws = w;
     return NC_OK;
 }
 
@@ -331,10 +350,13 @@ nc_status launched(hipError_t e, const char* what) {
 // Launch `fn` (returning hipError_t); if kernel class `cls` is being timed, bracket it with
 // an event pair on `st` that carries its algorithmic bytes and flops.
 // `kernels` = number of kernels `fn` launches through NC_TLAUNCH (at most NC_MAX_STAMPS).
+// Set while the allocation-free decode step enqueues: no timing events are created.
+thread_local bool t_untimed = false;
+
 template <typename F>
 hipError_t timed(int cls, double bytes, double flops, hipStream_t st, F fn, int kernels = 1) {
     (void)st;
-    if (g_tm.cls != cls) return fn();
+    if (g_tm.cls != cls || t_untimed) return fn();
     TimingPair tp = {};
     tp.bytes = bytes;
     tp.flops = flops;
@@ -397,56 +419,56 @@ hipError_t prefill_gemm(nc_model* m, Epi epi, const GemmArgs& g, hipStream_t st)
 
 // Embedding of M = B T token rows (positions lens[b] + t), with the later-version blocks'
 // smear, x0 and layer-0 scaling when they are on.
-EmbedArgs embed_args(nc_model* m, nc_kv* kv, const int32_t* tokens, int M, int T, bool blocked) {
+EmbedArgs embed_args(nc_model* m, nc_kv* kv, const Ws& ws, const int32_t* tokens, int M, int T, bool blocked) {
     const nc_config& c = m->cfg;
     const nc_model::Extras& ex = m->ex;
     EmbedArgs e{};
     e.tok = tokens; e.M = M; e.T = T; e.wte = m->wte; e.vocab = c.vocab; e.d = c.d_model;
     e.eps = c.norm_eps; e.scale0 = 1.f;
-    e.x = kv->x; e.act = kv->act; e.ss = kv->ss_a; e.blocked = blocked;
+    e.x = ws.x; e.act = ws.act; e.ss = ws.ss_a; e.blocked = blocked;
     e.lens = kv->lens_dev; e.hist = kv->hist; e.S = kv->S;
     if (ex.on) {
         e.scale0 = ex.lam[0] + ex.mu[0];
-        e.x0 = kv->x0;
-        if (ex.backout_layer == 0) e.xb = kv->xb;
+        e.x0 = ws.x0;
+        if (ex.backout_layer == 0) e.xb = ws.xb;
         e.smear_gate = ex.smear_gate; e.smear_ch = ex.smear_ch; e.smear_lambda = ex.smear_lambda;
-        e.tok_out = kv->tokbuf;
+        e.tok_out = ws.tokbuf;
     }
     return e;
 }
 
 // Enqueue one decode step (everything after the host-side checks) on `st`.
-nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* logits, hipStream_t st) {
+nc_status enqueue_decode(nc_model* m, nc_kv* kv, const Ws& ws, const int32_t* tokens, float* logits, hipStream_t st) {
     const nc_config& c = m->cfg;
     const int B = kv->B;
     const int d = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_ff, V = c.vocab, nkv = c.n_kv_head;
     const int nqkv = (H + 2 * nkv) * hd;
     const size_t per_layer = (size_t)B * nkv * kv->S * hd * m->esz;
     const int parts_d = (d + dec_gemm_tile_n() - 1) / dec_gemm_tile_n();
-    const int ss = (int)kv->cap_m;
+    const int ss = (int)ws.cap_m;
     nc_status s;
 
-    LAUNCH(launch_embed(m->dt, embed_args(m, kv, tokens, B, 1, true), st));
+    LAUNCH(launch_embed(m->dt, embed_args(m, kv, ws, tokens, B, 1, true), st));
     int ss_a_parts = 1;
     for (int l = 0; l < c.n_layer; ++l) {
         const nc_model::Layer& L = m->layers[l];
         void* kc = (char*)kv->kcache + l * per_layer;
         void* vtc = (char*)kv->vcache + l * per_layer;
         DecGemmArgs a{};
-        a.M = B; a.eps = c.norm_eps; a.cap = c.softcap; a.ss_stride = ss; a.part = kv->dpart;
+        a.M = B; a.eps = c.norm_eps; a.cap = c.softcap; a.ss_stride = ss; a.part = ws.dpart;
         // QKV raw product, then norm scale + RoPE + QK-norm + cache write at lens[b]
-        a.A = kv->act; a.W = L.wqkv; a.N = nqkv; a.K = d;
-        a.out_f32 = kv->qkv; a.ldo = nqkv;
+        a.A = ws.act; a.W = L.wqkv; a.N = nqkv; a.K = d;
+        a.out_f32 = ws.qkv; a.ldo = nqkv;
         if ((s = decode_gemm(kv, EPI_STORE, a, st)) != NC_OK) return s;
         // QKV finish (norm scale, RoPE, QK-norm, cache write) + attention over the cache
         DecAttnArgs at{};
-        at.qkv = kv->qkv; at.ss_in = kv->ss_a; at.ss_in_parts = ss_a_parts; at.ss_stride = ss;
+        at.qkv = ws.qkv; at.ss_in = ws.ss_a; at.ss_in_parts = ss_a_parts; at.ss_stride = ss;
         at.norm_dim = d; at.eps = c.norm_eps; at.rope_cos = m->rope_cos; at.rope_sin = m->rope_sin;
-        at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = kv->apart; at.flags = kv->actr;
-        at.y = kv->y;
-        at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.nkv = nkv; at.max_slots = kv->apart_slots;
+        at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = ws.apart; at.flags = ws.actr;
+        at.y = ws.y;
+        at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.nkv = nkv; at.max_slots = ws.apart_slots;
         at.window = m->windows[l];
-        at.vemb = (m->ex.on && m->ex.ve[l]) ? kv->ve_dev + l : nullptr;
+        at.vemb = (m->ex.on && m->ex.ve[l]) ? ws.ve_dev + l : nullptr;
         {   // bytes: the K/V read for every row (its visible positions, the new one
             // included) of each K/V head, q/k/v in fp32, y out; flops 4 hd per
             // (query head, key) pair
@@ -460,28 +482,28 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const int32_t* tokens, float* l
         }
         // O + residual
         DecGemmArgs o = a;
-        o.A = kv->y; o.W = L.wo; o.N = d; o.K = H * hd;
-        o.out_f32 = kv->x; o.out_t = kv->act; o.ldo = d; o.ss_out = kv->ss_b;
-        o.out_lo = kv->act_lo;
+        o.A = ws.y; o.W = L.wo; o.N = d; o.K = H * hd;
+        o.out_f32 = ws.x; o.out_t = ws.act; o.ldo = d; o.ss_out = ws.ss_b;
+        o.out_lo = ws.act_lo;
         if ((s = decode_gemm(kv, EPI_RESID, o, st)) != NC_OK) return s;
         // FC + norm scale + relu^2 (compensated operand)
         DecGemmArgs f = a;
-        f.A = kv->act; f.A_lo = kv->act_lo; f.W = L.wfc; f.N = F; f.K = d;
-        f.out_t = kv->u; f.out_lo = kv->u_lo; f.ldo = F; f.ss_in = kv->ss_b; f.ss_in_parts = parts_d;
+        f.A = ws.act; f.A_lo = ws.act_lo; f.W = L.wfc; f.N = F; f.K = d;
+        f.out_t = ws.u; f.out_lo = ws.u_lo; f.ldo = F; f.ss_in = ws.ss_b; f.ss_in_parts = parts_d;
         if ((s = decode_gemm(kv, EPI_RELU2, f, st)) != NC_OK) return s;
         // PROJ + residual (compensated operand)
         DecGemmArgs pj = a;
-        pj.A = kv->u; pj.A_lo = kv->u_lo; pj.W = L.wproj; pj.N = d; pj.K = F;
-        pj.out_f32 = kv->x; pj.out_t = kv->act; pj.ldo = d; pj.ss_out = kv->ss_a;
-        pj.rx = m->ex.on ? kv->rx_dev + l : nullptr;
-        if (l == c.n_layer - 1) pj.out_lo = kv->act_lo;  // the LM head's operand is compensated
+        pj.A = ws.u; pj.A_lo = ws.u_lo; pj.W = L.wproj; pj.N = d; pj.K = F;
+        pj.out_f32 = ws.x; pj.out_t = ws.act; pj.ldo = d; pj.ss_out = ws.ss_a;
+        pj.rx = m->ex.on ? ws.rx_dev + l : nullptr;
+        if (l == c.n_layer - 1) pj.out_lo = ws.act_lo;  // the LM head's operand is compensated
         if ((s = decode_gemm(kv, EPI_RESID, pj, st)) != NC_OK) return s;
         ss_a_parts = parts_d;
     }
     DecGemmArgs h{};
-    h.M = B; h.eps = c.norm_eps; h.cap = c.softcap; h.ss_stride = ss; h.part = kv->dpart;
-    h.A = kv->act; h.A_lo = kv->act_lo; h.W = m->lm; h.N = V; h.K = d;
-    h.out_f32 = logits; h.ldo = V; h.ss_in = kv->ss_a; h.ss_in_parts = ss_a_parts;
+    h.M = B; h.eps = c.norm_eps; h.cap = c.softcap; h.ss_stride = ss; h.part = ws.dpart;
+    h.A = ws.act; h.A_lo = ws.act_lo; h.W = m->lm; h.N = V; h.K = d;
+    h.out_f32 = logits; h.ldo = V; h.ss_in = ws.ss_a; h.ss_in_parts = ss_a_parts;
     h.lens_inc = kv->lens_dev;  // the step's last kernel also advances every row by one
     if ((s = decode_gemm(kv, EPI_SOFTCAP, h, st)) != NC_OK) return s;
     return NC_OK;
@@ -894,23 +916,23 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
         const int Mi = (int)M;
 
         // bf16 activations of prefill are stored blocked, the layout the products read
-        LAUNCH(launch_embed(m->dt, embed_args(m, kv, tokens, Mi, T, m->dt == BF16), st));
+        LAUNCH(launch_embed(m->dt, embed_args(m, kv, kv->ws, tokens, Mi, T, m->dt == BF16), st));
         int ss_a_parts = 1;
         for (int l = 0; l < c.n_layer; ++l) {
             const nc_model::Layer& L = m->layers[l];
             GemmArgs g{};
             g.M = Mi; g.lda = d; g.k_split = 1; g.eps = c.norm_eps; g.cap = c.softcap;
             // QKV raw product
-            g.A = kv->act; g.B = L.wqkv; g.N = nqkv; g.K = d; g.Npad = nqkv;
-            g.out_f32 = kv->qkv; g.ldo = nqkv; g.z_stride = 0;
+            g.A = kv->ws.act; g.B = L.wqkv; g.N = nqkv; g.K = d; g.Npad = nqkv;
+            g.out_f32 = kv->ws.qkv; g.ldo = nqkv; g.z_stride = 0;
             LAUNCH(prefill_gemm(m, EPI_STORE, g, st));
             QkvPostArgs qa{};
-            qa.part = kv->qkv; qa.splits = 1; qa.z_stride = 0; qa.M = Mi; qa.T = T; qa.H = H; qa.hd = hd; qa.nkv = nkv;
-            qa.ss_in = kv->ss_a; qa.ss_in_parts = ss_a_parts; qa.ss_stride = (int)kv->cap_m; qa.norm_dim = d;
+            qa.part = kv->ws.qkv; qa.splits = 1; qa.z_stride = 0; qa.M = Mi; qa.T = T; qa.H = H; qa.hd = hd; qa.nkv = nkv;
+            qa.ss_in = kv->ws.ss_a; qa.ss_in_parts = ss_a_parts; qa.ss_stride = (int)kv->ws.cap_m; qa.norm_dim = d;
             qa.lens = kv->lens_dev; qa.rope_cos = m->rope_cos; qa.rope_sin = m->rope_sin;
-            qa.q = kv->q; qa.kc = (char*)kv->kcache + l * per_layer; qa.vtc = (char*)kv->vcache + l * per_layer;
+            qa.q = kv->ws.q; qa.kc = (char*)kv->kcache + l * per_layer; qa.vtc = (char*)kv->vcache + l * per_layer;
             qa.S = kv->S; qa.eps = c.norm_eps;
-            qa.vemb = value_embed(m, kv, l);
+            qa.vemb = value_embed(m, kv->ws, l);
             LAUNCH(launch_qkv_post(m->dt, qa, st));
             {   // causal attention flops: 4 hd per visible (query, key) pair and head; bytes:
                 // q in, y out, and every key/value a query of the row sees, read once
@@ -924,26 +946,26 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
                 const double fl = 4.0 * H * hd * vis;
                 const double by = ((double)B * T * 2 * H + keys * 2 * nkv) * hd * m->esz;
                 LAUNCH(timed(NC_KC_PREFILL_ATTN, by, fl, st, [&] {
-                    return launch_attn_prefill(m->dt, hd, kv->q, qa.kc, qa.vtc, kv->y, B, T, H, nkv, kv->S, w,
+                    return launch_attn_prefill(m->dt, hd, kv->ws.q, qa.kc, qa.vtc, kv->ws.y, B, T, H, nkv, kv->S, w,
                                                kv->lens_dev, st);
                 }));
             }
             // O product + residual
-            g.A = kv->y; g.lda = H * hd; g.B = L.wo; g.N = d; g.K = H * hd; g.Npad = d;
-            g.out_f32 = kv->x; g.out_t = kv->act; g.ldo = d; g.ss_out = kv->ss_b; g.ss_stride = (int)kv->cap_m;
-            g.A_lo = nullptr; g.out_lo = kv->act_lo;
+            g.A = kv->ws.y; g.lda = H * hd; g.B = L.wo; g.N = d; g.K = H * hd; g.Npad = d;
+            g.out_f32 = kv->ws.x; g.out_t = kv->ws.act; g.ldo = d; g.ss_out = kv->ws.ss_b; g.ss_stride = (int)kv->ws.cap_m;
+            g.A_lo = nullptr; g.out_lo = kv->ws.act_lo;
             LAUNCH(prefill_gemm(m, EPI_RESID, g, st));
             // FC + norm + relu^2 (compensated operand)
-            g.A = kv->act; g.lda = d; g.B = L.wfc; g.N = F; g.K = d; g.Npad = F;
-            g.out_t = kv->u; g.ldo = F; g.ss_in = kv->ss_b; g.ss_in_parts = parts_d; g.ss_stride = (int)kv->cap_m;
-            g.A_lo = kv->act_lo; g.out_lo = kv->u_lo;
+            g.A = kv->ws.act; g.lda = d; g.B = L.wfc; g.N = F; g.K = d; g.Npad = F;
+            g.out_t = kv->ws.u; g.ldo = F; g.ss_in = kv->ws.ss_b; g.ss_in_parts = parts_d; g.ss_stride = (int)kv->ws.cap_m;
+            g.A_lo = kv->ws.act_lo; g.out_lo = kv->ws.u_lo;
             LAUNCH(prefill_gemm(m, EPI_RELU2, g, st));
             // PROJ + residual (compensated operand)
-            g.A = kv->u; g.lda = F; g.B = L.wproj; g.N = d; g.K = F; g.Npad = d;
-            g.out_f32 = kv->x; g.out_t = kv->act; g.ldo = d; g.ss_out = kv->ss_a; g.ss_stride = (int)kv->cap_m;
-            g.A_lo = kv->u_lo;
-            g.out_lo = (l == c.n_layer - 1) ? kv->act_lo : nullptr;  // LM head operand, compensated
-            g.rx = proj_resid_extra(m, kv, l);
+            g.A = kv->ws.u; g.lda = F; g.B = L.wproj; g.N = d; g.K = F; g.Npad = d;
+            g.out_f32 = kv->ws.x; g.out_t = kv->ws.act; g.ldo = d; g.ss_out = kv->ws.ss_a; g.ss_stride = (int)kv->ws.cap_m;
+            g.A_lo = kv->ws.u_lo;
+            g.out_lo = (l == c.n_layer - 1) ? kv->ws.act_lo : nullptr;  // LM head operand, compensated
+            g.rx = proj_resid_extra(m, kv->ws, l);
             LAUNCH(prefill_gemm(m, EPI_RESID, g, st));
             g.A_lo = nullptr;
             g.rx = ResidExtra{};
@@ -951,10 +973,10 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
         }
         if (logits) {
             GemmArgs g{};
-            g.A = kv->act; g.A_lo = kv->act_lo; g.lda = d; g.B = m->lm; g.M = Mi; g.N = V; g.K = d;
+            g.A = kv->ws.act; g.A_lo = kv->ws.act_lo; g.lda = d; g.B = m->lm; g.M = Mi; g.N = V; g.K = d;
             g.Npad = (V + 31) / 32 * 32; g.k_split = 1;
-            g.out_f32 = logits; g.ldo = V; g.ss_in = kv->ss_a; g.ss_in_parts = ss_a_parts;
-            g.ss_stride = (int)kv->cap_m; g.eps = c.norm_eps; g.cap = c.softcap;
+            g.out_f32 = logits; g.ldo = V; g.ss_in = kv->ws.ss_a; g.ss_in_parts = ss_a_parts;
+            g.ss_stride = (int)kv->ws.cap_m; g.eps = c.norm_eps; g.cap = c.softcap;
             LAUNCH(prefill_gemm(m, EPI_SOFTCAP, g, st));
         }
         LAUNCH(launch_lens_add(kv->lens_dev, B, T, -1, st));
@@ -983,7 +1005,7 @@ nc_status decode_impl(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* kv, 
         if (s != NC_OK) return s;
         hipStream_t st = (hipStream_t)stream;
         auto enqueue = [&](hipStream_t q) {
-            nc_status r = enqueue_decode(m, kv, tokens, logits, q);
+            nc_status r = enqueue_decode(m, kv, kv->ws, tokens, logits, q);
             if (r == NC_OK && next) {
                 const hipError_t e = launch_argmax(logits, B, m->cfg.vocab, next, q);
                 if (e != hipSuccess) r = fail(NC_ERR_DEVICE, std::string("argmax: ") + hipGetErrorString(e));
@@ -1050,6 +1072,74 @@ nc_status nc_decode_greedy(nc_model* m, const int32_t* tokens, int32_t B, nc_kv*
                            int32_t* next, void* stream) {
     if (!next) return fail(NC_ERR_INVALID_ARG, "next is NULL");
     return decode_impl(m, tokens, B, kv, logits, next, stream);
+}
+
+}  // extern "C"
+
+// ---- allocation-free decode step, for callers that cannot allocate (code under HIP graph
+// capture, tight serving loops, harnesses that forbid hipMalloc): the workspace of the step
+// lives in this file-scope device array.  Each GPU that loads the library holds its own
+// copy until the process ends; its device address is looked up once per device.
+static __device__ __align__(256) unsigned char scratch[NC_STATIC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+nc_status scratch_of_device(void** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(NC_ERR_UNSUPPORTED, "device index beyond the supported range");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(NC_ERR_DEVICE, std::string("scratch address: ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return NC_OK;
+}
+}  // namespace
+
+extern "C" {
+
+nc_status nc_decode_step_static(nc_model* m, const int32_t* tokens, int32_t B, nc_kv* kv, float* logits,
+                                void* stream) {
+    try {
+        if (!m || !tokens || !kv || !logits) return fail(NC_ERR_INVALID_ARG, "NULL argument");
+        if (kv->m != m) return fail(NC_ERR_INVALID_ARG, "kv belongs to another model");
+        if (B != kv->B) return fail(NC_ERR_INVALID_ARG, "B differs from the cache's batch");
+        if (B > 128) return fail(NC_ERR_UNSUPPORTED, "decode supports at most 128 rows");
+        if (m->ex.on)
+            return fail(NC_ERR_UNSUPPORTED, "the allocation-free decode step does not take the later-version blocks");
+        for (int b = 0; b < B; ++b)
+            if (kv->lens_host[b] + 1 > kv->max_seq) return fail(NC_ERR_CAPACITY, "a row is full (lens + 1 > max_seq)");
+        const size_t need = ws_layout(m, kv->B, kv->S, B, nullptr).bytes;
+        if (need > NC_STATIC_SCRATCH_BYTES)
+            return fail(NC_ERR_CAPACITY, "the step's workspace (" + std::to_string(need) + " bytes) exceeds the " +
+                                             std::to_string((size_t)NC_STATIC_SCRATCH_BYTES) + "-byte static array");
+        void* base = nullptr;
+        nc_status s = scratch_of_device(&base);
+        if (s != NC_OK) return s;
+        const Ws w = ws_layout(m, kv->B, kv->S, B, base);
+        hipStream_t st = (hipStream_t)stream;
+        // the array keeps the last call's contents: the attention ready flags and the
+        // split-K arrival counters must start at zero
+        LAUNCH(launch_zero_i32(w.actr, w.actr_elems, st));
+        if (w.dpart) LAUNCH(launch_zero_i32((int32_t*)w.dpart, DEC_PART_CTRS, st));
+        t_untimed = true;
+        s = enqueue_decode(m, kv, w, tokens, logits, st);
+        t_untimed = false;
+        if (s != NC_OK) return s;
+        for (int b = 0; b < B; ++b) kv->lens_host[b] += 1;
+        return NC_OK;
+    } catch (...) {
+        t_untimed = false;
+        return fail(NC_ERR_DEVICE, "unexpected exception");
+    }
 }
 
 nc_status nc_timing_enable(int32_t kernel_class) {

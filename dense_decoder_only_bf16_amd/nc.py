@@ -35,10 +35,12 @@ NC_KC_DECODE_GEMM = 1
 NC_KC_PREFILL_GEMM = 2
 NC_KC_PREFILL_ATTN = 3
 NC_KC_DECODE_ATTN = 4
+NC_STATIC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = ("nc_model_create", "nc_model_free", "nc_model_set_windows", "nc_model_set_extras",
             "nc_kv_create", "nc_kv_free", "nc_kv_set_lens",
             "nc_kv_get_lens", "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step",
+            "nc_decode_step_static",
             "nc_decode_greedy", "nc_argmax",
             "nc_sample", "nc_timing_enable", "nc_timing_read", "nc_last_error", "nc_abi_version",
             "nc_diag_mfma_rate", "nc_diag_hbm_read_rate")
@@ -100,6 +102,7 @@ def lib():
         L.nc_kv_copy_rows.argtypes = [vp, ctypes.POINTER(i32), vp, ctypes.POINTER(i32), i32, vp]
         L.nc_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.nc_decode_step.argtypes = [vp, vp, i32, vp, vp, vp]
+        L.nc_decode_step_static.argtypes = [vp, vp, i32, vp, vp, vp]
         L.nc_decode_greedy.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.nc_argmax.argtypes = [vp, i32, i32, vp, vp]
         L.nc_sample.argtypes = [vp, i32, i32, ctypes.c_float, i32, vp, vp, vp]
@@ -113,6 +116,7 @@ def lib():
         L.nc_abi_version.restype = i32
         for name in ("nc_model_create", "nc_model_set_windows", "nc_model_set_extras", "nc_kv_create", "nc_kv_set_lens", "nc_kv_get_lens",
                      "nc_kv_export", "nc_kv_copy_rows", "nc_prefill", "nc_decode_step", "nc_decode_greedy",
+                     "nc_decode_step_static",
                      "nc_argmax",
                      "nc_sample", "nc_timing_enable", "nc_timing_read", "nc_diag_mfma_rate",
                      "nc_diag_hbm_read_rate"):
@@ -311,6 +315,13 @@ def nc_decode_step(m, tokens, B, kv, logits, stream=None):
                                 _stream(stream)))
 
 
+def nc_decode_step_static(m, tokens, B, kv, logits, stream=None):
+    """tokens int32 [B]; logits float32 [B, V]; the workspace in the library's static array."""
+    _check(lib().nc_decode_step_static(m, _arg(tokens, "int32", max(B, 0), "tokens"), B, kv,
+                                       _arg(logits, "float32", max(B, 0) * _vocab(m), "logits"),
+                                       _stream(stream)))
+
+
 def nc_decode_greedy(m, tokens, B, kv, logits, next_tokens, stream=None):
     """tokens int32 [B]; logits float32 [B, V]; next_tokens int32 [B] (may be tokens)."""
     _check(lib().nc_decode_greedy(m, _arg(tokens, "int32", max(B, 0), "tokens"), B, kv,
@@ -408,6 +419,12 @@ class KV:
         self._shape(tokens, (self.batch,), "tokens")
         self._shape(logits, (self.batch, self.model.shape.vocab), "logits")
         nc_decode_step(self.model.handle, tokens, self.batch, self.handle, logits, stream)
+
+    def decode_static(self, tokens, logits, stream=None):
+        """decode with the workspace in the library's static array (allocates nothing)."""
+        self._shape(tokens, (self.batch,), "tokens")
+        self._shape(logits, (self.batch, self.model.shape.vocab), "logits")
+        nc_decode_step_static(self.model.handle, tokens, self.batch, self.handle, logits, stream)
 
     def decode_greedy(self, tokens, logits, next_tokens, stream=None):
         """decode + argmax of the logits into next_tokens (may be tokens), one graph."""

@@ -204,6 +204,24 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens_dev, int32_t B, int32_t 
 nc_status nc_decode_step(nc_model* m, const int32_t* tokens_dev, int32_t B, nc_kv* kv,
                          float* logits_dev, void* stream);
 
+/* Allocation-free decode step, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same step as
+ * nc_decode_step, with the same arguments, requirements, results (bitwise) and errors, but
+ * its workspace (residual stream, activations, raw QKV product, attention partial states
+ * and ready flags, split-K partial sums and arrival counters) lives in a file-scope device
+ * array of NC_STATIC_SCRATCH_BYTES that every GPU the library runs on holds until the
+ * process ends, not in memory of the kv object; kernels are launched one by one (no graph
+ * is captured).  The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine) and clears the array's flags and counters with a kernel before the step.
+ * Errors beyond nc_decode_step's: NC_ERR_CAPACITY when the step's workspace for this
+ * (model, kv) exceeds the array (the message gives the bytes needed); NC_ERR_UNSUPPORTED
+ * for a model with the later version's blocks (nc_model_set_extras).  Every call on a GPU
+ * uses the same array, which keeps the last call's contents: calls that overlap on one GPU
+ * (other streams or threads) race and give wrong results. */
+#define NC_STATIC_SCRATCH_BYTES 67108864 /* 64 MiB */
+nc_status nc_decode_step_static(nc_model* m, const int32_t* tokens_dev, int32_t B, nc_kv* kv,
+                                float* logits_dev, void* stream);
+
 /* Greedy decode step, the engine's generation loop with argmax picks (apidog.com/th guide,
  * part 6): nc_decode_step followed by nc_argmax of its logits into next_dev (int32 [B]),
  * both in one captured graph: one call per generated token.  next_dev may be
