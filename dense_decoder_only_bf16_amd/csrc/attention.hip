@@ -348,11 +348,11 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 // already holds the 4 keys of its column).  fp32 (small check models) loads the same
 // fragments straight from memory.
 //
-// QKV finish.  While the first stages load, the workgroup finishes the raw QKV product for
-// the units of its run (row norm scale, RoPE at pos_b and QK-norm of the group's query heads;
-// for the unit whose last block it holds, also the new key and value, which it writes into
-// the cache).  The new key is not read back from the cache: the wave whose keys hold
-// position pos_b takes its K and V operands for that key from the finished values.
+// Queries.  The finished queries (qkv_finish_decode, which also put the new key and value
+// into the cache) of a unit's group are copied into LDS by a fifth wave, the I/O wave, with
+// direct-to-LDS loads: the first units' before the ring's first stages, a later unit's while
+// the run is still DEC_QSEG units before it.  The I/O wave also issues the ring's first
+// stages and does the run's output stores, so the streaming waves never wait on them.
 //
 // End of a unit's run: the 4 waves' states merge in LDS; a unit inside one run is
 // normalised and stored to y; otherwise the state goes to the unit's partial slot and, at
@@ -360,7 +360,7 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 // scope stores completed first, no cache-wide fence); the last to arrive merges the unit's
 // partials into y and resets the counter.  y is [B][H hd] stored blocked (blocked_index).
 constexpr int DEC_KB = 64;       // keys per block (one ring stage)
-constexpr int DEC_QSEG = 4;      // units whose finished q the prologue prepares
+constexpr int DEC_QSEG = 4;      // query slots in LDS (units whose queries are staged ahead)
 constexpr int DEC_PER_MIN = 2;   // at least this many blocks per workgroup
 constexpr int DEC_MAX_WG = 256;  // workgroups per launch (one per CU)
 constexpr int DEC_MAX_B = 128;
@@ -374,6 +374,9 @@ int attn_decode_slots(int units, int S) {
     (void)units;
     return std::min(DEC_MAX_WG, (S / DEC_KB + DEC_PER_MIN - 1) / DEC_PER_MIN + 2);
 }
+
+// vmcnt waits take at most 63
+constexpr int vm_cap(int n) { return n > 63 ? 63 : n; }
 
 __device__ __forceinline__ f32x4 mma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
     typedef short s4 __attribute__((ext_vector_type(4)));
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
     constexpr int HALF = HD / 2;
     constexpr int PSZ = 16 * (HD + 2);
     constexpr int TPH = HD / 8;                             // merge threads per head, 8 features each
-    constexpr int FSL = 5;                                  // finish slots per streaming wave (18 / 4)
+    constexpr int QBYTES = 16 * HD * (int)sizeof(T);        // a query slot: 16 heads
     static_assert(!STAGE || LK >= 1, "stage split");
 
     // One LDS array, carved into regions (a single LDS object leaves the compiler's wait
@@ -419,20 +422,21 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
     //   ring  NS stages of SBYTES (K rows, then V^T rows)
     //   mrg   per streaming wave: o[16][OP], m[16], l[16] (fp32)
     //   outb  a unit's merged state: m[16], l[16], o[16][HD] (fp32)
-    //   qsl   DEC_QSEG x 18 x HD elements: q heads 0..15, new key, new value
+    //   qsl   DEC_QSEG x 16 x HD elements: query heads of a group
     //   pre / jlo / posr / flag / desc  int tables
     constexpr int MRG_FL = 16 * OP + 32;
     constexpr int MRG_OFF = NS * SBYTES;
     constexpr int OUT_OFF = MRG_OFF + NSW * MRG_FL * 4;
     constexpr int QSL_OFF = OUT_OFF + PSZ * 4;
-    constexpr int INT_OFF = QSL_OFF + DEC_QSEG * 18 * HD * (int)sizeof(T);
+    constexpr int INT_OFF = QSL_OFF + DEC_QSEG * QBYTES;
     constexpr int LDS_BYTES = INT_OFF + (3 * DEC_MAX_B + 1 + 1 + 4) * 4;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(QSL_OFF % 16 == 0 && QBYTES % 1024 == 0, "query slots: whole 1 KB loads");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
     unsigned char* const ring = lds;
     float (*const mrg)[MRG_FL] = (float (*)[MRG_FL])(lds + MRG_OFF);
     float* const outb = (float*)(lds + OUT_OFF);
-    T (*const qsl)[18][HD] = (T (*)[18][HD])(lds + QSL_OFF);
+    T (*const qsl)[16][HD] = (T (*)[16][HD])(lds + QSL_OFF);
     int* const pre = (int*)(lds + INT_OFF);  // DEC_MAX_B + 1
     int* const jlo = pre + DEC_MAX_B + 1;     // DEC_MAX_B
     int* const posr = jlo + DEC_MAX_B;        // DEC_MAX_B
@@ -550,90 +554,18 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
     // the segment reaches the unit's last block: this run owns the unit
     auto owns = [&](const Cur& c) { return c.jend == c.nb; };
 
-    // ---- QKV finish, split in a load phase and an arithmetic phase so that its loads go
-    //      out before the ring's first stages and overlap them.  Segment k (processing
-    //      order, k < DEC_QSEG) of unit (b, g): slots 0..15 its query heads (zero past G),
-    //      16 the new key, 17 the new value (only for an owned unit).  Streaming wave w takes
-    //      slots w, w + 4, ...; lane i < hd/2 holds the RoPE pair (i, i + hd/2).
+    // ---- query slot of segment k: heads g G .. g G + 15 of unit (b, g) (heads past the
+    //      group repeat its last head; their scores are never used), 1 KB loads by the I/O wave
     const int nq = min(nseg, DEC_QSEG);
-    int fb[DEC_QSEG], fg[DEC_QSEG];
-    bool fown[DEC_QSEG];
+    auto issue_q = [&](const Cur& c, int sl) {
+        unsigned char* dst = (unsigned char*)&qsl[sl][0][0];
+        const unsigned char* src = (const unsigned char*)a.q + ((long long)c.b * H + c.g * G) * HD * sizeof(T);
 #pragma unroll
-    for (int k = 0; k < DEC_QSEG; ++k) {
-        Cur c;
-        seg_begin(c, min(k, nq - 1));
-        fb[k] = c.b; fg[k] = c.g; fown[k] = k < nq && owns(c);
-    }
-    const bool act = lane < HALF;
-    const int fi = act ? lane : 0;
-    float fv1[DEC_QSEG][FSL], fv2[DEC_QSEG][FSL], fcs[DEC_QSEG], fsn[DEC_QSEG], fss[DEC_QSEG][2];
-    auto finish_load = [&](int k) {
-        const float* raw = a.qkv + (long long)fb[k] * (H + 2 * nkv) * HD;
-#pragma unroll
-        for (int x = 0; x < FSL; ++x) {
-            const int j = wave + NSW * x;
-            const int src = j < G ? fg[k] * G + j : (j == 16 ? H + fg[k] : (j == 17 ? H + nkv + fg[k] : 0));
-            fv1[k][x] = raw[src * HD + fi];
-            fv2[k][x] = raw[src * HD + fi + HALF];
-        }
-        const int pos = lds_s(&posr[fb[k]]);
-        fcs[k] = a.rope_cos[(long long)pos * HALF + fi];
-        fsn[k] = a.rope_sin[(long long)pos * HALF + fi];
-        // this lane's share of the row's partial sums of squares (<= 128 parts: d_model <= 4096
-        // in 32-column tiles), two fixed loads, summed in the arithmetic phase
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int q = lane + 64 * x;
-            fss[k][x] = a.ss_in[(long long)min(q, a.ss_in_parts - 1) * a.ss_stride + fb[k]];
-        }
-    };
-    auto finish_compute = [&](int k, int sl) {
-        const int b = fb[k], g = fg[k];
-        const float ssl = (lane < a.ss_in_parts ? fss[k][0] : 0.f) + (lane + 64 < a.ss_in_parts ? fss[k][1] : 0.f);
-        const float r = 1.0f / sqrtf(wave_sum(ssl) / (float)a.norm_dim + a.eps);
-#pragma unroll
-        for (int x = 0; x < FSL; ++x) {
-            const int j = wave + NSW * x;
-            if (j >= 18 || (j >= 16 && !fown[k])) continue;  // wave-uniform
-            T* dst = qsl[sl][j];
-            if (j < G || j == 16) {  // rotate, then normalise over the head
-                const float x1 = fv1[k][x] * r, x2 = fv2[k][x] * r;
-                const float o1 = x1 * fcs[k] - x2 * fsn[k], o2 = x1 * fsn[k] + x2 * fcs[k];
-                const float ss = wave_sum(act ? o1 * o1 + o2 * o2 : 0.f);
-                const float rr = 1.0f / sqrtf(ss / (float)HD + a.eps);
-                if (act) {
-                    const T t1 = from_f32<T>(o1 * rr), t2 = from_f32<T>(o2 * rr);
-                    dst[fi] = t1;
-                    dst[fi + HALF] = t2;
-                    if (j == 16) {  // the new key into the cache
-                        T* kd = (T*)a.kc + (((long long)b * nkv + g) * S + lds_s(&posr[b])) * HD;
-                        kd[fi] = t1;
-                        kd[fi + HALF] = t2;
-                    }
-                }
-            } else if (j == 17) {
-                float w1 = fv1[k][x] * r, w2 = fv2[k][x] * r;
-                if (a.vemb) {  // the layer's value embedding (wave-uniform)
-                    const ValueEmbed& ve = *a.vemb;
-                    const float gt = value_embed_gate<T>((const T*)ve.ve_gate, g, ve.ve_ch,
-                                                         ve.xin + (long long)b * ve.xin_stride, r, lane);
-                    const T* e = (const T*)ve.ve + ((long long)ve.tok[b] * nkv + g) * HD;
-                    w1 += gt * to_f32(e[fi]);
-                    w2 += gt * to_f32(e[fi + HALF]);
-                }
-                if (act) {
-                    const T t1 = from_f32<T>(w1), t2 = from_f32<T>(w2);
-                    dst[fi] = t1;
-                    dst[fi + HALF] = t2;
-                    // the new value into the (transposed) cache
-                    T* vd = (T*)a.vtc + ((long long)b * nkv + g) * HD * S + lds_s(&posr[b]);
-                    vd[(long long)fi * S] = t1;
-                    vd[(long long)(fi + HALF) * S] = t2;
-                }
-            } else if (act) {  // padding head
-                dst[fi] = from_f32<T>(0.f);
-                dst[fi + HALF] = from_f32<T>(0.f);
-            }
+        for (int ch = 0; ch < QBYTES / 1024; ++ch) {
+            const int byte = ch * 1024 + lane * 16;
+            const int h = min(byte / (HD * (int)sizeof(T)), G - 1);
+            const int within = byte % (HD * (int)sizeof(T));
+            __builtin_amdgcn_global_load_lds((gvoid*)(src + h * HD * sizeof(T) + within), (lvoid*)(dst + ch * 1024), 16, 0, 0);
         }
     };
     // ---- ring: stage t (t-th block in processing order) into slot t % NS.  A stage is 4 LK
@@ -641,8 +573,7 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
     // l of its load fetches the 16 bytes that land at 16 l (K: LDS chunk p = 64 c + l holds
     // key p / KCH, chunk (p % KCH) ^ (key % KCH); V^T: row d = p / 8, keys
     // 8 ((p % 8) ^ (d % 8)) .. + 8).  Streaming wave w loads chunks w LK .. w LK + LK - 1 of
-    // the stages it issues; the I/O wave loads all chunks of the first NS - 1 stages, so the
-    // streaming waves' own load counters hold only the QKV finish's loads meanwhile.
+    // the stages it issues; the I/O wave loads all chunks of the first NS - 1 stages.
     auto issue = [&](int t, const Cur& c, int c0, int nc) {
         if constexpr (STAGE) {
             unsigned char* sb = ring + (t % NS) * SBYTES;
@@ -664,26 +595,33 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
             }
         }
     };
-    // prologue: the streaming waves issue the QKV finish's loads of the first units; then
-    // (a CU returns its loads in order) the I/O wave issues the first NS - 1 stages while the
-    // streaming waves finish (their new keys and values go to the cache)
-    if (!io) {
-#pragma unroll
-        for (int k = 0; k < DEC_QSEG; ++k)
-            if (k < nq) finish_load(k);
-    }
-    __builtin_amdgcn_s_barrier();
+    // prologue (I/O wave): the first segments' queries, then the first NS - 1 stages; the
+    // queries (loaded first; loads complete in order) have landed before the barrier
     Cur ci = cstart();
+    if (io)
+        for (int k = 0; k < nq; ++k) {
+            Cur c;
+            seg_begin(c, k);
+            issue_q(c, k);
+        }
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t)
         if (t < nblk) {
             if (io) issue(t, ci, 0, NSW * LK);
             cadvance(ci);
         }
-    if (!io) {
-#pragma unroll
-        for (int k = 0; k < DEC_QSEG; ++k)
-            if (k < nq) finish_compute(k, k);
+    if (io) {
+        if constexpr (STAGE) {
+            constexpr int PIO = 2 * NSW * LK;  // loads of a whole stage
+            const int ns = min(NS - 1, nblk);
+            if (ns >= 4) NC_WAIT_VM(vm_cap(4 * PIO));
+            else if (ns == 3) NC_WAIT_VM(vm_cap(3 * PIO));
+            else if (ns == 2) NC_WAIT_VM(vm_cap(2 * PIO));
+            else if (ns == 1) NC_WAIT_VM(vm_cap(PIO));
+            else NC_WAIT_VM(0);
+        } else {
+            NC_WAIT_VM(0);
+        }
     }
     __syncthreads();
 
@@ -747,8 +685,6 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
         if (!io) {
             const int kbeg = (lds_s(&jlo[b]) + cc.j) * DEC_KB;
             const int kw = kbeg + 16 * wave;          // first key of this wave
-            const bool has_new = pos >= kw && pos < kw + 16;  // wave-uniform
-            const int sl = seg % DEC_QSEG;
             // operands: K rows of keys kw + col (A of S^T), V^T rows d = 16 dt + col at keys
             // kw + 4 grp .. + 3 (A of O^T)
             CT kf[DS];
@@ -771,17 +707,6 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
                 const T* vb = (const T*)a.vtc + u * HD * S + kw + 4 * grp;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) vf[dt] = *(const HT*)(vb + (long long)(16 * dt + col) * S);
-            }
-            if (has_new) {  // the new key and value from the finish, not from the cache
-                if (kw + col == pos) {
-#pragma unroll
-                    for (int s = 0; s < DS; ++s) kf[s] = *(const CT*)(&qsl[sl][16][8 * (4 * s + grp)]);
-                }
-                const int jn = pos - kw - 4 * grp;
-                if (jn >= 0 && jn < 4) {
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) vf[dt][jn] = qsl[sl][17][16 * dt + col];
-                }
             }
             // scores S^T: lane holds head col, keys kw + 4 grp + j
             f32x4 sc = zero_vec<f32x4>();
@@ -856,6 +781,9 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
                     outb[16 + hh] = l;
                 }
             }
+            // the next segment's queries were loaded by the I/O wave at an earlier unit's end
+            // (or in the prologue, already waited for): they land before the barrier
+            if (io && seg + 1 >= DEC_QSEG && t + 1 < nblk) NC_WAIT_VM(0);
             __syncthreads();  // outb is complete; the merge area is free again
             if (nsu > 1 && w == ws1) {  // owned, shared with earlier runs: merged after the loop
                 own_u = (int)u;
@@ -878,6 +806,13 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
                     pend_t = t;
                 }
             }
+            // this segment's slot is free (its queries are in the streaming waves' registers):
+            // it takes the queries of the segment DEC_QSEG later
+            if (io && seg + DEC_QSEG < nseg) {
+                Cur c;
+                seg_begin(c, seg + DEC_QSEG);
+                issue_q(c, seg % DEC_QSEG);
+            }
             // next unit
             if (t + 1 < nblk) {
                 ++seg;
@@ -890,14 +825,6 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
                 g = cc.g;
                 pos = lds_s(&posr[b]);
                 lo = (a.window < 0 || a.window >= pos) ? 0 : pos - a.window;
-                if (seg >= DEC_QSEG) {  // finish this unit now (more units than q slots)
-                    fb[0] = b; fg[0] = g; fown[0] = owns(cc);
-                    if (!io) {
-                        finish_load(0);
-                        finish_compute(0, seg % DEC_QSEG);
-                    }
-                    __syncthreads();
-                }
                 if (!io) load_q(seg % DEC_QSEG);
             }
             continue;

@@ -573,9 +573,15 @@ static hipError_t wide_t(const DecGemmArgs& args, hipStream_t st) {
     dim3 g(w.tiles, w.splits);
     if (a.M <= 64) NC_TLAUNCH((dec_gemm_wide_kernel<2, LO, EPI>), g, dim3(256), 0, st, a, w.splits, w.per);
     else NC_TLAUNCH((dec_gemm_wide_kernel<4, LO, EPI>), g, dim3(256), 0, st, a, w.splits, w.per);
-    if (w.splits > 1)
+    // the raw QKV product's slices are added by the QKV finish (dec_gemm_store_slices)
+    if (EPI != EPI_STORE && w.splits > 1)
         NC_TLAUNCH((dec_reduce_kernel<EPI>), dim3((a.N + 31) / 32, (a.M + 7) / 8), dim3(256), 0, st, a, w.splits);
     return hipGetLastError();
+}
+
+int dec_gemm_store_slices(DType dt, int M, int N, int K) {
+    if (dt != BF16 || M <= 32) return 0;
+    return wide_shape(EPI_STORE, M, false, N, K).splits;
 }
 
 long long dec_gemm_part_elems(DType dt, Epi epi, int M, int N, int K) {

@@ -99,6 +99,11 @@ int gemm_tile_n();             // N extent of one tile (ss_out parts = ceil(N / 
 int gemm_tile_k(DType dt);     // K granularity
 hipError_t launch_gemm(DType dt, Epi epi, const GemmArgs& a, hipStream_t st);
 
+// Decode projection of the raw QKV product (EPI_STORE): the number of K slices it leaves in
+// `part` (after the DEC_PART_CTRS counters, slice z at z M N) for the QKV finish to add, or 0
+// when it writes the sum to out_f32 itself.
+int dec_gemm_store_slices(DType dt, int M, int N, int K);
+
 // Decode projection (M <= 128 rows, K a multiple of 16) with the epilogue fused
 // (STORE / RELU2 / RESID / SOFTCAP).  Tiles are dec_gemm_tile_n() columns; RESID writes
 // ss_out[tile_n * ss_stride + m] (parts = ceil(N / tile_n)).
@@ -177,6 +182,26 @@ struct QkvPostArgs {
 };
 hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st);
 
+// QKV finish of a decode step (one token per row, at position lens[b]): adds the `splits`
+// K slices of the raw product part[z * z_stride + b * (H + 2 nkv) hd + ...] in slice order,
+// scales row b by its norm scale, rotates and QK-normalises the query and key heads, adds
+// the layer's value embedding to the value heads; writes q [B][H][hd] and the key / value
+// into this layer's cache at position lens[b].  One wave per (row, head slot).
+struct DecFinishArgs {
+    const float* part; long long z_stride;
+    const float* ss_in;
+    const int32_t* lens;
+    const float* rope_cos; const float* rope_sin;  // [max_seq][hd/2]
+    void* q;          // [B][H][hd]
+    void* kc;         // [B][nkv][S][hd]
+    void* vtc;        // [B][nkv][hd][S]
+    const ValueEmbed* vemb;  // device memory (null: none); tok[b], xin row b
+    int splits, B, H, hd, nkv, S;
+    int ss_in_parts, ss_stride, norm_dim;
+    float eps;
+};
+hipError_t launch_qkv_finish_decode(DType dt, const DecFinishArgs& a, hipStream_t st);
+
 // Causal attention of a prefill of T tokens per row: q [B*T][H][hd], the queries of row b
 // at positions off_b .. off_b + T - 1 (off_b = offs[b], or 0 when offs is null), the K/V
 // of this layer in the cache (positions 0 .. off_b + T - 1, nkv heads; query head h reads
@@ -187,19 +212,15 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
                                const int32_t* offs, hipStream_t st);
 
 // Decode attention for one step: one query per row at position lens[b] against keys
-// 0..lens[b] (or lens[b] - window .. lens[b] with a window >= 0) of each K/V head.  The
-// kernel first finishes the row's raw QKV product (norm scale, RoPE, QK-norm) and stores the
-// new key/value into the cache; the 64-key blocks of all (row, K/V head) units are split
-// into equal runs, one per workgroup; a unit cut by run boundaries leaves partial softmax
+// 0..lens[b] (or lens[b] - window .. lens[b] with a window >= 0) of each K/V head, the new
+// key/value already in the cache (qkv_finish_decode).  The 64-key blocks of all (row, K/V
+// head) units are split into equal runs, one per workgroup; a unit cut by run boundaries leaves partial softmax
 // states that the run holding its last block merges.  y: [B][H hd] stored blocked
 // (blocked_index, rows rounded up to 32).
 struct DecAttnArgs {
-    const float* qkv;   // raw product [B][(H+2 nkv) hd] fp32
-    const float* ss_in; int ss_in_parts, ss_stride, norm_dim;
-    float eps;
-    const float* rope_cos; const float* rope_sin;
-    const int32_t* lens;
-    void* kc; void* vtc;  // this layer's cache: K [B][nkv][S][hd], V^T [B][nkv][hd][S]
+    const void* q;        // finished queries [B][H][hd] (qkv_finish_decode)
+    const int32_t* lens;  // position of each row's new token, already in the cache
+    const void* kc; const void* vtc;  // this layer's cache: K [B][nkv][S][hd], V^T [B][nkv][hd][S]
     float* part;          // partial states [B nkv][max_slots][16 (hd + 2)]
     int32_t* flags;       // ready flags of the partial states [B nkv][max_slots]: zero before
                           // the first launch, and every launch leaves them zero
@@ -208,7 +229,6 @@ struct DecAttnArgs {
     int window;           // sliding window (< 0: the whole causal context)
     int max_slots;        // partial slots per unit, >= attn_decode_slots(B nkv, S)
     float scale_log2;     // set by the launcher
-    const ValueEmbed* vemb;  // device memory (null: none); tok[b], xin row b
 };
 // Keys a query can see at most: min(S, window + 1), or S without a window.
 int attn_decode_span(int S, int window);

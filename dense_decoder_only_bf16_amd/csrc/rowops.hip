@@ -266,6 +266,87 @@ hipError_t launch_qkv_post(DType dt, const QkvPostArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Decode step: one token per row at position lens[b].  Workgroup (4 head slots, row b),
+// one wave per slot; lane i < hd/2 holds the RoPE pair (i, i + hd/2).  The slices' loads
+// of a batch are all issued before they are added, in slice order.
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_finish_decode_kernel(DecFinishArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int j = 4 * blockIdx.x + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int b = blockIdx.y;
+    const int slots = a.H + 2 * a.nkv;
+    if (j >= slots) return;  // wave-uniform; no workgroup barrier below
+    const int half = a.hd / 2;
+    const bool act = lane < half;
+    const int i = act ? lane : 0;
+    const int pos = min(max(a.lens[b], 0), a.S - 1);  // capacity is checked by the host
+    const float* src = a.part + (long long)b * slots * a.hd + j * a.hd;
+    const bool is_q = j < a.H, is_k = !is_q && j < a.H + a.nkv;
+    float c = 0.f, sn = 0.f;
+    if (is_q || is_k) {
+        c = a.rope_cos[(long long)pos * half + i];
+        sn = a.rope_sin[(long long)pos * half + i];
+    }
+    float ssl = 0.f;
+    for (int q = lane; q < a.ss_in_parts; q += 64) ssl += a.ss_in[(long long)q * a.ss_stride + b];
+    float v1 = 0.f, v2 = 0.f;
+    for (int z0 = 0; z0 < a.splits; z0 += 8) {
+        float t1[8], t2[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const long long o = (long long)min(z0 + u, a.splits - 1) * a.z_stride;
+            t1[u] = src[o + i];
+            t2[u] = src[o + i + half];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            v1 += (z0 + u < a.splits) ? t1[u] : 0.f;
+            v2 += (z0 + u < a.splits) ? t2[u] : 0.f;
+        }
+    }
+    const float r = 1.0f / sqrtf(wave_sum(ssl) / (float)a.norm_dim + a.eps);
+    v1 = act ? v1 * r : 0.f;
+    v2 = act ? v2 * r : 0.f;
+    if (!is_q && !is_k) {  // value head: value embedding, then the transposed cache
+        const int g = j - a.H - a.nkv;
+        if (a.vemb) {
+            const ValueEmbed& ve = *a.vemb;
+            const float gt = value_embed_gate<T>((const T*)ve.ve_gate, g, ve.ve_ch,
+                                                 ve.xin + (long long)b * ve.xin_stride, r, lane);
+            const T* e = (const T*)ve.ve + ((long long)ve.tok[b] * a.nkv + g) * a.hd;
+            v1 += act ? gt * to_f32(e[i]) : 0.f;
+            v2 += act ? gt * to_f32(e[i + half]) : 0.f;
+        }
+        if (act) {
+            T* vt = (T*)a.vtc + ((long long)b * a.nkv + g) * a.hd * a.S + pos;
+            vt[(long long)i * a.S] = from_f32<T>(v1);
+            vt[(long long)(i + half) * a.S] = from_f32<T>(v2);
+        }
+        return;
+    }
+    // query / key head: rotate, then normalise over the head
+    const float o1 = v1 * c - v2 * sn;
+    const float o2 = v1 * sn + v2 * c;
+    const float rr = 1.0f / sqrtf(wave_sum(o1 * o1 + o2 * o2) / (float)a.hd + a.eps);
+    if (act) {
+        T* dst = is_q ? (T*)a.q + ((long long)b * a.H + j) * a.hd
+                      : (T*)a.kc + (((long long)b * a.nkv + (j - a.H)) * a.S + pos) * a.hd;
+        dst[i] = from_f32<T>(o1 * rr);
+        dst[i + half] = from_f32<T>(o2 * rr);
+    }
+}
+
+hipError_t launch_qkv_finish_decode(DType dt, const DecFinishArgs& a, hipStream_t st) {
+    if (a.nkv < 1 || a.H % a.nkv || a.hd > 128 || a.hd % 2 || a.B < 1 || a.splits < 1 || !a.part || !a.lens)
+        return hipErrorInvalidValue;
+    dim3 grid((a.H + 2 * a.nkv + 3) / 4, a.B);
+    if (dt == BF16)
+        hipLaunchKernelGGL(qkv_finish_decode_kernel<bf16>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(qkv_finish_decode_kernel<float>, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ argmax ----------
 // Lowest index wins ties; NaN never wins against a number.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {

@@ -456,27 +456,39 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const Ws& ws, const int32_t* to
         void* vtc = (char*)kv->vcache + l * per_layer;
         DecGemmArgs a{};
         a.M = B; a.eps = c.norm_eps; a.cap = c.softcap; a.ss_stride = ss; a.part = ws.dpart;
-        // QKV raw product, then norm scale + RoPE + QK-norm + cache write at lens[b]
+        // QKV raw product (its K slices left apart when split), then its finish: norm scale,
+        // RoPE + QK-norm at lens[b], the query heads to ws.q, the new key / value into the cache
         a.A = ws.act; a.W = L.wqkv; a.N = nqkv; a.K = d;
         a.out_f32 = ws.qkv; a.ldo = nqkv;
         if ((s = decode_gemm(kv, EPI_STORE, a, st)) != NC_OK) return s;
-        // QKV finish (norm scale, RoPE, QK-norm, cache write) + attention over the cache
+        {
+            const int sl = dec_gemm_store_slices(m->dt, B, nqkv, d);
+            DecFinishArgs fa{};
+            fa.part = sl ? ws.dpart + DEC_PART_CTRS : ws.qkv; fa.splits = sl ? sl : 1;
+            fa.z_stride = (long long)B * nqkv;
+            fa.ss_in = ws.ss_a; fa.ss_in_parts = ss_a_parts; fa.ss_stride = ss; fa.norm_dim = d;
+            fa.eps = c.norm_eps; fa.lens = kv->lens_dev; fa.rope_cos = m->rope_cos; fa.rope_sin = m->rope_sin;
+            fa.q = ws.q; fa.kc = kc; fa.vtc = vtc;
+            fa.vemb = (m->ex.on && m->ex.ve[l]) ? ws.ve_dev + l : nullptr;
+            fa.B = B; fa.H = H; fa.hd = hd; fa.nkv = nkv; fa.S = kv->S;
+            // timed with the projections: for 33 or more rows it also adds the product's K
+            // slices (bytes: the raw product read once, q / k / v written)
+            LAUNCH(timed(NC_KC_DECODE_GEMM, (double)B * nqkv * (4 + m->esz), 0, st,
+                         [&] { return launch_qkv_finish_decode(m->dt, fa, st); }));
+        }
+        // attention over the cache
         DecAttnArgs at{};
-        at.qkv = ws.qkv; at.ss_in = ws.ss_a; at.ss_in_parts = ss_a_parts; at.ss_stride = ss;
-        at.norm_dim = d; at.eps = c.norm_eps; at.rope_cos = m->rope_cos; at.rope_sin = m->rope_sin;
-        at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = ws.apart; at.flags = ws.actr;
+        at.q = ws.q; at.lens = kv->lens_dev; at.kc = kc; at.vtc = vtc; at.part = ws.apart; at.flags = ws.actr;
         at.y = ws.y;
         at.B = B; at.H = H; at.hd = hd; at.S = kv->S; at.nkv = nkv; at.max_slots = ws.apart_slots;
         at.window = m->windows[l];
-        at.vemb = (m->ex.on && m->ex.ve[l]) ? ws.ve_dev + l : nullptr;
         {   // bytes: the K/V read for every row (its visible positions, the new one
-            // included) of each K/V head, q/k/v in fp32, y out; flops 4 hd per
-            // (query head, key) pair
+            // included) of each K/V head, q in and y out; flops 4 hd per (query head, key) pair
             const double es = (double)m->esz;
             double keys = 0;
             for (int b = 0; b < B; ++b)
                 keys += at.window < 0 ? kv->lens_host[b] + 1 : std::min(kv->lens_host[b], at.window) + 1;
-            const double by = keys * nkv * hd * 2 * es + (double)B * nqkv * 4 + (double)B * H * hd * es;
+            const double by = keys * nkv * hd * 2 * es + 2.0 * B * H * hd * es;
             LAUNCH(timed(NC_KC_DECODE_ATTN, by, 4.0 * H * hd * keys, st,
                          [&] { return launch_attn_decode(m->dt, at, st); }));
         }

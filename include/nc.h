@@ -263,10 +263,10 @@ nc_status nc_sample(const float* logits_dev, int32_t B, int32_t V, float tempera
  * nc_timing_enable resets the totals.  Process-wide, not thread-safe.  Returns
  * NC_ERR_INVALID_ARG for an unknown class. */
 #define NC_KC_NONE 0
-#define NC_KC_DECODE_GEMM 1  /* decode projections: QKV, O, FC, PROJ, LM head            */
+#define NC_KC_DECODE_GEMM 1  /* decode projections: QKV (with its finish), O, FC, PROJ, LM head */
 #define NC_KC_PREFILL_GEMM 2 /* prefill projections                                       */
 #define NC_KC_PREFILL_ATTN 3 /* prefill attention                                         */
-#define NC_KC_DECODE_ATTN 4  /* decode attention: split + combine kernels, one operation   */
+#define NC_KC_DECODE_ATTN 4  /* decode attention                                          */
 typedef struct nc_timing {
     int64_t launches; /* timed operations (one decode attention = its two kernels)       */
     double ms;    /* summed kernel time of the launches (start/stop of each kernel)        */
