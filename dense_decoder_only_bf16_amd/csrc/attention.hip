@@ -350,9 +350,9 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 //
 // Queries.  The finished queries (qkv_finish_decode, which also put the new key and value
 // into the cache) of a unit's group are copied into LDS by a fifth wave, the I/O wave, with
-// direct-to-LDS loads: the first units' before the ring's first stages, a later unit's while
-// the run is still DEC_QSEG units before it.  The I/O wave also issues the ring's first
-// stages and does the run's output stores, so the streaming waves never wait on them.
+// direct-to-LDS loads: the first units' while the ring's first stages load, a later unit's
+// while the run is still DEC_QSEG units before it.  The I/O wave also does the run's output
+// stores, so the streaming waves never wait on them.
 //
 // End of a unit's run: the 4 waves' states merge in LDS; a unit inside one run is
 // normalised and stored to y; otherwise the state goes to the unit's partial slot and, at
@@ -360,7 +360,7 @@ hipError_t launch_attn_prefill(DType dt, int hd, const void* q, const void* kc, 
 // scope stores completed first, no cache-wide fence); the last to arrive merges the unit's
 // partials into y and resets the counter.  y is [B][H hd] stored blocked (blocked_index).
 constexpr int DEC_KB = 64;       // keys per block (one ring stage)
-constexpr int DEC_QSEG = 4;      // query slots in LDS (units whose queries are staged ahead)
+constexpr int DEC_QSEG = 2;      // query slots in LDS (units whose queries are staged ahead)
 constexpr int DEC_PER_MIN = 2;   // at least this many blocks per workgroup
 constexpr int DEC_MAX_WG = 256;  // workgroups per launch (one per CU)
 constexpr int DEC_MAX_B = 128;
@@ -374,9 +374,6 @@ int attn_decode_slots(int units, int S) {
     (void)units;
     return std::min(DEC_MAX_WG, (S / DEC_KB + DEC_PER_MIN - 1) / DEC_PER_MIN + 2);
 }
-
-// vmcnt waits take at most 63
-constexpr int vm_cap(int n) { return n > 63 ? 63 : n; }
 
 __device__ __forceinline__ f32x4 mma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
     typedef short s4 __attribute__((ext_vector_type(4)));
@@ -414,6 +411,7 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
     constexpr int PSZ = 16 * (HD + 2);
     constexpr int TPH = HD / 8;                             // merge threads per head, 8 features each
     constexpr int QBYTES = 16 * HD * (int)sizeof(T);        // a query slot: 16 heads
+    constexpr int PFB = (PSZ * 4 + 1023) / 1024 * 1024;     // LDS of a prefetched partial state
     static_assert(!STAGE || LK >= 1, "stage split");
 
     // One LDS array, carved into regions (a single LDS object leaves the compiler's wait
@@ -423,25 +421,29 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
     //   mrg   per streaming wave: o[16][OP], m[16], l[16] (fp32)
     //   outb  a unit's merged state: m[16], l[16], o[16][HD] (fp32)
     //   qsl   DEC_QSEG x 16 x HD elements: query heads of a group
+    //   pfb   a partial state of an earlier run, prefetched (PSZ floats)
     //   pre / jlo / posr / flag / desc  int tables
     constexpr int MRG_FL = 16 * OP + 32;
     constexpr int MRG_OFF = NS * SBYTES;
     constexpr int OUT_OFF = MRG_OFF + NSW * MRG_FL * 4;
     constexpr int QSL_OFF = OUT_OFF + PSZ * 4;
-    constexpr int INT_OFF = QSL_OFF + DEC_QSEG * QBYTES;
-    constexpr int LDS_BYTES = INT_OFF + (3 * DEC_MAX_B + 1 + 1 + 4) * 4;
+    constexpr int PFB_OFF = QSL_OFF + DEC_QSEG * QBYTES;
+    constexpr int INT_OFF = PFB_OFF + PFB;
+    constexpr int LDS_BYTES = INT_OFF + (3 * DEC_MAX_B + 1 + 2 + 4) * 4;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(QSL_OFF % 16 == 0 && QBYTES % 1024 == 0, "query slots: whole 1 KB loads");
+
     __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
     unsigned char* const ring = lds;
     float (*const mrg)[MRG_FL] = (float (*)[MRG_FL])(lds + MRG_OFF);
     float* const outb = (float*)(lds + OUT_OFF);
     T (*const qsl)[16][HD] = (T (*)[16][HD])(lds + QSL_OFF);
+    float* const pfb = (float*)(lds + PFB_OFF);
     int* const pre = (int*)(lds + INT_OFF);  // DEC_MAX_B + 1
     int* const jlo = pre + DEC_MAX_B + 1;     // DEC_MAX_B
     int* const posr = jlo + DEC_MAX_B;        // DEC_MAX_B
-    int* const flag = posr + DEC_MAX_B;       // 1
-    int* const desc = flag + 1;               // 4: first unit, its block; last unit, its block
+    int* const flag = posr + DEC_MAX_B;       // 2: a partial state never came; states prefetched
+    int* const desc = flag + 2;               // 4: first unit, its block; last unit, its block
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -573,7 +575,7 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
     // l of its load fetches the 16 bytes that land at 16 l (K: LDS chunk p = 64 c + l holds
     // key p / KCH, chunk (p % KCH) ^ (key % KCH); V^T: row d = p / 8, keys
     // 8 ((p % 8) ^ (d % 8)) .. + 8).  Streaming wave w loads chunks w LK .. w LK + LK - 1 of
-    // the stages it issues; the I/O wave loads all chunks of the first NS - 1 stages.
+    // every stage.
     auto issue = [&](int t, const Cur& c, int c0, int nc) {
         if constexpr (STAGE) {
             unsigned char* sb = ring + (t % NS) * SBYTES;
@@ -595,8 +597,9 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
             }
         }
     };
-    // prologue (I/O wave): the first segments' queries, then the first NS - 1 stages; the
-    // queries (loaded first; loads complete in order) have landed before the barrier
+    // prologue: the I/O wave loads the first segments' queries; then (a CU returns its
+    // loads in order, so the queries are not queued behind a stage) the streaming waves
+    // issue their shares of the first NS - 1 stages while the I/O wave waits for the queries
     Cur ci = cstart();
     if (io)
         for (int k = 0; k < nq; ++k) {
@@ -604,25 +607,16 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
             seg_begin(c, k);
             issue_q(c, k);
         }
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t)
         if (t < nblk) {
-            if (io) issue(t, ci, 0, NSW * LK);
+            if (!io) issue(t, ci, wave * LK, LK);
             cadvance(ci);
         }
-    if (io) {
-        if constexpr (STAGE) {
-            constexpr int PIO = 2 * NSW * LK;  // loads of a whole stage
-            const int ns = min(NS - 1, nblk);
-            if (ns >= 4) NC_WAIT_VM(vm_cap(4 * PIO));
-            else if (ns == 3) NC_WAIT_VM(vm_cap(3 * PIO));
-            else if (ns == 2) NC_WAIT_VM(vm_cap(2 * PIO));
-            else if (ns == 1) NC_WAIT_VM(vm_cap(PIO));
-            else NC_WAIT_VM(0);
-        } else {
-            NC_WAIT_VM(0);
-        }
-    }
+    if (io) NC_WAIT_VM(0);
+    // (a full barrier: the streaming waves also wait for their prologue stages, which
+    // measured faster overall than entering the loop with them in flight)
     __syncthreads();
 
     // ---- main loop
@@ -647,6 +641,25 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
     // streaming waves at the next barrier)
     long long pend_flag = -1;
     int pend_t = 0;
+    // The run's first unit, processed last, is owned by this run and shared with earlier
+    // runs when the run starts inside it and holds its last block.  Those runs mostly store
+    // their partial states early (a run's last unit comes first in its order), so the I/O
+    // wave polls the flag of the first of them (slot 0) during the loop and, once it is set,
+    // copies that state into pfb with device-scope direct-to-LDS loads.
+    //   pf_st: -1 nothing to prefetch, 0 poll next, 1 poll in flight, 2 state loading
+    int pf_st = -1, pf_fv = 0;
+    const int32_t* pf_fl = nullptr;
+    const unsigned char* pf_src = nullptr;
+    if (io && jf > 0) {
+        Cur c;
+        seg_begin(c, nseg - 1);
+        if (owns(c) && wg_of(unit_first(c)) < w) {
+            const long long uf = (long long)c.b * nkv + c.g;
+            pf_fl = a.flags + uf * a.max_slots;
+            pf_src = (const unsigned char*)(a.part + uf * a.max_slots * PSZ);
+            pf_st = 0;
+        }
+    }
     auto set_flag = [&]() {
         wait_stores_complete();
         if (lane == 0) __hip_atomic_store(a.flags + pend_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -656,19 +669,9 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
     for (int t = 0; t < nblk; ++t) {
         if (io && pend_flag >= 0 && t >= pend_t + 2) set_flag();
         if constexpr (STAGE) {
-            // wait for this wave's loads of stage t: the I/O wave issued stages 0 .. NS - 2,
-            // the streaming waves the later ones (later stages of the same issuer may stay
+            // wait for this wave's loads of stage t (its loads of the later stages may stay
             // in flight)
-            if (t <= NS - 2) {
-                if (io) {
-                    constexpr int PIO = 2 * NSW * LK;  // loads of a whole stage
-                    const int ahead = min(NS - 2, nblk - 1) - t;
-                    if (ahead >= 3) NC_WAIT_VM(3 * PIO);
-                    else if (ahead == 2) NC_WAIT_VM(2 * PIO);
-                    else if (ahead == 1) NC_WAIT_VM(PIO);
-                    else NC_WAIT_VM(0);
-                }
-            } else if (!io) {
+            if (!io) {
                 const int ahead = min(NS - 2, nblk - 1 - t);
                 if (ahead >= 3) NC_WAIT_VM(3 * 2 * LK);
                 else if (ahead == 2) NC_WAIT_VM(2 * 2 * LK);
@@ -680,6 +683,27 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
                 if (!io) issue(t + NS - 1, ci, wave * LK, LK);
                 cadvance(ci);
             }
+        }
+        if (io && pf_st == 1) {  // the flag polled one block ago
+            if (__shfl(pf_fv, 0, 64) != 0) {
+                if (pend_flag < 0) {  // (so that no wait of this wave holds up the loads)
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    constexpr int NCH = (PSZ * 4 + 1023) / 1024;
+#pragma unroll
+                    for (int ch = 0; ch < NCH; ++ch) {
+                        const int byte = min(ch * 1024 + lane * 16, PSZ * 4 - 16);
+                        __builtin_amdgcn_global_load_lds((gvoid*)(pf_src + byte), (lvoid*)((unsigned char*)pfb + ch * 1024),
+                                                         16, 0, NC_CPOL_DEVICE);
+                    }
+                    pf_st = 2;
+                }
+            } else {
+                pf_st = 0;
+            }
+        }
+        if (io && pf_st == 0) {
+            if (lane == 0) pf_fv = __hip_atomic_load(pf_fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pf_st = 1;
         }
         const long long u = (long long)b * nkv + g;
         if (!io) {
@@ -751,7 +775,7 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) *(f32x4*)(&mw[col * OP + 16 * dt + 4 * grp]) = o_run[dt];
             }
-            __syncthreads();
+            lds_barrier();
             const int q0 = unit_first(cc);
             const int ws0 = wg_of(q0), ws1 = wg_of(q0 + cc.nb - 1);
             const int nsu = ws1 - ws0 + 1;  // runs holding blocks of this unit
@@ -784,7 +808,7 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
             // the next segment's queries were loaded by the I/O wave at an earlier unit's end
             // (or in the prologue, already waited for): they land before the barrier
             if (io && seg + 1 >= DEC_QSEG && t + 1 < nblk) NC_WAIT_VM(0);
-            __syncthreads();  // outb is complete; the merge area is free again
+            lds_barrier();  // outb is complete; the merge area is free again
             if (nsu > 1 && w == ws1) {  // owned, shared with earlier runs: merged after the loop
                 own_u = (int)u;
                 own_ws0 = ws0;
@@ -799,8 +823,10 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
                         *(CT*)((T*)a.y + blocked_index(b, (g * G + h2) * HD + f0, H * HD)) = yo;
                     }
                 } else {
-                    float* ps = a.part + (u * a.max_slots + (w - ws0)) * PSZ;
-                    for (int e = lane; e < 32 + G * HD; e += 64) store_device(ps + e, outb[e]);
+                    // 16-byte device-scope stores: few instructions, so that the wave does not
+                    // queue long behind the ring's loads for vector-memory slots
+                    const __amdgpu_buffer_rsrc_t ps = buffer_rsrc(a.part + (u * a.max_slots + (w - ws0)) * PSZ, PSZ * 4);
+                    for (int e = lane; e < (32 + G * HD) / 4; e += 64) store_device4(ps, 16 * e, *(const f32x4*)&outb[4 * e]);
                     if (pend_flag >= 0) set_flag();  // (a run shares at most two units)
                     pend_flag = u * a.max_slots + (w - ws0);
                     pend_t = t;
@@ -837,50 +863,88 @@ __global__ __launch_bounds__(320) void attn_decode_kernel(DecAttnArgs a) {
     // with this run's state (outb) into y, and clear the flags for the next launch
     if (io && pend_flag >= 0) set_flag();  // the state is visible device-wide before its flag
     if (own_u < 0) return;  // workgroup-uniform
-    if (io) return;
     const long long u = own_u;
     const int nprev = own_n - 1;  // slots 0 .. nprev - 1
     int32_t* fl = a.flags + u * a.max_slots;
-    if (tid < nprev) {  // bounded wait: the states were written long before, in practice at once
-        int v = 0;
-        for (int it = 0; it < (1 << 22); ++it) {
-            v = __hip_atomic_load(fl + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (v) break;
-            __builtin_amdgcn_s_sleep(2);
-        }
-        if (!v) flag[0] = 1;  // never set: the output is made NaN rather than wrong
+    if (io) {
+        if (pf_st == 2) NC_WAIT_VM(0);  // the prefetched state has landed in pfb
+        if (lane == 0) flag[1] = pf_st == 2 ? 1 : 0;
     }
     __syncthreads();
+    const int npf = lds_s(&flag[1]);
+    if (npf < nprev) {  // workgroup-uniform: wait for the other states (flags set once each
+        // state is visible; they were written at the start of those runs, or at their end)
+        if (tid >= npf && tid < nprev) {  // bounded wait
+            int v = 0;
+            for (int it = 0; it < (1 << 22); ++it) {
+                v = __hip_atomic_load(fl + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (v) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            if (!v) flag[0] = 1;  // never set: the output is made NaN rather than wrong
+        }
+        __syncthreads();
+    }
+    if (io) return;
+    // merge the earlier runs' states with this run's (outb) into y; clear the flags for the
+    // next launch
     const bool bad = flag[0] != 0;
     const int hh = tid / TPH, d0 = 8 * (tid % TPH);
     if (hh < G) {
         const int bb = (int)(u / nkv), gg = (int)(u % nkv);
         const float* pu = a.part + u * a.max_slots * PSZ;
+        float mt[4], lt[4], ot[4][8];
+        auto fetch = [&](int s0) {  // 4 slots per batch of independent loads
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int sl = min(s0 + x, nprev - 1);
+                f32x4 o0, o1;
+                if (sl < npf) {  // prefetched (wave-uniform)
+                    mt[x] = pfb[hh];
+                    lt[x] = pfb[16 + hh];
+                    o0 = *(const f32x4*)&pfb[32 + hh * HD + d0];
+                    o1 = *(const f32x4*)&pfb[32 + hh * HD + d0 + 4];
+                } else {
+                    const float* ps = pu + (long long)sl * PSZ;
+                    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(ps, PSZ * 4);
+                    mt[x] = load_device(ps + hh);
+                    lt[x] = load_device(ps + 16 + hh);
+                    o0 = load_device4(r, 4 * (32 + hh * HD + d0));
+                    o1 = load_device4(r, 4 * (32 + hh * HD + d0 + 4));
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ot[x][e] = o0[e];
+                    ot[x][4 + e] = o1[e];
+                }
+            }
+        };
         float M = outb[hh];
-        for (int s = 0; s < nprev; ++s) M = fmaxf(M, load_device(pu + (long long)s * PSZ + hh));
-        const float mr = (M == -INFINITY) ? 0.f : M;
-        float o[8];
-        const float f_own = fast_exp2(outb[hh] - mr);
-        float l = f_own * outb[16 + hh];
+        float l = 0.f, o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = f_own * outb[32 + hh * HD + d0 + e];
-        for (int s0 = 0; s0 < nprev; s0 += 4) {  // 4 slots per batch of independent loads
-            float mt[4], lt[4], ot[4][8];
+        for (int e = 0; e < 8; ++e) o[e] = 0.f;
+        // running merge: scale what is summed so far whenever the maximum grows
+        auto absorb = [&](float m, float lv, const float* ov) {
+            const float Mn = fmaxf(M, m);
+            const float mr = (Mn == -INFINITY) ? 0.f : Mn;
+            const float fo = fast_exp2(M - mr), fn = fast_exp2(m - mr);
+            l = l * fo + lv * fn;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const float* ps = pu + (long long)min(s0 + x, nprev - 1) * PSZ;
-                mt[x] = load_device(ps + hh);
-                lt[x] = load_device(ps + 16 + hh);
+            for (int e = 0; e < 8; ++e) o[e] = o[e] * fo + ov[e] * fn;
+            M = Mn;
+        };
+        {
+            float ov[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ot[x][e] = load_device(ps + 32 + hh * HD + d0 + e);
-            }
+            for (int e = 0; e < 8; ++e) ov[e] = outb[32 + hh * HD + d0 + e];
+            M = -INFINITY;
+            absorb(outb[hh], outb[16 + hh], ov);
+        }
+        for (int s0 = 0; s0 < nprev; s0 += 4) {
+            fetch(s0);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const float f = s0 + x < nprev ? fast_exp2(mt[x] - mr) : 0.f;
-                l += f * lt[x];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] += f * ot[x][e];
-            }
+            for (int x = 0; x < 4; ++x)
+                if (s0 + x < nprev) absorb(mt[x], lt[x], ot[x]);
         }
         const float inv = bad ? __builtin_nanf("") : 1.0f / l;
         CT yo;

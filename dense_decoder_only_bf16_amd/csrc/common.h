@@ -10,6 +10,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -135,6 +136,34 @@ __device__ __forceinline__ void wait_stores_complete() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     NC_WAIT_VM_ALL();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Workgroup barrier for LDS data: this wave's LDS accesses complete, then s_barrier.  Unlike
+// __syncthreads() it leaves the wave's outstanding global loads alone, so the direct-to-LDS
+// loads of later pipeline stages stay in flight across it (their own waits are explicit).
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maximum
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Cache-policy operand of a direct-to-LDS load that reads at device scope (sc1: the bits the
+// compiler gives a relaxed agent-scope atomic load), for data another workgroup stored with
+// store_device.
+#define NC_CPOL_DEVICE 16
+
+// 16-byte device-scope accesses (sc1) through a buffer resource: base must be the same in
+// every lane (it goes to scalar registers), the byte offset may differ per lane.  Word 3 of
+// the resource selects the 32-bit data format for raw (untyped) access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_device4(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, NC_CPOL_DEVICE);
+}
+__device__ __forceinline__ f32x4 load_device4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, NC_CPOL_DEVICE));
 }
 
 typedef __attribute__((address_space(1))) void gvoid;  // global memory, for direct-to-LDS loads
