@@ -361,7 +361,8 @@ static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant) {
 // stages ahead.  The LM head (softcap; N = vocab gives hundreds of column tiles) runs its
 // whole K in one workgroup and its epilogue here.  The other products split K into slices
 // so that there are a few hundred workgroups; their fp32 partial products go to `part` and
-// dec_reduce_kernel adds the slices in a fixed order and runs the epilogue.
+// dec_reduce4_kernel (or, for the raw QKV product, the QKV finish) adds the slices in a
+// fixed order and runs the epilogue.
 constexpr int WBN = 128;  // columns per workgroup
 constexpr int WKC = 2;    // 16-deep steps per LDS stage
 constexpr int WNS = 6;    // stages in the ring
@@ -369,10 +370,12 @@ constexpr int WNS = 6;    // stages in the ring
 struct WideShape {
     int tiles, splits, per;  // column tiles, K slices, 16-deep steps per slice
 };
-// Slices: as many as fill one round of workgroup slots (256 CUs, one or two resident
-// workgroups each by LDS size), at least 2 and each slice at least 2 stages long.  A
-// workgroup's ring runs at a fixed latency-bound rate, so a second round of workgroups
-// costs more than the larger partial sums of a finer split.
+// Slices: a workgroup streams its A slice (the activation rows, both parts when
+// compensated) and its W tile at a roughly fixed rate, and each slice leaves an fp32 partial
+// product that is written and read back once more.  The slice count S minimises the
+// estimate  (A / S + W / (tiles S)) / 50 GB/s  +  2 S M N 4 / 5 TB/s  over 2 <= S, each
+// slice at least 2 stages long and every workgroup in one round of slots (256 CUs, one or
+// two resident workgroups each by LDS size).  The LM head (softcap) is never split.
 static WideShape wide_shape(Epi epi, int M, bool lo, int N, int K) {
     WideShape w;
     const int ksteps = K / 16;  // >= 4 (K >= 64)
@@ -385,9 +388,18 @@ static WideShape wide_shape(Epi epi, int M, bool lo, int N, int K) {
     const int fm = M <= 64 ? 2 : 4;
     const int stage_kb = WKC * (fm * (lo ? 2 : 1) + 4);
     const int slots = 256 * std::max(1, 160 / (WNS * stage_kb));
-    int s = slots / w.tiles;
-    s = std::max(2, std::min(s, ksteps / (2 * WKC)));
-    w.per = (ksteps + s - 1) / s;
+    const int smax = std::max(2, std::min(slots / w.tiles, ksteps / (2 * WKC)));
+    const double a_bytes = (double)M * K * 2 * (lo ? 2 : 1), w_bytes = (double)N * K * 2;
+    int best = 2;
+    double best_t = 1e30;
+    for (int s = 2; s <= smax; ++s) {
+        const double t = (a_bytes / s + w_bytes / ((double)w.tiles * s)) / 50e9 + 2.0 * s * M * N * 4 / 5e12;
+        if (t < best_t) {
+            best_t = t;
+            best = s;
+        }
+    }
+    w.per = (ksteps + best - 1) / best;
     w.splits = (ksteps + w.per - 1) / w.per;  // every slice non-empty, >= 2
     return w;
 }
@@ -513,54 +525,72 @@ __global__ __launch_bounds__(256) void dec_gemm_wide_kernel(DecGemmArgs p, int s
     }
 }
 
-// Split-K finish: workgroup (32 columns, 8 rows), wave w finishes rows w and w + 4: the
-// slices' partial products are added in slice order, then the row epilogue runs.
+// Split-K finish of the wide products, four columns per lane: workgroup (256 columns,
+// 4 rows), wave w finishes row 4 blockIdx.y + w.  Each lane adds its 4 columns' slices in
+// slice order with 16-byte loads (8 slices per batch of independent loads), then runs the
+// row epilogue on them (N is a multiple of 4):
+//   RELU2  relu(r_m c)^2 -> bf16 hi / lo (blocked)
+//   RESID  x += c, bf16 hi / lo copies of x (blocked), per-row sums of x^2 over each 32
+//          columns (the same partial sums the other decode kernels leave)
 template <int EPI>
-__global__ __launch_bounds__(256) void dec_reduce_kernel(DecGemmArgs p, int splits) {
-    constexpr int RPW = 2;
+__global__ __launch_bounds__(256) void dec_reduce4_kernel(DecGemmArgs p, int splits) {
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 8;
-    const int nn = min(n0 + (lane & 31), p.N - 1);
+    const int m = blockIdx.y * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (m >= p.M) return;  // wave-uniform; no workgroup barrier below
+    const int n = blockIdx.x * 256 + 4 * lane;
+    const bool ok = n < p.N;
+    const int nc = ok ? n : 0;
     const long long slice = (long long)p.M * p.N;
-    float v[RPW], pre[RPW];
+    const float* src = p.part + (long long)m * p.N + nc;
+    f32x4 x_old = zero_vec<f32x4>();
+    if (EPI == EPI_RESID) x_old = *(const f32x4*)(p.out_f32 + (long long)m * p.ldo + nc);
+    float pre = 0.f;
+    if (EPI == EPI_RELU2)
+        for (int q = lane; q < p.ss_in_parts; q += 64) pre += p.ss_in[(long long)q * p.ss_stride + m];
+    f32x4 v = zero_vec<f32x4>();
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+        f32x4 t[8];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        v[i] = 0.f;
-        pre[i] = 0.f;
-    }
-    for (int s0 = 0; s0 < splits; s0 += 8) {  // 8 slices per batch of independent loads
-        float t[8][RPW];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int i = 0; i < RPW; ++i) {
-                const int m = min(m0 + wave + 4 * i, p.M - 1);
-                const int s = min(s0 + u, splits - 1);
-                t[u][i] = p.part[s * slice + (long long)m * p.N + nn];
-            }
+        for (int u = 0; u < 8; ++u) t[u] = *(const f32x4*)(src + min(s0 + u, splits - 1) * slice);
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int i = 0; i < RPW; ++i) v[i] += (s0 + u < splits) ? t[u][i] : 0.f;
+            if (s0 + u < splits) v += t[u];
     }
-    if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
-        for (int q = lane; q < p.ss_in_parts; q += 64)
+    const long long ob = blocked_index(m, nc, p.N);  // 4 consecutive bf16 (n % 4 == 0)
+    if (EPI == EPI_RELU2) {
+        const float r = 1.0f / sqrtf(wave_sum(pre) / (float)p.K + p.eps);
+        bf16x4 hi, lo;
 #pragma unroll
-            for (int i = 0; i < RPW; ++i)
-                pre[i] += p.ss_in[(long long)q * p.ss_stride + min(m0 + wave + 4 * i, p.M - 1)];
-    } else if (EPI == EPI_RESID) {
-#pragma unroll
-        for (int i = 0; i < RPW; ++i) pre[i] = p.out_f32[(long long)min(m0 + wave + 4 * i, p.M - 1) * p.ldo + nn];
-    }
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int m = m0 + wave + 4 * i;
-        if (m < p.M) {  // wave-uniform
-            float r = 1.f;
-            if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) r = 1.0f / sqrtf(wave_sum(pre[i]) / (float)p.K + p.eps);
-            dec_row_epilogue<bf16, EPI>(p, m, n0, 32, lane, lane < 32 ? v[i] : 0.f, r, pre[i]);
+        for (int e = 0; e < 4; ++e) {
+            const float t = fmaxf(v[e] * r, 0.f);
+            hi[e] = (bf16)(t * t);
+            lo[e] = (bf16)(t * t - (float)hi[e]);
         }
+        if (ok) {
+            *(bf16x4*)((bf16*)p.out_t + ob) = hi;
+            if (p.out_lo) *(bf16x4*)((bf16*)p.out_lo + ob) = lo;
+        }
+    } else {  // EPI_RESID
+        const long long o = (long long)m * p.ldo + nc;
+        f32x4 xn;
+        float sq = 0.f;
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xn[e] = ok ? resid_value(p.rx, o + e, x_old[e], v[e]) : 0.f;
+            hi[e] = (bf16)xn[e];
+            lo[e] = (bf16)(xn[e] - (float)hi[e]);
+            sq += xn[e] * xn[e];
+        }
+        if (ok) {
+            *(f32x4*)(p.out_f32 + o) = xn;
+            *(bf16x4*)((bf16*)p.out_t + ob) = hi;
+            if (p.out_lo) *(bf16x4*)((bf16*)p.out_lo + ob) = lo;
+        }
+        sq += __shfl_xor(sq, 1, 64);  // the 8 lanes of a 32-column tile
+        sq += __shfl_xor(sq, 2, 64);
+        sq += __shfl_xor(sq, 4, 64);
+        if ((lane & 7) == 0 && ok) p.ss_out[(long long)(n / 32) * p.ss_stride + m] = sq;
     }
 }
 
@@ -574,8 +604,11 @@ static hipError_t wide_t(const DecGemmArgs& args, hipStream_t st) {
     if (a.M <= 64) NC_TLAUNCH((dec_gemm_wide_kernel<2, LO, EPI>), g, dim3(256), 0, st, a, w.splits, w.per);
     else NC_TLAUNCH((dec_gemm_wide_kernel<4, LO, EPI>), g, dim3(256), 0, st, a, w.splits, w.per);
     // the raw QKV product's slices are added by the QKV finish (dec_gemm_store_slices)
-    if (EPI != EPI_STORE && w.splits > 1)
-        NC_TLAUNCH((dec_reduce_kernel<EPI>), dim3((a.N + 31) / 32, (a.M + 7) / 8), dim3(256), 0, st, a, w.splits);
+    if ((EPI == EPI_RELU2 || EPI == EPI_RESID) && w.splits > 1) {
+        if (a.N % 4) return hipErrorInvalidValue;
+        NC_TLAUNCH((dec_reduce4_kernel<EPI == EPI_RELU2 ? EPI_RELU2 : EPI_RESID>), dim3((a.N + 255) / 256, (a.M + 3) / 4),
+                   dim3(256), 0, st, a, w.splits);
+    }
     return hipGetLastError();
 }
 
