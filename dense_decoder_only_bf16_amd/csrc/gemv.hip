@@ -415,8 +415,10 @@ __global__ __launch_bounds__(256) void dec_gemm_wide_kernel(DecGemmArgs p, int s
     static_assert(BPS % 4 == 0, "stage must split evenly over the 4 waves");
     static_assert((WNS - 2) * BPW <= 63, "vmcnt range");
     constexpr int STAGE = BPS * 512;       // bf16 elements per stage
-    __shared__ __attribute__((aligned(1024))) bf16 lds[WNS * STAGE];
-    __shared__ float rs[32 * FM];
+    // one LDS object (the ring, then the LM head's row scales): with a second one the
+    // compiler cannot tell its reads from the ring's in-flight loads and waits for them all
+    __shared__ __attribute__((aligned(1024))) bf16 lds[WNS * STAGE + 64 * FM];
+    float* const rs = (float*)(lds + WNS * STAGE);  // 32 FM row scales
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
