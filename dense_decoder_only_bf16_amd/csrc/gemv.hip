@@ -20,6 +20,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "finish.h"
 #include "kernels.h"
 
 namespace nc {
@@ -74,8 +75,12 @@ __device__ __forceinline__ void dec_row_epilogue(const DecGemmArgs& p, int m, in
 // caches are coherent), and each workgroup waits for its stores to complete before it
 // counts itself, so no cache-wide write-back or invalidation is needed; such fences
 // would flush the whole L2 of a die under the other workgroups' weight streams.
-template <typename T, int FM, int NW, int U, int EPI, bool LO>
-__global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
+// FIN (QKV, one row block): the tile's raw rows are stored at device scope, and the last
+// workgroup to store a tile of a head (an arrival counter per head slot, which it sets back
+// to zero) finishes that head for every row (qkv_finish_head), one wave per row.
+struct NoFinish {};
+template <typename T, int FM, int NW, int U, int EPI, bool LO, bool FIN, typename FA>
+__device__ __forceinline__ void dec_gemm_body(const DecGemmArgs& p, const FA& f) {
     typedef typename Chunk<T>::type CT;
     constexpr int BM = 32 * FM, BN = 32, TP = BN + 1;
     __shared__ float red[NW * BM * TP];
@@ -215,6 +220,31 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
         }
     }
     __syncthreads();
+    if constexpr (FIN) {
+        const int nn = n0 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int ml = wave + NW * i;
+            if (ml < rows && lane < BN && nn < p.N)
+                store_device(p.out_f32 + (long long)(m0 + ml) * p.ldo + nn, red[ml * TP + lane]);
+        }
+        wait_stores_complete();  // the tile is visible device-wide before it is counted
+        __syncthreads();
+        const int hd = f.hd, head = n0 / hd;
+        if (tid == 0) {
+            const int before = __hip_atomic_fetch_add(f.head_ctr + head, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_in = before == hd / BN - 1;
+            if (before == hd / BN - 1) __hip_atomic_store(f.head_ctr + head, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!last_in) return;  // workgroup-uniform
+        const int half = hd / 2, ii = lane < half ? lane : 0;
+        for (int b = wave; b < p.M; b += NW) {
+            const float* src = p.out_f32 + (long long)b * p.ldo + head * hd;
+            qkv_finish_head<T>(f, b, head, lane, load_device(src + ii), load_device(src + ii + half));
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int ml = wave + NW * i;
@@ -224,6 +254,15 @@ __global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
             dec_row_epilogue<T, EPI>(p, m0 + ml, n0, BN, lane, lane < BN ? red[ml * TP + lane] : 0.f, r, pre[i]);
         }
     }
+}
+
+template <typename T, int FM, int NW, int U, int EPI, bool LO>
+__global__ __launch_bounds__(NW * 64) void dec_gemm_kernel(DecGemmArgs p) {
+    dec_gemm_body<T, FM, NW, U, EPI, LO, false>(p, NoFinish{});
+}
+template <typename T, int NW, int U>
+__global__ __launch_bounds__(NW * 64) void dec_gemm_fin_kernel(DecGemmArgs p, DecFinishArgs f) {
+    dec_gemm_body<T, 1, NW, U, EPI_STORE, false, true>(p, f);
 }
 
 // LM head of a decode step with at most 32 rows (softcap epilogue).  One wave per 32-column
@@ -311,7 +350,7 @@ static int dec_ksplit(int M, int N, int K) {
 
 // Launch shape.  `variant` picks alternative (waves, steps-in-flight) choices for tuning.
 template <typename T, int EPI, bool LO>
-static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant) {
+static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant, const DecFinishArgs* fin) {
     const unsigned gx = (a.N + DEC_BN - 1) / DEC_BN;
     const int fm = a.M <= 32 ? 1 : (a.M <= 64 ? 2 : 4);
     const unsigned gy = (a.M + 32 * fm - 1) / (32 * fm);
@@ -327,6 +366,11 @@ static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant) {
     // wave's weight steps in flight at once (one memory round trip), except for the wide
     // LM head
     if (fm == 1 && variant == 0 && (ks > 1 || a.K <= 1024) && a.N <= 16384) variant = 2;
+    if (fin) {  // QKV with its finish (EPI_STORE, one row block)
+        if (variant == 2) NC_TLAUNCH((dec_gemm_fin_kernel<T, 8, 8>), g, dim3(512), 0, st, a, *fin);
+        else NC_TLAUNCH((dec_gemm_fin_kernel<T, 8, 4>), g, dim3(512), 0, st, a, *fin);
+        return hipGetLastError();
+    }
     if (fm == 1) {
         if (variant == 1) NC_DG(1, 16, 4);
         else if (variant == 2) NC_DG(1, 8, 8);
@@ -635,11 +679,22 @@ long long dec_gemm_part_elems(DType dt, Epi epi, int M, int N, int K) {
 
 int dec_gemm_tile_n() { return DEC_BN; }
 
+bool dec_gemm_fuses_finish(DType dt, int M, int hd, int slots) {
+    (void)dt;
+    return M <= 32 && hd % DEC_BN == 0 && slots <= DEC_FIN_SLOTS;
+}
+
 template <typename T>
-static hipError_t dec_dt(Epi epi, const DecGemmArgs& a, hipStream_t st, int variant) {
+static hipError_t dec_dt(Epi epi, const DecGemmArgs& a, hipStream_t st, int variant, const DecFinishArgs* fin) {
     // compensated operands exist for the MLP products and the LM head (bf16 only)
     const bool lo = a.A_lo != nullptr;
     if (lo && (sizeof(T) != 2 || epi == EPI_STORE)) return hipErrorInvalidValue;
+    if (fin) {
+        if (epi != EPI_STORE || !fin->head_ctr || fin->B != a.M || a.N != (fin->H + 2 * fin->nkv) * fin->hd ||
+            a.ldo != a.N || !dec_gemm_fuses_finish(sizeof(T) == 2 ? BF16 : F32, a.M, fin->hd, fin->H + 2 * fin->nkv))
+            return hipErrorInvalidValue;
+        return dec_t<T, EPI_STORE, false>(a, st, variant, fin);
+    }
     if (sizeof(T) == 2 && a.M > 32) {
         switch (epi) {
             case EPI_STORE: return wide_t<EPI_STORE, false>(a, st);
@@ -650,20 +705,24 @@ static hipError_t dec_dt(Epi epi, const DecGemmArgs& a, hipStream_t st, int vari
         }
     }
     switch (epi) {
-        case EPI_STORE: return dec_t<T, EPI_STORE, false>(a, st, variant);
+        case EPI_STORE: return dec_t<T, EPI_STORE, false>(a, st, variant, nullptr);
         case EPI_RELU2:
-            return lo ? dec_t<T, EPI_RELU2, sizeof(T) == 2>(a, st, variant) : dec_t<T, EPI_RELU2, false>(a, st, variant);
+            return lo ? dec_t<T, EPI_RELU2, sizeof(T) == 2>(a, st, variant, nullptr)
+                      : dec_t<T, EPI_RELU2, false>(a, st, variant, nullptr);
         case EPI_RESID:
-            return lo ? dec_t<T, EPI_RESID, sizeof(T) == 2>(a, st, variant) : dec_t<T, EPI_RESID, false>(a, st, variant);
+            return lo ? dec_t<T, EPI_RESID, sizeof(T) == 2>(a, st, variant, nullptr)
+                      : dec_t<T, EPI_RESID, false>(a, st, variant, nullptr);
         case EPI_SOFTCAP:
-            return lo ? dec_t<T, EPI_SOFTCAP, sizeof(T) == 2>(a, st, variant) : dec_t<T, EPI_SOFTCAP, false>(a, st, variant);
+            return lo ? dec_t<T, EPI_SOFTCAP, sizeof(T) == 2>(a, st, variant, nullptr)
+                      : dec_t<T, EPI_SOFTCAP, false>(a, st, variant, nullptr);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t st, int variant) {
+hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t st, int variant,
+                           const DecFinishArgs* fin) {
     if (a.M < 1 || a.M > 128 || a.K % 16) return hipErrorInvalidValue;
-    return dt == BF16 ? dec_dt<bf16>(epi, a, st, variant) : dec_dt<float>(epi, a, st, variant);
+    return dt == BF16 ? dec_dt<bf16>(epi, a, st, variant, fin) : dec_dt<float>(epi, a, st, variant, fin);
 }
 
 }  // namespace nc

@@ -109,6 +109,7 @@ int dec_gemm_store_slices(DType dt, int M, int N, int K);
 // ss_out[tile_n * ss_stride + m] (parts = ceil(N / tile_n)).
 // Decode activations (A, A_lo and the dtype outputs out_t, out_lo) are stored blocked with
 // rows rounded up to 32 (blocked_index); the fp32 outputs are row-major with stride ldo.
+struct DecFinishArgs;
 struct DecGemmArgs {  // pointers first, then 4-byte fields: no padding (120 bytes)
     const void* A;              // blocked [ceil(M/32)][K/16][32][16] dtype
     const void* W;              // blocked weight, Npad = N rounded up to 32 rows
@@ -131,7 +132,11 @@ int dec_gemm_tile_n();
 constexpr int DEC_PART_CTRS = 64;
 // Elements of DecGemmArgs::part that a product of this shape needs (0: none).
 long long dec_gemm_part_elems(DType dt, Epi epi, int M, int N, int K);
-hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t st, int variant = 0);
+// fin (EPI_STORE only, dec_gemm_fuses_finish): the QKV finish runs in the product's
+// epilogue: the last workgroup to store a column tile of a head finishes that head for every
+// row (fin->part, splits and z_stride unused: the raw product is out_f32).
+hipError_t launch_dec_gemm(DType dt, Epi epi, const DecGemmArgs& a, hipStream_t st, int variant = 0,
+                           const DecFinishArgs* fin = nullptr);
 
 // x[m] = scale0 norm(wte[tok[m]]) (fp32, row-major), act[m] = dtype copy (row-major, or
 // blocked with rows rounded up to 32 when `blocked`), ss[m] = sum(x^2); with the later
@@ -196,11 +201,17 @@ struct DecFinishArgs {
     void* kc;         // [B][nkv][S][hd]
     void* vtc;        // [B][nkv][hd][S]
     const ValueEmbed* vemb;  // device memory (null: none); tok[b], xin row b
+    int32_t* head_ctr;       // fused finish (launch_dec_gemm with a finish): one arrival
+                             // counter per head slot, zero before the launch and left zero
     int splits, B, H, hd, nkv, S;
     int ss_in_parts, ss_stride, norm_dim;
     float eps;
 };
 hipError_t launch_qkv_finish_decode(DType dt, const DecFinishArgs& a, hipStream_t st);
+// Whether the raw QKV product of M rows can finish in its own epilogue (launch_dec_gemm
+// with `fin`): at most 32 rows, head_dim a multiple of 32, at most DEC_FIN_SLOTS head slots.
+constexpr int DEC_FIN_SLOTS = 256;
+bool dec_gemm_fuses_finish(DType dt, int M, int hd, int slots);
 
 // Causal attention of a prefill of T tokens per row: q [B*T][H][hd], the queries of row b
 // at positions off_b .. off_b + T - 1 (off_b = offs[b], or 0 when offs is null), the K/V

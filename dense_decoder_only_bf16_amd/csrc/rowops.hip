@@ -9,6 +9,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "finish.h"
 #include "kernels.h"
 
 namespace nc {
@@ -274,21 +275,10 @@ __global__ __launch_bounds__(256) void qkv_finish_decode_kernel(DecFinishArgs a)
     const int lane = threadIdx.x & 63;
     const int j = 4 * blockIdx.x + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int b = blockIdx.y;
-    const int slots = a.H + 2 * a.nkv;
-    if (j >= slots) return;  // wave-uniform; no workgroup barrier below
+    if (j >= a.H + 2 * a.nkv) return;  // wave-uniform; no workgroup barrier below
     const int half = a.hd / 2;
-    const bool act = lane < half;
-    const int i = act ? lane : 0;
-    const int pos = min(max(a.lens[b], 0), a.S - 1);  // capacity is checked by the host
-    const float* src = a.part + (long long)b * slots * a.hd + j * a.hd;
-    const bool is_q = j < a.H, is_k = !is_q && j < a.H + a.nkv;
-    float c = 0.f, sn = 0.f;
-    if (is_q || is_k) {
-        c = a.rope_cos[(long long)pos * half + i];
-        sn = a.rope_sin[(long long)pos * half + i];
-    }
-    float ssl = 0.f;
-    for (int q = lane; q < a.ss_in_parts; q += 64) ssl += a.ss_in[(long long)q * a.ss_stride + b];
+    const int i = lane < half ? lane : 0;
+    const float* src = a.part + (long long)b * (a.H + 2 * a.nkv) * a.hd + j * a.hd;
     float v1 = 0.f, v2 = 0.f;
     for (int z0 = 0; z0 < a.splits; z0 += 8) {
         float t1[8], t2[8];
@@ -304,36 +294,7 @@ __global__ __launch_bounds__(256) void qkv_finish_decode_kernel(DecFinishArgs a)
             v2 += (z0 + u < a.splits) ? t2[u] : 0.f;
         }
     }
-    const float r = 1.0f / sqrtf(wave_sum(ssl) / (float)a.norm_dim + a.eps);
-    v1 = act ? v1 * r : 0.f;
-    v2 = act ? v2 * r : 0.f;
-    if (!is_q && !is_k) {  // value head: value embedding, then the transposed cache
-        const int g = j - a.H - a.nkv;
-        if (a.vemb) {
-            const ValueEmbed& ve = *a.vemb;
-            const float gt = value_embed_gate<T>((const T*)ve.ve_gate, g, ve.ve_ch,
-                                                 ve.xin + (long long)b * ve.xin_stride, r, lane);
-            const T* e = (const T*)ve.ve + ((long long)ve.tok[b] * a.nkv + g) * a.hd;
-            v1 += act ? gt * to_f32(e[i]) : 0.f;
-            v2 += act ? gt * to_f32(e[i + half]) : 0.f;
-        }
-        if (act) {
-            T* vt = (T*)a.vtc + ((long long)b * a.nkv + g) * a.hd * a.S + pos;
-            vt[(long long)i * a.S] = from_f32<T>(v1);
-            vt[(long long)(i + half) * a.S] = from_f32<T>(v2);
-        }
-        return;
-    }
-    // query / key head: rotate, then normalise over the head
-    const float o1 = v1 * c - v2 * sn;
-    const float o2 = v1 * sn + v2 * c;
-    const float rr = 1.0f / sqrtf(wave_sum(o1 * o1 + o2 * o2) / (float)a.hd + a.eps);
-    if (act) {
-        T* dst = is_q ? (T*)a.q + ((long long)b * a.H + j) * a.hd
-                      : (T*)a.kc + (((long long)b * a.nkv + (j - a.H)) * a.S + pos) * a.hd;
-        dst[i] = from_f32<T>(o1 * rr);
-        dst[i + half] = from_f32<T>(o2 * rr);
-    }
+    qkv_finish_head<T>(a, b, j, lane, v1, v2);
 }
 
 hipError_t launch_qkv_finish_decode(DType dt, const DecFinishArgs& a, hipStream_t st) {

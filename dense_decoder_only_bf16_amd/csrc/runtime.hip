@@ -131,6 +131,7 @@ struct Ws {
     void* u_lo = nullptr;     // products): x - bf16(x) after attention, u - bf16(u)
     float* apart = nullptr;   // decode attention partial states
     int32_t* actr = nullptr;  // decode attention ready flags, one per (row, K/V head) and slot
+    int32_t* fctr = nullptr;  // decode QKV finish in the product's epilogue: arrival counters per head slot
     float* dpart = nullptr;   // decode projections: split-K arrival counters, then partials
     float* x0 = nullptr;      // later-version blocks: stream before layer 0's scaling [M][d]
     float* xb = nullptr;      // and the backout source [M][d]
@@ -257,6 +258,7 @@ Ws ws_layout(const nc_model* m, int B, int S, long long M, void* base) {
     w.apart = (float*)take(w.apart_elems * 4);
     w.actr_elems = (long long)units * w.apart_slots;
     w.actr = (int32_t*)take(w.actr_elems * 4);
+    w.fctr = (int32_t*)take(DEC_FIN_SLOTS * 4);
     {   // split-K partials of the decode projections (M = batch rows)
         const int hqv = c.n_head * c.head_dim, nq = (c.n_head + 2 * c.n_kv_head) * c.head_dim;
         w.dpart_elems = std::max({dec_gemm_part_elems(m->dt, EPI_STORE, B, nq, c.d_model),
@@ -283,6 +285,7 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
     // the attention ready flags and the split-K arrival counters start at zero, and every
     // launch leaves them so
     hipError_t e = hipMemset(w.actr, 0, (size_t)w.actr_elems * 4);
+    if (e == hipSuccess) e = hipMemset(w.fctr, 0, DEC_FIN_SLOTS * 4);
     if (e == hipSuccess && w.dpart) e = hipMemset(w.dpart, 0, DEC_PART_CTRS * 4);
     if (e == hipSuccess && kv->m->ex.on) {  // the per-layer blocks that decode kernels read through pointers
         const nc_config& c = kv->m->cfg;
@@ -393,7 +396,7 @@ double visible_pairs(long long off, long long T, int w) {
 // Algorithmic bytes of a decode projection: weights, activations (both parts of a
 // compensated operand), and the epilogue's outputs (RESID also reads x; low parts where
 // written); flops 2 M N K of the model (the extra MFMAs of the low part are not counted).
-nc_status decode_gemm(nc_kv* kv, Epi epi, const DecGemmArgs& a, hipStream_t st) {
+nc_status decode_gemm(nc_kv* kv, Epi epi, const DecGemmArgs& a, hipStream_t st, const DecFinishArgs* fin = nullptr) {
     const double es = (double)kv->m->esz, M = a.M, N = a.N, K = a.K;
     double out = 0;
     if (epi == EPI_STORE || epi == EPI_SOFTCAP) out = M * N * 4;
@@ -402,7 +405,7 @@ nc_status decode_gemm(nc_kv* kv, Epi epi, const DecGemmArgs& a, hipStream_t st) 
     if (a.out_lo) out += M * N * es;
     const double bytes = N * K * es + M * K * es * (a.A_lo ? 2 : 1) + out;
     LAUNCH(timed(NC_KC_DECODE_GEMM, bytes, 2 * M * N * K, st,
-                 [&] { return launch_dec_gemm(kv->m->dt, epi, a, st); }, 2));
+                 [&] { return launch_dec_gemm(kv->m->dt, epi, a, st, 0, fin); }, 2));
     return NC_OK;
 }
 
@@ -456,11 +459,12 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const Ws& ws, const int32_t* to
         void* vtc = (char*)kv->vcache + l * per_layer;
         DecGemmArgs a{};
         a.M = B; a.eps = c.norm_eps; a.cap = c.softcap; a.ss_stride = ss; a.part = ws.dpart;
-        // QKV raw product (its K slices left apart when split), then its finish: norm scale,
-        // RoPE + QK-norm at lens[b], the query heads to ws.q, the new key / value into the cache
+        // QKV product and its finish (norm scale, RoPE + QK-norm at lens[b], the query heads
+        // to ws.q, the new key / value into the cache): for at most 32 rows in the product's
+        // epilogue; otherwise the product leaves its K slices apart and the finish kernel
+        // adds them
         a.A = ws.act; a.W = L.wqkv; a.N = nqkv; a.K = d;
         a.out_f32 = ws.qkv; a.ldo = nqkv;
-        if ((s = decode_gemm(kv, EPI_STORE, a, st)) != NC_OK) return s;
         {
             const int sl = dec_gemm_store_slices(m->dt, B, nqkv, d);
             DecFinishArgs fa{};
@@ -470,11 +474,17 @@ nc_status enqueue_decode(nc_model* m, nc_kv* kv, const Ws& ws, const int32_t* to
             fa.eps = c.norm_eps; fa.lens = kv->lens_dev; fa.rope_cos = m->rope_cos; fa.rope_sin = m->rope_sin;
             fa.q = ws.q; fa.kc = kc; fa.vtc = vtc;
             fa.vemb = (m->ex.on && m->ex.ve[l]) ? ws.ve_dev + l : nullptr;
+            fa.head_ctr = ws.fctr;
             fa.B = B; fa.H = H; fa.hd = hd; fa.nkv = nkv; fa.S = kv->S;
-            // timed with the projections: for 33 or more rows it also adds the product's K
-            // slices (bytes: the raw product read once, q / k / v written)
-            LAUNCH(timed(NC_KC_DECODE_GEMM, (double)B * nqkv * (4 + m->esz), 0, st,
-                         [&] { return launch_qkv_finish_decode(m->dt, fa, st); }));
+            if (dec_gemm_fuses_finish(m->dt, B, hd, H + 2 * nkv)) {
+                if ((s = decode_gemm(kv, EPI_STORE, a, st, &fa)) != NC_OK) return s;
+            } else {
+                if ((s = decode_gemm(kv, EPI_STORE, a, st)) != NC_OK) return s;
+                // timed with the projections: it also adds the product's K slices (bytes: the
+                // raw product read once, q / k / v written)
+                LAUNCH(timed(NC_KC_DECODE_GEMM, (double)B * nqkv * (4 + m->esz), 0, st,
+                             [&] { return launch_qkv_finish_decode(m->dt, fa, st); }));
+            }
         }
         // attention over the cache
         DecAttnArgs at{};
@@ -1141,6 +1151,7 @@ nc_status nc_decode_step_static(nc_model* m, const int32_t* tokens, int32_t B, n
         // the array keeps the last call's contents: the attention ready flags and the
         // split-K arrival counters must start at zero
         LAUNCH(launch_zero_i32(w.actr, w.actr_elems, st));
+        LAUNCH(launch_zero_i32(w.fctr, DEC_FIN_SLOTS, st));
         if (w.dpart) LAUNCH(launch_zero_i32((int32_t*)w.dpart, DEC_PART_CTRS, st));
         t_untimed = true;
         s = enqueue_decode(m, kv, w, tokens, logits, st);
