@@ -115,9 +115,18 @@ KERNEL_NAMES = {"decode_gemm": "dec_gemm_kernel (decode projections)",
 # (FETCH_SIZE, WRITE_SIZE) scaled by a plain-copy calibration, valid only for the kernel
 # sources they were taken with (hash of the listed files); otherwise the report says null.
 TRAFFIC = {
-    ("d12", "decode_gemm"): {"bytes_per_launch": 5.602e6, "profile": "profiles/d12_pmc_traffic.md",
-                             "sources": ("csrc/gemv.hip", "csrc/common.h", "csrc/kernels.h"),
-                             "sha": "cbc11e4fb6d22557"},
+    ("d20", "prefill_gemm"): {"bytes_per_launch": 2.9474e+09, "profile": "profiles/d20_prefill_pmc_traffic.md",
+                             "sources": ('csrc/gemm.hip', 'csrc/common.h', 'csrc/kernels.h'),
+                             "sha": "9fc4209b4a7c2e7f"},
+    ("d26", "prefill_gemm"): {"bytes_per_launch": 2.0919e+09, "profile": "profiles/d26_prefill_pmc.md",
+                             "sources": ('csrc/gemm.hip', 'csrc/common.h', 'csrc/kernels.h'),
+                             "sha": "9fc4209b4a7c2e7f"},
+    ("d30", "decode_attn"): {"bytes_per_launch": 8.5875e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
+                             "sources": ('csrc/attention.hip', 'csrc/common.h', 'csrc/kernels.h'),
+                             "sha": "21200aaa87186870"},
+    ("d30", "decode_gemm"): {"bytes_per_launch": 4.7365e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
+                             "sources": ('csrc/gemv.hip', 'csrc/rowops.hip', 'csrc/finish.h', 'csrc/common.h', 'csrc/kernels.h'),
+                             "sha": "6bcad75aafc8e281"},
 }
 
 
