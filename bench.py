@@ -105,9 +105,9 @@ CLASSES = (  # (timing class, name, bound); classes without a launch in the work
     ("NC_KC_PREFILL_GEMM", "prefill_gemm", "mfma"),
     ("NC_KC_PREFILL_ATTN", "prefill_attn", "mfma"),
 )
-KERNEL_NAMES = {"decode_gemm": "dec_gemm_kernel (decode projections)",
+KERNEL_NAMES = {"decode_gemm": "dec_gemm_wide_kernel + dec_reduce4_kernel / dec_gemm_kernel (decode projections)",
                 "decode_attn": "attn_decode_kernel (decode attention)",
-                "prefill_gemm": "gemm_bf16_kernel (prefill projections)",
+                "prefill_gemm": "gemm_bf16_kernel / gemm_bf16_comp_kernel (prefill projections)",
                 "prefill_attn": "attn_prefill_kernel"}
 
 
@@ -115,9 +115,15 @@ KERNEL_NAMES = {"decode_gemm": "dec_gemm_kernel (decode projections)",
 # (FETCH_SIZE, WRITE_SIZE) scaled by a plain-copy calibration, valid only for the kernel
 # sources they were taken with (hash of the listed files); otherwise the report says null.
 TRAFFIC = {
-    ("d20", "prefill_gemm"): {"bytes_per_launch": 2.9474e+09, "profile": "profiles/d20_prefill_pmc_traffic.md",
+    ("d20", "prefill_gemm"): {"bytes_per_launch": 2.9474e+09, "profile": "profiles/d20_pmc_traffic.md",
                              "sources": ('csrc/gemm.hip', 'csrc/common.h', 'csrc/kernels.h'),
                              "sha": "9fc4209b4a7c2e7f"},
+    ("d20", "decode_gemm"): {"bytes_per_launch": 2.0057e+07, "profile": "profiles/d20_pmc_traffic.md",
+                             "sources": ('csrc/gemv.hip', 'csrc/rowops.hip', 'csrc/finish.h', 'csrc/common.h', 'csrc/kernels.h'),
+                             "sha": "6bcad75aafc8e281"},
+    ("d20", "decode_attn"): {"bytes_per_launch": 7.2360e+07, "profile": "profiles/d20_pmc_traffic.md",
+                             "sources": ('csrc/attention.hip', 'csrc/common.h', 'csrc/kernels.h'),
+                             "sha": "21200aaa87186870"},
     ("d26", "prefill_gemm"): {"bytes_per_launch": 2.0919e+09, "profile": "profiles/d26_prefill_pmc.md",
                              "sources": ('csrc/gemm.hip', 'csrc/common.h', 'csrc/kernels.h'),
                              "sha": "9fc4209b4a7c2e7f"},
