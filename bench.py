@@ -123,13 +123,13 @@ TRAFFIC = {
                              "sha": "6bcad75aafc8e281"},
     ("d20", "decode_attn"): {"bytes_per_launch": 7.2360e+07, "profile": "profiles/d20_pmc_traffic.md",
                              "sources": ('csrc/attention.hip', 'csrc/common.h', 'csrc/kernels.h'),
-                             "sha": "21200aaa87186870"},
+                             "sha": "57be915b2a74c7f7"},
     ("d26", "prefill_gemm"): {"bytes_per_launch": 2.0919e+09, "profile": "profiles/d26_prefill_pmc.md",
                              "sources": ('csrc/gemm.hip', 'csrc/common.h', 'csrc/kernels.h'),
                              "sha": "9fc4209b4a7c2e7f"},
     ("d30", "decode_attn"): {"bytes_per_launch": 8.5875e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
                              "sources": ('csrc/attention.hip', 'csrc/common.h', 'csrc/kernels.h'),
-                             "sha": "21200aaa87186870"},
+                             "sha": "57be915b2a74c7f7"},
     ("d30", "decode_gemm"): {"bytes_per_launch": 4.7365e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
                              "sources": ('csrc/gemv.hip', 'csrc/rowops.hip', 'csrc/finish.h', 'csrc/common.h', 'csrc/kernels.h'),
                              "sha": "6bcad75aafc8e281"},

@@ -1,5 +1,5 @@
-// Causal multi-query attention for gfx950: a flash-style prefill kernel and a split-context
-// decode kernel with a combine kernel.  Both write the attention output y in the layout the
+// Causal multi-query attention for gfx950: a flash-style prefill kernel and a decode kernel
+// over balanced runs of 64-key blocks.  Both write the attention output y in the layout the
 // O product reads: MFMA-blocked (kernels.h, blocked_index) for bf16, row-major for fp32
 // prefill.
 //

@@ -4,21 +4,25 @@
 // Schedule of one layer (the block structure of the yelogs.com launch write-up's
 // architecture answer; plain pre-norm residual reading):
 //   QKV product (raw, fp32)  -> QKV finish: row norm scale, RoPE, QK-norm, KV-cache write
-//   attention (prefill: flash kernel; decode: split-context + combine, with the QKV
-//   finish done inside the split kernel)
+//   attention (prefill: flash kernel; decode: one kernel over balanced runs of 64-key
+//   blocks that merges rows cut between runs itself)
 //   O product  + residual epilogue (x += ., dtype copy of x, per-row sum of squares)
 //   FC product + norm scale + ReLU^2 epilogue
 //   PROJ product + residual epilogue
 // then the LM head with norm scale and softcap.  Prefill uses the 256x256 MFMA tile with
 // the epilogues fused (the QKV finish is a separate row kernel).  Decode (M = batch rows)
-// uses the weight-streaming decode product (K split over the waves of one workgroup) with
-// the elementwise epilogues fused and the QKV finish inside the attention kernel; the LM
-// head's launch also advances the row lengths.  The whole decode step is
+// uses the weight-streaming decode products with the elementwise epilogues fused (at most
+// 32 rows: K split over the waves of one workgroup, the QKV finish in the QKV product's
+// epilogue; more rows: 128-column workgroups with K split across workgroups, a split-K
+// finish kernel, and a separate QKV finish kernel); the LM head's launch also advances the
+// row lengths.  The whole decode step is
 // captured once per (token buffer, logit buffer) pair as a HIP graph and replayed.
 // The L2 caches of the chip's dies are not coherent with each other, so a device-wide
 // fence costs a write-back and invalidation of a die's L2.  Reductions across workgroups
-// are separate launches, except the decode down-projection's K slices, which pass through
-// device-scope stores and loads and an arrival counter, with no fence and no waiting.
+// are separate launches, except where data passes through device-scope stores and loads
+// and an arrival counter or ready flag, with no fence: the decode down-projection's K
+// slices, the fused QKV finish's head tiles, and the decode attention's partial states
+// (whose merging workgroup waits, bounded, only for runs dispatched before it).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

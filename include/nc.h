@@ -208,7 +208,8 @@ nc_status nc_decode_step(nc_model* m, const int32_t* tokens_dev, int32_t B, nc_k
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same step as
  * nc_decode_step, with the same arguments, requirements, results (bitwise) and errors, but
  * its workspace (residual stream, activations, raw QKV product, attention partial states
- * and ready flags, split-K partial sums and arrival counters) lives in a file-scope device
+ * and ready flags, split-K partial sums and arrival counters, the QKV finish's per-head
+ * arrival counters) lives in a file-scope device
  * array of NC_STATIC_SCRATCH_BYTES that every GPU the library runs on holds until the
  * process ends, not in memory of the kv object; kernels are launched one by one (no graph
  * is captured).  The call allocates nothing (no hipMalloc, hipFree or allocating library

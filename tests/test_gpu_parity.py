@@ -507,8 +507,8 @@ def test_bf16_split_k_decode(B):
 @pytest.mark.parametrize("B", [3, 40])
 def test_bf16_gqa_decode_many_rows(B):
     """Grouped-query decode at mixed context lengths up to 600 (B = 40: 80 (row, K/V head)
-    units, so the split kernel runs 4 waves and merges them in LDS; B = 3: one block per
-    wave), 2 teacher-forced steps; every row is checked against the oracle."""
+    units, many of them cut between workgroup runs and merged; B = 3: units spread over many
+    short runs), 2 teacher-forced steps; every row is checked against the oracle."""
     shape = replace(GQA_8_2, n_layer=1, max_seq=640)
     w = make_weights(shape, seed=42)
     orc = OracleModel(shape, w)
@@ -577,8 +577,8 @@ def test_bf16_window_pattern_prefill(short):
 @pytest.mark.parametrize("B", [3, 40])
 def test_bf16_window_pattern_decode_many_rows(B):
     """SSSL decode with a 100-key short window at mixed context lengths up to 600: the
-    split kernel launches only the chunks the window touches (B = 40: 80 units, 4 waves
-    merged in LDS; B = 3: one block per wave); every row is checked."""
+    decode attention counts only the blocks the window touches (B = 40: 80 units; B = 3:
+    units spread over many short runs); every row is checked."""
     wins = nc.layer_windows("SSSL", SSSL.n_layer, 100)
     w = make_weights(SSSL, seed=54)
     orc = OracleModel(SSSL, w, windows=wins)
