@@ -50,20 +50,44 @@ template <typename T> struct KT {
 
 constexpr int TBM = 256, TBN = 256;  // workgroup tile
 
-// (m0, n0, tile column index) of this workgroup's tile.
-__device__ __forceinline__ void tile_coords(const GemmArgs& p, int& m0, int& n0, int& tn) {
+// (m0, n0, tile column index) of this workgroup's tile, and its K tiles [kt0, kt1) of nk.
+// The first tiles - p.tail workgroups take whole tiles, numbered XCD-aware: workgroup ids
+// go round-robin over the 8 XCDs, so each XCD gets a contiguous run of tile numbers and its
+// L2 sees whole row groups.  The last 2 p.tail workgroups, dispatched last, take one K half
+// each of the last p.tail tiles (tail split, GemmArgs): workgroups 2 s and 2 s + 1 of them
+// share tail tile s (`slot`; -1 for a whole tile).  `even`: the halves split at an even K
+// tile.
+struct TileWork {
+    int m0, n0, tn, kt0, kt1, slot;
+};
+__device__ __forceinline__ TileWork tile_work(const GemmArgs& p, int nk, bool even) {
     constexpr int GM = 8;
     const int ntn = (p.N + TBN - 1) / TBN, ntm = (p.M + TBM - 1) / TBM;
-    const int total = ntn * ntm;
+    const int whole = ntn * ntm - p.tail;
     const int pid = blockIdx.x;
-    const int xcd = pid % 8, loc = pid / 8, q8 = total / 8, r8 = total % 8;
-    const int t = (xcd < r8) ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
+    TileWork w;
+    w.kt0 = 0;
+    w.kt1 = nk;
+    w.slot = -1;
+    int t;
+    if (pid < whole) {
+        const int xcd = pid % 8, loc = pid / 8, q8 = whole / 8, r8 = whole % 8;
+        t = (xcd < r8) ? xcd * (q8 + 1) + loc : r8 * (q8 + 1) + (xcd - r8) * q8 + loc;
+    } else {  // a K half of a tail tile
+        const int v = pid - whole;
+        w.slot = v / 2;
+        t = whole + w.slot;
+        const int mid = even ? (nk / 2) & ~1 : nk / 2;
+        if (v % 2 == 0) w.kt1 = mid;
+        else w.kt0 = mid;
+    }
     const int grp = t / (GM * ntn), first_m = grp * GM;
     const int gsize = min(ntm - first_m, GM);
     const int tm = first_m + (t % (GM * ntn)) % gsize;
-    tn = (t % (GM * ntn)) / gsize;
-    n0 = tn * TBN;
-    m0 = tm * TBM;
+    w.tn = (t % (GM * ntn)) / gsize;
+    w.n0 = w.tn * TBN;
+    w.m0 = tm * TBM;
+    return w;
 }
 
 // Row scales r_m of the tile (RELU2 / SOFTCAP), computed once into LDS.
@@ -157,6 +181,75 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, f32x16 (&acc)[2
     }
 }
 
+// Tail split join (all 512 threads; after the main loop, with the ring free).  For a whole
+// tile (slot < 0) it adds nothing.  Of the two halves of tail tile `slot`, the first to
+// arrive stores its accumulators (device scope, thread-major so each 16-byte store is
+// coalesced), waits for the stores and sets the ready flag, and is done (false); the other
+// waits for the flag (bounded: the first is already running), adds the stored sums to its
+// own and clears both words for the next launch (true).  A flag that never comes makes the
+// tile NaN rather than wrong.  Every workgroup runs the same add, a whole tile's through a
+// zero-size buffer (its loads return 0 without touching memory): one straight path keeps
+// the accumulators in place for the epilogue instead of merging two versions of them.
+__device__ __forceinline__ bool tail_join(const GemmArgs& p, int slot, f32x16 (&acc)[4][2], int* lflag) {
+    const int tid = threadIdx.x;
+    float* part = p.tail_part + (long long)(slot < 0 ? 0 : slot) * GEMM_TAIL_FLOATS;
+    int32_t* ctr = p.tail_ctr + 2 * (slot < 0 ? 0 : slot);
+    bool bad = false;
+    if (slot >= 0) {
+        if (tid == 0) lflag[0] = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
+        __syncthreads();
+        if (lflag[0]) {
+            const __amdgpu_buffer_rsrc_t w = buffer_rsrc(part, GEMM_TAIL_FLOATS * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        f32x4 v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+                        store_device4(w, 16 * (((i * 2 + j) * 4 + q) * 512 + tid), v);
+                    }
+            wait_stores_complete();  // the sums are visible device-wide before the flag
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+        if (tid == 0) {
+            int v = 0;
+            for (int it = 0; it < (1 << 22); ++it) {
+                v = __hip_atomic_load(ctr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (v) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            lflag[1] = v ? 0 : 1;
+            __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        bad = lflag[1] != 0;
+        __syncthreads();  // every thread has read lflag before the epilogue reuses the LDS
+    }
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(part, slot < 0 ? 0 : GEMM_TAIL_FLOATS * 4);
+    const float keep = bad ? __builtin_nanf("") : 1.f;
+    // A quarter of the sums at a time (32 registers in flight), so the accumulators and the
+    // loads fit beside each other.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v = load_device4(r, 16 * (((i * 2 + j) * 4 + q) * 512 + tid));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = acc[i][j][4 * q + e] * keep + v[e];
+            }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return true;
+}
+
 // ---------------------------------------------------------------------- bf16 ----------
 
 template <int EPI>
@@ -174,13 +267,13 @@ void gemm_bf16_kernel(GemmArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / 4, wn = wave % 4;       // 2 x 4 waves, 128 x 64 each
     const int l32 = lane & 31, hh = lane >> 5;
-    int m0, n0, tn;
-    tile_coords(p, m0, n0, tn);
     const int ksteps = p.K / 16;
     // A compensated product runs twice as many K tiles: tile 2k takes A's columns of tile
     // k, tile 2k + 1 the same columns of A_lo, both against the same weight block.
     const bool comp = p.A_lo != nullptr;
-    const int nk = comp ? 2 * (p.K / BK) : p.K / BK;
+    const TileWork tw = tile_work(p, comp ? 2 * (p.K / BK) : p.K / BK, comp);
+    const int m0 = tw.m0, n0 = tw.n0, tn = tw.tn;
+    const int kt0 = tw.kt0, nk = tw.kt1 - tw.kt0;  // this workgroup's K tiles kt0 + [0, nk)
     const bf16* A = (const bf16*)p.A;
     const bf16* A_lo = (const bf16*)p.A_lo;
     const bf16* B = (const bf16*)p.B;
@@ -211,8 +304,9 @@ void gemm_bf16_kernel(GemmArgs p) {
     const int lchunk = 2 * l32 + hh;  // the memory chunk this lane moves into LDS chunk `lane`
     auto issue = [&](int kt) {
         bf16* sbase = lds + (kt % NS) * STAGE;
-        const int k0 = (comp ? kt >> 1 : kt) * BK;
-        const bf16* As = (comp && (kt & 1)) ? A_lo : A;
+        const int kg = kt0 + kt;
+        const int k0 = (comp ? kg >> 1 : kg) * BK;
+        const bf16* As = (comp && (kg & 1)) ? A_lo : A;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int b = wave * 2 + u;
@@ -299,6 +393,7 @@ void gemm_bf16_kernel(GemmArgs p) {
         mfmas(a1, b1, more);
     }
     __syncthreads();  // every wave is done with the ring (all its loads have landed)
+    if (p.tail && !tail_join(p, tw.slot, acc, (int*)lds + 8192)) return;  // workgroup-uniform
     if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
         if (tid < TBM) {
             float s = 0.f;
@@ -333,9 +428,10 @@ void gemm_bf16_comp_kernel(GemmArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / 4, wn = wave % 4;  // 2 x 4 waves, 128 x 64 each
     const int l32 = lane & 31, hh = lane >> 5;
-    int m0, n0, tn;
-    tile_coords(p, m0, n0, tn);
-    const int nk = p.K / 16;  // stages
+    const int nk_all = p.K / 16;  // 16-deep steps, one per stage
+    const TileWork tw = tile_work(p, nk_all, false);
+    const int m0 = tw.m0, n0 = tw.n0, tn = tw.tn;
+    const int nk = tw.kt1 - tw.kt0;  // this workgroup's stages (from step kt0)
 
     constexpr int MAXP = 16;
     float ssp[MAXP];
@@ -355,9 +451,9 @@ void gemm_bf16_comp_kernel(GemmArgs p) {
     const int lchunk = 2 * l32 + hh;
     const int mb = min(m0 / 32 + wave, (p.M + 31) / 32 - 1);
     const int nb = min(n0 / 32 + wave, p.Npad / 32 - 1);
-    const bf16* srcA = (const bf16*)p.A + (long long)mb * nk * 512 + lchunk * 8;
-    const bf16* srcL = (const bf16*)p.A_lo + (long long)mb * nk * 512 + lchunk * 8;
-    const bf16* srcB = (const bf16*)p.B + (long long)nb * nk * 512 + lchunk * 8;
+    const bf16* srcA = (const bf16*)p.A + ((long long)mb * nk_all + tw.kt0) * 512 + lchunk * 8;
+    const bf16* srcL = (const bf16*)p.A_lo + ((long long)mb * nk_all + tw.kt0) * 512 + lchunk * 8;
+    const bf16* srcB = (const bf16*)p.B + ((long long)nb * nk_all + tw.kt0) * 512 + lchunk * 8;
     auto issue = [&](int kt) {
         bf16* s = lds + (kt % NS) * STAGE;
         __builtin_amdgcn_global_load_lds((gvoid*)(srcA + (long long)kt * 512), (lvoid*)(s + wave * 512), 16, 0, 0);
@@ -435,6 +531,7 @@ void gemm_bf16_comp_kernel(GemmArgs p) {
         if (kt + 1 < nk) step(kt + 1, f1, f0);
     }
     __syncthreads();  // every wave is done with the ring (all its loads have landed)
+    if (p.tail && !tail_join(p, tw.slot, acc, (int*)lds + 8192)) return;  // workgroup-uniform
     if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
         if (tid < TBM) {
             float s = 0.f;
@@ -465,8 +562,8 @@ void gemm_f32_kernel(GemmArgs p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / 2, wn = wave % 2;
     const int l32 = lane & 31, hh = lane >> 5;
-    int m0, n0, tn;
-    tile_coords(p, m0, n0, tn);
+    const TileWork tw = tile_work(p, 1, false);  // no tail split: p.tail is 0
+    const int m0 = tw.m0, n0 = tw.n0, tn = tw.tn;
     const int kspan = p.K / p.k_split;
     const int kbeg = blockIdx.z * kspan;
     const int nk = kspan / BK;
@@ -540,9 +637,22 @@ void gemm_f32_kernel(GemmArgs p) {
     tile_epilogue<T, EPI, 2, 2>(p, acc, m0, n0, tn, rs, red);
 }
 
+// Tail split (GemmArgs): the last round of workgroups (256 CUs, one 160 KB workgroup each)
+// holds tiles % 256 tiles; when that is at most half a round they run as 2 K halves each, so
+// the round is twice as full and ends in about half the time.  Kept to K of at least 16 K
+// tiles, so each half has a pipeline's worth of stages.
+static int tail_tiles(const GemmArgs& a, int tiles, int ktiles) {
+    if (!a.tail_part || !a.tail_ctr || ktiles < 16) return 0;
+    const int r = tiles % 256;
+    return (r > 0 && r <= 128 && r <= GEMM_TAIL_SLOTS) ? r : 0;
+}
+
 template <int EPI>
-static hipError_t launch_e(DType dt, const GemmArgs& a, hipStream_t st) {
-    dim3 grid(((a.N + TBN - 1) / TBN) * ((a.M + TBM - 1) / TBM), 1, a.k_split);
+static hipError_t launch_e(DType dt, const GemmArgs& a_in, hipStream_t st) {
+    GemmArgs a = a_in;
+    const int tiles = ((a.N + TBN - 1) / TBN) * ((a.M + TBM - 1) / TBM);
+    a.tail = dt == BF16 ? tail_tiles(a, tiles, a.K / 32) : 0;
+    dim3 grid(tiles + a.tail, 1, a.k_split);
     if (dt == BF16) {
         if (a.k_split != 1 || a.K % 32) return hipErrorInvalidValue;
         if constexpr (EPI != EPI_STORE) {

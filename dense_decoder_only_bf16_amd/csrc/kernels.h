@@ -92,7 +92,16 @@ struct GemmArgs {
     // compensated product reads).  Null: not written.
     void* out_lo;
     ResidExtra rx;  // RESID: the later version's residual scaling and backout
+    // Tail split (bf16): when the tiles leave the last round of workgroups (one per CU) at
+    // most half full, that round's tiles run as two K halves each; the half that arrives
+    // first on its tile leaves its partial sums in tail_part and sets a ready flag, the other
+    // adds them and runs the epilogue.  Null tail_part: off.  tail is set by the launcher.
+    float* tail_part;    // GEMM_TAIL_SLOTS x GEMM_TAIL_FLOATS fp32
+    int32_t* tail_ctr;   // 2 per slot, zero before the launch; every launch leaves them zero
+    int tail;
 };
+constexpr int GEMM_TAIL_SLOTS = 128;
+constexpr long long GEMM_TAIL_FLOATS = 512 * 128;  // a tile's accumulators: 512 threads x 128
 
 // Prefill product (M in the thousands): 256 x 256 tiles.
 int gemm_tile_n();             // N extent of one tile (ss_out parts = ceil(N / tile_n))

@@ -137,6 +137,8 @@ struct Ws {
     int32_t* actr = nullptr;  // decode attention ready flags, one per (row, K/V head) and slot
     int32_t* fctr = nullptr;  // decode QKV finish in the product's epilogue: arrival counters per head slot
     float* dpart = nullptr;   // decode projections: split-K arrival counters, then partials
+    float* tpart = nullptr;   // prefill products (bf16): partial sums of the tail split's K halves
+    int32_t* tctr = nullptr;  // and their arrival counters / ready flags (2 per tile slot)
     float* x0 = nullptr;      // later-version blocks: stream before layer 0's scaling [M][d]
     float* xb = nullptr;      // and the backout source [M][d]
     int32_t* tokbuf = nullptr;   // the rows' clamped tokens (value embeddings) [M]
@@ -272,6 +274,10 @@ Ws ws_layout(const nc_model* m, int B, int S, long long M, void* base) {
                                   dec_gemm_part_elems(m->dt, EPI_SOFTCAP, B, c.vocab, c.d_model)});
         w.dpart = w.dpart_elems > 0 ? (float*)take(w.dpart_elems * 4) : nullptr;
     }
+    if (m->dt == BF16 && M > 1024) {  // prefill sizes only (32 MB); decode rows never need it
+        w.tpart = (float*)take((long long)GEMM_TAIL_SLOTS * GEMM_TAIL_FLOATS * 4);
+        w.tctr = (int32_t*)take(2LL * GEMM_TAIL_SLOTS * 4);
+    }
     w.bytes = off;
     w.base = base;
     return w;
@@ -291,6 +297,7 @@ nc_status ws_ensure(nc_kv* kv, long long M) {
     hipError_t e = hipMemset(w.actr, 0, (size_t)w.actr_elems * 4);
     if (e == hipSuccess) e = hipMemset(w.fctr, 0, DEC_FIN_SLOTS * 4);
     if (e == hipSuccess && w.dpart) e = hipMemset(w.dpart, 0, DEC_PART_CTRS * 4);
+    if (e == hipSuccess && w.tctr) e = hipMemset(w.tctr, 0, 2 * GEMM_TAIL_SLOTS * 4);
     if (e == hipSuccess && kv->m->ex.on) {  // the per-layer blocks that decode kernels read through pointers
         const nc_config& c = kv->m->cfg;
         std::vector<ResidExtra> rx(c.n_layer);
@@ -948,6 +955,7 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             const nc_model::Layer& L = m->layers[l];
             GemmArgs g{};
             g.M = Mi; g.lda = d; g.k_split = 1; g.eps = c.norm_eps; g.cap = c.softcap;
+            g.tail_part = kv->ws.tpart; g.tail_ctr = kv->ws.tctr;
             // QKV raw product
             g.A = kv->ws.act; g.B = L.wqkv; g.N = nqkv; g.K = d; g.Npad = nqkv;
             g.out_f32 = kv->ws.qkv; g.ldo = nqkv; g.z_stride = 0;
@@ -1001,6 +1009,7 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             GemmArgs g{};
             g.A = kv->ws.act; g.A_lo = kv->ws.act_lo; g.lda = d; g.B = m->lm; g.M = Mi; g.N = V; g.K = d;
             g.Npad = (V + 31) / 32 * 32; g.k_split = 1;
+            g.tail_part = kv->ws.tpart; g.tail_ctr = kv->ws.tctr;
             g.out_f32 = logits; g.ldo = V; g.ss_in = kv->ws.ss_a; g.ss_in_parts = ss_a_parts;
             g.ss_stride = (int)kv->ws.cap_m; g.eps = c.norm_eps; g.cap = c.softcap;
             LAUNCH(prefill_gemm(m, EPI_SOFTCAP, g, st));

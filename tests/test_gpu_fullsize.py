@@ -144,11 +144,14 @@ def test_d26_prefill_16x2048():
     kv.prefill(torch.from_numpy(toks).cuda(), logits)
     torch.cuda.synchronize()
     g = logits[7, :768].cpu().numpy()
+    g15 = logits[15, :256].cpu().numpy()  # rows 13..15 sit in the O / PROJ tail tiles (K halves)
     del logits
     kv.close()
     r.close()
     w, _ = r.orc.prefill(toks[7:8, :768])
     check("d26 prefill row 7 (first 768)", g, w[0])
+    w15, _ = r.orc.prefill(toks[15:16, :256])
+    check("d26 prefill row 15 (first 256)", g15, w15[0])
 
 
 @pytest.fixture(scope="module")

@@ -389,6 +389,31 @@ def test_bf16_other_head_shapes(shape):
     gm.close()
 
 
+# Prefill products whose tiles leave the last round of workgroups at most half full run
+# that round's tiles as two K halves, joined through a partial-sum buffer.  M = 2 x 1100 rows
+# (9 row tiles, ragged), K >= 512: every tile of QKV (54), O (18), FC (72) and PROJ (18) is
+# split (no whole tiles before them), and the LM head's 34 x 9 = 306 tiles leave 50 tail
+# tiles after 256 whole ones (the compensated kernel).
+TAIL = Shape("tail-split", n_layer=1, d_model=512, n_head=4, head_dim=128, d_ff=2048, vocab=8500,
+             dtype="bf16", max_seq=1104)
+
+
+def test_bf16_prefill_tail_split():
+    w = make_weights(TAIL, seed=21)
+    orc = OracleModel(TAIL, w)
+    gm = gpu_model(TAIL, w)
+    toks = make_tokens(TAIL.vocab, 2, 1100, seed=22)
+    want, _ = orc.prefill(toks)
+    kv, got = prefill(gm, toks, TAIL.max_seq)
+    err, agr = report("tail-split prefill", got, want)
+    assert err <= BF16_TOL and agr >= AGREE
+    kv.close()
+    kv, got2 = prefill(gm, toks, TAIL.max_seq)  # the join's counters are left at zero
+    assert np.array_equal(got, got2)
+    kv.close()
+    gm.close()
+
+
 # fp32 grouped-query model: 4 query heads over 2 K/V heads, checked at the fp32 bar
 TINY_GQA = replace(TINY, name="tiny-gqa", d_model=256, n_head=4, n_kv_head=2, d_ff=512)
 
