@@ -101,6 +101,117 @@ __device__ __forceinline__ void tile_row_scales(const GemmArgs& p, int m0, float
     }
 }
 
+// Transpose of a 4 x 4 block held by a lane quad: lane a (= lane % 4) holds x[k] = B[k][a]
+// and leaves with x[k] = B[a][k].  Two rounds of quad DPP exchanges (lane xor 1, then xor 2);
+// in each, a lane keeps the two entries whose bit already matches its own and takes the
+// other two from its partner, one exchange per pair.
+__device__ __forceinline__ void quad_transpose4(float (&x)[4], int a) {
+#pragma unroll
+    for (int k0 = 0; k0 < 4; k0 += 2) {  // bit 0: pairs (0, 1), (2, 3)
+        const bool hi = a & 1;
+        const float r = dpp_lane<DPP_QUAD_XOR1>(hi ? x[k0] : x[k0 + 1]);
+        if (hi) x[k0] = r;
+        else x[k0 + 1] = r;
+    }
+#pragma unroll
+    for (int k0 = 0; k0 < 2; ++k0) {  // bit 1: pairs (0, 2), (1, 3)
+        const bool hi = a & 2;
+        const float r = dpp_lane<DPP_QUAD_XOR2>(hi ? x[k0] : x[k0 + 2]);
+        if (hi) x[k0] = r;
+        else x[k0 + 2] = r;
+    }
+}
+
+// bf16 RELU2 / RESID epilogue of the 2 x 4-wave kernels with each lane finishing 4
+// consecutive columns of one row.  In the accumulator layout a lane holds one column and
+// rows 8 q + 4 hh + k (k < 4) of each 32-row block; a quad transpose turns every such 4 x 4
+// block around, so lane 4 c + e holds row 8 q + 4 hh + e, columns 4 c .. 4 c + 3.  Then x
+// moves as 16-byte loads and stores and the blocked bf16 outputs as 8-byte stores (4
+// columns of one 16-column chunk), a quarter of the memory instructions of the column
+// layout.  N and ldo are multiples of 4 (host check), so a lane's 4 columns all exist or
+// none does.
+template <int EPI>
+__device__ __forceinline__ void tile_epilogue4(const GemmArgs& p, f32x16 (&acc)[4][2], int m0, int n0, const float* rs,
+                                               float (*red)[TBM]) {
+    constexpr int WN = 4, IM = 4, JN = 2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int e = l32 & 3, cq = l32 & ~3;
+#pragma unroll
+    for (int i = 0; i < IM; ++i) {
+        const int rb = wm * 128 + i * 32 + 4 * hh + e;  // + 8 q: this lane's rows in the tile
+        // RESID: the old residual of every row and column this lane finishes in this row
+        // block, all loaded before any store (the stores write the same array)
+        f32x4 xold[4][JN];
+        if (EPI == EPI_RESID) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int j = 0; j < JN; ++j) {
+                    const int m = min(m0 + rb + 8 * q, p.M - 1);
+                    const int n = min(n0 + wn * 64 + j * 32 + cq, p.N - 4);
+                    xold[q][j] = *(const f32x4*)(p.out_f32 + (long long)m * p.ldo + n);
+                }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int rl = rb + 8 * q, m = m0 + rl;
+            float sq = 0.f;
+#pragma unroll
+            for (int j = 0; j < JN; ++j) {
+                float v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] = acc[i][j][4 * q + k];
+                quad_transpose4(v, e);
+                const int n = n0 + wn * 64 + j * 32 + cq;
+                const bool ok = m < p.M && n < p.N;
+                const long long ot = blocked_index(m, n, p.ldo);
+                bf16x4 hi, lo;
+                if (EPI == EPI_RELU2) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float t = fmaxf(v[k] * rs[rl], 0.f);
+                        hi[k] = (bf16)(t * t);
+                        lo[k] = (bf16)(t * t - (float)hi[k]);
+                    }
+                } else {  // EPI_RESID
+                    const long long o = (long long)m * p.ldo + n;
+                    f32x4 xn;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        xn[k] = ok ? resid_value(p.rx, o + k, xold[q][j][k], v[k]) : 0.f;
+                        hi[k] = (bf16)xn[k];
+                        lo[k] = (bf16)(xn[k] - (float)hi[k]);
+                        sq += xn[k] * xn[k];
+                    }
+                    if (ok) *(f32x4*)(p.out_f32 + o) = xn;
+                }
+                if (ok) {
+                    *(bf16x4*)((bf16*)p.out_t + ot) = hi;
+                    if (p.out_lo) *(bf16x4*)((bf16*)p.out_lo + ot) = lo;
+                }
+            }
+            if (EPI == EPI_RESID) {  // the row's sum over the wave's 64 columns: the 8 quads
+                sq += __shfl_xor(sq, 4, 64);
+                sq += __shfl_xor(sq, 8, 64);
+                sq += __shfl_xor(sq, 16, 64);
+                if (cq == 0) red[wn][rl] = sq;
+            }
+        }
+    }
+    if (EPI == EPI_RESID) {
+        __syncthreads();
+        for (int r = tid; r < TBM; r += 512) {
+            const int m = m0 + r;
+            float s = 0.f;
+#pragma unroll
+            for (int w = 0; w < WN; ++w) s += red[w][r];
+            if (m < p.M) p.ss_out[(long long)(n0 / TBN) * p.ss_stride + m] = s;
+        }
+    }
+}
+
 // Epilogue on the accumulators of a workgroup of WM x WN waves: wave (wm, wn) owns rows
 // m0 + wm (256/WM) + [0, 256/WM) and columns n0 + wn (256/WN) + [0, 256/WN); its lane holds
 // column n0 + wn (256/WN) + 32 j + l32 and rows ... + 32 i + 8 (r/4) + 4 hh + (r%4) of
@@ -403,7 +514,8 @@ void gemm_bf16_kernel(GemmArgs p) {
         }
         __syncthreads();
     }
-    tile_epilogue<bf16, EPI, 2, 4>(p, acc, m0, n0, tn, rs, red);
+    if constexpr (EPI == EPI_RELU2 || EPI == EPI_RESID) tile_epilogue4<EPI>(p, acc, m0, n0, rs, red);
+    else tile_epilogue<bf16, EPI, 2, 4>(p, acc, m0, n0, tn, rs, red);
 }
 
 // Compensated products (A + A_lo against one weight: the MLP products and the LM head).  A
@@ -541,7 +653,8 @@ void gemm_bf16_comp_kernel(GemmArgs p) {
         }
         __syncthreads();
     }
-    tile_epilogue<bf16, EPI, 2, 4>(p, acc, m0, n0, tn, rs, red);
+    if constexpr (EPI == EPI_RELU2 || EPI == EPI_RESID) tile_epilogue4<EPI>(p, acc, m0, n0, rs, red);
+    else tile_epilogue<bf16, EPI, 2, 4>(p, acc, m0, n0, tn, rs, red);
 }
 
 // ---------------------------------------------------------------------- fp32 ----------
@@ -639,10 +752,13 @@ void gemm_f32_kernel(GemmArgs p) {
 
 // Tail split (GemmArgs): the last round of workgroups (256 CUs, one 160 KB workgroup each)
 // holds tiles % 256 tiles; when that is at most half a round they run as 2 K halves each, so
-// the round is twice as full and ends in about half the time.  Kept to K of at least 16 K
-// tiles, so each half has a pipeline's worth of stages.
+// the round is twice as full and ends in about half the time.  With the split on, every
+// workgroup runs the join's add (a whole tile's through an empty buffer), about a microsecond
+// per tile, so it is kept to K of at least 64 K tiles (2048), where half a round is worth
+// far more: d26's MLP down-projection (K 6656) 1488 -> 1362 us, its attention output
+// projection (K 1664) 349 -> 345 us.
 static int tail_tiles(const GemmArgs& a, int tiles, int ktiles) {
-    if (!a.tail_part || !a.tail_ctr || ktiles < 16) return 0;
+    if (!a.tail_part || !a.tail_ctr || ktiles < 64) return 0;
     const int r = tiles % 256;
     return (r > 0 && r <= 128 && r <= GEMM_TAIL_SLOTS) ? r : 0;
 }
@@ -655,6 +771,7 @@ static hipError_t launch_e(DType dt, const GemmArgs& a_in, hipStream_t st) {
     dim3 grid(tiles + a.tail, 1, a.k_split);
     if (dt == BF16) {
         if (a.k_split != 1 || a.K % 32) return hipErrorInvalidValue;
+        if ((EPI == EPI_RELU2 || EPI == EPI_RESID) && (a.N % 4 || a.ldo % 4)) return hipErrorInvalidValue;
         if constexpr (EPI != EPI_STORE) {
             if (a.A_lo) {
                 NC_TLAUNCH((gemm_bf16_comp_kernel<EPI>), grid, dim3(512), 0, st, a);

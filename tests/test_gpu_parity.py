@@ -389,12 +389,13 @@ def test_bf16_other_head_shapes(shape):
     gm.close()
 
 
-# Prefill products whose tiles leave the last round of workgroups at most half full run
-# that round's tiles as two K halves, joined through a partial-sum buffer.  M = 2 x 1100 rows
-# (9 row tiles, ragged), K >= 512: every tile of QKV (54), O (18), FC (72) and PROJ (18) is
-# split (no whole tiles before them), and the LM head's 34 x 9 = 306 tiles leave 50 tail
-# tiles after 256 whole ones (the compensated kernel).
-TAIL = Shape("tail-split", n_layer=1, d_model=512, n_head=4, head_dim=128, d_ff=2048, vocab=8500,
+# Prefill products with K >= 2048 whose tiles leave the last round of workgroups at most
+# half full run that round's tiles as two K halves, joined through a partial-sum buffer.
+# M = 2 x 1100 rows (9 row tiles, ragged), d 2048: O (72 tiles, the plain kernel), PROJ (72,
+# K 8192) and the LM head (36) have every tile split; FC's 288 tiles leave 32 tail tiles
+# after 256 whole ones (the compensated kernel); QKV (216 tiles, a round over half full) is
+# not split.
+TAIL = Shape("tail-split", n_layer=1, d_model=2048, n_head=16, head_dim=128, d_ff=8192, vocab=1000,
              dtype="bf16", max_seq=1104)
 
 
