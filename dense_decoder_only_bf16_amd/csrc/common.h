@@ -34,6 +34,47 @@ __device__ __forceinline__ f32x16 mma32(f32x8 a, f32x8 b, f32x16 c) {
     return c;
 }
 
+// 32x32 output tile, 64-deep contraction of e4m3 operands (gfx950's scaled f8f6f4 MFMA):
+// c + 2^(sa - 127) 2^(sb - 127) sum_k a_k b_k.  Each lane holds 32 bytes of its row (A) or
+// column (B); the instruction pairs byte p of lane l in A with byte p of lane l' = column +
+// 32 (l / 32) in B, so any assignment of k to (l / 32, p) that both operands share gives the
+// same product.  Measured on gfx950: subnormal inputs are kept, and the accumulator is added
+// at fp32 precision (within 2 ulp).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mma32_e4m3(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+// Four fp32 values -> four e4m3 bytes of x 2^shift (round to nearest even), clamped to the
+// largest finite e4m3 value (448): the conversion itself gives NaN beyond it.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float scale) {
+    auto cl = [&](float x) { return fminf(fmaxf(x * scale, -448.f), 448.f); };
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), v, true);
+    return (uint32_t)v;
+}
+// Eight bf16 values -> eight e4m3 bytes (two dwords) of w / inv_scale (round to nearest
+// even); |w / inv_scale| must stay within 448 (larger values give NaN).  The values go
+// through fp32 (a shift or a mask per value): the conversion builtin that takes bf16 pairs
+// directly was compiled here as if every pair were the first one.
+__device__ __forceinline__ void e4m3x8_bf16(bf16x8 w, float inv_scale, int& d0, int& d1) {
+    typedef short s2 __attribute__((ext_vector_type(2)));
+    const u32x4 u = __builtin_bit_cast(u32x4, w);  // bf16 pairs, element 2i in the low half
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __builtin_bit_cast(float, u[i] << 16);
+        f[2 * i + 1] = __builtin_bit_cast(float, u[i] & 0xffff0000u);
+    }
+    s2 o = {0, 0};
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, f[0], f[1], inv_scale, false);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, f[2], f[3], inv_scale, true);
+    d0 = __builtin_bit_cast(int, o);
+    s2 o2 = {0, 0};
+    o2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o2, f[4], f[5], inv_scale, false);
+    o2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o2, f[6], f[7], inv_scale, true);
+    d1 = __builtin_bit_cast(int, o2);
+}
+
 // 16x16 output tile, 32-deep contraction.  Operand layout: lane l holds row/column (l % 16)
 // and contraction indices 8*(l/16) .. 8*(l/16)+7.  Output: lane l, register j holds row
 // 4*(l/16) + j, column l % 16.

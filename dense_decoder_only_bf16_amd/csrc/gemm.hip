@@ -10,10 +10,12 @@
 //
 // Compensated operands: a bf16 operand carries a relative rounding error of up to 2^-9, and
 // in the MLP that error is amplified by the squared ReLU and summed over d_ff terms.  For
-// the MLP products and the LM head the activation is therefore passed as two bf16 arrays,
-// hi = bf16(a) and lo = bf16(a - hi), and multiplied as hi W^T + lo W^T with fp32
-// accumulation, which leaves a relative operand error near 2^-17 (the weights are exact
-// bf16 values).  The producing epilogue writes both parts.
+// the MLP products and the LM head the activation is therefore carried as a high part
+// hi = bf16(a) and a low part lo = a - hi, and multiplied as hi W^T + lo W^T with fp32
+// accumulation.  The low part is stored as an e4m3 byte (lo 2^8) and its product runs on
+// the fp8 matrix cores against an e4m3 copy of the weight made in registers: the operand
+// error left is about 2^-12 of a at worst, against 2^-9 for a plain bf16 operand.  The
+// producing epilogue writes both parts.
 //
 // Tiling: a workgroup computes a 256 x 256 tile.  bf16: 2 x 4 waves (two per SIMD, so one
 // wave's MFMAs cover the other's waits at barriers and LDS reads), each owning a 128 x 64
@@ -29,13 +31,17 @@
 //    fragments of the next 16-deep step (also across a K-tile boundary) are read from LDS
 //    while the MFMAs of the current step run (fragments double-buffered in registers,
 //    reads interleaved one per MFMA).
-//  * bf16 with a compensated operand (gemm_bf16_comp_kernel): 6 stages of one 16-deep step
-//    holding A, A_lo and the weight block, so each weight block is loaded once.
+//  * bf16 with a compensated operand (gemm_bf16_comp_kernel): 7 stages of one 16-deep step
+//    holding the A and weight blocks, beside 3 slots of 64-deep groups of e4m3 low parts.
 //  * fp32 (the small fp32 check model): loads staged through registers into two LDS
 //    buffers (A kept row-major with an XOR swizzle).
 // Workgroups are dealt round-robin to the 8 dies (XCDs), each with its own L2; tiles are
 // renumbered so each die works on a contiguous range, walked in groups of 8 row tiles so
 // tiles running together share A rows and weight columns in the die's L2.
+#include <algorithm>
+#include <cmath>
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -167,13 +173,14 @@ __device__ __forceinline__ void tile_epilogue4(const GemmArgs& p, f32x16 (&acc)[
                 const int n = n0 + wn * 64 + j * 32 + cq;
                 const bool ok = m < p.M && n < p.N;
                 const long long ot = blocked_index(m, n, p.ldo);
-                bf16x4 hi, lo;
+                bf16x4 hi;
+                float lo[4];
                 if (EPI == EPI_RELU2) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         const float t = fmaxf(v[k] * rs[rl], 0.f);
                         hi[k] = (bf16)(t * t);
-                        lo[k] = (bf16)(t * t - (float)hi[k]);
+                        lo[k] = t * t - (float)hi[k];
                     }
                 } else {  // EPI_RESID
                     const long long o = (long long)m * p.ldo + n;
@@ -182,14 +189,17 @@ __device__ __forceinline__ void tile_epilogue4(const GemmArgs& p, f32x16 (&acc)[
                     for (int k = 0; k < 4; ++k) {
                         xn[k] = ok ? resid_value(p.rx, o + k, xold[q][j][k], v[k]) : 0.f;
                         hi[k] = (bf16)xn[k];
-                        lo[k] = (bf16)(xn[k] - (float)hi[k]);
+                        lo[k] = xn[k] - (float)hi[k];
                         sq += xn[k] * xn[k];
                     }
                     if (ok) *(f32x4*)(p.out_f32 + o) = xn;
                 }
                 if (ok) {
                     *(bf16x4*)((bf16*)p.out_t + ot) = hi;
-                    if (p.out_lo) *(bf16x4*)((bf16*)p.out_lo + ot) = lo;
+                    // the low parts as e4m3 in the lo8 layout: 4 consecutive bytes (n % 4 == 0)
+                    if (p.out_lo)
+                        *(uint32_t*)((unsigned char*)p.out_lo + lo8_index(m, n, p.ldo)) =
+                            e4m3x4(lo[0], lo[1], lo[2], lo[3], (float)(1 << LO8_SHIFT));
                 }
             }
             if (EPI == EPI_RESID) {  // the row's sum over the wave's 64 columns: the 8 quads
@@ -518,21 +528,31 @@ void gemm_bf16_kernel(GemmArgs p) {
     else tile_epilogue<bf16, EPI, 2, 4>(p, acc, m0, n0, tn, rs, red);
 }
 
-// Compensated products (A + A_lo against one weight: the MLP products and the LM head).  A
-// stage is one 16-deep step holding the tile's 8 A blocks, its 8 A_lo blocks and its 8
-// weight blocks (24 KB; wave w loads block w of each), so a weight block is brought into
-// LDS once for both MFMAs that use it: 24 KB of loads per 16 MFMAs of each wave, where
-// running A_lo as extra K tiles of the kernel above loads 32 KB (the weight twice).  The
-// loads into LDS, not the matrix cores, bound these products.  Six stages (144 KB), five
-// in flight; a stage's 8 hi MFMAs come before its 8 lo MFMAs, so the two updates of an
-// accumulator are 8 MFMAs apart, and the next stage's 10 fragment reads are interleaved
-// with them.
+// Compensated products (A + A_lo against one weight: the MLP products and the LM head).  The
+// high part runs the bf16 MFMAs of the plain kernel; the low part, a correction near 2^-9 of
+// the operand, runs at fp8 rate: A_lo arrives as e4m3 bytes (lo8 layout, kernels.h), the
+// weight fragments of every 16-deep step are converted to e4m3 in registers (w 2^w8_exp),
+// and after four steps one scaled 32x32x64 e4m3 MFMA per accumulator tile adds
+// lo W^T 2^-LO8_SHIFT 2^-w8_exp into the same fp32 accumulators.  Per 64 deep a wave then
+// issues 32 bf16 and 8 fp8 MFMAs (the time of 48 bf16 ones, against 64 with a bf16 low
+// part), and a 16-deep step moves 20 KB into LDS instead of 24 KB.
+// LDS: a ring of 7 stages of one 16-deep step (the tile's 8 A and 8 weight blocks, 16 KB;
+// wave w loads block w of each, loads issued six stages ahead) and a ring of 3 slots of one
+// 64-deep group of low parts (8 row blocks x 2 KB).  A group's 16 KB low-part block loads
+// are spread over its four steps' stages (waves 0-3 take one each), so it has landed when its
+// last step's stage has, and its slot is refilled only two steps after that step's reads.
+// Operand error of the product: the e4m3 rounding of lo (2^-4 relative) and of the weight
+// copy (2^-4 relative) act on a term 2^-9 the size of a, leaving about 2^-12 of a at worst
+// and far less on average, against 2^-9 for a plain bf16 operand.
 template <int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_comp_kernel(GemmArgs p) {
-    constexpr int NS = 6, BPS = 24;   // stages, 1 KB blocks per stage
-    constexpr int STAGE = BPS * 512;  // elements per stage
-    __shared__ __attribute__((aligned(1024))) bf16 lds[NS * STAGE];
+    constexpr int NSM = 7, NSL = 3;  // main stages, low-part group slots
+    constexpr int MST = 16 * 512;    // bf16 elements per main stage
+    constexpr int LST = 16 * 1024;   // bytes per low-part slot
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[NSM * MST * 2 + NSL * LST];
+    bf16* const ring = (bf16*)lds;
+    unsigned char* const lring = lds + NSM * MST * 2;
     float* rs = (float*)lds;
     float (*red)[TBM] = (float (*)[TBM])((float*)lds + TBM);
 
@@ -540,10 +560,11 @@ void gemm_bf16_comp_kernel(GemmArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / 4, wn = wave % 4;  // 2 x 4 waves, 128 x 64 each
     const int l32 = lane & 31, hh = lane >> 5;
-    const int nk_all = p.K / 16;  // 16-deep steps, one per stage
-    const TileWork tw = tile_work(p, nk_all, false);
+    const int ksteps = p.K / 16, ngroups = p.K / 64;
+    const TileWork tw = tile_work(p, ngroups, false);  // K tiles of 64 (K halves for the tail split)
     const int m0 = tw.m0, n0 = tw.n0, tn = tw.tn;
-    const int nk = tw.kt1 - tw.kt0;  // this workgroup's stages (from step kt0)
+    const int g0 = tw.kt0;              // first 64-deep group
+    const int nk = 4 * (tw.kt1 - g0);   // this workgroup's 16-deep steps (stages), from step 4 g0
 
     constexpr int MAXP = 16;
     float ssp[MAXP];
@@ -556,21 +577,50 @@ void gemm_bf16_comp_kernel(GemmArgs p) {
             if (q < p.ss_in_parts) ssp[q] = p.ss_in[(long long)q * p.ss_stride + m];
     }
 
-    // Wave w moves row block w of A and A_lo and weight block w; lane l takes memory chunk
-    // 2 (l % 32) + l / 32 of a block into LDS chunk l (MFMA lane order, as above).  Row
-    // blocks past A's last and weight blocks past Npad read a clamped block; their outputs
-    // are masked in the epilogue.
+    // Wave w moves row block w of A and weight block w; lane l takes memory chunk
+    // 2 (l % 32) + l / 32 of a block into LDS chunk l (MFMA lane order, as above).  The low
+    // parts are already in lane order in memory and move as plain 1 KB copies.  Row blocks
+    // past A's last and weight blocks past Npad read a clamped block; their outputs are
+    // masked in the epilogue.
     const int lchunk = 2 * l32 + hh;
-    const int mb = min(m0 / 32 + wave, (p.M + 31) / 32 - 1);
+    const int mblast = (p.M + 31) / 32 - 1;
+    const int mb = min(m0 / 32 + wave, mblast);
     const int nb = min(n0 / 32 + wave, p.Npad / 32 - 1);
-    const bf16* srcA = (const bf16*)p.A + ((long long)mb * nk_all + tw.kt0) * 512 + lchunk * 8;
-    const bf16* srcL = (const bf16*)p.A_lo + ((long long)mb * nk_all + tw.kt0) * 512 + lchunk * 8;
-    const bf16* srcB = (const bf16*)p.B + ((long long)nb * nk_all + tw.kt0) * 512 + lchunk * 8;
+    const bf16* srcA = (const bf16*)p.A + ((long long)mb * ksteps + 4 * g0) * 512 + lchunk * 8;
+    const bf16* srcB = (const bf16*)p.B + ((long long)nb * ksteps + 4 * g0) * 512 + lchunk * 8;
+    const unsigned char* lo8 = (const unsigned char*)p.A_lo + (long long)g0 * 2048 + lane * 16;
     auto issue = [&](int kt) {
-        bf16* s = lds + (kt % NS) * STAGE;
+        bf16* s = ring + (kt % NSM) * MST;
         __builtin_amdgcn_global_load_lds((gvoid*)(srcA + (long long)kt * 512), (lvoid*)(s + wave * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gvoid*)(srcL + (long long)kt * 512), (lvoid*)(s + (8 + wave) * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gvoid*)(srcB + (long long)kt * 512), (lvoid*)(s + (16 + wave) * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gvoid*)(srcB + (long long)kt * 512), (lvoid*)(s + (8 + wave) * 512), 16, 0, 0);
+        if (wave < 4) {  // 1 KB half h of row block r of group kt / 4: load 4 (kt % 4) + wave
+            const int g = kt >> 2, i = 4 * (kt & 3) + wave, r = i >> 1, h = i & 1;
+            const int mbr = min(m0 / 32 + r, mblast);
+            const unsigned char* src = lo8 + ((long long)mbr * ngroups + g) * 2048 + h * 1024;
+            __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(lring + (g % NSL) * LST + r * 2048 + h * 1024), 16, 0, 0);
+        }
+    };
+    // this wave's loads per stage: 3 (waves 0-3) or 2; wait until at most n stages are in flight
+    auto wait_stages = [&](int n) {
+        if (wave < 4) {
+            switch (n) {
+                case 5: NC_WAIT_VM(15); break;
+                case 4: NC_WAIT_VM(12); break;
+                case 3: NC_WAIT_VM(9); break;
+                case 2: NC_WAIT_VM(6); break;
+                case 1: NC_WAIT_VM(3); break;
+                default: NC_WAIT_VM(0); break;
+            }
+        } else {
+            switch (n) {
+                case 5: NC_WAIT_VM(10); break;
+                case 4: NC_WAIT_VM(8); break;
+                case 3: NC_WAIT_VM(6); break;
+                case 2: NC_WAIT_VM(4); break;
+                case 1: NC_WAIT_VM(2); break;
+                default: NC_WAIT_VM(0); break;
+            }
+        }
     };
 
     f32x16 acc[4][2];
@@ -578,79 +628,89 @@ void gemm_bf16_comp_kernel(GemmArgs p) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = zero_vec<f32x16>();
+    i32x8 wq[2];  // e4m3 copies of this wave's two weight blocks over the current group's 4 steps
+    const float winv = ldexpf(1.0f, -p.w8_exp);
+    const int sa = 127 - LO8_SHIFT, sb = 127 - p.w8_exp;
 
-    typedef bf16x8 Frag[10];  // A blocks 0..3, A_lo blocks 4..7, weight blocks 8..9
+    typedef bf16x8 Frag[6];  // A blocks 0..3, weight blocks 4..5
     auto fload = [&](int kt, Frag& f) {
-        const bf16* s = lds + (kt % NS) * STAGE + lane * 8;
+        const bf16* s = ring + (kt % NSM) * MST + lane * 8;
 #pragma unroll
         for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(s + (wm * 4 + i) * 512);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[4 + i] = *(const bf16x8*)(s + (8 + wm * 4 + i) * 512);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) f[8 + j] = *(const bf16x8*)(s + (16 + wn * 2 + j) * 512);
+        for (int j = 0; j < 2; ++j) f[4 + j] = *(const bf16x8*)(s + (8 + wn * 2 + j) * 512);
     };
-    auto mfmas = [&](Frag& f, bool interleave) {
+    // One stage (step kt, q = kt % 4): wait until this wave's loads of stage kt + 1 have
+    // landed (later stages, at most 4, may stay in flight), barrier (every wave's loads of
+    // kt + 1 are in LDS and every wave is done with stage kt - 1, whose slot the next issue
+    // refills), refill, then the 8 bf16 MFMAs of stage kt with the fragment reads of stage
+    // kt + 1 interleaved, the weight blocks' e4m3 copy, and after the group's last step its
+    // 8 e4m3 MFMAs.
+    auto step = [&](auto qc, int kt, Frag& cur, Frag& nxt) {
+        constexpr int q = decltype(qc)::value;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            wait_stages(min(NSM - 3, nk - 2 - kt));
+            __builtin_amdgcn_s_barrier();
+            if (kt + NSM - 1 < nk) issue(kt + NSM - 1);
+            fload(kt + 1, nxt);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mma32(f[i], f[8 + j], acc[i][j]);
+            for (int j = 0; j < 2; ++j) acc[i][j] = mma32(cur[i], cur[4 + j], acc[i][j]);
+        if (more) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mma32(f[4 + i], f[8 + j], acc[i][j]);
-        if (interleave) {
-#pragma unroll
-            for (int g = 0; g < 10; ++g) {
+            for (int g = 0; g < 6; ++g) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
-    };
-    // One stage: wait until this wave's loads of stage kt + 1 have landed (later stages,
-    // at most 3, may stay in flight), barrier (every wave's loads of kt + 1 are in LDS and
-    // every wave is done with stage kt - 1, whose slot the next issue refills), refill, then
-    // the MFMAs of stage kt with the fragment reads of stage kt + 1.
-    auto step = [&](int kt, Frag& cur, Frag& nxt) {
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const int ahead = min(NS - 3, nk - 2 - kt);
-            if (ahead >= 3) NC_WAIT_VM(9);
-            else if (ahead == 2) NC_WAIT_VM(6);
-            else if (ahead == 1) NC_WAIT_VM(3);
-            else NC_WAIT_VM(0);
-            __builtin_amdgcn_s_barrier();
-            if (kt + NS - 1 < nk) issue(kt + NS - 1);
-            fload(kt + 1, nxt);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            int d0, d1;
+            e4m3x8_bf16(cur[4 + j], winv, d0, d1);
+            wq[j][2 * q] = d0;
+            wq[j][2 * q + 1] = d1;
         }
-        mfmas(cur, more);
+        if constexpr (q == 3) {
+            const unsigned char* ls = lring + ((kt >> 2) % NSL) * LST + lane * 32;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bf16x8 l0 = *(const bf16x8*)(ls + (wm * 4 + i) * 2048);
+                const bf16x8 l1 = *(const bf16x8*)(ls + (wm * 4 + i) * 2048 + 16);
+                const u32x4 u0 = __builtin_bit_cast(u32x4, l0), u1 = __builtin_bit_cast(u32x4, l1);
+                const i32x8 la = {(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3], (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mma32_e4m3(la, wq[j], acc[i][j], sa, sb);
+            }
+        }
     };
 
-    // Prologue: stages 0 .. NS-2 in flight (3 loads per wave each), stage 0's fragments.
+    // Prologue: stages 0 .. NSM-2 in flight, stage 0's fragments.
 #pragma unroll
-    for (int kt = 0; kt < NS - 1; ++kt)
+    for (int kt = 0; kt < NSM - 1; ++kt)
         if (kt < nk) issue(kt);
-    if (nk > 4) NC_WAIT_VM(12);
-    else if (nk > 3) NC_WAIT_VM(9);
-    else if (nk > 2) NC_WAIT_VM(6);
-    else if (nk > 1) NC_WAIT_VM(3);
-    else NC_WAIT_VM(0);
+    wait_stages(min(NSM - 2, nk - 1));
+    // (the row statistics were loaded before the stages, so they have landed too: one
+    // register instead of MAXP stays live across the main loop)
+    float ssum = 0.f;
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) ssum += ssp[q];
     __builtin_amdgcn_s_barrier();
     Frag f0, f1;
     fload(0, f0);
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, f0, f1);
-        if (kt + 1 < nk) step(kt + 1, f1, f0);
+    for (int kt = 0; kt < nk; kt += 4) {  // nk is a multiple of 4
+        step(std::integral_constant<int, 0>{}, kt, f0, f1);
+        step(std::integral_constant<int, 1>{}, kt + 1, f1, f0);
+        step(std::integral_constant<int, 2>{}, kt + 2, f0, f1);
+        step(std::integral_constant<int, 3>{}, kt + 3, f1, f0);
     }
-    __syncthreads();  // every wave is done with the ring (all its loads have landed)
+    __syncthreads();  // every wave is done with the rings (all its loads have landed)
     if (p.tail && !tail_join(p, tw.slot, acc, (int*)lds + 8192)) return;  // workgroup-uniform
     if (EPI == EPI_RELU2 || EPI == EPI_SOFTCAP) {
-        if (tid < TBM) {
-            float s = 0.f;
-#pragma unroll
-            for (int q = 0; q < MAXP; ++q) s += ssp[q];
-            rs[tid] = 1.0f / sqrtf(s / (float)p.K + p.eps);
-        }
+        if (tid < TBM) rs[tid] = 1.0f / sqrtf(ssum / (float)p.K + p.eps);
         __syncthreads();
     }
     if constexpr (EPI == EPI_RELU2 || EPI == EPI_RESID) tile_epilogue4<EPI>(p, acc, m0, n0, rs, red);
@@ -772,6 +832,7 @@ static hipError_t launch_e(DType dt, const GemmArgs& a_in, hipStream_t st) {
     if (dt == BF16) {
         if (a.k_split != 1 || a.K % 32) return hipErrorInvalidValue;
         if ((EPI == EPI_RELU2 || EPI == EPI_RESID) && (a.N % 4 || a.ldo % 4)) return hipErrorInvalidValue;
+        if ((a.A_lo && a.K % 64) || (a.out_lo && a.ldo % 64)) return hipErrorInvalidValue;  // lo8 layout
         if constexpr (EPI != EPI_STORE) {
             if (a.A_lo) {
                 NC_TLAUNCH((gemm_bf16_comp_kernel<EPI>), grid, dim3(512), 0, st, a);
@@ -784,6 +845,29 @@ static hipError_t launch_e(DType dt, const GemmArgs& a_in, hipStream_t st) {
         NC_TLAUNCH((gemm_f32_kernel<EPI>), grid, dim3(256), 0, st, a);
     }
     return hipGetLastError();
+}
+
+// Largest |w| of a bf16 weight: grid-stride maximum, one atomic per wave on the float's bit
+// pattern (non-negative floats order like their bit patterns).
+__global__ __launch_bounds__(256) void absmax_kernel(const bf16* w, long long n, unsigned* out) {
+    float m = 0.f;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+        m = fmaxf(m, fabsf((float)w[i]));
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) atomicMax(out, __float_as_uint(m));
+}
+
+hipError_t launch_absmax(const void* w, long long n, unsigned* out, hipStream_t st) {
+    if (n < 1) return hipSuccess;
+    const long long blocks = std::min<long long>(1024, (n + 255) / 256);
+    hipLaunchKernelGGL(absmax_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const bf16*)w, n, out);
+    return hipGetLastError();
+}
+
+int lo8_weight_exp(float absmax) {
+    if (!(absmax > 0.f)) return 16;
+    const int s = (int)std::floor(std::log2(448.0 / (double)absmax));
+    return std::max(-16, std::min(16, s));
 }
 
 int gemm_tile_n() { return TBN; }

@@ -49,6 +49,26 @@ __host__ __device__ inline long long blocked_index(int n, int k, int K) {
 }
 hipError_t launch_repack(DType dt, const void* src, void* dst, int N, int K, hipStream_t st);
 
+// Low parts of the compensated prefill operands (bf16 model): lo = a - bf16(a) is stored as
+// one e4m3 byte, e4m3(lo 2^LO8_SHIFT) clamped to +-448 (|lo| <= 2^-8 |a|, so the scaled value
+// stays in range for |a| < 448), in the operand layout of the 32x32x64 fp8 MFMA: row block
+// m / 32 and 64-deep group k / 64 form a 2 KB block whose 64 lanes hold 32 bytes each;
+// lane (m % 32) + 32 ((k % 16) / 8) holds byte (k % 64) / 16 * 8 + k % 8, i.e. the 8 values
+// of its row and k half in each of the group's four 16-deep steps, in step order.  The
+// weight side of that MFMA is made from the bf16 fragments of the same four steps in
+// registers, so both operands pair the same k in the same lane byte.  K % 64 == 0.
+constexpr int LO8_SHIFT = 8;
+__host__ __device__ inline long long lo8_index(int m, int k, int K) {
+    return ((long long)(m >> 5) * (K >> 6) + (k >> 6)) * 2048 + ((m & 31) + 32 * ((k >> 3) & 1)) * 32 +
+           ((k >> 4) & 3) * 8 + (k & 7);
+}
+// Largest |w| of n bf16 values, as the bit pattern of a non-negative float, max-ed into *out
+// (which the caller zeroes first).
+hipError_t launch_absmax(const void* w, long long n, unsigned* out, hipStream_t st);
+// Exponent s of the weight's e4m3 copy in the fp8 low-part product: e4m3(w 2^s) with
+// |w| 2^s <= 448 for the largest |w| (s in [0, 12]).
+int lo8_weight_exp(float absmax);
+
 // RESID with the later version's blocks (x0 non-null): the new residual is
 //   x = ra (x_old + C) + rb x0 + rc xb        (xb null: no last term)
 // with x0, xb fp32 [M][ldo] like x; xb_out (if set) receives a copy of the new x.
@@ -71,8 +91,8 @@ __device__ inline float resid_value(const ResidExtra* e, long long o, float x_ol
 
 struct GemmArgs {
     // bf16: blocked [ceil(M/32)][K/16][32][16] (whole 32-row blocks; lda unused);
-    // fp32: [M][lda], K contiguous.  The same holds for A_lo and for the dtype outputs
-    // out_t / out_lo of RELU2 and RESID (blocked with K = ldo for bf16).
+    // fp32: [M][lda], K contiguous.  The same holds for the dtype outputs out_t of RELU2 and
+    // RESID (blocked with K = ldo for bf16); low parts: see A_lo.
     const void* A;
     const void* B;  // blocked weight (see above), Npad rows
     int M, N, K, lda, Npad;
@@ -85,12 +105,16 @@ struct GemmArgs {
     int ss_in_parts, ss_stride;
     float* ss_out;      // RESID: ss_out[tile_n * ss_stride + m]
     float eps, cap;
-    // Compensated operand (bf16 only): A_lo (laid out like A) holds a - bf16(a) in bf16, and the
-    // product is taken over both parts (A + A_lo) W^T.  Null: plain A.
+    // Compensated operand (bf16 only): A_lo holds a - bf16(a), and the product is taken over
+    // both parts (A + A_lo) W^T.  Null: plain A.
+    // bf16: A_lo holds the e4m3 low parts in the lo8 layout (see lo8_index), and w8_exp is
+    // the exponent of B's e4m3 copy (lo8_weight_exp of B's largest |w|).
     const void* A_lo;
-    // RELU2 / RESID: also write value - dtype(value) in dtype here (the low part a later
-    // compensated product reads).  Null: not written.
+    // RELU2 / RESID: also write value - dtype(value) here (the low part a later
+    // compensated product reads; bf16: e4m3 in the lo8 layout with K = ldo).  Null: not
+    // written.
     void* out_lo;
+    int w8_exp;
     ResidExtra rx;  // RESID: the later version's residual scaling and backout
     // Tail split (bf16): when the tiles leave the last round of workgroups (one per CU) at
     // most half full, that round's tiles run as two K halves each; the half that arrives
@@ -126,8 +150,8 @@ struct DecGemmArgs {  // pointers first, then 4-byte fields: no padding (120 byt
     const float* ss_in;
     float* ss_out;
     int32_t* lens_inc;  // if set, workgroup 0 adds one to lens_inc[0..M) (end of a decode step)
-    const void* A_lo;   // compensated operand, as in GemmArgs (bf16 only; null: plain A)
-    void* out_lo;       // RELU2 / RESID low-part output, as in GemmArgs (null: not written)
+    const void* A_lo;   // compensated operand a - bf16(a), bf16 blocked like A (bf16 only; null: plain A)
+    void* out_lo;       // RELU2 / RESID low-part output, bf16 blocked like out_t (null: not written)
     // split-K workspace, dec_gemm_part_elems(M, N, K) elements: DEC_PART_CTRS int32 arrival
     // counters (zero before the first launch; every launch leaves them at zero), then the
     // fp32 partial products

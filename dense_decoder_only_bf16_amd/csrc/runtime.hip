@@ -94,8 +94,10 @@ struct nc_model {
     void* arena = nullptr;
     const void* wte = nullptr;
     const void* lm = nullptr;
+    int e8_lm = 0;
     struct Layer {
         const void *wqkv, *wo, *wfc, *wproj;
+        int e8_fc = 0, e8_proj = 0;  // exponents of the e4m3 weight copies (compensated prefill)
     };
     std::vector<Layer> layers;
     float* rope_cos = nullptr;
@@ -420,14 +422,14 @@ nc_status decode_gemm(nc_kv* kv, Epi epi, const DecGemmArgs& a, hipStream_t st, 
     return NC_OK;
 }
 
-// Prefill projection: flops 2 M N K of the model; bytes: A (both parts when compensated),
-// weights and the outputs once.
+// Prefill projection: flops 2 M N K of the model; bytes: A (and its one-byte e4m3 low part
+// when compensated), weights and the outputs once (low parts one byte each).
 hipError_t prefill_gemm(nc_model* m, Epi epi, const GemmArgs& g, hipStream_t st) {
     const double es = (double)m->esz, M = g.M, N = g.N, K = g.K;
     const double out = ((epi == EPI_STORE || epi == EPI_SOFTCAP) ? M * N * 4
                         : (epi == EPI_RELU2 ? M * N * es : M * N * (8 + es))) +
-                       (g.out_lo ? M * N * es : 0);
-    return timed(NC_KC_PREFILL_GEMM, M * K * es * (g.A_lo ? 2 : 1) + N * K * es + out, 2 * M * N * K, st,
+                       (g.out_lo ? M * N : 0);
+    return timed(NC_KC_PREFILL_GEMM, M * K * es + (g.A_lo ? M * K : 0) + N * K * es + out, 2 * M * N * K, st,
                  [&] { return launch_gemm(m->dt, epi, g, st); });
 }
 
@@ -622,6 +624,29 @@ nc_status nc_model_create(const nc_config* cfg, const void* const* weights, nc_m
         }
         if (ce == hipSuccess) ce = launch_repack(m->dt, weights[nw - 1], p, (int)V, (int)d, 0);
         m->lm = p;
+        if (ce == hipSuccess && m->dt == BF16) {
+            // largest |w| of the compensated products' weights (MLP and LM head): the exponent
+            // of their e4m3 copies in the prefill's low-part product
+            const int L = cfg->n_layer;
+            unsigned* amax = nullptr;
+            ce = hipMalloc((void**)&amax, (2 * L + 1) * sizeof(unsigned));
+            if (ce == hipSuccess) ce = hipMemset(amax, 0, (2 * L + 1) * sizeof(unsigned));
+            for (int l = 0; l < L && ce == hipSuccess; ++l) {
+                const void* const* w = weights + 1 + 6 * l;
+                ce = launch_absmax(w[4], (long long)F * d, amax + 2 * l, 0);
+                if (ce == hipSuccess) ce = launch_absmax(w[5], (long long)d * F, amax + 2 * l + 1, 0);
+            }
+            if (ce == hipSuccess) ce = launch_absmax(weights[nw - 1], (long long)V * d, amax + 2 * L, 0);
+            std::vector<unsigned> h(2 * L + 1, 0);
+            if (ce == hipSuccess) ce = hipMemcpy(h.data(), amax, h.size() * sizeof(unsigned), hipMemcpyDeviceToHost);
+            if (amax) (void)hipFree(amax);
+            auto as_float = [](unsigned u) { float f; std::memcpy(&f, &u, 4); return f; };
+            for (int l = 0; l < L && ce == hipSuccess; ++l) {
+                m->layers[l].e8_fc = lo8_weight_exp(as_float(h[2 * l]));
+                m->layers[l].e8_proj = lo8_weight_exp(as_float(h[2 * l + 1]));
+            }
+            m->e8_lm = lo8_weight_exp(as_float(h[2 * L]));
+        }
         if (ce == hipSuccess) ce = hipDeviceSynchronize();
         // RoPE tables: angle p * base^(-2i/hd), evaluated in double, stored fp32.
         const size_t half = hd / 2, S = cfg->max_seq;
@@ -992,12 +1017,12 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
             // FC + norm + relu^2 (compensated operand)
             g.A = kv->ws.act; g.lda = d; g.B = L.wfc; g.N = F; g.K = d; g.Npad = F;
             g.out_t = kv->ws.u; g.ldo = F; g.ss_in = kv->ws.ss_b; g.ss_in_parts = parts_d; g.ss_stride = (int)kv->ws.cap_m;
-            g.A_lo = kv->ws.act_lo; g.out_lo = kv->ws.u_lo;
+            g.A_lo = kv->ws.act_lo; g.out_lo = kv->ws.u_lo; g.w8_exp = L.e8_fc;
             LAUNCH(prefill_gemm(m, EPI_RELU2, g, st));
             // PROJ + residual (compensated operand)
             g.A = kv->ws.u; g.lda = F; g.B = L.wproj; g.N = d; g.K = F; g.Npad = d;
             g.out_f32 = kv->ws.x; g.out_t = kv->ws.act; g.ldo = d; g.ss_out = kv->ws.ss_a; g.ss_stride = (int)kv->ws.cap_m;
-            g.A_lo = kv->ws.u_lo;
+            g.A_lo = kv->ws.u_lo; g.w8_exp = L.e8_proj;
             g.out_lo = (l == c.n_layer - 1) ? kv->ws.act_lo : nullptr;  // LM head operand, compensated
             g.rx = proj_resid_extra(m, kv->ws, l);
             LAUNCH(prefill_gemm(m, EPI_RESID, g, st));
@@ -1007,7 +1032,7 @@ nc_status nc_prefill(nc_model* m, const int32_t* tokens, int32_t B, int32_t T, n
         }
         if (logits) {
             GemmArgs g{};
-            g.A = kv->ws.act; g.A_lo = kv->ws.act_lo; g.lda = d; g.B = m->lm; g.M = Mi; g.N = V; g.K = d;
+            g.A = kv->ws.act; g.A_lo = kv->ws.act_lo; g.w8_exp = m->e8_lm; g.lda = d; g.B = m->lm; g.M = Mi; g.N = V; g.K = d;
             g.Npad = (V + 31) / 32 * 32; g.k_split = 1;
             g.tail_part = kv->ws.tpart; g.tail_ctr = kv->ws.tctr;
             g.out_f32 = logits; g.ldo = V; g.ss_in = kv->ws.ss_a; g.ss_in_parts = ss_a_parts;
