@@ -115,24 +115,24 @@ KERNEL_NAMES = {"decode_gemm": "dec_gemm_wide_kernel + dec_reduce4_kernel / dec_
 # (FETCH_SIZE, WRITE_SIZE) scaled by a plain-copy calibration, valid only for the kernel
 # sources they were taken with (hash of the listed files); otherwise the report says null.
 TRAFFIC = {
-    ("d20", "prefill_gemm"): {"bytes_per_launch": 2.9474e+09, "profile": "profiles/d20_pmc_traffic.md",
+    ("d20", "prefill_gemm"): {"bytes_per_launch": 2.5061e+09, "profile": "profiles/d20_pmc_traffic.md",
                              "sources": ('csrc/gemm.hip', 'csrc/common.h', 'csrc/kernels.h'),
-                             "sha": "9fc4209b4a7c2e7f"},
+                             "sha": "5b9355c020fafcab"},
     ("d20", "decode_gemm"): {"bytes_per_launch": 2.0057e+07, "profile": "profiles/d20_pmc_traffic.md",
                              "sources": ('csrc/gemv.hip', 'csrc/rowops.hip', 'csrc/finish.h', 'csrc/common.h', 'csrc/kernels.h'),
-                             "sha": "6bcad75aafc8e281"},
-    ("d20", "decode_attn"): {"bytes_per_launch": 7.2360e+07, "profile": "profiles/d20_pmc_traffic.md",
+                             "sha": "0327d87d5a36dc8b"},
+    ("d20", "decode_attn"): {"bytes_per_launch": 7.2362e+07, "profile": "profiles/d20_pmc_traffic.md",
                              "sources": ('csrc/attention.hip', 'csrc/common.h', 'csrc/kernels.h'),
-                             "sha": "57be915b2a74c7f7"},
-    ("d26", "prefill_gemm"): {"bytes_per_launch": 2.0919e+09, "profile": "profiles/d26_prefill_pmc.md",
+                             "sha": "f54dc1c6d04247cb"},
+    ("d26", "prefill_gemm"): {"bytes_per_launch": 1.7564e+09, "profile": "profiles/d26_prefill_pmc.md",
                              "sources": ('csrc/gemm.hip', 'csrc/common.h', 'csrc/kernels.h'),
-                             "sha": "9fc4209b4a7c2e7f"},
+                             "sha": "5b9355c020fafcab"},
     ("d30", "decode_attn"): {"bytes_per_launch": 8.5875e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
                              "sources": ('csrc/attention.hip', 'csrc/common.h', 'csrc/kernels.h'),
-                             "sha": "57be915b2a74c7f7"},
-    ("d30", "decode_gemm"): {"bytes_per_launch": 4.7365e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
+                             "sha": "f54dc1c6d04247cb"},
+    ("d30", "decode_gemm"): {"bytes_per_launch": 4.7366e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
                              "sources": ('csrc/gemv.hip', 'csrc/rowops.hip', 'csrc/finish.h', 'csrc/common.h', 'csrc/kernels.h'),
-                             "sha": "6bcad75aafc8e281"},
+                             "sha": "0327d87d5a36dc8b"},
 }
 
 
