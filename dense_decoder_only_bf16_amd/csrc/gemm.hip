@@ -671,6 +671,7 @@ void gemm_bf16_comp_kernel(GemmArgs p) {
         for (int j = 0; j < 2; ++j) {
             int d0, d1;
             e4m3x8_bf16(cur[4 + j], winv, d0, d1);
+            asm volatile("" ::"v"(d0), "v"(d1));  // converted in this step, not all at the group's end
             wq[j][2 * q] = d0;
             wq[j][2 * q + 1] = d1;
         }
