@@ -398,19 +398,25 @@ static hipError_t dec_t(const DecGemmArgs& a, hipStream_t st, int variant, const
 // ------------------------------------------------------------ wide (32 < M <= 128) -------
 // With up to 128 rows, a 32-column workgroup that reads all of A moves several times more
 // activation bytes (out of L2) than weight bytes, and the L2s become the bound.  For bf16
-// and M > 32 a workgroup therefore owns 128 columns (4 waves x one 32-column weight block)
-// and one slice of K, and its waves share the activation operand through LDS: every stage
-// of an LDS ring holds WKC 16-deep steps of the A blocks (both parts when compensated) and
-// of the 4 waves' weight blocks, all filled by direct-to-LDS 1 KB loads issued WNS - 1
-// stages ahead.  The ring is short (3 stages) so that two or three workgroups fit a CU:
+// and M > 32 a workgroup therefore owns 256 or 128 columns (8 or 4 waves x one 32-column
+// weight block) and one slice of K, and its waves share the activation operand through
+// LDS: every stage of an LDS ring holds WKC 16-deep steps of the A blocks (both parts when
+// compensated) and of the waves' weight blocks, all filled by direct-to-LDS 1 KB loads
+// issued WNS - 1 stages ahead.  The ring is short (3 stages) so that two or three workgroups fit a CU:
 // that measured 5-10% faster on the projections than one workgroup with a 6-stage ring,
 // and 40% faster on the LM head, whose hundreds of tiles then run in one round.  The LM head (softcap; N = vocab gives hundreds of column tiles) runs its
 // whole K in one workgroup and its epilogue here.  The other products split K into slices
 // so that there are a few hundred workgroups; their fp32 partial products go to `part` and
 // dec_reduce4_kernel (or, for the raw QKV product, the QKV finish) adds the slices in a
 // fixed order and runs the epilogue.
-constexpr int WBN = 128;  // columns per workgroup
-constexpr int WKC = 2;    // 16-deep steps per LDS stage
+// Waves per workgroup (one 32-column weight block each) for FM row tiles: 8 at up to 64
+// rows, where the activation operand is small and sharing it over twice the columns halves
+// its LDS fills per weight byte (d20, 64 rows: decode projections 9.57 -> 9.06 us per
+// operation); 4 at more rows, where 8 waves measured slower (d30, 128 rows: 13.5 -> 14.3 us).
+constexpr int wide_waves(int fm) { return fm <= 2 ? 8 : 4; }
+// 16-deep steps per LDS stage: 2, or 4 where a 2-step stage's blocks would not split
+// evenly over the waves (ablk: A blocks per step)
+constexpr int wide_wkc(int ablk, int nw) { return (2 * (ablk + nw)) % nw == 0 ? 2 : 4; }
 constexpr int WNS = 3;    // stages in the ring (two or three resident workgroups per CU)
 
 struct WideShape {
@@ -425,14 +431,15 @@ struct WideShape {
 static WideShape wide_shape(Epi epi, int M, bool lo, int N, int K) {
     WideShape w;
     const int ksteps = K / 16;  // >= 4 (K >= 64)
-    w.tiles = (N + WBN - 1) / WBN;
+    const int fm = M <= 64 ? 2 : 4, nw = wide_waves(fm);
+    w.tiles = (N + 32 * nw - 1) / (32 * nw);
     if (epi == EPI_SOFTCAP) {
         w.splits = 1;
         w.per = ksteps;
         return w;
     }
-    const int fm = M <= 64 ? 2 : 4;
-    const int stage_kb = WKC * (fm * (lo ? 2 : 1) + 4);
+    const int ablk = fm * (lo ? 2 : 1), WKC = wide_wkc(ablk, nw);
+    const int stage_kb = WKC * (ablk + nw);
     const int slots = 256 * std::max(1, 160 / (WNS * stage_kb));
     const int smax = std::max(2, std::min(slots / w.tiles, ksteps / (2 * WKC)));
     const double a_bytes = (double)M * K * 2 * (lo ? 2 : 1), w_bytes = (double)N * K * 2;
@@ -451,12 +458,14 @@ static WideShape wide_shape(Epi epi, int M, bool lo, int N, int K) {
 }
 
 template <int FM, bool LO, int EPI>
-__global__ __launch_bounds__(256) void dec_gemm_wide_kernel(DecGemmArgs p, int splits, int per) {
+__global__ __launch_bounds__(64 * wide_waves(FM)) void dec_gemm_wide_kernel(DecGemmArgs p, int splits, int per) {
+    constexpr int WNW = wide_waves(FM), WBN = 32 * WNW;
     constexpr int NA = LO ? 2 : 1;
     constexpr int ABLK = FM * NA;          // A blocks per 16-deep step
-    constexpr int BPS = WKC * (ABLK + 4);  // 1 KB blocks per stage: A blocks, then W blocks
-    constexpr int BPW = BPS / 4;           // blocks each wave loads per stage
-    static_assert(BPS % 4 == 0, "stage must split evenly over the 4 waves");
+    constexpr int WKC = wide_wkc(ABLK, WNW);
+    constexpr int BPS = WKC * (ABLK + WNW);  // 1 KB blocks per stage: A blocks, then W blocks
+    constexpr int BPW = BPS / WNW;           // blocks each wave loads per stage
+    static_assert(BPS % WNW == 0, "stage must split evenly over the waves");
     static_assert((WNS - 2) * BPW <= 63, "vmcnt range");
     constexpr int STAGE = BPS * 512;       // bf16 elements per stage
     // one LDS object (the ring, then the LM head's row scales): with a second one the
@@ -478,34 +487,34 @@ __global__ __launch_bounds__(256) void dec_gemm_wide_kernel(DecGemmArgs p, int s
     const bf16* W = (const bf16*)p.W;
     (void)splits;
     if (p.lens_inc && blockIdx.x == 0 && blockIdx.y == 0)  // end of a decode step
-        for (int r = tid; r < p.M; r += 256) p.lens_inc[r] += 1;
+        for (int r = tid; r < p.M; r += 64 * WNW) p.lens_inc[r] += 1;
 
-    if (EPI == EPI_SOFTCAP) {  // row scales of the final norm: wave w does rows w + 4 j,
+    if (EPI == EPI_SOFTCAP) {  // row scales of the final norm: wave w does rows w + WNW j,
         // lanes over the partial sums, every load of every row issued before any sum
-        constexpr int RW = 8 * FM;
+        constexpr int RW = 32 * FM / WNW;
         float s[RW];
 #pragma unroll
         for (int j = 0; j < RW; ++j) s[j] = 0.f;
         for (int q = lane; q < p.ss_in_parts; q += 64)
 #pragma unroll
-            for (int j = 0; j < RW; ++j) s[j] += p.ss_in[(long long)q * p.ss_stride + min(wave + 4 * j, p.M - 1)];
+            for (int j = 0; j < RW; ++j) s[j] += p.ss_in[(long long)q * p.ss_stride + min(wave + WNW * j, p.M - 1)];
 #pragma unroll
         for (int j = 0; j < RW; ++j) {
             const float t = wave_sum(s[j]);
-            if (lane == 0) rs[wave + 4 * j] = 1.0f / sqrtf(t / (float)p.K + p.eps);
+            if (lane == 0) rs[wave + WNW * j] = 1.0f / sqrtf(t / (float)p.K + p.eps);
         }
         __syncthreads();
     }
 
     // Stage t: block q < WKC ABLK is A (step q / ABLK, row block (q % ABLK) / NA, part
-    // q % NA); the rest are W (step (q - WKC ABLK) / 4, column block of wave
-    // (q - WKC ABLK) % 4).  Steps past the slice and blocks past the matrices load clamped
+    // q % NA); the rest are W (step (q - WKC ABLK) / WNW, column block of wave
+    // (q - WKC ABLK) % WNW).  Steps past the slice and blocks past the matrices load clamped
     // addresses whose data is never used.
     auto issue = [&](int t) {
         bf16* sb = lds + (t % WNS) * STAGE;
 #pragma unroll
         for (int u = 0; u < BPW; ++u) {
-            const int q = u * 4 + wave;
+            const int q = u * WNW + wave;
             const bf16* src;
             if (q < WKC * ABLK) {
                 const int kc = q / ABLK, r = q % ABLK;
@@ -514,8 +523,8 @@ __global__ __launch_bounds__(256) void dec_gemm_wide_kernel(DecGemmArgs p, int s
                 src = ((r % NA) ? AL : A) + ((long long)rb * ksteps + step) * 512 + lane * 8;
             } else {
                 const int q2 = q - WKC * ABLK;
-                const int step = min(s0 + t * WKC + q2 / 4, s1 - 1);
-                const int nb = min(n0 / 32 + q2 % 4, nblk_w - 1);
+                const int step = min(s0 + t * WKC + q2 / WNW, s1 - 1);
+                const int nb = min(n0 / 32 + q2 % WNW, nblk_w - 1);
                 src = W + ((long long)nb * ksteps + step) * 512 + lane * 8;
             }
             __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(sb + q * 512), 16, 0, 0);
@@ -535,7 +544,7 @@ __global__ __launch_bounds__(256) void dec_gemm_wide_kernel(DecGemmArgs p, int s
 #pragma unroll
         for (int kc = 0; kc < WKC; ++kc) {
             if (s0 + t * WKC + kc < s1) {
-                const bf16x8 wf = *(const bf16x8*)(sb + (WKC * ABLK + kc * 4 + wave) * 512 + l32 * 16 + 8 * hh);
+                const bf16x8 wf = *(const bf16x8*)(sb + (WKC * ABLK + kc * WNW + wave) * 512 + l32 * 16 + 8 * hh);
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -649,8 +658,8 @@ static hipError_t wide_t(const DecGemmArgs& args, hipStream_t st) {
     DecGemmArgs a = args;
     if (a.part) a.part += DEC_PART_CTRS;  // the partials follow the counters
     dim3 g(w.tiles, w.splits);
-    if (a.M <= 64) NC_TLAUNCH((dec_gemm_wide_kernel<2, LO, EPI>), g, dim3(256), 0, st, a, w.splits, w.per);
-    else NC_TLAUNCH((dec_gemm_wide_kernel<4, LO, EPI>), g, dim3(256), 0, st, a, w.splits, w.per);
+    if (a.M <= 64) NC_TLAUNCH((dec_gemm_wide_kernel<2, LO, EPI>), g, dim3(64 * wide_waves(2)), 0, st, a, w.splits, w.per);
+    else NC_TLAUNCH((dec_gemm_wide_kernel<4, LO, EPI>), g, dim3(64 * wide_waves(4)), 0, st, a, w.splits, w.per);
     // the raw QKV product's slices are added by the QKV finish (dec_gemm_store_slices)
     if ((EPI == EPI_RELU2 || EPI == EPI_RESID) && w.splits > 1) {
         if (a.N % 4) return hipErrorInvalidValue;
