@@ -13,7 +13,7 @@
 // the epilogues fused (the QKV finish is a separate row kernel).  Decode (M = batch rows)
 // uses the weight-streaming decode products with the elementwise epilogues fused (at most
 // 32 rows: K split over the waves of one workgroup, the QKV finish in the QKV product's
-// epilogue; more rows: 128-column workgroups with K split across workgroups, a split-K
+// epilogue; more rows: 256- or 128-column workgroups with K split across workgroups, a split-K
 // finish kernel, and a separate QKV finish kernel); the LM head's launch also advances the
 // row lengths.  The whole decode step is
 // captured once per (token buffer, logit buffer) pair as a HIP graph and replayed.
