@@ -866,7 +866,8 @@ hipError_t launch_absmax(const void* w, long long n, unsigned* out, hipStream_t 
 }
 
 int lo8_weight_exp(float absmax) {
-    if (!(absmax > 0.f)) return 16;
+    if (!(absmax > 0.f)) return 16;       // all zero (or NaN)
+    if (!(absmax <= 3.0e38f)) return -16;  // infinite weights: the smallest scale
     const int s = (int)std::floor(std::log2(448.0 / (double)absmax));
     return std::max(-16, std::min(16, s));
 }
