@@ -15,8 +15,9 @@
 // softmax statistics of a query then live in one lane (plus its partner half-wave), and
 // the probabilities already sit in the B-operand layout of O^T = V^T P^T once the keys of a
 // 16/32-deep contraction step are taken in the order the output layout holds them.  V is
-// kept transposed in the cache ([hd][positions]) so that the A operand of O^T (8 keys of
-// one feature) is two short contiguous reads.
+// kept transposed in the cache ([hd][positions]) so that the A operand of O^T (the keys of
+// one feature that a step contracts) is contiguous: in prefill the score tile's rows are
+// taken in a permuted key order (pf_kperm) so that it is one 16-byte read.
 #include "common.h"
 #include "kernels.h"
 
@@ -33,6 +34,15 @@ namespace nc {
 // offs[b]: the tokens already in the row's cache, 0 for a first prefill) and keys are
 // cache positions.  Sliding window: a query at position p sees keys p - win .. p (win
 // = 2^30: the whole causal context).
+// Key order of a 32-key score tile: A-operand row i of S^T = K Q^T reads key pf_kperm(i)
+// (bits 2 and 3 of i swapped).  Output register r of lane (l32, hh) then holds key
+// 16 (r / 8) + 8 hh + r % 8, so the eight scores a lane feeds into one 16-deep step of
+// O^T = V^T P^T are eight consecutive keys, whose V^T operand is one 16-byte read.
+__device__ __forceinline__ int pf_kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+// K chunk swizzle: the eight rows that eight neighbouring lanes read (keys pf_kperm(8 g + j),
+// j = 0..7) get eight different values, pf_kswz(pf_kperm(x)) = x % 8.
+__device__ __forceinline__ int pf_kswz(int key) { return (key & 3) | ((key & 8) >> 1); }
+
 template <typename T, int HD, int JN>
 __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __restrict__ q,
                                                            const T* __restrict__ kc,
@@ -100,8 +110,8 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
     constexpr int VCH = HD * (KB / 8) / NT;
     static_assert(KCH >= 1 && VCH >= 1, "block too small for the workgroup");
 
-    // LDS layouts (16-byte chunks): K row `key` holds chunk ch at chunk position
-    // ch ^ (key % 8); V^T row d (KB keys) holds chunk ch at position ch ^ (d % 8), so that
+    // LDS layouts (8-element chunks): K row `key` holds chunk ch at chunk position
+    // ch ^ pf_kswz(key); V^T row d (KB keys) holds chunk ch at position ch ^ (d % 8), so that
     // the operand reads below are spread over the banks.
     // bf16: block kbi goes straight into buffer `bufi` with 1 KB direct-to-LDS loads; lane l
     // of a load writes chunk position l of its 1 KB and so fetches the chunk that the
@@ -117,7 +127,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 #pragma unroll
         for (int j = 0; j < KJ; ++j) {
             const int p = (wave * KJ + j) * 64 + lane;
-            const int key = p / CPRK, ch = (p % CPRK) ^ (key & 7);
+            const int key = p / CPRK, ch = (p % CPRK) ^ pf_kswz(key);
             __builtin_amdgcn_global_load_lds((gvoid*)(kb_base + (long long)(k0 + key) * HD + ch * 8),
                                              (lvoid*)(kl + (wave * KJ + j) * 512), 16, 0, 0);
         }
@@ -173,7 +183,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 #pragma unroll
             for (int i = 0; i < KCH; ++i) {
                 int c = tid + i * NT, key = c / CPRK, ch = c % CPRK;
-                *(CT*)(&smem[key * HD + ((ch ^ (key & 7)) * 8)]) = rk[i];
+                *(CT*)(&smem[key * HD + ((ch ^ pf_kswz(key)) * 8)]) = rk[i];
             }
 #pragma unroll
             for (int i = 0; i < VCH; ++i) {
@@ -195,8 +205,8 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
             for (int jn = 0; jn < JN; ++jn) sacc[mt][jn] = zero_vec<f32x16>();
 #pragma unroll
             for (int s = 0; s < KSTEPS; ++s) {
-                const int key = mt * 32 + l32, ch = 2 * s + hh;
-                CT kf = *(const CT*)(&Ks[key * HD + ((ch ^ (key & 7)) * 8)]);
+                const int key = mt * 32 + pf_kperm(l32), ch = 2 * s + hh;
+                CT kf = *(const CT*)(&Ks[key * HD + ((ch ^ (l32 & 7)) * 8)]);  // l32 % 8 = pf_kswz(key)
 #pragma unroll
                 for (int jn = 0; jn < JN; ++jn) sacc[mt][jn] = mma32(kf, qf[jn][s], sacc[mt][jn]);
             }
@@ -206,8 +216,8 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
         // p = 2^(c s - c m) with c = log2(e)/sqrt(hd), one FMA per score.  Only a block that
         // reaches past a query of this wave (the diagonal), past Kn, or before the window
         // start of a query of this wave needs the mask.  A query whose keys in the blocks
-        // so far are all masked keeps an empty state (m = -inf, reference 0).  Row index of
-        // register r in a 32x32 output tile: 8*(r/4) + 4*hh + (r%4).
+        // so far are all masked keeps an empty state (m = -inf, reference 0).  Key of
+        // register r in score tile mt: k0 + 32 mt + 16 (r / 8) + 8 hh + r % 8 (pf_kperm).
         const bool need_mask = (k0 + KB - 1 > p0w) || (k0 + KB > Kn) || (k0 < plast_w - win);  // wave-uniform
 #pragma unroll
         for (int jn = 0; jn < JN; ++jn) {
@@ -218,7 +228,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + mt * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
+                        const int key = k0 + mt * 32 + 16 * (r / 8) + 8 * hh + (r % 8);
                         const float v = (key <= qp && key < Kn && key >= qp - win) ? sacc[mt][jn][r] : -INFINITY;
                         sacc[mt][jn][r] = v;
                         mx = fmaxf(mx, v);
@@ -256,7 +266,9 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
             }
         }
 
-        // O^T += V^T P^T over the block's 64 keys in four 16-deep steps.
+        // O^T += V^T P^T over the block's 64 keys in four 16-deep steps; step t contracts keys
+        // 16 t + 8 hh .. 16 t + 8 hh + 7 in this lane (registers 8 (t % 2) .. + 7 of score
+        // tile t / 2), which V^T row d holds as its chunk 2 t + hh.
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int mt = t / 2, rb = 8 * (t % 2);
@@ -268,16 +280,7 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 #pragma unroll
             for (int md = 0; md < MD; ++md) {
                 const int d = md * 32 + l32;
-                const int u1 = 4 * t + hh, u2 = 4 * t + 2 + hh;  // 4-key units of this lane
-                const int sw = 2 * (d & 7);
-                HT lo = *(const HT*)(&Vs[d * KB + ((u1 ^ sw) * 4)]);
-                HT hi = *(const HT*)(&Vs[d * KB + ((u2 ^ sw) * 4)]);
-                CT vf;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    vf[i] = lo[i];
-                    vf[4 + i] = hi[i];
-                }
+                const CT vf = *(const CT*)(&Vs[d * KB + (((2 * t + hh) ^ (d & 7)) * 8)]);
 #pragma unroll
                 for (int jn = 0; jn < JN; ++jn) oacc[md][jn] = mma32(vf, pf[jn], oacc[md][jn]);
             }
