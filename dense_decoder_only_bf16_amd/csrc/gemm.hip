@@ -632,13 +632,16 @@ void gemm_bf16_comp_kernel(GemmArgs p) {
     const float winv = ldexpf(1.0f, -p.w8_exp);
     const int sa = 127 - LO8_SHIFT, sb = 127 - p.w8_exp;
 
-    typedef bf16x8 Frag[6];  // A blocks 0..3, weight blocks 4..5
+    // A blocks 0..3, weight blocks 4..5, as raw 32-bit words: carried through the loop's
+    // branches as vectors of bf16, the fragments were split into 16-bit halves and packed
+    // again at every step (48 extra VALU instructions per step)
+    typedef u32x4 Frag[6];
     auto fload = [&](int kt, Frag& f) {
         const bf16* s = ring + (kt % NSM) * MST + lane * 8;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(s + (wm * 4 + i) * 512);
+        for (int i = 0; i < 4; ++i) f[i] = *(const u32x4*)(s + (wm * 4 + i) * 512);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) f[4 + j] = *(const bf16x8*)(s + (8 + wn * 2 + j) * 512);
+        for (int j = 0; j < 2; ++j) f[4 + j] = *(const u32x4*)(s + (8 + wn * 2 + j) * 512);
     };
     // One stage (step kt, q = kt % 4): wait until this wave's loads of stage kt + 1 have
     // landed (later stages, at most 4, may stay in flight), barrier (every wave's loads of
@@ -658,7 +661,8 @@ void gemm_bf16_comp_kernel(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mma32(cur[i], cur[4 + j], acc[i][j]);
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = mma32(__builtin_bit_cast(bf16x8, cur[i]), __builtin_bit_cast(bf16x8, cur[4 + j]), acc[i][j]);
         if (more) {
 #pragma unroll
             for (int g = 0; g < 6; ++g) {
@@ -670,7 +674,7 @@ void gemm_bf16_comp_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             int d0, d1;
-            e4m3x8_bf16(cur[4 + j], winv, d0, d1);
+            e4m3x8_bf16(__builtin_bit_cast(bf16x8, cur[4 + j]), winv, d0, d1);
             asm volatile("" ::"v"(d0), "v"(d1));  // converted in this step, not all at the group's end
             wq[j][2 * q] = d0;
             wq[j][2 * q + 1] = d1;
