@@ -115,22 +115,22 @@ KERNEL_NAMES = {"decode_gemm": "dec_gemm_wide_kernel + dec_reduce4_kernel / dec_
 # (FETCH_SIZE, WRITE_SIZE) scaled by a plain-copy calibration, valid only for the kernel
 # sources they were taken with (hash of the listed files); otherwise the report says null.
 TRAFFIC = {
-    ("d20", "prefill_gemm"): {"bytes_per_launch": 2.5036e+09, "profile": "profiles/d20_pmc_traffic.md",
+    ("d20", "prefill_gemm"): {"bytes_per_launch": 2.5033e+09, "profile": "profiles/d20_pmc_traffic.md",
                              "sources": ('csrc/gemm.hip', 'csrc/common.h', 'csrc/kernels.h'),
-                             "sha": "65c52f29cb85db7a"},
+                             "sha": "706ed5f8bdd703e1"},
     ("d20", "decode_gemm"): {"bytes_per_launch": 2.0450e+07, "profile": "profiles/d20_pmc_traffic.md",
                              "sources": ('csrc/gemv.hip', 'csrc/rowops.hip', 'csrc/finish.h', 'csrc/common.h', 'csrc/kernels.h'),
                              "sha": "b2c8f44f8b37a5e7"},
-    ("d20", "decode_attn"): {"bytes_per_launch": 7.2349e+07, "profile": "profiles/d20_pmc_traffic.md",
+    ("d20", "decode_attn"): {"bytes_per_launch": 7.2347e+07, "profile": "profiles/d20_pmc_traffic.md",
                              "sources": ('csrc/attention.hip', 'csrc/common.h', 'csrc/kernels.h'),
                              "sha": "a34f6c8ef3c678e3"},
-    ("d26", "prefill_gemm"): {"bytes_per_launch": 1.7558e+09, "profile": "profiles/d26_prefill_pmc.md",
+    ("d26", "prefill_gemm"): {"bytes_per_launch": 1.7559e+09, "profile": "profiles/d26_prefill_pmc.md",
                              "sources": ('csrc/gemm.hip', 'csrc/common.h', 'csrc/kernels.h'),
-                             "sha": "65c52f29cb85db7a"},
+                             "sha": "706ed5f8bdd703e1"},
     ("d30", "decode_attn"): {"bytes_per_launch": 8.5856e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
                              "sources": ('csrc/attention.hip', 'csrc/common.h', 'csrc/kernels.h'),
                              "sha": "a34f6c8ef3c678e3"},
-    ("d30", "decode_gemm"): {"bytes_per_launch": 4.7362e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
+    ("d30", "decode_gemm"): {"bytes_per_launch": 4.7364e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
                              "sources": ('csrc/gemv.hip', 'csrc/rowops.hip', 'csrc/finish.h', 'csrc/common.h', 'csrc/kernels.h'),
                              "sha": "b2c8f44f8b37a5e7"},
 }
