@@ -66,8 +66,14 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int qb = gridDim.x - 1 - blockIdx.x;  // longest (latest) query blocks first
-    const int head = blockIdx.y, b = blockIdx.z;
+    // Work order over the whole launch (workgroups are dispatched x fastest, then y, then z):
+    // query blocks by decreasing length across every (row, head), so the launch ends on the
+    // shortest blocks (longest-first list scheduling); the (head, row) pairs of one query
+    // block follow each other, head fastest.
+    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int hb = gridDim.y * gridDim.z;
+    const int qb = gridDim.x - 1 - lin / hb;
+    const int head = (lin % hb) % gridDim.y, b = (lin % hb) / gridDim.y;
     const int q0 = qb * BQ;
     const int q0w = q0 + wave * 32 * JN;
     const int off = offs ? offs[b] : 0;  // position of query 0
