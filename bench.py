@@ -121,15 +121,15 @@ TRAFFIC = {
     ("d20", "decode_gemm"): {"bytes_per_launch": 2.0450e+07, "profile": "profiles/d20_pmc_traffic.md",
                              "sources": ('csrc/gemv.hip', 'csrc/rowops.hip', 'csrc/finish.h', 'csrc/common.h', 'csrc/kernels.h'),
                              "sha": "b2c8f44f8b37a5e7"},
-    ("d20", "decode_attn"): {"bytes_per_launch": 7.2347e+07, "profile": "profiles/d20_pmc_traffic.md",
+    ("d20", "decode_attn"): {"bytes_per_launch": 7.2363e+07, "profile": "profiles/d20_pmc_traffic.md",
                              "sources": ('csrc/attention.hip', 'csrc/common.h', 'csrc/kernels.h'),
-                             "sha": "a34f6c8ef3c678e3"},
+                             "sha": "04f7d6c2a87f0269"},
     ("d26", "prefill_gemm"): {"bytes_per_launch": 1.7559e+09, "profile": "profiles/d26_prefill_pmc.md",
                              "sources": ('csrc/gemm.hip', 'csrc/common.h', 'csrc/kernels.h'),
                              "sha": "706ed5f8bdd703e1"},
-    ("d30", "decode_attn"): {"bytes_per_launch": 8.5856e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
+    ("d30", "decode_attn"): {"bytes_per_launch": 8.5874e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
                              "sources": ('csrc/attention.hip', 'csrc/common.h', 'csrc/kernels.h'),
-                             "sha": "a34f6c8ef3c678e3"},
+                             "sha": "04f7d6c2a87f0269"},
     ("d30", "decode_gemm"): {"bytes_per_launch": 4.7364e+07, "profile": "profiles/d30_decode_pmc_traffic.md",
                              "sources": ('csrc/gemv.hip', 'csrc/rowops.hip', 'csrc/finish.h', 'csrc/common.h', 'csrc/kernels.h'),
                              "sha": "b2c8f44f8b37a5e7"},

@@ -66,10 +66,11 @@ __global__ __launch_bounds__(64 * 8 / JN) void attn_prefill_kernel(const T* __re
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
-    // Work order over the whole launch (workgroups are dispatched x fastest, then y, then z):
-    // query blocks by decreasing length across every (row, head), so the launch ends on the
-    // shortest blocks (longest-first list scheduling); the (head, row) pairs of one query
-    // block follow each other, head fastest.
+    // Work order over the whole launch.  Workgroups are dispatched x fastest, then y, then z,
+    // and dealt round-robin to the 8 XCDs; with the query block in x (8 blocks for a 2048-token
+    // row) each XCD would always get the same block, the longest 8x the shortest's work.  So
+    // query blocks go by decreasing length across every (row, head), head fastest: each
+    // length spreads over all XCDs and the launch ends on the shortest blocks.
     const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const int hb = gridDim.y * gridDim.z;
     const int qb = gridDim.x - 1 - lin / hb;
